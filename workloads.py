@@ -1,0 +1,113 @@
+"""Seeded synthetic decode-attention workloads (shared input generator).
+
+This module is the only thing the oracle and the HIP path both consume.  It draws random
+numbers (query/key/value activations, outlier channels, per-channel scales, the +-1 sign
+flips and the SO(4) quaternion pairs of the rotation) and holds none of the method's
+arithmetic.  Shapes and distributions follow the workloads the pages measure on: a 4B
+GQA model at 8K context ("TurboQuant ... MNN on phones", section 4), 128K-token decode
+("RoPE-Aware Bit Allocation for KV-Cache Quantization", deployment results) and 32K
+contexts with the IsoQuant rotation ("RotaryQuant ...", key findings).  No dataset is
+read; Gaussian activations with outlier channels stand in for real model activations.
+"""
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    bits_k: int
+    bits_v: int
+    group: int               # rotation block = norm group = codebook dimension
+    so4: bool                # compose the Hadamard with SO(4) block rotations
+    dtype: str               # "float32" or "float16" activations
+    outliers: str            # "fixed2x10", "seeded4x8" or "lognormal"
+    n_splits: int = 1        # key-axis splits used when the workload is timed
+    scale: float = HEAD_DIM ** -0.5
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def with_len(self, seq_len, batch=None):
+        return replace(self, seq_len=seq_len, batch=self.batch if batch is None else batch)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 1, 256, 3, 3, 32, False, "float32", "fixed2x10"),
+    "gqa8k": Workload("gqa8k", 1, 32, 8, 8192, 3, 3, 32, False, "float16", "seeded4x8", n_splits=16),
+    "batched": Workload("batched", 32, 32, 8, 4096, 4, 3, 32, False, "float16", "seeded4x8"),
+    "long128k": Workload("long128k", 1, 16, 2, 131072, 3, 3, 32, False, "float16", "lognormal",
+                         n_splits=64),
+    "isoquant32k": Workload("isoquant32k", 8, 32, 8, 32768, 3, 3, 128, True, "float16", "seeded4x8",
+                            n_splits=4),
+}
+
+
+def generate(w: Workload, seed: int = 0, with_kv: bool = True):
+    """Draw one workload's inputs.
+
+    Returns a dict of numpy arrays:
+      q [B, Hq, 128], k [B, Hkv, T, 128], v [B, Hkv, T, 128] in ``w.dtype``;
+      signs [Hkv, 128] float32 (+-1); so4 [Hkv, 32, 2, 4] float32 unit (q_L, q_R) or None;
+      seq_lens [B] int32 (all equal to T).
+    Separate random streams feed each array, so changing one size leaves the others'
+    draws for a given seed unchanged where shapes allow.
+    """
+    ss = np.random.SeedSequence(seed)
+    r_q, r_k, r_v, r_sign, r_so4, r_ch, r_sk, r_sv = [np.random.default_rng(s) for s in ss.spawn(8)]
+    bsz, hq, hkv, t = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len
+    g = w.group_size
+
+    q = r_q.standard_normal((bsz, hq, HEAD_DIM), dtype=np.float32)
+    k = r_k.standard_normal((bsz, hkv, t, HEAD_DIM), dtype=np.float32) if with_kv else None
+    v = r_v.standard_normal((bsz, hkv, t, HEAD_DIM), dtype=np.float32) if with_kv else None
+
+    if w.outliers == "fixed2x10":
+        # channels 3 and 77 scaled by 10 in q, K and V
+        for arr in (q, k, v):
+            if arr is not None:
+                arr[..., [3, 77]] *= 10.0
+    elif w.outliers == "seeded4x8":
+        # 4 seeded channels per KV head scaled by 8 in K, V and that head's queries
+        for kv in range(hkv):
+            ch = r_ch.choice(HEAD_DIM, size=4, replace=False)
+            q[:, kv * g:(kv + 1) * g][..., ch] *= 8.0
+            if with_kv:
+                k[:, kv][..., ch] *= 8.0
+                v[:, kv][..., ch] *= 8.0
+    elif w.outliers == "lognormal":
+        # per-(KV head, channel) scale e^z, z ~ N(0, 1): one draw shared by K and its
+        # queries, an independent draw for V
+        sk = np.exp(r_sk.standard_normal((hkv, HEAD_DIM))).astype(np.float32)
+        sv = np.exp(r_sv.standard_normal((hkv, HEAD_DIM))).astype(np.float32)
+        for kv in range(hkv):
+            q[:, kv * g:(kv + 1) * g] *= sk[kv]
+            if with_kv:
+                k[:, kv] *= sk[kv]
+                v[:, kv] *= sv[kv]
+    else:
+        raise ValueError(w.outliers)
+
+    dt = np.float16 if w.dtype == "float16" else np.float32
+    signs = np.where(r_sign.random((hkv, HEAD_DIM)) < 0.5, -1.0, 1.0).astype(np.float32)
+    so4 = None
+    if w.so4:
+        quat = r_so4.standard_normal((hkv, HEAD_DIM // 4, 2, 4))
+        so4 = (quat / np.linalg.norm(quat, axis=-1, keepdims=True)).astype(np.float32)
+    return {
+        "q": q.astype(dt),
+        "k": None if k is None else k.astype(dt),
+        "v": None if v is None else v.astype(dt),
+        "signs": signs,
+        "so4": so4,
+        "seq_lens": np.full(bsz, t, dtype=np.int32),
+    }
