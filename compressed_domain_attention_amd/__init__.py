@@ -1,0 +1,205 @@
+"""Compressed-domain decode attention on a packed 3/4-bit KV cache, for MI355X (gfx950).
+
+Thin ctypes binding over ``libtq.so`` (C ABI in ``include/tq.h``).  This module only
+marshals arguments: it allocates cache buffers with PyTorch (device memory is PyTorch's
+job here), fills the C structs, and passes raw device pointers plus the current HIP
+stream.  Every step of quantisation and attention runs in the library's HIP kernels.
+There is no fallback: if the library is missing the calls raise ``NativeLibraryMissing``.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "NativeLibraryMissing", "TQError", "Codebook", "make_codebook", "Rotation", "PackedCache",
+    "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
+    "TQ_KEYS", "TQ_VALUES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+HEAD_DIM = 128
+TILE = 32
+TQ_KEYS = 0
+TQ_VALUES = 1
+_SCHEDULES = {"auto": 0, "vec": 1, "mfma": 2}
+_DTYPES = {torch.float32: 0, torch.float16: 1}
+
+
+class NativeLibraryMissing(RuntimeError):
+    pass
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s (status %d)" % (what, _status_string(status), status))
+        self.status = status
+
+
+class Codebook(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("centroid", ctypes.c_float * 16), ("boundary", ctypes.c_float * 15)]
+
+    @property
+    def centroids(self):
+        return [self.centroid[k] for k in range(1 << self.bits)]
+
+    @property
+    def boundaries(self):
+        return [self.boundary[k] for k in range((1 << self.bits) - 1)]
+
+
+class _Rotation(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("signs", ctypes.c_void_p), ("so4", ctypes.c_void_p)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("role", ctypes.c_int32), ("codebook", Codebook)]
+
+
+_lib = None
+
+EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_decode_attention", "tq_merge_splits")
+
+
+def library():
+    """Load libtq.so once; raise NativeLibraryMissing if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NativeLibraryMissing("%s is not built: run `python compressed_domain_attention_amd/build.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.tq_status_string.argtypes = [I]
+    lib.tq_status_string.restype = ctypes.c_char_p
+    lib.tq_make_codebook.argtypes = [I, I, ctypes.POINTER(Codebook)]
+    lib.tq_make_codebook.restype = I
+    lib.tq_quantize_append.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), P, I, I, P, I, I, P]
+    lib.tq_quantize_append.restype = I
+    lib.tq_decode_attention.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), ctypes.POINTER(_Cache),
+                                        P, I, I, P, I, F, I, I, P, P, P, P, P]
+    lib.tq_decode_attention.restype = I
+    lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
+    lib.tq_merge_splits.restype = I
+    _lib = lib
+    return lib
+
+
+def _status_string(status):
+    try:
+        return library().tq_status_string(status).decode()
+    except NativeLibraryMissing:
+        return "unknown"
+
+
+def _check(status, what):
+    if status != 0:
+        raise TQError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_codebook(bits: int, dim: int) -> Codebook:
+    """Lloyd-Max codebook for dimension ``dim`` (host computation inside the library)."""
+    cb = Codebook()
+    _check(library().tq_make_codebook(bits, dim, ctypes.byref(cb)), "tq_make_codebook")
+    return cb
+
+
+class Rotation:
+    """Per-KV-head rotation: signs [H, 128] (+-1) and optional SO(4) pairs [H, 32, 2, 4]."""
+
+    def __init__(self, signs: torch.Tensor, group: int, so4: torch.Tensor = None):
+        self.signs = signs.contiguous().to(torch.float32)
+        self.so4 = None if so4 is None else so4.contiguous().to(torch.float32)
+        self.group = group
+        self.n_kv_heads = self.signs.shape[0]
+        self.c = _Rotation(group, self.n_kv_heads, self.signs.data_ptr(),
+                           None if self.so4 is None else self.so4.data_ptr())
+
+
+class PackedCache:
+    """Caller-owned packed keys or values: codes + fp32 group norms, layout of include/tq.h."""
+
+    def __init__(self, batch, n_kv_heads, capacity, bits, group, role, device="cuda", codebook=None,
+                 codes=None, norms=None):
+        if capacity % TILE:
+            raise ValueError("capacity must be a multiple of %d" % TILE)
+        self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
+        self.bits, self.group, self.role = bits, group, role
+        self.codebook = codebook if codebook is not None else make_codebook(bits, group)
+        ng = HEAD_DIM // group
+        if codes is None:
+            shape = ((batch, n_kv_heads, capacity, 16 * bits) if role == TQ_KEYS
+                     else (batch, n_kv_heads, capacity // TILE, TILE * 16 * bits))
+            codes = torch.zeros(shape, dtype=torch.uint8, device=device)
+        if norms is None:
+            norms = torch.zeros((batch, n_kv_heads, capacity // TILE, ng, TILE), dtype=torch.float32, device=device)
+        self.codes, self.norms = codes, norms
+        self.c = _Cache(codes.data_ptr(), norms.data_ptr(), batch, n_kv_heads, capacity, bits, group, role,
+                        self.codebook)
+
+
+def quantize_append(rot: Rotation, cache: PackedCache, x: torch.Tensor, pos: torch.Tensor = None, pos0: int = 0,
+                    max_pos: int = None):
+    """Quantise x [batch, n_kv_heads, n_new, 128] (fp16/fp32) into slots pos.. of the cache."""
+    if x.dtype not in _DTYPES or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float16/float32 tensor")
+    n_new = x.shape[2]
+    if max_pos is None:
+        max_pos = int(pos.max().item()) if pos is not None else pos0
+    _check(library().tq_quantize_append(ctypes.byref(rot.c), ctypes.byref(cache.c), _ptr(x), _DTYPES[x.dtype],
+                                        n_new, _ptr(pos), pos0, max_pos, _stream()), "tq_quantize_append")
+
+
+def decode_attention(rot: Rotation, keys: PackedCache, values: PackedCache, q: torch.Tensor, seq_lens=None,
+                     max_len=None, scale=None, n_splits=1, schedule="auto", out=None, lse=None, part_o=None,
+                     part_lse=None):
+    """One decode step.  n_splits == 1 -> (out, lse); n_splits > 1 -> (part_o, part_lse)."""
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    if max_len is None:
+        max_len = int(seq_lens.max().item()) if seq_lens is not None else keys.capacity
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_decode_attention(
+        ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(q), _DTYPES[q.dtype], hq,
+        _ptr(seq_lens), max_len, scale, n_splits, _SCHEDULES[schedule], _ptr(out), _ptr(lse), _ptr(part_o),
+        _ptr(part_lse), _stream()), "tq_decode_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+def merge_splits(rot: Rotation, part_o: torch.Tensor, part_lse: torch.Tensor, out=None, lse=None):
+    """Log-sum-exp merge of split partials and the inverse rotation -> (out, lse)."""
+    n_splits, bsz, hq = part_lse.shape
+    if out is None:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=part_o.device)
+    if lse is None:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=part_o.device)
+    _check(library().tq_merge_splits(ctypes.byref(rot.c), n_splits, bsz, hq, _ptr(part_o), _ptr(part_lse),
+                                     _ptr(out), _ptr(lse), _stream()), "tq_merge_splits")
+    return out, lse

@@ -1,0 +1,147 @@
+// C ABI of the packed-KV decode attention library: argument checks on the host, then one
+// launch per call on the caller's stream.  No allocation, no global state.
+#include <cmath>
+#include <cstring>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool valid_codebook(const tq_codebook& cb, int bits, int group) { return cb.bits == bits && cb.dim == group; }
+
+tq_status check_rotation(const tq_rotation* rot) {
+  if (rot == nullptr || rot->signs == nullptr) return TQ_EINVAL;
+  if (rot->n_kv_heads <= 0) return TQ_EINVAL;
+  if (rot->group != 32 && rot->group != 128) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+tq_status check_cache(const tq_cache* c, const tq_rotation* rot, tq_role role) {
+  if (c == nullptr || c->codes == nullptr || c->norms == nullptr) return TQ_EINVAL;
+  if (c->role != role) return TQ_EINVAL;
+  if (c->batch <= 0 || c->capacity <= 0 || (c->capacity % TQ_TILE) != 0) return TQ_EINVAL;
+  if (c->n_kv_heads != rot->n_kv_heads) return TQ_EINVAL;
+  if (c->group != rot->group) return TQ_EINVAL;
+  if (c->bits != 3 && c->bits != 4) return TQ_EUNSUPPORTED;
+  if (!valid_codebook(c->codebook, c->bits, c->group)) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+}  // namespace
+
+extern "C" tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x, tq_dtype x_dtype,
+                                        int32_t n_new, const int32_t* pos, int32_t pos0, int32_t max_pos,
+                                        void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if ((st = check_cache(cache, rot, cache ? cache->role : TQ_KEYS)) != TQ_OK) return st;
+  if (cache->role != TQ_KEYS && cache->role != TQ_VALUES) return TQ_EINVAL;
+  if (x == nullptr || n_new < 0) return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
+  const int32_t first = pos ? max_pos : pos0;
+  if (first < 0 || pos0 < 0) return TQ_EINVAL;
+  if ((int64_t)first + n_new > cache->capacity) return TQ_ECAPACITY;
+  if (n_new == 0) return TQ_OK;
+
+  tq::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.codes = (uint8_t*)cache->codes;
+  a.norms = cache->norms;
+  a.signs = rot->signs;
+  a.so4 = rot->so4;
+  a.pos = pos;
+  a.pos0 = pos0;
+  a.n_new = n_new;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.capacity = cache->capacity;
+  for (int k = 0; k < 15; ++k) a.boundary[k] = cache->codebook.boundary[k];
+  // tiles touched: with a device-side start the alignment is unknown, so cover the worst
+  const int span = pos ? (TQ_TILE - 1) + n_new : (pos0 % TQ_TILE) + n_new;
+  const int n_tiles = (span + TQ_TILE - 1) / TQ_TILE;
+  return from_hip(tq::launch_append(a, cache->bits, cache->group, cache->role == TQ_VALUES, x_dtype == TQ_F16,
+                                    cache->batch, n_tiles, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                         const void* q, tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens,
+                                         int32_t max_len, float scale, int32_t n_splits, tq_schedule schedule,
+                                         float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if ((st = check_cache(keys, rot, TQ_KEYS)) != TQ_OK) return st;
+  if ((st = check_cache(values, rot, TQ_VALUES)) != TQ_OK) return st;
+  if (keys->batch != values->batch) return TQ_EINVAL;
+  if (q == nullptr || (q_dtype != TQ_F32 && q_dtype != TQ_F16)) return TQ_EINVAL;
+  if (n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
+  if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (max_len > keys->capacity || max_len > values->capacity) return TQ_ECAPACITY;
+  if (n_splits == 1 && out == nullptr) return TQ_EINVAL;
+  if (n_splits > 1 && (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
+  if (schedule != TQ_SCHEDULE_AUTO && schedule != TQ_SCHEDULE_VEC && schedule != TQ_SCHEDULE_MFMA) return TQ_EINVAL;
+
+  const int group_size = n_q_heads / rot->n_kv_heads;
+  const bool share = keys->bits == values->bits &&
+                     std::memcmp(keys->codebook.centroid, values->codebook.centroid, sizeof(float) * 16) == 0;
+  // every supported (bits, group) pair has a matrix-core kernel, so AUTO takes it
+  const int sched = schedule == TQ_SCHEDULE_VEC ? 1 : 2;
+
+  tq::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.kc = (const uint8_t*)keys->codes;
+  a.kn = keys->norms;
+  a.vc = (const uint8_t*)values->codes;
+  a.vn = values->norms;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.signs = rot->signs;
+  a.so4 = rot->so4;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.max_len = max_len;
+  a.batch = keys->batch;
+  a.n_kv_heads = rot->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group_size = group_size;
+  const int hps = sched == 2 ? tq::mfma_heads_per_slice(rot->group) : 16;
+  a.heads_per_slice = group_size < hps ? group_size : hps;
+  a.n_slices = (group_size + a.heads_per_slice - 1) / a.heads_per_slice;
+  a.n_splits = n_splits;
+  a.capacity = keys->capacity;
+  if (values->capacity != keys->capacity) return TQ_EINVAL;
+  a.rot_group = rot->group;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  for (int k = 0; k < 16; ++k) {
+    a.kcent[k] = keys->codebook.centroid[k];
+    a.vcent[k] = values->codebook.centroid[k];
+  }
+  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, share && sched == 2,
+                                    (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,
+                                     const float* part_o, const float* part_lse, float* out, float* lse_out,
+                                     void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if (n_splits < 1 || batch <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
+  if (part_o == nullptr || part_lse == nullptr || out == nullptr) return TQ_EINVAL;
+  tq::MergeArgs a;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.signs = rot->signs;
+  a.so4 = rot->so4;
+  a.n_splits = n_splits;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.group_size = n_q_heads / rot->n_kv_heads;
+  a.rot_group = rot->group;
+  return from_hip(tq::launch_merge(a, (hipStream_t)stream));
+}

@@ -1,0 +1,81 @@
+// Launch-level interface between the C ABI (tq_api.cpp) and the HIP kernels
+// (tq_kernels.hip).  Plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 32;
+
+struct AppendArgs {
+  const void* x;            // [batch][n_kv_heads][n_new][128]
+  uint8_t* codes;
+  float* norms;
+  const float* signs;       // [n_kv_heads][128]
+  const float* so4;         // [n_kv_heads][32][2][4] or null
+  const int32_t* pos;       // [batch] or null
+  int32_t pos0;
+  int32_t n_new;
+  int32_t n_kv_heads;
+  int32_t capacity;
+  float boundary[15];
+};
+
+struct DecodeArgs {
+  const uint8_t* kc;        // key records
+  const float* kn;          // key norms
+  const uint8_t* vc;        // value tiles
+  const float* vn;          // value norms
+  const void* q;            // [batch][n_q_heads][128]
+  const int32_t* seq_lens;  // [batch] or null
+  const float* signs;
+  const float* so4;
+  float* out;               // n_splits == 1
+  float* lse_out;           // optional
+  float* part_o;            // n_splits > 1
+  float* part_lse;
+  int32_t max_len;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t group_size;       // query heads per KV head
+  int32_t heads_per_slice;  // query heads one workgroup serves
+  int32_t n_slices;         // workgroups per (sequence, KV head, split)
+  int32_t n_splits;
+  int32_t capacity;
+  int32_t rot_group;        // 32 or 128
+  float scale_log2;         // softmax scale * log2(e)
+  float kcent[16];
+  float vcent[16];
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  float* out;
+  float* lse_out;
+  const float* signs;
+  const float* so4;
+  int32_t n_splits;
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t group_size;
+  int32_t rot_group;
+};
+
+// Each returns the hipError_t of the launch.
+hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, bool x_f16, int batch,
+                         int n_tiles, hipStream_t stream);
+// schedule: 1 = vector (fp32), 2 = matrix cores
+hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
+                         bool share_table, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// Heads one workgroup of the matrix-core schedule can serve (the 16 MFMA columns hold
+// (norm group, head) pairs).
+inline int mfma_heads_per_slice(int rot_group) { return rot_group == 32 ? 4 : 16; }
+
+}  // namespace tq

@@ -1,0 +1,881 @@
+// HIP kernels for decode attention on a rotated, Lloyd-Max-quantised, bit-packed KV cache.
+// Target: gfx950 (MI355X), wave64.
+//
+// Method sources (page, section): "TurboQuant: ... MNN on phones" 2.1-2.3 and 3.1-3.4
+// (norm -> rotate -> per-coordinate codebook search; block-32 Walsh-Hadamard with sign
+// flips; rotated-domain key dot and value sum); "RotaryQuant ... Fused Compressed-Space
+// Attention", key designs 2-3 (Hadamard followed by SO(4) block rotations; rotate the
+// query once and the output once); "RoPE-Aware Bit Allocation for KV-Cache
+// Quantization", packed-cache implementation details (key-axis split, log-sum-exp merge,
+// whole-prompt quantisation in one call).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Position of tile token t inside a tile's norm block (layout in tq.h).
+__device__ __forceinline__ int norm_pos(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
+
+__device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
+
+// ---------------------------------------------------------------------------------------
+// Quaternions (real, i, j, k): the IsoQuant block rotation v -> q_L v conj(q_R).
+struct Quat {
+  float w, x, y, z;
+};
+__device__ __forceinline__ Quat qmul(Quat a, Quat b) {
+  return {a.w * b.w - a.x * b.x - a.y * b.y - a.z * b.z, a.w * b.x + a.x * b.w + a.y * b.z - a.z * b.y,
+          a.w * b.y - a.x * b.z + a.y * b.w + a.z * b.x, a.w * b.z + a.x * b.y - a.y * b.x + a.z * b.w};
+}
+__device__ __forceinline__ Quat qconj(Quat a) { return {a.w, -a.x, -a.y, -a.z}; }
+__device__ __forceinline__ Quat qload(const float* p) {
+  const float4 v = *(const float4*)p;
+  return {v.x, v.y, v.z, v.w};
+}
+
+// Rotation of nh head vectors held in LDS (buf[nh][128]) by the whole workgroup.
+// Forward: signs, normalised Hadamard on every `group` block, then SO(4) if present.
+// Inverse: the reverse.  Called uniformly by every thread of the block.
+template <bool FWD>
+__device__ void lds_rotate(float* buf, int nh, const float* signs, const float* so4, int group) {
+  const int nt = blockDim.x, tid = threadIdx.x, n = nh * kHeadDim;
+  if (FWD) {
+    for (int i = tid; i < n; i += nt) buf[i] *= signs[i & (kHeadDim - 1)];
+    __syncthreads();
+  } else if (so4 != nullptr) {
+    for (int p = tid; p < nh * 32; p += nt) {
+      float* v = buf + (p >> 5) * kHeadDim + 4 * (p & 31);
+      const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
+      const Quat o = qmul(qmul(qconj(l), Quat{v[0], v[1], v[2], v[3]}), r);
+      v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
+    }
+    __syncthreads();
+  }
+  for (int s = 1; s < group; s <<= 1) {
+    for (int p = tid; p < nh * 64; p += nt) {
+      const int j = p & 63;
+      const int i0 = (p >> 6) * kHeadDim + (j / s) * 2 * s + (j % s);
+      const float x0 = buf[i0], x1 = buf[i0 + s];
+      buf[i0] = x0 + x1;
+      buf[i0 + s] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const float hs = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  if (FWD) {
+    for (int i = tid; i < n; i += nt) buf[i] *= hs;
+    __syncthreads();
+    if (so4 != nullptr) {
+      for (int p = tid; p < nh * 32; p += nt) {
+        float* v = buf + (p >> 5) * kHeadDim + 4 * (p & 31);
+        const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
+        const Quat o = qmul(qmul(l, Quat{v[0], v[1], v[2], v[3]}), qconj(r));
+        v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int i = tid; i < n; i += nt) buf[i] *= hs * signs[i & (kHeadDim - 1)];
+    __syncthreads();
+  }
+}
+
+// Bit field of width W at bit offset `off` of a little-endian dword array; `off` and W
+// are compile-time constants after unrolling.
+template <int W>
+__device__ __forceinline__ uint32_t field(const uint32_t* d, int off) {
+  const int wi = off >> 5, sh = off & 31;
+  const uint32_t x = (sh + W <= 32) ? (d[wi] >> sh) : __builtin_amdgcn_alignbit(d[wi + 1], d[wi], sh);
+  return x & ((1u << W) - 1u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Append: fused norm + sign flip + Walsh-Hadamard + [SO(4)] + codebook search + pack.
+// One workgroup of 128 threads owns one 32-slot tile of one (sequence, KV head); thread
+// (token, chunk) holds 32 consecutive coordinates in registers.  The 32-point transform
+// runs in registers; a whole-head (128) transform adds two cross-lane stages.
+template <int BITS, int GROUP, bool VALUES, bool XF16>
+__global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
+  constexpr int NB = (1 << BITS) - 1;
+  constexpr int NG = kHeadDim / GROUP;
+  __shared__ uint32_t tile_codes[VALUES ? kTile * kHeadDim / 4 : 1];  // u8 [32][128]
+  const int tid = threadIdx.x, tok = tid >> 2, chunk = tid & 3;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int pos = a.pos ? a.pos[b] : a.pos0;
+  const int t0 = (pos / kTile + (int)blockIdx.x) * kTile;
+  if (t0 >= pos + a.n_new) return;  // uniform over the block
+  const int slot = t0 + tok;
+  const bool valid = slot >= pos && slot < pos + a.n_new;
+  const size_t stream = (size_t)b * a.n_kv_heads + h;
+
+  float v[32];
+  if (valid) {
+    const size_t row = (stream * a.n_new + (slot - pos)) * kHeadDim + chunk * 32;
+    if (XF16) {
+      const uint4* p = (const uint4*)((const _Float16*)a.x + row);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8_t hv = __builtin_bit_cast(half8_t, p[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * j + e] = (float)hv[e];
+      }
+    } else {
+      const float4* p = (const float4*)((const float*)a.x + row);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 f = p[j];
+        v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.f;
+  }
+
+  // sign flips (exact) and the group's squared norm
+  const float4* sp = (const float4*)(a.signs + h * kHeadDim + chunk * 32);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float4 s = sp[j];
+    v[4 * j] *= s.x; v[4 * j + 1] *= s.y; v[4 * j + 2] *= s.z; v[4 * j + 3] *= s.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss = fmaf(v[i], v[i], ss);
+  if (GROUP == 128) {
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+  }
+  const float nrm = sqrtf(ss);
+  const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= inv;
+
+  // 32-point Walsh-Hadamard butterfly in registers (Sylvester order)
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & s) == 0) {
+        const float x0 = v[i], x1 = v[i + s];
+        v[i] = x0 + x1;
+        v[i + s] = x0 - x1;
+      }
+    }
+  }
+  if (GROUP == 128) {  // coordinate bits 5 and 6 live in the lane's chunk index
+#pragma unroll
+    for (int st = 1; st <= 2; st <<= 1) {
+      const bool upper = (chunk & st) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float o = __shfl_xor(v[i], st);
+        v[i] = upper ? (o - v[i]) : (v[i] + o);
+      }
+    }
+  }
+  const float hs = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= hs;
+
+  if (a.so4 != nullptr) {
+    const float* qp = a.so4 + ((size_t)h * 32 + chunk * 8) * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const Quat l = qload(qp + 8 * k), r = qload(qp + 8 * k + 4);
+      const Quat o = qmul(qmul(l, Quat{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]}), qconj(r));
+      v[4 * k] = o.w; v[4 * k + 1] = o.x; v[4 * k + 2] = o.y; v[4 * k + 3] = o.z;
+    }
+  }
+
+  // code = number of boundaries strictly below the value
+  uint32_t code[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) c += v[i] > a.boundary[k] ? 1u : 0u;
+    code[i] = c;
+  }
+
+  const int ntile = a.capacity / kTile;
+  if (valid && (GROUP == 32 || chunk == 0)) {
+    const int grp = GROUP == 32 ? chunk : 0;
+    a.norms[(stream * ntile + t0 / kTile) * (NG * kTile) + grp * kTile + norm_pos(tok)] = nrm;
+  }
+
+  if (!VALUES) {
+    if (valid) {
+      uint32_t* o = (uint32_t*)(a.codes + (stream * a.capacity + slot) * (16 * BITS) + chunk * (4 * BITS));
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x |= code[8 * j + e] << (BITS * e);
+        w[j] = x;
+      }
+      if (BITS == 3) {
+        o[0] = w[0] | (w[1] << 24);
+        o[1] = (w[1] >> 8) | (w[2] << 16);
+        o[2] = (w[2] >> 16) | (w[3] << 8);
+      } else {
+        *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    return;
+  }
+
+  // values: stage byte codes of the whole tile, then emit 8-token words
+  uint8_t* tc = (uint8_t*)tile_codes;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tile_codes[(tok * kHeadDim + chunk * 32) / 4 + j] =
+        code[4 * j] | (code[4 * j + 1] << 8) | (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
+  }
+  __syncthreads();
+  const int vlo = pos > t0 ? pos - t0 : 0;
+  const int vhi = min(kTile, pos + a.n_new - t0);
+  const int w0 = 4 * tid;  // four consecutive words: same (q, m), u = u0..u0+3
+  const int q = w0 >> 7, m = (w0 >> 3) & 15, u0 = w0 & 7;
+  uint32_t word[4], mask[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 16 * (u0 + j) + m;
+    uint32_t x = 0, mk = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = 16 * (k >> 2) + 4 * q + (k & 3);
+      if (t >= vlo && t < vhi) {
+        x |= (uint32_t)tc[t * kHeadDim + i] << (BITS * k);
+        mk |= (uint32_t)NB << (BITS * k);
+      }
+    }
+    word[j] = x;
+    mask[j] = mk;
+  }
+  uint32_t* o = (uint32_t*)(a.codes + (stream * ntile + t0 / kTile) * (kTile * 16 * BITS) + w0 * BITS);
+  constexpr int ND = BITS;  // dwords for 4 words
+  uint32_t dv[4], dm[4];
+  if (BITS == 3) {
+    dv[0] = word[0] | (word[1] << 24); dv[1] = (word[1] >> 8) | (word[2] << 16); dv[2] = (word[2] >> 16) | (word[3] << 8);
+    dm[0] = mask[0] | (mask[1] << 24); dm[1] = (mask[1] >> 8) | (mask[2] << 16); dm[2] = (mask[2] >> 16) | (mask[3] << 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { dv[j] = word[j]; dm[j] = mask[j]; }
+  }
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    if (dm[j] == 0xFFFFFFFFu) o[j] = dv[j];
+    else if (dm[j] != 0u) o[j] = (o[j] & ~dm[j]) | dv[j];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Shared decode pieces.
+
+struct Unit {
+  int b, kv, split, slice, h0, hs;
+};
+
+__device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, bool xcd_pairs) {
+  const int ns = a.n_slices;
+  const int n_units = a.batch * a.n_kv_heads * a.n_splits;
+  const int L = blockIdx.x;
+  int unit, slice;
+  if (xcd_pairs && ns > 1 && (n_units & 7) == 0) {
+    // the slices of one unit get linear ids 8 apart: same XCD, dispatched together, so the
+    // second one reads the shared codes from that XCD's L2
+    const int g8 = L / (8 * ns), rem = L - g8 * 8 * ns;
+    slice = rem >> 3;
+    unit = g8 * 8 + (rem & 7);
+  } else {
+    unit = L / ns;
+    slice = L - unit * ns;
+  }
+  Unit u;
+  u.split = unit % a.n_splits;
+  u.kv = (unit / a.n_splits) % a.n_kv_heads;
+  u.b = unit / (a.n_splits * a.n_kv_heads);
+  u.slice = slice;
+  u.h0 = u.kv * a.group_size + slice * a.heads_per_slice;
+  u.hs = min(a.heads_per_slice, a.group_size - slice * a.heads_per_slice);
+  return u;
+}
+
+template <bool QF16>
+__device__ __forceinline__ void load_queries(const DecodeArgs& a, const Unit& u, float* qbuf) {
+  for (int i = threadIdx.x; i < u.hs * kHeadDim; i += blockDim.x) {
+    const size_t qi = ((size_t)u.b * a.n_q_heads + u.h0 + (i >> 7)) * kHeadDim + (i & 127);
+    qbuf[i] = QF16 ? (float)((const _Float16*)a.q)[qi] : ((const float*)a.q)[qi];
+  }
+  __syncthreads();
+}
+
+// Final per-head result o_rot[hs][128] (rotated domain, normalised) and lse in log2 units:
+// either rotate back and write `out`, or write this split's partial.
+__device__ __forceinline__ void write_result(const DecodeArgs& a, const Unit& u, float* obuf,
+                                             const float* lse2) {
+  const int tid = threadIdx.x;
+  if (a.n_splits == 1) {
+    if (a.lse_out && tid < u.hs) {
+      a.lse_out[(size_t)u.b * a.n_q_heads + u.h0 + tid] = lse2[tid] * kLn2;
+    }
+    lds_rotate<false>(obuf, u.hs, a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.rot_group);
+    for (int i = tid; i < u.hs * kHeadDim; i += blockDim.x) {
+      a.out[((size_t)u.b * a.n_q_heads + u.h0 + (i >> 7)) * kHeadDim + (i & 127)] = obuf[i];
+    }
+  } else {
+    const size_t row0 = ((size_t)u.split * a.batch + u.b) * a.n_q_heads + u.h0;
+    if (tid < u.hs) a.part_lse[row0 + tid] = lse2[tid] * kLn2;
+    for (int i = tid; i < u.hs * kHeadDim; i += blockDim.x) {
+      a.part_o[(row0 + (i >> 7)) * kHeadDim + (i & 127)] = obuf[i];
+    }
+  }
+}
+
+__device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, int& lo, int& hi) {
+  // lengths beyond max_len (checked against the capacity on the host) are clamped, so a
+  // bad device length can never move a read outside the cache
+  const int T = a.seq_lens ? max(0, min(a.seq_lens[u.b], a.max_len)) : a.max_len;
+  const int C = (T + a.n_splits - 1) / a.n_splits;
+  lo = min(T, u.split * C);
+  hi = min(T, lo + C);
+}
+
+// ---------------------------------------------------------------------------------------
+// Matrix-core decode.
+//
+// Scores: for a 16-token tile, D[token][col] = sum_k A[token][k] B[k][col] with A = key
+// codebook values (fp16 hi and lo parts, decoded through an LDS table) and B = the rotated
+// query (fp16 hi and lo parts), col = (norm group, head) so that D holds per-group partial
+// dots; D is scaled by the group norms and summed across the group lanes.  Three products
+// per operand pair (hi.hi + hi.lo + lo.hi) keep the score at fp32-level accuracy.
+// Values: O[coord][col] += sum_k A[coord][k] P'[k][col] over the 32 tokens of a tile, with
+// A = value codebook values (value words hold 8 tokens of one coordinate) and P' = p * norm
+// in fp16, read straight from the score registers.  Online softmax per column.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
+                                                0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int BK, int BV>
+struct Block {
+  uint32_t k0[BK], k1[BK];  // this lane's 32 key coordinates of tile tokens (lane&15) and 16+(lane&15)
+  f32x4 kn0, kn1;           // key norms of tokens 4q'+r and 16+4q'+r
+  uint32_t v[2 * BV];       // this lane's 8 value words
+  f32x4 vn0, vn1;           // value norms, same tokens as kn
+};
+
+template <int BK, int BV, int NG, bool SHARE, bool QF16>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+  constexpr int NW = 4;
+  constexpr int HPS = NG == 4 ? 4 : 16;
+  constexpr int KTAB = BK == 3 ? 4096 * 16 : 256 * 8;   // entry: 4 (3-bit) or 2 (4-bit) codes, hi then lo
+  constexpr int VTAB = SHARE ? 0 : (BV == 3 ? 4096 * 8 : 256 * 4);
+  constexpr int VSTRIDE = SHARE ? (BV == 3 ? 16 : 8) : (BV == 3 ? 8 : 4);
+  constexpr int SCR = NW * HPS * (kHeadDim + 2) * 4;
+  constexpr int BIG = (KTAB + VTAB) > SCR ? (KTAB + VTAB) : SCR;
+  constexpr int KREC = 16 * BK;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[BIG];
+  __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
+  __shared__ uint32_t cbk[16], cbv[16];
+  __shared__ float red[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const Unit u = decode_unit(a, true);
+  const uint8_t* ktab = smem;
+  const uint8_t* vtab = SHARE ? smem : smem + KTAB;
+
+  // fp16 codebooks: keys as (hi, lo), values as hi
+  if (tid < 16) {
+    const float c = a.kcent[tid];
+    const _Float16 hi = (_Float16)c;
+    const _Float16 lo = (_Float16)(c - (float)hi);
+    cbk[tid] = f16_bits(hi) | (f16_bits(lo) << 16);
+    cbv[tid] = f16_bits((_Float16)a.vcent[tid]);
+  }
+  __syncthreads();
+  if (BK == 3) {
+    for (int e = tid; e < 4096; e += 256) {
+      const uint32_t c0 = cbk[e & 7], c1 = cbk[(e >> 3) & 7], c2 = cbk[(e >> 6) & 7], c3 = cbk[(e >> 9) & 7];
+      const u32x4 ent = {(c0 & 0xFFFFu) | (c1 << 16), (c2 & 0xFFFFu) | (c3 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u),
+                         (c2 >> 16) | (c3 & 0xFFFF0000u)};
+      *(u32x4*)(smem + e * 16) = ent;
+    }
+  } else {
+    for (int e = tid; e < 256; e += 256) {
+      const uint32_t c0 = cbk[e & 15], c1 = cbk[e >> 4];
+      const u32x2 ent = {(c0 & 0xFFFFu) | (c1 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u)};
+      *(u32x2*)(smem + e * 8) = ent;
+    }
+  }
+  if (!SHARE) {
+    if (BV == 3) {
+      for (int e = tid; e < 4096; e += 256) {
+        const u32x2 ent = {cbv[e & 7] | (cbv[(e >> 3) & 7] << 16), cbv[(e >> 6) & 7] | (cbv[(e >> 9) & 7] << 16)};
+        *(u32x2*)(smem + KTAB + e * 8) = ent;
+      }
+    } else {
+      for (int e = tid; e < 256; e += 256) *(uint32_t*)(smem + KTAB + e * 4) = cbv[e & 15] | (cbv[e >> 4] << 16);
+    }
+  }
+
+  // rotated, scaled query (log2 units), split into fp16 hi + lo with a power-of-two prescale
+  load_queries<QF16>(a, u, qbuf);
+  lds_rotate<true>(qbuf, u.hs, a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.rot_group);
+  float mx = 0.f;
+  for (int i = tid; i < u.hs * kHeadDim; i += 256) {
+    const float x = qbuf[i] * a.scale_log2;
+    qbuf[i] = x;
+    mx = fmaxf(mx, fabsf(x));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int ex = 0;
+  if (mx > 0.f && mx < INFINITY) (void)frexpf(mx, &ex);
+  const float qs = ldexpf(1.f, 14 - ex), qinv = ldexpf(1.f, ex - 14);
+
+  const int col = lane & 15, qg = lane >> 4;
+  const int cgrp = NG == 4 ? (col >> 2) : 0;
+  const int chl = NG == 4 ? (col & 3) : col;
+  const bool colok = chl < u.hs;
+  u32x4 Bh[4], Bl[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x0 = 0.f, x1 = 0.f;
+      if (colok && (NG == 1 || cgrp == qg)) {
+        const float* src = qbuf + chl * kHeadDim + 32 * qg + 8 * w + 2 * p;
+        x0 = src[0] * qs;
+        x1 = src[1] * qs;
+      }
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+      Bh[w][p] = f16_bits(h0) | (f16_bits(h1) << 16);
+      Bl[w][p] = f16_bits(l0) | (f16_bits(l1) << 16);
+    }
+  }
+
+  int lo, hi;
+  token_range(a, u, lo, hi);
+  const int blk0 = lo / kTile, blk1 = (hi + kTile - 1) / kTile;
+  const size_t sb = (size_t)u.b * a.n_kv_heads + u.kv;
+  const int ntile = a.capacity / kTile;
+  const uint8_t* kbase = a.kc + sb * a.capacity * KREC + (lane & 15) * KREC + qg * (4 * BK);
+  const float* knbase = a.kn + sb * ntile * (NG * kTile) + cgrp * kTile + 8 * qg;
+  const uint8_t* vbase = a.vc + sb * ntile * (kTile * 16 * BV) + lane * (8 * BV);
+  const float* vnbase = a.vn + sb * ntile * (NG * kTile) + cgrp * kTile + 8 * qg;
+
+  auto load_block = [&](Block<BK, BV>& d, int blk) {
+    const uint32_t* kp = (const uint32_t*)(kbase + (size_t)blk * kTile * KREC);
+#pragma unroll
+    for (int j = 0; j < BK; ++j) d.k0[j] = kp[j];
+    kp = (const uint32_t*)(kbase + ((size_t)blk * kTile + 16) * KREC);
+#pragma unroll
+    for (int j = 0; j < BK; ++j) d.k1[j] = kp[j];
+    const f32x4* knp = (const f32x4*)(knbase + (size_t)blk * (NG * kTile));
+    d.kn0 = knp[0];
+    d.kn1 = knp[1];
+    const uint32_t* vp = (const uint32_t*)(vbase + (size_t)blk * (kTile * 16 * BV));
+#pragma unroll
+    for (int j = 0; j < 2 * BV; ++j) d.v[j] = vp[j];
+    const f32x4* vnp = (const f32x4*)(vnbase + (size_t)blk * (NG * kTile));
+    d.vn0 = vnp[0];
+    d.vn1 = vnp[1];
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // tables complete
+
+  int blk = blk0 + wv;
+  Block<BK, BV> cur;
+  if (blk < blk1) load_block(cur, blk);
+  for (; blk < blk1; blk += NW) {
+    Block<BK, BV> nxt;
+    load_block(nxt, min(blk + NW, blk1 - 1));  // prefetch; the last one re-reads a valid block
+
+    // ---- scores of tokens 16h + 4q' + r
+    f32x4 D[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t* kk = h ? cur.k1 : cur.k0;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        u32x4 ah, al;
+        if (BK == 3) {
+          const u32x4 e0 = *(const u32x4*)(ktab + (field<12>(kk, 24 * w) << 4));
+          const u32x4 e1 = *(const u32x4*)(ktab + (field<12>(kk, 24 * w + 12) << 4));
+          ah = u32x4{e0.x, e0.y, e1.x, e1.y};
+          al = u32x4{e0.z, e0.w, e1.z, e1.w};
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 e = *(const u32x2*)(ktab + (((kk[w] >> (8 * j)) & 0xFFu) << 3));
+            ah[j] = e.x;
+            al[j] = e.y;
+          }
+        }
+        acc = mfma16(ah, Bh[w], acc);
+        acc = mfma16(ah, Bl[w], acc);
+        acc = mfma16(al, Bh[w], acc);
+      }
+      D[h] = acc;
+    }
+    float sc[8];
+    const int tb = blk * kTile + 4 * qg;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int h = k >> 2, r = k & 3;
+      float x = D[h][r] * (h ? cur.kn1[r] : cur.kn0[r]);
+      if (NG == 4) {
+        x += dpp<0x124>(x);  // row_ror:4
+        x += dpp<0x128>(x);  // row_ror:8
+      }
+      x *= qinv;
+      const int t = tb + 16 * h + r;
+      sc[k] = (t >= lo && t < hi) ? x : -INFINITY;
+    }
+
+    // ---- online softmax (log2 domain) for this lane's column
+    float bm = sc[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, sc[k]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mnew = fmaxf(m_run, bm);
+    if (__any(mnew > m_run)) {
+      const float al = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O[i] *= al;
+      l_run *= al;
+    }
+    m_run = mnew;
+    const float mu = m_run == -INFINITY ? 0.f : m_run;
+    u32x4 bp;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      float pv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = 2 * pr + e;
+        const float p = __builtin_amdgcn_exp2f(sc[k] - mu);
+        l_run += p;
+        const float nv = k < 4 ? cur.vn0[k] : cur.vn1[k - 4];
+        pv[e] = sc[k] == -INFINITY ? 0.f : p * nv;
+      }
+      bp[pr] = f16_bits((_Float16)pv[0]) | (f16_bits((_Float16)pv[1]) << 16);
+    }
+
+    // ---- value sum in the rotated domain
+#pragma unroll
+    for (int mu8 = 0; mu8 < 8; ++mu8) {
+      u32x4 av;
+      if (BV == 3) {
+        const u32x2 e0 = *(const u32x2*)(vtab + field<12>(cur.v, 24 * mu8) * VSTRIDE);
+        const u32x2 e1 = *(const u32x2*)(vtab + field<12>(cur.v, 24 * mu8 + 12) * VSTRIDE);
+        av = u32x4{e0.x, e0.y, e1.x, e1.y};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) av[j] = *(const uint32_t*)(vtab + ((cur.v[mu8] >> (8 * j)) & 0xFFu) * VSTRIDE);
+      }
+      O[mu8] = mfma16(av, bp, O[mu8]);
+    }
+    cur = nxt;
+  }
+
+  // ---- combine the waves of the workgroup
+  float lt = l_run;
+  lt += __shfl_xor(lt, 16);
+  lt += __shfl_xor(lt, 32);
+  __syncthreads();  // tables no longer read
+  float* so = (float*)smem;             // [NW][HPS][128]
+  float* sm = so + NW * HPS * kHeadDim;  // [NW][HPS]
+  float* sl = sm + NW * HPS;
+  if (colok) {
+#pragma unroll
+    for (int mu8 = 0; mu8 < 8; ++mu8) {
+      if (NG == 1 || (mu8 >> 1) == cgrp) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) so[(wv * HPS + chl) * kHeadDim + 16 * mu8 + 4 * qg + r] = O[mu8][r];
+      }
+    }
+    if (qg == 0 && cgrp == 0) {
+      sm[wv * HPS + chl] = m_run;
+      sl[wv * HPS + chl] = lt;
+    }
+  }
+  __syncthreads();
+  __shared__ float lse2[HPS];
+  for (int i = tid; i < u.hs * kHeadDim; i += 256) {
+    const int hl = i >> 7, c = i & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * HPS + hl]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm[w * HPS + hl] - mu);
+      L += sl[w * HPS + hl] * f;
+      acc += so[(w * HPS + hl) * kHeadDim + c] * f;
+    }
+    qbuf[i] = L > 0.f ? acc / L : 0.f;
+    if (c == 0) lse2[hl] = L > 0.f ? M + __log2f(L) : -INFINITY;
+  }
+  __syncthreads();
+  write_result(a, u, qbuf, lse2);
+}
+
+// ---------------------------------------------------------------------------------------
+// Vector (fp32) decode: token-parallel scores, dimension-parallel value sum, 64-token
+// steps.  Plain arithmetic; the cross-check for the matrix-core schedule and the fallback
+// for shapes it does not take.
+template <int BK, int BV, int NG, bool QF16>
+__global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
+  constexpr int MAXH = 16;
+  constexpr int KREC = 16 * BK;
+  __shared__ float qbuf[MAXH * kHeadDim];
+  __shared__ float cbk[16], cbv[16];
+  __shared__ float ps[MAXH][4][64];
+  __shared__ float pw[MAXH][64];
+  __shared__ float hm[MAXH], hsum[MAXH], halpha[MAXH];
+  __shared__ float oacc[2][MAXH][kHeadDim];
+  __shared__ float lse2[MAXH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const Unit u = decode_unit(a, false);
+  if (tid < 16) {
+    cbk[tid] = a.kcent[tid];
+    cbv[tid] = a.vcent[tid];
+  }
+  if (tid < MAXH) {
+    hm[tid] = -INFINITY;
+    hsum[tid] = 0.f;
+  }
+  load_queries<QF16>(a, u, qbuf);
+  lds_rotate<true>(qbuf, u.hs, a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.rot_group);
+  for (int i = tid; i < u.hs * kHeadDim; i += 256) qbuf[i] *= a.scale_log2;
+  __syncthreads();
+
+  int lo, hi;
+  token_range(a, u, lo, hi);
+  const size_t sb = (size_t)u.b * a.n_kv_heads + u.kv;
+  const int ntile = a.capacity / kTile;
+  const int i_coord = tid & 127, half = tid >> 7;
+  float acc[MAXH];
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h) acc[h] = 0.f;
+
+  for (int c0 = (lo / kTile) * kTile; c0 < hi; c0 += 64) {
+    // phase 1: partial scores, thread (token, quarter of the coordinates)
+    {
+      const int t = lane, part = wv, tok = c0 + t;
+      float pp[MAXH];
+#pragma unroll
+      for (int h = 0; h < MAXH; ++h) pp[h] = 0.f;
+      if (tok >= lo && tok < hi) {
+        uint32_t d[BK];
+        const uint32_t* kp = (const uint32_t*)(a.kc + (sb * a.capacity + tok) * KREC + part * 4 * BK);
+#pragma unroll
+        for (int j = 0; j < BK; ++j) d[j] = kp[j];
+        float cv[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) cv[e] = cbk[field<BK>(d, BK * e)];
+        const float nk = a.kn[(sb * ntile + tok / kTile) * (NG * kTile) + (NG == 4 ? part : 0) * kTile +
+                              norm_pos(tok & (kTile - 1))];
+#pragma unroll
+        for (int h = 0; h < MAXH; ++h) {
+          if (h < u.hs) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) s = fmaf(qbuf[h * kHeadDim + 32 * part + e], cv[e], s);
+            pp[h] = s * nk;
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < MAXH; ++h)
+        if (h < u.hs) ps[h][part][t] = pp[h];
+    }
+    __syncthreads();
+    // phase 2: per-head online softmax over the 64 tokens
+    for (int h = wv; h < u.hs; h += 4) {
+      const int tok = c0 + lane;
+      float s = ps[h][0][lane] + ps[h][1][lane] + ps[h][2][lane] + ps[h][3][lane];
+      s = (tok >= lo && tok < hi) ? s : -INFINITY;
+      float bm = s;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+      const float mold = hm[h];
+      const float mnew = fmaxf(mold, bm);
+      const float al = mnew > mold ? __builtin_amdgcn_exp2f(mold - mnew) : 1.f;
+      const float mu = mnew == -INFINITY ? 0.f : mnew;
+      const float p = __builtin_amdgcn_exp2f(s - mu);
+      float psum = p;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) psum += __shfl_xor(psum, o);
+      pw[h][lane] = p;
+      if (lane == 0) {
+        hm[h] = mnew;
+        hsum[h] = hsum[h] * al + psum;
+        halpha[h] = al;
+      }
+    }
+    __syncthreads();
+    // phase 3: thread (coordinate, tile half) accumulates its coordinate over 32 tokens
+    {
+#pragma unroll
+      for (int h = 0; h < MAXH; ++h)
+        if (h < u.hs) acc[h] *= halpha[h];
+      const int tile = c0 / kTile + half;
+      const int m = i_coord & 15, mu = i_coord >> 4;
+      const uint8_t* tbase = a.vc + (sb * ntile + tile) * (kTile * 16 * BV);
+      const float* nbase = a.vn + (sb * ntile + tile) * (NG * kTile) + (NG == 4 ? (i_coord >> 5) : 0) * kTile;
+      for (int t32 = 0; t32 < kTile; ++t32) {
+        const int tok = tile * kTile + t32;
+        if (tok < lo || tok >= hi) continue;
+        const int q = (t32 >> 2) & 3, kap = 4 * (t32 >> 4) + (t32 & 3);
+        const int bit = ((q * 16 + m) * 8 + mu) * (8 * BV) + BV * kap;
+        // a 3-bit field may straddle two bytes of its word; read the second only then, so
+        // the read never leaves the word
+        uint32_t two = tbase[bit >> 3];
+        if ((bit & 7) + BV > 8) two |= (uint32_t)tbase[(bit >> 3) + 1] << 8;
+        const uint32_t code = (two >> (bit & 7)) & ((1u << BV) - 1u);
+        const float f = cbv[code] * nbase[norm_pos(t32)];
+        const int pt = half * kTile + t32;
+#pragma unroll
+        for (int h = 0; h < MAXH; ++h)
+          if (h < u.hs) acc[h] = fmaf(pw[h][pt], f, acc[h]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h)
+    if (h < u.hs) oacc[half][h][i_coord] = acc[h];
+  __syncthreads();
+  for (int i = tid; i < u.hs * kHeadDim; i += 256) {
+    const int h = i >> 7, c = i & 127;
+    const float L = hsum[h];
+    qbuf[i] = L > 0.f ? (oacc[0][h][c] + oacc[1][h][c]) / L : 0.f;
+    if (c == 0) lse2[h] = L > 0.f ? hm[h] + __log2f(L) : -INFINITY;
+  }
+  __syncthreads();
+  write_result(a, u, qbuf, lse2);
+}
+
+// ---------------------------------------------------------------------------------------
+// Log-sum-exp merge of key-axis splits plus the single inverse rotation.
+__global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
+  __shared__ float obuf[kHeadDim];
+  __shared__ float wsum;
+  const int row = blockIdx.x;  // b * n_q_heads + h
+  const int h = row % a.n_q_heads;
+  const int kv = h / a.group_size;
+  const int c = threadIdx.x;
+  const size_t stride = (size_t)a.batch * a.n_q_heads;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_lse[s * stride + row]);
+  const float mu = M == -INFINITY ? 0.f : M;
+  float W = 0.f, acc = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float l = a.part_lse[s * stride + row];
+    const float w = l == -INFINITY ? 0.f : expf(l - mu);
+    W += w;
+    acc += w * a.part_o[(s * stride + row) * kHeadDim + c];
+  }
+  obuf[c] = W > 0.f ? acc / W : 0.f;
+  if (c == 0) wsum = W;
+  __syncthreads();
+  lds_rotate<false>(obuf, 1, a.signs + kv * kHeadDim, a.so4 ? a.so4 + kv * 256 : nullptr, a.rot_group);
+  a.out[(size_t)row * kHeadDim + c] = obuf[c];
+  if (a.lse_out && c == 0) a.lse_out[row] = wsum > 0.f ? mu + logf(wsum) : -INFINITY;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Launchers.
+
+hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, bool x_f16, int batch,
+                         int n_tiles, hipStream_t stream) {
+  const dim3 grid(n_tiles, a.n_kv_heads, batch), block(128);
+#define TQ_APPEND(B, G, V, X)                                                        \
+  if (bits == B && group == G && values == V && x_f16 == X) {                        \
+    hipLaunchKernelGGL((append_kernel<B, G, V, X>), grid, block, 0, stream, a);      \
+    return hipGetLastError();                                                        \
+  }
+#define TQ_APPEND_X(B, G, V) TQ_APPEND(B, G, V, true) TQ_APPEND(B, G, V, false)
+#define TQ_APPEND_V(B, G) TQ_APPEND_X(B, G, true) TQ_APPEND_X(B, G, false)
+  TQ_APPEND_V(3, 32) TQ_APPEND_V(3, 128) TQ_APPEND_V(4, 32) TQ_APPEND_V(4, 128)
+#undef TQ_APPEND_V
+#undef TQ_APPEND_X
+#undef TQ_APPEND
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool share_table,
+                         hipStream_t stream) {
+  const int units = a.batch * a.n_kv_heads * a.n_splits * a.n_slices;
+  const dim3 grid(units), block(256);
+  const int ng = kHeadDim / a.rot_group;
+  if (schedule == 2) {
+#define TQ_MF(BK, BV, NG, SH, QF)                                                           \
+  if (bits_k == BK && bits_v == BV && ng == NG && share_table == SH && q_f16 == QF) {       \
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, SH, QF>), grid, block, 0, stream, a); \
+    return hipGetLastError();                                                               \
+  }
+#define TQ_MF_Q(BK, BV, NG, SH) TQ_MF(BK, BV, NG, SH, true) TQ_MF(BK, BV, NG, SH, false)
+#define TQ_MF_NG(BK, BV, SH) TQ_MF_Q(BK, BV, 4, SH) TQ_MF_Q(BK, BV, 1, SH)
+    TQ_MF_NG(3, 3, true) TQ_MF_NG(4, 4, true) TQ_MF_NG(3, 3, false) TQ_MF_NG(4, 4, false)
+    TQ_MF_NG(4, 3, false) TQ_MF_NG(3, 4, false)
+#undef TQ_MF_NG
+#undef TQ_MF_Q
+#undef TQ_MF
+  } else {
+#define TQ_VEC(BK, BV, NG, QF)                                                               \
+  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF) {                             \
+    hipLaunchKernelGGL((decode_vec_kernel<BK, BV, NG, QF>), grid, block, 0, stream, a);      \
+    return hipGetLastError();                                                                \
+  }
+#define TQ_VEC_Q(BK, BV, NG) TQ_VEC(BK, BV, NG, true) TQ_VEC(BK, BV, NG, false)
+#define TQ_VEC_NG(BK, BV) TQ_VEC_Q(BK, BV, 4) TQ_VEC_Q(BK, BV, 1)
+    TQ_VEC_NG(3, 3) TQ_VEC_NG(4, 4) TQ_VEC_NG(4, 3) TQ_VEC_NG(3, 4)
+#undef TQ_VEC_NG
+#undef TQ_VEC_Q
+#undef TQ_VEC
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,168 @@
+/*
+ * tq.h -- decode attention computed directly on a rotated, Lloyd-Max-quantised,
+ * bit-packed KV cache (3- or 4-bit codes), for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer marked "device" is device memory owned by the caller; the library
+ * never allocates or frees memory, keeps no global state and launches everything on the
+ * HIP stream it is given (passed as void* = hipStream_t, NULL = default stream).  Calls
+ * return without synchronising.  Argument errors are detected on the host before any
+ * launch: the call then returns TQ_EINVAL / TQ_EUNSUPPORTED / TQ_ECAPACITY and writes
+ * nothing.  A failed launch returns TQ_EHIP.  No C++ exception crosses this boundary.
+ *
+ * The method (citations name the page and the section on it):
+ *   * a key or value vector is split into groups of g coordinates (g = 32, or g = 128 =
+ *     the whole head); each group stores its L2 norm, is divided by it and rotated
+ *     ("TurboQuant: ... MNN on phones", 2.1 and 3.1);
+ *   * the rotation is R = S_SO4 . H . D_s: per-coordinate +-1 sign flips, the normalised
+ *     Walsh-Hadamard transform on every g-block (3.1), and optionally (IsoQuant) the
+ *     SO(4) rotation v -> q_L v conj(q_R) of every 4-block ("RotaryQuant: Fitting 120B
+ *     MoE Models ... Fused Compressed-Space Attention", key design 2);
+ *   * every rotated coordinate is replaced by the index of its Lloyd-Max cell for the
+ *     law f(t) ~ (1 - t^2)^((g-3)/2) ("TurboQuant ...", 2.2 and 2.3), the index being the
+ *     number of cell boundaries strictly below the value (3.4);
+ *   * decode rotates the query once, forms scores and the value sum in the rotated
+ *     domain straight from the codes, and applies one inverse rotation to the output
+ *     ("RotaryQuant ...", key design 3; "TurboQuant ...", 3.3);
+ *   * long rows are split along the key axis and the partial results merged by
+ *     log-sum-exp ("RoPE-Aware Bit Allocation for KV-Cache Quantization", packed-cache
+ *     implementation details).
+ *
+ * Fixed sizes: head dimension 128; cache capacity a multiple of the 32-token tile.
+ *
+ * Packed layout (the pages fix only the unit: 8 three-bit codes in 3 bytes, or two
+ * four-bit codes per byte, "TurboQuant ...", 3.3).  A word of 8 codes of b bits is the
+ * integer sum_j code_j << (b*j) stored little-endian in b bytes (3 or 4).
+ *   keys:   codes [batch][n_kv_heads][capacity][16*b] bytes: per token 16 words, word w =
+ *           coordinates 8w..8w+7 of that token.
+ *   values: codes [batch][n_kv_heads][capacity/32][32*16*b] bytes: per 32-token tile 512
+ *           words, word (q*16 + m)*8 + u = coordinate 16u + m of tile tokens
+ *           16h + 4q + r (h = 0..1, r = 0..3) in slot 4h + r.
+ *   norms (both): fp32 [batch][n_kv_heads][capacity/32][128/g][32]; tile token t is at
+ *           position 8*((t >> 2) & 3) + 4*(t >> 4) + (t & 3).
+ * Keys keep a token's coordinates together because scores contract over coordinates;
+ * values keep 8 tokens of one coordinate together because the value sum contracts over
+ * tokens.  Each is then one matrix-core operand row per word.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_HEAD_DIM 128
+#define TQ_TILE 32
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* null pointer, bad size or inconsistent arguments */
+  TQ_EUNSUPPORTED = 2,  /* valid but not implemented (bits, group, head grouping) */
+  TQ_ECAPACITY = 3,     /* a write or read would pass the cache capacity */
+  TQ_EHIP = 4           /* a HIP launch or runtime call failed */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
+typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
+
+/* Decode schedules.  MFMA: scores and value sum as matrix-core products of fp16
+ * operands with fp32 accumulation (key codebook and query split into two fp16 parts so
+ * scores keep fp32-level accuracy).  VEC: plain fp32 vector arithmetic, token-parallel
+ * scores and dimension-parallel value sum.  AUTO picks MFMA whenever it applies. */
+typedef enum { TQ_SCHEDULE_AUTO = 0, TQ_SCHEDULE_VEC = 1, TQ_SCHEDULE_MFMA = 2 } tq_schedule;
+
+/* Static description of an error code (never NULL). */
+const char* tq_status_string(tq_status s);
+
+/* Lloyd-Max codebook for one coordinate of a uniformly rotated unit vector in R^dim.
+ * ("TurboQuant ...", 2.2: density f(t) ~ (1 - t^2)^((dim-3)/2) on [-1, 1];
+ *  2.3: centroid = conditional mean of its cell, boundary = midpoint, iterate.)
+ * Computed on the host in double precision (Gauss-Legendre quadrature of the cell
+ * masses, closed-form first moments) and stored rounded to float.
+ * centroid[0 .. 2^bits-1] ascending; boundary[k] = (centroid[k] + centroid[k+1]) / 2 for
+ * k < 2^bits - 1; unused entries are 0.  Host-only; no device work.
+ * Errors: TQ_EINVAL if out == NULL; TQ_EUNSUPPORTED unless bits is 3 or 4 and dim >= 3. */
+typedef struct {
+  int32_t bits;
+  int32_t dim;
+  float centroid[16];
+  float boundary[15];
+} tq_codebook;
+
+tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* out);
+
+/* Rotation shared by the keys, the values and the queries of one KV head. */
+typedef struct {
+  int32_t group;        /* g: Hadamard block = norm group = codebook dim; 32 or 128 */
+  int32_t n_kv_heads;
+  const float* signs;   /* device [n_kv_heads][128], each +1.0f or -1.0f, applied first */
+  const float* so4;     /* device [n_kv_heads][32][2][4] unit quaternions (q_L, q_R) as
+                           (real, i, j, k) for the 4-blocks, applied after the Hadamard;
+                           NULL = no SO(4) stage */
+} tq_rotation;
+
+/* One packed tensor (keys or values) of a batch of sequences.  Caller-owned memory. */
+typedef struct {
+  void* codes;          /* device, layout above for `role` */
+  float* norms;         /* device, layout above */
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t capacity;     /* tokens per (sequence, head); multiple of 32 */
+  int32_t bits;         /* 3 or 4 */
+  int32_t group;        /* must equal the rotation's group */
+  tq_role role;
+  tq_codebook codebook; /* tq_make_codebook(bits, group) */
+} tq_cache;
+
+/* Quantise n_new new vectors per (sequence, KV head) into the cache: per group, norm ->
+ * divide -> rotate -> codebook search -> pack ("TurboQuant ...", 2.1 and 3.3: quantise
+ * on write, no intermediate fp16 copy).  One call handles a decode step (n_new = 1) or
+ * a whole prompt (n_new = T; "RoPE-Aware Bit Allocation ...": one call per layer).
+ *   x:     device [batch][n_kv_heads][n_new][128] of x_dtype, read only.
+ *   pos:   device int32 [batch], first slot written per sequence, or NULL to use pos0
+ *          for every sequence.  max_pos: host upper bound on pos[] used for the
+ *          capacity check (ignored when pos == NULL).
+ * Slots [pos, pos + n_new) of every (sequence, head) are written; neighbouring value
+ * slots that share a packed word are preserved.  A zero group stores norm 0 and the
+ * code of 0.  Errors: TQ_ECAPACITY if max(pos) + n_new > capacity. */
+tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x,
+                             tq_dtype x_dtype, int32_t n_new, const int32_t* pos, int32_t pos0,
+                             int32_t max_pos, void* stream);
+
+/* One decode step of attention for every query head against the packed cache.
+ *   q:        device [batch][n_q_heads][128] of q_dtype; query head h reads KV head
+ *             h / (n_q_heads / n_kv_heads) (contiguous groups).
+ *   seq_lens: device int32 [batch] (each <= max_len) or NULL = every row has max_len
+ *             tokens; max_len <= capacity.
+ *   scale:    softmax scale applied to q.k (1/sqrt(128) in the usual convention).
+ *   n_splits: key-axis sections; section s of a length-T row covers tokens
+ *             [s*C, min(T, (s+1)*C)), C = ceil(T / n_splits).
+ * n_splits == 1: writes out [batch][n_q_heads][128] fp32 (original domain) and, if not
+ *             NULL, lse_out [batch][n_q_heads] (natural log of the softmax denominator).
+ * n_splits > 1: writes part_o [n_splits][batch][n_q_heads][128] (rotated domain,
+ *             normalised per section) and part_lse [n_splits][batch][n_q_heads]; an empty
+ *             section has lse = -inf and a zero partial.  Finish with tq_merge_splits.
+ * A row with no tokens gives out = 0 and lse = -inf.
+ * The MFMA schedule converts the scaled query and p * value-norm to fp16; it assumes
+ * those stay inside the fp16 range (|value group norm| < 65504). */
+tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                              const void* q, tq_dtype q_dtype, int32_t n_q_heads,
+                              const int32_t* seq_lens, int32_t max_len, float scale,
+                              int32_t n_splits, tq_schedule schedule, float* out, float* lse_out,
+                              float* part_o, float* part_lse, void* stream);
+
+/* Log-sum-exp merge of key-axis sections followed by the single inverse rotation:
+ * lse = ln sum_s e^{lse_s}; out = R^T sum_s e^{lse_s - lse} part_o_s
+ * ("RoPE-Aware Bit Allocation ...", packed-cache details; "RotaryQuant ...", key design 3).
+ * part_o/part_lse as written by tq_decode_attention; out [batch][n_q_heads][128];
+ * lse_out [batch][n_q_heads] or NULL.  n_q_heads must be a multiple of rot->n_kv_heads. */
+tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,
+                          const float* part_o, const float* part_lse, float* out, float* lse_out,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

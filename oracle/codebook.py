@@ -61,6 +61,10 @@ def _lloyd_max_cached(bits, dim):
             break
     else:  # pragma: no cover - convergence is fast for every supported (bits, dim)
         raise RuntimeError("Lloyd-Max iteration did not converge")
+    # The law is even in t (2.2), so the fixed point is odd-symmetric; fold away the
+    # last-bit asymmetry of the quadrature so that the middle boundary is exactly 0 (it
+    # decides the code of an exact zero coordinate).
+    c = 0.5 * (c - c[::-1])
     m = 0.5 * (c[:-1] + c[1:])
     return c, m
 

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/tq.h
+declares, its host-side codebook matches the oracle's, and argument errors are caught on
+the host (status codes, nothing launched).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_domain_attention_amd as tq
+from oracle import codebook as ocb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ECAPACITY = 0, 1, 2, 3
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tq.LIB_PATH):
+        pytest.fail("libtq.so is not built (run compressed_domain_attention_amd/build.py)")
+    return tq.library()
+
+
+def test_exports_every_declared_function(lib):
+    decl = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(tq_\w+)\s*\(", open(HEADER).read(), re.M))
+    assert decl == set(tq.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("bits,dim", [(3, 32), (4, 32), (3, 128), (4, 128)])
+def test_host_codebook_matches_oracle(lib, bits, dim):
+    cb = tq.make_codebook(bits, dim)
+    c, m = ocb.lloyd_max(bits, dim)
+    got_c = np.array(cb.centroids, dtype=np.float32)
+    got_m = np.array(cb.boundaries, dtype=np.float32)
+    # both round an fp64 fixed point to fp32: at most one fp32 ulp apart
+    for got, ref in ((got_c, c), (got_m, m)):
+        ref32 = ref.astype(np.float32)
+        assert np.all(np.abs(got - ref32) <= np.spacing(np.maximum(np.abs(got), np.abs(ref32))))
+    assert got_m[len(got_m) // 2] == 0.0 and m[len(m) // 2] == 0.0
+    assert cb.bits == bits and cb.dim == dim
+    assert all(cb.centroid[k] == 0.0 for k in range(1 << bits, 16))
+
+
+def test_codebook_errors(lib):
+    cb = tq.Codebook()
+    assert lib.tq_make_codebook(2, 32, ctypes.byref(cb)) == TQ_EUNSUPPORTED
+    assert lib.tq_make_codebook(3, 2, ctypes.byref(cb)) == TQ_EUNSUPPORTED
+    assert lib.tq_make_codebook(3, 32, None) == TQ_EINVAL
+    for s in range(5):
+        assert lib.tq_status_string(s)
+    assert lib.tq_status_string(99) == b"unknown status"
+
+
+def make_rot(group=32, heads=2, so4=False):
+    return tq._Rotation(group, heads, FAKE, FAKE if so4 else None)
+
+
+def make_cache(role, bits=3, group=32, heads=2, batch=1, capacity=64):
+    cb = tq.Codebook()
+    assert tq.library().tq_make_codebook(bits, group, ctypes.byref(cb)) == 0
+    return tq._Cache(FAKE, FAKE, batch, heads, capacity, bits, group, role, cb)
+
+
+def append(rot, cache, n_new=4, pos=None, pos0=0, max_pos=0, x=FAKE, dtype=1):
+    return tq.library().tq_quantize_append(ctypes.byref(rot), ctypes.byref(cache), x, dtype, n_new, pos, pos0,
+                                           max_pos, None)
+
+
+def test_append_validation(lib):
+    rot = make_rot()
+    k = make_cache(tq.TQ_KEYS)
+    assert append(rot, k, n_new=0) == TQ_OK                      # nothing to do, nothing launched
+    assert append(rot, k, n_new=65) == TQ_ECAPACITY
+    assert append(rot, k, n_new=4, pos0=61) == TQ_ECAPACITY
+    assert append(rot, k, n_new=4, pos=FAKE, max_pos=61) == TQ_ECAPACITY
+    assert append(rot, k, x=None) == TQ_EINVAL
+    assert append(rot, k, dtype=7) == TQ_EINVAL
+    assert append(rot, k, n_new=-1) == TQ_EINVAL
+    assert append(make_rot(group=64), k) == TQ_EUNSUPPORTED
+    assert append(make_rot(heads=3), k) == TQ_EINVAL               # head count mismatch
+    assert append(make_rot(group=128), k) == TQ_EINVAL             # group mismatch
+    bad = make_cache(tq.TQ_KEYS, capacity=48)
+    assert append(rot, bad) == TQ_EINVAL                           # capacity not a tile multiple
+    bad = make_cache(tq.TQ_KEYS)
+    bad.codebook.dim = 128
+    assert append(rot, bad) == TQ_EINVAL                           # codebook for another group
+    bad = make_cache(tq.TQ_KEYS)
+    bad.bits = 2
+    assert append(rot, bad) == TQ_EUNSUPPORTED
+    nulls = make_rot()
+    nulls.signs = None
+    assert append(nulls, k) == TQ_EINVAL
+
+
+def decode(rot, k, v, n_q_heads=4, max_len=10, n_splits=1, out=FAKE, part=FAKE, sched=0, scale=0.1):
+    return tq.library().tq_decode_attention(ctypes.byref(rot), ctypes.byref(k), ctypes.byref(v), FAKE, 1, n_q_heads,
+                                            None, max_len, scale, n_splits, sched, out, None, part, part, None)
+
+
+def test_decode_validation(lib):
+    rot = make_rot()
+    k, v = make_cache(tq.TQ_KEYS), make_cache(tq.TQ_VALUES)
+    assert decode(rot, k, k) == TQ_EINVAL                          # value cache with the key role
+    assert decode(rot, k, v, n_q_heads=3) == TQ_EINVAL             # not a multiple of the KV heads
+    assert decode(rot, k, v, max_len=65) == TQ_ECAPACITY
+    assert decode(rot, k, v, n_splits=0) == TQ_EINVAL
+    assert decode(rot, k, v, out=None) == TQ_EINVAL
+    assert decode(rot, k, v, n_splits=4, part=None) == TQ_EINVAL
+    assert decode(rot, k, v, sched=9) == TQ_EINVAL
+    assert decode(rot, k, v, scale=float("nan")) == TQ_EINVAL
+    assert decode(rot, k, make_cache(tq.TQ_VALUES, batch=2)) == TQ_EINVAL
+    assert decode(rot, k, make_cache(tq.TQ_VALUES, capacity=128)) == TQ_EINVAL
+
+
+def test_merge_validation(lib):
+    rot = make_rot()
+    m = lib.tq_merge_splits
+    assert m(ctypes.byref(rot), 0, 1, 4, FAKE, FAKE, FAKE, None, None) == TQ_EINVAL
+    assert m(ctypes.byref(rot), 2, 1, 3, FAKE, FAKE, FAKE, None, None) == TQ_EINVAL
+    assert m(ctypes.byref(rot), 2, 1, 4, None, FAKE, FAKE, None, None) == TQ_EINVAL
+    assert m(ctypes.byref(rot), 2, 1, 4, FAKE, FAKE, None, None, None) == TQ_EINVAL
+
+
+def test_product_path_has_no_cpu_fallback():
+    # the binding must not reach the oracle or any CPU computation
+    src = open(os.path.join(ROOT, "compressed_domain_attention_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("NativeLibraryMissing", "")

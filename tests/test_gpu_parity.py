@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Sizes are small enough for the oracle yet span several 32-token tiles and a ragged tail;
+every workload family is covered (fp32 tiny, 4B-style GQA, TQ4 keys / TQ3 values, G=8
+with log-normal channel scales, IsoQuant whole-head rotation with SO(4) blocks).
+Decode parity feeds the same oracle-packed cache to both sides.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_domain_attention_amd as tq
+import workloads
+from helpers import (OUT_RTOL, check_codes, dequantized, oracle_decode, oracle_quantize, pack, round_up,
+                     row_rel_err, unpack)
+from oracle import attention, rotation
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": dict(seq_len=256, batch=1),
+    "gqa8k": dict(seq_len=300, batch=1),
+    "batched": dict(seq_len=100, batch=2),
+    "long128k": dict(seq_len=200, batch=1),
+    "isoquant32k": dict(seq_len=96, batch=2),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.library()  # raises if the native library is missing
+
+
+def setup(name, seed=0, **over):
+    kw = dict(CASES[name])
+    kw.update(over)
+    w = workloads.WORKLOADS[name].with_len(kw["seq_len"], batch=kw["batch"])
+    inp = workloads.generate(w, seed)
+    print("case", name, "seed", seed, "shape", (w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len), flush=True)
+    return w, inp
+
+
+def device_rotation(w, inp):
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).cuda()
+    return tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, so4)
+
+
+def empty_caches(w, cap):
+    k = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS)
+    v = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES)
+    return k, v
+
+
+def oracle_caches(w, inp, cap):
+    """Oracle quantisation packed into the library layout, as device caches."""
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    kc, kn = pack(oqk, cap, "k")
+    vc, vn = pack(oqv, cap, "v")
+    k = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS,
+                       codes=torch.from_numpy(kc).cuda(), norms=torch.from_numpy(kn).cuda())
+    v = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES,
+                       codes=torch.from_numpy(vc).cuda(), norms=torch.from_numpy(vn).cuda())
+    return k, v, oqk, oqv
+
+
+def download(cache, role):
+    idx, n = unpack(cache.codes.cpu().numpy(), cache.norms.cpu().numpy(), cache.bits, role)
+    return idx, n
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_append_matches_oracle(name):
+    w, inp = setup(name)
+    t = w.seq_len
+    cap = round_up(t, 32) + 32
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, cap)
+    tq.quantize_append(rot, k, torch.from_numpy(inp["k"]).cuda())
+    tq.quantize_append(rot, v, torch.from_numpy(inp["v"]).cuda())
+    torch.cuda.synchronize()
+    total_flips = 0
+    for role, cache in (("k", k), ("v", v)):
+        oq = oracle_quantize(w, inp, role)
+        idx, n = download(cache, role)
+        total_flips += check_codes(idx, n, oq, t)
+        assert not idx[:, :, t:].any() and not n[:, :, t:].any(), "slots past the appended range were written"
+    print("near-boundary flips", total_flips, flush=True)
+
+
+def test_append_incremental_and_device_positions():
+    # prefill part of each row, then single-token steps, then a chunk at per-row device
+    # positions: partial 32-token tiles are read-modify-written and must keep neighbours
+    w, inp = setup("batched", seq_len=90, batch=2)
+    t = w.seq_len
+    cap = 128
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, cap)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    p1 = 37
+    for cache, x in ((k, kx), (v, vx)):
+        tq.quantize_append(rot, cache, x[:, :, :p1].contiguous(), pos0=0)
+        for s in range(p1, 45):
+            tq.quantize_append(rot, cache, x[:, :, s:s + 1].contiguous(), pos0=s)
+        pos = torch.tensor([45, 45], dtype=torch.int32, device="cuda")
+        tq.quantize_append(rot, cache, x[:, :, 45:t].contiguous(), pos=pos)
+    torch.cuda.synchronize()
+    for role, cache in (("k", k), ("v", v)):
+        idx, n = download(cache, role)
+        check_codes(idx, n, oracle_quantize(w, inp, role), t)
+        assert not idx[:, :, t:].any()
+
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("n_splits", [1, 3])
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_matches_oracle(name, n_splits, schedule):
+    w, inp = setup(name, seed=1)
+    t = w.seq_len
+    cap = round_up(t, 32)
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, cap)
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens = np.full(w.batch, t)
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    ref_out, ref_lse = oracle_decode(w, inp, kd, vd, lens)
+    if n_splits == 1:
+        out, lse = tq.decode_attention(rot, k, v, q, n_splits=1, schedule=schedule, max_len=t)
+    else:
+        po, pl = tq.decode_attention(rot, k, v, q, n_splits=n_splits, schedule=schedule, max_len=t)
+        ref_po, ref_pl = oracle_decode(w, inp, kd, vd, lens, n_splits)
+        err_p = row_rel_err(po.cpu().numpy(), ref_po)
+        assert err_p.max() <= OUT_RTOL, "partial err %g" % err_p.max()
+        np.testing.assert_allclose(pl.cpu().numpy(), ref_pl, rtol=1e-4, atol=1e-4)
+        out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    err = row_rel_err(out.cpu().numpy(), ref_out)
+    print("max row rel err %.3e (schedule %s, splits %d)" % (err.max(), schedule, n_splits), flush=True)
+    assert err.max() <= OUT_RTOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("n_splits", [1, 5, 40])
+def test_decode_ragged_lengths_and_empty_rows(n_splits, schedule):
+    w, inp = setup("gqa8k", seed=2, seq_len=300, batch=5)
+    cap = 320
+    lens = np.array([0, 1, 33, 300, 64], dtype=np.int32)
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, cap)
+    q = torch.from_numpy(inp["q"]).cuda()
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    ref_out, ref_lse = attention.decode(inp["q"].astype(np.float64), kd, vd, lens, w.scale)
+    seq = torch.from_numpy(lens).cuda()
+    if n_splits == 1:
+        out, lse = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=300, schedule=schedule)
+    else:
+        po, pl = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=300, n_splits=n_splits, schedule=schedule)
+        out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert not out[0].any() and np.all(np.isneginf(lse[0]))
+    err = row_rel_err(out[1:], ref_out[1:])
+    assert err.max() <= OUT_RTOL
+    np.testing.assert_allclose(lse[1:], ref_lse[1:], rtol=1e-4, atol=1e-4)
+
+
+def test_schedules_agree_and_are_deterministic():
+    w, inp = setup("gqa8k", seed=3, seq_len=300, batch=1)
+    rot = device_rotation(w, inp)
+    k, v, _, _ = oracle_caches(w, inp, 320)
+    q = torch.from_numpy(inp["q"]).cuda()
+    a1, _ = tq.decode_attention(rot, k, v, q, max_len=300, schedule="mfma")
+    a2, _ = tq.decode_attention(rot, k, v, q, max_len=300, schedule="mfma")
+    b1, _ = tq.decode_attention(rot, k, v, q, max_len=300, schedule="vec")
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+    assert row_rel_err(a1.cpu().numpy(), b1.cpu().numpy()).max() <= OUT_RTOL
+
+
+def test_merge_matches_oracle():
+    w, inp = setup("isoquant32k", seed=4, seq_len=32, batch=2)
+    rng = np.random.default_rng(5)
+    s, bsz, hq = 6, w.batch, w.n_q_heads
+    po = rng.standard_normal((s, bsz, hq, 128)).astype(np.float32)
+    pl = (rng.standard_normal((s, bsz, hq)) * 5).astype(np.float32)
+    pl[2] = -np.inf                       # an empty split everywhere
+    pl[:, 1, 3] = -np.inf                 # a row with no tokens at all
+    rot = device_rotation(w, inp)
+    out, lse = tq.merge_splits(rot, torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    m_out, m_lse = attention.merge(po, pl)
+    ref = np.empty_like(m_out)
+    for h in range(hq):
+        kv = h // w.group_size
+        ref[:, h] = rotation.unrotate(m_out[:, h], inp["signs"][kv], w.group, inp["so4"][kv])
+    err = row_rel_err(out.cpu().numpy(), ref)
+    assert err.max() <= 1e-5
+    np.testing.assert_allclose(lse.cpu().numpy(), m_lse, rtol=1e-6, atol=1e-6)
+    assert not out.cpu().numpy()[1, 3].any()
+
+
+@pytest.mark.parametrize("name", ["gqa8k", "isoquant32k"])
+def test_end_to_end_append_then_decode(name):
+    w, inp = setup(name, seed=6)
+    t = w.seq_len
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, round_up(t, 32))
+    tq.quantize_append(rot, k, torch.from_numpy(inp["k"]).cuda())
+    tq.quantize_append(rot, v, torch.from_numpy(inp["v"]).cuda())
+    out, _ = tq.decode_attention(rot, k, v, torch.from_numpy(inp["q"]).cuda(), max_len=t)
+    torch.cuda.synchronize()
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    ref, _ = oracle_decode(w, inp, dequantized(w, inp, oqk), dequantized(w, inp, oqv), np.full(w.batch, t))
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
