@@ -1,0 +1,367 @@
+"""Benchmark: decode attention on a packed 3/4-bit KV cache, one MI355X.
+
+One step = one pass of the whole hot path over one batch: quantise-append the newest
+token's key and value into slot T-1 of every (sequence, KV head), decode attention over T
+tokens straight from the codes (rotated query, online softmax, rotated-domain value sum),
+and merge the key-axis splits with the single inverse rotation.  Inputs are seeded and
+synthetic (workloads.py) and resident in HBM before timing.  The packed caches are
+replicated to more than 1 GiB and cycled so that the 256 MB last-level cache cannot hold
+them; the number is HBM-bound, not cache-bound.
+
+Prints one JSON line.  Value = KV token*heads per second for the whole step.  The
+roofline object is for the decode kernel: algorithmic bytes (codes + norms of every
+(token, KV head)) per launch over its average launch time, measured with events on the
+launch stream.  cpu_baseline times the fp64 oracle (dequantise + plain attention) on a
+bounded sample of the same workload on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "decode attn KV token·heads/s + achieved HBM GB/s vs peak (TQ3, T=32K)"
+HEADLINE = "isoquant32k"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", "tq_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_per_token_head(w):
+    """Packed bytes of one (token, KV head): key + value codes and fp32 group norms."""
+    ng = 128 // w.group
+    return (16 * w.bits_k + 4 * ng) + (16 * w.bits_v + 4 * ng)
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, n_splits):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    ent = rec.get("workloads", {}).get("%s/S%d" % (workload, n_splits))
+    return None if ent is None else ent["hbm_bytes_per_launch"]
+
+
+def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
+    import torch
+
+    import compressed_domain_attention_amd as tq
+
+    dev = torch.device("cuda:0")
+    T = w.seq_len
+    cap = (T + 31) // 32 * 32
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).to(dev)
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).to(dev), w.group, so4)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    kx = torch.from_numpy(inp["k"]).to(dev)
+    vx = torch.from_numpy(inp["v"]).to(dev)
+    newk = kx[:, :, T - 1:T].contiguous()
+    newv = vx[:, :, T - 1:T].contiguous()
+
+    # prefill: the whole prompt quantised in one call per tensor (after one small call that
+    # loads the kernels, so the timing excludes code-object loading)
+    k0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev)
+    v0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev)
+    tq.quantize_append(rot, k0, newk, pos0=0)
+    tq.quantize_append(rot, v0, newv, pos0=0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tq.quantize_append(rot, k0, kx[:, :, :T - 1].contiguous() if T > 1 else kx)
+    tq.quantize_append(rot, v0, vx[:, :, :T - 1].contiguous() if T > 1 else vx)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    in_bytes = 2 * (T - 1) * w.batch * w.n_kv_heads * 128 * kx.element_size()
+    out_bytes = 2 * (T - 1) * w.batch * w.n_kv_heads * bytes_per_token_head(w) // 2
+    del kx, vx
+
+    cache_bytes = sum(t.numel() * t.element_size() for t in (k0.codes, k0.norms, v0.codes, v0.norms))
+    # replicas totalling >= 1 GiB defeat the 256 MB last-level cache (capped for tiny caches,
+    # which then stay cache-resident: their number is a latency figure, not a bandwidth one)
+    reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
+    caches = [(k0, v0)]
+    for _ in range(reps - 1):
+        k = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev,
+                           codes=k0.codes.clone(), norms=k0.norms.clone())
+        v = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev,
+                           codes=v0.codes.clone(), norms=v0.norms.clone())
+        caches.append((k, v))
+    log("cache %.1f MB x %d replicas" % (cache_bytes / 1e6, reps))
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    po = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+
+    def decode(i):
+        k, v = caches[i % reps]
+        if n_splits == 1:
+            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=1, schedule=schedule, out=out, lse=lse)
+        else:
+            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=n_splits, schedule=schedule, part_o=po,
+                                part_lse=pl)
+
+    def step(i):
+        k, v = caches[i % reps]
+        tq.quantize_append(rot, k, newk, pos0=T - 1)
+        tq.quantize_append(rot, v, newv, pos0=T - 1)
+        decode(i)
+        if n_splits > 1:
+            tq.merge_splits(rot, po, pl, out=out, lse=lse)
+
+    # eager warm-up, and the reference output that every graph replay must reproduce
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+
+    # HIP graphs: one per cache replica holding exactly one step (no host work per kernel
+    # in the timed loop), and one holding a run of decode launches for the kernel timing
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for r in range(reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    n_dec = max(reps, 16)
+    gdec = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gdec):
+        for i in range(n_dec):
+            decode(i)
+    torch.cuda.synchronize()
+
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager_out):
+        raise SystemExit("graph replay does not reproduce the eager step")
+    for i in range(warmup):
+        graphs[i % reps].replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % reps].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    if not torch.equal(out, eager_out):
+        raise SystemExit("graph replays drifted from the eager step")
+
+    # decode kernel alone: back-to-back launches in one graph, events on the launch stream
+    gdec.replay()
+    torch.cuda.synchronize()
+    reps_dec = max(3, 200 // n_dec)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(reps_dec):
+        gdec.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / (reps_dec * n_dec)
+
+    parity = None
+    if check:
+        parity = sampled_parity(w, inp, out.cpu().numpy())
+    return dict(ms_per_step=total_ms / steps, decode_ms=dec_ms, prefill_ms=prefill_ms, prefill_bytes=in_bytes + out_bytes,
+                reps=reps, cache_bytes=cache_bytes, parity=parity, decode_launches=reps_dec * n_dec)
+
+
+def sampled_parity(w, inp, out):
+    """Oracle check of a few (sequence, query head) rows of the measured output."""
+    from helpers import OUT_RTOL, row_rel_err
+    from oracle import attention, codebook, quant
+
+    t0 = time.perf_counter()
+    worst = 0.0
+    units = [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]
+    ck, mk = codebook.lloyd_max(w.bits_k, w.group)
+    cv, mv = codebook.lloyd_max(w.bits_v, w.group)
+    for b, kv in units:
+        so = None if inp["so4"] is None else inp["so4"][kv]
+        sg = inp["signs"][kv]
+        ki, kn, _ = quant.quantize(inp["k"][b, kv].astype(np.float64), sg, w.group, ck, mk, so)
+        vi, vn, _ = quant.quantize(inp["v"][b, kv].astype(np.float64), sg, w.group, cv, mv, so)
+        kd = quant.dequantize(ki, kn, sg, w.group, ck, so)
+        vd = quant.dequantize(vi, vn, sg, w.group, cv, so)
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            worst = max(worst, float(row_rel_err(out[b, h], ref)))
+    log("sampled parity: worst row rel err %.3e over %d heads (%.1fs)" % (
+        worst, len(units) * w.group_size, time.perf_counter() - t0))
+    if worst > OUT_RTOL:
+        raise SystemExit("parity check failed: %.3e > %.1e" % (worst, OUT_RTOL))
+    return worst
+
+
+def _oracle_unit(args):
+    w, b, kv, seed = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import attention, codebook, quant
+    inp = _oracle_unit.inp
+    ck, mk = codebook.lloyd_max(w.bits_k, w.group)
+    cv, mv = codebook.lloyd_max(w.bits_v, w.group)
+    so = None if inp["so4"] is None else inp["so4"][kv]
+    sg = inp["signs"][kv]
+    ki, kn, _ = quant.quantize(inp["k"][b, kv].astype(np.float64), sg, w.group, ck, mk, so)
+    vi, vn, _ = quant.quantize(inp["v"][b, kv].astype(np.float64), sg, w.group, cv, mv, so)
+    t0 = time.perf_counter()
+    kd = quant.dequantize(ki, kn, sg, w.group, ck, so)
+    vd = quant.dequantize(vi, vn, sg, w.group, cv, so)
+    for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+        attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The oracle decode (dequantise every K/V vector of a stream, plain fp64 softmax
+    attention for its query heads) on whole (sequence, KV head) streams of the same
+    workload, one stream per worker process, until about budget_s of work is done."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    _oracle_unit.inp = inp
+    units = [(w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
+    done, busy, t0 = 0, 0.0, time.perf_counter()
+    with threadpool_limits(1):
+        ctx = mp.get_context("fork")
+        with ctx.Pool(cores) as pool:
+            while done < len(units) and time.perf_counter() - t0 < budget_s:
+                batch = units[done:done + cores]
+                busy += sum(pool.map(_oracle_unit, batch))
+                done += len(batch)
+    wall = time.perf_counter() - t0
+    token_heads = done * w.seq_len
+    return {"value": token_heads / wall, "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) streams of %s (T=%d), fp64 dequantise + attention, "
+                      "%d worker processes x 1 thread, %.1fs wall" % (done, len(units), w.name, w.seq_len, cores, wall)}
+
+
+def stream_read_probe_gbs():
+    """Achievable read bandwidth: the probe kernel streaming 2 GiB (16-byte loads)."""
+    import ctypes
+
+    import torch
+
+    from compressed_domain_attention_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.tq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = x.numel() * 4
+    best = 0.0
+    for blocks in (2048, 4096, 8192):
+        for _ in range(2):
+            assert lib.tq_probe_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), blocks, stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            lib.tq_probe_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 5 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del x
+    return best
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "mfma", "vec"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.WORKLOADS[args.workload]
+    n_splits = args.splits if args.splits is not None else w.n_splits
+    log("workload %s: %s, splits %d, schedule %s" % (w.name, w, n_splits, args.schedule))
+    t_gen = time.perf_counter()
+    inp = workloads.generate(w, 0)
+    log("generated inputs in %.1fs" % (time.perf_counter() - t_gen))
+    cpu = None
+    if not args.no_cpu_baseline:
+        # runs before anything initialises the GPU in this process (the pool forks)
+        cpu = cpu_baseline(w, inp)
+        log("cpu baseline: %.3g token*heads/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    r = run_gpu(w, inp, args.steps, args.warmup, n_splits, args.schedule, check=not args.no_check)
+    units = w.batch * w.n_kv_heads * w.seq_len
+    value = units / (r["ms_per_step"] / 1e3)
+    algo_bytes = units * bytes_per_token_head(w)
+    achieved = algo_bytes / (r["decode_ms"] / 1e3) / 1e9
+    probe = stream_read_probe_gbs()
+    log("step %.3f ms, decode kernel %.3f ms -> %.0f GB/s (%.1f%% of 8 TB/s, %.1f%% of the %.0f GB/s stream-read "
+        "probe); prefill %.3f ms for %.2f GB (%.0f GB/s)" % (
+            r["ms_per_step"], r["decode_ms"], achieved, 100 * achieved / HBM_PEAK_GBS, 100 * achieved / probe, probe,
+            r["prefill_ms"], r["prefill_bytes"] / 1e9, r["prefill_bytes"] / 1e6 / r["prefill_ms"]))
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV token·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA operands, f32 accumulate (3/4-bit codes)",
+        "data": "synthetic (seeded Gaussian activations with outlier channels; workloads.py)",
+        "config": {"workload": w.name, "timing": "HIP graph replay, one graph per step", "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "seq_len": w.seq_len, "bits_k": w.bits_k, "bits_v": w.bits_v, "group": w.group,
+                   "so4": w.so4, "n_splits": n_splits, "schedule": args.schedule,
+                   "step": "append 1 token K+V, decode, merge", "cache_replicas": r["reps"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, n_splits)},
+        "cpu_baseline": cpu,
+        "decode_kernel_ms": r["decode_ms"],
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "stream_read_probe_GBps": probe,
+        "parity_worst_row_rel_err": r["parity"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,6 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq_codebook.cpp", "tq_api.cpp", "tq_kernels.hip"]
+PROBE_LIB = os.path.join(HERE, "libtqprobe.so")   # bandwidth probe used by the benchmark
+PROBE_SOURCES = ["tq_probe.hip"]
 
 
 def hipcc():
@@ -15,8 +17,14 @@ def hipcc():
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib, verbose):
+    srcs = [os.path.join(HERE, "csrc", s) for s in sources]
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-Wall",
            # packed fp32 VALU ops are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,8 +38,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

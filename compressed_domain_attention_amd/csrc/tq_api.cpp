@@ -84,8 +84,6 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
   if (schedule != TQ_SCHEDULE_AUTO && schedule != TQ_SCHEDULE_VEC && schedule != TQ_SCHEDULE_MFMA) return TQ_EINVAL;
 
   const int group_size = n_q_heads / rot->n_kv_heads;
-  const bool share = keys->bits == values->bits &&
-                     std::memcmp(keys->codebook.centroid, values->codebook.centroid, sizeof(float) * 16) == 0;
   // every supported (bits, group) pair has a matrix-core kernel, so AUTO takes it
   const int sched = schedule == TQ_SCHEDULE_VEC ? 1 : 2;
 
@@ -120,8 +118,7 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
     a.kcent[k] = keys->codebook.centroid[k];
     a.vcent[k] = values->codebook.centroid[k];
   }
-  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, share && sched == 2,
-                                    (hipStream_t)stream));
+  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,

@@ -71,11 +71,11 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
                          int n_tiles, hipStream_t stream);
 // schedule: 1 = vector (fp32), 2 = matrix cores
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
-                         bool share_table, hipStream_t stream);
+                         hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
-// Heads one workgroup of the matrix-core schedule can serve (the 16 MFMA columns hold
-// (norm group, head) pairs).
-inline int mfma_heads_per_slice(int rot_group) { return rot_group == 32 ? 4 : 16; }
+// Heads one workgroup of the matrix-core schedule can serve: the 16 MFMA columns hold
+// (norm group, head) pairs for 32-groups and (query part, head) pairs for whole-head groups.
+inline int mfma_heads_per_slice(int rot_group) { return rot_group == 32 ? 4 : 8; }
 
 }  // namespace tq

@@ -357,14 +357,20 @@ __device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, 
 // ---------------------------------------------------------------------------------------
 // Matrix-core decode.
 //
-// Scores: for a 16-token tile, D[token][col] = sum_k A[token][k] B[k][col] with A = key
-// codebook values (fp16 hi and lo parts, decoded through an LDS table) and B = the rotated
-// query (fp16 hi and lo parts), col = (norm group, head) so that D holds per-group partial
-// dots; D is scaled by the group norms and summed across the group lanes.  Three products
-// per operand pair (hi.hi + hi.lo + lo.hi) keep the score at fp32-level accuracy.
+// Scores: for a 16-token tile, D[token][col] = sum_k A[token][k] B[k][col].  A holds key
+// codebook values decoded through LDS tables, B the rotated query, col = (norm group,
+// head) so that D holds per-group partial dots, which are scaled by the group norms and
+// summed across the group lanes.  The key codebook and the query are each split into an
+// fp16 high and low part; one A operand carries 4 codes as [hi x4 | lo x4] and is
+// multiplied by [q_hi x4 | q_hi x4] and by [q_lo x4 | 0 x4], which together give
+// (c_hi + c_lo) q_hi + c_hi q_lo: the score keeps fp32-level accuracy.
 // Values: O[coord][col] += sum_k A[coord][k] P'[k][col] over the 32 tokens of a tile, with
-// A = value codebook values (value words hold 8 tokens of one coordinate) and P' = p * norm
-// in fp16, read straight from the score registers.  Online softmax per column.
+// A = value codebook values (a value word holds 8 tokens of one coordinate) and P' = p *
+// value norm in fp16, taken straight from the score registers.  Online softmax per column.
+//
+// Decode tables: an index of two codes (6 bits for 3-bit codes, 8 for 4-bit) selects a
+// 4-byte entry holding the two fp16 values.  A 64-entry table is 256 bytes, one entry per
+// LDS bank, so lookups by any mix of lanes never conflict.
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
                                                 0, 0);
@@ -375,69 +381,149 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Byte offset (index * 4) of the two-code field of W = 2*BITS bits at bit `off` of d[].
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_addr(const uint32_t* d, int off) {
+  constexpr int W = 2 * BITS;
+  const int wi = off >> 5, sh = off & 31;
+  uint32_t x;
+  if (sh + W <= 32) {
+    x = sh >= 2 ? (d[wi] >> (sh - 2)) : (d[wi] << (2 - sh));
+  } else {
+    x = __builtin_amdgcn_alignbit(d[wi + 1], d[wi], sh - 2);
+  }
+  return x & (((1u << W) - 1u) << 2);
+}
+
+__device__ __forceinline__ uint32_t lds_word(const uint32_t* tab, uint32_t byte_off) {
+  return *(const uint32_t*)((const char*)tab + byte_off);
+}
+
 template <int BK, int BV>
 struct Block {
-  uint32_t k0[BK], k1[BK];  // this lane's 32 key coordinates of tile tokens (lane&15) and 16+(lane&15)
+  uint32_t k0[BK], k1[BK];  // this lane's 32 key codes of tile tokens (lane&15) and 16+(lane&15)
   f32x4 kn0, kn1;           // key norms of tokens 4q'+r and 16+4q'+r
   uint32_t v[2 * BV];       // this lane's 8 value words
   f32x4 vn0, vn1;           // value norms, same tokens as kn
 };
 
-template <int BK, int BV, int NG, bool SHARE, bool QF16>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+// Lazy softmax rescale: the running maximum is only moved when a block raises it by more
+// than 2^3, so p = 2^(s - m) stays below 8 and p * norm inside the fp16 range for value
+// group norms below 8188.
+constexpr float kRescaleLog2 = 3.0f;
+
+// Maximum / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <typename T>
+__device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
+  return *(const T*)(base + off);
+}
+
+template <int BK, int BV, int NG, bool QF16>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NW = 4;
-  constexpr int HPS = NG == 4 ? 4 : 16;
-  constexpr int KTAB = BK == 3 ? 4096 * 16 : 256 * 8;   // entry: 4 (3-bit) or 2 (4-bit) codes, hi then lo
-  constexpr int VTAB = SHARE ? 0 : (BV == 3 ? 4096 * 8 : 256 * 4);
-  constexpr int VSTRIDE = SHARE ? (BV == 3 ? 16 : 8) : (BV == 3 ? 8 : 4);
-  constexpr int SCR = NW * HPS * (kHeadDim + 2) * 4;
-  constexpr int BIG = (KTAB + VTAB) > SCR ? (KTAB + VTAB) : SCR;
+  // whole-head groups: the query's hi and lo parts take separate columns (8 + 8), so one
+  // product per key operand suffices; 32-groups: columns are (group, head), two products
+  constexpr bool SPLITQ = NG == 1;
+  constexpr int HPS = NG == 4 ? 4 : 8;
+  // blocks in flight ahead of the arithmetic (register budget: whole-head groups need half
+  // the query operands, which leaves room for a deeper ring)
+  constexpr int PREFETCH = 1;
+  constexpr int NEK = BK == 3 ? 64 : 256;   // table entries: all pairs of codes
+  constexpr int NEV = BV == 3 ? 64 : 256;
   constexpr int KREC = 16 * BK;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[BIG];
+  constexpr int VTILE = kTile * 16 * BV;
+  __shared__ uint32_t tab[2 * NEK + NEV];   // key hi, key lo, value hi
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
+  __shared__ float scr[NW * HPS * (kHeadDim + 2)];
   __shared__ uint32_t cbk[16], cbv[16];
   __shared__ float red[NW];
+  __shared__ float lse2[HPS];
+  const uint32_t* khi = tab;
+  const uint32_t* klo = tab + NEK;
+  const uint32_t* vhi = tab + 2 * NEK;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Unit u = decode_unit(a, true);
-  const uint8_t* ktab = smem;
-  const uint8_t* vtab = SHARE ? smem : smem + KTAB;
+  const int col = lane & 15, qg = lane >> 4;
+  const int cgrp = NG == 4 ? (col >> 2) : 0;
+  const int chl = NG == 4 ? (col & 3) : (col & 7);
+  const bool colok = chl < u.hs && (NG == 4 || col < 8);
 
-  // fp16 codebooks: keys as (hi, lo), values as hi
+  // ---- token range and the first two blocks' loads, issued before the prologue
+  int lo, hi;
+  token_range(a, u, lo, hi);
+  const int blk0 = lo / kTile, blk1 = (hi + kTile - 1) / kTile;
+  const size_t sb = (size_t)u.b * a.n_kv_heads + u.kv;
+  const int ntile = a.capacity / kTile;
+  const uint8_t* kbase = a.kc + sb * a.capacity * KREC;
+  const uint8_t* knbase = (const uint8_t*)(a.kn + sb * ntile * (NG * kTile));
+  const uint8_t* vbase = a.vc + sb * ntile * VTILE;
+  const uint8_t* vnbase = (const uint8_t*)(a.vn + sb * ntile * (NG * kTile));
+  const uint32_t koff = (lane & 15) * KREC + qg * (4 * BK);
+  const uint32_t noff = (cgrp * kTile + 8 * qg) * 4;
+  const uint32_t voff = lane * (8 * BV);
+
+  auto load_block = [&](Block<BK, BV>& d, int blk) {
+    const uint8_t* kb = kbase + (size_t)blk * kTile * KREC;
+    if (BK == 3) {
+      const uint3 x0 = load_at<uint3>(kb, koff), x1 = load_at<uint3>(kb, koff + 16 * KREC);
+      d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z;
+      d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z;
+    } else {
+      const uint4 x0 = load_at<uint4>(kb, koff), x1 = load_at<uint4>(kb, koff + 16 * KREC);
+      d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z; d.k0[BK - 1] = x0.w;
+      d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z; d.k1[BK - 1] = x1.w;
+    }
+    const uint8_t* nb = knbase + (size_t)blk * (NG * kTile * 4);
+    d.kn0 = load_at<f32x4>(nb, noff);
+    d.kn1 = load_at<f32x4>(nb, noff + 16);
+    const uint8_t* vb = vbase + (size_t)blk * VTILE;
+    if (BV == 3) {
+      const uint3 y0 = load_at<uint3>(vb, voff), y1 = load_at<uint3>(vb, voff + 12);
+      d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y1.x; d.v[4] = y1.y; d.v[5] = y1.z;
+    } else {
+      const uint4 y0 = load_at<uint4>(vb, voff), y1 = load_at<uint4>(vb, voff + 16);
+      d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y0.w;
+      d.v[4] = y1.x; d.v[5] = y1.y; d.v[2 * BV - 2] = y1.z; d.v[2 * BV - 1] = y1.w;
+    }
+    const uint8_t* vnb = vnbase + (size_t)blk * (NG * kTile * 4);
+    d.vn0 = load_at<f32x4>(vnb, noff);
+    d.vn1 = load_at<f32x4>(vnb, noff + 16);
+  };
+
+  Block<BK, BV> r0, r1, r2;
+  int blk = blk0 + wv;
+  if (blk < blk1) {
+    load_block(r0, blk);
+    if (PREFETCH == 2) load_block(r1, min(blk + NW, blk1 - 1 - ((blk1 - 1 - blk) % NW)));
+  }
+
+  // ---- decode tables
   if (tid < 16) {
     const float c = a.kcent[tid];
-    const _Float16 hi = (_Float16)c;
-    const _Float16 lo = (_Float16)(c - (float)hi);
-    cbk[tid] = f16_bits(hi) | (f16_bits(lo) << 16);
+    const _Float16 h = (_Float16)c;
+    cbk[tid] = f16_bits(h) | (f16_bits((_Float16)(c - (float)h)) << 16);
     cbv[tid] = f16_bits((_Float16)a.vcent[tid]);
   }
   __syncthreads();
-  if (BK == 3) {
-    for (int e = tid; e < 4096; e += 256) {
-      const uint32_t c0 = cbk[e & 7], c1 = cbk[(e >> 3) & 7], c2 = cbk[(e >> 6) & 7], c3 = cbk[(e >> 9) & 7];
-      const u32x4 ent = {(c0 & 0xFFFFu) | (c1 << 16), (c2 & 0xFFFFu) | (c3 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u),
-                         (c2 >> 16) | (c3 & 0xFFFF0000u)};
-      *(u32x4*)(smem + e * 16) = ent;
-    }
-  } else {
-    for (int e = tid; e < 256; e += 256) {
-      const uint32_t c0 = cbk[e & 15], c1 = cbk[e >> 4];
-      const u32x2 ent = {(c0 & 0xFFFFu) | (c1 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u)};
-      *(u32x2*)(smem + e * 8) = ent;
-    }
+  for (int e = tid; e < NEK; e += 256) {
+    const uint32_t c0 = cbk[e & ((1 << BK) - 1)], c1 = cbk[e >> BK];
+    tab[e] = (c0 & 0xFFFFu) | (c1 << 16);
+    tab[NEK + e] = (c0 >> 16) | (c1 & 0xFFFF0000u);
   }
-  if (!SHARE) {
-    if (BV == 3) {
-      for (int e = tid; e < 4096; e += 256) {
-        const u32x2 ent = {cbv[e & 7] | (cbv[(e >> 3) & 7] << 16), cbv[(e >> 6) & 7] | (cbv[(e >> 9) & 7] << 16)};
-        *(u32x2*)(smem + KTAB + e * 8) = ent;
-      }
-    } else {
-      for (int e = tid; e < 256; e += 256) *(uint32_t*)(smem + KTAB + e * 4) = cbv[e & 15] | (cbv[e >> 4] << 16);
-    }
-  }
+  for (int e = tid; e < NEV; e += 256) tab[2 * NEK + e] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
 
-  // rotated, scaled query (log2 units), split into fp16 hi + lo with a power-of-two prescale
+  // ---- rotated, scaled query (log2 units) with a power-of-two prescale into fp16 range
   load_queries<QF16>(a, u, qbuf);
   lds_rotate<true>(qbuf, u.hs, a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.rot_group);
   float mx = 0.f;
@@ -455,54 +541,41 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   if (mx > 0.f && mx < INFINITY) (void)frexpf(mx, &ex);
   const float qs = ldexpf(1.f, 14 - ex), qinv = ldexpf(1.f, ex - 14);
 
-  const int col = lane & 15, qg = lane >> 4;
-  const int cgrp = NG == 4 ? (col >> 2) : 0;
-  const int chl = NG == 4 ? (col & 3) : col;
-  const bool colok = chl < u.hs;
-  u32x4 Bh[4], Bl[4];
+  // B operands.  Key operand f of lane group q holds codes of coordinates 32q + 4f + j
+  // (j = 0..3) in fp16 slots [hi j0, hi j1, lo j0, lo j1, hi j2, hi j3, lo j2, lo j3].
+  // "hi" columns see q_hi in every slot ((c_hi + c_lo) q_hi), "lo" columns see q_lo in the
+  // c_hi slots only (c_hi q_lo).
+  u32x4 B1[8], B2[8];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int f = 0; f < 8; ++f) {
+    uint32_t hp[2], lp[2];
+    const int head = NG == 4 ? chl : (col & 7);
+    const bool live = head < u.hs && (NG == 1 || cgrp == qg);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < 2; ++p) {
       float x0 = 0.f, x1 = 0.f;
-      if (colok && (NG == 1 || cgrp == qg)) {
-        const float* src = qbuf + chl * kHeadDim + 32 * qg + 8 * w + 2 * p;
+      if (live) {
+        const float* src = qbuf + head * kHeadDim + 32 * qg + 4 * f + 2 * p;
         x0 = src[0] * qs;
         x1 = src[1] * qs;
       }
       const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-      Bh[w][p] = f16_bits(h0) | (f16_bits(h1) << 16);
-      Bl[w][p] = f16_bits(l0) | (f16_bits(l1) << 16);
+      hp[p] = f16_bits(h0) | (f16_bits(h1) << 16);
+      lp[p] = f16_bits((_Float16)(x0 - (float)h0)) | (f16_bits((_Float16)(x1 - (float)h1)) << 16);
+    }
+    const u32x4 bh = u32x4{hp[0], hp[0], hp[1], hp[1]};
+    const u32x4 bl = u32x4{lp[0], 0u, lp[1], 0u};
+    if (SPLITQ) {
+      B1[f] = col < 8 ? bh : bl;
+    } else {
+      B1[f] = bh;
+      B2[f] = bl;
     }
   }
 
-  int lo, hi;
-  token_range(a, u, lo, hi);
-  const int blk0 = lo / kTile, blk1 = (hi + kTile - 1) / kTile;
-  const size_t sb = (size_t)u.b * a.n_kv_heads + u.kv;
-  const int ntile = a.capacity / kTile;
-  const uint8_t* kbase = a.kc + sb * a.capacity * KREC + (lane & 15) * KREC + qg * (4 * BK);
-  const float* knbase = a.kn + sb * ntile * (NG * kTile) + cgrp * kTile + 8 * qg;
-  const uint8_t* vbase = a.vc + sb * ntile * (kTile * 16 * BV) + lane * (8 * BV);
-  const float* vnbase = a.vn + sb * ntile * (NG * kTile) + cgrp * kTile + 8 * qg;
-
-  auto load_block = [&](Block<BK, BV>& d, int blk) {
-    const uint32_t* kp = (const uint32_t*)(kbase + (size_t)blk * kTile * KREC);
-#pragma unroll
-    for (int j = 0; j < BK; ++j) d.k0[j] = kp[j];
-    kp = (const uint32_t*)(kbase + ((size_t)blk * kTile + 16) * KREC);
-#pragma unroll
-    for (int j = 0; j < BK; ++j) d.k1[j] = kp[j];
-    const f32x4* knp = (const f32x4*)(knbase + (size_t)blk * (NG * kTile));
-    d.kn0 = knp[0];
-    d.kn1 = knp[1];
-    const uint32_t* vp = (const uint32_t*)(vbase + (size_t)blk * (kTile * 16 * BV));
-#pragma unroll
-    for (int j = 0; j < 2 * BV; ++j) d.v[j] = vp[j];
-    const f32x4* vnp = (const f32x4*)(vnbase + (size_t)blk * (NG * kTile));
-    d.vn0 = vnp[0];
-    d.vn1 = vnp[1];
+  auto key_operand = [&](const uint32_t* kk, int f) {
+    const uint32_t a0 = pair_addr<BK>(kk, 4 * BK * f), a1 = pair_addr<BK>(kk, 4 * BK * f + 2 * BK);
+    return u32x4{lds_word(khi, a0), lds_word(klo, a0), lds_word(khi, a1), lds_word(klo, a1)};
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -511,126 +584,139 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   for (int i = 0; i < 8; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();  // tables complete
 
-  int blk = blk0 + wv;
-  Block<BK, BV> cur;
-  if (blk < blk1) load_block(cur, blk);
-  for (; blk < blk1; blk += NW) {
-    Block<BK, BV> nxt;
-    load_block(nxt, min(blk + NW, blk1 - 1));  // prefetch; the last one re-reads a valid block
-
-    // ---- scores of tokens 16h + 4q' + r
-    f32x4 D[2];
+  auto process = [&](const Block<BK, BV>& cb, int blk) {
+    // Table reads are issued in batches ahead of their consumers so that LDS latency
+    // overlaps matrix-core and vector work: all key operands of tile 0, then tile 1's
+    // while tile 0 multiplies, then every value operand before the softmax arithmetic.
+    u32x4 ka[8], kb[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t* kk = h ? cur.k1 : cur.k0;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < 8; ++f) ka[f] = key_operand(cb.k0, f);
+    f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4 ah, al;
-        if (BK == 3) {
-          const u32x4 e0 = *(const u32x4*)(ktab + (field<12>(kk, 24 * w) << 4));
-          const u32x4 e1 = *(const u32x4*)(ktab + (field<12>(kk, 24 * w + 12) << 4));
-          ah = u32x4{e0.x, e0.y, e1.x, e1.y};
-          al = u32x4{e0.z, e0.w, e1.z, e1.w};
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x2 e = *(const u32x2*)(ktab + (((kk[w] >> (8 * j)) & 0xFFu) << 3));
-            ah[j] = e.x;
-            al[j] = e.y;
-          }
-        }
-        acc = mfma16(ah, Bh[w], acc);
-        acc = mfma16(ah, Bl[w], acc);
-        acc = mfma16(al, Bh[w], acc);
-      }
-      D[h] = acc;
+    for (int f = 0; f < 8; ++f) {
+      kb[f] = key_operand(cb.k1, f);
+      D0 = mfma16(ka[f], B1[f], D0);
+      if (!SPLITQ) D0 = mfma16(ka[f], B2[f], D0);
     }
-    float sc[8];
-    const int tb = blk * kTile + 4 * qg;
+    u32x4 va[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      D1 = mfma16(kb[f], B1[f], D1);
+      if (!SPLITQ) D1 = mfma16(kb[f], B2[f], D1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) va[f][j] = lds_word(vhi, pair_addr<BV>(cb.v, 8 * BV * f + 2 * BV * j));
+    }
+    // raw scores (units of the prescaled query) of tokens 16h + 4q' + r, slot k = 4h + r
+    float x[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int h = k >> 2, r = k & 3;
-      float x = D[h][r] * (h ? cur.kn1[r] : cur.kn0[r]);
+      float d = k < 4 ? D0[k] : D1[k - 4];
+      const float n = k < 4 ? cb.kn0[k] : cb.kn1[k - 4];
       if (NG == 4) {
-        x += dpp<0x124>(x);  // row_ror:4
-        x += dpp<0x128>(x);  // row_ror:8
+        d *= n;
+        d += dpp<0x124>(d);  // row_ror:4
+        d += dpp<0x128>(d);  // row_ror:8
+      } else {
+        d = (d + dpp<0x128>(d)) * n;  // hi + lo columns
       }
-      x *= qinv;
-      const int t = tb + 16 * h + r;
-      sc[k] = (t >= lo && t < hi) ? x : -INFINITY;
+      x[k] = d;
     }
-
-    // ---- online softmax (log2 domain) for this lane's column
-    float bm = sc[0];
+    const int t0 = blk * kTile;
+    const bool edge = t0 < lo || t0 + kTile > hi;  // wave-uniform
+    if (edge) {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, sc[k]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mnew = fmaxf(m_run, bm);
-    if (__any(mnew > m_run)) {
-      const float al = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+      for (int k = 0; k < 8; ++k) {
+        const int t = t0 + 16 * (k >> 2) + 4 * qg + (k & 3);
+        if (t < lo || t >= hi) x[k] = -INFINITY;
+      }
+    }
+    const float bm =
+        rows_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+    const bool grow = m_run == -INFINITY ? bm > -INFINITY : (bm - m_run) * qinv > kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? bm : m_run;
+      const float al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * qinv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) O[i] *= al;
       l_run *= al;
+      m_run = mnew;
     }
-    m_run = mnew;
-    const float mu = m_run == -INFINITY ? 0.f : m_run;
+    const float nmq = m_run == -INFINITY ? 0.f : -m_run * qinv;
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = __builtin_amdgcn_exp2f(fmaf(x[k], qinv, nmq));
+      l_run += p[k];
+    }
+    float pv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pv[k] = p[k] * (k < 4 ? cb.vn0[k] : cb.vn1[k - 4]);
+    if (edge) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (p[k] == 0.f) pv[k] = 0.f;  // masked slots may hold undefined norms
+    }
     u32x4 bp;
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
-      float pv[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = 2 * pr + e;
-        const float p = __builtin_amdgcn_exp2f(sc[k] - mu);
-        l_run += p;
-        const float nv = k < 4 ? cur.vn0[k] : cur.vn1[k - 4];
-        pv[e] = sc[k] == -INFINITY ? 0.f : p * nv;
-      }
-      bp[pr] = f16_bits((_Float16)pv[0]) | (f16_bits((_Float16)pv[1]) << 16);
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+      const h2_t hv = {(_Float16)pv[2 * pr], (_Float16)pv[2 * pr + 1]};
+      bp[pr] = __builtin_bit_cast(uint32_t, hv);
     }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) O[w] = mfma16(va[w], bp, O[w]);
+  };
 
-    // ---- value sum in the rotated domain
-#pragma unroll
-    for (int mu8 = 0; mu8 < 8; ++mu8) {
-      u32x4 av;
-      if (BV == 3) {
-        const u32x2 e0 = *(const u32x2*)(vtab + field<12>(cur.v, 24 * mu8) * VSTRIDE);
-        const u32x2 e1 = *(const u32x2*)(vtab + field<12>(cur.v, 24 * mu8 + 12) * VSTRIDE);
-        av = u32x4{e0.x, e0.y, e1.x, e1.y};
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) av[j] = *(const uint32_t*)(vtab + ((cur.v[mu8] >> (8 * j)) & 0xFFu) * VSTRIDE);
-      }
-      O[mu8] = mfma16(av, bp, O[mu8]);
+  // register ring: the next PREFETCH blocks' loads are in flight while this one computes.
+  // The prefetch is unconditional (past the end it re-reads this wave's last block, which is
+  // still in L2) so that the wait counts are static and never wait on younger loads.
+  const int last = blk1 - 1 - ((blk1 - 1 - (blk0 + wv)) % NW + NW) % NW;  // this wave's last block
+  if (PREFETCH == 1) {
+    while (blk < blk1) {
+      load_block(r1, min(blk + NW, last));
+      process(r0, blk);
+      blk += NW;
+      if (blk >= blk1) break;
+      load_block(r0, min(blk + NW, last));
+      process(r1, blk);
+      blk += NW;
     }
-    cur = nxt;
+  } else {
+    while (blk < blk1) {
+      load_block(r2, min(blk + 2 * NW, last));
+      process(r0, blk);
+      blk += NW;
+      if (blk >= blk1) break;
+      load_block(r0, min(blk + 2 * NW, last));
+      process(r1, blk);
+      blk += NW;
+      if (blk >= blk1) break;
+      load_block(r1, min(blk + 2 * NW, last));
+      process(r2, blk);
+      blk += NW;
+    }
   }
 
-  // ---- combine the waves of the workgroup
-  float lt = l_run;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-  __syncthreads();  // tables no longer read
-  float* so = (float*)smem;             // [NW][HPS][128]
+  // ---- combine the waves of the workgroup (scores in prescaled units -> log2 units)
+  const float lt = rows_sum(l_run);
+  const float m2 = m_run == -INFINITY ? -INFINITY : m_run * qinv;
+  float* so = scr;                       // [NW][HPS][128]
   float* sm = so + NW * HPS * kHeadDim;  // [NW][HPS]
   float* sl = sm + NW * HPS;
   if (colok) {
 #pragma unroll
-    for (int mu8 = 0; mu8 < 8; ++mu8) {
-      if (NG == 1 || (mu8 >> 1) == cgrp) {
+    for (int w = 0; w < 8; ++w) {
+      if (NG == 1 || (w >> 1) == cgrp) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) so[(wv * HPS + chl) * kHeadDim + 16 * mu8 + 4 * qg + r] = O[mu8][r];
+        for (int r = 0; r < 4; ++r) so[(wv * HPS + chl) * kHeadDim + 16 * w + 4 * qg + r] = O[w][r];
       }
     }
     if (qg == 0 && cgrp == 0) {
-      sm[wv * HPS + chl] = m_run;
+      sm[wv * HPS + chl] = m2;
       sl[wv * HPS + chl] = lt;
     }
   }
   __syncthreads();
-  __shared__ float lse2[HPS];
   for (int i = tid; i < u.hs * kHeadDim; i += 256) {
     const int hl = i >> 7, c = i & 127;
     float M = -INFINITY;
@@ -790,31 +876,62 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Log-sum-exp merge of key-axis splits plus the single inverse rotation.
+// Log-sum-exp merge of key-axis splits plus the single inverse rotation.  One workgroup
+// per (sequence, query head): the split weights are formed once in LDS, then every thread
+// (coordinate) sums its column over the splits with independent, unrolled loads.
 __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
+  constexpr int kMaxStage = 1024;
   __shared__ float obuf[kHeadDim];
-  __shared__ float wsum;
+  __shared__ float wts[kMaxStage];
+  __shared__ float red[2][2];
   const int row = blockIdx.x;  // b * n_q_heads + h
   const int h = row % a.n_q_heads;
   const int kv = h / a.group_size;
-  const int c = threadIdx.x;
+  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   const size_t stride = (size_t)a.batch * a.n_q_heads;
+  // pass 1: maximum lse
   float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_lse[s * stride + row]);
+  for (int s = c; s < a.n_splits; s += 128) M = fmaxf(M, a.part_lse[s * stride + row]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[0][wv] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
   const float mu = M == -INFINITY ? 0.f : M;
-  float W = 0.f, acc = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
+  // pass 2: weights e^{lse_s - max} (kept in LDS when they fit) and their sum
+  float W = 0.f;
+  for (int s = c; s < a.n_splits; s += 128) {
     const float l = a.part_lse[s * stride + row];
     const float w = l == -INFINITY ? 0.f : expf(l - mu);
+    if (s < kMaxStage) wts[s] = w;
     W += w;
-    acc += w * a.part_o[(s * stride + row) * kHeadDim + c];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) W += __shfl_xor(W, o);
+  if (lane == 0) red[1][wv] = W;
+  __syncthreads();
+  W = red[1][0] + red[1][1];
+  // pass 3: weighted sum of the partials
+  float acc = 0.f;
+  const float* po = a.part_o + (size_t)row * kHeadDim + c;
+  int s = 0;
+  for (; s + 8 <= a.n_splits && s + 8 <= kMaxStage; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = po[(s + j) * stride * kHeadDim];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + j], v[j], acc);
+  }
+  for (; s < a.n_splits; ++s) {
+    const float l = a.part_lse[s * stride + row];
+    const float w = s < kMaxStage ? wts[s] : (l == -INFINITY ? 0.f : expf(l - mu));
+    acc = fmaf(w, po[s * stride * kHeadDim], acc);
   }
   obuf[c] = W > 0.f ? acc / W : 0.f;
-  if (c == 0) wsum = W;
   __syncthreads();
   lds_rotate<false>(obuf, 1, a.signs + kv * kHeadDim, a.so4 ? a.so4 + kv * 256 : nullptr, a.rot_group);
   a.out[(size_t)row * kHeadDim + c] = obuf[c];
-  if (a.lse_out && c == 0) a.lse_out[row] = wsum > 0.f ? mu + logf(wsum) : -INFINITY;
+  if (a.lse_out && c == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;
 }
 
 }  // namespace
@@ -839,21 +956,20 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool share_table,
+hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
                          hipStream_t stream) {
   const int units = a.batch * a.n_kv_heads * a.n_splits * a.n_slices;
   const dim3 grid(units), block(256);
   const int ng = kHeadDim / a.rot_group;
   if (schedule == 2) {
-#define TQ_MF(BK, BV, NG, SH, QF)                                                           \
-  if (bits_k == BK && bits_v == BV && ng == NG && share_table == SH && q_f16 == QF) {       \
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, SH, QF>), grid, block, 0, stream, a); \
+#define TQ_MF(BK, BV, NG, QF)                                                               \
+  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF) {                             \
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF>), grid, block, 0, stream, a);     \
     return hipGetLastError();                                                               \
   }
-#define TQ_MF_Q(BK, BV, NG, SH) TQ_MF(BK, BV, NG, SH, true) TQ_MF(BK, BV, NG, SH, false)
-#define TQ_MF_NG(BK, BV, SH) TQ_MF_Q(BK, BV, 4, SH) TQ_MF_Q(BK, BV, 1, SH)
-    TQ_MF_NG(3, 3, true) TQ_MF_NG(4, 4, true) TQ_MF_NG(3, 3, false) TQ_MF_NG(4, 4, false)
-    TQ_MF_NG(4, 3, false) TQ_MF_NG(3, 4, false)
+#define TQ_MF_Q(BK, BV, NG) TQ_MF(BK, BV, NG, true) TQ_MF(BK, BV, NG, false)
+#define TQ_MF_NG(BK, BV) TQ_MF_Q(BK, BV, 4) TQ_MF_Q(BK, BV, 1)
+    TQ_MF_NG(3, 3) TQ_MF_NG(4, 4) TQ_MF_NG(4, 3) TQ_MF_NG(3, 4)
 #undef TQ_MF_NG
 #undef TQ_MF_Q
 #undef TQ_MF

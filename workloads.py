@@ -10,6 +10,7 @@ contexts with the IsoQuant rotation ("RotaryQuant ...", key findings).  No datas
 read; Gaussian activations with outlier channels stand in for real model activations.
 """
 
+import os
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -52,6 +53,24 @@ WORKLOADS = {
 }
 
 
+def _stream_normals(seed_seq, bsz, hkv, t, fill):
+    """Draw K or V as one independent N(0, 1) stream per (sequence, KV head), on threads.
+
+    fill(b, kv, x) receives the float32 [t, 128] draw of that stream and stores it.  Each
+    stream has its own spawned seed, so the result does not depend on the thread count.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    seeds = seed_seq.spawn(bsz * hkv)
+
+    def one(i):
+        b, kv = divmod(i, hkv)
+        fill(b, kv, np.random.default_rng(seeds[i]).standard_normal((t, HEAD_DIM), dtype=np.float32))
+
+    with ThreadPoolExecutor(max_workers=max(1, min(16, len(seeds), os.cpu_count() or 1))) as ex:
+        list(ex.map(one, range(len(seeds))))
+
+
 def generate(w: Workload, seed: int = 0, with_kv: bool = True):
     """Draw one workload's inputs.
 
@@ -59,54 +78,62 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
       q [B, Hq, 128], k [B, Hkv, T, 128], v [B, Hkv, T, 128] in ``w.dtype``;
       signs [Hkv, 128] float32 (+-1); so4 [Hkv, 32, 2, 4] float32 unit (q_L, q_R) or None;
       seq_lens [B] int32 (all equal to T).
-    Separate random streams feed each array, so changing one size leaves the others'
-    draws for a given seed unchanged where shapes allow.
+    Every array has its own random stream (K and V one per (sequence, KV head)).
     """
     ss = np.random.SeedSequence(seed)
-    r_q, r_k, r_v, r_sign, r_so4, r_ch, r_sk, r_sv = [np.random.default_rng(s) for s in ss.spawn(8)]
+    s_q, s_k, s_v, s_sign, s_so4, s_ch, s_sk, s_sv = ss.spawn(8)
     bsz, hq, hkv, t = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len
     g = w.group_size
+    dt = np.float16 if w.dtype == "float16" else np.float32
 
-    q = r_q.standard_normal((bsz, hq, HEAD_DIM), dtype=np.float32)
-    k = r_k.standard_normal((bsz, hkv, t, HEAD_DIM), dtype=np.float32) if with_kv else None
-    v = r_v.standard_normal((bsz, hkv, t, HEAD_DIM), dtype=np.float32) if with_kv else None
-
+    # per-(KV head, channel) multipliers shared by K and that head's queries, and for V
+    mul_k = np.ones((hkv, HEAD_DIM), np.float32)
+    mul_v = np.ones((hkv, HEAD_DIM), np.float32)
     if w.outliers == "fixed2x10":
         # channels 3 and 77 scaled by 10 in q, K and V
-        for arr in (q, k, v):
-            if arr is not None:
-                arr[..., [3, 77]] *= 10.0
+        mul_k[:, [3, 77]] = 10.0
+        mul_v[:, [3, 77]] = 10.0
     elif w.outliers == "seeded4x8":
         # 4 seeded channels per KV head scaled by 8 in K, V and that head's queries
+        r_ch = np.random.default_rng(s_ch)
         for kv in range(hkv):
             ch = r_ch.choice(HEAD_DIM, size=4, replace=False)
-            q[:, kv * g:(kv + 1) * g][..., ch] *= 8.0
-            if with_kv:
-                k[:, kv][..., ch] *= 8.0
-                v[:, kv][..., ch] *= 8.0
+            mul_k[kv, ch] = 8.0
+            mul_v[kv, ch] = 8.0
     elif w.outliers == "lognormal":
         # per-(KV head, channel) scale e^z, z ~ N(0, 1): one draw shared by K and its
         # queries, an independent draw for V
-        sk = np.exp(r_sk.standard_normal((hkv, HEAD_DIM))).astype(np.float32)
-        sv = np.exp(r_sv.standard_normal((hkv, HEAD_DIM))).astype(np.float32)
-        for kv in range(hkv):
-            q[:, kv * g:(kv + 1) * g] *= sk[kv]
-            if with_kv:
-                k[:, kv] *= sk[kv]
-                v[:, kv] *= sv[kv]
+        mul_k = np.exp(np.random.default_rng(s_sk).standard_normal((hkv, HEAD_DIM))).astype(np.float32)
+        mul_v = np.exp(np.random.default_rng(s_sv).standard_normal((hkv, HEAD_DIM))).astype(np.float32)
     else:
         raise ValueError(w.outliers)
 
-    dt = np.float16 if w.dtype == "float16" else np.float32
+    q = np.random.default_rng(s_q).standard_normal((bsz, hq, HEAD_DIM), dtype=np.float32)
+    q *= np.repeat(mul_k, g, axis=0)[None]
+    k = v = None
+    if with_kv:
+        k = np.empty((bsz, hkv, t, HEAD_DIM), dt)
+        v = np.empty((bsz, hkv, t, HEAD_DIM), dt)
+
+        def fill_k(b, kv, x):
+            k[b, kv] = x * mul_k[kv]
+
+        def fill_v(b, kv, x):
+            v[b, kv] = x * mul_v[kv]
+
+        _stream_normals(s_k, bsz, hkv, t, fill_k)
+        _stream_normals(s_v, bsz, hkv, t, fill_v)
+
+    r_sign = np.random.default_rng(s_sign)
     signs = np.where(r_sign.random((hkv, HEAD_DIM)) < 0.5, -1.0, 1.0).astype(np.float32)
     so4 = None
     if w.so4:
-        quat = r_so4.standard_normal((hkv, HEAD_DIM // 4, 2, 4))
+        quat = np.random.default_rng(s_so4).standard_normal((hkv, HEAD_DIM // 4, 2, 4))
         so4 = (quat / np.linalg.norm(quat, axis=-1, keepdims=True)).astype(np.float32)
     return {
         "q": q.astype(dt),
-        "k": None if k is None else k.astype(dt),
-        "v": None if v is None else v.astype(dt),
+        "k": k,
+        "v": v,
         "signs": signs,
         "so4": so4,
         "seq_lens": np.full(bsz, t, dtype=np.int32),
