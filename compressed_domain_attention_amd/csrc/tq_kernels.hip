@@ -91,6 +91,62 @@ __device__ void lds_rotate(float* buf, int nh, const float* signs, const float* 
   }
 }
 
+// Forward rotation of up to eight query heads in registers: wave w, lane l holds head
+// 2w + (l >> 5), coordinates 4(l & 31) .. +3 (one SO(4) block).  The first two Hadamard
+// stages are in-lane, the rest exchange with lane l ^ m inside the 32-lane half.  The
+// global reads are issued by query_fetch, early, so that their latency overlaps the
+// decode-table setup; query_rotate does the arithmetic.
+struct QueryLane {
+  float4 x, sg;
+  Quat l, r;
+  bool live;
+};
+
+template <bool QF16>
+__device__ __forceinline__ QueryLane query_fetch(const float* signs, const float* so4, const void* q,
+                                                 size_t row0, int hs, int wv, int lane) {
+  QueryLane s;
+  const int hl = 2 * wv + (lane >> 5), p = lane & 31;
+  s.live = hl < hs;
+  s.x = make_float4(0.f, 0.f, 0.f, 0.f);
+  s.sg = s.x;
+  s.l = s.r = Quat{1.f, 0.f, 0.f, 0.f};
+  if (s.live) {
+    const size_t qi = (row0 + hl) * kHeadDim + 4 * p;
+    if (QF16) {
+      typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+      const h4_t h = *(const h4_t*)((const _Float16*)q + qi);
+      s.x = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+    } else {
+      s.x = *(const float4*)((const float*)q + qi);
+    }
+    s.sg = *(const float4*)(signs + 4 * p);
+    if (so4) {
+      s.l = qload(so4 + 8 * p);
+      s.r = qload(so4 + 8 * p + 4);
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ float4 query_rotate(const QueryLane& s, bool so4, int group, int lane) {
+  float x0 = s.x.x * s.sg.x, x1 = s.x.y * s.sg.y, x2 = s.x.z * s.sg.z, x3 = s.x.w * s.sg.w;
+  float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
+  x0 = y0 + y2; x1 = y1 + y3; x2 = y0 - y2; x3 = y1 - y3;
+  for (int m = 1; m < group / 4; m <<= 1) {
+    const bool up = (lane & m) != 0;
+    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    x0 = up ? o0 - x0 : x0 + o0;
+    x1 = up ? o1 - x1 : x1 + o1;
+    x2 = up ? o2 - x2 : x2 + o2;
+    x3 = up ? o3 - x3 : x3 + o3;
+  }
+  const float hsc = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  Quat v{x0 * hsc, x1 * hsc, x2 * hsc, x3 * hsc};
+  if (so4) v = qmul(qmul(s.l, v), qconj(s.r));
+  return make_float4(v.w, v.x, v.y, v.z);
+}
+
 // Bit field of width W at bit offset `off` of a little-endian dword array; `off` and W
 // are compile-time constants after unrolling.
 template <int W>
@@ -368,9 +424,11 @@ __device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, 
 // A = value codebook values (a value word holds 8 tokens of one coordinate) and P' = p *
 // value norm in fp16, taken straight from the score registers.  Online softmax per column.
 //
-// Decode tables: an index of two codes (6 bits for 3-bit codes, 8 for 4-bit) selects a
-// 4-byte entry holding the two fp16 values.  A 64-entry table is 256 bytes, one entry per
-// LDS bank, so lookups by any mix of lanes never conflict.
+// Decode tables: an index of two codes (6 bits for 3-bit codes, 8 for 4-bit) selects an
+// entry holding the two fp16 values (keys: 8 bytes, the high parts then the low parts;
+// values: 4 bytes).  Every table is stored 32 times, copy c serving lanes c and c + 32, with
+// the copies of one entry side by side: the bank a lane reads is fixed by its lane number,
+// so data-dependent lookups never conflict (LDS serves 32 lanes per pass).
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
                                                 0, 0);
@@ -381,22 +439,28 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Byte offset (index * 4) of the two-code field of W = 2*BITS bits at bit `off` of d[].
-template <int BITS>
-__device__ __forceinline__ uint32_t pair_addr(const uint32_t* d, int off) {
+// LDS byte address of a two-code table lookup: the 2*BITS-bit field at bit `off` of d[]
+// lands on bits [SH, SH + 2*BITS) of the address and the lane's copy offset fills the bits
+// below (one shift or align and one bit-field insert per lookup).
+template <int BITS, int SH>
+__device__ __forceinline__ uint32_t pair_lds_addr(const uint32_t* d, int off, uint32_t lane_off) {
   constexpr int W = 2 * BITS;
+  constexpr uint32_t mask = ((1u << W) - 1u) << SH;
   const int wi = off >> 5, sh = off & 31;
   uint32_t x;
-  if (sh + W <= 32) {
-    x = sh >= 2 ? (d[wi] >> (sh - 2)) : (d[wi] << (2 - sh));
+  if (sh + W > 32) {
+    x = __builtin_amdgcn_alignbit(d[wi + 1], d[wi], sh - SH);
+  } else if (sh >= SH) {
+    x = d[wi] >> (sh - SH);
   } else {
-    x = __builtin_amdgcn_alignbit(d[wi + 1], d[wi], sh - 2);
+    x = d[wi] << (SH - sh);
   }
-  return x & (((1u << W) - 1u) << 2);
+  return (x & mask) | lane_off;
 }
 
-__device__ __forceinline__ uint32_t lds_word(const uint32_t* tab, uint32_t byte_off) {
-  return *(const uint32_t*)((const char*)tab + byte_off);
+template <typename T>
+__device__ __forceinline__ T lds_at(const uint8_t* base, uint32_t byte_off) {
+  return *(const T*)(base + byte_off);
 }
 
 template <int BK, int BV>
@@ -427,6 +491,47 @@ __device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
   return *(const T*)(base + off);
 }
 
+// Direct global -> LDS copies: every lane reads BYTES bytes and the data lands in LDS at
+// lds_base + lane * stride (lds_base is wave-uniform, passed in M0), where the stride is
+// BYTES for 4- and 16-byte copies and 16 for 12-byte copies (the fourth dword of each lane
+// is left untouched).  They count in vmcnt
+// like ordinary loads but leave no register results, so a deep prefetch ring costs no
+// VGPRs.  Written as inline assembly: the compiler would otherwise make every later LDS
+// read wait for all of them.  The caller waits with vm_wait before reading the data.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(uint32_t lds_base, const void* sbase, uint32_t voff) {
+  if (BYTES == 16) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  } else if (BYTES == 12) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  } else {
+    static_assert(BYTES == 12 || BYTES == 16, "whole-lane copies of 12 or 16 bytes");
+  }
+}
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_addr(uint32_t lds_base, const void* addr) {
+  if (BYTES == 16) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+  } else if (BYTES == 4) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+  } else {
+    static_assert(BYTES == 4 || BYTES == 16, "whole-lane copies of 4 or 16 bytes");
+  }
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until every LDS access of this wave is complete.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <int BK, int BV, int NG, bool QF16>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NW = 4;
@@ -434,22 +539,39 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // product per key operand suffices; 32-groups: columns are (group, head), two products
   constexpr bool SPLITQ = NG == 1;
   constexpr int HPS = NG == 4 ? 4 : 8;
-  // blocks in flight ahead of the arithmetic (register budget: whole-head groups need half
-  // the query operands, which leaves room for a deeper ring)
-  constexpr int PREFETCH = 1;
   constexpr int NEK = BK == 3 ? 64 : 256;   // table entries: all pairs of codes
   constexpr int NEV = BV == 3 ? 64 : 256;
   constexpr int KREC = 16 * BK;
   constexpr int VTILE = kTile * 16 * BV;
-  __shared__ uint32_t tab[2 * NEK + NEV];   // key hi, key lo, value hi
+  // Decode tables [entry][copies]: keys uint2 at 0, values uint32 at VT_AT (a power of two
+  // no smaller than either table, so a value address is VT_AT | offset).  3-bit tables have
+  // 32 copies (conflict-free); 4-bit tables have 8 (key) or 16 (value) copies to fit the
+  // LDS budget of two workgroups per CU, at the price of occasional bank conflicts.
+  constexpr int RK = BK == 3 ? 32 : 8, RV = BV == 3 ? 32 : 16;
+  constexpr int SHK = BK == 3 ? 8 : 6, SHV = BV == 3 ? 7 : 6;  // log2 of an entry's row bytes
+  constexpr int KT_BYTES = NEK * RK * 8, VT_BYTES = NEV * RV * 4;
+  constexpr int VT_AT = KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
+  // Prefetch ring: per wave, D slots of one 32-token block each, filled by direct
+  // global -> LDS copies in the lane order the block is read back in: key codes (two
+  // 16-token halves), value words (two halves), then the key and value norm blocks.
+  constexpr int KSZ = 4 * BK, VSZ = 4 * BV, NSZ = NG == 1 ? 4 : 16;  // bytes per lane per copy
+  constexpr int LST = 16;  // LDS bytes per lane of a code copy (12-byte copies land 16 apart)
+  constexpr int S_K1 = 64 * LST, S_V0 = 128 * LST, S_V1 = S_V0 + 64 * LST, S_N = S_V1 + 64 * LST;
+  constexpr int SLOT = S_N + 64 * NSZ;
+  constexpr int RING_AT = VT_AT + VT_BYTES;
+  // two workgroups per CU: the pool stays under 78 KB
+  constexpr int D = RING_AT + 3 * NW * SLOT <= 78 * 1024 ? 3 : 2;
+  constexpr int NDMA = 5;  // copies per block
+  // the epilogue reuses the space for the per-wave partial results
+  constexpr int SCR_BYTES = NW * HPS * (kHeadDim + 2) * 4;
+  constexpr int POOL = RING_AT + D * NW * SLOT > SCR_BYTES ? RING_AT + D * NW * SLOT : SCR_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t pool[POOL];
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
-  __shared__ float scr[NW * HPS * (kHeadDim + 2)];
   __shared__ uint32_t cbk[16], cbv[16];
   __shared__ float red[NW];
   __shared__ float lse2[HPS];
-  const uint32_t* khi = tab;
-  const uint32_t* klo = tab + NEK;
-  const uint32_t* vhi = tab + 2 * NEK;
+  const uint8_t* ktab = pool;
+  float* scr = (float*)pool;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -473,39 +595,54 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   const uint32_t noff = (cgrp * kTile + 8 * qg) * 4;
   const uint32_t voff = lane * (8 * BV);
 
-  auto load_block = [&](Block<BK, BV>& d, int blk) {
+  // ---- query reads, then the first D blocks of this wave into its ring
+  const QueryLane qlane = query_fetch<QF16>(a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.q,
+                                            (size_t)u.b * a.n_q_heads + u.h0, u.hs, wv, lane);
+  const int nblk = blk0 + wv < blk1 ? (blk1 - (blk0 + wv) + NW - 1) / NW : 0;  // this wave's blocks
+  const uint32_t ring = lds_addr(pool) + RING_AT + wv * (D * SLOT);
+  const uint8_t* nlane = (lane < 32 ? knbase : vnbase) + (lane & 31) * NSZ;
+  // copies block j of this wave (clamped to its last block, so the count per block is
+  // fixed and the waits are static) into slot j % D
+  auto fetch = [&](int j) {
+    const int blk = blk0 + wv + NW * min(j, nblk - 1);
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(ring + (j % D) * SLOT);
     const uint8_t* kb = kbase + (size_t)blk * kTile * KREC;
+    const uint8_t* vb = vbase + (size_t)blk * VTILE;
+    lds_dma<KSZ>(sl, kb, koff);
+    lds_dma<KSZ>(sl + S_K1, kb, koff + 16 * KREC);
+    lds_dma<VSZ>(sl + S_V0, vb, voff);
+    lds_dma<VSZ>(sl + S_V1, vb, voff + VSZ);
+    lds_dma_addr<NSZ>(sl + S_N, nlane + (size_t)blk * (NG * kTile * 4));
+  };
+  auto read_block = [&](int j) {
+    const uint8_t* sl = pool + RING_AT + wv * (D * SLOT) + (j % D) * SLOT;
+    Block<BK, BV> d;
     if (BK == 3) {
-      const uint3 x0 = load_at<uint3>(kb, koff), x1 = load_at<uint3>(kb, koff + 16 * KREC);
+      const uint3 x0 = load_at<uint3>(sl, lane * LST), x1 = load_at<uint3>(sl + S_K1, lane * LST);
       d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z;
       d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z;
     } else {
-      const uint4 x0 = load_at<uint4>(kb, koff), x1 = load_at<uint4>(kb, koff + 16 * KREC);
+      const uint4 x0 = load_at<uint4>(sl, lane * LST), x1 = load_at<uint4>(sl + S_K1, lane * LST);
       d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z; d.k0[BK - 1] = x0.w;
       d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z; d.k1[BK - 1] = x1.w;
     }
-    const uint8_t* nb = knbase + (size_t)blk * (NG * kTile * 4);
-    d.kn0 = load_at<f32x4>(nb, noff);
-    d.kn1 = load_at<f32x4>(nb, noff + 16);
-    const uint8_t* vb = vbase + (size_t)blk * VTILE;
     if (BV == 3) {
-      const uint3 y0 = load_at<uint3>(vb, voff), y1 = load_at<uint3>(vb, voff + 12);
+      const uint3 y0 = load_at<uint3>(sl + S_V0, lane * LST), y1 = load_at<uint3>(sl + S_V1, lane * LST);
       d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y1.x; d.v[4] = y1.y; d.v[5] = y1.z;
     } else {
-      const uint4 y0 = load_at<uint4>(vb, voff), y1 = load_at<uint4>(vb, voff + 16);
+      const uint4 y0 = load_at<uint4>(sl + S_V0, lane * LST), y1 = load_at<uint4>(sl + S_V1, lane * LST);
       d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y0.w;
       d.v[4] = y1.x; d.v[5] = y1.y; d.v[2 * BV - 2] = y1.z; d.v[2 * BV - 1] = y1.w;
     }
-    const uint8_t* vnb = vnbase + (size_t)blk * (NG * kTile * 4);
-    d.vn0 = load_at<f32x4>(vnb, noff);
-    d.vn1 = load_at<f32x4>(vnb, noff + 16);
+    d.kn0 = load_at<f32x4>(sl + S_N, noff);
+    d.kn1 = load_at<f32x4>(sl + S_N, noff + 16);
+    d.vn0 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff);
+    d.vn1 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff + 16);
+    return d;
   };
-
-  Block<BK, BV> r0, r1, r2;
-  int blk = blk0 + wv;
-  if (blk < blk1) {
-    load_block(r0, blk);
-    if (PREFETCH == 2) load_block(r1, min(blk + NW, blk1 - 1 - ((blk1 - 1 - blk) % NW)));
+  if (nblk > 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch(j);
   }
 
   // ---- decode tables
@@ -516,21 +653,25 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     cbv[tid] = f16_bits((_Float16)a.vcent[tid]);
   }
   __syncthreads();
-  for (int e = tid; e < NEK; e += 256) {
+  for (int i = tid; i < NEK * RK; i += 256) {
+    const int e = i / RK;
     const uint32_t c0 = cbk[e & ((1 << BK) - 1)], c1 = cbk[e >> BK];
-    tab[e] = (c0 & 0xFFFFu) | (c1 << 16);
-    tab[NEK + e] = (c0 >> 16) | (c1 & 0xFFFF0000u);
+    ((uint2*)pool)[i] = make_uint2((c0 & 0xFFFFu) | (c1 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u));
   }
-  for (int e = tid; e < NEV; e += 256) tab[2 * NEK + e] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
+  for (int i = tid; i < NEV * RV; i += 256) {
+    const int e = i / RV;
+    ((uint32_t*)(pool + VT_AT))[i] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
+  }
 
   // ---- rotated, scaled query (log2 units) with a power-of-two prescale into fp16 range
-  load_queries<QF16>(a, u, qbuf);
-  lds_rotate<true>(qbuf, u.hs, a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.rot_group);
   float mx = 0.f;
-  for (int i = tid; i < u.hs * kHeadDim; i += 256) {
-    const float x = qbuf[i] * a.scale_log2;
-    qbuf[i] = x;
-    mx = fmaxf(mx, fabsf(x));
+  {
+    float4 r = query_rotate(qlane, a.so4 != nullptr, a.rot_group, lane);
+    r.x *= a.scale_log2; r.y *= a.scale_log2; r.z *= a.scale_log2; r.w *= a.scale_log2;
+    if (qlane.live) {
+      *(float4*)(qbuf + (2 * wv + (lane >> 5)) * kHeadDim + 4 * (lane & 31)) = r;
+      mx = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -573,9 +714,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     }
   }
 
+  const uint32_t klane = (lane & (RK - 1)) << 3, vlane = VT_AT | ((lane & (RV - 1)) << 2);
   auto key_operand = [&](const uint32_t* kk, int f) {
-    const uint32_t a0 = pair_addr<BK>(kk, 4 * BK * f), a1 = pair_addr<BK>(kk, 4 * BK * f + 2 * BK);
-    return u32x4{lds_word(khi, a0), lds_word(klo, a0), lds_word(khi, a1), lds_word(klo, a1)};
+    const uint2 x0 = lds_at<uint2>(ktab, pair_lds_addr<BK, SHK>(kk, 4 * BK * f, klane));
+    const uint2 x1 = lds_at<uint2>(ktab, pair_lds_addr<BK, SHK>(kk, 4 * BK * f + 2 * BK, klane));
+    return u32x4{x0.x, x0.y, x1.x, x1.y};
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -604,7 +747,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
       D1 = mfma16(kb[f], B1[f], D1);
       if (!SPLITQ) D1 = mfma16(kb[f], B2[f], D1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) va[f][j] = lds_word(vhi, pair_addr<BV>(cb.v, 8 * BV * f + 2 * BV * j));
+      for (int j = 0; j < 4; ++j) va[f][j] = lds_at<uint32_t>(pool, pair_lds_addr<BV, SHV>(cb.v, 8 * BV * f + 2 * BV * j, vlane));
     }
     // raw scores (units of the prescaled query) of tokens 16h + 4q' + r, slot k = 4h + r
     float x[8];
@@ -630,10 +773,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
         if (t < lo || t >= hi) x[k] = -INFINITY;
       }
     }
-    const float bm =
-        rows_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-    const bool grow = m_run == -INFINITY ? bm > -INFINITY : (bm - m_run) * qinv > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // Lazy maximum: while no score of the block exceeds the column's running maximum by
+    // more than 2^kRescaleLog2, p stays below that bound and nothing needs to be reduced
+    // across the lanes; only when some lane sees a larger score is the block maximum formed
+    // and the column rescaled.
+    const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const bool need = m_run == -INFINITY ? lm > -INFINITY : (lm - m_run) * qinv > kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float bm = rows_max(lm);
+      const bool grow = m_run == -INFINITY ? bm > -INFINITY : (bm - m_run) * qinv > kRescaleLog2;
       const float mnew = grow ? bm : m_run;
       const float al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * qinv);
 #pragma unroll
@@ -667,39 +815,22 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     for (int w = 0; w < 8; ++w) O[w] = mfma16(va[w], bp, O[w]);
   };
 
-  // register ring: the next PREFETCH blocks' loads are in flight while this one computes.
-  // The prefetch is unconditional (past the end it re-reads this wave's last block, which is
-  // still in L2) so that the wait counts are static and never wait on younger loads.
-  const int last = blk1 - 1 - ((blk1 - 1 - (blk0 + wv)) % NW + NW) % NW;  // this wave's last block
-  if (PREFETCH == 1) {
-    while (blk < blk1) {
-      load_block(r1, min(blk + NW, last));
-      process(r0, blk);
-      blk += NW;
-      if (blk >= blk1) break;
-      load_block(r0, min(blk + NW, last));
-      process(r1, blk);
-      blk += NW;
-    }
-  } else {
-    while (blk < blk1) {
-      load_block(r2, min(blk + 2 * NW, last));
-      process(r0, blk);
-      blk += NW;
-      if (blk >= blk1) break;
-      load_block(r0, min(blk + 2 * NW, last));
-      process(r1, blk);
-      blk += NW;
-      if (blk >= blk1) break;
-      load_block(r1, min(blk + 2 * NW, last));
-      process(r2, blk);
-      blk += NW;
-    }
+  // Block j waits until the copies of every older block are complete (the D - 1 younger
+  // blocks may still be in flight), is read into registers, and once those reads are
+  // complete its slot is refilled with block j + D, so D blocks load during the arithmetic.
+  for (int j = 0; j < nblk; ++j) {
+    vm_wait<NDMA * (D - 1)>();
+    const Block<BK, BV> cb = read_block(j);
+    lds_wait();
+    fetch(j + D);
+    process(cb, blk0 + wv + NW * j);
   }
+  vm_wait<0>();  // no copy may land in the pool once it is reused below
 
   // ---- combine the waves of the workgroup (scores in prescaled units -> log2 units)
   const float lt = rows_sum(l_run);
   const float m2 = m_run == -INFINITY ? -INFINITY : m_run * qinv;
+  __syncthreads();                       // every wave is done with the tables
   float* so = scr;                       // [NW][HPS][128]
   float* sm = so + NW * HPS * kHeadDim;  // [NW][HPS]
   float* sl = sm + NW * HPS;
