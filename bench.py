@@ -295,6 +295,98 @@ def stream_read_probe_gbs():
     return best
 
 
+COPY_BYTES = 1 << 30  # the calibration copy: bytes read and bytes written
+
+
+def counter_run(w, inp, n_splits, schedule, launches=24):
+    """Dispatches for a rocprofv3 --pmc pass: three copies of COPY_BYTES through the probe
+    library (known traffic), then `launches` decode launches over the cache replicas, as
+    bench timing issues them.  Prints nothing on stdout."""
+    import ctypes
+
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    from compressed_domain_attention_amd import build as _b
+
+    dev = torch.device("cuda:0")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.tq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
+    torch.cuda.synchronize()
+    del src, dst
+    T = w.seq_len
+    cap = (T + 31) // 32 * 32
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).to(dev)
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).to(dev), w.group, so4)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev)
+    v0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev)
+    tq.quantize_append(rot, k0, torch.from_numpy(inp["k"]).to(dev))
+    tq.quantize_append(rot, v0, torch.from_numpy(inp["v"]).to(dev))
+    cache_bytes = sum(t.numel() * t.element_size() for t in (k0.codes, k0.norms, v0.codes, v0.norms))
+    reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
+    caches = [(k0, v0)] + [
+        (tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev, codes=k0.codes.clone(),
+                        norms=k0.norms.clone()),
+         tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev, codes=v0.codes.clone(),
+                        norms=v0.norms.clone())) for _ in range(reps - 1)]
+    po = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    for i in range(launches):
+        k, v = caches[i % reps]
+        if n_splits == 1:
+            tq.decode_attention(rot, k, v, q, max_len=T, schedule=schedule, out=out)
+        else:
+            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=n_splits, schedule=schedule, part_o=po,
+                                part_lse=pl)
+    torch.cuda.synchronize()
+    log("counter run: 3 copies of %d bytes, %d decode launches over %d replicas" % (COPY_BYTES, launches, reps))
+
+
+def _per_dispatch(csv_path, counter, name_part):
+    import csv
+    import collections
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return [per[d] for d in sorted(per)]
+
+
+def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for the
+    calibration copy of known size, and store HBM bytes per decode launch."""
+    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy_kernel"), _per_dispatch(write_csv, "WRITE_SIZE", "copy_kernel")
+    fd = _per_dispatch(fetch_csv, "FETCH_SIZE", "decode_")
+    wd = _per_dispatch(write_csv, "WRITE_SIZE", "decode_")
+    if not (fc and wc and fd and wd):
+        raise SystemExit("counter files hold no copy or decode dispatches")
+    f_factor = COPY_BYTES / (sum(fc) / len(fc) * 1024)
+    w_factor = COPY_BYTES / (sum(wc) / len(wc) * 1024)
+    # the first launches warm the code object; use the second half
+    fd, wd = fd[len(fd) // 2:], wd[len(wd) // 2:]
+    read = sum(fd) / len(fd) * 1024 * f_factor
+    written = sum(wd) / len(wd) * 1024 * w_factor
+    rec = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        rec = {"kernel_sha256_16": kernel_hash(), "workloads": {}}
+    rec["workloads"]["%s/S%d" % (w.name, n_splits)] = {
+        "hbm_bytes_per_launch": read + written, "read_bytes": read, "written_bytes": written,
+        "algorithmic_bytes_per_launch": w.batch * w.n_kv_heads * w.seq_len * bytes_per_token_head(w),
+        "fetch_scale": f_factor, "write_scale": w_factor, "commands": commands}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    log("traffic %s/S%d: read %.1f MB + written %.2f MB per launch (scales %.3f, %.3f)" % (
+        w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +397,12 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "mfma", "vec"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only issue the calibration copies and decode launches (run under rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--counter-run into profiles/decode_traffic.json")
+    ap.add_argument("--commands", default="", help="the profiling commands, recorded with --write-traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -313,18 +411,24 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     n_splits = args.splits if args.splits is not None else w.n_splits
+    if args.write_traffic:
+        write_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
+        return
     log("workload %s: %s, splits %d, schedule %s" % (w.name, w, n_splits, args.schedule))
     t_gen = time.perf_counter()
     inp = workloads.generate(w, 0)
     log("generated inputs in %.1fs" % (time.perf_counter() - t_gen))
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.counter_run:
         # runs before anything initialises the GPU in this process (the pool forks)
         cpu = cpu_baseline(w, inp)
         log("cpu baseline: %.3g token*heads/s (%s)" % (cpu["value"], cpu["sample"]))
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.counter_run:
+        counter_run(w, inp, n_splits, args.schedule)
+        return
     r = run_gpu(w, inp, args.steps, args.warmup, n_splits, args.schedule, check=not args.no_check)
     units = w.batch * w.n_kv_heads * w.seq_len
     value = units / (r["ms_per_step"] / 1e3)
@@ -356,6 +460,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, n_splits)},
         "cpu_baseline": cpu,
         "decode_kernel_ms": r["decode_ms"],
+        "prefill_ms": r["prefill_ms"],
+        "prefill_GBps": r["prefill_bytes"] / 1e6 / r["prefill_ms"],
         "algorithmic_bytes_per_launch": algo_bytes,
         "stream_read_probe_GBps": probe,
         "parity_worst_row_rel_err": r["parity"],

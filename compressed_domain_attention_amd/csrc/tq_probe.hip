@@ -1,6 +1,8 @@
-// Stream-read probe: the achievable HBM read bandwidth on this device, measured with the
-// same kind of loads the decode kernel issues (16 bytes per lane, fully coalesced).
-// Measurement helper for the benchmark; not part of the attention library's C ABI.
+// Measurement helpers for the benchmark; not part of the attention library's C ABI.
+// Stream read: the achievable HBM read bandwidth on this device, measured with the same
+// kind of loads the decode kernel issues (16 bytes per lane, fully coalesced).
+// Copy: a known number of bytes read and written once, the reference that scales the
+// hardware byte counters (FETCH_SIZE, WRITE_SIZE) to bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,6 +24,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (acc == 0x9E3779B9u) sink[0] = acc;  // data-dependent store keeps every load live
 }
 
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from device memory `buf` once.  Returns 0 on success.
@@ -29,5 +36,14 @@ extern "C" int tq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sin
   if (buf == nullptr || sink == nullptr || bytes % 16 != 0 || blocks <= 0) return 1;
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf,
                      bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Copies `bytes` (a multiple of 16) from `src` to `dst` (device, not overlapping).  Returns 0
+// on success.
+extern "C" int tq_probe_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes % 16 != 0 || blocks <= 0) return 1;
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+                     bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

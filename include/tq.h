@@ -144,8 +144,10 @@ tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, cons
  *             normalised per section) and part_lse [n_splits][batch][n_q_heads]; an empty
  *             section has lse = -inf and a zero partial.  Finish with tq_merge_splits.
  * A row with no tokens gives out = 0 and lse = -inf.
- * The MFMA schedule converts the scaled query and p * value-norm to fp16; it assumes
- * those stay inside the fp16 range (|value group norm| < 65504). */
+ * The MFMA schedule converts the scaled query (after an exact power-of-two prescale) and
+ * p * value-norm to fp16.  Its running maximum may lag the true one by up to 2^3, so p <= 8
+ * and value group norms must stay below 8188 for p * norm to fit fp16; larger values need
+ * the VEC schedule. */
 tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
                               const void* q, tq_dtype q_dtype, int32_t n_q_heads,
                               const int32_t* seq_lens, int32_t max_len, float scale,
