@@ -1,7 +1,7 @@
 """Benchmark: decode attention on a packed 3/4-bit KV cache, one MI355X.
 
 One step = one pass of the whole hot path over one batch: quantise-append the newest
-token's key and value into slot T-1 of every (sequence, KV head), decode attention over T
+token's key and value (one launch) into slot T-1 of every (sequence, KV head), decode attention over T
 tokens straight from the codes (rotated query, online softmax, rotated-domain value sum),
 and merge the key-axis splits with the single inverse rotation.  Inputs are seeded and
 synthetic (workloads.py) and resident in HBM before timing.  The packed caches are
@@ -125,8 +125,7 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
 
     def step(i):
         k, v = caches[i % reps]
-        tq.quantize_append(rot, k, newk, pos0=T - 1)
-        tq.quantize_append(rot, v, newv, pos0=T - 1)
+        tq.quantize_append_kv(rot, k, v, newk, newv, pos0=T - 1)
         decode(i)
         if n_splits > 1:
             tq.merge_splits(rot, po, pl, out=out, lse=lse)
@@ -163,8 +162,14 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
     torch.cuda.synchronize()
     if not torch.equal(out, eager_out):
         raise SystemExit("graph replay does not reproduce the eager step")
-    for i in range(warmup):
+    # warm-up: the W steps asked for, and at least ~0.3 s of them, so that the timed region
+    # sees the device at its settled clock and power state rather than ramping up from idle
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < 0.3:
         graphs[i % reps].replay()
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -179,7 +184,11 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
     # decode kernel alone: back-to-back launches in one graph, events on the launch stream
     gdec.replay()
     torch.cuda.synchronize()
-    reps_dec = max(3, 200 // n_dec)
+    t_d = time.perf_counter()
+    gdec.replay()
+    torch.cuda.synchronize()
+    # about half a second of launches
+    reps_dec = max(3, int(0.5 / max(time.perf_counter() - t_d, 1e-6)))
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record()
     for _ in range(reps_dec):
@@ -390,8 +399,8 @@ def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--schedule", default="auto", choices=["auto", "mfma", "vec"])
@@ -455,7 +464,7 @@ def main():
         "config": {"workload": w.name, "timing": "HIP graph replay, one graph per step", "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "seq_len": w.seq_len, "bits_k": w.bits_k, "bits_v": w.bits_v, "group": w.group,
                    "so4": w.so4, "n_splits": n_splits, "schedule": args.schedule,
-                   "step": "append 1 token K+V, decode, merge", "cache_replicas": r["reps"]},
+                   "step": "append 1 token K+V (one launch), decode, merge", "cache_replicas": r["reps"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, n_splits)},
         "cpu_baseline": cpu,

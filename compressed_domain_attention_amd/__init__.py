@@ -40,7 +40,7 @@ class TQError(RuntimeError):
 
 class Codebook(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("dim", ctypes.c_int32),
-                ("centroid", ctypes.c_float * 16), ("boundary", ctypes.c_float * 15)]
+                ("centroid", ctypes.c_float * 16), ("boundary", ctypes.c_float * 15), ("f16_scale", ctypes.c_float)]
 
     @property
     def centroids(self):
@@ -64,7 +64,8 @@ class _Cache(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_decode_attention", "tq_merge_splits")
+EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
+           "tq_decode_attention", "tq_merge_splits")
 
 
 def library():
@@ -82,6 +83,9 @@ def library():
     lib.tq_make_codebook.restype = I
     lib.tq_quantize_append.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), P, I, I, P, I, I, P]
     lib.tq_quantize_append.restype = I
+    lib.tq_quantize_append_kv.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), ctypes.POINTER(_Cache),
+                                          P, P, I, I, P, I, I, P]
+    lib.tq_quantize_append_kv.restype = I
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), ctypes.POINTER(_Cache),
                                         P, I, I, P, I, F, I, I, P, P, P, P, P]
     lib.tq_decode_attention.restype = I
@@ -162,6 +166,21 @@ def quantize_append(rot: Rotation, cache: PackedCache, x: torch.Tensor, pos: tor
         max_pos = int(pos.max().item()) if pos is not None else pos0
     _check(library().tq_quantize_append(ctypes.byref(rot.c), ctypes.byref(cache.c), _ptr(x), _DTYPES[x.dtype],
                                         n_new, _ptr(pos), pos0, max_pos, _stream()), "tq_quantize_append")
+
+
+def quantize_append_kv(rot: Rotation, keys: PackedCache, values: PackedCache, xk: torch.Tensor, xv: torch.Tensor,
+                       pos: torch.Tensor = None, pos0: int = 0, max_pos: int = None):
+    """Quantise new keys xk and values xv [batch, n_kv_heads, n_new, 128] in one launch."""
+    for x in (xk, xv):
+        if x.dtype not in _DTYPES or not x.is_contiguous():
+            raise ValueError("xk and xv must be contiguous float16/float32 tensors")
+    if xk.dtype != xv.dtype or xk.shape != xv.shape:
+        raise ValueError("xk and xv must have the same dtype and shape")
+    if max_pos is None:
+        max_pos = int(pos.max().item()) if pos is not None else pos0
+    _check(library().tq_quantize_append_kv(ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c),
+                                           _ptr(xk), _ptr(xv), _DTYPES[xk.dtype], xk.shape[2], _ptr(pos), pos0,
+                                           max_pos, _stream()), "tq_quantize_append_kv")
 
 
 def decode_attention(rot: Rotation, keys: PackedCache, values: PackedCache, q: torch.Tensor, seq_lens=None,

@@ -8,7 +8,9 @@
 
 namespace {
 
-bool valid_codebook(const tq_codebook& cb, int bits, int group) { return cb.bits == bits && cb.dim == group; }
+bool valid_codebook(const tq_codebook& cb, int bits, int group) {
+  return cb.bits == bits && cb.dim == group && cb.f16_scale >= 1.f && cb.f16_scale < 2.f;
+}
 
 tq_status check_rotation(const tq_rotation* rot) {
   if (rot == nullptr || rot->signs == nullptr) return TQ_EINVAL;
@@ -30,23 +32,17 @@ tq_status check_cache(const tq_cache* c, const tq_rotation* rot, tq_role role) {
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 
-}  // namespace
-
-extern "C" tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x, tq_dtype x_dtype,
-                                        int32_t n_new, const int32_t* pos, int32_t pos0, int32_t max_pos,
-                                        void* stream) {
-  tq_status st = check_rotation(rot);
+// Host checks shared by the append calls; fills the launch arguments of one cache.
+tq_status append_args(const tq_rotation* rot, const tq_cache* cache, const void* x, tq_dtype x_dtype, int32_t n_new,
+                      const int32_t* pos, int32_t pos0, int32_t max_pos, tq::AppendArgs& a) {
+  tq_status st = check_cache(cache, rot, cache ? cache->role : TQ_KEYS);
   if (st != TQ_OK) return st;
-  if ((st = check_cache(cache, rot, cache ? cache->role : TQ_KEYS)) != TQ_OK) return st;
   if (cache->role != TQ_KEYS && cache->role != TQ_VALUES) return TQ_EINVAL;
   if (x == nullptr || n_new < 0) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
   const int32_t first = pos ? max_pos : pos0;
   if (first < 0 || pos0 < 0) return TQ_EINVAL;
   if ((int64_t)first + n_new > cache->capacity) return TQ_ECAPACITY;
-  if (n_new == 0) return TQ_OK;
-
-  tq::AppendArgs a;
   std::memset(&a, 0, sizeof(a));
   a.x = x;
   a.codes = (uint8_t*)cache->codes;
@@ -59,11 +55,44 @@ extern "C" tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* 
   a.n_kv_heads = cache->n_kv_heads;
   a.capacity = cache->capacity;
   for (int k = 0; k < 15; ++k) a.boundary[k] = cache->codebook.boundary[k];
-  // tiles touched: with a device-side start the alignment is unknown, so cover the worst
+  return TQ_OK;
+}
+
+// Tiles touched per (sequence, head): with a device-side start the alignment is unknown,
+// so cover the worst case.
+int append_tiles(const int32_t* pos, int32_t pos0, int32_t n_new) {
   const int span = pos ? (TQ_TILE - 1) + n_new : (pos0 % TQ_TILE) + n_new;
-  const int n_tiles = (span + TQ_TILE - 1) / TQ_TILE;
+  return (span + TQ_TILE - 1) / TQ_TILE;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x, tq_dtype x_dtype,
+                                        int32_t n_new, const int32_t* pos, int32_t pos0, int32_t max_pos,
+                                        void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  tq::AppendArgs a;
+  if ((st = append_args(rot, cache, x, x_dtype, n_new, pos, pos0, max_pos, a)) != TQ_OK) return st;
+  if (n_new == 0) return TQ_OK;
   return from_hip(tq::launch_append(a, cache->bits, cache->group, cache->role == TQ_VALUES, x_dtype == TQ_F16,
-                                    cache->batch, n_tiles, (hipStream_t)stream));
+                                    cache->batch, append_tiles(pos, pos0, n_new), (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                           const void* xk, const void* xv, tq_dtype x_dtype, int32_t n_new,
+                                           const int32_t* pos, int32_t pos0, int32_t max_pos, void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if (keys == nullptr || values == nullptr) return TQ_EINVAL;
+  if (keys->role != TQ_KEYS || values->role != TQ_VALUES) return TQ_EINVAL;
+  if (keys->batch != values->batch) return TQ_EINVAL;
+  tq::AppendArgs ak, av;
+  if ((st = append_args(rot, keys, xk, x_dtype, n_new, pos, pos0, max_pos, ak)) != TQ_OK) return st;
+  if ((st = append_args(rot, values, xv, x_dtype, n_new, pos, pos0, max_pos, av)) != TQ_OK) return st;
+  if (n_new == 0) return TQ_OK;
+  return from_hip(tq::launch_append_kv(ak, av, keys->bits, values->bits, keys->group, x_dtype == TQ_F16, keys->batch,
+                                       append_tiles(pos, pos0, n_new), (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
@@ -114,6 +143,7 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
   if (values->capacity != keys->capacity) return TQ_EINVAL;
   a.rot_group = rot->group;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.kscale = keys->codebook.f16_scale;
   for (int k = 0; k < 16; ++k) {
     a.kcent[k] = keys->codebook.centroid[k];
     a.vcent[k] = values->codebook.centroid[k];

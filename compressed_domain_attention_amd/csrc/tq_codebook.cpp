@@ -56,6 +56,28 @@ double first_moment(double lo, double hi, double mu) {
 
 }  // namespace
 
+// The scale s in [1, 2) (a 2^-16 grid) at which every s * centroid lies closest, in the
+// worst relative error over the levels, to an fp16 number.  Matrix-core decode stores the
+// key codebook as fp16(s * c) and divides the query by s.
+static float f16_scale(const float* centroid, int n) {
+  float best = 1.f, best_err = INFINITY;
+  for (int i = 0; i < 65536; ++i) {
+    const float s = 1.f + (float)i / 65536.f;
+    float err = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const float v = s * centroid[k];
+      if (v == 0.f) continue;
+      const float r = (float)(_Float16)v;
+      err = std::fmax(err, std::fabs(r - v) / std::fabs(v));
+    }
+    if (err < best_err) {
+      best_err = err;
+      best = s;
+    }
+  }
+  return best;
+}
+
 extern "C" tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* out) {
   if (out == nullptr) return TQ_EINVAL;
   if ((bits != 3 && bits != 4) || dim < 3) return TQ_EUNSUPPORTED;
@@ -87,6 +109,7 @@ extern "C" tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* ou
   out->dim = dim;
   for (int k = 0; k < n; ++k) out->centroid[k] = (float)c[k];
   for (int k = 0; k + 1 < n; ++k) out->boundary[k] = (float)(0.5 * (c[k] + c[k + 1]));
+  out->f16_scale = f16_scale(out->centroid, n);
   return TQ_OK;
 }
 

@@ -48,6 +48,7 @@ struct DecodeArgs {
   int32_t capacity;
   int32_t rot_group;        // 32 or 128
   float scale_log2;         // softmax scale * log2(e)
+  float kscale;             // key codebook scale making every level nearly fp16-exact
   float kcent[16];
   float vcent[16];
 };
@@ -69,6 +70,9 @@ struct MergeArgs {
 // Each returns the hipError_t of the launch.
 hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, bool x_f16, int batch,
                          int n_tiles, hipStream_t stream);
+// Keys and values in one launch (both caches share batch, heads, group and rotation).
+hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits_k, int bits_v, int group, bool x_f16,
+                            int batch, int n_tiles, hipStream_t stream);
 // schedule: 1 = vector (fp32), 2 = matrix cores
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
                          hipStream_t stream);

@@ -162,18 +162,44 @@ __device__ __forceinline__ uint32_t field(const uint32_t* d, int off) {
 // (token, chunk) holds 32 consecutive coordinates in registers.  The 32-point transform
 // runs in registers; a whole-head (128) transform adds two cross-lane stages.
 template <int BITS, int GROUP, bool VALUES, bool XF16>
-__global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
+__device__ __forceinline__ void append_tile(const AppendArgs& a, int b, int h, int tile) {
   constexpr int NB = (1 << BITS) - 1;
   constexpr int NG = kHeadDim / GROUP;
+  constexpr int ND = BITS;  // dwords of the four value words a thread merges
   __shared__ uint32_t tile_codes[VALUES ? kTile * kHeadDim / 4 : 1];  // u8 [32][128]
   const int tid = threadIdx.x, tok = tid >> 2, chunk = tid & 3;
-  const int h = blockIdx.y, b = blockIdx.z;
   const int pos = a.pos ? a.pos[b] : a.pos0;
-  const int t0 = (pos / kTile + (int)blockIdx.x) * kTile;
+  const int t0 = (pos / kTile + tile) * kTile;
   if (t0 >= pos + a.n_new) return;  // uniform over the block
   const int slot = t0 + tok;
   const bool valid = slot >= pos && slot < pos + a.n_new;
   const size_t stream = (size_t)b * a.n_kv_heads + h;
+  const int ntile = a.capacity / kTile;
+
+  // Reads that do not depend on the new vectors are issued first, beside the vector load:
+  // the SO(4) parameters of this thread's eight 4-blocks, and the packed value words this
+  // thread merges when the tile is only partly rewritten.
+  Quat ql[8], qr[8];
+  if (a.so4 != nullptr) {
+    const float* qp = a.so4 + ((size_t)h * 32 + chunk * 8) * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ql[k] = qload(qp + 8 * k);
+      qr[k] = qload(qp + 8 * k + 4);
+    }
+  }
+  const int vlo = pos > t0 ? pos - t0 : 0;
+  const int vhi = min(kTile, pos + a.n_new - t0);
+  const bool partial = vlo > 0 || vhi < kTile;
+  uint32_t* vo = VALUES ? (uint32_t*)(a.codes + (stream * ntile + t0 / kTile) * (kTile * 16 * BITS) + 4 * tid * BITS)
+                        : nullptr;
+  uint32_t old[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) old[j] = 0u;
+  if (VALUES && partial) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) old[j] = vo[j];
+  }
 
   float v[32];
   if (valid) {
@@ -246,11 +272,9 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
   for (int i = 0; i < 32; ++i) v[i] *= hs;
 
   if (a.so4 != nullptr) {
-    const float* qp = a.so4 + ((size_t)h * 32 + chunk * 8) * 8;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const Quat l = qload(qp + 8 * k), r = qload(qp + 8 * k + 4);
-      const Quat o = qmul(qmul(l, Quat{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]}), qconj(r));
+      const Quat o = qmul(qmul(ql[k], Quat{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]}), qconj(qr[k]));
       v[4 * k] = o.w; v[4 * k + 1] = o.x; v[4 * k + 2] = o.y; v[4 * k + 3] = o.z;
     }
   }
@@ -265,7 +289,6 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
     code[i] = c;
   }
 
-  const int ntile = a.capacity / kTile;
   if (valid && (GROUP == 32 || chunk == 0)) {
     const int grp = GROUP == 32 ? chunk : 0;
     a.norms[(stream * ntile + t0 / kTile) * (NG * kTile) + grp * kTile + norm_pos(tok)] = nrm;
@@ -301,8 +324,6 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
         code[4 * j] | (code[4 * j + 1] << 8) | (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
   }
   __syncthreads();
-  const int vlo = pos > t0 ? pos - t0 : 0;
-  const int vhi = min(kTile, pos + a.n_new - t0);
   const int w0 = 4 * tid;  // four consecutive words: same (q, m), u = u0..u0+3
   const int q = w0 >> 7, m = (w0 >> 3) & 15, u0 = w0 & 7;
   uint32_t word[4], mask[4];
@@ -321,8 +342,6 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
     word[j] = x;
     mask[j] = mk;
   }
-  uint32_t* o = (uint32_t*)(a.codes + (stream * ntile + t0 / kTile) * (kTile * 16 * BITS) + w0 * BITS);
-  constexpr int ND = BITS;  // dwords for 4 words
   uint32_t dv[4], dm[4];
   if (BITS == 3) {
     dv[0] = word[0] | (word[1] << 24); dv[1] = (word[1] >> 8) | (word[2] << 16); dv[2] = (word[2] >> 16) | (word[3] << 8);
@@ -333,8 +352,24 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < ND; ++j) {
-    if (dm[j] == 0xFFFFFFFFu) o[j] = dv[j];
-    else if (dm[j] != 0u) o[j] = (o[j] & ~dm[j]) | dv[j];
+    if (dm[j] == 0xFFFFFFFFu) vo[j] = dv[j];
+    else if (dm[j] != 0u) vo[j] = (old[j] & ~dm[j]) | dv[j];
+  }
+}
+
+template <int BITS, int GROUP, bool VALUES, bool XF16>
+__global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
+  append_tile<BITS, GROUP, VALUES, XF16>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+}
+
+// Keys and values of one step in one launch: grid z covers the keys' sequences, then the
+// values' (same tiles, same rotation).
+template <int BK, int BV, int GROUP, bool XF16>
+__global__ __launch_bounds__(128) void append_kv_kernel(const AppendArgs ak, const AppendArgs av, int batch) {
+  if ((int)blockIdx.z < batch) {
+    append_tile<BK, GROUP, false, XF16>(ak, blockIdx.z, blockIdx.y, blockIdx.x);
+  } else {
+    append_tile<BV, GROUP, true, XF16>(av, blockIdx.z - batch, blockIdx.y, blockIdx.x);
   }
 }
 
@@ -547,9 +582,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // no smaller than either table, so a value address is VT_AT | offset).  3-bit tables have
   // 32 copies (conflict-free); 4-bit tables have 8 (key) or 16 (value) copies to fit the
   // LDS budget of two workgroups per CU, at the price of occasional bank conflicts.
-  constexpr int RK = BK == 3 ? 32 : 8, RV = BV == 3 ? 32 : 16;
-  constexpr int SHK = BK == 3 ? 8 : 6, SHV = BV == 3 ? 7 : 6;  // log2 of an entry's row bytes
-  constexpr int KT_BYTES = NEK * RK * 8, VT_BYTES = NEV * RV * 4;
+  constexpr int RK = BK == 3 ? 32 : 16, RV = BV == 3 ? 32 : 16;
+  constexpr int SHK = BK == 3 ? 7 : 6, SHV = BV == 3 ? 7 : 6;  // log2 of an entry's row bytes
+  constexpr int KT_BYTES = NEK * RK * 4, VT_BYTES = NEV * RV * 4;
   constexpr int VT_AT = KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
   // Prefetch ring: per wave, D slots of one 32-token block each, filled by direct
   // global -> LDS copies in the lane order the block is read back in: key codes (two
@@ -580,6 +615,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   const int cgrp = NG == 4 ? (col >> 2) : 0;
   const int chl = NG == 4 ? (col & 3) : (col & 7);
   const bool colok = chl < u.hs && (NG == 4 || col < 8);
+  // columns that carry no live head get p = 0: their value products multiply zeros
+  const float cdead = colok ? 0.f : -INFINITY;
 
   // ---- token range and the first two blocks' loads, issued before the prologue
   int lo, hi;
@@ -647,16 +684,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
 
   // ---- decode tables
   if (tid < 16) {
-    const float c = a.kcent[tid];
-    const _Float16 h = (_Float16)c;
-    cbk[tid] = f16_bits(h) | (f16_bits((_Float16)(c - (float)h)) << 16);
+    cbk[tid] = f16_bits((_Float16)(a.kcent[tid] * a.kscale));
     cbv[tid] = f16_bits((_Float16)a.vcent[tid]);
   }
   __syncthreads();
   for (int i = tid; i < NEK * RK; i += 256) {
     const int e = i / RK;
-    const uint32_t c0 = cbk[e & ((1 << BK) - 1)], c1 = cbk[e >> BK];
-    ((uint2*)pool)[i] = make_uint2((c0 & 0xFFFFu) | (c1 << 16), (c0 >> 16) | (c1 & 0xFFFF0000u));
+    ((uint32_t*)pool)[i] = cbk[e & ((1 << BK) - 1)] | (cbk[e >> BK] << 16);
   }
   for (int i = tid; i < NEV * RV; i += 256) {
     const int e = i / RV;
@@ -667,7 +701,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   float mx = 0.f;
   {
     float4 r = query_rotate(qlane, a.so4 != nullptr, a.rot_group, lane);
-    r.x *= a.scale_log2; r.y *= a.scale_log2; r.z *= a.scale_log2; r.w *= a.scale_log2;
+    const float qsc = a.scale_log2 / a.kscale;
+    r.x *= qsc; r.y *= qsc; r.z *= qsc; r.w *= qsc;
     if (qlane.live) {
       *(float4*)(qbuf + (2 * wv + (lane >> 5)) * kHeadDim + 4 * (lane & 31)) = r;
       mx = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
@@ -682,30 +717,27 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   if (mx > 0.f && mx < INFINITY) (void)frexpf(mx, &ex);
   const float qs = ldexpf(1.f, 14 - ex), qinv = ldexpf(1.f, ex - 14);
 
-  // B operands.  Key operand f of lane group q holds codes of coordinates 32q + 4f + j
-  // (j = 0..3) in fp16 slots [hi j0, hi j1, lo j0, lo j1, hi j2, hi j3, lo j2, lo j3].
-  // "hi" columns see q_hi in every slot ((c_hi + c_lo) q_hi), "lo" columns see q_lo in the
-  // c_hi slots only (c_hi q_lo).
-  u32x4 B1[8], B2[8];
+  // B operands.  Key operand f of lane group q holds codes of coordinates 32q + 8f + j
+  // (j = 0..7); "hi" columns see q_hi, "lo" columns q_lo (whole-head groups), or every
+  // column sees q_hi in one product and q_lo in a second (32-groups).
+  u32x4 B1[4], B2[4];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    uint32_t hp[2], lp[2];
+  for (int f = 0; f < 4; ++f) {
+    u32x4 bh, bl;
     const int head = NG == 4 ? chl : (col & 7);
     const bool live = head < u.hs && (NG == 1 || cgrp == qg);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 4; ++p) {
       float x0 = 0.f, x1 = 0.f;
       if (live) {
-        const float* src = qbuf + head * kHeadDim + 32 * qg + 4 * f + 2 * p;
+        const float* src = qbuf + head * kHeadDim + 32 * qg + 8 * f + 2 * p;
         x0 = src[0] * qs;
         x1 = src[1] * qs;
       }
       const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      hp[p] = f16_bits(h0) | (f16_bits(h1) << 16);
-      lp[p] = f16_bits((_Float16)(x0 - (float)h0)) | (f16_bits((_Float16)(x1 - (float)h1)) << 16);
+      bh[p] = f16_bits(h0) | (f16_bits(h1) << 16);
+      bl[p] = f16_bits((_Float16)(x0 - (float)h0)) | (f16_bits((_Float16)(x1 - (float)h1)) << 16);
     }
-    const u32x4 bh = u32x4{hp[0], hp[0], hp[1], hp[1]};
-    const u32x4 bl = u32x4{lp[0], 0u, lp[1], 0u};
     if (SPLITQ) {
       B1[f] = col < 8 ? bh : bl;
     } else {
@@ -714,11 +746,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     }
   }
 
-  const uint32_t klane = (lane & (RK - 1)) << 3, vlane = VT_AT | ((lane & (RV - 1)) << 2);
+  const uint32_t klane = (lane & (RK - 1)) << 2, vlane = VT_AT | ((lane & (RV - 1)) << 2);
   auto key_operand = [&](const uint32_t* kk, int f) {
-    const uint2 x0 = lds_at<uint2>(ktab, pair_lds_addr<BK, SHK>(kk, 4 * BK * f, klane));
-    const uint2 x1 = lds_at<uint2>(ktab, pair_lds_addr<BK, SHK>(kk, 4 * BK * f + 2 * BK, klane));
-    return u32x4{x0.x, x0.y, x1.x, x1.y};
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = lds_at<uint32_t>(ktab, pair_lds_addr<BK, SHK>(kk, 8 * BK * f + 2 * BK * i, klane));
+    return r;
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -731,21 +764,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     // Table reads are issued in batches ahead of their consumers so that LDS latency
     // overlaps matrix-core and vector work: all key operands of tile 0, then tile 1's
     // while tile 0 multiplies, then every value operand before the softmax arithmetic.
-    u32x4 ka[8], kb[8];
+    u32x4 ka[4], kb[4];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) ka[f] = key_operand(cb.k0, f);
+    for (int f = 0; f < 4; ++f) ka[f] = key_operand(cb.k0, f);
     f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
+    for (int f = 0; f < 4; ++f) {
       kb[f] = key_operand(cb.k1, f);
       D0 = mfma16(ka[f], B1[f], D0);
       if (!SPLITQ) D0 = mfma16(ka[f], B2[f], D0);
     }
     u32x4 va[8];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
+    for (int f = 0; f < 4; ++f) {
       D1 = mfma16(kb[f], B1[f], D1);
       if (!SPLITQ) D1 = mfma16(kb[f], B2[f], D1);
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) va[f][j] = lds_at<uint32_t>(pool, pair_lds_addr<BV, SHV>(cb.v, 8 * BV * f + 2 * BV * j, vlane));
     }
@@ -789,7 +825,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
       l_run *= al;
       m_run = mnew;
     }
-    const float nmq = m_run == -INFINITY ? 0.f : -m_run * qinv;
+    const float nmq = (m_run == -INFINITY ? 0.f : -m_run * qinv) + cdead;
     float p[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -1010,9 +1046,33 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
 // Log-sum-exp merge of key-axis splits plus the single inverse rotation.  One workgroup
 // per (sequence, query head): the split weights are formed once in LDS, then every thread
 // (coordinate) sums its column over the splits with independent, unrolled loads.
+// Inverse of query_rotate for one head held by 32 lanes (4 coordinates each): SO(4)
+// inverse, the (self-inverse) normalised Hadamard, then the sign flips.
+__device__ __forceinline__ float4 unrotate4(float4 x, const QueryLane& s, bool so4, int group, int lane) {
+  Quat v{x.x, x.y, x.z, x.w};
+  if (so4) v = qmul(qmul(qconj(s.l), v), s.r);
+  float x0 = v.w, x1 = v.x, x2 = v.y, x3 = v.z;
+  float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
+  x0 = y0 + y2; x1 = y1 + y3; x2 = y0 - y2; x3 = y1 - y3;
+  for (int m = 1; m < group / 4; m <<= 1) {
+    const bool up = (lane & m) != 0;
+    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    x0 = up ? o0 - x0 : x0 + o0;
+    x1 = up ? o1 - x1 : x1 + o1;
+    x2 = up ? o2 - x2 : x2 + o2;
+    x3 = up ? o3 - x3 : x3 + o3;
+  }
+  const float hsc = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  return make_float4(x0 * hsc * s.sg.x, x1 * hsc * s.sg.y, x2 * hsc * s.sg.z, x3 * hsc * s.sg.w);
+}
+
+// Log-sum-exp merge of the split partials of one (sequence, query head) and the single
+// inverse rotation.  Every global read that does not depend on another is issued first:
+// the section lse values, the first partials, the signs and SO(4) parameters.
 __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   constexpr int kMaxStage = 1024;
-  __shared__ float obuf[kHeadDim];
+  constexpr int kAhead = 16;  // partials held in registers ahead of the weights
+  __shared__ __attribute__((aligned(16))) float obuf[kHeadDim];
   __shared__ float wts[kMaxStage];
   __shared__ float red[2][2];
   const int row = blockIdx.x;  // b * n_q_heads + h
@@ -1020,19 +1080,37 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   const int kv = h / a.group_size;
   const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   const size_t stride = (size_t)a.batch * a.n_q_heads;
-  // pass 1: maximum lse
-  float M = -INFINITY;
-  for (int s = c; s < a.n_splits; s += 128) M = fmaxf(M, a.part_lse[s * stride + row]);
+  const int S = a.n_splits;
+  const float* po = a.part_o + (size_t)row * kHeadDim + c;
+
+  float lse0 = c < S ? a.part_lse[c * stride + row] : -INFINITY;
+  float ahead[kAhead];
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j) ahead[j] = j < S ? po[j * stride * kHeadDim] : 0.f;
+  QueryLane rl;
+  rl.live = wv == 0 && lane < 32;
+  rl.sg = make_float4(1.f, 1.f, 1.f, 1.f);
+  rl.l = rl.r = Quat{1.f, 0.f, 0.f, 0.f};
+  if (rl.live) {
+    rl.sg = *(const float4*)(a.signs + kv * kHeadDim + 4 * lane);
+    if (a.so4) {
+      rl.l = qload(a.so4 + kv * 256 + 8 * lane);
+      rl.r = qload(a.so4 + kv * 256 + 8 * lane + 4);
+    }
+  }
+
+  // maximum lse, then the weights e^{lse_s - max} (in LDS when they fit) and their sum
+  float M = lse0;
+  for (int s = c + 128; s < S; s += 128) M = fmaxf(M, a.part_lse[s * stride + row]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[0][wv] = M;
   __syncthreads();
   M = fmaxf(red[0][0], red[0][1]);
   const float mu = M == -INFINITY ? 0.f : M;
-  // pass 2: weights e^{lse_s - max} (kept in LDS when they fit) and their sum
   float W = 0.f;
-  for (int s = c; s < a.n_splits; s += 128) {
-    const float l = a.part_lse[s * stride + row];
+  for (int s = c; s < S; s += 128) {
+    const float l = s == c ? lse0 : a.part_lse[s * stride + row];
     const float w = l == -INFINITY ? 0.f : expf(l - mu);
     if (s < kMaxStage) wts[s] = w;
     W += w;
@@ -1042,26 +1120,32 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   if (lane == 0) red[1][wv] = W;
   __syncthreads();
   W = red[1][0] + red[1][1];
-  // pass 3: weighted sum of the partials
+
+  // weighted sum of the partials
   float acc = 0.f;
-  const float* po = a.part_o + (size_t)row * kHeadDim + c;
-  int s = 0;
-  for (; s + 8 <= a.n_splits && s + 8 <= kMaxStage; s += 8) {
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (j < S) acc = fmaf(wts[j], ahead[j], acc);
+  int s = kAhead;
+  for (; s + 8 <= S && s + 8 <= kMaxStage; s += 8) {
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = po[(s + j) * stride * kHeadDim];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + j], v[j], acc);
   }
-  for (; s < a.n_splits; ++s) {
+  for (; s < S; ++s) {
     const float l = a.part_lse[s * stride + row];
     const float w = s < kMaxStage ? wts[s] : (l == -INFINITY ? 0.f : expf(l - mu));
     acc = fmaf(w, po[s * stride * kHeadDim], acc);
   }
   obuf[c] = W > 0.f ? acc / W : 0.f;
   __syncthreads();
-  lds_rotate<false>(obuf, 1, a.signs + kv * kHeadDim, a.so4 ? a.so4 + kv * 256 : nullptr, a.rot_group);
-  a.out[(size_t)row * kHeadDim + c] = obuf[c];
+  if (wv == 0) {  // the whole first wave takes part in the lane exchanges
+    const float4 x = *(const float4*)(obuf + 4 * (lane & 31));
+    const float4 y = unrotate4(x, rl, a.so4 != nullptr, a.rot_group, lane);
+    if (rl.live) *(float4*)(a.out + (size_t)row * kHeadDim + 4 * lane) = y;
+  }
   if (a.lse_out && c == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;
 }
 
@@ -1084,6 +1168,23 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
 #undef TQ_APPEND_V
 #undef TQ_APPEND_X
 #undef TQ_APPEND
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits_k, int bits_v, int group, bool x_f16,
+                            int batch, int n_tiles, hipStream_t stream) {
+  const dim3 grid(n_tiles, ak.n_kv_heads, 2 * batch), block(128);
+#define TQ_APPEND_KV(BK, BV, G, X)                                                              \
+  if (bits_k == BK && bits_v == BV && group == G && x_f16 == X) {                              \
+    hipLaunchKernelGGL((append_kv_kernel<BK, BV, G, X>), grid, block, 0, stream, ak, av, batch); \
+    return hipGetLastError();                                                                  \
+  }
+#define TQ_APPEND_KV_X(BK, BV, G) TQ_APPEND_KV(BK, BV, G, true) TQ_APPEND_KV(BK, BV, G, false)
+#define TQ_APPEND_KV_G(BK, BV) TQ_APPEND_KV_X(BK, BV, 32) TQ_APPEND_KV_X(BK, BV, 128)
+  TQ_APPEND_KV_G(3, 3) TQ_APPEND_KV_G(4, 3) TQ_APPEND_KV_G(3, 4) TQ_APPEND_KV_G(4, 4)
+#undef TQ_APPEND_KV_G
+#undef TQ_APPEND_KV_X
+#undef TQ_APPEND_KV
   return hipErrorInvalidValue;
 }
 

@@ -67,8 +67,8 @@ typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
 typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
 
 /* Decode schedules.  MFMA: scores and value sum as matrix-core products of fp16
- * operands with fp32 accumulation (key codebook and query split into two fp16 parts so
- * scores keep fp32-level accuracy).  VEC: plain fp32 vector arithmetic, token-parallel
+ * operands with fp32 accumulation (the key codebook scaled to be nearly fp16-exact, see
+ * tq_codebook.f16_scale, and the query split into two fp16 parts).  VEC: plain fp32 vector arithmetic, token-parallel
  * scores and dimension-parallel value sum.  AUTO picks MFMA whenever it applies. */
 typedef enum { TQ_SCHEDULE_AUTO = 0, TQ_SCHEDULE_VEC = 1, TQ_SCHEDULE_MFMA = 2 } tq_schedule;
 
@@ -81,13 +81,18 @@ const char* tq_status_string(tq_status s);
  * Computed on the host in double precision (Gauss-Legendre quadrature of the cell
  * masses, closed-form first moments) and stored rounded to float.
  * centroid[0 .. 2^bits-1] ascending; boundary[k] = (centroid[k] + centroid[k+1]) / 2 for
- * k < 2^bits - 1; unused entries are 0.  Host-only; no device work.
+ * k < 2^bits - 1; unused entries are 0.  f16_scale is the s in [1, 2) (searched on a 2^-16
+ * grid) at which every s * centroid[k] is nearest to an fp16 number in relative terms
+ * (worst level: 2.6e-5 for 3-bit, 9e-5 for 4-bit codebooks of the supported groups, against
+ * up to 3.2e-4 at s = 1); the matrix-core decode holds the key codebook as fp16(s * c) and
+ * divides the query by s.  Host-only; no device work.
  * Errors: TQ_EINVAL if out == NULL; TQ_EUNSUPPORTED unless bits is 3 or 4 and dim >= 3. */
 typedef struct {
   int32_t bits;
   int32_t dim;
   float centroid[16];
   float boundary[15];
+  float f16_scale;
 } tq_codebook;
 
 tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* out);
@@ -129,6 +134,16 @@ typedef struct {
 tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x,
                              tq_dtype x_dtype, int32_t n_new, const int32_t* pos, int32_t pos0,
                              int32_t max_pos, void* stream);
+
+/* The keys and the values of one step in one launch: the same result, bit for bit, as
+ * tq_quantize_append(keys, xk) followed by tq_quantize_append(values, xv) with the same
+ * n_new, pos, pos0 and max_pos ("TurboQuant ...", 3.3: K and V are quantised on write).
+ * keys must have role TQ_KEYS and values TQ_VALUES, with equal batch; xk and xv are
+ * device [batch][n_kv_heads][n_new][128] of x_dtype.  Errors as tq_quantize_append,
+ * checked for both caches before anything is launched. */
+tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                const void* xk, const void* xv, tq_dtype x_dtype, int32_t n_new,
+                                const int32_t* pos, int32_t pos0, int32_t max_pos, void* stream);
 
 /* One decode step of attention for every query head against the packed cache.
  *   q:        device [batch][n_q_heads][128] of q_dtype; query head h reads KV head

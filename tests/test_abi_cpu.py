@@ -48,6 +48,22 @@ def test_host_codebook_matches_oracle(lib, bits, dim):
     assert all(cb.centroid[k] == 0.0 for k in range(1 << bits, 16))
 
 
+@pytest.mark.parametrize("bits,dim", [(3, 32), (4, 32), (3, 128), (4, 128)])
+def test_codebook_fp16_scale(lib, bits, dim):
+    # the key codebook scaled by f16_scale is within the stated relative distance of fp16
+    # numbers (checked with numpy's own fp16 rounding), and the scale beats no scaling
+    cb = tq.make_codebook(bits, dim)
+    s = np.float32(cb.f16_scale)
+    assert 1.0 <= s < 2.0
+    c = np.array(cb.centroids, dtype=np.float32)
+    c = c[c != 0]
+    def worst(scale):
+        v = (np.float32(scale) * c).astype(np.float32)
+        return float(np.max(np.abs(v.astype(np.float16).astype(np.float32) - v) / np.abs(v)))
+    assert worst(s) <= (3e-5 if bits == 3 else 1e-4)
+    assert worst(s) < worst(1.0)
+
+
 def test_codebook_errors(lib):
     cb = tq.Codebook()
     assert lib.tq_make_codebook(2, 32, ctypes.byref(cb)) == TQ_EUNSUPPORTED
@@ -94,9 +110,33 @@ def test_append_validation(lib):
     bad = make_cache(tq.TQ_KEYS)
     bad.bits = 2
     assert append(rot, bad) == TQ_EUNSUPPORTED
+    bad = make_cache(tq.TQ_KEYS)
+    bad.codebook.f16_scale = 0.0
+    assert append(rot, bad) == TQ_EINVAL                           # codebook not from tq_make_codebook
     nulls = make_rot()
     nulls.signs = None
     assert append(nulls, k) == TQ_EINVAL
+
+
+def append_kv(rot, k, v, n_new=4, pos=None, pos0=0, max_pos=0, xk=FAKE, xv=FAKE, dtype=1):
+    return tq.library().tq_quantize_append_kv(ctypes.byref(rot), ctypes.byref(k), ctypes.byref(v), xk, xv, dtype,
+                                              n_new, pos, pos0, max_pos, None)
+
+
+def test_append_kv_validation(lib):
+    rot = make_rot()
+    k, v = make_cache(tq.TQ_KEYS), make_cache(tq.TQ_VALUES, bits=4)
+    assert append_kv(rot, k, v, n_new=0) == TQ_OK
+    assert append_kv(rot, k, v, n_new=65) == TQ_ECAPACITY
+    assert append_kv(rot, k, v, pos=FAKE, max_pos=61) == TQ_ECAPACITY
+    assert append_kv(rot, v, k) == TQ_EINVAL                       # roles swapped
+    assert append_kv(rot, k, k) == TQ_EINVAL
+    assert append_kv(rot, k, v, xk=None) == TQ_EINVAL
+    assert append_kv(rot, k, v, xv=None) == TQ_EINVAL
+    assert append_kv(rot, k, make_cache(tq.TQ_VALUES, batch=2)) == TQ_EINVAL   # batch mismatch
+    assert append_kv(rot, k, make_cache(tq.TQ_VALUES, capacity=32), n_new=40) == TQ_ECAPACITY  # values only
+    assert append_kv(rot, k, make_cache(tq.TQ_VALUES, group=128)) == TQ_EINVAL  # group mismatch
+    assert append_kv(make_rot(heads=3), k, v) == TQ_EINVAL
 
 
 def decode(rot, k, v, n_q_heads=4, max_len=10, n_splits=1, out=FAKE, part=FAKE, sched=0, scale=0.1):

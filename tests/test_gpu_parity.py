@@ -112,6 +112,38 @@ def test_append_incremental_and_device_positions():
         assert not idx[:, :, t:].any()
 
 
+@pytest.mark.parametrize("name", ["batched", "isoquant32k", "tiny"])
+def test_fused_append_equals_separate_calls(name):
+    # one launch for keys and values gives the two separate calls' bytes exactly: a prefill
+    # into a fresh cache, then single-token steps and a partial-tile chunk at device positions
+    w, inp = setup(name, seed=7, seq_len=70, batch=2)
+    t = w.seq_len
+    cap = 128
+    rot = device_rotation(w, inp)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    k1, v1 = empty_caches(w, cap)
+    k2, v2 = empty_caches(w, cap)
+    p1 = 37
+    tq.quantize_append(rot, k1, kx[:, :, :p1].contiguous())
+    tq.quantize_append(rot, v1, vx[:, :, :p1].contiguous())
+    tq.quantize_append_kv(rot, k2, v2, kx[:, :, :p1].contiguous(), vx[:, :, :p1].contiguous())
+    for s in range(p1, 41):
+        xs, ys = kx[:, :, s:s + 1].contiguous(), vx[:, :, s:s + 1].contiguous()
+        tq.quantize_append(rot, k1, xs, pos0=s)
+        tq.quantize_append(rot, v1, ys, pos0=s)
+        tq.quantize_append_kv(rot, k2, v2, xs, ys, pos0=s)
+    pos = torch.full((w.batch,), 41, dtype=torch.int32, device="cuda")
+    xs, ys = kx[:, :, 41:t].contiguous(), vx[:, :, 41:t].contiguous()
+    tq.quantize_append(rot, k1, xs, pos=pos)
+    tq.quantize_append(rot, v1, ys, pos=pos)
+    tq.quantize_append_kv(rot, k2, v2, xs, ys, pos=pos)
+    torch.cuda.synchronize()
+    for a, b in ((k1, k2), (v1, v2)):
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.norms, b.norms)
+    idx, n = download(v2, "v")
+    check_codes(idx, n, oracle_quantize(w, inp, "v"), t)
+
+
 @pytest.mark.parametrize("schedule", ["mfma", "vec"])
 @pytest.mark.parametrize("n_splits", [1, 3])
 @pytest.mark.parametrize("name", list(CASES))
