@@ -362,6 +362,129 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
   append_tile<BITS, GROUP, VALUES, XF16>(a, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
+// One new token per (sequence, KV head), keys and values together: one wave per stream,
+// lanes 0-31 quantise the key and lanes 32-63 the value, lane l & 31 holding coordinates
+// 4(l & 31) .. +3 (one SO(4) block).  Same steps as append_tile (norm, signs, normalised
+// Hadamard with the first two stages in-lane and the rest by lane exchange, SO(4), count
+// of boundaries below, pack); the group norm is summed in another order, so results may
+// differ from append_tile in the last bit of a norm.  Value codes are merged byte by byte:
+// every byte a lane writes belongs to its own words.
+template <int BK, int BV, int GROUP, bool XF16>
+__global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, const AppendArgs av, int batch) {
+  constexpr int NG = kHeadDim / GROUP;
+  const int lane = threadIdx.x & 63;
+  const int st = blockIdx.x * 4 + (threadIdx.x >> 6);  // stream = b * n_kv_heads + kv
+  if (st >= batch * ak.n_kv_heads) return;            // whole waves only
+  const bool val = lane >= 32;
+  const AppendArgs& a = val ? av : ak;
+  const int bits = val ? BV : BK;
+  const int b = st / ak.n_kv_heads, kv = st - b * ak.n_kv_heads;
+  const int pb = lane & 31;
+  const int slot = a.pos ? a.pos[b] : a.pos0;
+  const int ntile = a.capacity / kTile;
+  const int t = slot & (kTile - 1);
+
+  // global reads first: the vector, signs, SO(4) block, and the value bytes to be merged
+  float4 x;
+  const size_t xi = (size_t)st * kHeadDim + 4 * pb;  // n_new == 1
+  if (XF16) {
+    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+    const h4_t h = *(const h4_t*)((const _Float16*)a.x + xi);
+    x = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+  } else {
+    x = *(const float4*)((const float*)a.x + xi);
+  }
+  const float4 sg = *(const float4*)(a.signs + kv * kHeadDim + 4 * pb);
+  Quat ql{1.f, 0.f, 0.f, 0.f}, qr{1.f, 0.f, 0.f, 0.f};
+  if (a.so4) {
+    ql = qload(a.so4 + ((size_t)kv * 32 + pb) * 8);
+    qr = qload(a.so4 + ((size_t)kv * 32 + pb) * 8 + 4);
+  }
+  // value word of coordinate i = 16u + m for tile token t = 16h + 4q + r: (q*16 + m)*8 + u,
+  // field 4h + r; 3-bit words are 3 bytes, 4-bit words 4 bytes
+  const int q = (t >> 2) & 3, fk = 4 * (t >> 4) + (t & 3);
+  uint8_t* vtile = av.codes + ((size_t)st * ntile + slot / kTile) * (kTile * 16 * BV);
+  uint8_t vold[4][2];
+  int vbyte[4];
+  if (val) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * pb + j, u = i >> 4, m = i & 15;
+      const int w = (q * 16 + m) * 8 + u;
+      vbyte[j] = w * BV + (BV * fk) / 8;
+      vold[j][0] = vtile[vbyte[j]];
+      vold[j][1] = (BV == 3 && (BV * fk) % 8 > 5) ? vtile[vbyte[j] + 1] : 0;
+    }
+  }
+
+  // norm of the group (lanes of one group: GROUP / 4 consecutive lanes of the half)
+  float x0 = x.x * sg.x, x1 = x.y * sg.y, x2 = x.z * sg.z, x3 = x.w * sg.w;
+  float ss = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+#pragma unroll
+  for (int m = 1; m < GROUP / 4; m <<= 1) ss += __shfl_xor(ss, m);
+  const float nrm = sqrtf(ss);
+  const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
+  x0 *= inv; x1 *= inv; x2 *= inv; x3 *= inv;
+  // normalised Hadamard on each GROUP-block, then SO(4)
+  float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
+  x0 = y0 + y2; x1 = y1 + y3; x2 = y0 - y2; x3 = y1 - y3;
+#pragma unroll
+  for (int m = 1; m < GROUP / 4; m <<= 1) {
+    const bool up = (lane & m) != 0;
+    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    x0 = up ? o0 - x0 : x0 + o0;
+    x1 = up ? o1 - x1 : x1 + o1;
+    x2 = up ? o2 - x2 : x2 + o2;
+    x3 = up ? o3 - x3 : x3 + o3;
+  }
+  const float hsc = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  Quat v{x0 * hsc, x1 * hsc, x2 * hsc, x3 * hsc};
+  if (a.so4) v = qmul(qmul(ql, v), qconj(qr));
+  const float yv[4] = {v.w, v.x, v.y, v.z};
+  uint32_t code[4];
+  const int nb = (1 << bits) - 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t c = 0;
+    for (int k = 0; k < nb; ++k) c += yv[j] > a.boundary[k] ? 1u : 0u;
+    code[j] = c;
+  }
+
+  // norms: one lane per group
+  if ((pb & (GROUP / 4 - 1)) == 0) {
+    const int grp = (4 * pb) / GROUP;
+    a.norms[((size_t)st * ntile + slot / kTile) * (NG * kTile) + grp * kTile + norm_pos(t)] = nrm;
+  }
+  if (!val) {
+    // key record: word w = coordinates 8w..8w+7 = lanes 2w (low half) and 2w + 1
+    const uint32_t half = BK == 3 ? (code[0] | code[1] << 3 | code[2] << 6 | code[3] << 9)
+                                  : (code[0] | code[1] << 4 | code[2] << 8 | code[3] << 12);
+    const uint32_t other = __shfl_xor(half, 1);
+    uint8_t* rec = a.codes + ((size_t)st * a.capacity + slot) * (16 * BK);
+    if ((pb & 1) == 0) {
+      const int w = pb >> 1;
+      if (BK == 3) {
+        const uint32_t word = half | (other << 12);
+        rec[3 * w] = (uint8_t)word;
+        rec[3 * w + 1] = (uint8_t)(word >> 8);
+        rec[3 * w + 2] = (uint8_t)(word >> 16);
+      } else {
+        *(uint32_t*)(rec + 4 * w) = half | (other << 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sh = (BV * fk) % 8;
+      const uint32_t fmask = ((1u << BV) - 1u) << sh, fval = code[j] << sh;
+      const uint32_t cur = vold[j][0] | ((uint32_t)vold[j][1] << 8);
+      const uint32_t nw = (cur & ~fmask) | fval;
+      vtile[vbyte[j]] = (uint8_t)nw;
+      if (BV == 3 && sh > 5) vtile[vbyte[j] + 1] = (uint8_t)(nw >> 8);
+    }
+  }
+}
+
 // Keys and values of one step in one launch: grid z covers the keys' sequences, then the
 // values' (same tiles, same rotation).
 template <int BK, int BV, int GROUP, bool XF16>
@@ -1173,6 +1296,21 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
 
 hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits_k, int bits_v, int group, bool x_f16,
                             int batch, int n_tiles, hipStream_t stream) {
+  if (ak.n_new == 1) {
+    const dim3 grid((batch * ak.n_kv_heads + 3) / 4), block(256);
+#define TQ_STEP(BK, BV, G, X)                                                                    \
+  if (bits_k == BK && bits_v == BV && group == G && x_f16 == X) {                                \
+    hipLaunchKernelGGL((append_step_kernel<BK, BV, G, X>), grid, block, 0, stream, ak, av, batch); \
+    return hipGetLastError();                                                                    \
+  }
+#define TQ_STEP_X(BK, BV, G) TQ_STEP(BK, BV, G, true) TQ_STEP(BK, BV, G, false)
+#define TQ_STEP_G(BK, BV) TQ_STEP_X(BK, BV, 32) TQ_STEP_X(BK, BV, 128)
+    TQ_STEP_G(3, 3) TQ_STEP_G(4, 3) TQ_STEP_G(3, 4) TQ_STEP_G(4, 4)
+#undef TQ_STEP_G
+#undef TQ_STEP_X
+#undef TQ_STEP
+    return hipErrorInvalidValue;
+  }
   const dim3 grid(n_tiles, ak.n_kv_heads, 2 * batch), block(128);
 #define TQ_APPEND_KV(BK, BV, G, X)                                                              \
   if (bits_k == BK && bits_v == BV && group == G && x_f16 == X) {                              \

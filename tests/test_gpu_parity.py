@@ -114,10 +114,9 @@ def test_append_incremental_and_device_positions():
 
 @pytest.mark.parametrize("name", ["batched", "isoquant32k", "tiny"])
 def test_fused_append_equals_separate_calls(name):
-    # one launch for keys and values gives the two separate calls' bytes exactly: a prefill
-    # into a fresh cache, then single-token steps and a partial-tile chunk at device positions
+    # multi-token appends in one launch give the two separate calls' bytes exactly: a
+    # prefill into a fresh cache, then a partial-tile chunk at per-row device positions
     w, inp = setup(name, seed=7, seq_len=70, batch=2)
-    t = w.seq_len
     cap = 128
     rot = device_rotation(w, inp)
     kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
@@ -127,21 +126,41 @@ def test_fused_append_equals_separate_calls(name):
     tq.quantize_append(rot, k1, kx[:, :, :p1].contiguous())
     tq.quantize_append(rot, v1, vx[:, :, :p1].contiguous())
     tq.quantize_append_kv(rot, k2, v2, kx[:, :, :p1].contiguous(), vx[:, :, :p1].contiguous())
-    for s in range(p1, 41):
-        xs, ys = kx[:, :, s:s + 1].contiguous(), vx[:, :, s:s + 1].contiguous()
-        tq.quantize_append(rot, k1, xs, pos0=s)
-        tq.quantize_append(rot, v1, ys, pos0=s)
-        tq.quantize_append_kv(rot, k2, v2, xs, ys, pos0=s)
-    pos = torch.full((w.batch,), 41, dtype=torch.int32, device="cuda")
-    xs, ys = kx[:, :, 41:t].contiguous(), vx[:, :, 41:t].contiguous()
+    pos = torch.full((w.batch,), p1, dtype=torch.int32, device="cuda")
+    xs, ys = kx[:, :, p1:].contiguous(), vx[:, :, p1:].contiguous()
     tq.quantize_append(rot, k1, xs, pos=pos)
     tq.quantize_append(rot, v1, ys, pos=pos)
     tq.quantize_append_kv(rot, k2, v2, xs, ys, pos=pos)
     torch.cuda.synchronize()
     for a, b in ((k1, k2), (v1, v2)):
         assert torch.equal(a.codes, b.codes) and torch.equal(a.norms, b.norms)
-    idx, n = download(v2, "v")
-    check_codes(idx, n, oracle_quantize(w, inp, "v"), t)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_single_token_steps_match_oracle(name):
+    # a prefill, then one-token steps through the fused call (its single-token kernel) at
+    # host and at device positions, across a tile boundary; neighbours in shared value words
+    # must survive every step
+    w, inp = setup(name, seed=8, seq_len=70, batch=2)
+    t = w.seq_len
+    cap = 96
+    rot = device_rotation(w, inp)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    k, v = empty_caches(w, cap)
+    p1 = 29
+    tq.quantize_append_kv(rot, k, v, kx[:, :, :p1].contiguous(), vx[:, :, :p1].contiguous())
+    for s in range(p1, t):
+        xs, ys = kx[:, :, s:s + 1].contiguous(), vx[:, :, s:s + 1].contiguous()
+        if s % 2:
+            tq.quantize_append_kv(rot, k, v, xs, ys, pos0=s)
+        else:
+            pos = torch.full((w.batch,), s, dtype=torch.int32, device="cuda")
+            tq.quantize_append_kv(rot, k, v, xs, ys, pos=pos, max_pos=s)
+    torch.cuda.synchronize()
+    for role, cache in (("k", k), ("v", v)):
+        idx, n = download(cache, role)
+        check_codes(idx, n, oracle_quantize(w, inp, role), t)
+        assert not idx[:, :, t:].any() and not n[:, :, t:].any()
 
 
 @pytest.mark.parametrize("schedule", ["mfma", "vec"])

@@ -44,12 +44,12 @@ class Workload:
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 1, 256, 3, 3, 32, False, "float32", "fixed2x10"),
-    "gqa8k": Workload("gqa8k", 1, 32, 8, 8192, 3, 3, 32, False, "float16", "seeded4x8", n_splits=16),
-    "batched": Workload("batched", 32, 32, 8, 4096, 4, 3, 32, False, "float16", "seeded4x8"),
+    "gqa8k": Workload("gqa8k", 1, 32, 8, 8192, 3, 3, 32, False, "float16", "seeded4x8", n_splits=32),
+    "batched": Workload("batched", 32, 32, 8, 4096, 4, 3, 32, False, "float16", "seeded4x8", n_splits=2),
     "long128k": Workload("long128k", 1, 16, 2, 131072, 3, 3, 32, False, "float16", "lognormal",
                          n_splits=64),
     "isoquant32k": Workload("isoquant32k", 8, 32, 8, 32768, 3, 3, 128, True, "float16", "seeded4x8",
-                            n_splits=4),
+                            n_splits=8),
 }
 
 
