@@ -148,7 +148,10 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
     a.kcent[k] = keys->codebook.centroid[k];
     a.vcent[k] = values->codebook.centroid[k];
   }
-  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, (hipStream_t)stream));
+  // one shared four-code table when keys and values are 3-bit with the same codebook
+  bool same = keys->bits == 3 && values->bits == 3 && keys->codebook.f16_scale == values->codebook.f16_scale;
+  for (int k = 0; k < 8 && same; ++k) same = keys->codebook.centroid[k] == values->codebook.centroid[k];
+  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,

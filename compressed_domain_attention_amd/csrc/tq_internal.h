@@ -48,7 +48,8 @@ struct DecodeArgs {
   int32_t capacity;
   int32_t rot_group;        // 32 or 128
   float scale_log2;         // softmax scale * log2(e)
-  float kscale;             // key codebook scale making every level nearly fp16-exact
+  float kscale;             // key codebook scale making every level nearly fp16-exact (also
+                            // the value scale when keys and values share one table)
   float kcent[16];
   float vcent[16];
 };
@@ -74,7 +75,8 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
 hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits_k, int bits_v, int group, bool x_f16,
                             int batch, int n_tiles, hipStream_t stream);
 // schedule: 1 = vector (fp32), 2 = matrix cores
-hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
+// shared_table: 3-bit keys and values with identical codebooks (one four-code table)
+hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

@@ -616,6 +616,15 @@ __device__ __forceinline__ uint32_t pair_lds_addr(const uint32_t* d, int off, ui
   return (x & mask) | lane_off;
 }
 
+__device__ __forceinline__ uint32_t quad_lds_addr(const uint32_t* d, int off) {
+  const int wi = off >> 5, sh = off & 31;
+  uint32_t x;
+  if (sh + 12 > 32) x = __builtin_amdgcn_alignbit(d[wi + 1], d[wi], sh - 3);
+  else if (sh >= 3) x = d[wi] >> (sh - 3);
+  else x = d[wi] << (3 - sh);
+  return x & (0xFFFu << 3);
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_at(const uint8_t* base, uint32_t byte_off) {
   return *(const T*)(base + byte_off);
@@ -690,7 +699,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int BK, int BV, int NG, bool QF16>
+template <int BK, int BV, int NG, bool QF16, bool QUAD>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NW = 4;
   // whole-head groups: the query's hi and lo parts take separate columns (8 + 8), so one
@@ -701,13 +710,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   constexpr int NEV = BV == 3 ? 64 : 256;
   constexpr int KREC = 16 * BK;
   constexpr int VTILE = kTile * 16 * BV;
-  // Decode tables [entry][copies]: keys uint2 at 0, values uint32 at VT_AT (a power of two
+  // Decode tables.  3-bit keys and values with one codebook (QUAD) share one table indexed
+  // by four codes (12 bits, 4096 entries of four fp16 values, 32 KB): one read per four
+  // codes.  Otherwise two-code tables [entry][copies]: keys at 0, values at VT_AT (a power of two
   // no smaller than either table, so a value address is VT_AT | offset).  3-bit tables have
   // 32 copies (conflict-free); 4-bit tables have 8 (key) or 16 (value) copies to fit the
   // LDS budget of two workgroups per CU, at the price of occasional bank conflicts.
   constexpr int RK = BK == 3 ? 32 : 16, RV = BV == 3 ? 32 : 16;
   constexpr int SHK = BK == 3 ? 7 : 6, SHV = BV == 3 ? 7 : 6;  // log2 of an entry's row bytes
-  constexpr int KT_BYTES = NEK * RK * 4, VT_BYTES = NEV * RV * 4;
+  static_assert(!QUAD || (BK == 3 && BV == 3), "the four-code table holds 3-bit codes");
+  constexpr int KT_BYTES = QUAD ? 32768 : NEK * RK * 4, VT_BYTES = QUAD ? 0 : NEV * RV * 4;
   constexpr int VT_AT = KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
   // Prefetch ring: per wave, D slots of one 32-token block each, filled by direct
   // global -> LDS copies in the lane order the block is read back in: key codes (two
@@ -808,14 +820,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // ---- decode tables
   if (tid < 16) {
     cbk[tid] = f16_bits((_Float16)(a.kcent[tid] * a.kscale));
-    cbv[tid] = f16_bits((_Float16)a.vcent[tid]);
+    cbv[tid] = f16_bits((_Float16)(QUAD ? a.vcent[tid] * a.kscale : a.vcent[tid]));
   }
   __syncthreads();
-  for (int i = tid; i < NEK * RK; i += 256) {
-    const int e = i / RK;
-    ((uint32_t*)pool)[i] = cbk[e & ((1 << BK) - 1)] | (cbk[e >> BK] << 16);
+  if (QUAD) {
+    for (int e = tid; e < 4096; e += 256)
+      ((uint2*)pool)[e] = make_uint2(cbk[e & 7] | (cbk[(e >> 3) & 7] << 16), cbk[(e >> 6) & 7] | (cbk[e >> 9] << 16));
+  } else {
+    for (int i = tid; i < NEK * RK; i += 256) {
+      const int e = i / RK;
+      ((uint32_t*)pool)[i] = cbk[e & ((1 << BK) - 1)] | (cbk[e >> BK] << 16);
+    }
   }
-  for (int i = tid; i < NEV * RV; i += 256) {
+  for (int i = tid; i < (QUAD ? 0 : NEV * RV); i += 256) {
     const int e = i / RV;
     ((uint32_t*)(pool + VT_AT))[i] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
   }
@@ -872,6 +889,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   const uint32_t klane = (lane & (RK - 1)) << 2, vlane = VT_AT | ((lane & (RV - 1)) << 2);
   auto key_operand = [&](const uint32_t* kk, int f) {
     u32x4 r;
+    if (QUAD) {
+      const uint2 x0 = lds_at<uint2>(pool, quad_lds_addr(kk, 24 * f)), x1 = lds_at<uint2>(pool, quad_lds_addr(kk, 24 * f + 12));
+      return u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = lds_at<uint32_t>(ktab, pair_lds_addr<BK, SHK>(kk, 8 * BK * f + 2 * BK * i, klane));
     return r;
@@ -905,8 +926,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     }
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
+      if (QUAD) {
+        const uint2 x0 = lds_at<uint2>(pool, quad_lds_addr(cb.v, 24 * f)), x1 = lds_at<uint2>(pool, quad_lds_addr(cb.v, 24 * f + 12));
+        va[f] = u32x4{x0.x, x0.y, x1.x, x1.y};
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) va[f][j] = lds_at<uint32_t>(pool, pair_lds_addr<BV, SHV>(cb.v, 8 * BV * f + 2 * BV * j, vlane));
+        for (int j = 0; j < 4; ++j) va[f][j] = lds_at<uint32_t>(pool, pair_lds_addr<BV, SHV>(cb.v, 8 * BV * f + 2 * BV * j, vlane));
+      }
     }
     // raw scores (units of the prescaled query) of tokens 16h + 4q' + r, slot k = 4h + r
     float x[8];
@@ -1020,7 +1046,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
       L += sl[w * HPS + hl] * f;
       acc += so[(w * HPS + hl) * kHeadDim + c] * f;
     }
-    qbuf[i] = L > 0.f ? acc / L : 0.f;
+    qbuf[i] = L > 0.f ? (QUAD ? acc / (L * a.kscale) : acc / L) : 0.f;
     if (c == 0) lse2[hl] = L > 0.f ? M + __log2f(L) : -INFINITY;
   }
   __syncthreads();
@@ -1326,20 +1352,20 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16,
+hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream) {
   const int units = a.batch * a.n_kv_heads * a.n_splits * a.n_slices;
   const dim3 grid(units), block(256);
   const int ng = kHeadDim / a.rot_group;
   if (schedule == 2) {
-#define TQ_MF(BK, BV, NG, QF)                                                               \
-  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF) {                             \
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF>), grid, block, 0, stream, a);     \
-    return hipGetLastError();                                                               \
+#define TQ_MF(BK, BV, NG, QF, QD)                                                              \
+  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF && shared_table == QD) {          \
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD>), grid, block, 0, stream, a);    \
+    return hipGetLastError();                                                                  \
   }
-#define TQ_MF_Q(BK, BV, NG) TQ_MF(BK, BV, NG, true) TQ_MF(BK, BV, NG, false)
-#define TQ_MF_NG(BK, BV) TQ_MF_Q(BK, BV, 4) TQ_MF_Q(BK, BV, 1)
-    TQ_MF_NG(3, 3) TQ_MF_NG(4, 4) TQ_MF_NG(4, 3) TQ_MF_NG(3, 4)
+#define TQ_MF_Q(BK, BV, NG, QD) TQ_MF(BK, BV, NG, true, QD) TQ_MF(BK, BV, NG, false, QD)
+#define TQ_MF_NG(BK, BV, QD) TQ_MF_Q(BK, BV, 4, QD) TQ_MF_Q(BK, BV, 1, QD)
+    TQ_MF_NG(3, 3, true) TQ_MF_NG(3, 3, false) TQ_MF_NG(4, 4, false) TQ_MF_NG(4, 3, false) TQ_MF_NG(3, 4, false)
 #undef TQ_MF_NG
 #undef TQ_MF_Q
 #undef TQ_MF

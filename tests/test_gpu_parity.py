@@ -217,6 +217,29 @@ def test_decode_ragged_lengths_and_empty_rows(n_splits, schedule):
     np.testing.assert_allclose(lse[1:], ref_lse[1:], rtol=1e-4, atol=1e-4)
 
 
+@pytest.mark.parametrize("name", ["gqa8k", "isoquant32k"])
+def test_decode_with_distinct_value_codebook(name):
+    # 3-bit keys and values normally share one decode table; a value codebook that differs
+    # from the key codebook must take the separate-table kernel and still be right
+    w, inp = setup(name, seed=10, seq_len=96, batch=2)
+    t = w.seq_len
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, t)
+    cb = tq.make_codebook(w.bits_v, w.group)
+    for i in range(1 << w.bits_v):
+        cb.centroid[i] *= 1.01
+    v2 = tq.PackedCache(w.batch, w.n_kv_heads, t, w.bits_v, w.group, tq.TQ_VALUES, codes=v.codes, norms=v.norms,
+                        codebook=cb)
+    oqv2 = dict(oqv)
+    oqv2["centroids"] = np.asarray(oqv["centroids"]) * 1.01
+    q = torch.from_numpy(inp["q"]).cuda()
+    ref, _ = oracle_decode(w, inp, dequantized(w, inp, oqk), dequantized(w, inp, oqv2), np.full(w.batch, t))
+    for schedule in ("mfma", "vec"):
+        out, _ = tq.decode_attention(rot, k, v2, q, max_len=t, schedule=schedule)
+        torch.cuda.synchronize()
+        assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
+
+
 def test_schedules_agree_and_are_deterministic():
     w, inp = setup("gqa8k", seed=3, seq_len=300, batch=1)
     rot = device_rotation(w, inp)
