@@ -129,6 +129,36 @@ __device__ __forceinline__ QueryLane query_fetch(const float* signs, const float
   return s;
 }
 
+// The same lane values read back from LDS, where direct copies staged them: the raw
+// query rows of this wave's two heads at qraw (fp32 rows of 128, or fp16 rows packed), the
+// signs and then the SO(4) parameters at stage.
+template <bool QF16>
+__device__ __forceinline__ QueryLane query_staged(const uint8_t* qraw, const float* stage, bool so4, int hs, int wv,
+                                                 int lane) {
+  QueryLane s;
+  const int hl = 2 * wv + (lane >> 5), p = lane & 31;
+  s.live = hl < hs;
+  s.x = make_float4(0.f, 0.f, 0.f, 0.f);
+  s.sg = s.x;
+  s.l = s.r = Quat{1.f, 0.f, 0.f, 0.f};
+  if (s.live) {
+    const int i = (lane >> 5) * kHeadDim + 4 * p;
+    if (QF16) {
+      typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+      const h4_t h = *(const h4_t*)(qraw + 2 * i);
+      s.x = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+    } else {
+      s.x = *(const float4*)(qraw + 4 * i);
+    }
+    s.sg = *(const float4*)(stage + 4 * p);
+    if (so4) {
+      s.l = qload(stage + kHeadDim + 8 * p);
+      s.r = qload(stage + kHeadDim + 8 * p + 4);
+    }
+  }
+  return s;
+}
+
 __device__ __forceinline__ float4 query_rotate(const QueryLane& s, bool so4, int group, int lane) {
   float x0 = s.x.x * s.sg.x, x1 = s.x.y * s.sg.y, x2 = s.x.z * s.sg.z, x3 = s.x.w * s.sg.w;
   float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
@@ -633,7 +663,7 @@ __device__ __forceinline__ T lds_at(const uint8_t* base, uint32_t byte_off) {
 template <int BK, int BV>
 struct Block {
   uint32_t k0[BK], k1[BK];  // this lane's 32 key codes of tile tokens (lane&15) and 16+(lane&15)
-  f32x4 kn0, kn1;           // key norms of tokens 4q'+r and 16+4q'+r
+  f32x4 kn0, kn1;           // key norms of tokens 4q'+r and 16+4q'+r (folded: kn0 only, own tile)
   uint32_t v[2 * BV];       // this lane's 8 value words
   f32x4 vn0, vn1;           // value norms, same tokens as kn
 };
@@ -706,6 +736,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // product per key operand suffices; 32-groups: columns are (group, head), two products
   constexpr bool SPLITQ = NG == 1;
   constexpr int HPS = NG == 4 ? 4 : 8;
+  // With hi/lo columns, columns c and c + 8 see the same head.  The two 16-token tiles of a
+  // block are folded across that pair: after the hi + lo exchange, column c keeps tile 0's
+  // scores and column c + 8 tile 1's, so the softmax runs on 4 scores per lane instead of
+  // 8 duplicated ones.  Each column then carries its own running maximum and sum and its
+  // own value accumulator (a partial over its tile's tokens), merged in the epilogue.
+  constexpr bool FOLD = SPLITQ;
+  constexpr int NPART = FOLD ? 2 * NW : NW;  // partial results per head in the epilogue
+  constexpr int NP = FOLD ? 4 : 8;           // scores per lane and block
   constexpr int NEK = BK == 3 ? 64 : 256;   // table entries: all pairs of codes
   constexpr int NEV = BV == 3 ? 64 : 256;
   constexpr int KREC = 16 * BK;
@@ -729,27 +767,37 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   constexpr int S_K1 = 64 * LST, S_V0 = 128 * LST, S_V1 = S_V0 + 64 * LST, S_N = S_V1 + 64 * LST;
   constexpr int SLOT = S_N + 64 * NSZ;
   constexpr int RING_AT = VT_AT + VT_BYTES;
-  // two workgroups per CU: the pool stays under 78 KB
-  constexpr int D = RING_AT + 3 * NW * SLOT <= 78 * 1024 ? 3 : 2;
+  // two workgroups per CU: the pool and the other shared arrays (query rows, staged
+  // inputs, codebook, reductions) stay within 80 KB
+  constexpr int STATIC_LDS = HPS * kHeadDim * 4 + (kHeadDim + 256) * 4 + 256;
+  constexpr int D = RING_AT + 3 * NW * SLOT + STATIC_LDS <= 80 * 1024 ? 3 : 2;
   constexpr int NDMA = 5;  // copies per block
   // the epilogue reuses the space for the per-wave partial results
-  constexpr int SCR_BYTES = NW * HPS * (kHeadDim + 2) * 4;
+  constexpr int SCR_BYTES = NPART * HPS * (kHeadDim + 2) * 4;
   constexpr int POOL = RING_AT + D * NW * SLOT > SCR_BYTES ? RING_AT + D * NW * SLOT : SCR_BYTES;
+  static_assert(POOL + STATIC_LDS <= 80 * 1024, "two workgroups per CU share its 160 KB of LDS");
   __shared__ __attribute__((aligned(16))) uint8_t pool[POOL];
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float qstage[kHeadDim + 256];  // signs, SO(4) parameters
   __shared__ uint32_t cbk[16], cbv[16];
   __shared__ float red[NW];
   __shared__ float lse2[HPS];
   const uint8_t* ktab = pool;
   float* scr = (float*)pool;
 
+  // Every argument the prologue needs is loaded in one batch here: left to itself the
+  // compiler issues the scalar argument loads one dependent round trip at a time.
+  asm volatile("" ::"s"(a.kc), "s"(a.kn), "s"(a.vc), "s"(a.vn), "s"(a.q), "s"(a.seq_lens), "s"(a.signs), "s"(a.so4));
+  asm volatile("" ::"s"(a.max_len), "s"(a.batch), "s"(a.n_kv_heads), "s"(a.n_q_heads), "s"(a.group_size),
+               "s"(a.heads_per_slice), "s"(a.n_slices), "s"(a.n_splits), "s"(a.capacity));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Unit u = decode_unit(a, true);
   const int col = lane & 15, qg = lane >> 4;
   const int cgrp = NG == 4 ? (col >> 2) : 0;
   const int chl = NG == 4 ? (col & 3) : (col & 7);
-  const bool colok = chl < u.hs && (NG == 4 || col < 8);
+  const int half = FOLD ? col >> 3 : 0;  // the tile this column keeps
+  const bool colok = chl < u.hs && (NG == 4 || FOLD || col < 8);
   // columns that carry no live head get p = 0: their value products multiply zeros
   const float cdead = colok ? 0.f : -INFINITY;
 
@@ -764,12 +812,28 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   const uint8_t* vbase = a.vc + sb * ntile * VTILE;
   const uint8_t* vnbase = (const uint8_t*)(a.vn + sb * ntile * (NG * kTile));
   const uint32_t koff = (lane & 15) * KREC + qg * (4 * BK);
-  const uint32_t noff = (cgrp * kTile + 8 * qg) * 4;
+  // norm slots: tile token 16h + 4q + r sits at 8q + 4h + r of its group's 32
+  const uint32_t noff = (cgrp * kTile + 8 * qg + 4 * half) * 4;
   const uint32_t voff = lane * (8 * BV);
 
-  // ---- query reads, then the first D blocks of this wave into its ring
-  const QueryLane qlane = query_fetch<QF16>(a.signs + u.kv * kHeadDim, a.so4 ? a.so4 + u.kv * 256 : nullptr, a.q,
-                                            (size_t)u.b * a.n_q_heads + u.h0, u.hs, wv, lane);
+  // ---- The small inputs (this wave's two query rows, the signs, the SO(4) parameters) are
+  // staged in LDS by direct copies issued ahead of the ring's, so that one counted wait
+  // covers them while the ring copies stay in flight (a register load would make the
+  // compiler wait for every outstanding copy).  The raw rows sit at the start of the
+  // wave's own two rows of qbuf, which it later overwrites with the rotated query.
+  const uint32_t qraw = lds_addr(qbuf) + wv * (2 * kHeadDim * 4);
+  {
+    const size_t row = (size_t)u.b * a.n_q_heads + u.h0 + 2 * wv;
+    if (QF16) {
+      if (lane < 32 && 2 * wv + (lane >> 4) < u.hs)
+        lds_dma_addr<16>(qraw, (const _Float16*)a.q + row * kHeadDim + 8 * lane);
+    } else {
+      if (2 * wv + (lane >> 5) < u.hs) lds_dma_addr<16>(qraw, (const float*)a.q + row * kHeadDim + 4 * lane);
+    }
+    if (wv == 0 && lane < 32) lds_dma_addr<16>(lds_addr(qstage), a.signs + u.kv * kHeadDim + 4 * lane);
+    if (wv == 1 && a.so4 != nullptr) lds_dma_addr<16>(lds_addr(qstage) + kHeadDim * 4, a.so4 + u.kv * 256 + 4 * lane);
+  }
+  // ---- then the first D blocks of this wave into its ring
   const int nblk = blk0 + wv < blk1 ? (blk1 - (blk0 + wv) + NW - 1) / NW : 0;  // this wave's blocks
   const uint32_t ring = lds_addr(pool) + RING_AT + wv * (D * SLOT);
   const uint8_t* nlane = (lane < 32 ? knbase : vnbase) + (lane & 31) * NSZ;
@@ -807,9 +871,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
       d.v[4] = y1.x; d.v[5] = y1.y; d.v[2 * BV - 2] = y1.z; d.v[2 * BV - 1] = y1.w;
     }
     d.kn0 = load_at<f32x4>(sl + S_N, noff);
-    d.kn1 = load_at<f32x4>(sl + S_N, noff + 16);
     d.vn0 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff);
-    d.vn1 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff + 16);
+    if (!FOLD) {
+      d.kn1 = load_at<f32x4>(sl + S_N, noff + 16);
+      d.vn1 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff + 16);
+    }
     return d;
   };
   if (nblk > 0) {
@@ -817,15 +883,28 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     for (int j = 0; j < D; ++j) fetch(j);
   }
 
-  // ---- decode tables
-  if (tid < 16) {
-    cbk[tid] = f16_bits((_Float16)(a.kcent[tid] * a.kscale));
-    cbv[tid] = f16_bits((_Float16)(QUAD ? a.vcent[tid] * a.kscale : a.vcent[tid]));
+  // ---- decode tables.  The codebook comes from the kernel arguments at constant offsets
+  // (scalar loads, which the copies' wait does not involve).
+  if (tid == 0) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      cbk[c] = f16_bits((_Float16)(a.kcent[c] * a.kscale));
+      cbv[c] = f16_bits((_Float16)(QUAD ? a.vcent[c] * a.kscale : a.vcent[c]));
+    }
   }
+  if (nblk > 0) vm_wait<NDMA * D>();  // the staged inputs (copied first) have landed
+  else vm_wait<0>();
   __syncthreads();
   if (QUAD) {
-    for (int e = tid; e < 4096; e += 256)
-      ((uint2*)pool)[e] = make_uint2(cbk[e & 7] | (cbk[(e >> 3) & 7] << 16), cbk[(e >> 6) & 7] | (cbk[e >> 9] << 16));
+    // Thread tid owns the entries whose two low codes are (tid >> 3) & 7, tid & 7 and whose
+    // third code is 2wv or 2wv + 1: the low half of its entries is fixed, and each step
+    // writes 64 consecutive entries.
+    const uint32_t lo = cbk[tid & 7] | (cbk[(tid >> 3) & 7] << 16);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c2 = 2 * wv + (j & 1), c3 = j >> 1;
+      ((uint2*)pool)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, cbk[c2] | (cbk[c3] << 16));
+    }
   } else {
     for (int i = tid; i < NEK * RK; i += 256) {
       const int e = i / RK;
@@ -840,6 +919,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // ---- rotated, scaled query (log2 units) with a power-of-two prescale into fp16 range
   float mx = 0.f;
   {
+    const QueryLane qlane = query_staged<QF16>((const uint8_t*)qbuf + wv * (2 * kHeadDim * 4), qstage, a.so4 != nullptr,
+                                               u.hs, wv, lane);
     float4 r = query_rotate(qlane, a.so4 != nullptr, a.rot_group, lane);
     const float qsc = a.scale_log2 / a.kscale;
     r.x *= qsc; r.y *= qsc; r.z *= qsc; r.w *= qsc;
@@ -898,7 +979,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     return r;
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // running maximum (prescaled units), sum, the rescale bound m_run + 2^3 (prescaled) and
+  // the exponent offset -m_run (log2 units) plus the dead-column mask
+  float m_run = -INFINITY, l_run = 0.f, thr = -INFINITY, nmq = cdead;
   f32x4 O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -934,67 +1017,89 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
         for (int j = 0; j < 4; ++j) va[f][j] = lds_at<uint32_t>(pool, pair_lds_addr<BV, SHV>(cb.v, 8 * BV * f + 2 * BV * j, vlane));
       }
     }
-    // raw scores (units of the prescaled query) of tokens 16h + 4q' + r, slot k = 4h + r
-    float x[8];
+    // raw scores (units of the prescaled query).  Unfolded: tokens 16h + 4q' + r in slot
+    // k = 4h + r.  Folded: tokens 16*half + 4q' + r in slot r.
+    float x[NP];
+    if (FOLD) {
+      // column c < 8 holds tile 0's hi part and needs its lo part from column c + 8;
+      // column c + 8 holds tile 1's lo part and needs its hi part from column c
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float d = k < 4 ? D0[k] : D1[k - 4];
-      const float n = k < 4 ? cb.kn0[k] : cb.kn1[k - 4];
-      if (NG == 4) {
-        d *= n;
-        d += dpp<0x124>(d);  // row_ror:4
-        d += dpp<0x128>(d);  // row_ror:8
-      } else {
-        d = (d + dpp<0x128>(d)) * n;  // hi + lo columns
+      for (int r = 0; r < 4; ++r) {
+        const float own = half ? D1[r] : D0[r], send = half ? D0[r] : D1[r];
+        x[r] = (own + dpp<0x128>(send)) * cb.kn0[r];  // row_ror:8
       }
-      x[k] = d;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float d = k < 4 ? D0[k] : D1[k - 4];
+        const float n = k < 4 ? cb.kn0[k] : cb.kn1[k - 4];
+        if (NG == 4) {
+          d *= n;
+          d += dpp<0x124>(d);  // row_ror:4
+          d += dpp<0x128>(d);  // row_ror:8
+        } else {
+          d = (d + dpp<0x128>(d)) * n;  // hi + lo columns
+        }
+        x[k] = d;
+      }
     }
     const int t0 = blk * kTile;
     const bool edge = t0 < lo || t0 + kTile > hi;  // wave-uniform
     if (edge) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t = t0 + 16 * (k >> 2) + 4 * qg + (k & 3);
+      for (int k = 0; k < NP; ++k) {
+        const int t = FOLD ? t0 + 16 * half + 4 * qg + k : t0 + 16 * (k >> 2) + 4 * qg + (k & 3);
         if (t < lo || t >= hi) x[k] = -INFINITY;
       }
     }
     // Lazy maximum: while no score of the block exceeds the column's running maximum by
-    // more than 2^kRescaleLog2, p stays below that bound and nothing needs to be reduced
-    // across the lanes; only when some lane sees a larger score is the block maximum formed
-    // and the column rescaled.
-    const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const bool need = m_run == -INFINITY ? lm > -INFINITY : (lm - m_run) * qinv > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    // more than 2^kRescaleLog2 (thr is that bound in prescaled units), p stays below it and
+    // nothing needs to be reduced across the lanes; only when some lane sees a larger
+    // score is the block maximum formed and the column rescaled.
+    float lm = x[0];
+#pragma unroll
+    for (int k = 1; k < NP; ++k) lm = fmaxf(lm, x[k]);
+    if (__builtin_amdgcn_ballot_w64(lm > thr) != 0) {
       const float bm = rows_max(lm);
-      const bool grow = m_run == -INFINITY ? bm > -INFINITY : (bm - m_run) * qinv > kRescaleLog2;
-      const float mnew = grow ? bm : m_run;
+      const float mnew = bm > thr ? bm : m_run;
       const float al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * qinv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) O[i] *= al;
       l_run *= al;
       m_run = mnew;
+      thr = m_run + kRescaleLog2 * qs;
+      nmq = (m_run == -INFINITY ? 0.f : -m_run * qinv) + cdead;
     }
-    const float nmq = (m_run == -INFINITY ? 0.f : -m_run * qinv) + cdead;
-    float p[8];
+    float p[NP];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NP; ++k) {
       p[k] = __builtin_amdgcn_exp2f(fmaf(x[k], qinv, nmq));
       l_run += p[k];
     }
-    float pv[8];
+    float pv[NP];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pv[k] = p[k] * (k < 4 ? cb.vn0[k] : cb.vn1[k - 4]);
+    for (int k = 0; k < NP; ++k) pv[k] = p[k] * (FOLD || k < 4 ? cb.vn0[k & 3] : cb.vn1[k - 4]);
     if (edge) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < NP; ++k)
         if (p[k] == 0.f) pv[k] = 0.f;  // masked slots may hold undefined norms
     }
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     u32x4 bp;
+    if (FOLD) {
+      // this column's tile takes K slots 4*half .. 4*half + 3; the other tile's are zero
+      const uint32_t c01 = __builtin_bit_cast(uint32_t, h2_t{(_Float16)pv[0], (_Float16)pv[1]});
+      const uint32_t c23 = __builtin_bit_cast(uint32_t, h2_t{(_Float16)pv[2], (_Float16)pv[3]});
+      bp[0] = half ? 0u : c01;
+      bp[1] = half ? 0u : c23;
+      bp[2] = half ? c01 : 0u;
+      bp[3] = half ? c23 : 0u;
+    } else {
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-      const h2_t hv = {(_Float16)pv[2 * pr], (_Float16)pv[2 * pr + 1]};
-      bp[pr] = __builtin_bit_cast(uint32_t, hv);
+      for (int pr = 0; pr < 4; ++pr) {
+        const h2_t hv = {(_Float16)pv[2 * pr], (_Float16)pv[2 * pr + 1]};
+        bp[pr] = __builtin_bit_cast(uint32_t, hv);
+      }
     }
 #pragma unroll
     for (int w = 0; w < 8; ++w) O[w] = mfma16(va[w], bp, O[w]);
@@ -1012,24 +1117,26 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   }
   vm_wait<0>();  // no copy may land in the pool once it is reused below
 
-  // ---- combine the waves of the workgroup (scores in prescaled units -> log2 units)
+  // ---- combine the partials of the workgroup: one per wave, or per wave and tile when
+  // folded (scores in prescaled units -> log2 units)
   const float lt = rows_sum(l_run);
   const float m2 = m_run == -INFINITY ? -INFINITY : m_run * qinv;
-  __syncthreads();                       // every wave is done with the tables
-  float* so = scr;                       // [NW][HPS][128]
-  float* sm = so + NW * HPS * kHeadDim;  // [NW][HPS]
-  float* sl = sm + NW * HPS;
+  __syncthreads();                          // every wave is done with the tables
+  const int part = FOLD ? 2 * wv + half : wv;
+  float* so = scr;                          // [NPART][HPS][128]
+  float* sm = so + NPART * HPS * kHeadDim;  // [NPART][HPS]
+  float* sl = sm + NPART * HPS;
   if (colok) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       if (NG == 1 || (w >> 1) == cgrp) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) so[(wv * HPS + chl) * kHeadDim + 16 * w + 4 * qg + r] = O[w][r];
+        for (int r = 0; r < 4; ++r) so[(part * HPS + chl) * kHeadDim + 16 * w + 4 * qg + r] = O[w][r];
       }
     }
     if (qg == 0 && cgrp == 0) {
-      sm[wv * HPS + chl] = m2;
-      sl[wv * HPS + chl] = lt;
+      sm[part * HPS + chl] = m2;
+      sl[part * HPS + chl] = lt;
     }
   }
   __syncthreads();
@@ -1037,11 +1144,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     const int hl = i >> 7, c = i & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * HPS + hl]);
+    for (int w = 0; w < NPART; ++w) M = fmaxf(M, sm[w * HPS + hl]);
     const float mu = M == -INFINITY ? 0.f : M;
     float L = 0.f, acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < NPART; ++w) {
       const float f = __builtin_amdgcn_exp2f(sm[w * HPS + hl] - mu);
       L += sl[w * HPS + hl] * f;
       acc += so[(w * HPS + hl) * kHeadDim + c] * f;
