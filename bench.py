@@ -1,15 +1,16 @@
 """Benchmark: decode attention on a packed 3/4-bit KV cache, one MI355X.
 
 One step = one pass of the whole hot path over one batch: quantise-append the newest
-token's key and value (one launch) into slot T-1 of every (sequence, KV head), decode attention over T
-tokens straight from the codes (rotated query, online softmax, rotated-domain value sum),
-and merge the key-axis splits with the single inverse rotation.  Inputs are seeded and
+token's key and value into slot T-1 of every (sequence, KV head) and decode attention over
+T tokens straight from the codes (rotated query, online softmax, rotated-domain value sum)
+in one launch (tq_append_decode_attention: the workgroups whose key-axis section holds the
+new slot write it first), then merge the key-axis splits with the single inverse rotation.  Inputs are seeded and
 synthetic (workloads.py) and resident in HBM before timing.  The packed caches are
 replicated to more than 1 GiB and cycled so that the 256 MB last-level cache cannot hold
 them; the number is HBM-bound, not cache-bound.
 
 Prints one JSON line.  Value = KV token*heads per second for the whole step.  The
-roofline object is for the decode kernel: algorithmic bytes (codes + norms of every
+roofline object is for that decode launch: algorithmic bytes (codes + norms of every
 (token, KV head)) per launch over its average launch time, measured with events on the
 launch stream.  cpu_baseline times the fp64 oracle (dequantise + plain attention) on a
 bounded sample of the same workload on this host.
@@ -116,16 +117,17 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
     pl = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
 
     def decode(i):
+        # the step's new key and value (slot T - 1) are quantised and written by the decode
+        # launch itself, which then attends over all T tokens
         k, v = caches[i % reps]
         if n_splits == 1:
-            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=1, schedule=schedule, out=out, lse=lse)
+            tq.append_decode_attention(rot, k, v, newk, newv, q, pos0=T - 1, n_splits=1, schedule=schedule, out=out,
+                                       lse=lse)
         else:
-            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=n_splits, schedule=schedule, part_o=po,
-                                part_lse=pl)
+            tq.append_decode_attention(rot, k, v, newk, newv, q, pos0=T - 1, n_splits=n_splits, schedule=schedule,
+                                       part_o=po, part_lse=pl)
 
     def step(i):
-        k, v = caches[i % reps]
-        tq.quantize_append_kv(rot, k, v, newk, newv, pos0=T - 1)
         decode(i)
         if n_splits > 1:
             tq.merge_splits(rot, po, pl, out=out, lse=lse)
@@ -347,13 +349,15 @@ def counter_run(w, inp, n_splits, schedule, launches=24):
     po = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
     pl = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
-    for i in range(launches):
+    newk = torch.from_numpy(inp["k"][:, :, T - 1:T].copy()).to(dev)
+    newv = torch.from_numpy(inp["v"][:, :, T - 1:T].copy()).to(dev)
+    for i in range(launches):  # the launch the timed step makes
         k, v = caches[i % reps]
         if n_splits == 1:
-            tq.decode_attention(rot, k, v, q, max_len=T, schedule=schedule, out=out)
+            tq.append_decode_attention(rot, k, v, newk, newv, q, pos0=T - 1, schedule=schedule, out=out)
         else:
-            tq.decode_attention(rot, k, v, q, max_len=T, n_splits=n_splits, schedule=schedule, part_o=po,
-                                part_lse=pl)
+            tq.append_decode_attention(rot, k, v, newk, newv, q, pos0=T - 1, n_splits=n_splits, schedule=schedule,
+                                       part_o=po, part_lse=pl)
     torch.cuda.synchronize()
     log("counter run: 3 copies of %d bytes, %d decode launches over %d replicas" % (COPY_BYTES, launches, reps))
 
@@ -464,7 +468,7 @@ def main():
         "config": {"workload": w.name, "timing": "HIP graph replay, one graph per step", "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "seq_len": w.seq_len, "bits_k": w.bits_k, "bits_v": w.bits_v, "group": w.group,
                    "so4": w.so4, "n_splits": n_splits, "schedule": args.schedule,
-                   "step": "append 1 token K+V (one launch), decode, merge", "cache_replicas": r["reps"]},
+                   "step": "append 1 token K+V and decode in one launch, then merge", "cache_replicas": r["reps"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, n_splits)},
         "cpu_baseline": cpu,

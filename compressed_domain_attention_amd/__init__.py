@@ -65,7 +65,7 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
-           "tq_decode_attention", "tq_merge_splits")
+           "tq_decode_attention", "tq_append_decode_attention", "tq_merge_splits")
 
 
 def library():
@@ -89,6 +89,10 @@ def library():
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache), ctypes.POINTER(_Cache),
                                         P, I, I, P, I, F, I, I, P, P, P, P, P]
     lib.tq_decode_attention.restype = I
+    lib.tq_append_decode_attention.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache),
+                                               ctypes.POINTER(_Cache), P, P, I, P, I, I, P, I, I, F, I, I, P, P, P,
+                                               P, P]
+    lib.tq_append_decode_attention.restype = I
     lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
     lib.tq_merge_splits.restype = I
     _lib = lib
@@ -209,6 +213,42 @@ def decode_attention(rot: Rotation, keys: PackedCache, values: PackedCache, q: t
         ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(q), _DTYPES[q.dtype], hq,
         _ptr(seq_lens), max_len, scale, n_splits, _SCHEDULES[schedule], _ptr(out), _ptr(lse), _ptr(part_o),
         _ptr(part_lse), _stream()), "tq_decode_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+def append_decode_attention(rot: Rotation, keys: PackedCache, values: PackedCache, xk: torch.Tensor,
+                            xv: torch.Tensor, q: torch.Tensor, pos: torch.Tensor = None, pos0: int = 0,
+                            max_pos: int = None, scale=None, n_splits=1, schedule="auto", out=None, lse=None,
+                            part_o=None, part_lse=None):
+    """Append one new key/value token per (sequence, KV head) at pos (or pos0), then decode
+    over rows ending at it, in one call.  Returns as decode_attention."""
+    for x in (xk, xv):
+        if x.dtype not in _DTYPES or not x.is_contiguous():
+            raise ValueError("xk and xv must be contiguous float16/float32 tensors")
+    if xk.dtype != xv.dtype or xk.shape != xv.shape or xk.shape[2] != 1:
+        raise ValueError("xk and xv must have the same dtype and shape, one token per stream")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    if max_pos is None:
+        max_pos = int(pos.max().item()) if pos is not None else pos0
+    bsz, hq = q.shape[0], q.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_append_decode_attention(
+        ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(xk), _ptr(xv), _DTYPES[xk.dtype],
+        _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits, _SCHEDULES[schedule], _ptr(out),
+        _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_append_decode_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)
 
 

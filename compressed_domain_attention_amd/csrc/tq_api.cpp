@@ -95,10 +95,14 @@ extern "C" tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cach
                                        append_tiles(pos, pos0, n_new), (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
-                                         const void* q, tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens,
-                                         int32_t max_len, float scale, int32_t n_splits, tq_schedule schedule,
-                                         float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+namespace {
+
+// Host checks of a decode call; fills the launch arguments.  `same` reports whether keys and
+// values share one four-code table (3-bit, identical codebooks).
+tq_status decode_args(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values, const void* q,
+                      tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                      int32_t n_splits, tq_schedule schedule, float* out, float* lse_out, float* part_o,
+                      float* part_lse, tq::DecodeArgs& a, int& sched, bool& same) {
   tq_status st = check_rotation(rot);
   if (st != TQ_OK) return st;
   if ((st = check_cache(keys, rot, TQ_KEYS)) != TQ_OK) return st;
@@ -111,12 +115,12 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
   if (n_splits == 1 && out == nullptr) return TQ_EINVAL;
   if (n_splits > 1 && (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
   if (schedule != TQ_SCHEDULE_AUTO && schedule != TQ_SCHEDULE_VEC && schedule != TQ_SCHEDULE_MFMA) return TQ_EINVAL;
+  if (values->capacity != keys->capacity) return TQ_EINVAL;
 
   const int group_size = n_q_heads / rot->n_kv_heads;
   // every supported (bits, group) pair has a matrix-core kernel, so AUTO takes it
-  const int sched = schedule == TQ_SCHEDULE_VEC ? 1 : 2;
+  sched = schedule == TQ_SCHEDULE_VEC ? 1 : 2;
 
-  tq::DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.kc = (const uint8_t*)keys->codes;
   a.kn = keys->norms;
@@ -140,7 +144,6 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
   a.n_slices = (group_size + a.heads_per_slice - 1) / a.heads_per_slice;
   a.n_splits = n_splits;
   a.capacity = keys->capacity;
-  if (values->capacity != keys->capacity) return TQ_EINVAL;
   a.rot_group = rot->group;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.kscale = keys->codebook.f16_scale;
@@ -148,10 +151,61 @@ extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache*
     a.kcent[k] = keys->codebook.centroid[k];
     a.vcent[k] = values->codebook.centroid[k];
   }
-  // one shared four-code table when keys and values are 3-bit with the same codebook
-  bool same = keys->bits == 3 && values->bits == 3 && keys->codebook.f16_scale == values->codebook.f16_scale;
+  same = keys->bits == 3 && values->bits == 3 && keys->codebook.f16_scale == values->codebook.f16_scale;
   for (int k = 0; k < 8 && same; ++k) same = keys->codebook.centroid[k] == values->codebook.centroid[k];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                         const void* q, tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens,
+                                         int32_t max_len, float scale, int32_t n_splits, tq_schedule schedule,
+                                         float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+  tq::DecodeArgs a;
+  int sched;
+  bool same;
+  const tq_status st = decode_args(rot, keys, values, q, q_dtype, n_q_heads, seq_lens, max_len, scale, n_splits,
+                                   schedule, out, lse_out, part_o, part_lse, a, sched, same);
+  if (st != TQ_OK) return st;
   return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_append_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                                const void* xk, const void* xv, tq_dtype x_dtype, const int32_t* pos,
+                                                int32_t pos0, int32_t max_pos, const void* q, tq_dtype q_dtype,
+                                                int32_t n_q_heads, float scale, int32_t n_splits,
+                                                tq_schedule schedule, float* out, float* lse_out, float* part_o,
+                                                float* part_lse, void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if (keys == nullptr || values == nullptr) return TQ_EINVAL;
+  if (keys->role != TQ_KEYS || values->role != TQ_VALUES) return TQ_EINVAL;
+  if (keys->batch != values->batch) return TQ_EINVAL;
+  tq::AppendArgs ak, av;
+  if ((st = append_args(rot, keys, xk, x_dtype, 1, pos, pos0, max_pos, ak)) != TQ_OK) return st;
+  if ((st = append_args(rot, values, xv, x_dtype, 1, pos, pos0, max_pos, av)) != TQ_OK) return st;
+  // rows end at their new token: length pos[b] + 1, or pos0 + 1 for every row
+  const int32_t max_len = (pos ? max_pos : pos0) + 1;
+  tq::DecodeArgs a;
+  int sched;
+  bool same;
+  if ((st = decode_args(rot, keys, values, q, q_dtype, n_q_heads, pos, max_len, scale, n_splits, schedule, out,
+                        lse_out, part_o, part_lse, a, sched, same)) != TQ_OK)
+    return st;
+  a.len_bias = pos ? 1 : 0;
+  const hipStream_t s = (hipStream_t)stream;
+  if (sched == 1) {  // the vector schedule keeps two launches
+    if ((st = from_hip(tq::launch_append_kv(ak, av, keys->bits, values->bits, keys->group, x_dtype == TQ_F16,
+                                            keys->batch, append_tiles(pos, pos0, 1), s))) != TQ_OK)
+      return st;
+    return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, s));
+  }
+  a.append = 1;
+  a.append_f16 = x_dtype == TQ_F16;
+  a.ak = ak;
+  a.av = av;
+  return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, s));
 }
 
 extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,

@@ -52,6 +52,12 @@ struct DecodeArgs {
                             // the value scale when keys and values share one table)
   float kcent[16];
   float vcent[16];
+  // Fused single-token append: the workgroups whose section holds a row's new position
+  // quantise and write that token (keys and values) before reading the cache.
+  int32_t append;           // 0 or 1
+  int32_t append_f16;       // the new vectors are fp16
+  int32_t len_bias;         // a row has seq_lens[b] + len_bias tokens (1: seq_lens holds positions)
+  AppendArgs ak, av;
 };
 
 struct MergeArgs {

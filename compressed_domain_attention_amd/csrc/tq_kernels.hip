@@ -399,36 +399,40 @@ __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
 // of boundaries below, pack); the group norm is summed in another order, so results may
 // differ from append_tile in the last bit of a norm.  Value codes are merged byte by byte:
 // every byte a lane writes belongs to its own words.
-template <int BK, int BV, int GROUP, bool XF16>
-__global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, const AppendArgs av, int batch) {
+// One wave appends the token of stream st = b * n_kv_heads + kv; x_f16 selects the vector
+// type.  Shared by the append kernel below and by the decode kernel's fused append.
+template <int BK, int BV, int GROUP>
+__device__ __forceinline__ void append_step_wave(const AppendArgs& ak, const AppendArgs& av, int st, bool x_f16,
+                                                 int lane) {
   constexpr int NG = kHeadDim / GROUP;
-  const int lane = threadIdx.x & 63;
-  const int st = blockIdx.x * 4 + (threadIdx.x >> 6);  // stream = b * n_kv_heads + kv
-  if (st >= batch * ak.n_kv_heads) return;            // whole waves only
   const bool val = lane >= 32;
-  const AppendArgs& a = val ? av : ak;
+  // the lane's own cache, field by field (a lane-selected reference to either argument
+  // block would be copied to private memory); positions, signs and SO(4) are common
   const int bits = val ? BV : BK;
+  const int capacity = val ? av.capacity : ak.capacity;
+  float* const norms = val ? av.norms : ak.norms;
+  const void* const xsrc = val ? av.x : ak.x;
   const int b = st / ak.n_kv_heads, kv = st - b * ak.n_kv_heads;
   const int pb = lane & 31;
-  const int slot = a.pos ? a.pos[b] : a.pos0;
-  const int ntile = a.capacity / kTile;
+  const int slot = ak.pos ? ak.pos[b] : ak.pos0;
+  const int ntile = capacity / kTile;
   const int t = slot & (kTile - 1);
 
   // global reads first: the vector, signs, SO(4) block, and the value bytes to be merged
   float4 x;
   const size_t xi = (size_t)st * kHeadDim + 4 * pb;  // n_new == 1
-  if (XF16) {
+  if (x_f16) {
     typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-    const h4_t h = *(const h4_t*)((const _Float16*)a.x + xi);
+    const h4_t h = *(const h4_t*)((const _Float16*)xsrc + xi);
     x = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
   } else {
-    x = *(const float4*)((const float*)a.x + xi);
+    x = *(const float4*)((const float*)xsrc + xi);
   }
-  const float4 sg = *(const float4*)(a.signs + kv * kHeadDim + 4 * pb);
+  const float4 sg = *(const float4*)(ak.signs + kv * kHeadDim + 4 * pb);
   Quat ql{1.f, 0.f, 0.f, 0.f}, qr{1.f, 0.f, 0.f, 0.f};
-  if (a.so4) {
-    ql = qload(a.so4 + ((size_t)kv * 32 + pb) * 8);
-    qr = qload(a.so4 + ((size_t)kv * 32 + pb) * 8 + 4);
+  if (ak.so4) {
+    ql = qload(ak.so4 + ((size_t)kv * 32 + pb) * 8);
+    qr = qload(ak.so4 + ((size_t)kv * 32 + pb) * 8 + 4);
   }
   // value word of coordinate i = 16u + m for tile token t = 16h + 4q + r: (q*16 + m)*8 + u,
   // field 4h + r; 3-bit words are 3 bytes, 4-bit words 4 bytes
@@ -469,28 +473,30 @@ __global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, c
   }
   const float hsc = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
   Quat v{x0 * hsc, x1 * hsc, x2 * hsc, x3 * hsc};
-  if (a.so4) v = qmul(qmul(ql, v), qconj(qr));
+  if (ak.so4) v = qmul(qmul(ql, v), qconj(qr));
   const float yv[4] = {v.w, v.x, v.y, v.z};
   uint32_t code[4];
   const int nb = (1 << bits) - 1;
+  constexpr int NBMAX = (1 << (BK > BV ? BK : BV)) - 1;  // constant trip count: no indexed arrays
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t c = 0;
-    for (int k = 0; k < nb; ++k) c += yv[j] > a.boundary[k] ? 1u : 0u;
+#pragma unroll
+    for (int k = 0; k < NBMAX; ++k) c += k < nb && yv[j] > (val ? av.boundary[k] : ak.boundary[k]) ? 1u : 0u;
     code[j] = c;
   }
 
   // norms: one lane per group
   if ((pb & (GROUP / 4 - 1)) == 0) {
     const int grp = (4 * pb) / GROUP;
-    a.norms[((size_t)st * ntile + slot / kTile) * (NG * kTile) + grp * kTile + norm_pos(t)] = nrm;
+    norms[((size_t)st * ntile + slot / kTile) * (NG * kTile) + grp * kTile + norm_pos(t)] = nrm;
   }
   if (!val) {
     // key record: word w = coordinates 8w..8w+7 = lanes 2w (low half) and 2w + 1
     const uint32_t half = BK == 3 ? (code[0] | code[1] << 3 | code[2] << 6 | code[3] << 9)
                                   : (code[0] | code[1] << 4 | code[2] << 8 | code[3] << 12);
     const uint32_t other = __shfl_xor(half, 1);
-    uint8_t* rec = a.codes + ((size_t)st * a.capacity + slot) * (16 * BK);
+    uint8_t* rec = ak.codes + ((size_t)st * ak.capacity + slot) * (16 * BK);
     if ((pb & 1) == 0) {
       const int w = pb >> 1;
       if (BK == 3) {
@@ -513,6 +519,13 @@ __global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, c
       if (BV == 3 && sh > 5) vtile[vbyte[j] + 1] = (uint8_t)(nw >> 8);
     }
   }
+}
+
+template <int BK, int BV, int GROUP, bool XF16>
+__global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, const AppendArgs av, int batch) {
+  const int st = blockIdx.x * 4 + (threadIdx.x >> 6);  // stream = b * n_kv_heads + kv
+  if (st >= batch * ak.n_kv_heads) return;            // whole waves only
+  append_step_wave<BK, BV, GROUP>(ak, av, st, XF16, threadIdx.x & 63);
 }
 
 // Keys and values of one step in one launch: grid z covers the keys' sequences, then the
@@ -548,10 +561,15 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, bool xcd_pairs)
     unit = L / ns;
     slice = L - unit * ns;
   }
+  // split-major with the last section first: the workgroups holding the newest tokens
+  // (which also append them when the append is fused) are dispatched first, so they are
+  // the older, first-served workgroup on their CU
   Unit u;
-  u.split = unit % a.n_splits;
-  u.kv = (unit / a.n_splits) % a.n_kv_heads;
-  u.b = unit / (a.n_splits * a.n_kv_heads);
+  const int rows = a.batch * a.n_kv_heads;
+  const int rank = unit / rows, row = unit - rank * rows;
+  u.split = a.n_splits - 1 - rank;
+  u.kv = row % a.n_kv_heads;
+  u.b = row / a.n_kv_heads;
   u.slice = slice;
   u.h0 = u.kv * a.group_size + slice * a.heads_per_slice;
   u.hs = min(a.heads_per_slice, a.group_size - slice * a.heads_per_slice);
@@ -592,7 +610,7 @@ __device__ __forceinline__ void write_result(const DecodeArgs& a, const Unit& u,
 __device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, int& lo, int& hi) {
   // lengths beyond max_len (checked against the capacity on the host) are clamped, so a
   // bad device length can never move a read outside the cache
-  const int T = a.seq_lens ? max(0, min(a.seq_lens[u.b], a.max_len)) : a.max_len;
+  const int T = a.seq_lens ? max(0, min(a.seq_lens[u.b] + a.len_bias, a.max_len)) : a.max_len;
   const int C = (T + a.n_splits - 1) / a.n_splits;
   lo = min(T, u.split * C);
   hi = min(T, lo + C);
@@ -788,7 +806,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // Every argument the prologue needs is loaded in one batch here: left to itself the
   // compiler issues the scalar argument loads one dependent round trip at a time.
   asm volatile("" ::"s"(a.kc), "s"(a.kn), "s"(a.vc), "s"(a.vn), "s"(a.q), "s"(a.seq_lens), "s"(a.signs), "s"(a.so4));
-  asm volatile("" ::"s"(a.max_len), "s"(a.batch), "s"(a.n_kv_heads), "s"(a.n_q_heads), "s"(a.group_size),
+  asm volatile("" ::"s"(a.max_len), "s"(a.len_bias), "s"(a.batch), "s"(a.n_kv_heads), "s"(a.n_q_heads), "s"(a.group_size),
                "s"(a.heads_per_slice), "s"(a.n_slices), "s"(a.n_splits), "s"(a.capacity));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -815,6 +833,18 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   // norm slots: tile token 16h + 4q + r sits at 8q + 4h + r of its group's 32
   const uint32_t noff = (cgrp * kTile + 8 * qg + 4 * half) * 4;
   const uint32_t voff = lane * (8 * BV);
+
+  // ---- Fused append: if this workgroup's section holds the row's new position, one wave
+  // quantises and writes that token first; the barrier orders its stores before every
+  // read of the cache by the workgroup.  Other sections that share the token's 32-token
+  // tile mask it, and the bytes it rewrites keep their other tokens' fields.
+  if (a.append) {
+    const int p = a.ak.pos ? a.ak.pos[u.b] : a.ak.pos0;
+    if (p >= lo && p < hi) {
+      if (wv == 0) append_step_wave<BK, BV, NG == 4 ? 32 : 128>(a.ak, a.av, u.b * a.n_kv_heads + u.kv, a.append_f16 != 0, lane);
+      __syncthreads();
+    }
+  }
 
   // ---- The small inputs (this wave's two query rows, the signs, the SO(4) parameters) are
   // staged in LDS by direct copies issued ahead of the ring's, so that one counted wait

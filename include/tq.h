@@ -169,6 +169,22 @@ tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, cons
                               int32_t n_splits, tq_schedule schedule, float* out, float* lse_out,
                               float* part_o, float* part_lse, void* stream);
 
+/* One decode step with its new token: the same result, bit for bit (cache and outputs), as
+ * tq_quantize_append_kv(rot, keys, values, xk, xv, x_dtype, 1, pos, pos0, max_pos)
+ * followed by tq_decode_attention over rows of length pos[b] + 1 (pos0 + 1 when pos is
+ * NULL) with max_len = max_pos + 1 (pos0 + 1) and the remaining arguments as given
+ * ("TurboQuant ...", 3.3: K and V are quantised on write and attention reads the
+ * packed cache).  xk, xv: device [batch][n_kv_heads][1][128] of x_dtype; pos, pos0,
+ * max_pos as for tq_quantize_append.  With the matrix-core schedule it is one launch: the
+ * workgroups whose key-axis section holds a row's new position write that token before
+ * reading the cache.  The vector schedule makes the two launches.  Errors: those of the
+ * two calls it stands for; nothing is written when a check fails. */
+tq_status tq_append_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                     const void* xk, const void* xv, tq_dtype x_dtype, const int32_t* pos,
+                                     int32_t pos0, int32_t max_pos, const void* q, tq_dtype q_dtype,
+                                     int32_t n_q_heads, float scale, int32_t n_splits, tq_schedule schedule,
+                                     float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
+
 /* Log-sum-exp merge of key-axis sections followed by the single inverse rotation:
  * lse = ln sum_s e^{lse_s}; out = R^T sum_s e^{lse_s - lse} part_o_s
  * ("RoPE-Aware Bit Allocation ...", packed-cache details; "RotaryQuant ...", key design 3).

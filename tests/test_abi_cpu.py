@@ -159,6 +159,34 @@ def test_decode_validation(lib):
     assert decode(rot, k, make_cache(tq.TQ_VALUES, capacity=128)) == TQ_EINVAL
 
 
+def append_decode(rot, k, v, xk=FAKE, xv=FAKE, pos=None, pos0=5, max_pos=0, n_q_heads=4, n_splits=1, out=FAKE,
+                  part=FAKE, sched=0, scale=0.1, q=FAKE):
+    return tq.library().tq_append_decode_attention(ctypes.byref(rot), ctypes.byref(k), ctypes.byref(v), xk, xv, 1,
+                                                   pos, pos0, max_pos, q, 1, n_q_heads, scale, n_splits, sched, out,
+                                                   None, part, part, None)
+
+
+def test_append_decode_validation(lib):
+    # the one-call step rejects what either of the two calls it stands for rejects
+    rot = make_rot()
+    k, v = make_cache(tq.TQ_KEYS), make_cache(tq.TQ_VALUES)
+    assert append_decode(rot, k, v, pos0=64) == TQ_ECAPACITY              # new token past the cache
+    assert append_decode(rot, k, v, pos=FAKE, max_pos=64) == TQ_ECAPACITY
+    assert append_decode(rot, k, v, pos0=-1) == TQ_EINVAL
+    assert append_decode(rot, v, k) == TQ_EINVAL                          # roles swapped
+    assert append_decode(rot, k, v, xk=None) == TQ_EINVAL
+    assert append_decode(rot, k, v, xv=None) == TQ_EINVAL
+    assert append_decode(rot, k, v, q=None) == TQ_EINVAL
+    assert append_decode(rot, k, v, n_q_heads=3) == TQ_EINVAL
+    assert append_decode(rot, k, v, n_splits=0) == TQ_EINVAL
+    assert append_decode(rot, k, v, out=None) == TQ_EINVAL
+    assert append_decode(rot, k, v, n_splits=4, part=None) == TQ_EINVAL
+    assert append_decode(rot, k, v, sched=9) == TQ_EINVAL
+    assert append_decode(rot, k, v, scale=float("inf")) == TQ_EINVAL
+    assert append_decode(rot, k, make_cache(tq.TQ_VALUES, batch=2)) == TQ_EINVAL
+    assert append_decode(rot, k, make_cache(tq.TQ_VALUES, capacity=128)) == TQ_EINVAL
+
+
 def test_merge_validation(lib):
     rot = make_rot()
     m = lib.tq_merge_splits

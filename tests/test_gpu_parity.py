@@ -136,6 +136,46 @@ def test_fused_append_equals_separate_calls(name):
         assert torch.equal(a.codes, b.codes) and torch.equal(a.norms, b.norms)
 
 
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_append_decode_equals_separate_calls(name, schedule):
+    # one call that appends each row's new token and decodes over rows ending at it gives
+    # the cache bytes and the outputs of the append call followed by the decode call: at a
+    # host position and at per-row device positions (one overwriting an earlier slot), whole
+    # and split, where the section holding the new token is the last one, an inner one
+    # (short sections, empty ones after it) or the only one
+    w, inp = setup(name, seed=9, seq_len=80, batch=2)
+    cap = 96
+    rot = device_rotation(w, inp)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    q = torch.from_numpy(inp["q"]).cuda()
+    p = 61
+    xs, ys = kx[:, :, p:p + 1].contiguous(), vx[:, :, p:p + 1].contiguous()
+    for device_pos in (False, True):
+        for n_splits in (1, 4, 40):
+            k1, v1 = empty_caches(w, cap)
+            k2, v2 = empty_caches(w, cap)
+            for k, v in ((k1, v1), (k2, v2)):
+                tq.quantize_append_kv(rot, k, v, kx[:, :, :p].contiguous(), vx[:, :, :p].contiguous())
+            if device_pos:
+                pos = torch.tensor([p, p - 5], dtype=torch.int32, device="cuda")
+                kw = dict(pos=pos, max_pos=p)
+                tq.quantize_append_kv(rot, k1, v1, xs, ys, **kw)
+                r1 = tq.decode_attention(rot, k1, v1, q, seq_lens=pos + 1, max_len=p + 1, n_splits=n_splits,
+                                         schedule=schedule)
+            else:
+                kw = dict(pos0=p)
+                tq.quantize_append_kv(rot, k1, v1, xs, ys, **kw)
+                r1 = tq.decode_attention(rot, k1, v1, q, max_len=p + 1, n_splits=n_splits, schedule=schedule)
+            r2 = tq.append_decode_attention(rot, k2, v2, xs, ys, q, n_splits=n_splits, schedule=schedule, **kw)
+            torch.cuda.synchronize()
+            print("positions %s, splits %d" % ("device" if device_pos else "host", n_splits), flush=True)
+            for a, b in ((k1, k2), (v1, v2)):
+                assert torch.equal(a.codes, b.codes) and torch.equal(a.norms, b.norms)
+            for a, b in zip(r1, r2):
+                assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_single_token_steps_match_oracle(name):
     # a prefill, then one-token steps through the fused call (its single-token kernel) at
