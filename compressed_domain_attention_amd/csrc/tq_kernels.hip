@@ -91,6 +91,23 @@ __device__ void lds_rotate(float* buf, int nh, const float* signs, const float* 
   }
 }
 
+// The value of lane `lane ^ m` (m a power of two below 64).  Inside a 16-lane row the
+// exchange is a DPP lane move (quad permutes for 1 and 2, a shift left or right by 4, a
+// rotation by 8), with no round trip through the LDS crossbar; 16 and 32 cross rows with a
+// bpermute.  m is a constant after unrolling, so the branches fold.
+__device__ __forceinline__ float lane_xor(float x, int m, int lane) {
+  const int v = __builtin_bit_cast(int, x);
+  if (m == 1) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  if (m == 2) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  if (m == 4) {
+    const int from_above = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4, lane i + 4
+    const int from_below = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4, lane i - 4
+    return __builtin_bit_cast(float, (lane & 4) ? from_below : from_above);
+  }
+  if (m == 8) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  return __shfl_xor(x, m);
+}
+
 // Forward rotation of up to eight query heads in registers: wave w, lane l holds head
 // 2w + (l >> 5), coordinates 4(l & 31) .. +3 (one SO(4) block).  The first two Hadamard
 // stages are in-lane, the rest exchange with lane l ^ m inside the 32-lane half.  The
@@ -159,13 +176,17 @@ __device__ __forceinline__ QueryLane query_staged(const uint8_t* qraw, const flo
   return s;
 }
 
-__device__ __forceinline__ float4 query_rotate(const QueryLane& s, bool so4, int group, int lane) {
+template <int GROUP>
+__device__ __forceinline__ float4 query_rotate(const QueryLane& s, bool so4, int lane) {
+  constexpr int group = GROUP;
   float x0 = s.x.x * s.sg.x, x1 = s.x.y * s.sg.y, x2 = s.x.z * s.sg.z, x3 = s.x.w * s.sg.w;
   float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
   x0 = y0 + y2; x1 = y1 + y3; x2 = y0 - y2; x3 = y1 - y3;
+#pragma unroll
   for (int m = 1; m < group / 4; m <<= 1) {
     const bool up = (lane & m) != 0;
-    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    const float o0 = lane_xor(x0, m, lane), o1 = lane_xor(x1, m, lane), o2 = lane_xor(x2, m, lane),
+                o3 = lane_xor(x3, m, lane);
     x0 = up ? o0 - x0 : x0 + o0;
     x1 = up ? o1 - x1 : x1 + o1;
     x2 = up ? o2 - x2 : x2 + o2;
@@ -455,7 +476,7 @@ __device__ __forceinline__ void append_step_wave(const AppendArgs& ak, const App
   float x0 = x.x * sg.x, x1 = x.y * sg.y, x2 = x.z * sg.z, x3 = x.w * sg.w;
   float ss = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
 #pragma unroll
-  for (int m = 1; m < GROUP / 4; m <<= 1) ss += __shfl_xor(ss, m);
+  for (int m = 1; m < GROUP / 4; m <<= 1) ss += lane_xor(ss, m, lane);
   const float nrm = sqrtf(ss);
   const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
   x0 *= inv; x1 *= inv; x2 *= inv; x3 *= inv;
@@ -465,7 +486,8 @@ __device__ __forceinline__ void append_step_wave(const AppendArgs& ak, const App
 #pragma unroll
   for (int m = 1; m < GROUP / 4; m <<= 1) {
     const bool up = (lane & m) != 0;
-    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    const float o0 = lane_xor(x0, m, lane), o1 = lane_xor(x1, m, lane), o2 = lane_xor(x2, m, lane),
+                o3 = lane_xor(x3, m, lane);
     x0 = up ? o0 - x0 : x0 + o0;
     x1 = up ? o1 - x1 : x1 + o1;
     x2 = up ? o2 - x2 : x2 + o2;
@@ -495,7 +517,7 @@ __device__ __forceinline__ void append_step_wave(const AppendArgs& ak, const App
     // key record: word w = coordinates 8w..8w+7 = lanes 2w (low half) and 2w + 1
     const uint32_t half = BK == 3 ? (code[0] | code[1] << 3 | code[2] << 6 | code[3] << 9)
                                   : (code[0] | code[1] << 4 | code[2] << 8 | code[3] << 12);
-    const uint32_t other = __shfl_xor(half, 1);
+    const uint32_t other = __builtin_bit_cast(uint32_t, lane_xor(__builtin_bit_cast(float, half), 1, lane));
     uint8_t* rec = ak.codes + ((size_t)st * ak.capacity + slot) * (16 * BK);
     if ((pb & 1) == 0) {
       const int w = pb >> 1;
@@ -951,7 +973,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   {
     const QueryLane qlane = query_staged<QF16>((const uint8_t*)qbuf + wv * (2 * kHeadDim * 4), qstage, a.so4 != nullptr,
                                                u.hs, wv, lane);
-    float4 r = query_rotate(qlane, a.so4 != nullptr, a.rot_group, lane);
+    float4 r = query_rotate<NG == 4 ? 32 : 128>(qlane, a.so4 != nullptr, lane);
     const float qsc = a.scale_log2 / a.kscale;
     r.x *= qsc; r.y *= qsc; r.z *= qsc; r.w *= qsc;
     if (qlane.live) {
@@ -960,7 +982,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, lane_xor(mx, o, lane));
   if (lane == 0) red[wv] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -1329,32 +1351,34 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Log-sum-exp merge of key-axis splits plus the single inverse rotation.  One workgroup
-// per (sequence, query head): the split weights are formed once in LDS, then every thread
-// (coordinate) sums its column over the splits with independent, unrolled loads.
+// Log-sum-exp merge of key-axis splits plus the single inverse rotation.
 // Inverse of query_rotate for one head held by 32 lanes (4 coordinates each): SO(4)
 // inverse, the (self-inverse) normalised Hadamard, then the sign flips.
-__device__ __forceinline__ float4 unrotate4(float4 x, const QueryLane& s, bool so4, int group, int lane) {
+template <int GROUP>
+__device__ __forceinline__ float4 unrotate4(float4 x, const QueryLane& s, bool so4, int lane) {
   Quat v{x.x, x.y, x.z, x.w};
   if (so4) v = qmul(qmul(qconj(s.l), v), s.r);
   float x0 = v.w, x1 = v.x, x2 = v.y, x3 = v.z;
   float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
   x0 = y0 + y2; x1 = y1 + y3; x2 = y0 - y2; x3 = y1 - y3;
-  for (int m = 1; m < group / 4; m <<= 1) {
+#pragma unroll
+  for (int m = 1; m < GROUP / 4; m <<= 1) {
     const bool up = (lane & m) != 0;
-    const float o0 = __shfl_xor(x0, m), o1 = __shfl_xor(x1, m), o2 = __shfl_xor(x2, m), o3 = __shfl_xor(x3, m);
+    const float o0 = lane_xor(x0, m, lane), o1 = lane_xor(x1, m, lane), o2 = lane_xor(x2, m, lane),
+                o3 = lane_xor(x3, m, lane);
     x0 = up ? o0 - x0 : x0 + o0;
     x1 = up ? o1 - x1 : x1 + o1;
     x2 = up ? o2 - x2 : x2 + o2;
     x3 = up ? o3 - x3 : x3 + o3;
   }
-  const float hsc = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  const float hsc = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
   return make_float4(x0 * hsc * s.sg.x, x1 * hsc * s.sg.y, x2 * hsc * s.sg.z, x3 * hsc * s.sg.w);
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, query head) and the single
 // inverse rotation.  Every global read that does not depend on another is issued first:
 // the section lse values, the first partials, the signs and SO(4) parameters.
+template <int GROUP>
 __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   constexpr int kMaxStage = 1024;
   constexpr int kAhead = 16;  // partials held in registers ahead of the weights
@@ -1429,7 +1453,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   __syncthreads();
   if (wv == 0) {  // the whole first wave takes part in the lane exchanges
     const float4 x = *(const float4*)(obuf + 4 * (lane & 31));
-    const float4 y = unrotate4(x, rl, a.so4 != nullptr, a.rot_group, lane);
+    const float4 y = unrotate4<GROUP>(x, rl, a.so4 != nullptr, lane);
     if (rl.live) *(float4*)(a.out + (size_t)row * kHeadDim + 4 * lane) = y;
   }
   if (a.lse_out && c == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;
@@ -1523,7 +1547,12 @@ hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, stream, a);
+  const dim3 grid(a.batch * a.n_q_heads), block(128);
+  if (a.rot_group == 32) {
+    hipLaunchKernelGGL(merge_kernel<32>, grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
