@@ -769,9 +769,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int BK, int BV, int NG, bool QF16, bool QUAD>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a) {
-  constexpr int NW = 4;
+// NW waves per workgroup: 4 with two workgroups per CU, or 8 with one (grids of at most
+// one workgroup per CU, where four waves would leave one wave per SIMD).
+template <int BK, int BV, int NG, bool QF16, bool QUAD, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(const DecodeArgs a) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int NT = 64 * NW;
+  constexpr int LDS_BUDGET = NW == 4 ? 80 * 1024 : 160 * 1024;  // per workgroup
   // whole-head groups: the query's hi and lo parts take separate columns (8 + 8), so one
   // product per key operand suffices; 32-groups: columns are (group, head), two products
   constexpr bool SPLITQ = NG == 1;
@@ -807,15 +811,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   constexpr int S_K1 = 64 * LST, S_V0 = 128 * LST, S_V1 = S_V0 + 64 * LST, S_N = S_V1 + 64 * LST;
   constexpr int SLOT = S_N + 64 * NSZ;
   constexpr int RING_AT = VT_AT + VT_BYTES;
-  // two workgroups per CU: the pool and the other shared arrays (query rows, staged
-  // inputs, codebook, reductions) stay within 80 KB
+  // the pool and the other shared arrays (query rows, staged inputs, codebook, reductions)
+  // stay within the workgroup's share of the CU's 160 KB
   constexpr int STATIC_LDS = HPS * kHeadDim * 4 + (kHeadDim + 256) * 4 + 256;
-  constexpr int D = RING_AT + 3 * NW * SLOT + STATIC_LDS <= 80 * 1024 ? 3 : 2;
+  constexpr int D = RING_AT + 3 * NW * SLOT + STATIC_LDS <= LDS_BUDGET ? 3 : 2;
   constexpr int NDMA = 5;  // copies per block
   // the epilogue reuses the space for the per-wave partial results
   constexpr int SCR_BYTES = NPART * HPS * (kHeadDim + 2) * 4;
   constexpr int POOL = RING_AT + D * NW * SLOT > SCR_BYTES ? RING_AT + D * NW * SLOT : SCR_BYTES;
-  static_assert(POOL + STATIC_LDS <= 80 * 1024, "two workgroups per CU share its 160 KB of LDS");
+  static_assert(POOL + STATIC_LDS <= LDS_BUDGET, "the workgroups of a CU share its 160 KB of LDS");
   __shared__ __attribute__((aligned(16))) uint8_t pool[POOL];
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
   __shared__ __attribute__((aligned(16))) float qstage[kHeadDim + 256];  // signs, SO(4) parameters
@@ -948,22 +952,22 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   else vm_wait<0>();
   __syncthreads();
   if (QUAD) {
-    // Thread tid owns the entries whose two low codes are (tid >> 3) & 7, tid & 7 and whose
-    // third code is 2wv or 2wv + 1: the low half of its entries is fixed, and each step
-    // writes 64 consecutive entries.
+    // Thread tid owns the entries whose two low codes are (tid >> 3) & 7, tid & 7; wave wv
+    // takes 64 / NW of the 64 pairs of high codes.  The low half of a thread's entries is
+    // fixed, and each step writes 64 consecutive entries.
     const uint32_t lo = cbk[tid & 7] | (cbk[(tid >> 3) & 7] << 16);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c2 = 2 * wv + (j & 1), c3 = j >> 1;
+    for (int j = 0; j < 64 / NW; ++j) {
+      const int hc = wv * (64 / NW) + j, c2 = hc & 7, c3 = hc >> 3;
       ((uint2*)pool)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, cbk[c2] | (cbk[c3] << 16));
     }
   } else {
-    for (int i = tid; i < NEK * RK; i += 256) {
+    for (int i = tid; i < NEK * RK; i += NT) {
       const int e = i / RK;
       ((uint32_t*)pool)[i] = cbk[e & ((1 << BK) - 1)] | (cbk[e >> BK] << 16);
     }
   }
-  for (int i = tid; i < (QUAD ? 0 : NEV * RV); i += 256) {
+  for (int i = tid; i < (QUAD ? 0 : NEV * RV); i += NT) {
     const int e = i / RV;
     ((uint32_t*)(pool + VT_AT))[i] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
   }
@@ -985,7 +989,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, lane_xor(mx, o, lane));
   if (lane == 0) red[wv] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
   int ex = 0;
   if (mx > 0.f && mx < INFINITY) (void)frexpf(mx, &ex);
   const float qs = ldexpf(1.f, 14 - ex), qinv = ldexpf(1.f, ex - 14);
@@ -1192,7 +1198,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeArgs a)
     }
   }
   __syncthreads();
-  for (int i = tid; i < u.hs * kHeadDim; i += 256) {
+  for (int i = tid; i < u.hs * kHeadDim; i += NT) {
     const int hl = i >> 7, c = i & 127;
     float M = -INFINITY;
 #pragma unroll
@@ -1513,16 +1519,34 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
   return hipErrorInvalidValue;
 }
 
+// Compute units of the current device, read once per device.
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream) {
   const int units = a.batch * a.n_kv_heads * a.n_splits * a.n_slices;
   const dim3 grid(units), block(256);
   const int ng = kHeadDim / a.rot_group;
   if (schedule == 2) {
-#define TQ_MF(BK, BV, NG, QF, QD)                                                              \
-  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF && shared_table == QD) {          \
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD>), grid, block, 0, stream, a);    \
-    return hipGetLastError();                                                                  \
+    // a grid that leaves CUs without a second workgroup runs eight waves per workgroup
+    const int nw = units <= device_cus() ? 8 : 4;
+#define TQ_MF(BK, BV, NG, QF, QD)                                                                  \
+  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF && shared_table == QD) {              \
+    if (nw == 8)                                                                                   \
+      hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, 8>), grid, dim3(512), 0, stream, a); \
+    else                                                                                           \
+      hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, 4>), grid, dim3(256), 0, stream, a); \
+    return hipGetLastError();                                                                      \
   }
 #define TQ_MF_Q(BK, BV, NG, QD) TQ_MF(BK, BV, NG, true, QD) TQ_MF(BK, BV, NG, false, QD)
 #define TQ_MF_NG(BK, BV, QD) TQ_MF_Q(BK, BV, 4, QD) TQ_MF_Q(BK, BV, 1, QD)
