@@ -55,6 +55,31 @@ def decode(q, k, v, seq_lens, scale):
     return out, lse
 
 
+def decode_two_stores(q, k_a, v_a, lens_a, k_b, v_b, lens_b, scale):
+    """Attention of every query row over the union of two token stores of its row.
+
+    Store a holds the quantised tokens (already dequantised), store b the unquantised ones:
+    the prefill kept in fp16 while decode-phase tokens are quantised ("RotaryQuant ...",
+    method overview), or a window of recent tokens ("RoPE-Aware Bit Allocation ...", results:
+    the recent-token buffer).  Softmax attention is a sum over the row's tokens, so the union
+    is their concatenation: k_a[b, kv, :lens_a[b]] followed by k_b[b, kv, :lens_b[b]].
+    Returns (out[B, Hq, d], lse[B, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, d = q.shape
+    g = hq // k_a.shape[1]
+    out = np.zeros((bsz, hq, d))
+    lse = np.zeros((bsz, hq))
+    for b in range(bsz):
+        la, lb = int(lens_a[b]), int(lens_b[b])
+        for h in range(hq):
+            kv = h // g
+            k = np.concatenate([np.asarray(k_a[b, kv, :la], np.float64), np.asarray(k_b[b, kv, :lb], np.float64)])
+            v = np.concatenate([np.asarray(v_a[b, kv, :la], np.float64), np.asarray(v_b[b, kv, :lb], np.float64)])
+            out[b, h], lse[b, h] = softmax_attend(q[b, h], k, v, scale)
+    return out, lse
+
+
 def split_bounds(t, n_splits):
     """Token ranges of the key-axis splits: chunk C = ceil(t / S)."""
     c = -(-t // n_splits) if t > 0 else 0

@@ -77,6 +77,52 @@ def test_split_merge_equals_unsplit(n_splits):
     np.testing.assert_allclose(lse2, lse, rtol=1e-13)
 
 
+def test_two_stores_closed_form():
+    # one token in each store, scores 0 and ln 3: weights 1/4 and 3/4, lse = ln 4
+    scale = 0.5
+    q = np.zeros((1, 1, 128))
+    q[0, 0, 0] = 1.0
+    ka = np.zeros((1, 1, 1, 128))
+    kb = np.zeros((1, 1, 1, 128))
+    kb[0, 0, 0, 0] = math.log(3.0) / scale
+    rng = np.random.default_rng(30)
+    va, vb = rng.standard_normal((1, 1, 1, 128)), rng.standard_normal((1, 1, 1, 128))
+    out, lse = attention.decode_two_stores(q, ka, va, [1], kb, vb, [1], scale)
+    np.testing.assert_allclose(out[0, 0], 0.25 * va[0, 0, 0] + 0.75 * vb[0, 0, 0], rtol=1e-14, atol=1e-15)
+    assert abs(lse[0, 0] - math.log(4.0)) < 1e-14
+
+
+def test_two_stores_against_sdpa_and_invariants():
+    rng = np.random.default_rng(31)
+    b, hq, hkv = 2, 8, 2
+    la, lb = np.array([40, 0]), np.array([9, 17])
+    q = rng.standard_normal((b, hq, 128))
+    ka, va = rng.standard_normal((b, hkv, 40, 128)) * 2, rng.standard_normal((b, hkv, 40, 128))
+    kb, vb = rng.standard_normal((b, hkv, 17, 128)) * 2, rng.standard_normal((b, hkv, 17, 128))
+    scale = 128 ** -0.5
+    out, lse = attention.decode_two_stores(q, ka, va, la, kb, vb, lb, scale)
+    # the library routine on the concatenated rows
+    for i in range(b):
+        k = np.concatenate([ka[i, :, :la[i]], kb[i, :, :lb[i]]], axis=1)
+        v = np.concatenate([va[i, :, :la[i]], vb[i, :, :lb[i]]], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[i:i + 1])[:, :, None], torch.from_numpy(k[None]), torch.from_numpy(v[None]),
+            scale=scale, enable_gqa=True)[0, :, 0]
+        np.testing.assert_allclose(out[i], ref.numpy(), rtol=1e-12, atol=1e-13)
+    # the stores' order does not matter; an empty store reduces to the other alone
+    out2, lse2 = attention.decode_two_stores(q, kb, vb, lb, ka, va, la, scale)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+    only_b, lse_b = attention.decode(q, kb, vb, lb, scale)
+    np.testing.assert_allclose(out[1], only_b[1], rtol=1e-12, atol=1e-13)
+    # and the union is the log-sum-exp merge of the two stores' section partials
+    pa, la_s = attention.decode_splits(q, ka, va, la, scale, 3)
+    pb, lb_s = attention.decode_splits(q, kb, vb, lb, scale, 2)
+    m, ml = attention.merge(np.concatenate([pa, pb]), np.concatenate([la_s, lb_s]))
+    np.testing.assert_allclose(m, out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml, lse, rtol=1e-13)
+
+
 def test_split_bounds_and_all_empty_merge():
     assert attention.split_bounds(10, 3) == [(0, 4), (4, 8), (8, 10)]
     assert attention.split_bounds(2, 4) == [(0, 1), (1, 2), (2, 2), (2, 2)]
