@@ -206,6 +206,119 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
                 reps=reps, cache_bytes=cache_bytes, parity=parity, decode_launches=reps_dec * n_dec)
 
 
+def run_tail(w, inp, n_tail, tail_splits, steps, warmup, n_splits, schedule):
+    """The step with an unquantised tail of n_tail tokens per row (the pages' fp16 prefill or
+    recent-token window): the packed append+decode launch into sections 0..S-1, dense attention
+    over the tail into the next tail_splits sections, one merge over all of them.  The tail is
+    the workload's first n_tail key/value vectors in its own dtype."""
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    from oracle import attention, codebook, quant
+
+    dev = torch.device("cuda:0")
+    T = w.seq_len
+    cap = (T + 31) // 32 * 32
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).to(dev)
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).to(dev), w.group, so4)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev)
+    v0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev)
+    tq.quantize_append(rot, k0, torch.from_numpy(inp["k"]).to(dev))
+    tq.quantize_append(rot, v0, torch.from_numpy(inp["v"]).to(dev))
+    newk = torch.from_numpy(inp["k"][:, :, T - 1:T].copy()).to(dev)
+    newv = torch.from_numpy(inp["v"][:, :, T - 1:T].copy()).to(dev)
+    kt = torch.from_numpy(inp["k"][:, :, :n_tail].copy()).to(dev)
+    vt = torch.from_numpy(inp["v"][:, :, :n_tail].copy()).to(dev)
+    cache_bytes = sum(t.numel() * t.element_size() for t in (k0.codes, k0.norms, v0.codes, v0.norms))
+    reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
+    caches = [(k0, v0)] + [
+        (tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev, codes=k0.codes.clone(),
+                        norms=k0.norms.clone()),
+         tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev, codes=v0.codes.clone(),
+                        norms=v0.norms.clone())) for _ in range(reps - 1)]
+    S, St = n_splits, tail_splits
+    po = torch.empty((S + St, w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((S + St, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+
+    def dense(i):
+        tq.dense_attention(rot, kt, vt, q, max_len=n_tail, n_splits=St, part_o=po[S:], part_lse=pl[S:])
+
+    def step(i):
+        k, v = caches[i % reps]
+        tq.append_decode_attention(rot, k, v, newk, newv, q, pos0=T - 1, n_splits=S, schedule=schedule,
+                                   part_o=po[:S], part_lse=pl[:S])
+        dense(i)
+        tq.merge_splits(rot, po, pl, out=out, lse=lse)
+
+    def graph(fn, n):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < 0.3:
+        graphs[i % reps].replay()
+        i += 1
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % reps].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    gd = graph(dense, 16)
+    gd.replay()
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_d = time.perf_counter()
+    n_rep = 0
+    d0.record()
+    while time.perf_counter() - t_d < 0.5:
+        gd.replay()
+        n_rep += 1
+        if n_rep % 64 == 0:
+            torch.cuda.synchronize()
+    d1.record()
+    torch.cuda.synchronize()
+    dense_ms = d0.elapsed_time(d1) / (16 * n_rep)
+
+    # sampled parity: two (sequence, KV head) units against the oracle over packed + tail
+    from helpers import OUT_RTOL, row_rel_err
+    o = out.cpu().numpy()
+    worst = 0.0
+    ck, mk = codebook.lloyd_max(w.bits_k, w.group)
+    cv, mv = codebook.lloyd_max(w.bits_v, w.group)
+    for b, kv in [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
+        so = None if inp["so4"] is None else inp["so4"][kv]
+        sg = inp["signs"][kv]
+        ki, kn, _ = quant.quantize(inp["k"][b, kv].astype(np.float64), sg, w.group, ck, mk, so)
+        vi, vn, _ = quant.quantize(inp["v"][b, kv].astype(np.float64), sg, w.group, cv, mv, so)
+        kd = np.concatenate([quant.dequantize(ki, kn, sg, w.group, ck, so), inp["k"][b, kv, :n_tail]])
+        vd = np.concatenate([quant.dequantize(vi, vn, sg, w.group, cv, so), inp["v"][b, kv, :n_tail]])
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            worst = max(worst, float(row_rel_err(o[b, h], ref)))
+    if worst > OUT_RTOL:
+        raise SystemExit("parity check failed: %.3e > %.1e" % (worst, OUT_RTOL))
+    tail_bytes = 2 * w.batch * w.n_kv_heads * n_tail * 128 * kt.element_size()
+    return dict(step_ms=step_ms, dense_ms=dense_ms, tail_bytes=tail_bytes, parity=worst, reps=reps)
+
+
 def sampled_parity(w, inp, out):
     """Oracle check of a few (sequence, query head) rows of the measured output."""
     from helpers import OUT_RTOL, row_rel_err
@@ -410,6 +523,9 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "mfma", "vec"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--tail", type=int, default=0,
+                    help="an unquantised tail of this many tokens per row (dense sections merged with the packed ones)")
+    ap.add_argument("--tail-splits", type=int, default=None)
     ap.add_argument("--counter-run", action="store_true",
                     help="only issue the calibration copies and decode launches (run under rocprofv3 --pmc)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -441,6 +557,30 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.counter_run:
         counter_run(w, inp, n_splits, args.schedule)
+        return
+    if args.tail > w.seq_len:
+        raise SystemExit("--tail takes at most the workload's %d generated tokens" % w.seq_len)
+    if args.tail > 0:
+        # enough sections for about 512 workgroups, at most one per 64-token chunk
+        slices = -(-w.group_size // 8)
+        tail_splits = args.tail_splits or max(1, min(-(-args.tail // 64), -(-512 // (w.batch * w.n_kv_heads * slices))))
+        r = run_tail(w, inp, args.tail, tail_splits, args.steps, args.warmup, n_splits, args.schedule)
+        units = w.batch * w.n_kv_heads * (w.seq_len + args.tail)
+        dense_gbs = r["tail_bytes"] / (r["dense_ms"] / 1e3) / 1e9
+        log("step %.3f ms with a %d-token %s tail; dense kernel %.4f ms -> %.0f GB/s (%.1f%% of 8 TB/s); parity %.2e" % (
+            r["step_ms"], args.tail, w.dtype, r["dense_ms"], dense_gbs, 100 * dense_gbs / HBM_PEAK_GBS, r["parity"]))
+        print(json.dumps({
+            "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands (packed); f32 FMA (tail)",
+            "data": "synthetic (seeded Gaussian activations with outlier channels; workloads.py)",
+            "config": {"workload": "%s+tail%d" % (w.name, args.tail), "n_splits": n_splits, "tail_tokens": args.tail,
+                       "tail_splits": tail_splits, "tail_dtype": w.dtype,
+                       "step": "append+decode launch, dense tail launch, merge", "cache_replicas": r["reps"]},
+            "roofline": {"bound": "hbm", "achieved": dense_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dense_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "dense_kernel"},
+            "cpu_baseline": cpu, "dense_kernel_ms": r["dense_ms"], "tail_bytes_per_launch": r["tail_bytes"],
+            "parity_worst_row_rel_err": r["parity"]}), flush=True)
         return
     r = run_gpu(w, inp, args.steps, args.warmup, n_splits, args.schedule, check=not args.no_check)
     units = w.batch * w.n_kv_heads * w.seq_len

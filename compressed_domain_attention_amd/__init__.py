@@ -65,7 +65,7 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
-           "tq_decode_attention", "tq_append_decode_attention", "tq_merge_splits")
+           "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits")
 
 
 def library():
@@ -93,6 +93,8 @@ def library():
                                                ctypes.POINTER(_Cache), P, P, I, P, I, I, P, I, I, F, I, I, P, P, P,
                                                P, P]
     lib.tq_append_decode_attention.restype = I
+    lib.tq_dense_attention.argtypes = [ctypes.POINTER(_Rotation), P, P, I, I, I, P, I, I, P, I, F, I, P, P, P]
+    lib.tq_dense_attention.restype = I
     lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
     lib.tq_merge_splits.restype = I
     _lib = lib
@@ -250,6 +252,41 @@ def append_decode_attention(rot: Rotation, keys: PackedCache, values: PackedCach
         _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits, _SCHEDULES[schedule], _ptr(out),
         _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_append_decode_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+def dense_attention(rot: Rotation, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, seq_lens=None, max_len=None,
+                    scale=None, n_splits=1, part_o=None, part_lse=None):
+    """Attention over unquantised k, v [batch, n_kv_heads, capacity, 128] (fp16/fp32) as n_splits
+    section partials in the packed cache's rotated domain -> (part_o, part_lse).  part_o and
+    part_lse may be views of a larger partial buffer (sections after the packed ones)."""
+    for x in (k, v):
+        if x.dtype not in _DTYPES or not x.is_contiguous() or x.dim() != 4 or x.shape[3] != HEAD_DIM:
+            raise ValueError("k and v must be contiguous [batch, n_kv_heads, capacity, 128] float16/float32")
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same dtype and shape")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    if k.shape[0] != bsz or k.shape[1] != rot.n_kv_heads:
+        raise ValueError("k and v must be [batch, n_kv_heads, capacity, 128] for this query and rotation")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
+        raise ValueError("seq_lens must be int32 [batch]")
+    cap = k.shape[2]
+    if max_len is None:
+        max_len = int(seq_lens.max().item()) if seq_lens is not None else cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    if part_o is None:
+        part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=q.device)
+    for t, shape in ((part_o, (n_splits, bsz, hq, HEAD_DIM)), (part_lse, (n_splits, bsz, hq))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous float32 of shape %s" % (shape,))
+    _check(library().tq_dense_attention(
+        ctypes.byref(rot.c), _ptr(k), _ptr(v), _DTYPES[k.dtype], bsz, cap, _ptr(q), _DTYPES[q.dtype], hq,
+        _ptr(seq_lens), max_len, scale, n_splits, _ptr(part_o), _ptr(part_lse), _stream()), "tq_dense_attention")
+    return part_o, part_lse
 
 
 def merge_splits(rot: Rotation, part_o: torch.Tensor, part_lse: torch.Tensor, out=None, lse=None):

@@ -208,6 +208,41 @@ extern "C" tq_status tq_append_decode_attention(const tq_rotation* rot, const tq
   return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, s));
 }
 
+extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* v, tq_dtype kv_dtype,
+                                        int32_t batch, int32_t capacity, const void* q, tq_dtype q_dtype,
+                                        int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                                        int32_t n_splits, float* part_o, float* part_lse, void* stream) {
+  tq_status st = check_rotation(rot);
+  if (st != TQ_OK) return st;
+  if (k == nullptr || v == nullptr || q == nullptr || part_o == nullptr || part_lse == nullptr) return TQ_EINVAL;
+  if ((kv_dtype != TQ_F32 && kv_dtype != TQ_F16) || (q_dtype != TQ_F32 && q_dtype != TQ_F16)) return TQ_EINVAL;
+  if (batch <= 0 || capacity <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
+  if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (max_len > capacity) return TQ_ECAPACITY;
+  tq::DenseArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.signs = rot->signs;
+  a.so4 = rot->so4;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.max_len = max_len;
+  a.batch = batch;
+  a.n_kv_heads = rot->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group_size = n_q_heads / rot->n_kv_heads;
+  a.heads_per_slice = a.group_size < 8 ? a.group_size : 8;
+  a.n_slices = (a.group_size + a.heads_per_slice - 1) / a.heads_per_slice;
+  a.n_splits = n_splits;
+  a.capacity = capacity;
+  a.rot_group = rot->group;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(tq::launch_dense(a, kv_dtype == TQ_F16, q_dtype == TQ_F16, (hipStream_t)stream));
+}
+
 extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,
                                      const float* part_o, const float* part_lse, float* out, float* lse_out,
                                      void* stream) {

@@ -60,6 +60,30 @@ struct DecodeArgs {
   AppendArgs ak, av;
 };
 
+// Attention over an unquantised (fp16/fp32) K/V region, written as key-axis section partials
+// in the rotated domain so that they merge with the packed sections.
+struct DenseArgs {
+  const void* k;            // [batch][n_kv_heads][capacity][128]
+  const void* v;
+  const void* q;            // [batch][n_q_heads][128]
+  const int32_t* seq_lens;  // [batch] or null
+  const float* signs;
+  const float* so4;
+  float* part_o;            // [n_splits][batch][n_q_heads][128]
+  float* part_lse;          // [n_splits][batch][n_q_heads]
+  int32_t max_len;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t group_size;
+  int32_t heads_per_slice;
+  int32_t n_slices;
+  int32_t n_splits;
+  int32_t capacity;
+  int32_t rot_group;
+  float scale_log2;
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
@@ -84,6 +108,7 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
 // shared_table: 3-bit keys and values with identical codebooks (one four-code table)
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream);
+hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 // Heads one workgroup of the matrix-core schedule can serve: the 16 MFMA columns hold

@@ -823,7 +823,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   __shared__ __attribute__((aligned(16))) uint8_t pool[POOL];
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
   __shared__ __attribute__((aligned(16))) float qstage[kHeadDim + 256];  // signs, SO(4) parameters
-  __shared__ uint32_t cbk[16], cbv[16];
   __shared__ float red[NW];
   __shared__ float lse2[HPS];
   const uint8_t* ktab = pool;
@@ -834,6 +833,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   asm volatile("" ::"s"(a.kc), "s"(a.kn), "s"(a.vc), "s"(a.vn), "s"(a.q), "s"(a.seq_lens), "s"(a.signs), "s"(a.so4));
   asm volatile("" ::"s"(a.max_len), "s"(a.len_bias), "s"(a.batch), "s"(a.n_kv_heads), "s"(a.n_q_heads), "s"(a.group_size),
                "s"(a.heads_per_slice), "s"(a.n_slices), "s"(a.n_splits), "s"(a.capacity));
+  asm volatile("" ::"s"(a.kscale), "s"(a.kcent[0]), "s"(a.kcent[8]), "s"(a.vcent[0]), "s"(a.vcent[8]));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Unit u = decode_unit(a, true);
@@ -934,43 +934,50 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     }
     return d;
   };
-  if (nblk > 0) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch(j);
+  for (int j = 0; j < D; ++j) {
+    if (j < nblk) fetch(j);
   }
 
-  // ---- decode tables.  The codebook comes from the kernel arguments at constant offsets
-  // (scalar loads, which the copies' wait does not involve).
-  if (tid == 0) {
+  // ---- decode tables, built while the staged inputs are in flight.  The codebook's fp16
+  // values (kernel arguments at constant offsets: scalar loads) go to lanes 0-15 of one
+  // register (lane c selects value c), and each thread takes its entries' values by lane
+  // exchange.
+  int kcb = 0, vcb = 0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      cbk[c] = f16_bits((_Float16)(a.kcent[c] * a.kscale));
-      cbv[c] = f16_bits((_Float16)(QUAD ? a.vcent[c] * a.kscale : a.vcent[c]));
+  for (int c = 0; c < 16; ++c) {
+    if (lane == c) {
+      kcb = (int)f16_bits((_Float16)(a.kcent[c] * a.kscale));
+      vcb = (int)f16_bits((_Float16)(QUAD ? a.vcent[c] * a.kscale : a.vcent[c]));
     }
   }
-  if (nblk > 0) vm_wait<NDMA * D>();  // the staged inputs (copied first) have landed
-  else vm_wait<0>();
-  __syncthreads();
   if (QUAD) {
     // Thread tid owns the entries whose two low codes are (tid >> 3) & 7, tid & 7; wave wv
     // takes 64 / NW of the 64 pairs of high codes.  The low half of a thread's entries is
     // fixed, and each step writes 64 consecutive entries.
-    const uint32_t lo = cbk[tid & 7] | (cbk[(tid >> 3) & 7] << 16);
+    const uint32_t lo = (uint32_t)__shfl(kcb, tid & 7) | ((uint32_t)__shfl(kcb, (tid >> 3) & 7) << 16);
 #pragma unroll
     for (int j = 0; j < 64 / NW; ++j) {
       const int hc = wv * (64 / NW) + j, c2 = hc & 7, c3 = hc >> 3;
-      ((uint2*)pool)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, cbk[c2] | (cbk[c3] << 16));
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(kcb, c2) | ((uint32_t)__builtin_amdgcn_readlane(kcb, c3) << 16);
+      ((uint2*)pool)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, hi);
     }
   } else {
     for (int i = tid; i < NEK * RK; i += NT) {
       const int e = i / RK;
-      ((uint32_t*)pool)[i] = cbk[e & ((1 << BK) - 1)] | (cbk[e >> BK] << 16);
+      ((uint32_t*)pool)[i] = (uint32_t)__shfl(kcb, e & ((1 << BK) - 1)) | ((uint32_t)__shfl(kcb, e >> BK) << 16);
     }
   }
   for (int i = tid; i < (QUAD ? 0 : NEV * RV); i += NT) {
     const int e = i / RV;
-    ((uint32_t*)(pool + VT_AT))[i] = cbv[e & ((1 << BV) - 1)] | (cbv[e >> BV] << 16);
+    ((uint32_t*)(pool + VT_AT))[i] = (uint32_t)__shfl(vcb, e & ((1 << BV) - 1)) | ((uint32_t)__shfl(vcb, e >> BV) << 16);
   }
+  // the staged inputs (copied before the ring's min(D, nblk) blocks) have landed
+  if (nblk >= D) vm_wait<NDMA * D>();
+  else if (D == 3 && nblk == 2) vm_wait<2 * NDMA>();
+  else if (nblk >= 1) vm_wait<NDMA>();
+  else vm_wait<0>();
+  __syncthreads();
 
   // ---- rotated, scaled query (log2 units) with a power-of-two prescale into fp16 range
   float mx = 0.f;
@@ -1043,7 +1050,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   f32x4 O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();  // tables complete
 
   auto process = [&](const Block<BK, BV>& cb, int blk) {
     // Table reads are issued in batches ahead of their consumers so that LDS latency
@@ -1163,14 +1169,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     for (int w = 0; w < 8; ++w) O[w] = mfma16(va[w], bp, O[w]);
   };
 
-  // Block j waits until the copies of every older block are complete (the D - 1 younger
-  // blocks may still be in flight), is read into registers, and once those reads are
-  // complete its slot is refilled with block j + D, so D blocks load during the arithmetic.
+  // Block j waits until its copies are complete (the younger blocks, at most D - 1, may
+  // still be in flight; copies complete in issue order), is read into registers, and once
+  // those reads are complete its slot is refilled with block j + D, so D blocks load
+  // during the arithmetic.  No copy is issued past the wave's last block.
   for (int j = 0; j < nblk; ++j) {
-    vm_wait<NDMA * (D - 1)>();
+    const int younger = min(D - 1, nblk - 1 - j);  // wave-uniform
+    if (younger == D - 1) vm_wait<NDMA * (D - 1)>();
+    else if (younger == 1) vm_wait<NDMA>();
+    else vm_wait<0>();
     const Block<BK, BV> cb = read_block(j);
     lds_wait();
-    fetch(j + D);
+    if (j + D < nblk) fetch(j + D);
     process(cb, blk0 + wv + NW * j);
   }
   vm_wait<0>();  // no copy may land in the pool once it is reused below
@@ -1211,11 +1221,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
       L += sl[w * HPS + hl] * f;
       acc += so[(w * HPS + hl) * kHeadDim + c] * f;
     }
-    qbuf[i] = L > 0.f ? (QUAD ? acc / (L * a.kscale) : acc / L) : 0.f;
-    if (c == 0) lse2[hl] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    const float o = L > 0.f ? (QUAD ? acc / (L * a.kscale) : acc / L) : 0.f;
+    const float lse = L > 0.f ? M + __log2f(L) : -INFINITY;
+    if (a.n_splits > 1) {
+      // a section's partial stays in the rotated domain: written straight from here
+      const size_t row = ((size_t)u.split * a.batch + u.b) * a.n_q_heads + u.h0 + hl;
+      a.part_o[row * kHeadDim + c] = o;
+      if (c == 0) a.part_lse[row] = lse * kLn2;
+    } else {
+      qbuf[i] = o;
+      if (c == 0) lse2[hl] = lse;
+    }
   }
-  __syncthreads();
-  write_result(a, u, qbuf, lse2);
+  if (a.n_splits == 1) {
+    __syncthreads();
+    write_result(a, u, qbuf, lse2);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1354,6 +1375,220 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
   }
   __syncthreads();
   write_result(a, u, qbuf, lse2);
+}
+
+// ---------------------------------------------------------------------------------------
+// Attention over an unquantised K/V region (fp16 or fp32): the prefill kept in fp16, or a
+// window of recent tokens ("RotaryQuant ...", method overview: deferred prefill; "RoPE-Aware
+// Bit Allocation ...", results: the recent-token buffer).  Same section split as the packed
+// decode; each section's partial is rotated forward by R, so that it is in the rotated domain
+// of the packed partials and the merge's one inverse rotation applies to both.
+//
+// One workgroup per (sequence, KV head, section, head slice of up to 8 heads), 64-token
+// chunks: thread (token, quarter) forms 32-coordinate partial scores for every head, summed
+// over the four quarter lanes by DPP; one wave per head runs the online softmax over the
+// chunk; thread (8 coordinates, token slot) accumulates 4 tokens of each chunk per head.
+// Raw 16-byte words of one thread's share of a 64-token chunk: 32 key values of its score
+// token, 8 value coordinates of each of its 4 value tokens; converted to fp32 when used.
+template <bool KV16>
+struct DenseRaw {
+  static constexpr int KW = KV16 ? 4 : 8;  // 16-byte words per 32 values
+  static constexpr int VW = KV16 ? 1 : 2;  // per 8 values
+  uint4 k[KW];
+  uint4 v[4][VW];
+};
+
+template <bool KV16>
+__device__ __forceinline__ void unpack8(const uint4* w, float* out) {
+  if (KV16) {
+    const uint32_t x[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+      const h2_t h = __builtin_bit_cast(h2_t, x[j]);
+      out[2 * j] = (float)h[0];
+      out[2 * j + 1] = (float)h[1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      out[4 * j] = __uint_as_float(w[j].x);
+      out[4 * j + 1] = __uint_as_float(w[j].y);
+      out[4 * j + 2] = __uint_as_float(w[j].z);
+      out[4 * j + 3] = __uint_as_float(w[j].w);
+    }
+  }
+}
+
+template <bool KV16, bool QF16>
+__global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
+  constexpr int MAXH = 8;
+  constexpr int ES = KV16 ? 2 : 4;  // bytes per value
+  __shared__ __attribute__((aligned(16))) float qb[MAXH * kHeadDim];  // scaled query, later the output
+  __shared__ float pw[MAXH][64];                                      // chunk scores, then weights
+  __shared__ float hm[MAXH], hsum[MAXH], halpha[MAXH];
+  __shared__ __attribute__((aligned(16))) float ob[4][MAXH][kHeadDim];  // per-wave value sums
+  __shared__ float lse2[MAXH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int unit = blockIdx.x / a.n_slices, slice = blockIdx.x - unit * a.n_slices;
+  const int split = unit % a.n_splits, kv = (unit / a.n_splits) % a.n_kv_heads;
+  const int b = unit / (a.n_splits * a.n_kv_heads);
+  const int h0 = kv * a.group_size + slice * a.heads_per_slice;
+  const int hs = min(a.heads_per_slice, a.group_size - slice * a.heads_per_slice);
+  // lengths beyond max_len (checked against the capacity on the host) are clamped
+  const int T = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_len)) : a.max_len;
+  const int C = (T + a.n_splits - 1) / a.n_splits;
+  const int lo = min(T, split * C), hi = min(T, lo + C);
+
+  const size_t row0 = ((size_t)b * a.n_kv_heads + kv) * a.capacity;  // first token row of the stream
+  const int st = tid >> 2, qd = tid & 3;                              // scores: token, quarter
+  const int dg = tid & 15, ts = tid >> 4;                             // values: 8 coordinates, slot
+  const uint8_t* kb = (const uint8_t*)a.k + row0 * kHeadDim * ES;
+  const uint8_t* vb = (const uint8_t*)a.v + row0 * kHeadDim * ES;
+  // this thread's raw words of the chunk at c0 (tokens past the section are not read)
+  auto fetch = [&](int c0, DenseRaw<KV16>& r) {
+    const int tk = c0 + st;
+    if (tk < hi) {
+      const uint4* p = (const uint4*)(kb + ((size_t)tk * kHeadDim + 32 * qd) * ES);
+#pragma unroll
+      for (int i = 0; i < DenseRaw<KV16>::KW; ++i) r.k[i] = p[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tv = c0 + ts + 16 * j;
+      if (tv < hi) {
+        const uint4* p = (const uint4*)(vb + ((size_t)tv * kHeadDim + 8 * dg) * ES);
+#pragma unroll
+        for (int i = 0; i < DenseRaw<KV16>::VW; ++i) r.v[j][i] = p[i];
+      }
+    }
+  };
+  DenseRaw<KV16> nxt;
+  if (lo < hi) fetch(lo, nxt);  // the first chunk's reads overlap the query set-up
+
+  for (int i = tid; i < hs * kHeadDim; i += 256) {
+    const size_t qi = ((size_t)b * a.n_q_heads + h0 + (i >> 7)) * kHeadDim + (i & 127);
+    qb[i] = (QF16 ? (float)((const _Float16*)a.q)[qi] : ((const float*)a.q)[qi]) * a.scale_log2;
+  }
+  if (tid < MAXH) {
+    hm[tid] = -INFINITY;
+    hsum[tid] = 0.f;
+  }
+  __syncthreads();
+
+  float acc[MAXH][8];
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  for (int c0 = lo; c0 < hi; c0 += 64) {
+    const DenseRaw<KV16> cur = nxt;
+    if (c0 + 64 < hi) fetch(c0 + 64, nxt);  // the next chunk loads during this one
+    // scores of the chunk's tokens, all heads (scale and log2 e folded into the query)
+    {
+      const int tok = c0 + st;
+      float kx[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack8<KV16>(cur.k + i * (KV16 ? 1 : 2), kx + 8 * i);
+#pragma unroll
+      for (int h = 0; h < MAXH; ++h) {
+        if (h < hs) {
+          const float4* qp = (const float4*)(qb + h * kHeadDim + 32 * qd);
+          float sc = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float4 qq = qp[i];
+            sc = fmaf(qq.x, kx[4 * i], sc);
+            sc = fmaf(qq.y, kx[4 * i + 1], sc);
+            sc = fmaf(qq.z, kx[4 * i + 2], sc);
+            sc = fmaf(qq.w, kx[4 * i + 3], sc);
+          }
+          sc += lane_xor(sc, 1, lane);
+          sc += lane_xor(sc, 2, lane);
+          if (qd == 0) pw[h][st] = tok < hi ? sc : -INFINITY;  // tokens past the section are masked
+        }
+      }
+    }
+    __syncthreads();
+    // online softmax per head over the chunk (log2 units)
+    for (int h = wv; h < hs; h += 4) {
+      const float sc = pw[h][lane];
+      float bm = sc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) bm = fmaxf(bm, lane_xor(bm, o, lane));
+      const float mold = hm[h];
+      const float mnew = fmaxf(mold, bm);
+      const float al = mnew > mold ? __builtin_amdgcn_exp2f(mold - mnew) : 1.f;
+      const float mu = mnew == -INFINITY ? 0.f : mnew;
+      const float p = __builtin_amdgcn_exp2f(sc - mu);
+      float psum = p;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) psum += lane_xor(psum, o, lane);
+      pw[h][lane] = p;
+      if (lane == 0) {
+        hm[h] = mnew;
+        hsum[h] = hsum[h] * al + psum;
+        halpha[h] = al;
+      }
+    }
+    __syncthreads();
+    // value sums: tokens ts, ts + 16, ts + 32, ts + 48 of the chunk, coordinates 8dg .. +7
+    {
+#pragma unroll
+      for (int h = 0; h < MAXH; ++h) {
+        if (h < hs) {
+          const float al = halpha[h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + ts + 16 * j < hi) {
+          float vx[8];
+          unpack8<KV16>(cur.v[j], vx);
+#pragma unroll
+          for (int h = 0; h < MAXH; ++h) {
+            if (h < hs) {
+              const float p = pw[h][ts + 16 * j];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // the weights are rewritten by the next chunk
+  }
+
+  // sum the 16 token slots (lane bits 4, 5, then the four waves), normalise
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h) {
+    if (h < hs) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[h][e];
+        x += lane_xor(x, 16, lane);
+        x += lane_xor(x, 32, lane);
+        if ((lane >> 4) == 0) ob[wv][h][8 * dg + e] = x;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < hs * kHeadDim; i += 256) {
+    const int h = i >> 7, c = i & 127;
+    const float L = hsum[h];
+    qb[i] = L > 0.f ? (ob[0][h][c] + ob[1][h][c] + ob[2][h][c] + ob[3][h][c]) / L : 0.f;
+    if (c == 0) lse2[h] = L > 0.f ? hm[h] + __log2f(L) : -INFINITY;
+  }
+  __syncthreads();
+  // into the rotated domain of the packed partials: signs, normalised Hadamard, SO(4)
+  lds_rotate<true>(qb, hs, a.signs + kv * kHeadDim, a.so4 ? a.so4 + kv * 256 : nullptr, a.rot_group);
+  const size_t prow = ((size_t)split * a.batch + b) * a.n_q_heads + h0;
+  if (tid < hs) a.part_lse[prow + tid] = lse2[tid] * kLn2;
+  for (int i = tid; i < hs * kHeadDim; i += 256) a.part_o[(prow + (i >> 7)) * kHeadDim + (i & 127)] = qb[i];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1568,6 +1803,15 @@ hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits
 #undef TQ_VEC
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t stream) {
+  const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(256);
+  if (kv_f16 && q_f16) hipLaunchKernelGGL((dense_kernel<true, true>), grid, block, 0, stream, a);
+  else if (kv_f16) hipLaunchKernelGGL((dense_kernel<true, false>), grid, block, 0, stream, a);
+  else if (q_f16) hipLaunchKernelGGL((dense_kernel<false, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((dense_kernel<false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {

@@ -185,6 +185,32 @@ tq_status tq_append_decode_attention(const tq_rotation* rot, const tq_cache* key
                                      int32_t n_q_heads, float scale, int32_t n_splits, tq_schedule schedule,
                                      float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
 
+/* Attention over an unquantised K/V region, as key-axis section partials that merge with the
+ * packed cache's: the prefill kept in fp16 while only decode-phase tokens are quantised
+ * ("RotaryQuant ...", method overview, deferred prefill), or a window of recent tokens kept
+ * unquantised ("RoPE-Aware Bit Allocation ...", results and limitations: the recent-token
+ * buffer).  Softmax attention is a sum over tokens, so a row split between the two stores
+ * is merged exactly by tq_merge_splits over all sections.
+ *   k, v:     device [batch][n_kv_heads][capacity][128] of kv_dtype (TQ_F16 or TQ_F32);
+ *             row b has seq_lens[b] tokens (device int32 [batch], each <= max_len) or max_len
+ *             when seq_lens is NULL; max_len <= capacity.
+ *   q:        device [batch][n_q_heads][128] of q_dtype; query head h reads KV head
+ *             h / (n_q_heads / n_kv_heads).
+ *   n_splits: sections as for tq_decode_attention: section s covers tokens [s*C,
+ *             min(T, (s+1)*C)), C = ceil(T / n_splits).
+ *   part_o, part_lse: written exactly as tq_decode_attention's partials
+ *             ([n_splits][batch][n_q_heads][128] normalised and rotated forward by R, and
+ *             [n_splits][batch][n_q_heads] natural-log lse; an empty section has lse = -inf
+ *             and a zero partial).  Pointing them at section S of a larger partial buffer
+ *             puts these sections after S packed ones for one tq_merge_splits call.
+ * Scores and sums are fp32.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or
+ * scale, n_q_heads not a multiple of the rotation's KV heads; TQ_ECAPACITY for
+ * max_len > capacity. */
+tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* v, tq_dtype kv_dtype,
+                             int32_t batch, int32_t capacity, const void* q, tq_dtype q_dtype,
+                             int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                             int32_t n_splits, float* part_o, float* part_lse, void* stream);
+
 /* Log-sum-exp merge of key-axis sections followed by the single inverse rotation:
  * lse = ln sum_s e^{lse_s}; out = R^T sum_s e^{lse_s - lse} part_o_s
  * ("RoPE-Aware Bit Allocation ...", packed-cache details; "RotaryQuant ...", key design 3).

@@ -187,6 +187,29 @@ def test_append_decode_validation(lib):
     assert append_decode(rot, k, make_cache(tq.TQ_VALUES, capacity=128)) == TQ_EINVAL
 
 
+def dense(rot, k=FAKE, v=FAKE, kv_dtype=1, batch=1, capacity=64, q=FAKE, n_q_heads=4, max_len=10, n_splits=1,
+          part=FAKE, scale=0.1):
+    return tq.library().tq_dense_attention(ctypes.byref(rot), k, v, kv_dtype, batch, capacity, q, 1, n_q_heads, None,
+                                           max_len, scale, n_splits, part, part, None)
+
+
+def test_dense_validation(lib):
+    rot = make_rot()
+    assert dense(rot, k=None) == TQ_EINVAL
+    assert dense(rot, v=None) == TQ_EINVAL
+    assert dense(rot, q=None) == TQ_EINVAL
+    assert dense(rot, part=None) == TQ_EINVAL
+    assert dense(rot, kv_dtype=7) == TQ_EINVAL
+    assert dense(rot, batch=0) == TQ_EINVAL
+    assert dense(rot, capacity=0) == TQ_EINVAL
+    assert dense(rot, n_q_heads=3) == TQ_EINVAL
+    assert dense(rot, n_splits=0) == TQ_EINVAL
+    assert dense(rot, max_len=-1) == TQ_EINVAL
+    assert dense(rot, max_len=65) == TQ_ECAPACITY
+    assert dense(rot, scale=float("nan")) == TQ_EINVAL
+    assert dense(make_rot(group=64)) == TQ_EUNSUPPORTED
+
+
 def test_merge_validation(lib):
     rot = make_rot()
     m = lib.tq_merge_splits

@@ -176,6 +176,69 @@ def test_append_decode_equals_separate_calls(name, schedule):
                 assert torch.equal(a, b)
 
 
+DENSE_RTOL = 1e-4  # fp32 scores and sums over unquantised inputs
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 40])
+@pytest.mark.parametrize("name", list(CASES))
+def test_dense_sections_match_oracle(name, n_splits):
+    # unquantised K/V (the workload's dtype): section partials in the rotated domain and their
+    # merge, ragged rows including an empty one
+    w, inp = setup(name, seed=11, seq_len=150, batch=3)
+    rot = device_rotation(w, inp)
+    k, v = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens = np.array([150, 0, 67], dtype=np.int32)
+    po, pl = tq.dense_attention(rot, k, v, q, seq_lens=torch.from_numpy(lens).cuda(), max_len=150,
+                                n_splits=n_splits)
+    out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    kd, vd = inp["k"].astype(np.float64), inp["v"].astype(np.float64)
+    ref, ref_lse = oracle_decode(w, inp, kd, vd, lens)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print("dense: max row rel err %.3e (splits %d)" % (err.max(), n_splits), flush=True)
+    assert err.max() <= DENSE_RTOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+    if n_splits > 1:
+        ref_po, ref_pl = oracle_decode(w, inp, kd, vd, lens, n_splits)
+        assert row_rel_err(po.cpu().numpy(), ref_po).max() <= DENSE_RTOL
+        np.testing.assert_allclose(pl.cpu().numpy(), ref_pl, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_packed_prefix_with_unquantised_tail(name):
+    # a row is a packed prefix plus an unquantised tail (recent tokens, or an fp16 prefill):
+    # packed sections and dense sections share one partial buffer and one merge
+    w, inp = setup(name, seed=12, seq_len=180, batch=2)
+    tp = 120
+    cap = round_up(tp, 32)
+    rot = device_rotation(w, inp)
+    wp = w.with_len(tp)
+    inp_p = dict(inp, k=inp["k"][:, :, :tp].copy(), v=inp["v"][:, :, :tp].copy())
+    k, v, oqk, oqv = oracle_caches(wp, inp_p, cap)
+    kt = torch.from_numpy(inp["k"][:, :, tp:].copy()).cuda()
+    vt = torch.from_numpy(inp["v"][:, :, tp:].copy()).cuda()
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens_p = np.array([tp, 75], dtype=np.int32)
+    lens_t = np.array([60, 0], dtype=np.int32)
+    sp, st = 3, 2
+    po = torch.empty((sp + st, w.batch, w.n_q_heads, 128), device="cuda")
+    pl = torch.empty((sp + st, w.batch, w.n_q_heads), device="cuda")
+    tq.decode_attention(rot, k, v, q, seq_lens=torch.from_numpy(lens_p).cuda(), max_len=tp, n_splits=sp,
+                        part_o=po[:sp], part_lse=pl[:sp])
+    tq.dense_attention(rot, kt, vt, q, seq_lens=torch.from_numpy(lens_t).cuda(), max_len=60, n_splits=st,
+                       part_o=po[sp:], part_lse=pl[sp:])
+    out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    ref, ref_lse = attention.decode_two_stores(inp["q"].astype(np.float64), dequantized(wp, inp_p, oqk),
+                                               dequantized(wp, inp_p, oqv), lens_p, inp["k"][:, :, tp:],
+                                               inp["v"][:, :, tp:], lens_t, w.scale)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print("packed + tail: max row rel err %.3e" % err.max(), flush=True)
+    assert err.max() <= OUT_RTOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_single_token_steps_match_oracle(name):
     # a prefill, then one-token steps through the fused call (its single-token kernel) at
