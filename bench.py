@@ -391,7 +391,8 @@ def cpu_baseline(w, inp, budget_s=15.0):
 
 
 def stream_read_probe_gbs():
-    """Achievable read bandwidth: the probe kernel streaming 2 GiB (16-byte loads)."""
+    """Achievable read bandwidth: the probe kernel streaming 2 GiB (contiguous per-workgroup
+    ranges, 16-byte non-temporal loads, the decode's streamed-copy policy)."""
     import ctypes
 
     import torch
@@ -405,7 +406,7 @@ def stream_read_probe_gbs():
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = x.numel() * 4
     best = 0.0
-    for blocks in (2048, 4096, 8192):
+    for blocks in (512, 1024, 4096):
         for _ in range(2):
             assert lib.tq_probe_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), blocks, stream) == 0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -735,24 +735,40 @@ __device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
 // like ordinary loads but leave no register results, so a deep prefetch ring costs no
 // VGPRs.  Written as inline assembly: the compiler would otherwise make every later LDS
 // read wait for all of them.  The caller waits with vm_wait before reading the data.
-template <int BYTES>
+// STREAM marks data read once (the cache stream): the non-temporal policy, which on this
+// chip lifts a pure read stream from about 6.2 to 7.0 TB/s.
+template <int BYTES, bool STREAM>
 __device__ __forceinline__ void lds_dma(uint32_t lds_base, const void* sbase, uint32_t voff) {
   if (BYTES == 16) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+    if (STREAM)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
   } else if (BYTES == 12) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+    if (STREAM)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
   } else {
     static_assert(BYTES == 12 || BYTES == 16, "whole-lane copies of 12 or 16 bytes");
   }
 }
-template <int BYTES>
+template <int BYTES, bool STREAM>
 __device__ __forceinline__ void lds_dma_addr(uint32_t lds_base, const void* addr) {
   if (BYTES == 16) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+    if (STREAM)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
   } else if (BYTES == 4) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+    if (STREAM)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off nt" ::"s"(lds_base), "v"(addr) : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
   } else {
     static_assert(BYTES == 4 || BYTES == 16, "whole-lane copies of 4 or 16 bytes");
   }
@@ -882,12 +898,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     const size_t row = (size_t)u.b * a.n_q_heads + u.h0 + 2 * wv;
     if (QF16) {
       if (lane < 32 && 2 * wv + (lane >> 4) < u.hs)
-        lds_dma_addr<16>(qraw, (const _Float16*)a.q + row * kHeadDim + 8 * lane);
+        lds_dma_addr<16, false>(qraw, (const _Float16*)a.q + row * kHeadDim + 8 * lane);
     } else {
-      if (2 * wv + (lane >> 5) < u.hs) lds_dma_addr<16>(qraw, (const float*)a.q + row * kHeadDim + 4 * lane);
+      if (2 * wv + (lane >> 5) < u.hs) lds_dma_addr<16, false>(qraw, (const float*)a.q + row * kHeadDim + 4 * lane);
     }
-    if (wv == 0 && lane < 32) lds_dma_addr<16>(lds_addr(qstage), a.signs + u.kv * kHeadDim + 4 * lane);
-    if (wv == 1 && a.so4 != nullptr) lds_dma_addr<16>(lds_addr(qstage) + kHeadDim * 4, a.so4 + u.kv * 256 + 4 * lane);
+    if (wv == 0 && lane < 32) lds_dma_addr<16, false>(lds_addr(qstage), a.signs + u.kv * kHeadDim + 4 * lane);
+    if (wv == 1 && a.so4 != nullptr) lds_dma_addr<16, false>(lds_addr(qstage) + kHeadDim * 4, a.so4 + u.kv * 256 + 4 * lane);
   }
   // ---- then the first D blocks of this wave into its ring
   const int nblk = blk0 + wv < blk1 ? (blk1 - (blk0 + wv) + NW - 1) / NW : 0;  // this wave's blocks
@@ -900,11 +916,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     const uint32_t sl = __builtin_amdgcn_readfirstlane(ring + (j % D) * SLOT);
     const uint8_t* kb = kbase + (size_t)blk * kTile * KREC;
     const uint8_t* vb = vbase + (size_t)blk * VTILE;
-    lds_dma<KSZ>(sl, kb, koff);
-    lds_dma<KSZ>(sl + S_K1, kb, koff + 16 * KREC);
-    lds_dma<VSZ>(sl + S_V0, vb, voff);
-    lds_dma<VSZ>(sl + S_V1, vb, voff + VSZ);
-    lds_dma_addr<NSZ>(sl + S_N, nlane + (size_t)blk * (NG * kTile * 4));
+    lds_dma<KSZ, true>(sl, kb, koff);
+    lds_dma<KSZ, true>(sl + S_K1, kb, koff + 16 * KREC);
+    lds_dma<VSZ, true>(sl + S_V0, vb, voff);
+    lds_dma<VSZ, true>(sl + S_V1, vb, voff + VSZ);
+    lds_dma_addr<NSZ, true>(sl + S_N, nlane + (size_t)blk * (NG * kTile * 4));
   };
   auto read_block = [&](int j) {
     const uint8_t* sl = pool + RING_AT + wv * (D * SLOT) + (j % D) * SLOT;
