@@ -22,11 +22,15 @@ What it computes, and where the pages define it (page title, then section):
 * ``attention`` -- plain softmax attention over explicitly dequantised K/V, key-axis
   splits with a log-sum-exp merge ("RoPE-Aware Bit Allocation for KV-Cache
   Quantization", packed-cache implementation details), and the rotated-domain
-  rewrite used as a self-check ("RotaryQuant ...", key design 3).
+  rewrite used as a self-check ("RotaryQuant ...", key design 3); attention over a row's
+  quantised and unquantised token stores.
+* ``zipcodec``  -- the lossless BF16 exponent codec of the KV cache: chunk rule, 4-bit
+  codes, page metadata and the decode by integer adds ("ZipFusion ...", compression format
+  and register decode sections).
 
 Every function works in float64 unless it is explicitly producing a stored fp32 value.
 Parity pins for each function live in ``tests/test_oracle_*.py``; nothing here is
 "parity unpinned".
 """
 
-from . import codebook, rotation, quant, layout, attention  # noqa: F401
+from . import codebook, rotation, quant, layout, attention, zipcodec  # noqa: F401
