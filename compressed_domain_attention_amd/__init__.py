@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "NativeLibraryMissing", "TQError", "Codebook", "make_codebook", "Rotation", "PackedCache",
     "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
+    "zip_store", "zip_compress", "zip_attention",
     "TQ_KEYS", "TQ_VALUES",
 ]
 
@@ -26,6 +27,9 @@ TQ_KEYS = 0
 TQ_VALUES = 1
 _SCHEDULES = {"auto": 0, "vec": 1, "mfma": 2}
 _DTYPES = {torch.float32: 0, torch.float16: 1}
+_ZIP_Q_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+ZIP_PAGE = 16      # tokens per compressed page
+ZIP_SLOT = 4096    # bytes of one page's slot in the store
 
 
 class NativeLibraryMissing(RuntimeError):
@@ -65,7 +69,8 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
-           "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits")
+           "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
+           "tq_zip_compress", "tq_zip_attention")
 
 
 def library():
@@ -97,6 +102,10 @@ def library():
     lib.tq_dense_attention.restype = I
     lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
     lib.tq_merge_splits.restype = I
+    lib.tq_zip_compress.argtypes = [P, I, I, I, I, I, I, P, P, I, P]
+    lib.tq_zip_compress.restype = I
+    lib.tq_zip_attention.argtypes = [P, P, P, P, I, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
+    lib.tq_zip_attention.restype = I
     _lib = lib
     return lib
 
@@ -289,13 +298,91 @@ def dense_attention(rot: Rotation, k: torch.Tensor, v: torch.Tensor, q: torch.Te
     return part_o, part_lse
 
 
-def merge_splits(rot: Rotation, part_o: torch.Tensor, part_lse: torch.Tensor, out=None, lse=None):
-    """Log-sum-exp merge of split partials and the inverse rotation -> (out, lse)."""
+def merge_splits(rot, part_o: torch.Tensor, part_lse: torch.Tensor, out=None, lse=None):
+    """Log-sum-exp merge of split partials and the inverse rotation -> (out, lse).  rot=None
+    merges partials of the original domain (zip_attention's) with no rotation."""
     n_splits, bsz, hq = part_lse.shape
     if out is None:
         out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=part_o.device)
     if lse is None:
         lse = torch.empty((bsz, hq), dtype=torch.float32, device=part_o.device)
-    _check(library().tq_merge_splits(ctypes.byref(rot.c), n_splits, bsz, hq, _ptr(part_o), _ptr(part_lse),
+    _check(library().tq_merge_splits(None if rot is None else ctypes.byref(rot.c), n_splits, bsz, hq,
+                                     _ptr(part_o), _ptr(part_lse),
                                      _ptr(out), _ptr(lse), _stream()), "tq_merge_splits")
     return out, lse
+
+
+def zip_store(batch: int, n_kv_heads: int, pages: int, device="cuda"):
+    """Empty compressed store for one role (keys or values) -> (store uint8 [batch, n_kv_heads,
+    pages, 4096], meta uint8 [batch, n_kv_heads, pages, 8])."""
+    store = torch.zeros((batch, n_kv_heads, pages, ZIP_SLOT), dtype=torch.uint8, device=device)
+    meta = torch.zeros((batch, n_kv_heads, pages, 8), dtype=torch.uint8, device=device)
+    return store, meta
+
+
+def _check_store(store, meta, batch, n_kv_heads):
+    if store.dtype != torch.uint8 or store.dim() != 4 or store.shape[3] != ZIP_SLOT or not store.is_contiguous():
+        raise ValueError("store must be contiguous uint8 [batch, n_kv_heads, pages, 4096]")
+    if meta.dtype != torch.uint8 or tuple(meta.shape) != tuple(store.shape[:3]) + (8,) or not meta.is_contiguous():
+        raise ValueError("meta must be contiguous uint8 [batch, n_kv_heads, pages, 8] matching the store")
+    if store.shape[0] != batch or store.shape[1] != n_kv_heads:
+        raise ValueError("store must be [batch, n_kv_heads, ...] of the BF16 buffer")
+
+
+def zip_compress(x: torch.Tensor, store: torch.Tensor, meta: torch.Tensor, n_pages=None, src_page0=0,
+                 dst_page0=0):
+    """Compress whole 16-token pages of x (bfloat16 [batch, n_kv_heads, rows, 128]): page i is
+    rows 16 (src_page0 + i) .. +15 and becomes store page dst_page0 + i.  n_pages defaults to
+    every whole page of x from src_page0."""
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or x.shape[3] != HEAD_DIM or not x.is_contiguous():
+        raise ValueError("x must be contiguous bfloat16 [batch, n_kv_heads, rows, 128]")
+    bsz, hkv, rows = x.shape[0], x.shape[1], x.shape[2]
+    _check_store(store, meta, bsz, hkv)
+    if n_pages is None:
+        n_pages = rows // ZIP_PAGE - src_page0
+    _check(library().tq_zip_compress(_ptr(x), bsz, hkv, rows, src_page0, dst_page0, n_pages, _ptr(store),
+                                     _ptr(meta), store.shape[2], _stream()), "tq_zip_compress")
+    return store, meta
+
+
+def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=None, max_len=None, scale=None,
+                  n_splits=1, out=None, lse=None, part_o=None, part_lse=None):
+    """Decode attention read from compressed BF16 pages plus BF16 tail buffers (token t of a
+    row past its last whole page at tail row t mod tail_rows).  n_splits == 1 -> (out, lse);
+    otherwise (part_o, part_lse) in the original domain, for merge_splits(None, ...)."""
+    if q.dtype not in _ZIP_Q_DTYPES or not q.is_contiguous() or q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be contiguous [batch, n_q_heads, 128] float32/float16/bfloat16")
+    bsz, hq = q.shape[0], q.shape[1]
+    for t in (k_tail, v_tail):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or t.shape[3] != HEAD_DIM or not t.is_contiguous():
+            raise ValueError("tails must be contiguous bfloat16 [batch, n_kv_heads, rows, 128]")
+    if k_tail.shape != v_tail.shape or k_tail.shape[0] != bsz:
+        raise ValueError("k_tail and v_tail must have the same shape [batch, n_kv_heads, rows, 128]")
+    hkv = k_tail.shape[1]
+    _check_store(k_store, k_meta, bsz, hkv)
+    _check_store(v_store, v_meta, bsz, hkv)
+    if k_store.shape != v_store.shape:
+        raise ValueError("key and value stores must have the same shape")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
+        raise ValueError("seq_lens must be int32 [batch]")
+    pages = k_store.shape[2]
+    if max_len is None:
+        max_len = int(seq_lens.max().item()) if seq_lens is not None else ZIP_PAGE * pages
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_zip_attention(
+        _ptr(k_store), _ptr(k_meta), _ptr(v_store), _ptr(v_meta), pages, _ptr(k_tail), _ptr(v_tail),
+        k_tail.shape[2], bsz, hkv, _ptr(q), _ZIP_Q_DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits,
+        _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_zip_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)

@@ -246,21 +246,96 @@ extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, c
 extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,
                                      const float* part_o, const float* part_lse, float* out, float* lse_out,
                                      void* stream) {
-  tq_status st = check_rotation(rot);
-  if (st != TQ_OK) return st;
-  if (n_splits < 1 || batch <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
+  if (rot != nullptr) {
+    tq_status st = check_rotation(rot);
+    if (st != TQ_OK) return st;
+  }
+  if (n_splits < 1 || batch <= 0 || n_q_heads <= 0) return TQ_EINVAL;
+  if (rot != nullptr && n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
   if (part_o == nullptr || part_lse == nullptr || out == nullptr) return TQ_EINVAL;
   tq::MergeArgs a;
   a.part_o = part_o;
   a.part_lse = part_lse;
   a.out = out;
   a.lse_out = lse_out;
-  a.signs = rot->signs;
-  a.so4 = rot->so4;
+  // no rotation: partials of the original domain, merged without the inverse rotation
+  a.signs = rot ? rot->signs : nullptr;
+  a.so4 = rot ? rot->so4 : nullptr;
   a.n_splits = n_splits;
   a.batch = batch;
   a.n_q_heads = n_q_heads;
-  a.group_size = n_q_heads / rot->n_kv_heads;
-  a.rot_group = rot->group;
+  a.group_size = rot ? n_q_heads / rot->n_kv_heads : 1;
+  a.rot_group = rot ? rot->group : 128;
   return from_hip(tq::launch_merge(a, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_heads, int32_t x_rows,
+                                     int32_t src_page0, int32_t dst_page0, int32_t n_pages, uint8_t* store,
+                                     uint8_t* meta, int32_t store_pages, void* stream) {
+  if (x == nullptr || store == nullptr || meta == nullptr) return TQ_EINVAL;
+  if (batch <= 0 || n_kv_heads <= 0 || x_rows <= 0 || store_pages <= 0) return TQ_EINVAL;
+  if (src_page0 < 0 || dst_page0 < 0 || n_pages < 0) return TQ_EINVAL;
+  if ((int64_t)tq::kZipPage * ((int64_t)src_page0 + n_pages) > x_rows) return TQ_ECAPACITY;
+  if ((int64_t)dst_page0 + n_pages > store_pages) return TQ_ECAPACITY;
+  if ((int64_t)store_pages * tq::kZipSlot > 0xFFFFFFFFll) return TQ_ECAPACITY;  // 32-bit start offsets
+  if (batch > 65535 || n_kv_heads > 65535) return TQ_EINVAL;                     // grid z and y
+  if (n_pages == 0) return TQ_OK;
+  tq::ZipCompressArgs a;
+  a.x = (const uint16_t*)x;
+  a.store = store;
+  a.meta = meta;
+  a.n_kv_heads = n_kv_heads;
+  a.x_rows = x_rows;
+  a.store_pages = store_pages;
+  a.src_page0 = src_page0;
+  a.dst_page0 = dst_page0;
+  return from_hip(tq::launch_zip_compress(a, batch, n_pages, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const uint8_t* v_store,
+                                      const uint8_t* v_meta, int32_t store_pages, const void* k_tail,
+                                      const void* v_tail, int32_t tail_rows, int32_t batch, int32_t n_kv_heads,
+                                      const void* q, tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens,
+                                      int32_t max_len, float scale, int32_t n_splits, float* out, float* lse_out,
+                                      float* part_o, float* part_lse, void* stream) {
+  if (k_store == nullptr || k_meta == nullptr || v_store == nullptr || v_meta == nullptr) return TQ_EINVAL;
+  if (k_tail == nullptr || v_tail == nullptr || q == nullptr) return TQ_EINVAL;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EINVAL;
+  if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0) return TQ_EINVAL;
+  if (store_pages < 0 || tail_rows <= 0 || tail_rows % tq::kZipPage != 0) return TQ_EINVAL;
+  if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
+  const int group = n_q_heads / n_kv_heads;
+  if (group > 8 && group % 8 != 0) return TQ_EINVAL;
+  if ((int64_t)store_pages * tq::kZipSlot > 0xFFFFFFFFll) return TQ_ECAPACITY;
+  if ((int64_t)max_len > (int64_t)tq::kZipPage * store_pages + tq::kZipPage - 1) return TQ_ECAPACITY;
+  if (store_pages == 0 && max_len > tail_rows) return TQ_ECAPACITY;
+  const int hps = group <= 4 ? group : 8;
+  if ((int64_t)batch * n_kv_heads * n_splits * ((group + hps - 1) / hps) > 0x7FFFFFFFll) return TQ_EINVAL;
+  tq::ZipAttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_store = k_store;
+  a.k_meta = k_meta;
+  a.v_store = v_store;
+  a.v_meta = v_meta;
+  a.k_tail = (const uint16_t*)k_tail;
+  a.v_tail = (const uint16_t*)v_tail;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.max_len = max_len;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group_size = group;
+  a.heads_per_slice = hps;
+  a.n_slices = (group + hps - 1) / hps;
+  a.n_splits = n_splits;
+  a.store_pages = store_pages;
+  a.tail_rows = tail_rows;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(tq::launch_zip_attention(a, (int)q_dtype, (hipStream_t)stream));
 }

@@ -84,6 +84,48 @@ struct DenseArgs {
   float scale_log2;
 };
 
+// Lossless BF16 exponent codec of a KV cache (16-token pages, 4096-byte page slots, 8
+// bytes of metadata per page) and attention read straight from it.
+constexpr int kZipPage = 16;
+constexpr int kZipSlot = 4096;
+
+struct ZipCompressArgs {
+  const uint16_t* x;   // BF16 [batch][n_kv_heads][x_rows][128]
+  uint8_t* store;      // [batch][n_kv_heads][store_pages][4096]
+  uint8_t* meta;       // [batch][n_kv_heads][store_pages][8]
+  int32_t n_kv_heads;
+  int32_t x_rows;
+  int32_t store_pages;
+  int32_t src_page0;   // page i of the call reads x rows 16 (src_page0 + i) ..
+  int32_t dst_page0;   // .. and becomes store page dst_page0 + i
+};
+
+struct ZipAttnArgs {
+  const uint8_t* k_store;  // as ZipCompressArgs
+  const uint8_t* k_meta;
+  const uint8_t* v_store;
+  const uint8_t* v_meta;
+  const uint16_t* k_tail;  // BF16 [batch][n_kv_heads][tail_rows][128]: tokens past the last full page
+  const uint16_t* v_tail;
+  const void* q;           // [batch][n_q_heads][128]
+  const int32_t* seq_lens; // [batch] or null
+  float* out;              // n_splits == 1: [batch][n_q_heads][128]
+  float* lse_out;          // optional
+  float* part_o;           // n_splits > 1: [n_splits][batch][n_q_heads][128]
+  float* part_lse;         // [n_splits][batch][n_q_heads]
+  int32_t max_len;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t group_size;
+  int32_t heads_per_slice;
+  int32_t n_slices;
+  int32_t n_splits;
+  int32_t store_pages;
+  int32_t tail_rows;
+  float scale_log2;
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
@@ -109,6 +151,9 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream);
 hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t stream);
+hipError_t launch_zip_compress(const ZipCompressArgs& a, int batch, int n_pages, hipStream_t stream);
+// q_type: 0 fp32, 1 fp16, 2 bf16
+hipError_t launch_zip_attention(const ZipAttnArgs& a, int q_type, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 // Heads one workgroup of the matrix-core schedule can serve: the 16 MFMA columns hold

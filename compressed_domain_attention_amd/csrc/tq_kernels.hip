@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "tq_internal.h"
+#include "tq_lanes.h"
 
 namespace tq {
 namespace {
@@ -91,22 +92,6 @@ __device__ void lds_rotate(float* buf, int nh, const float* signs, const float* 
   }
 }
 
-// The value of lane `lane ^ m` (m a power of two below 64).  Inside a 16-lane row the
-// exchange is a DPP lane move (quad permutes for 1 and 2, a shift left or right by 4, a
-// rotation by 8), with no round trip through the LDS crossbar; 16 and 32 cross rows with a
-// bpermute.  m is a constant after unrolling, so the branches fold.
-__device__ __forceinline__ float lane_xor(float x, int m, int lane) {
-  const int v = __builtin_bit_cast(int, x);
-  if (m == 1) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-  if (m == 2) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-  if (m == 4) {
-    const int from_above = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4, lane i + 4
-    const int from_below = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4, lane i - 4
-    return __builtin_bit_cast(float, (lane & 4) ? from_below : from_above);
-  }
-  if (m == 8) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
-  return __shfl_xor(x, m);
-}
 
 // Forward rotation of up to eight query heads in registers: wave w, lane l holds head
 // 2w + (l >> 5), coordinates 4(l & 31) .. +3 (one SO(4) block).  The first two Hadamard
@@ -1658,7 +1643,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   rl.live = wv == 0 && lane < 32;
   rl.sg = make_float4(1.f, 1.f, 1.f, 1.f);
   rl.l = rl.r = Quat{1.f, 0.f, 0.f, 0.f};
-  if (rl.live) {
+  if (rl.live && a.signs) {
     rl.sg = *(const float4*)(a.signs + kv * kHeadDim + 4 * lane);
     if (a.so4) {
       rl.l = qload(a.so4 + kv * 256 + 8 * lane);
@@ -1710,7 +1695,8 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   __syncthreads();
   if (wv == 0) {  // the whole first wave takes part in the lane exchanges
     const float4 x = *(const float4*)(obuf + 4 * (lane & 31));
-    const float4 y = unrotate4<GROUP>(x, rl, a.so4 != nullptr, lane);
+    // partials formed in the original domain (no rotation given) are already the output
+    const float4 y = a.signs ? unrotate4<GROUP>(x, rl, a.so4 != nullptr, lane) : x;
     if (rl.live) *(float4*)(a.out + (size_t)row * kHeadDim + 4 * lane) = y;
   }
   if (a.lse_out && c == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;

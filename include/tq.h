@@ -63,7 +63,8 @@ typedef enum {
   TQ_EHIP = 4           /* a HIP launch or runtime call failed */
 } tq_status;
 
-typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
+/* TQ_BF16 is accepted only where a declaration says so (the compressed BF16 cache). */
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
 typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
 
 /* Decode schedules.  MFMA: scores and value sum as matrix-core products of fp16
@@ -215,10 +216,74 @@ tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* 
  * lse = ln sum_s e^{lse_s}; out = R^T sum_s e^{lse_s - lse} part_o_s
  * ("RoPE-Aware Bit Allocation ...", packed-cache details; "RotaryQuant ...", key design 3).
  * part_o/part_lse as written by tq_decode_attention; out [batch][n_q_heads][128];
- * lse_out [batch][n_q_heads] or NULL.  n_q_heads must be a multiple of rot->n_kv_heads. */
+ * lse_out [batch][n_q_heads] or NULL.  n_q_heads must be a multiple of rot->n_kv_heads.
+ * rot == NULL merges partials of the original domain (tq_zip_attention's) with no
+ * rotation: out = sum_s e^{lse_s - lse} part_o_s. */
 tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batch, int32_t n_q_heads,
                           const float* part_o, const float* part_lse, float* out, float* lse_out,
                           void* stream);
+
+/* ---- Lossless BF16 exponent codec of a KV cache ("ZipFusion: Fusing Lossless KV
+ * Decompression with Attention ...", compression format, page metadata, register decode).
+ *
+ * A BF16 cache of [batch][n_kv_heads][tokens][128] (keys and values separately) is cut into
+ * pages of 16 tokens; a page of one (sequence, KV head) is 4 chunks of 512 values, chunk c
+ * holding the page's tokens 4c .. 4c+3 (token-major).  A chunk whose exponents all lie in
+ * [b, b+15], b = its smallest exponent rounded down to even, is coded: its 512 low bytes
+ * (7 mantissa bits and the exponent's lowest bit) as they are, then 256 code bytes, byte
+ * 4g+j holding value 8g+j (sign in bit 7, d = (exponent-b)/2 rounded down in bits 0-2) and
+ * value 8g+j+4 (sign bit 6, d bits 3-5): 768 bytes, 75% of the original.  Any other chunk
+ * is kept as its 1024 bytes.
+ *   store: uint8 [batch][n_kv_heads][store_pages][4096]: page p's chunks back to back from
+ *          the start of its 4096-byte slot; the slot's other bytes are zero.
+ *   meta:  uint8 [batch][n_kv_heads][store_pages][8]: little-endian u32 byte offset of the
+ *          page's first chunk within its (sequence, KV head) store (p * 4096 as written
+ *          here), then one byte per chunk: 0xFF when kept, else b/2.
+ * Decoding is exact: the high byte of a coded value is sign*128 + b/2 + d. */
+
+/* Compresses n_pages whole pages of a BF16 token buffer into a store.
+ *   x:     device BF16 [batch][n_kv_heads][x_rows][128]; page i of the call is rows
+ *          16*(src_page0+i) .. +15 and becomes store page dst_page0+i, for every
+ *          (sequence, KV head).  A prefilled cache is compressed with x = the cache,
+ *          src_page0 = dst_page0 = 0; a tail buffer of 16 rows that has just filled, with
+ *          x_rows = 16, src_page0 = 0 and dst_page0 = its page number.
+ *   store, meta: device, as above; only the n_pages pages are written.
+ * Errors: TQ_EINVAL for null pointers, non-positive counts or negative page numbers;
+ * TQ_ECAPACITY when the pages pass x_rows or store_pages.  n_pages == 0 is a no-op. */
+tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_heads, int32_t x_rows, int32_t src_page0,
+                          int32_t dst_page0, int32_t n_pages, uint8_t* store, uint8_t* meta, int32_t store_pages,
+                          void* stream);
+
+/* Decode attention read straight from the compressed pages: out = softmax(scale q K^T) V
+ * over a row's T tokens, every stored value decoded in registers ("ZipFusion ...", fused
+ * decompression and attention).  Pages 0 .. floor(T/16)-1 are read from the stores; the
+ * T mod 16 tokens after them from the BF16 tail buffers, token t at row t mod tail_rows
+ * (tail_rows = 16 for a buffer of the open page; a whole BF16 cache also serves, since
+ * t mod tail_rows = t there).
+ *   k_store, k_meta, v_store, v_meta: device, as written by tq_zip_compress; offsets read
+ *          from the metadata are clamped so that a page slot stays inside the stream.
+ *   k_tail, v_tail: device BF16 [batch][n_kv_heads][tail_rows][128]; tail_rows a positive
+ *          multiple of 16.
+ *   q:     device [batch][n_q_heads][128] of q_dtype (TQ_F32, TQ_F16 or TQ_BF16); query
+ *          head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads / n_kv_heads <= 8,
+ *          or a multiple of 8.
+ *   seq_lens: device int32 [batch] (each clamped to [0, max_len]) or NULL (all max_len);
+ *          max_len <= 16 * store_pages + 15, and <= tail_rows when no page is stored.
+ *   n_splits: key-axis sections of whole pages: section s covers tokens [s*C, min(T,
+ *          (s+1)*C)), C = ceil(T / n_splits) rounded up to a multiple of 16.
+ *   out, lse_out: n_splits == 1: device fp32 [batch][n_q_heads][128] and natural-log lse
+ *          [batch][n_q_heads] (lse_out may be NULL); an empty row gives zeros and -inf.
+ *   part_o, part_lse: n_splits > 1: fp32 [n_splits][batch][n_q_heads][128] normalised
+ *          section outputs in the original domain and [n_splits][batch][n_q_heads] lse;
+ *          tq_merge_splits with rot == NULL combines them.
+ * Scores and sums are fp32.  Errors: TQ_EINVAL for null pointers, bad dtype, counts, scale
+ * or head grouping; TQ_ECAPACITY when max_len passes the stored pages and the tail. */
+tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const uint8_t* v_store,
+                           const uint8_t* v_meta, int32_t store_pages, const void* k_tail, const void* v_tail,
+                           int32_t tail_rows, int32_t batch, int32_t n_kv_heads, const void* q, tq_dtype q_dtype,
+                           int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                           int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
+                           void* stream);
 
 #ifdef __cplusplus
 }

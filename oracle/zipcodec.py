@@ -23,16 +23,27 @@ compressed"), the page metadata and the register decode.
   for where the first chunk starts, 1 byte per chunk: "uncompressed" or b/2), and the 4
   value chunks another 8.
 
+* Attention reads a row straight from its compressed pages: only whole pages are
+  compressed; the open page (its last T mod 16 tokens) is kept uncompressed so that new
+  tokens append to it ("ZipFusion ...", system overview: pages are compressed when full).
+
 Readings (the pages leave these open): chunk c of a page is tokens 4c .. 4c+3, token-major
 (coordinate order within a token); the 8 values that share 4 code bytes are 8 consecutive
 values of the chunk (group g = values 8g .. 8g+7, code byte 4g + j holds values 8g + j and
 8g + j + 4); a compressed chunk is its 512 low bytes, then its 256 code bytes; the
 "uncompressed" mark is 0xFF (b/2 is at most 127); a page's chunks are stored back to back
 from the start of a fixed 4096-byte page slot, and the 4-byte start field is the byte
-offset of that slot within the (sequence, KV head) stream, little-endian.
+offset of that slot within the (sequence, KV head) stream, little-endian; the open page's
+tokens sit in a BF16 tail buffer of tail_rows rows (a multiple of 16), token t at row
+t mod tail_rows; key-axis sections of a row are whole pages: C = ceil(T / S) rounded up to
+a multiple of 16.
 """
 
+import math
+
 import numpy as np
+
+from . import attention
 
 PAGE = 16          # tokens per page
 HEAD_DIM = 128
@@ -131,3 +142,39 @@ def decompress_stream(store, meta, n_pages):
 def page_bytes(meta_row):
     """Stored bytes of one page (its 4 chunks) from its metadata row."""
     return sum(CHUNK * 2 if int(m) == RAW else COMPRESSED_BYTES for m in meta_row[4:])
+
+
+def row_tokens(store, meta, tail, t):
+    """The BF16 bits [t][128] of one (sequence, KV head) row of t tokens: pages 0 ..
+    t // 16 - 1 decompressed from its store and metadata, the rest from its tail buffer
+    (token i at tail row i mod len(tail))."""
+    full = t // PAGE
+    out = np.zeros((t, HEAD_DIM), dtype=np.uint16)
+    if full:
+        out[:full * PAGE] = decompress_stream(store, meta, full)
+    for i in range(full * PAGE, t):
+        out[i] = tail[i % len(tail)]
+    return out
+
+
+def decode_from_pages(q, k_store, k_meta, v_store, v_meta, k_tail, v_tail, seq_lens, scale):
+    """Decode attention of q[B, Hq, 128] over every row's tokens read back from its
+    compressed pages and tail: (out[B, Hq, 128], lse[B, Hq]) in fp64, by plain softmax
+    attention on the exact BF16 values."""
+    bsz, hkv = k_store.shape[:2]
+    tmax = max([int(t) for t in seq_lens] + [0])
+    k = np.zeros((bsz, hkv, tmax, HEAD_DIM))
+    v = np.zeros((bsz, hkv, tmax, HEAD_DIM))
+    for b in range(bsz):
+        t = int(seq_lens[b])
+        for h in range(hkv):
+            k[b, h, :t] = bf16_to_float(row_tokens(k_store[b, h], k_meta[b, h], k_tail[b, h], t))
+            v[b, h, :t] = bf16_to_float(row_tokens(v_store[b, h], v_meta[b, h], v_tail[b, h], t))
+    return attention.decode(bf16_to_float(q), k, v, seq_lens, scale)
+
+
+def section_bounds(t, n_splits):
+    """Key-axis sections of a row of t tokens in whole pages: C = ceil(t / S) rounded up to
+    a multiple of 16; section s is [min(t, s C), min(t, (s + 1) C))."""
+    c = math.ceil(math.ceil(t / n_splits) / PAGE) * PAGE if t > 0 else 0
+    return [(min(t, s * c), min(t, (s + 1) * c)) for s in range(n_splits)]

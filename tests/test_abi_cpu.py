@@ -219,6 +219,62 @@ def test_merge_validation(lib):
     assert m(ctypes.byref(rot), 2, 1, 4, FAKE, FAKE, None, None, None) == TQ_EINVAL
 
 
+def zip_compress(lib, x=FAKE, batch=1, heads=1, rows=64, src=0, dst=0, n=4, store=FAKE, meta=FAKE, pages=4):
+    return lib.tq_zip_compress(x, batch, heads, rows, src, dst, n, store, meta, pages, None)
+
+
+def test_zip_compress_validation(lib):
+    assert zip_compress(lib, x=None) == TQ_EINVAL
+    assert zip_compress(lib, store=None) == TQ_EINVAL
+    assert zip_compress(lib, meta=None) == TQ_EINVAL
+    assert zip_compress(lib, batch=0) == TQ_EINVAL
+    assert zip_compress(lib, heads=0) == TQ_EINVAL
+    assert zip_compress(lib, rows=0) == TQ_EINVAL
+    assert zip_compress(lib, pages=0) == TQ_EINVAL
+    assert zip_compress(lib, src=-1) == TQ_EINVAL
+    assert zip_compress(lib, dst=-1) == TQ_EINVAL
+    assert zip_compress(lib, n=-1) == TQ_EINVAL
+    assert zip_compress(lib, rows=63) == TQ_ECAPACITY          # page 3 needs rows 48..63
+    assert zip_compress(lib, src=1) == TQ_ECAPACITY
+    assert zip_compress(lib, dst=1) == TQ_ECAPACITY            # pages 1..4 of a 4-page store
+    assert zip_compress(lib, pages=1 << 20) == TQ_ECAPACITY    # 32-bit start offsets
+    assert zip_compress(lib, n=0) == TQ_OK                     # nothing to do, nothing launched
+
+
+def zip_attn(lib, ks=FAKE, km=FAKE, vs=FAKE, vm=FAKE, pages=4, kt=FAKE, vt=FAKE, tail_rows=16, batch=1, heads=2,
+             q=FAKE, q_dtype=2, hq=8, max_len=64, scale=0.1, n_splits=1, out=FAKE, part=FAKE):
+    return lib.tq_zip_attention(ks, km, vs, vm, pages, kt, vt, tail_rows, batch, heads, q, q_dtype, hq, None,
+                                max_len, scale, n_splits, out, None, part, part, None)
+
+
+def test_zip_attention_validation(lib):
+    for kw in ("ks", "km", "vs", "vm", "kt", "vt", "q"):
+        assert zip_attn(lib, **{kw: None}) == TQ_EINVAL, kw
+    assert zip_attn(lib, out=None) == TQ_EINVAL                 # n_splits == 1 writes out
+    assert zip_attn(lib, n_splits=2, part=None) == TQ_EINVAL   # n_splits > 1 writes partials
+    assert zip_attn(lib, q_dtype=3) == TQ_EINVAL
+    assert zip_attn(lib, batch=0) == TQ_EINVAL
+    assert zip_attn(lib, heads=0) == TQ_EINVAL
+    assert zip_attn(lib, hq=7) == TQ_EINVAL                    # not a multiple of the KV heads
+    assert zip_attn(lib, heads=1, hq=12) == TQ_EINVAL          # groups above 8 come in multiples of 8
+    assert zip_attn(lib, tail_rows=0) == TQ_EINVAL
+    assert zip_attn(lib, tail_rows=24) == TQ_EINVAL
+    assert zip_attn(lib, pages=-1) == TQ_EINVAL
+    assert zip_attn(lib, n_splits=0) == TQ_EINVAL
+    assert zip_attn(lib, max_len=-1) == TQ_EINVAL
+    assert zip_attn(lib, scale=float("inf")) == TQ_EINVAL
+    assert zip_attn(lib, max_len=80) == TQ_ECAPACITY           # 4 pages + at most 15 open tokens
+    assert zip_attn(lib, pages=0, max_len=17) == TQ_ECAPACITY  # no page: the tail holds every token
+    assert zip_attn(lib, pages=1 << 20) == TQ_ECAPACITY
+
+
+def test_merge_without_rotation_validation(lib):
+    m = lib.tq_merge_splits
+    assert m(None, 0, 1, 4, FAKE, FAKE, FAKE, None, None) == TQ_EINVAL
+    assert m(None, 2, 0, 4, FAKE, FAKE, FAKE, None, None) == TQ_EINVAL
+    assert m(None, 2, 1, 4, None, FAKE, FAKE, None, None) == TQ_EINVAL
+
+
 def test_product_path_has_no_cpu_fallback():
     # the binding must not reach the oracle or any CPU computation
     src = open(os.path.join(ROOT, "compressed_domain_attention_amd", "__init__.py")).read()

@@ -1,6 +1,8 @@
 """Pins of the lossless BF16 exponent codec oracle against the page's worked examples and
 the definitions ("ZipFusion ...", compression format and register decode sections)."""
 
+import math
+
 import numpy as np
 import pytest
 
@@ -105,3 +107,67 @@ def test_stream_pages_round_trip_and_metadata():
         assert zc.page_bytes(meta[p]) <= zc.SLOT
     assert zc.page_bytes(meta[1]) == 3 * zc.COMPRESSED_BYTES + 2 * zc.CHUNK
     assert all(zc.page_bytes(meta[p]) == 4 * zc.COMPRESSED_BYTES for p in (0, 2, 3))
+
+
+def bf16_stream(rng, t):
+    # magnitudes over a few binades with random signs: most chunks compress
+    f = (rng.uniform(0.25, 4.0, (t, 128)) * rng.choice([-1.0, 1.0], (t, 128))).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("t", [0, 5, 16, 70])
+def test_row_tokens_reads_pages_then_open_page(t):
+    rng = np.random.default_rng(4)
+    x = bf16_stream(rng, max(t, 1))[:t]
+    full = t // zc.PAGE
+    store, meta = zc.compress_stream(x, max(full, 1)) if full else (np.zeros((1, zc.SLOT), np.uint8),
+                                                                     np.zeros((1, 8), np.uint8))
+    # an open-page buffer of 16 rows: token i at row i mod 16; other rows are stale
+    tail = bf16_stream(rng, 16)
+    for i in range(full * zc.PAGE, t):
+        tail[i % 16] = x[i]
+    assert np.array_equal(zc.row_tokens(store, meta, tail, t), x)
+    # a whole BF16 cache serves as the tail too (t mod rows = t)
+    cache = np.concatenate([x, bf16_stream(rng, 16)])
+    assert np.array_equal(zc.row_tokens(store, meta, cache, t), x)
+
+
+def test_decode_from_pages_is_attention_on_the_original_values():
+    # lossless: attention read back from pages and tail equals attention on the BF16 values
+    rng = np.random.default_rng(5)
+    lens = [37, 16, 0]
+    bsz, hkv, g, cap = len(lens), 2, 2, 48
+    x_k = np.stack([np.stack([bf16_stream(rng, cap) for _ in range(hkv)]) for _ in range(bsz)])
+    x_v = np.stack([np.stack([bf16_stream(rng, cap) for _ in range(hkv)]) for _ in range(bsz)])
+    q = (rng.standard_normal((bsz, hkv * g, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ks = np.zeros((bsz, hkv, 3, zc.SLOT), np.uint8)
+    km = np.zeros((bsz, hkv, 3, 8), np.uint8)
+    vs, vm = ks.copy(), km.copy()
+    for b in range(bsz):
+        for h in range(hkv):
+            ks[b, h], km[b, h] = zc.compress_stream(x_k[b, h], 3)
+            vs[b, h], vm[b, h] = zc.compress_stream(x_v[b, h], 3)
+    scale = 128 ** -0.5
+    out, lse = zc.decode_from_pages(q, ks, km, vs, vm, x_k, x_v, lens, scale)
+    qf = zc.bf16_to_float(q)
+    for b, t in enumerate(lens):
+        for h in range(hkv * g):
+            if t == 0:
+                assert lse[b, h] == -math.inf and not out[b, h].any()
+                continue
+            kf, vf = zc.bf16_to_float(x_k[b, h // g, :t]), zc.bf16_to_float(x_v[b, h // g, :t])
+            s = np.array([scale * sum(qf[b, h, d] * kf[j, d] for d in range(128)) for j in range(t)])
+            p = np.exp(s - s.max())
+            ref = (p[:, None] * vf).sum(0) / p.sum()
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-12)
+            assert math.isclose(lse[b, h], s.max() + math.log(p.sum()), rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("t,s", [(0, 3), (1, 1), (70, 1), (70, 3), (70, 8), (8200, 4), (100, 40)])
+def test_sections_are_whole_pages_covering_the_row(t, s):
+    b = zc.section_bounds(t, s)
+    assert len(b) == s and b[0][0] == 0 and b[-1][1] == t
+    for (lo, hi), (lo2, _) in zip(b, b[1:]):
+        assert lo <= hi == lo2
+    assert all(lo % zc.PAGE == 0 or lo == t for lo, _ in b)
+    assert max(hi - lo for lo, hi in b) <= math.ceil(math.ceil(t / s) / zc.PAGE) * zc.PAGE

@@ -6,8 +6,10 @@ flips and the SO(4) quaternion pairs of the rotation) and holds none of the meth
 arithmetic.  Shapes and distributions follow the workloads the pages measure on: a 4B
 GQA model at 8K context ("TurboQuant ... MNN on phones", section 4), 128K-token decode
 ("RoPE-Aware Bit Allocation for KV-Cache Quantization", deployment results) and 32K
-contexts with the IsoQuant rotation ("RotaryQuant ...", key findings).  No dataset is
-read; Gaussian activations with outlier channels stand in for real model activations.
+contexts with the IsoQuant rotation ("RotaryQuant ...", key findings) and a BF16 8B GQA
+model at 8K context, batch 32, for the lossless exponent codec ("ZipFusion ...",
+experiments: Llama 3.1 8B / Qwen3-8B, 8192-token prompts).  No dataset is read; Gaussian
+activations with outlier channels stand in for real model activations.
 """
 
 import os
@@ -29,10 +31,11 @@ class Workload:
     bits_v: int
     group: int               # rotation block = norm group = codebook dimension
     so4: bool                # compose the Hadamard with SO(4) block rotations
-    dtype: str               # "float32" or "float16" activations
+    dtype: str               # "float32", "float16" or "bfloat16" activations (bfloat16 as uint16 bits)
     outliers: str            # "fixed2x10", "seeded4x8" or "lognormal"
     n_splits: int = 1        # key-axis splits used when the workload is timed
     scale: float = HEAD_DIM ** -0.5
+    codec: str = "turboquant"  # "turboquant" (packed 3/4-bit codes) or "zip" (lossless BF16 pages)
 
     @property
     def group_size(self):
@@ -50,7 +53,18 @@ WORKLOADS = {
                          n_splits=64),
     "isoquant32k": Workload("isoquant32k", 8, 32, 8, 32768, 3, 3, 128, True, "float16", "seeded4x8",
                             n_splits=8),
+    # 8192-token prompt in compressed pages plus 8 generated tokens in the open page; the
+    # bits, group and so4 fields do not apply to the lossless codec
+    "zipfusion8k": Workload("zipfusion8k", 32, 32, 8, 8200, 16, 16, 128, False, "bfloat16", "seeded4x8",
+                            n_splits=4, codec="zip"),
 }
+
+
+def bf16_bits(x):
+    """float32 array -> BF16 bit patterns (uint16), rounded to nearest even: how a BF16
+    model stores its activations.  Input preparation only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
 def _stream_normals(seed_seq, bsz, hkv, t, fill):
@@ -75,7 +89,8 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
     """Draw one workload's inputs.
 
     Returns a dict of numpy arrays:
-      q [B, Hq, 128], k [B, Hkv, T, 128], v [B, Hkv, T, 128] in ``w.dtype``;
+      q [B, Hq, 128], k [B, Hkv, T, 128], v [B, Hkv, T, 128] in ``w.dtype`` (bfloat16 as
+      uint16 bit patterns);
       signs [Hkv, 128] float32 (+-1); so4 [Hkv, 32, 2, 4] float32 unit (q_L, q_R) or None;
       seq_lens [B] int32 (all equal to T).
     Every array has its own random stream (K and V one per (sequence, KV head)).
@@ -84,7 +99,9 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
     s_q, s_k, s_v, s_sign, s_so4, s_ch, s_sk, s_sv = ss.spawn(8)
     bsz, hq, hkv, t = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len
     g = w.group_size
-    dt = np.float16 if w.dtype == "float16" else np.float32
+    bf16 = w.dtype == "bfloat16"
+    dt = np.float16 if w.dtype == "float16" else np.uint16 if bf16 else np.float32
+    cast = bf16_bits if bf16 else (lambda a: a)
 
     # per-(KV head, channel) multipliers shared by K and that head's queries, and for V
     mul_k = np.ones((hkv, HEAD_DIM), np.float32)
@@ -116,10 +133,10 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
         v = np.empty((bsz, hkv, t, HEAD_DIM), dt)
 
         def fill_k(b, kv, x):
-            k[b, kv] = x * mul_k[kv]
+            k[b, kv] = cast(x * mul_k[kv])
 
         def fill_v(b, kv, x):
-            v[b, kv] = x * mul_v[kv]
+            v[b, kv] = cast(x * mul_v[kv])
 
         _stream_normals(s_k, bsz, hkv, t, fill_k)
         _stream_normals(s_v, bsz, hkv, t, fill_v)
@@ -131,7 +148,7 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
         quat = np.random.default_rng(s_so4).standard_normal((hkv, HEAD_DIM // 4, 2, 4))
         so4 = (quat / np.linalg.norm(quat, axis=-1, keepdims=True)).astype(np.float32)
     return {
-        "q": q.astype(dt),
+        "q": bf16_bits(q) if bf16 else q.astype(dt),
         "k": k,
         "v": v,
         "signs": signs,
