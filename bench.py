@@ -35,6 +35,7 @@ import workloads  # noqa: E402
 METRIC = "decode attn KV token·heads/s + achieved HBM GB/s vs peak (TQ3, T=32K)"
 HEADLINE = "isoquant32k"
 HBM_PEAK_GBS = 8000.0
+ZIP_RTOL = 1e-4  # lossless codec: fp32 sums of exact BF16 values against fp64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", "tq_kernels.hip")
 
@@ -319,6 +320,234 @@ def run_tail(w, inp, n_tail, tail_splits, steps, warmup, n_splits, schedule):
     return dict(step_ms=step_ms, dense_ms=dense_ms, tail_bytes=tail_bytes, parity=worst, reps=reps)
 
 
+ZIP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zip_traffic.json")
+ZIP_KERNEL_SRC = os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", "tq_zip.hip")
+
+
+def zip_kernel_hash():
+    return hashlib.sha256(open(ZIP_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def zip_setup(w, inp, dev):
+    """Compressed stores of the workload's K and V (every whole page of the row) plus the
+    open-page buffers of 16 rows holding its last T mod 16 tokens, and the query."""
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    T = w.seq_len
+    pages = T // 16
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    stores, compress_ms = [], []
+    for role, rc in (("k", tq.TQ_KEYS), ("v", tq.TQ_VALUES)):
+        x = bf16(inp[role][:, :, :16 * pages])
+        s, m = tq.zip_store(w.batch, w.n_kv_heads, pages, device=dev)
+        tq.zip_compress(x, s, m, rc, n_pages=1)  # loads the kernel before timing
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.zip_compress(x, s, m, rc, n_pages=pages)
+        e1.record()
+        torch.cuda.synchronize()
+        compress_ms.append(e0.elapsed_time(e1))
+        stores += [s, m]
+        del x
+    tails = []
+    for role in ("k", "v"):
+        t = torch.zeros((w.batch, w.n_kv_heads, 16, 128), dtype=torch.bfloat16, device=dev)
+        n = T - 16 * pages
+        if n:
+            t[:, :, :n] = bf16(inp[role][:, :, 16 * pages:T])
+        tails.append(t)
+    q = bf16(inp["q"])
+    return stores, tails, q, sum(compress_ms)
+
+
+def zip_algorithmic_bytes(w, k_meta, v_meta):
+    """KV bytes one launch must read: every page's stored chunks (768 coded, 1024 kept) and
+    its 8 metadata bytes, and the open page's BF16 tokens, for keys and values."""
+    total = 0
+    for m in (k_meta, v_meta):
+        flags = m[..., 4:].cpu().numpy()
+        total += int(np.where(flags == 0xFF, 1024, 768).sum()) + 8 * flags.shape[0] * flags.shape[1] * flags.shape[2]
+    total += 2 * w.batch * w.n_kv_heads * (w.seq_len % 16) * 256
+    return total
+
+
+def run_zip(w, inp, steps, warmup, n_splits, check=True):
+    """The step on the lossless BF16 codec: attention read straight from the compressed
+    pages (and the open page), its sections merged without rotation."""
+    import torch
+
+    import compressed_domain_attention_amd as tq
+
+    dev = torch.device("cuda:0")
+    (ks, km, vs, vm), (kt, vt), q, compress_ms = zip_setup(w, inp, dev)
+    store_bytes = 2 * (ks.numel() + km.numel())
+    reps = min(256, max(2, math.ceil((1 << 30) / store_bytes)))
+    sets = [(ks, km, vs, vm)] + [tuple(t.clone() for t in (ks, km, vs, vm)) for _ in range(reps - 1)]
+    log("compressed stores %.1f MB x %d replicas" % (store_bytes / 1e6, reps))
+    S = n_splits
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    po = torch.empty((S, w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((S, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+
+    def attend(i):
+        a = sets[i % reps]
+        if S == 1:
+            tq.zip_attention(*a, kt, vt, q, max_len=w.seq_len, scale=w.scale, out=out, lse=lse)
+        else:
+            tq.zip_attention(*a, kt, vt, q, max_len=w.seq_len, scale=w.scale, n_splits=S, part_o=po, part_lse=pl)
+
+    def step(i):
+        attend(i)
+        if S > 1:
+            tq.merge_splits(None, po, pl, out=out, lse=lse)
+
+    def graph(fn, n):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager_out):
+        raise SystemExit("graph replay does not reproduce the eager step")
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < 0.3:
+        graphs[i % reps].replay()
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % reps].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    if not torch.equal(out, eager_out):
+        raise SystemExit("graph replays drifted from the eager step")
+    n_att = max(reps, 16)
+    ga = graph(lambda i: attend(i), n_att)
+    ga.replay()
+    torch.cuda.synchronize()
+    t_d = time.perf_counter()
+    ga.replay()
+    torch.cuda.synchronize()
+    reps_att = max(3, int(0.5 / max(time.perf_counter() - t_d, 1e-6)))
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(reps_att):
+        ga.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    att_ms = d0.elapsed_time(d1) / (reps_att * n_att)
+
+    parity = None
+    if check:
+        # lossless: the output must be attention on the original BF16 values
+        from helpers import row_rel_err
+        from oracle import attention, zipcodec as zc
+        o = out.cpu().numpy()
+        parity = 0.0
+        for b, kv in [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
+            kf = zc.bf16_to_float(inp["k"][b, kv, :w.seq_len])
+            vf = zc.bf16_to_float(inp["v"][b, kv, :w.seq_len])
+            for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+                ref, _ = attention.softmax_attend(zc.bf16_to_float(inp["q"][b, h]), kf, vf, w.scale)
+                parity = max(parity, float(row_rel_err(o[b, h], ref)))
+        if parity > ZIP_RTOL:
+            raise SystemExit("parity check failed: %.3e > %.1e" % (parity, ZIP_RTOL))
+    algo = zip_algorithmic_bytes(w, km, vm)
+    raw = 2 * w.batch * w.n_kv_heads * w.seq_len * 256
+    frac_kept = float(np.mean(np.concatenate([(m[..., 4:].cpu().numpy() == 0xFF).ravel() for m in (km, vm)])))
+    return dict(step_ms=step_ms, attn_ms=att_ms, algo_bytes=algo, bf16_bytes=raw, reps=reps, parity=parity,
+                compress_ms=compress_ms, kept_fraction=frac_kept, store_bytes=store_bytes)
+
+
+def zip_counter_run(w, inp, n_splits, launches=24):
+    """rocprofv3 --pmc dispatches for the codec: the calibration copies, then `launches`
+    attention launches over the store replicas, as run_zip times them."""
+    import ctypes
+
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    from compressed_domain_attention_amd import build as _b
+
+    dev = torch.device("cuda:0")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.tq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
+    torch.cuda.synchronize()
+    del src, dst
+    (ks, km, vs, vm), (kt, vt), q, _ = zip_setup(w, inp, dev)
+    store_bytes = 2 * (ks.numel() + km.numel())
+    reps = min(256, max(2, math.ceil((1 << 30) / store_bytes)))
+    sets = [(ks, km, vs, vm)] + [tuple(t.clone() for t in (ks, km, vs, vm)) for _ in range(reps - 1)]
+    po = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((max(n_splits, 1), w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    for i in range(launches):
+        a = sets[i % reps]
+        if n_splits == 1:
+            tq.zip_attention(*a, kt, vt, q, max_len=w.seq_len, scale=w.scale, out=out)
+        else:
+            tq.zip_attention(*a, kt, vt, q, max_len=w.seq_len, scale=w.scale, n_splits=n_splits, part_o=po,
+                             part_lse=pl)
+    torch.cuda.synchronize()
+    log("counter run: 3 copies of %d bytes, %d zip attention launches over %d replicas" % (
+        COPY_BYTES, launches, reps))
+
+
+def zip_measured_traffic(workload, n_splits):
+    if not os.path.exists(ZIP_TRAFFIC_FILE):
+        return None
+    rec = json.load(open(ZIP_TRAFFIC_FILE))
+    if rec.get("kernel_sha256_16") != zip_kernel_hash():
+        return None
+    ent = rec.get("workloads", {}).get("%s/S%d" % (workload, n_splits))
+    return None if ent is None else ent["hbm_bytes_per_launch"]
+
+
+def _oracle_zip_unit(args):
+    w, b, kv = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import attention, zipcodec as zc
+    inp = _oracle_unit.inp
+    T = w.seq_len
+    pages = T // zc.PAGE
+    ks, km = zc.compress_stream(inp["k"][b, kv], pages, "k")  # the cache as stored (not timed)
+    vs, vm = zc.compress_stream(inp["v"][b, kv], pages, "v")
+    t0 = time.perf_counter()
+    kf = zc.bf16_to_float(zc.row_tokens(ks, km, inp["k"][b, kv], T, "k"))
+    vf = zc.bf16_to_float(zc.row_tokens(vs, vm, inp["v"][b, kv], T, "v"))
+    for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+        attention.softmax_attend(zc.bf16_to_float(inp["q"][b, h]), kf, vf, w.scale)
+    return time.perf_counter() - t0
+
+
 def sampled_parity(w, inp, out):
     """Oracle check of a few (sequence, query head) rows of the measured output."""
     from helpers import OUT_RTOL, row_rel_err
@@ -374,20 +603,26 @@ def cpu_baseline(w, inp, budget_s=15.0):
 
     cores = min(len(os.sched_getaffinity(0)), 16)
     _oracle_unit.inp = inp
-    units = [(w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
+    zip_ = w.codec == "zip"
+    units = [(w, b, kv) if zip_ else (w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
     done, busy, t0 = 0, 0.0, time.perf_counter()
     with threadpool_limits(1):
         ctx = mp.get_context("fork")
         with ctx.Pool(cores) as pool:
             while done < len(units) and time.perf_counter() - t0 < budget_s:
                 batch = units[done:done + cores]
-                busy += sum(pool.map(_oracle_unit, batch))
+                busy += sum(pool.map(_oracle_zip_unit if zip_ else _oracle_unit, batch))
                 done += len(batch)
     wall = time.perf_counter() - t0
     token_heads = done * w.seq_len
-    return {"value": token_heads / wall, "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d (sequence, KV head) streams of %s (T=%d), fp64 dequantise + attention, "
-                      "%d worker processes x 1 thread, %.1fs wall" % (done, len(units), w.name, w.seq_len, cores, wall)}
+    what = ("decompress the stored pages + fp64 attention (compression of the stream not timed)" if zip_
+            else "fp64 dequantise + attention")
+    # the rate over the time the workers spent in the timed part, all workers together
+    value = token_heads / (busy / cores) if zip_ else token_heads / wall
+    return {"value": value, "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) streams of %s (T=%d), %s, "
+                      "%d worker processes x 1 thread, %.1fs wall" % (done, len(units), w.name, w.seq_len, what,
+                                                                       cores, wall)}
 
 
 def stream_read_probe_gbs():
@@ -514,6 +749,31 @@ def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
         w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
 
 
+def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
+    """As write_traffic, for the codec's attention kernel (profiles/zip_traffic.json)."""
+    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy_kernel"), _per_dispatch(write_csv, "WRITE_SIZE", "copy_kernel")
+    fd = _per_dispatch(fetch_csv, "FETCH_SIZE", "zip_attention")
+    wd = _per_dispatch(write_csv, "WRITE_SIZE", "zip_attention")
+    if not (fc and wc and fd and wd):
+        raise SystemExit("counter files hold no copy or zip attention dispatches")
+    f_factor = COPY_BYTES / (sum(fc) / len(fc) * 1024)
+    w_factor = COPY_BYTES / (sum(wc) / len(wc) * 1024)
+    fd, wd = fd[len(fd) // 2:], wd[len(wd) // 2:]
+    read = sum(fd) / len(fd) * 1024 * f_factor
+    written = sum(wd) / len(wd) * 1024 * w_factor
+    rec = json.load(open(ZIP_TRAFFIC_FILE)) if os.path.exists(ZIP_TRAFFIC_FILE) else {}
+    if rec.get("kernel_sha256_16") != zip_kernel_hash():
+        rec = {"kernel_sha256_16": zip_kernel_hash(), "workloads": {}}
+    rec["workloads"]["%s/S%d" % (w.name, n_splits)] = {
+        "hbm_bytes_per_launch": read + written, "read_bytes": read, "written_bytes": written,
+        "fetch_scale": f_factor, "write_scale": w_factor, "commands": commands}
+    os.makedirs(os.path.dirname(ZIP_TRAFFIC_FILE), exist_ok=True)
+    with open(ZIP_TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    log("traffic %s/S%d: read %.1f MB + written %.2f MB per launch (scales %.3f, %.3f)" % (
+        w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -542,7 +802,10 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     n_splits = args.splits if args.splits is not None else w.n_splits
     if args.write_traffic:
-        write_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
+        if w.codec == "zip":
+            write_zip_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
+        else:
+            write_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
         return
     log("workload %s: %s, splits %d, schedule %s" % (w.name, w, n_splits, args.schedule))
     t_gen = time.perf_counter()
@@ -558,6 +821,37 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.counter_run:
         counter_run(w, inp, n_splits, args.schedule)
+        return
+    if w.codec == "zip":
+        if args.counter_run:
+            zip_counter_run(w, inp, n_splits)
+            return
+        r = run_zip(w, inp, args.steps, args.warmup, n_splits, check=not args.no_check)
+        units = w.batch * w.n_kv_heads * w.seq_len
+        achieved = r["algo_bytes"] / (r["attn_ms"] / 1e3) / 1e9
+        bf16_gbs = r["bf16_bytes"] / (r["attn_ms"] / 1e3) / 1e9
+        probe = stream_read_probe_gbs()
+        log("step %.3f ms, attention kernel %.3f ms -> %.0f GB/s of compressed pages (%.1f%% of 8 TB/s, %.1f%% of "
+            "the %.0f GB/s probe); %.0f GB/s BF16-equivalent; %.1f%% of chunks kept; compress %.3f ms" % (
+                r["step_ms"], r["attn_ms"], achieved, 100 * achieved / HBM_PEAK_GBS, 100 * achieved / probe, probe,
+                bf16_gbs, 100 * r["kept_fraction"], r["compress_ms"]))
+        print(json.dumps({
+            "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 exact (lossless codes), f32 FMA",
+            "data": "synthetic (seeded Gaussian activations with outlier channels, rounded to BF16; workloads.py)",
+            "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                       "seq_len": w.seq_len, "codec": "lossless BF16 exponent codec (16-token pages)",
+                       "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
+                       "step": "attention from the compressed pages + open page, then merge",
+                       "store_replicas": r["reps"]},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": zip_measured_traffic(w.name, n_splits),
+                         "kernel": "zip_attention_kernel"},
+            "cpu_baseline": cpu, "attention_kernel_ms": r["attn_ms"], "algorithmic_bytes_per_launch": r["algo_bytes"],
+            "bf16_equivalent_GBps": bf16_gbs, "kept_chunk_fraction": r["kept_fraction"],
+            "compress_ms": r["compress_ms"], "stream_read_probe_GBps": probe,
+            "parity_worst_row_rel_err": r["parity"]}), flush=True)
         return
     if args.tail > w.seq_len:
         raise SystemExit("--tail takes at most the workload's %d generated tokens" % w.seq_len)

@@ -102,7 +102,7 @@ def library():
     lib.tq_dense_attention.restype = I
     lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
     lib.tq_merge_splits.restype = I
-    lib.tq_zip_compress.argtypes = [P, I, I, I, I, I, I, P, P, I, P]
+    lib.tq_zip_compress.argtypes = [P, I, I, I, I, I, I, I, P, P, I, P]
     lib.tq_zip_compress.restype = I
     lib.tq_zip_attention.argtypes = [P, P, P, P, I, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_zip_attention.restype = I
@@ -329,18 +329,19 @@ def _check_store(store, meta, batch, n_kv_heads):
         raise ValueError("store must be [batch, n_kv_heads, ...] of the BF16 buffer")
 
 
-def zip_compress(x: torch.Tensor, store: torch.Tensor, meta: torch.Tensor, n_pages=None, src_page0=0,
+def zip_compress(x: torch.Tensor, store: torch.Tensor, meta: torch.Tensor, role: int, n_pages=None, src_page0=0,
                  dst_page0=0):
-    """Compress whole 16-token pages of x (bfloat16 [batch, n_kv_heads, rows, 128]): page i is
-    rows 16 (src_page0 + i) .. +15 and becomes store page dst_page0 + i.  n_pages defaults to
-    every whole page of x from src_page0."""
+    """Compress whole 16-token pages of keys (role TQ_KEYS) or values (TQ_VALUES) x
+    (bfloat16 [batch, n_kv_heads, rows, 128]): page i is rows 16 (src_page0 + i) .. +15 and
+    becomes store page dst_page0 + i.  n_pages defaults to every whole page of x from
+    src_page0."""
     if x.dtype != torch.bfloat16 or x.dim() != 4 or x.shape[3] != HEAD_DIM or not x.is_contiguous():
         raise ValueError("x must be contiguous bfloat16 [batch, n_kv_heads, rows, 128]")
     bsz, hkv, rows = x.shape[0], x.shape[1], x.shape[2]
     _check_store(store, meta, bsz, hkv)
     if n_pages is None:
         n_pages = rows // ZIP_PAGE - src_page0
-    _check(library().tq_zip_compress(_ptr(x), bsz, hkv, rows, src_page0, dst_page0, n_pages, _ptr(store),
+    _check(library().tq_zip_compress(_ptr(x), role, bsz, hkv, rows, src_page0, dst_page0, n_pages, _ptr(store),
                                      _ptr(meta), store.shape[2], _stream()), "tq_zip_compress")
     return store, meta
 

@@ -269,10 +269,11 @@ extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, i
   return from_hip(tq::launch_merge(a, (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_heads, int32_t x_rows,
+extern "C" tq_status tq_zip_compress(const void* x, tq_role role, int32_t batch, int32_t n_kv_heads, int32_t x_rows,
                                      int32_t src_page0, int32_t dst_page0, int32_t n_pages, uint8_t* store,
                                      uint8_t* meta, int32_t store_pages, void* stream) {
   if (x == nullptr || store == nullptr || meta == nullptr) return TQ_EINVAL;
+  if (role != TQ_KEYS && role != TQ_VALUES) return TQ_EINVAL;
   if (batch <= 0 || n_kv_heads <= 0 || x_rows <= 0 || store_pages <= 0) return TQ_EINVAL;
   if (src_page0 < 0 || dst_page0 < 0 || n_pages < 0) return TQ_EINVAL;
   if ((int64_t)tq::kZipPage * ((int64_t)src_page0 + n_pages) > x_rows) return TQ_ECAPACITY;
@@ -282,6 +283,7 @@ extern "C" tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_
   if (n_pages == 0) return TQ_OK;
   tq::ZipCompressArgs a;
   a.x = (const uint16_t*)x;
+  a.values = role == TQ_VALUES;
   a.store = store;
   a.meta = meta;
   a.n_kv_heads = n_kv_heads;

@@ -91,6 +91,7 @@ constexpr int kZipSlot = 4096;
 
 struct ZipCompressArgs {
   const uint16_t* x;   // BF16 [batch][n_kv_heads][x_rows][128]
+  int32_t values;      // 0 keys (chunks of 4 tokens), 1 values (chunks of 32 coordinates)
   uint8_t* store;      // [batch][n_kv_heads][store_pages][4096]
   uint8_t* meta;       // [batch][n_kv_heads][store_pages][8]
   int32_t n_kv_heads;

@@ -13,7 +13,7 @@
 #include <stdint.h>
 
 #include "tq_internal.h"
-#include "tq_lanes.h"
+#include "tq_device.h"
 
 namespace tq {
 namespace {
@@ -647,10 +647,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                 0, 0);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
 
 // LDS byte address of a two-code table lookup: the 2*BITS-bit field at bit `off` of d[]
 // lands on bits [SH, SH + 2*BITS) of the address and the lane's copy offset fills the bits
@@ -711,63 +707,6 @@ __device__ __forceinline__ float rows_sum(float x) {
 template <typename T>
 __device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
   return *(const T*)(base + off);
-}
-
-// Direct global -> LDS copies: every lane reads BYTES bytes and the data lands in LDS at
-// lds_base + lane * stride (lds_base is wave-uniform, passed in M0), where the stride is
-// BYTES for 4- and 16-byte copies and 16 for 12-byte copies (the fourth dword of each lane
-// is left untouched).  They count in vmcnt
-// like ordinary loads but leave no register results, so a deep prefetch ring costs no
-// VGPRs.  Written as inline assembly: the compiler would otherwise make every later LDS
-// read wait for all of them.  The caller waits with vm_wait before reading the data.
-// STREAM marks data read once (the cache stream): the non-temporal policy, which on this
-// chip lifts a pure read stream from about 6.2 to 7.0 TB/s.
-template <int BYTES, bool STREAM>
-__device__ __forceinline__ void lds_dma(uint32_t lds_base, const void* sbase, uint32_t voff) {
-  if (BYTES == 16) {
-    if (STREAM)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
-  } else if (BYTES == 12) {
-    if (STREAM)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
-  } else {
-    static_assert(BYTES == 12 || BYTES == 16, "whole-lane copies of 12 or 16 bytes");
-  }
-}
-template <int BYTES, bool STREAM>
-__device__ __forceinline__ void lds_dma_addr(uint32_t lds_base, const void* addr) {
-  if (BYTES == 16) {
-    if (STREAM)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(addr) : "memory", "m0");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
-  } else if (BYTES == 4) {
-    if (STREAM)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off nt" ::"s"(lds_base), "v"(addr) : "memory", "m0");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(addr) : "memory", "m0");
-  } else {
-    static_assert(BYTES == 4 || BYTES == 16, "whole-lane copies of 4 or 16 bytes");
-  }
-}
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Wait until every LDS access of this wave is complete.
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // NW waves per workgroup: 4 with two workgroups per CU, or 8 with one (grids of at most

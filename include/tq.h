@@ -227,13 +227,16 @@ tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batc
  * Decompression with Attention ...", compression format, page metadata, register decode).
  *
  * A BF16 cache of [batch][n_kv_heads][tokens][128] (keys and values separately) is cut into
- * pages of 16 tokens; a page of one (sequence, KV head) is 4 chunks of 512 values, chunk c
- * holding the page's tokens 4c .. 4c+3 (token-major).  A chunk whose exponents all lie in
- * [b, b+15], b = its smallest exponent rounded down to even, is coded: its 512 low bytes
- * (7 mantissa bits and the exponent's lowest bit) as they are, then 256 code bytes, byte
- * 4g+j holding value 8g+j (sign in bit 7, d = (exponent-b)/2 rounded down in bits 0-2) and
- * value 8g+j+4 (sign bit 6, d bits 3-5): 768 bytes, 75% of the original.  Any other chunk
- * is kept as its 1024 bytes.
+ * pages of 16 tokens; a page of one (sequence, KV head) is 4 chunks of 512 values, laid out
+ * for the matrix products that read them (groups of 8 consecutive values are one thread's
+ * operand): keys, chunk c = the page's tokens 4c .. 4c+3, token-major (a group = 8
+ * coordinates of one token); values, chunk c = coordinates 32c .. 32c+31 of the page's 16
+ * tokens, coordinate-major, value (d - 32c)*16 + t (a group = 8 tokens of one coordinate).
+ * A chunk whose exponents all lie in [b, b+15], b = its smallest exponent rounded down to
+ * even, is coded: its 512 low bytes (7 mantissa bits and the exponent's lowest bit) as they
+ * are, then 256 code bytes, byte 4g+j holding value 8g+j (sign in bit 7, d = (exponent-b)/2
+ * rounded down in bits 0-2) and value 8g+j+4 (sign bit 6, d bits 3-5): 768 bytes, 75% of
+ * the original.  Any other chunk is kept as its 512 BF16 values (1024 bytes, same order).
  *   store: uint8 [batch][n_kv_heads][store_pages][4096]: page p's chunks back to back from
  *          the start of its 4096-byte slot; the slot's other bytes are zero.
  *   meta:  uint8 [batch][n_kv_heads][store_pages][8]: little-endian u32 byte offset of the
@@ -241,16 +244,17 @@ tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, int32_t batc
  *          here), then one byte per chunk: 0xFF when kept, else b/2.
  * Decoding is exact: the high byte of a coded value is sign*128 + b/2 + d. */
 
-/* Compresses n_pages whole pages of a BF16 token buffer into a store.
+/* Compresses n_pages whole pages of a BF16 token buffer of keys (role TQ_KEYS) or values
+ * (TQ_VALUES) into a store.
  *   x:     device BF16 [batch][n_kv_heads][x_rows][128]; page i of the call is rows
  *          16*(src_page0+i) .. +15 and becomes store page dst_page0+i, for every
  *          (sequence, KV head).  A prefilled cache is compressed with x = the cache,
  *          src_page0 = dst_page0 = 0; a tail buffer of 16 rows that has just filled, with
  *          x_rows = 16, src_page0 = 0 and dst_page0 = its page number.
  *   store, meta: device, as above; only the n_pages pages are written.
- * Errors: TQ_EINVAL for null pointers, non-positive counts or negative page numbers;
- * TQ_ECAPACITY when the pages pass x_rows or store_pages.  n_pages == 0 is a no-op. */
-tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_heads, int32_t x_rows, int32_t src_page0,
+ * Errors: TQ_EINVAL for null pointers, a bad role, non-positive counts or negative page
+ * numbers; TQ_ECAPACITY when the pages pass x_rows or store_pages.  n_pages == 0 is a no-op. */
+tq_status tq_zip_compress(const void* x, tq_role role, int32_t batch, int32_t n_kv_heads, int32_t x_rows, int32_t src_page0,
                           int32_t dst_page0, int32_t n_pages, uint8_t* store, uint8_t* meta, int32_t store_pages,
                           void* stream);
 
@@ -262,8 +266,8 @@ tq_status tq_zip_compress(const void* x, int32_t batch, int32_t n_kv_heads, int3
  * t mod tail_rows = t there).
  *   k_store, k_meta, v_store, v_meta: device, as written by tq_zip_compress; offsets read
  *          from the metadata are clamped so that a page slot stays inside the stream.
- *   k_tail, v_tail: device BF16 [batch][n_kv_heads][tail_rows][128]; tail_rows a positive
- *          multiple of 16.
+ *   k_tail, v_tail: device BF16 [batch][n_kv_heads][tail_rows][128], token-major for both
+ *          roles; tail_rows a positive multiple of 16.
  *   q:     device [batch][n_q_heads][128] of q_dtype (TQ_F32, TQ_F16 or TQ_BF16); query
  *          head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads / n_kv_heads <= 8,
  *          or a multiple of 8.

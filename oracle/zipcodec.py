@@ -27,10 +27,18 @@ compressed"), the page metadata and the register decode.
   compressed; the open page (its last T mod 16 tokens) is kept uncompressed so that new
   tokens append to it ("ZipFusion ...", system overview: pages are compressed when full).
 
-Readings (the pages leave these open): chunk c of a page is tokens 4c .. 4c+3, token-major
-(coordinate order within a token); the 8 values that share 4 code bytes are 8 consecutive
-values of the chunk (group g = values 8g .. 8g+7, code byte 4g + j holds values 8g + j and
-8g + j + 4); a compressed chunk is its 512 low bytes, then its 256 code bytes; the
+* Layout follows the matrix products: the 8 values one thread feeds the matrix unit are
+  stored together, and keys and values, which play different parts in the two products
+  (scores: tokens x coordinates; output: coordinates summed over tokens), are laid out
+  separately ("ZipFusion ...", register decode section).
+
+Readings (the pages leave these open): the 8 values that share 4 code bytes are 8
+consecutive values of the chunk (group g = values 8g .. 8g+7, code byte 4g + j holds values
+8g + j and 8g + j + 4); keys: chunk c of a page is tokens 4c .. 4c+3, token-major, so a
+group is 8 consecutive coordinates of one token; values: chunk c of a page is coordinates
+32c .. 32c+31 of its 16 tokens, coordinate-major (value (d - 32c) * 16 + t), so a group is
+8 consecutive tokens of one coordinate; a kept chunk holds its 512 values in the same
+order; a compressed chunk is its 512 low bytes, then its 256 code bytes; the
 "uncompressed" mark is 0xFF (b/2 is at most 127); a page's chunks are stored back to back
 from the start of a fixed 4096-byte page slot, and the 4-byte start field is the byte
 offset of that slot within the (sequence, KV head) stream, little-endian; the open page's
@@ -104,15 +112,27 @@ def decompress_chunk(b_half, payload):
     return out
 
 
-def compress_stream(bits, n_pages):
-    """One (sequence, KV head) stream of keys or values [T >= 16 n_pages][128] (uint16)
-    -> (store bytes [n_pages][4096] uint8, metadata [n_pages][8] uint8).  Only full pages
-    are compressed; unused slot bytes are zero."""
+def page_values(page, role):
+    """A page's [16][128] values in chunk order: keys token-major, values coordinate-major."""
+    page = np.asarray(page)
+    return (page if role == "k" else page.T).reshape(-1)
+
+
+def page_from_values(vals, role):
+    """Inverse of page_values: chunk-order values -> the page's [16][128] values."""
+    vals = np.asarray(vals)
+    return vals.reshape(PAGE, HEAD_DIM) if role == "k" else vals.reshape(HEAD_DIM, PAGE).T
+
+
+def compress_stream(bits, n_pages, role):
+    """One (sequence, KV head) stream of keys (role "k") or values ("v") [T >= 16 n_pages]
+    [128] (uint16) -> (store bytes [n_pages][4096] uint8, metadata [n_pages][8] uint8).
+    Only full pages are compressed; unused slot bytes are zero."""
     x = np.asarray(bits, dtype=np.uint16)
     store = np.zeros((n_pages, SLOT), dtype=np.uint8)
     meta = np.zeros((n_pages, 8), dtype=np.uint8)
     for p in range(n_pages):
-        page = x[PAGE * p:PAGE * (p + 1)].reshape(-1)  # token-major
+        page = page_values(x[PAGE * p:PAGE * (p + 1)], role)
         pos = 0
         meta[p, :4] = np.frombuffer(np.uint32(p * SLOT).astype("<u4").tobytes(), dtype=np.uint8)
         for c in range(CHUNKS):
@@ -123,7 +143,7 @@ def compress_stream(bits, n_pages):
     return store, meta
 
 
-def decompress_stream(store, meta, n_pages):
+def decompress_stream(store, meta, n_pages, role):
     """Inverse of compress_stream: -> bits [16 n_pages][128] uint16."""
     out = np.zeros((n_pages * PAGE, HEAD_DIM), dtype=np.uint16)
     for p in range(n_pages):
@@ -135,7 +155,7 @@ def decompress_stream(store, meta, n_pages):
             n = CHUNK * 2 if m == RAW else COMPRESSED_BYTES
             vals.append(decompress_chunk(None if m == RAW else m, store[p, pos:pos + n].tobytes()))
             pos += n
-        out[PAGE * p:PAGE * (p + 1)] = np.concatenate(vals).reshape(PAGE, HEAD_DIM)
+        out[PAGE * p:PAGE * (p + 1)] = page_from_values(np.concatenate(vals), role)
     return out
 
 
@@ -144,14 +164,14 @@ def page_bytes(meta_row):
     return sum(CHUNK * 2 if int(m) == RAW else COMPRESSED_BYTES for m in meta_row[4:])
 
 
-def row_tokens(store, meta, tail, t):
+def row_tokens(store, meta, tail, t, role):
     """The BF16 bits [t][128] of one (sequence, KV head) row of t tokens: pages 0 ..
     t // 16 - 1 decompressed from its store and metadata, the rest from its tail buffer
-    (token i at tail row i mod len(tail))."""
+    (token i at tail row i mod len(tail), token-major for both roles)."""
     full = t // PAGE
     out = np.zeros((t, HEAD_DIM), dtype=np.uint16)
     if full:
-        out[:full * PAGE] = decompress_stream(store, meta, full)
+        out[:full * PAGE] = decompress_stream(store, meta, full, role)
     for i in range(full * PAGE, t):
         out[i] = tail[i % len(tail)]
     return out
@@ -168,8 +188,8 @@ def decode_from_pages(q, k_store, k_meta, v_store, v_meta, k_tail, v_tail, seq_l
     for b in range(bsz):
         t = int(seq_lens[b])
         for h in range(hkv):
-            k[b, h, :t] = bf16_to_float(row_tokens(k_store[b, h], k_meta[b, h], k_tail[b, h], t))
-            v[b, h, :t] = bf16_to_float(row_tokens(v_store[b, h], v_meta[b, h], v_tail[b, h], t))
+            k[b, h, :t] = bf16_to_float(row_tokens(k_store[b, h], k_meta[b, h], k_tail[b, h], t, "k"))
+            v[b, h, :t] = bf16_to_float(row_tokens(v_store[b, h], v_meta[b, h], v_tail[b, h], t, "v"))
     return attention.decode(bf16_to_float(q), k, v, seq_lens, scale)
 
 

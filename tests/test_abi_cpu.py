@@ -219,14 +219,15 @@ def test_merge_validation(lib):
     assert m(ctypes.byref(rot), 2, 1, 4, FAKE, FAKE, None, None, None) == TQ_EINVAL
 
 
-def zip_compress(lib, x=FAKE, batch=1, heads=1, rows=64, src=0, dst=0, n=4, store=FAKE, meta=FAKE, pages=4):
-    return lib.tq_zip_compress(x, batch, heads, rows, src, dst, n, store, meta, pages, None)
+def zip_compress(lib, x=FAKE, role=1, batch=1, heads=1, rows=64, src=0, dst=0, n=4, store=FAKE, meta=FAKE, pages=4):
+    return lib.tq_zip_compress(x, role, batch, heads, rows, src, dst, n, store, meta, pages, None)
 
 
 def test_zip_compress_validation(lib):
     assert zip_compress(lib, x=None) == TQ_EINVAL
     assert zip_compress(lib, store=None) == TQ_EINVAL
     assert zip_compress(lib, meta=None) == TQ_EINVAL
+    assert zip_compress(lib, role=2) == TQ_EINVAL
     assert zip_compress(lib, batch=0) == TQ_EINVAL
     assert zip_compress(lib, heads=0) == TQ_EINVAL
     assert zip_compress(lib, rows=0) == TQ_EINVAL

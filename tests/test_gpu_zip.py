@@ -43,19 +43,22 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def oracle_stores(x, pages):
+ROLE = {"k": tq.TQ_KEYS, "v": tq.TQ_VALUES}
+
+
+def oracle_stores(x, pages, role):
     bsz, hkv = x.shape[:2]
     store = np.zeros((bsz, hkv, pages, zc.SLOT), np.uint8)
     meta = np.zeros((bsz, hkv, pages, 8), np.uint8)
     for b in range(bsz):
         for h in range(hkv):
-            store[b, h], meta[b, h] = zc.compress_stream(x[b, h], pages)
+            store[b, h], meta[b, h] = zc.compress_stream(x[b, h], pages, role)
     return store, meta
 
 
-def device_stores(x, pages):
+def device_stores(x, pages, role):
     s, m = tq.zip_store(x.shape[0], x.shape[1], pages)
-    tq.zip_compress(dev_bf16(x), s, m, n_pages=pages)
+    tq.zip_compress(dev_bf16(x), s, m, ROLE[role], n_pages=pages)
     return s, m
 
 
@@ -72,12 +75,12 @@ def test_compress_matches_oracle_bytes(seed):
     k[0, 0, 36:40] = (k[0, 0, 36:40] & 0x807F) | (125 << 7)
     k[0, 0, 36, 0] = (k[0, 0, 36, 0] & 0x807F) | (120 << 7)
     k[0, 0, 37, 1] = (k[0, 0, 37, 1] & 0x807F) | (136 << 7)
-    for x in (k, inp["v"]):
-        os_, om = oracle_stores(x, pages)
-        ds, dm = device_stores(x, pages)
+    for x, role in ((k, "k"), (inp["v"], "v")):
+        os_, om = oracle_stores(x, pages, role)
+        ds, dm = device_stores(x, pages, role)
         assert np.array_equal(dm.cpu().numpy(), om)
         assert np.array_equal(ds.cpu().numpy(), os_)
-    om = oracle_stores(k, pages)[1]
+    om = oracle_stores(k, pages, "k")[1]
     assert om[0, 0, 2, 4] == 60 and om[0, 0, 2, 5] == zc.RAW
     flags = om[..., 4:]
     assert 0 < np.mean(flags == zc.RAW) < 0.5  # the data has both kinds of chunk
@@ -87,21 +90,22 @@ def test_compress_open_page_into_its_slot():
     # a 16-row open-page buffer that has filled becomes page p of the store; other pages stay
     w, inp = case(lens=[40, 40])
     pages = w.seq_len // zc.PAGE
-    full_s, full_m = oracle_stores(inp["k"], pages)
-    s, m = device_stores(inp["k"], pages)
-    p = 7
-    open_page = inp["k"][:, :, 16 * p:16 * (p + 1)].copy()
-    s[:, :, p].fill_(0xAB)
-    m[:, :, p].fill_(0xAB)
-    tq.zip_compress(dev_bf16(open_page), s, m, src_page0=0, dst_page0=p)
-    assert np.array_equal(s.cpu().numpy(), full_s)
-    assert np.array_equal(m.cpu().numpy(), full_m)
+    for role in ("k", "v"):
+        full_s, full_m = oracle_stores(inp[role], pages, role)
+        s, m = device_stores(inp[role], pages, role)
+        p = 7
+        open_page = inp[role][:, :, 16 * p:16 * (p + 1)].copy()
+        s[:, :, p].fill_(0xAB)
+        m[:, :, p].fill_(0xAB)
+        tq.zip_compress(dev_bf16(open_page), s, m, ROLE[role], src_page0=0, dst_page0=p)
+        assert np.array_equal(s.cpu().numpy(), full_s)
+        assert np.array_equal(m.cpu().numpy(), full_m)
 
 
 def run_attention(w, inp, lens, n_splits, q_dtype=torch.bfloat16, tail="cache"):
     pages = w.seq_len // zc.PAGE
-    ks, km = device_stores(inp["k"], pages)
-    vs, vm = device_stores(inp["v"], pages)
+    ks, km = device_stores(inp["k"], pages, "k")
+    vs, vm = device_stores(inp["v"], pages, "v")
     if tail == "cache":
         kt, vt = dev_bf16(inp["k"]), dev_bf16(inp["v"])
     else:
@@ -123,8 +127,8 @@ def run_attention(w, inp, lens, n_splits, q_dtype=torch.bfloat16, tail="cache"):
 
 def oracle_attention(w, inp, lens):
     pages = w.seq_len // zc.PAGE
-    ks, km = oracle_stores(inp["k"], pages)
-    vs, vm = oracle_stores(inp["v"], pages)
+    ks, km = oracle_stores(inp["k"], pages, "k")
+    vs, vm = oracle_stores(inp["v"], pages, "v")
     return zc.decode_from_pages(inp["q"], ks, km, vs, vm, inp["k"], inp["v"], lens, w.scale)
 
 
@@ -154,13 +158,15 @@ def test_sections_match_oracle_and_merge(n_splits):
     w, inp = case()
     po, pl = run_attention(w, inp, LENS, n_splits)
     pages = w.seq_len // zc.PAGE
-    ks, km = oracle_stores(inp["k"], pages)
-    vs, vm = oracle_stores(inp["v"], pages)
+    ks, km = oracle_stores(inp["k"], pages, "k")
+    vs, vm = oracle_stores(inp["v"], pages, "v")
     q = zc.bf16_to_float(inp["q"])
     g = w.group_size
     for b, t in enumerate(LENS):
-        kf = [zc.bf16_to_float(zc.row_tokens(ks[b, h], km[b, h], inp["k"][b, h], t)) for h in range(w.n_kv_heads)]
-        vf = [zc.bf16_to_float(zc.row_tokens(vs[b, h], vm[b, h], inp["v"][b, h], t)) for h in range(w.n_kv_heads)]
+        kf = [zc.bf16_to_float(zc.row_tokens(ks[b, h], km[b, h], inp["k"][b, h], t, "k"))
+              for h in range(w.n_kv_heads)]
+        vf = [zc.bf16_to_float(zc.row_tokens(vs[b, h], vm[b, h], inp["v"][b, h], t, "v"))
+              for h in range(w.n_kv_heads)]
         for s, (lo, hi) in enumerate(zc.section_bounds(t, n_splits)):
             for h in range(w.n_q_heads):
                 ro, rl = attention.softmax_attend(q[b, h], kf[h // g][lo:hi], vf[h // g][lo:hi], w.scale)

@@ -92,15 +92,18 @@ def test_one_add_decodes_four_values():
             assert first == h1 * 0x01010101 and fifth == h5 * 0x01010101
 
 
-def test_stream_pages_round_trip_and_metadata():
+@pytest.mark.parametrize("role", ["k", "v"])
+def test_stream_pages_round_trip_and_metadata(role):
     rng = np.random.default_rng(3)
     t, n_pages = 70, 4                      # the tail beyond 4 full pages is not compressed
     # magnitudes in [1, 4): two exponents, so every chunk compresses
     f = (rng.uniform(1.0, 4.0, (t, 128)) * rng.choice([-1.0, 1.0], (t, 128))).astype(np.float32)
     x = (f.view(np.uint32) >> 16).astype(np.uint16)
-    x[20, 5] = bf16(0, 200, 0)              # makes chunk 1 of page 1 incompressible
-    store, meta = zc.compress_stream(x, n_pages)
-    assert np.array_equal(zc.decompress_stream(store, meta, n_pages), x[:64])
+    # makes chunk 1 of page 1 incompressible: keys' chunk 1 holds tokens 4-7 (token 20 is
+    # page 1's token 4); values' chunk 1 holds coordinates 32-63
+    x[20, 40] = bf16(0, 200, 0)
+    store, meta = zc.compress_stream(x, n_pages, role)
+    assert np.array_equal(zc.decompress_stream(store, meta, n_pages, role), x[:64])
     assert meta[1, 5] == zc.RAW
     for p in range(n_pages):
         assert int(np.frombuffer(meta[p, :4].tobytes(), "<u4")[0]) == p * zc.SLOT
@@ -115,21 +118,22 @@ def bf16_stream(rng, t):
     return (f.view(np.uint32) >> 16).astype(np.uint16)
 
 
+@pytest.mark.parametrize("role", ["k", "v"])
 @pytest.mark.parametrize("t", [0, 5, 16, 70])
-def test_row_tokens_reads_pages_then_open_page(t):
+def test_row_tokens_reads_pages_then_open_page(t, role):
     rng = np.random.default_rng(4)
     x = bf16_stream(rng, max(t, 1))[:t]
     full = t // zc.PAGE
-    store, meta = zc.compress_stream(x, max(full, 1)) if full else (np.zeros((1, zc.SLOT), np.uint8),
-                                                                     np.zeros((1, 8), np.uint8))
+    store, meta = zc.compress_stream(x, max(full, 1), role) if full else (np.zeros((1, zc.SLOT), np.uint8),
+                                                                           np.zeros((1, 8), np.uint8))
     # an open-page buffer of 16 rows: token i at row i mod 16; other rows are stale
     tail = bf16_stream(rng, 16)
     for i in range(full * zc.PAGE, t):
         tail[i % 16] = x[i]
-    assert np.array_equal(zc.row_tokens(store, meta, tail, t), x)
+    assert np.array_equal(zc.row_tokens(store, meta, tail, t, role), x)
     # a whole BF16 cache serves as the tail too (t mod rows = t)
     cache = np.concatenate([x, bf16_stream(rng, 16)])
-    assert np.array_equal(zc.row_tokens(store, meta, cache, t), x)
+    assert np.array_equal(zc.row_tokens(store, meta, cache, t, role), x)
 
 
 def test_decode_from_pages_is_attention_on_the_original_values():
@@ -145,8 +149,8 @@ def test_decode_from_pages_is_attention_on_the_original_values():
     vs, vm = ks.copy(), km.copy()
     for b in range(bsz):
         for h in range(hkv):
-            ks[b, h], km[b, h] = zc.compress_stream(x_k[b, h], 3)
-            vs[b, h], vm[b, h] = zc.compress_stream(x_v[b, h], 3)
+            ks[b, h], km[b, h] = zc.compress_stream(x_k[b, h], 3, "k")
+            vs[b, h], vm[b, h] = zc.compress_stream(x_v[b, h], 3, "v")
     scale = 128 ** -0.5
     out, lse = zc.decode_from_pages(q, ks, km, vs, vm, x_k, x_v, lens, scale)
     qf = zc.bf16_to_float(q)
@@ -171,3 +175,20 @@ def test_sections_are_whole_pages_covering_the_row(t, s):
         assert lo <= hi == lo2
     assert all(lo % zc.PAGE == 0 or lo == t for lo, _ in b)
     assert max(hi - lo for lo, hi in b) <= math.ceil(math.ceil(t / s) / zc.PAGE) * zc.PAGE
+
+
+def test_chunk_orders_put_each_group_where_the_matrix_unit_needs_it():
+    # keys: a group is 8 consecutive coordinates of one token; values: 8 consecutive tokens
+    # of one coordinate; both orders are permutations of the page
+    page = np.arange(zc.PAGE * zc.HEAD_DIM).reshape(zc.PAGE, zc.HEAD_DIM)
+    kv = zc.page_values(page, "k").reshape(-1, 8)
+    vv = zc.page_values(page, "v").reshape(-1, 8)
+    t_k, d_k = np.divmod(kv, zc.HEAD_DIM)
+    t_v, d_v = np.divmod(vv, zc.HEAD_DIM)
+    assert (t_k == t_k[:, :1]).all() and (np.diff(d_k, axis=1) == 1).all()
+    assert (d_v == d_v[:, :1]).all() and (np.diff(t_v, axis=1) == 1).all()
+    # values: chunk c holds coordinates 32c .. 32c+31 of all 16 tokens
+    chunks = zc.page_values(page, "v").reshape(zc.CHUNKS, -1) % zc.HEAD_DIM
+    assert all(set(chunks[c]) == set(range(32 * c, 32 * c + 32)) for c in range(zc.CHUNKS))
+    for role in ("k", "v"):
+        assert np.array_equal(zc.page_from_values(zc.page_values(page, role), role), page)
