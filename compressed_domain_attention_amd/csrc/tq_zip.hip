@@ -162,38 +162,69 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 // x = hi + lo with hi, lo BF16 (round to nearest even): hi + lo carries 16 significant bits
 __device__ __forceinline__ float bf16_lo(float x) { return x - (float)(__bf16)x; }
 
+// The pair {v[l], v[l ^ 16]} (or l ^ 32) in some order, with the row (half) swaps of
+// gfx950: plain vector instructions, no round trip through the LDS crossbar.  Reductions
+// (max, sum) over the pair do not depend on the order.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_rows(float v) {  // max over lanes l, l^16, l^32, l^48
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_rows(float v) {  // sum over lanes l, l^16, l^32, l^48
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
+}
+
+// kept ? raw : coded, word by word (a bit select, no branch)
+__device__ __forceinline__ u32x4 pick(bool kept, u32x4 raw, u32x4 coded) {
+  const uint32_t m = kept ? 0xFFFFFFFFu : 0u;
+  return (raw & m) | (coded & ~m);
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read(const uint8_t* p) {
   return *(const T*)p;
 }
 
 // Attention of one (sequence, KV head, section, head slice of up to 8 heads) over its
-// tokens, on the matrix unit.  The section's pages go in pairs (32 tokens) to the waves
-// in turn; each wave streams its pairs through its own ring of D LDS stages with direct
-// global -> LDS copies of exactly the stored bytes (a stage: the pair's key pages, then its
-// value pages, each at 4 KB; the metadata of the stage D pairs ahead rides along), so the
-// copies in flight cost no registers.
+// tokens, on the matrix unit.  The section's pages go to the waves in turn; each wave
+// streams its pages through its own ring of D LDS stages (a stage: the page's keys, then
+// its values, 4 KB each) with direct global -> LDS copies of exactly the stored bytes, the
+// metadata of the page D stages ahead riding along, so the copies in flight cost no
+// registers and several pages per wave are in flight while one is computed.
 //
-// Per pair, with bf16 16x16x32 products:
+// Per page, with bf16 16x16x32 products:
 //   scores S[token][col] = K (16 tokens x 32 coordinates, a key group per lane) x Q (32 x 16)
-//     over 4 coordinate blocks, for two 16-token tiles.  Columns are (part, head): the query
-//     in BF16 as hi + lo, heads in columns 0-7 (hi) and 8-15 (lo); a lane exchange adds the
-//     two parts.  The tiles' rows are chosen so that each lane ends up holding exactly the 8
-//     tokens whose value group (8 tokens of one coordinate) the output product pairs it with:
-//     tile T row 4j + i is token 8(j&1) + 4T + i of page j>>1.
-//   output O[col][coord] += P (16 x 32 tokens) x V (32 x 16 coordinates) for 8 coordinate
-//     tiles, the weights as BF16 hi + lo in rows 0-7 and 8-15, straight from the lanes'
-//     score registers.
+//     over 4 coordinate blocks.  Columns are (part, head): the query in BF16 as hi + lo,
+//     heads in columns 0-7 (hi) and 8-15 (lo); a lane exchange adds the two parts.  Lane l
+//     ends up with tokens 4 (l >> 4) .. + 3 of the page for its column.
+//   output O[col][coord] += P (16 x 32) x V (32 x 16 coordinates) for 8 coordinate tiles:
+//     the weights as BF16 hi + lo in rows 0-7 and 8-15, straight from the lanes' score
+//     registers, in k slots 8 (l >> 4) .. + 3; slots + 4 .. + 7 carry zero weight.  The value
+//     operand of those 4 tokens is half a value group (8 tokens of one coordinate).
 // The softmax reference m is updated lazily (only when a score exceeds it by 8 in log2
 // units), so that weights stay in (0, 256]; each wave keeps its own m, sum and output,
 // merged across waves at the end.  Results are in the original domain.
 template <int NW, int D, int QT>
 __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArgs a) {
-  constexpr int STAGE = 4 * kZipSlot;  // key page A, key page B, value page A, value page B
-  constexpr int MSLOT = 256;           // one stage's metadata (32 bytes used)
+  constexpr int STAGE = 2 * kZipSlot;  // the page's keys, then its values
+  constexpr int MSLOT = 256;           // one stage's metadata (16 bytes used)
   constexpr int WAVE_LDS = D * STAGE + 2 * D * MSLOT;
-  constexpr int NDMA = 17;             // copies per stage: 4 pages x 4, and the metadata
-  static_assert(D >= 2 && D <= 4, "ring depth");
+  constexpr int NDMA = 9;              // copies per stage: 2 pages x 4, and the metadata
+  static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NW * WAVE_LDS];
   __shared__ float part_m[NW][8], part_l[NW][8];
 
@@ -211,8 +242,8 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
   const int C = (((T + a.n_splits - 1) / a.n_splits) + 15) & ~15;
   const int lo = min(T, split * C), hi = min(T, lo + C);
   const int pg_lo = lo >> 4, pg_hi = (hi + 15) >> 4;
-  const int npairs = lo < hi ? (pg_hi - pg_lo + 1) >> 1 : 0;  // an empty section (lo = hi = T) has none
-  const int n = npairs > wv ? (npairs - wv + NW - 1) / NW : 0;  // this wave's pairs
+  const int npages = lo < hi ? pg_hi - pg_lo : 0;  // an empty section (lo = hi = T) has none
+  const int n = npages > wv ? (npages - wv + NW - 1) / NW : 0;  // this wave's pages
 
   const size_t stream = (size_t)b * a.n_kv_heads + kv;
   const uint8_t* ks = a.k_store + stream * a.store_pages * kZipSlot;
@@ -224,17 +255,17 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
   // a start offset is trusted only as far as a whole page slot stays inside the stream
   const uint32_t lim = (uint32_t)max(a.store_pages - 1, 0) * (uint32_t)kZipSlot;
 
-  uint8_t* wlds = lds + wv * WAVE_LDS;                // this wave's ring, then its metadata slots
+  uint8_t* wlds = lds + wv * WAVE_LDS;  // this wave's ring, then its metadata slots
   uint8_t* mlds = wlds + D * STAGE;
   const uint32_t wlds_a = lds_addr(wlds), mlds_a = lds_addr(mlds);
 
-  auto first_page = [&](int s) { return pg_lo + 2 * (wv + NW * s); };
-  // metadata of stage s (its two pages, keys then values) into metadata slot s mod 2D;
+  auto page_of = [&](int s) { return pg_lo + wv + NW * s; };
+  // metadata of stage s (keys: start, flags; values: start, flags) into slot s mod 2D;
   // words of pages outside the store are copied from a valid dummy address
   auto meta_dma = [&](int s) {
-    const int p = first_page(s) + ((lane >> 1) & 1);
-    const uint8_t* m = (lane & 4) ? vm : km;
-    const void* src = (lane < 8 && p < full) ? (const void*)(m + (size_t)p * 8 + 4 * (lane & 1)) : (const void*)kt;
+    const int p = page_of(s);
+    const uint8_t* m = (lane & 2) ? vm : km;
+    const void* src = (lane < 4 && p < full) ? (const void*)(m + (size_t)p * 8 + 4 * (lane & 1)) : (const void*)kt;
     lds_dma_addr<4, false>(mlds_a + (s % (2 * D)) * MSLOT, src);
   };
   // one 4 KB page region of a stage: `bytes` from `src`; lanes past them copy the first
@@ -243,41 +274,31 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t o = 1024u * k + 16u * lane;
-      lds_dma_addr<16, true>(dst + 1024u * k, o < bytes ? src + o : src);
+      lds_dma<16, true>(dst + 1024u * k, src, o < bytes ? o : 0u);
     }
   };
   auto page_bytes = [&](uint32_t flags) {
-    uint32_t n = 0;
+    uint32_t nb = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) n += ((flags >> (8 * j)) & 0xFFu) == 0xFFu ? 1024u : 768u;
-    return n;
+    for (int j = 0; j < 4; ++j) nb += ((flags >> (8 * j)) & 0xFFu) == 0xFFu ? 1024u : 768u;
+    return nb;
   };
-  // stage s: the pair's pages (store pages compressed, the open page from the tail buffer,
-  // pages past the section not at all), then the metadata of stage s + D
+  // stage s: a stored page compressed, or the open page from the tail buffer; then the
+  // metadata of stage s + D
   auto issue = [&](int s) {
-    const int p0 = first_page(s);
-    const u32x4 mk = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT);
-    const u32x4 mv = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT + 16);
+    const int p = page_of(s);
+    const u32x4 m = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT);
     lds_wait();
     const uint32_t dst = wlds_a + (s % D) * STAGE;
-#pragma unroll
-    for (int P = 0; P < 2; ++P) {
-      const int p = p0 + P;
-      const uint32_t kst = __builtin_amdgcn_readfirstlane(P ? mk.z : mk.x);
-      const uint32_t kfl = __builtin_amdgcn_readfirstlane(P ? mk.w : mk.y);
-      const uint32_t vst = __builtin_amdgcn_readfirstlane(P ? mv.z : mv.x);
-      const uint32_t vfl = __builtin_amdgcn_readfirstlane(P ? mv.w : mv.y);
-      if (p < full) {
-        page_dma(dst + P * kZipSlot, ks + min(kst & ~15u, lim), page_bytes(kfl));
-        page_dma(dst + (2 + P) * kZipSlot, vs + min(vst & ~15u, lim), page_bytes(vfl));
-      } else if (p < pg_hi) {
-        const size_t row = (size_t)((16 * p) % a.tail_rows) * 256;
-        page_dma(dst + P * kZipSlot, kt + row, kZipSlot);
-        page_dma(dst + (2 + P) * kZipSlot, vt + row, kZipSlot);
-      } else {
-        page_dma(dst + P * kZipSlot, kt, 0);
-        page_dma(dst + (2 + P) * kZipSlot, vt, 0);
-      }
+    if (p < full) {
+      page_dma(dst, ks + min(__builtin_amdgcn_readfirstlane(m.x) & ~15u, lim),
+               page_bytes(__builtin_amdgcn_readfirstlane(m.y)));
+      page_dma(dst + kZipSlot, vs + min(__builtin_amdgcn_readfirstlane(m.z) & ~15u, lim),
+               page_bytes(__builtin_amdgcn_readfirstlane(m.w)));
+    } else {
+      const size_t row = (size_t)((16 * p) % a.tail_rows) * 256;
+      page_dma(dst, kt + row, kZipSlot);
+      page_dma(dst + kZipSlot, vt + row, kZipSlot);
     }
     meta_dma(s + D);
   };
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
   for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mref = -INFINITY, thr = -INFINITY, lsum = 0.f;
   const int col = lane & 15;
-  const int jr = lane >> 4;  // row group: score rows 4 jr .. 4 jr + 3, operand k = 8 jr ..
+  const int jr = lane >> 4;  // row group: score rows (tokens) 4 jr .. 4 jr + 3
 
   for (int s = 0; s < n; ++s) {
     const int younger = min(D - 1, n - 1 - s);
@@ -325,57 +346,85 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
     else if (younger == 2) vm_wait<2 * NDMA>();
     else if (younger == 1) vm_wait<NDMA>();
     else vm_wait<0>();
-    const int p0 = first_page(s);
-    const u32x4 mk = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT);
-    const u32x4 mv = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT + 16);
+    const int p = page_of(s);
+    const bool stored = p < full;
+    const int np = min(16, hi - 16 * p);  // the page's tokens in the section
+    const u32x4 m = lds_read<u32x4>(mlds + (s % (2 * D)) * MSLOT);
+    const uint32_t kflags = stored ? __builtin_amdgcn_readfirstlane(m.y) : kKept;
+    const uint32_t vflags = __builtin_amdgcn_readfirstlane(m.w);
     const uint8_t* sb = wlds + (s % D) * STAGE;
-    const int nA = min(16, hi - 16 * p0), nB = p0 + 1 < pg_hi ? min(16, hi - 16 * (p0 + 1)) : 0;
-    // page kinds: 0 stored, 1 open (BF16 tail rows), 2 absent
-    const int kA = p0 < full ? 0 : 1, kB = p0 + 1 < full ? 0 : (p0 + 1 < pg_hi ? 1 : 2);
 
-    // ---- scores: two 16-token tiles
-    f32x4 sc[2];
+    // ---- operand reads, all issued before any use (branch-free: a kept key group is one
+    // 16-byte word, a coded one 8 low bytes and a code word; both are read, the mode picks)
+    u32x4 kraw[4];
+    uint32_t kcode[4], kmode;
     {
-      const int r = col, j = r >> 2, i = r & 3, P = j >> 1;
-      const int kind = P ? kB : kA;
-      const uint32_t flags = kind == 0 ? (P ? mk.w : mk.y) : kKept;
+      const int i = col & 3;  // key operand row = token col: chunk col >> 2, row i in it
+      uint32_t off;
+      chunk_at(kflags, col >> 2, off, kmode);
+      const bool kept = kmode == kKept;
+      const uint8_t* cw = sb + off + (kept ? 256 * i : 128 * i);
+      const uint8_t* cc = sb + off + 512 + 64 * i;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t off, mode;
-        chunk_at(flags, 2 * (j & 1) + t, off, mode);
-        const uint8_t* cb = sb + P * kZipSlot + off;
-        f32x4 acc_s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int g = 4 * kb + jr;  // group of the token: coordinates 8g .. 8g + 7
-          u32x4 kop;
-          if (mode == kKept) kop = lds_read<u32x4>(cb + 256 * i + 16 * g);
-          else kop = decode_group(lds_read<u32x2>(cb + 128 * i + 8 * g), lds_read<uint32_t>(cb + 512 + 64 * i + 4 * g), mode);
-          acc_s = mfma_bf16(kop, qf[kb], acc_s);
-        }
-        sc[t] = acc_s;
+      for (int kb = 0; kb < 4; ++kb) {
+        const int g = 4 * kb + jr;  // group of the token: coordinates 8g .. 8g + 7
+        kraw[kb] = lds_read<u32x4>(cw + (kept ? 16 * g : 8 * g));
+        kcode[kb] = lds_read<uint32_t>(cc + 4 * g);
       }
     }
-    // hi + lo parts, scale, mask; this lane's rows: tile t row 4 jr + e = token
-    // 8 (jr & 1) + 4 t + e of page jr >> 1
-    float x[2][4];
-    float bm = -INFINITY;
-    {
-      const int np = (jr >> 1) ? nB : nA;
+    // value operand of coordinate 16 ct + col, tokens 4 jr .. + 3: half (jr & 1) of group
+    // (coordinate, tokens 8 (jr >> 1) .. + 7)
+    u32x2 vraw[8];
+    uint32_t vcode[8], vmode[8];
+    const int half = jr & 1;
+    if (stored) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int ct = 0; ct < 8; ++ct) {
+        uint32_t off, mode;
+        chunk_at(vflags, ct >> 1, off, mode);
+        const int g = 2 * (16 * (ct & 1) + col) + (jr >> 1);
+        vmode[ct] = mode;
+        vraw[ct] = mode == kKept ? lds_read<u32x2>(sb + kZipSlot + off + 16 * g + 8 * half)
+                                 : u32x2{lds_read<uint32_t>(sb + kZipSlot + off + 8 * g + 4 * half), 0u};
+        vcode[ct] = lds_read<uint32_t>(sb + kZipSlot + off + 512 + 4 * g);
+      }
+    } else {
+      // the open page, token-major BF16; tokens past the row are zeros
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const int d = 16 * ct + col;
+        uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = (sc[t][e] + dpp<0x128>(sc[t][e])) * a.scale_log2;
-          x[t][e] = 8 * (jr & 1) + 4 * t + e < np ? v : -INFINITY;
-          bm = fmaxf(bm, x[t][e]);
+          const int t = 4 * jr + e;
+          w[e] = t < np ? (uint32_t)lds_read<uint16_t>(sb + kZipSlot + 256 * t + 2 * d) : 0u;
         }
+        vmode[ct] = kKept;
+        vraw[ct] = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        vcode[ct] = 0u;
+      }
     }
-    bm = fmaxf(bm, lane_xor(bm, 16, lane));
-    bm = fmaxf(bm, lane_xor(bm, 32, lane));
-    if (__builtin_amdgcn_ballot_w64(bm > thr)) {
+
+    // ---- scores of the page's 16 tokens
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 dec = decode_group(u32x2{kraw[kb].x, kraw[kb].y}, kcode[kb], kmode);
+      sc = mfma_bf16(pick(kmode == kKept, kraw[kb], dec), qf[kb], sc);
+    }
+    // hi + lo parts, scale, mask; this lane's rows are tokens 4 jr + e
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = (sc[e] + dpp<0x128>(sc[e])) * a.scale_log2;
+      x[e] = 4 * jr + e < np ? v : -INFINITY;
+      bm = fmaxf(bm, x[e]);
+    }
+    bm = max_rows(bm);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bm > thr) != 0, 0)) {
       const float mnew = fmaxf(mref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 on the first block
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 on the first page
       lsum *= alpha;
       // output rows 4 jr + e are (part, head) (4 jr + e) & 7: that head's factor
 #pragma unroll
@@ -387,54 +436,32 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
       mref = mnew;
       thr = mnew + kRescale;
     }
-    // weights: BF16 hi (columns 0-7) or lo (8-15) parts, in the operand's k order
+    // weights: BF16 hi (columns 0-7) or lo (8-15) parts in k slots 8 jr .. + 3
     u32x4 pf;
     {
-      float p[2][4];
+      float pw[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[t][e] = __builtin_amdgcn_exp2f(x[t][e] - mref);
-          lsum += p[t][e];
-          if (col >= 8) p[t][e] = bf16_lo(p[t][e]);
-        }
-      pf = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
-                 pack_bf16(p[1][2], p[1][3])};
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = __builtin_amdgcn_exp2f(x[e] - mref);
+        lsum += pw[e];
+        if (col >= 8) pw[e] = bf16_lo(pw[e]);
+      }
+      pf = u32x4{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]), 0u, 0u};
     }
 
-    // ---- output: 8 coordinate tiles; lane holds coordinate 16 ct + col, tokens
-    // 8 (jr & 1) .. + 7 of page jr >> 1 (a value group)
-    {
-      const int P = jr >> 1, hh = jr & 1;
-      const int kind = P ? kB : kA;
-      const int np = P ? nB : nA;
-      const uint32_t flags = P ? mv.w : mv.y;
-      const uint8_t* pb = sb + (2 + P) * kZipSlot;
+    // ---- output: 8 coordinate tiles
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const int d = 16 * ct + col;
-        u32x4 vop;
-        if (kind == 0) {
-          uint32_t off, mode;
-          chunk_at(flags, ct >> 1, off, mode);
-          const int g = 2 * (d & 31) + hh;
-          if (mode == kKept) vop = lds_read<u32x4>(pb + off + 16 * g);
-          else vop = decode_group(lds_read<u32x2>(pb + off + 8 * g), lds_read<uint32_t>(pb + off + 512 + 4 * g), mode);
-        } else if (kind == 1) {
-          // the open page, token-major BF16: gather the group, zero tokens past the row
-          uint32_t w[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = 8 * hh + e;
-            w[e] = t < np ? (uint32_t)lds_read<uint16_t>(pb + 256 * t + 2 * d) : 0u;
-          }
-          vop = u32x4{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
-        } else {
-          vop = u32x4{0u, 0u, 0u, 0u};
-        }
-        acc[ct] = mfma_bf16(pf, vop, acc[ct]);
-      }
+    for (int ct = 0; ct < 8; ++ct) {
+      // coded: the half's 4 high bytes (values 1-4 or 5-8 of the group: the signs in bit 7
+      // or 6, the offsets in bits 0-2 or 3-5) plus b/2, paired byte by byte with its low
+      // word; kept: the two raw words, passed through by the same permutes
+      const bool kept = vmode[ct] == kKept;
+      const uint32_t c = vcode[ct];
+      const uint32_t hb = (((c >> (3 * half)) & 0x07070707u) | ((c << half) & 0x80808080u)) + vmode[ct];
+      const uint32_t H = kept ? vraw[ct].y : hb;
+      const uint32_t w0 = __builtin_amdgcn_perm(H, vraw[ct].x, kept ? 0x03020100u : 0x05010400u);
+      const uint32_t w1 = __builtin_amdgcn_perm(H, vraw[ct].x, kept ? 0x07060504u : 0x07030602u);
+      acc[ct] = mfma_bf16(pf, u32x4{w0, w1, 0u, 0u}, acc[ct]);
     }
     // the stage's slot is refilled with stage s + D once its reads are done
     if (s + D < n) {
@@ -445,16 +472,16 @@ __global__ __launch_bounds__(64 * NW) void zip_attention_kernel(const ZipAttnArg
 
   // ---- merge the waves: sums over the row groups, hi + lo output rows
   vm_wait<0>();
-  lsum += lane_xor(lsum, 16, lane);
-  lsum += lane_xor(lsum, 32, lane);
+  lsum = sum_rows(lsum);
   __syncthreads();  // every wave is done with its ring
   float* po = (float*)wlds;  // this wave's output partial [8][128]
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float o = acc[ct][e] + lane_xor(acc[ct][e], 32, lane);
-      if (jr < 2) po[(4 * jr + e) * kHeadDim + 16 * ct + col] = o;
+      float o0, o1;
+      pair32(acc[ct][e], o0, o1);
+      if (jr < 2) po[(4 * jr + e) * kHeadDim + 16 * ct + col] = o0 + o1;
     }
   if (lane < 8) {
     part_m[wv][lane] = mref;
@@ -496,7 +523,7 @@ hipError_t launch_zip_compress(const ZipCompressArgs& a, int batch, int n_pages,
 }
 
 hipError_t launch_zip_attention(const ZipAttnArgs& a, int q_type, hipStream_t stream) {
-  constexpr int NW = 4, D = 2;
+  constexpr int NW = 8, D = 2;
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
   if (a.heads_per_slice > 8) return hipErrorInvalidValue;
   if (q_type == 0) hipLaunchKernelGGL((zip_attention_kernel<NW, D, 0>), grid, block, 0, stream, a);

@@ -56,7 +56,7 @@ WORKLOADS = {
     # 8192-token prompt in compressed pages plus 8 generated tokens in the open page; the
     # bits, group and so4 fields do not apply to the lossless codec
     "zipfusion8k": Workload("zipfusion8k", 32, 32, 8, 8200, 16, 16, 128, False, "bfloat16", "seeded4x8",
-                            n_splits=4, codec="zip"),
+                            n_splits=1, codec="zip"),
 }
 
 
