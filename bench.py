@@ -711,12 +711,17 @@ def counter_run(w, inp, n_splits, schedule, launches=24):
     log("counter run: 3 copies of %d bytes, %d decode launches over %d replicas" % (COPY_BYTES, launches, reps))
 
 
+CALIBRATION_KERNEL = "(anonymous namespace)::copy_kernel("  # the probe library's copy, not torch's
+
+
 def _per_dispatch(csv_path, counter, name_part):
     import csv
     import collections
     per = collections.defaultdict(float)
     for r in csv.DictReader(open(csv_path)):
-        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+        name = r["Kernel_Name"]
+        hit = name.startswith(name_part) if name_part == CALIBRATION_KERNEL else name_part in name
+        if r["Counter_Name"] == counter and hit:
             per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
     return [per[d] for d in sorted(per)]
 
@@ -724,7 +729,7 @@ def _per_dispatch(csv_path, counter, name_part):
 def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for the
     calibration copy of known size, and store HBM bytes per decode launch."""
-    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy_kernel"), _per_dispatch(write_csv, "WRITE_SIZE", "copy_kernel")
+    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", CALIBRATION_KERNEL), _per_dispatch(write_csv, "WRITE_SIZE", CALIBRATION_KERNEL)
     fd = _per_dispatch(fetch_csv, "FETCH_SIZE", "decode_")
     wd = _per_dispatch(write_csv, "WRITE_SIZE", "decode_")
     if not (fc and wc and fd and wd):
@@ -751,7 +756,7 @@ def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
 
 def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
     """As write_traffic, for the codec's attention kernel (profiles/zip_traffic.json)."""
-    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy_kernel"), _per_dispatch(write_csv, "WRITE_SIZE", "copy_kernel")
+    fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", CALIBRATION_KERNEL), _per_dispatch(write_csv, "WRITE_SIZE", CALIBRATION_KERNEL)
     fd = _per_dispatch(fetch_csv, "FETCH_SIZE", "zip_attention")
     wd = _per_dispatch(write_csv, "WRITE_SIZE", "zip_attention")
     if not (fc and wc and fd and wd):
@@ -820,12 +825,12 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.counter_run:
-        counter_run(w, inp, n_splits, args.schedule)
+        if w.codec == "zip":
+            zip_counter_run(w, inp, n_splits)
+        else:
+            counter_run(w, inp, n_splits, args.schedule)
         return
     if w.codec == "zip":
-        if args.counter_run:
-            zip_counter_run(w, inp, n_splits)
-            return
         r = run_zip(w, inp, args.steps, args.warmup, n_splits, check=not args.no_check)
         units = w.batch * w.n_kv_heads * w.seq_len
         achieved = r["algo_bytes"] / (r["attn_ms"] / 1e3) / 1e9
@@ -843,7 +848,8 @@ def main():
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                        "seq_len": w.seq_len, "codec": "lossless BF16 exponent codec (16-token pages)",
                        "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
-                       "step": "attention from the compressed pages + open page, then merge",
+                       "step": "attention from the compressed pages + open page" +
+                               (", then merge" if n_splits > 1 else " (one section per row: no merge)"),
                        "store_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": zip_measured_traffic(w.name, n_splits),
