@@ -694,14 +694,20 @@ struct Block {
 // group norms below 8188.
 constexpr float kRescaleLog2 = 3.0f;
 
-// Maximum / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+// Maximum / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), with the gfx950
+// row swaps: each returns the pair {x[l], x[l ^ 16]} (or ^ 32) as two values, and max and
+// + do not depend on their order, so the result equals the exchange form bit for bit.
 __device__ __forceinline__ float rows_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float rows_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <typename T>

@@ -1,0 +1,186 @@
+"""Block-GTQ: RoPE-block bit allocation for the keys of a TurboQuant-MSE cache (oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (aitrends.kr): the overview
+(RoPE splits the head dimension into 2-D frequency blocks; the query-key logit is exactly a
+sum of per-block dot products), the block energy score, the greedy integer allocation, the
+grouping into one TQ-MSE encoder per bit width, and the packed-cache paragraph (nibble
+containers; the main benchmark evaluates keys only, values kept in fp16).
+
+* Energy of block i of KV head h: s_i = 1/2 (E_{t, g in G(h)} ||q_g,t^(i)||^2 +
+  E_t ||k_h,t^(i)||^2), over a short calibration prefix; G(h) = the query heads reading h.
+* Objective J(b) = sum_i s_i 4^(-b_i) (TurboQuant-MSE's rate law: error ~ 4^-b), subject to
+  b_min <= b_i <= b_max and sum_i b_i = B.  Adding a bit to block i lowers J by
+  Delta_i = (3/4) s_i 4^(-b_i); the greedy rule starts every block at b_min and gives the
+  remaining B - L b_min bits one at a time to the block with the largest Delta_i.
+* Blocks with the same width form one group, encoded by one TQ-MSE encoder (norm ->
+  normalise -> rotate -> per-coordinate Lloyd-Max search at that width).
+
+Readings (the pages leave these open): block i is coordinates (2i, 2i+1) (RoPE's 2-D
+pairs); greedy ties go to the lowest block index; widths run from 1 to 4 bits (nibble
+containers); a group's coordinates are its blocks' pairs in block order; its rotation is
+the orthogonal factor Q (with positive diagonal of R) of the leading n x n part of a
+Gaussian matrix drawn per (KV head, width), n = the group's dimension -- a uniformly random
+rotation, as the TurboQuant-MSE encoder assumes; the codebook is the Lloyd-Max quantiser
+for a rotated unit vector's coordinate in n dimensions; a token's key record holds one
+4-bit code per coordinate in group order (widths ascending, then the group's rotated
+coordinate order), even coordinates in the low nibble, and one fp32 norm per group.
+"""
+
+import heapq
+import math
+
+import numpy as np
+
+from . import codebook
+
+HEAD_DIM = 128
+BLOCKS = HEAD_DIM // 2
+
+
+def block_energies(q_cal, k_cal):
+    """q_cal [N, Hq, 128], k_cal [N, Hkv, 128] -> s [Hkv, 64] (fp64)."""
+    q = np.asarray(q_cal, dtype=np.float64)
+    k = np.asarray(k_cal, dtype=np.float64)
+    hq, hkv = q.shape[1], k.shape[1]
+    g = hq // hkv
+    qb = (q.reshape(q.shape[0], hq, BLOCKS, 2) ** 2).sum(-1)  # ||q^(i)||^2 per token, head
+    kb = (k.reshape(k.shape[0], hkv, BLOCKS, 2) ** 2).sum(-1)
+    s = np.zeros((hkv, BLOCKS))
+    for h in range(hkv):
+        s[h] = 0.5 * (qb[:, h * g:(h + 1) * g].mean(axis=(0, 1)) + kb[:, h].mean(axis=0))
+    return s
+
+
+def objective(s, b):
+    return float(np.sum(np.asarray(s, np.float64) * 4.0 ** (-np.asarray(b, np.float64))))
+
+
+def allocate(s, budget, b_min, b_max):
+    """Greedy integer allocation: every block at b_min, then one bit at a time to the block
+    with the largest marginal gain (3/4) s_i 4^-b_i among those below b_max."""
+    s = np.asarray(s, dtype=np.float64)
+    L = len(s)
+    if not (L * b_min <= budget <= L * b_max):
+        raise ValueError("budget outside [L b_min, L b_max]")
+    b = np.full(L, b_min, dtype=np.int64)
+    # a max-heap on the gain, ties to the lowest block index
+    heap = [(-0.75 * s[i] * 4.0 ** (-b_min), i) for i in range(L) if b_min < b_max]
+    heapq.heapify(heap)
+    for _ in range(budget - L * b_min):
+        _, i = heapq.heappop(heap)
+        b[i] += 1
+        if b[i] < b_max:
+            heapq.heappush(heap, (-0.75 * s[i] * 4.0 ** (-float(b[i])), i))
+    return b
+
+
+def groups(b, b_min=1, b_max=4):
+    """The groups of a head's allocation: [(width, coordinates)] for every width present,
+    widths ascending, coordinates = the blocks' pairs in block order."""
+    out = []
+    for w in range(b_min, b_max + 1):
+        blocks = [i for i in range(len(b)) if b[i] == w]
+        if blocks:
+            out.append((w, np.array([c for i in blocks for c in (2 * i, 2 * i + 1)], dtype=np.int64)))
+    return out
+
+
+def rotation(gauss, n):
+    """The orthogonal factor of the leading n x n part of a Gaussian matrix (QR with the
+    diagonal of R made positive, which makes the factor unique)."""
+    a = np.asarray(gauss, dtype=np.float64)[:n, :n]
+    qm, r = np.linalg.qr(a)
+    return qm * np.sign(np.diag(r))[None, :]
+
+
+def head_encoders(b, gauss_by_width):
+    """[(width, coordinates, rotation R (y = R^T-free form: y = R.T @ x? no: y = Q^T x), centroids,
+    boundaries)] for one KV head.  The rotation applied to a group vector u is y = Q^T u."""
+    enc = []
+    for w, coords in groups(b):
+        n = len(coords)
+        qm = rotation(gauss_by_width[w - 1], n)
+        c, m = codebook.lloyd_max(w, n)
+        enc.append((w, coords, qm, c, m))
+    return enc
+
+
+def quantize_keys(x, enc):
+    """x [T, 128] -> (codes [T, 128] in group order, norms [T, groups], y [T, 128] the
+    rotated unit coordinates in group order, for boundary distances)."""
+    x = np.asarray(x, dtype=np.float64)
+    t = x.shape[0]
+    codes = np.zeros((t, HEAD_DIM), dtype=np.uint8)
+    norms = np.zeros((t, len(enc)))
+    ys = np.zeros((t, HEAD_DIM))
+    pos = 0
+    for gi, (w, coords, qm, c, m) in enumerate(enc):
+        n = len(coords)
+        xg = x[:, coords]
+        nu = np.sqrt(np.sum(xg * xg, axis=1))
+        u = np.where(nu[:, None] > 0, xg / np.where(nu > 0, nu, 1.0)[:, None], 0.0)
+        y = u @ qm  # y = Q^T u for every token (rows)
+        codes[:, pos:pos + n] = np.sum(y[:, :, None] > m[None, None, :], axis=2)  # compare-count
+        norms[:, gi] = nu
+        ys[:, pos:pos + n] = y
+        pos += n
+    return codes, norms, ys
+
+
+def dequantize_keys(codes, norms, enc):
+    """Inverse: [T, 128] in the original coordinate order."""
+    codes = np.asarray(codes)
+    t = codes.shape[0]
+    out = np.zeros((t, HEAD_DIM))
+    pos = 0
+    for gi, (w, coords, qm, c, m) in enumerate(enc):
+        n = len(coords)
+        y = c[codes[:, pos:pos + n].astype(np.int64)]
+        out[:, coords] = (y @ qm.T) * norms[:, gi:gi + 1]  # x = nu Q y
+        pos += n
+    return out
+
+
+def pack_codes(codes):
+    """[T, 128] codes (< 16) -> [T, 64] bytes: code j in byte j // 2, low nibble for even j."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] & 0xF) | ((codes[:, 1::2] & 0xF) << 4)
+
+
+def unpack_codes(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.zeros((p.shape[0], HEAD_DIM), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def key_record_bytes(n_groups):
+    """Stored bytes of one (token, KV head) key: 64 code bytes + one fp32 norm per group."""
+    return HEAD_DIM // 2 + 4 * n_groups
+
+
+def rate_law_gain(s, b, i):
+    """J(b) - J(b + e_i), the closed form (3/4) s_i 4^-b_i."""
+    return 0.75 * float(s[i]) * 4.0 ** (-float(b[i]))
+
+
+def decode(q, keys_dequantized, v, seq_lens, scale):
+    """Attention of q[B, Hq, 128] over dequantised keys and unquantised values."""
+    from . import attention
+    return attention.decode(q, keys_dequantized, v, seq_lens, scale)
+
+
+def brute_force_min(s, budget, b_min, b_max):
+    """Minimum of J over every integer allocation (tiny L only)."""
+    L = len(s)
+    best, arg = math.inf, None
+    for b in np.ndindex(*([b_max - b_min + 1] * L)):
+        bb = np.array(b) + b_min
+        if bb.sum() == budget:
+            j = objective(s, bb)
+            if j < best:
+                best, arg = j, bb
+    return best, arg
