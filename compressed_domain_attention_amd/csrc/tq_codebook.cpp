@@ -8,7 +8,9 @@
 //
 // Cell masses use composite Gauss-Legendre quadrature (16 nodes per panel); the first
 // moment has the closed form  int t (1-t^2)^mu dt = -(1-t^2)^(mu+1) / (2(mu+1)),  so a
-// centroid is that difference over the mass.  The normalising constant cancels.
+// centroid is that difference over the mass.  The normalising constant cancels.  In two
+// dimensions (mu = -1/2, the arcsine law, singular at the ends) the mass is also closed
+// form: asin(hi) - asin(lo).
 #include <cmath>
 #include <cstring>
 
@@ -80,19 +82,21 @@ static float f16_scale(const float* centroid, int n) {
 
 extern "C" tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* out) {
   if (out == nullptr) return TQ_EINVAL;
-  if ((bits != 3 && bits != 4) || dim < 3) return TQ_EUNSUPPORTED;
+  if (bits < 1 || bits > 4 || dim < 2) return TQ_EUNSUPPORTED;
   const int n = 1 << bits;
   const double mu = 0.5 * (dim - 3);
-  // the law has standard deviation 1/sqrt(dim): start from levels spread over +-2 sd
+  // the law has standard deviation 1/sqrt(dim): start from levels spread over +-2 sd, kept
+  // inside (-1, 1) for the smallest dimensions
   double c[16], e[17];
-  for (int k = 0; k < n; ++k) c[k] = (-2.0 + 4.0 * k / (n - 1)) / std::sqrt((double)dim);
+  for (int k = 0; k < n; ++k)
+    c[k] = dim < 4 ? -0.9 + 1.8 * k / (n - 1) : (-2.0 + 4.0 * k / (n - 1)) / std::sqrt((double)dim);
   for (int it = 0; it < 20000; ++it) {
     e[0] = -1.0;
     e[n] = 1.0;
     for (int k = 1; k < n; ++k) e[k] = 0.5 * (c[k - 1] + c[k]);
     double delta = 0.0;
     for (int k = 0; k < n; ++k) {
-      const double m0 = mass(e[k], e[k + 1], mu, 64);
+      const double m0 = dim == 2 ? std::asin(e[k + 1]) - std::asin(e[k]) : mass(e[k], e[k + 1], mu, 64);
       const double nc = m0 > 0.0 ? first_moment(e[k], e[k + 1], mu) / m0 : 0.5 * (e[k] + e[k + 1]);
       delta = std::fmax(delta, std::fabs(nc - c[k]));
       c[k] = nc;

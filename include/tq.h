@@ -80,14 +80,17 @@ const char* tq_status_string(tq_status s);
  * ("TurboQuant ...", 2.2: density f(t) ~ (1 - t^2)^((dim-3)/2) on [-1, 1];
  *  2.3: centroid = conditional mean of its cell, boundary = midpoint, iterate.)
  * Computed on the host in double precision (Gauss-Legendre quadrature of the cell
- * masses, closed-form first moments) and stored rounded to float.
+ * masses, closed-form first moments; in two dimensions, the arcsine law, closed-form
+ * masses too) and stored rounded to float.
  * centroid[0 .. 2^bits-1] ascending; boundary[k] = (centroid[k] + centroid[k+1]) / 2 for
  * k < 2^bits - 1; unused entries are 0.  f16_scale is the s in [1, 2) (searched on a 2^-16
  * grid) at which every s * centroid[k] is nearest to an fp16 number in relative terms
  * (worst level: 2.6e-5 for 3-bit, 9e-5 for 4-bit codebooks of the supported groups, against
  * up to 3.2e-4 at s = 1); the matrix-core decode holds the key codebook as fp16(s * c) and
  * divides the query by s.  Host-only; no device work.
- * Errors: TQ_EINVAL if out == NULL; TQ_EUNSUPPORTED unless bits is 3 or 4 and dim >= 3. */
+ * Errors: TQ_EINVAL if out == NULL; TQ_EUNSUPPORTED unless 1 <= bits <= 4 and dim >= 2
+ * (the packed caches take 3 or 4 bits; Block-GTQ key groups take 1 to 4 bits and any even
+ * dimension). */
 typedef struct {
   int32_t bits;
   int32_t dim;

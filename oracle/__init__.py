@@ -24,6 +24,10 @@ What it computes, and where the pages define it (page title, then section):
   Quantization", packed-cache implementation details), and the rotated-domain
   rewrite used as a self-check ("RotaryQuant ...", key design 3); attention over a row's
   quantised and unquantised token stores.
+* ``blockgtq``  -- Block-GTQ keys: RoPE-block energies, the greedy integer bit allocation,
+  one TQ-MSE encoder per width (rotation, codebook, compare-count), nibble records
+  ("RoPE-Aware Bit Allocation ...", overview, energy score, greedy allocation, grouping and
+  packed-cache paragraphs).
 * ``zipcodec``  -- the lossless BF16 exponent codec of the KV cache: chunk rule, 4-bit
   codes, page metadata and the decode by integer adds ("ZipFusion ...", compression format
   and register decode sections).
@@ -33,4 +37,4 @@ Parity pins for each function live in ``tests/test_oracle_*.py``; nothing here i
 "parity unpinned".
 """
 
-from . import codebook, rotation, quant, layout, attention, zipcodec  # noqa: F401
+from . import codebook, rotation, quant, layout, attention, zipcodec, blockgtq  # noqa: F401

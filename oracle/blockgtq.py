@@ -96,8 +96,8 @@ def rotation(gauss, n):
 
 
 def head_encoders(b, gauss_by_width):
-    """[(width, coordinates, rotation R (y = R^T-free form: y = R.T @ x? no: y = Q^T x), centroids,
-    boundaries)] for one KV head.  The rotation applied to a group vector u is y = Q^T u."""
+    """[(width, coordinates, Q, centroids, boundaries)] for one KV head's groups.  A group
+    vector u is rotated as y = Q^T u and restored as u = Q y."""
     enc = []
     for w, coords in groups(b):
         n = len(coords)

@@ -35,7 +35,11 @@ def _f(t, dim):
 
 
 def _cell_moments(lo, hi, dim):
-    """(mass, first moment) of the law on [lo, hi] by adaptive quadrature."""
+    """(mass, first moment) of the law on [lo, hi] by adaptive quadrature; in 2 dimensions
+    (the arcsine law 1 / (pi sqrt(1 - t^2)), singular at the ends) by its closed forms."""
+    if dim == 2:
+        return ((np.arcsin(hi) - np.arcsin(lo)) / np.pi,
+                (np.sqrt(max(0.0, 1.0 - lo * lo)) - np.sqrt(max(0.0, 1.0 - hi * hi))) / np.pi)
     m0 = integrate.quad(_f, lo, hi, args=(dim,), epsabs=1e-16, epsrel=1e-13, limit=200)[0]
     m1 = integrate.quad(lambda t: t * _f(t, dim), lo, hi, epsabs=1e-16, epsrel=1e-13, limit=200)[0]
     return m0, m1
@@ -43,11 +47,14 @@ def _cell_moments(lo, hi, dim):
 
 @lru_cache(maxsize=None)
 def _lloyd_max_cached(bits, dim):
-    if bits < 1 or dim < 3:
-        raise ValueError("bits >= 1 and dim >= 3 are required")
+    if bits < 1 or dim < 2:
+        raise ValueError("bits >= 1 and dim >= 2 are required")
     n = 2 ** bits
-    # start from evenly spaced levels over +-2 standard deviations (std = 1/sqrt(dim))
+    # start from evenly spaced levels over +-2 standard deviations (std = 1/sqrt(dim)),
+    # kept inside (-1, 1) for the smallest dimensions
     c = np.linspace(-2.0, 2.0, n) / np.sqrt(dim)
+    if dim < 4:
+        c = np.linspace(-0.9, 0.9, n)
     for _ in range(100000):
         m = 0.5 * (c[:-1] + c[1:])                     # boundary = midpoint (2.3)
         edges = np.concatenate([[-1.0], m, [1.0]])

@@ -66,8 +66,9 @@ def test_codebook_fp16_scale(lib, bits, dim):
 
 def test_codebook_errors(lib):
     cb = tq.Codebook()
-    assert lib.tq_make_codebook(2, 32, ctypes.byref(cb)) == TQ_EUNSUPPORTED
-    assert lib.tq_make_codebook(3, 2, ctypes.byref(cb)) == TQ_EUNSUPPORTED
+    assert lib.tq_make_codebook(0, 32, ctypes.byref(cb)) == TQ_EUNSUPPORTED
+    assert lib.tq_make_codebook(5, 32, ctypes.byref(cb)) == TQ_EUNSUPPORTED
+    assert lib.tq_make_codebook(3, 1, ctypes.byref(cb)) == TQ_EUNSUPPORTED
     assert lib.tq_make_codebook(3, 32, None) == TQ_EINVAL
     for s in range(5):
         assert lib.tq_status_string(s)
