@@ -17,6 +17,7 @@ __all__ = [
     "NativeLibraryMissing", "TQError", "Codebook", "make_codebook", "Rotation", "PackedCache",
     "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
     "zip_store", "zip_compress", "zip_attention",
+    "gtq_allocate", "GtqKeys", "gtq_quantize_keys", "gtq_attention",
     "TQ_KEYS", "TQ_VALUES",
 ]
 
@@ -60,6 +61,13 @@ class _Rotation(ctypes.Structure):
                 ("signs", ctypes.c_void_p), ("so4", ctypes.c_void_p)]
 
 
+class GtqHead(ctypes.Structure):
+    """tq_gtq_head: one KV head's Block-GTQ key encoder (layout in include/tq.h)."""
+    _fields_ = [("n_groups", ctypes.c_int32), ("width", ctypes.c_int32 * 4), ("start", ctypes.c_int32 * 4),
+                ("dim", ctypes.c_int32 * 4), ("rot_offset", ctypes.c_int32 * 4), ("coord", ctypes.c_int32 * 128),
+                ("centroid", (ctypes.c_float * 16) * 4), ("boundary", (ctypes.c_float * 15) * 4)]
+
+
 class _Cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32), ("bits", ctypes.c_int32),
@@ -70,7 +78,8 @@ _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
            "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
-           "tq_zip_compress", "tq_zip_attention")
+           "tq_zip_compress", "tq_zip_attention", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
+           "tq_gtq_attention")
 
 
 def library():
@@ -106,6 +115,14 @@ def library():
     lib.tq_zip_compress.restype = I
     lib.tq_zip_attention.argtypes = [P, P, P, P, I, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_zip_attention.restype = I
+    lib.tq_gtq_allocate.argtypes = [P, I, I, I, I, P]
+    lib.tq_gtq_allocate.restype = I
+    lib.tq_gtq_prepare.argtypes = [P, P, ctypes.POINTER(GtqHead), P]
+    lib.tq_gtq_prepare.restype = I
+    lib.tq_gtq_quantize_keys.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
+    lib.tq_gtq_quantize_keys.restype = I
+    lib.tq_gtq_attention.argtypes = [P, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
+    lib.tq_gtq_attention.restype = I
     _lib = lib
     return lib
 
@@ -386,4 +403,98 @@ def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=
         _ptr(k_store), _ptr(k_meta), _ptr(v_store), _ptr(v_meta), pages, _ptr(k_tail), _ptr(v_tail),
         k_tail.shape[2], bsz, hkv, _ptr(q), _ZIP_Q_DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits,
         _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_zip_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+GTQ_ROTATION_FLOATS = 16384
+
+
+def gtq_allocate(energies, budget: int, b_min: int = 1, b_max: int = 4):
+    """Block-GTQ greedy integer allocation (host, in the library) -> int32 bits per block."""
+    import numpy as np
+    e = np.ascontiguousarray(energies, dtype=np.float32)
+    bits = np.zeros(e.shape[0], dtype=np.int32)
+    _check(library().tq_gtq_allocate(e.ctypes.data, e.shape[0], budget, b_min, b_max, bits.ctypes.data),
+           "tq_gtq_allocate")
+    return bits
+
+
+class GtqKeys:
+    """Block-GTQ key encoders of every KV head (built on the host, held on the device).
+
+    block_bits: int [n_kv_heads, 64] widths in 1..4; gauss: float32 [n_kv_heads, 4, 128, 128]
+    (width w of head h uses gauss[h, w-1])."""
+
+    def __init__(self, block_bits, gauss, device="cuda"):
+        import numpy as np
+        bits = np.ascontiguousarray(block_bits, dtype=np.int32)
+        g = np.ascontiguousarray(gauss, dtype=np.float32)
+        hkv = bits.shape[0]
+        if bits.shape != (hkv, 64) or g.shape != (hkv, 4, 128, 128):
+            raise ValueError("block_bits [n_kv_heads, 64] and gauss [n_kv_heads, 4, 128, 128] are required")
+        self.heads_host = (GtqHead * hkv)()
+        rot = np.zeros((hkv, GTQ_ROTATION_FLOATS), dtype=np.float32)
+        for h in range(hkv):
+            _check(library().tq_gtq_prepare(bits[h].ctypes.data, g[h].ctypes.data, ctypes.byref(self.heads_host[h]),
+                                            rot[h].ctypes.data), "tq_gtq_prepare")
+        raw = np.frombuffer(bytes(self.heads_host), dtype=np.uint8).copy()
+        self.heads = torch.from_numpy(raw).to(device)
+        self.rotations = torch.from_numpy(rot).to(device)
+        self.n_kv_heads = hkv
+        self.block_bits = bits
+
+    def n_groups(self, h):
+        return self.heads_host[h].n_groups
+
+
+def gtq_quantize_keys(enc: GtqKeys, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, pos0: int = 0):
+    """Encode x [batch, n_kv_heads, n_new, 128] (fp16/fp32) into codes uint8 [batch,
+    n_kv_heads, capacity, 64] and norms fp32 [batch, n_kv_heads, capacity, 4] at pos0 .."""
+    if x.dtype not in _DTYPES or not x.is_contiguous() or x.dim() != 4 or x.shape[3] != HEAD_DIM:
+        raise ValueError("x must be contiguous [batch, n_kv_heads, n_new, 128] float16/float32")
+    bsz, hkv, n_new = x.shape[:3]
+    if hkv != enc.n_kv_heads:
+        raise ValueError("x has %d KV heads, the encoders %d" % (hkv, enc.n_kv_heads))
+    cap = codes.shape[2]
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (bsz, hkv, cap, 64) or not codes.is_contiguous()
+            or norms.dtype != torch.float32 or tuple(norms.shape) != (bsz, hkv, cap, 4) or not norms.is_contiguous()):
+        raise ValueError("codes uint8 [batch, n_kv_heads, capacity, 64] and norms float32 [.., capacity, 4]")
+    _check(library().tq_gtq_quantize_keys(_ptr(enc.heads), _ptr(enc.rotations), _ptr(x), _DTYPES[x.dtype], bsz, hkv,
+                                          n_new, pos0, cap, _ptr(codes), _ptr(norms), _stream()),
+           "tq_gtq_quantize_keys")
+    return codes, norms
+
+
+def gtq_attention(enc: GtqKeys, codes, norms, v, q, seq_lens=None, max_len=None, scale=None, n_splits=1, out=None,
+                  lse=None, part_o=None, part_lse=None):
+    """Decode attention over Block-GTQ keys and fp16 values v [batch, n_kv_heads, capacity,
+    128].  n_splits == 1 -> (out, lse); otherwise (part_o, part_lse) for merge_splits(None, ..)."""
+    if v.dtype != torch.float16 or not v.is_contiguous() or v.dim() != 4 or v.shape[3] != HEAD_DIM:
+        raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    hkv, cap = v.shape[1], v.shape[2]
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+            tuple(norms.shape) != (bsz, hkv, cap, 4):
+        raise ValueError("codes, norms and v must describe the same [batch, n_kv_heads, capacity] cache")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
+        raise ValueError("seq_lens must be int32 [batch]")
+    if max_len is None:
+        max_len = int(seq_lens.max().item()) if seq_lens is not None else cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_gtq_attention(
+        _ptr(enc.heads), _ptr(enc.rotations), _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(q),
+        _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse), _ptr(part_o),
+        _ptr(part_lse), _stream()), "tq_gtq_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)

@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_codebook.cpp", "tq_api.cpp", "tq_kernels.hip", "tq_zip.hip"]
+SOURCES = ["tq_codebook.cpp", "tq_api.cpp", "tq_gtq.cpp", "tq_kernels.hip", "tq_zip.hip", "tq_gtq.hip"]
 PROBE_LIB = os.path.join(HERE, "libtqprobe.so")   # bandwidth probe used by the benchmark
 PROBE_SOURCES = ["tq_probe.hip"]
 
@@ -50,7 +50,7 @@ def _compile(sources, lib, verbose):
     tag = ".tmp%d" % os.getpid()
     jobs = []
     for s in sources:
-        obj = os.path.join(HERE, "%s%s.o" % (os.path.splitext(s)[0], tag))
+        obj = os.path.join(HERE, "%s%s.o" % (s.replace(".", "_"), tag))
         cmd = [hipcc(), *_flags(), *SEPARATE.get(s, []), "-c", os.path.join(HERE, "csrc", s), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -341,3 +341,69 @@ extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_m
   a.scale_log2 = scale * 1.4426950408889634f;
   return from_hip(tq::launch_zip_attention(a, (int)q_dtype, (hipStream_t)stream));
 }
+
+extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x,
+                                          tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new,
+                                          int32_t pos0, int32_t capacity, uint8_t* codes, float* norms, void* stream) {
+  if (heads == nullptr || rotations == nullptr || x == nullptr || codes == nullptr || norms == nullptr)
+    return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch <= 0 || batch > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_new < 0 || pos0 < 0 || capacity <= 0)
+    return TQ_EINVAL;
+  if ((int64_t)pos0 + n_new > capacity) return TQ_ECAPACITY;
+  if (n_new == 0) return TQ_OK;
+  tq::GtqQuantArgs a;
+  a.heads = heads;
+  a.rotations = rotations;
+  a.x = x;
+  a.codes = codes;
+  a.norms = norms;
+  a.n_kv_heads = n_kv_heads;
+  a.n_new = n_new;
+  a.pos0 = pos0;
+  a.capacity = capacity;
+  return from_hip(tq::launch_gtq_quantize(a, x_dtype == TQ_F16, batch, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
+                                      const float* norms, const void* v, int32_t capacity, int32_t batch,
+                                      int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
+                                      const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
+                                      float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+  if (heads == nullptr || rotations == nullptr || codes == nullptr || norms == nullptr || v == nullptr || q == nullptr)
+    return TQ_EINVAL;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0 || capacity <= 0)
+    return TQ_EINVAL;
+  if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
+  if (max_len > capacity) return TQ_ECAPACITY;
+  const int group = n_q_heads / n_kv_heads;
+  const int hps = group < 8 ? group : 8;
+  const int slices = (group + hps - 1) / hps;
+  if ((int64_t)batch * n_kv_heads * n_splits * slices > 0x7FFFFFFFll) return TQ_EINVAL;
+  tq::GtqAttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.heads = heads;
+  a.rotations = rotations;
+  a.codes = codes;
+  a.norms = norms;
+  a.v = v;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.max_len = max_len;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group_size = group;
+  a.heads_per_slice = hps;
+  a.n_slices = slices;
+  a.n_splits = n_splits;
+  a.capacity = capacity;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
+}

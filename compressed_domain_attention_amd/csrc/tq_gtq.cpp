@@ -1,0 +1,89 @@
+// Host side of Block-GTQ keys ("RoPE-Aware Bit Allocation for KV-Cache Quantization"): the
+// greedy integer bit allocation and the per-head encoder (groups of equal width, their
+// uniformly random rotations and Lloyd-Max codebooks).
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "tq.h"
+
+extern "C" tq_status tq_gtq_allocate(const float* energies, int32_t n_blocks, int32_t budget, int32_t b_min,
+                                     int32_t b_max, int32_t* bits) {
+  if (energies == nullptr || bits == nullptr || n_blocks <= 0) return TQ_EINVAL;
+  if (b_min < 0 || b_max < b_min || b_max > 30) return TQ_EINVAL;
+  if ((int64_t)budget < (int64_t)n_blocks * b_min || (int64_t)budget > (int64_t)n_blocks * b_max) return TQ_EINVAL;
+  for (int i = 0; i < n_blocks; ++i)
+    if (!(energies[i] >= 0.f) || !std::isfinite(energies[i])) return TQ_EINVAL;
+  for (int i = 0; i < n_blocks; ++i) bits[i] = b_min;
+  // each extra bit to the block with the largest gain (3/4) s 4^-b; 4^-b is a power of two,
+  // so the gain is (0.75 s) rounded once, scaled exactly
+  for (int64_t r = (int64_t)budget - (int64_t)n_blocks * b_min; r > 0; --r) {
+    int best = -1;
+    double gain = -1.0;
+    for (int i = 0; i < n_blocks; ++i) {
+      if (bits[i] >= b_max) continue;
+      const double g = std::ldexp(0.75 * (double)energies[i], -2 * bits[i]);
+      if (g > gain) {
+        gain = g;
+        best = i;
+      }
+    }
+    bits[best] += 1;
+  }
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gauss, tq_gtq_head* head,
+                                    float* rotation) {
+  if (block_bits == nullptr || gauss == nullptr || head == nullptr || rotation == nullptr) return TQ_EINVAL;
+  for (int i = 0; i < TQ_GTQ_BLOCKS; ++i)
+    if (block_bits[i] < 1 || block_bits[i] > 4) return TQ_EINVAL;
+  std::memset(head, 0, sizeof(*head));
+  std::memset(rotation, 0, sizeof(float) * TQ_GTQ_ROTATION_FLOATS);
+  int pos = 0, off = 0, g = 0;
+  for (int w = 1; w <= 4; ++w) {
+    std::vector<int> coords;
+    for (int i = 0; i < TQ_GTQ_BLOCKS; ++i)
+      if (block_bits[i] == w) {
+        coords.push_back(2 * i);
+        coords.push_back(2 * i + 1);
+      }
+    if (coords.empty()) continue;
+    const int n = (int)coords.size();
+    head->width[g] = w;
+    head->start[g] = pos;
+    head->dim[g] = n;
+    head->rot_offset[g] = off;
+    for (int j = 0; j < n; ++j) head->coord[pos + j] = coords[j];
+    // columns of the leading n x n part, orthonormalised in order (modified Gram-Schmidt):
+    // the Q of the QR factorisation whose R has a positive diagonal
+    std::vector<double> q((size_t)n * n);
+    const float* a = gauss + (size_t)(w - 1) * 128 * 128;
+    for (int c = 0; c < n; ++c) {
+      std::vector<double> v(n);
+      for (int r = 0; r < n; ++r) v[r] = a[r * 128 + c];
+      for (int p = 0; p < c; ++p) {
+        double d = 0.0;
+        for (int r = 0; r < n; ++r) d += q[(size_t)r * n + p] * v[r];
+        for (int r = 0; r < n; ++r) v[r] -= d * q[(size_t)r * n + p];
+      }
+      double nrm = 0.0;
+      for (int r = 0; r < n; ++r) nrm += v[r] * v[r];
+      nrm = std::sqrt(nrm);
+      if (!(nrm > 0.0)) return TQ_EINVAL;
+      for (int r = 0; r < n; ++r) q[(size_t)r * n + c] = v[r] / nrm;
+    }
+    for (int i = 0; i < n * n; ++i) rotation[off + i] = (float)q[i];
+    tq_codebook cb;
+    const tq_status st = tq_make_codebook(w, n, &cb);
+    if (st != TQ_OK) return st;
+    for (int k = 0; k < 16; ++k) head->centroid[g][k] = cb.centroid[k];
+    for (int k = 0; k < 15; ++k) head->boundary[g][k] = cb.boundary[k];
+    pos += n;
+    off += n * n;
+    ++g;
+  }
+  head->n_groups = g;
+  for (int k = g; k < TQ_GTQ_MAX_GROUPS; ++k) head->start[k] = 128;
+  return TQ_OK;
+}

@@ -127,6 +127,43 @@ struct ZipAttnArgs {
   float scale_log2;
 };
 
+// Block-GTQ keys (heads: tq_gtq_head layout, declared in tq.h).
+struct GtqQuantArgs {
+  const void* heads;        // tq_gtq_head [n_kv_heads]
+  const float* rotations;   // [n_kv_heads][16384]
+  const void* x;            // [batch][n_kv_heads][n_new][128]
+  uint8_t* codes;           // [batch][n_kv_heads][capacity][64]
+  float* norms;             // [batch][n_kv_heads][capacity][4]
+  int32_t n_kv_heads;
+  int32_t n_new;
+  int32_t pos0;
+  int32_t capacity;
+};
+
+struct GtqAttnArgs {
+  const void* heads;
+  const float* rotations;
+  const uint8_t* codes;
+  const float* norms;
+  const void* v;            // fp16 [batch][n_kv_heads][capacity][128]
+  const void* q;
+  const int32_t* seq_lens;
+  float* out;
+  float* lse_out;
+  float* part_o;
+  float* part_lse;
+  int32_t max_len;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t group_size;
+  int32_t heads_per_slice;
+  int32_t n_slices;
+  int32_t n_splits;
+  int32_t capacity;
+  float scale_log2;
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
@@ -155,6 +192,8 @@ hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t
 hipError_t launch_zip_compress(const ZipCompressArgs& a, int batch, int n_pages, hipStream_t stream);
 // q_type: 0 fp32, 1 fp16, 2 bf16
 hipError_t launch_zip_attention(const ZipAttnArgs& a, int q_type, hipStream_t stream);
+hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream);
+hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 // Heads one workgroup of the matrix-core schedule can serve: the 16 MFMA columns hold

@@ -292,6 +292,87 @@ tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const 
                            int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
                            void* stream);
 
+/* ---- Block-GTQ keys ("RoPE-Aware Bit Allocation for KV-Cache Quantization": overview,
+ * block energy score, greedy allocation, grouping and packed-cache paragraphs).
+ *
+ * A head's 128 key coordinates form 64 RoPE blocks, block i = coordinates (2i, 2i+1).  Each
+ * block gets an integer width b_i in [b_min, b_max] (1 <= b_min <= b_max <= 4) with
+ * sum b_i = budget, greedily by the marginal gain (3/4) s_i 4^-b_i of the objective
+ * sum s_i 4^-b_i, s_i the block's energy.  Blocks of equal width form one group, encoded by
+ * one TQ-MSE encoder: the group's coordinates (its blocks' pairs in block order, n = 2 x
+ * blocks) -> norm -> normalise -> y = Q^T u with a uniformly random rotation Q -> codes
+ * by compare-count against the width's Lloyd-Max boundaries for n dimensions.  Values are
+ * kept in fp16, the configuration of the page's main benchmark (keys only).
+ *
+ * Key record of one (token, KV head): codes[64] bytes, one 4-bit code per position of the
+ * group order (groups by width ascending, each in its rotated coordinate order), position j
+ * in byte j/2, the low nibble for even j; norms[4] fp32, one per group (0 for absent
+ * groups). */
+#define TQ_GTQ_BLOCKS 64
+#define TQ_GTQ_MAX_GROUPS 4
+#define TQ_GTQ_ROTATION_FLOATS 16384 /* per head: every group's n x n rotation */
+
+/* Greedy integer allocation (host): bits[i] for n_blocks blocks with energies[i] >= 0.
+ * Every block starts at b_min; each of the budget - n_blocks*b_min remaining bits goes to
+ * the block below b_max with the largest (3/4) energies[i] 4^-bits[i] (in double; ties to
+ * the lowest index).  Errors: TQ_EINVAL for null pointers, n_blocks <= 0, negative or
+ * non-finite energies, b_min < 0, b_max < b_min, or a budget outside
+ * [n_blocks*b_min, n_blocks*b_max]. */
+tq_status tq_gtq_allocate(const float* energies, int32_t n_blocks, int32_t budget, int32_t b_min, int32_t b_max,
+                          int32_t* bits);
+
+/* One KV head's key encoder.  Plain data, copied to the device as an array per KV head. */
+typedef struct {
+  int32_t n_groups;                 /* 1 .. 4 */
+  int32_t width[TQ_GTQ_MAX_GROUPS]; /* bits of group g, ascending */
+  int32_t start[TQ_GTQ_MAX_GROUPS]; /* first group-order position of group g (128 if absent) */
+  int32_t dim[TQ_GTQ_MAX_GROUPS];   /* coordinates of group g (0 if absent) */
+  int32_t rot_offset[TQ_GTQ_MAX_GROUPS]; /* group g's rotation in the head's rotation array */
+  int32_t coord[128];               /* original coordinate of group-order position j */
+  float centroid[TQ_GTQ_MAX_GROUPS][16];
+  float boundary[TQ_GTQ_MAX_GROUPS][15];
+} tq_gtq_head;
+
+/* Builds one head's encoder on the host from its 64 block widths (1 .. 4) and a Gaussian
+ * matrix per width (gauss: float [4][128][128], width w uses gauss[w-1]).  Group g's
+ * rotation Q is the orthogonal factor, with positive diagonal of R, of the leading n x n
+ * part of its width's matrix (QR by Gram-Schmidt in double): a uniformly random rotation.
+ * rotation: float [16384] (host), group g's Q row-major at rot_offset[g] (Q[i][j] =
+ * rotation[rot_offset + i*n + j]; y_j = sum_i Q[i][j] u_i).  Codebooks are
+ * tq_make_codebook(width, n).  Errors: TQ_EINVAL for null pointers or widths outside 1..4. */
+tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gauss, tq_gtq_head* head, float* rotation);
+
+/* Encodes n_new keys per (sequence, KV head) into token positions pos0 .. pos0+n_new-1.
+ *   heads:     device tq_gtq_head [n_kv_heads]; rotations: device float [n_kv_heads][16384].
+ *   x:         device [batch][n_kv_heads][n_new][128] of x_dtype (TQ_F32 or TQ_F16).
+ *   codes:     device uint8 [batch][n_kv_heads][capacity][64]; norms: device float
+ *              [batch][n_kv_heads][capacity][4].
+ * Errors: TQ_EINVAL for null pointers, bad dtype or counts; TQ_ECAPACITY when
+ * pos0 + n_new > capacity.  n_new == 0 is a no-op. */
+tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x, tq_dtype x_dtype,
+                               int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0, int32_t capacity,
+                               uint8_t* codes, float* norms, void* stream);
+
+/* Decode attention over Block-GTQ keys and fp16 values: out = softmax(scale q K^T) V with
+ * every key decoded from its codes, group norms and the rotated query (q~_g = Q_g^T q_g,
+ * so q . k = sum_g norm_g sum_j q~_j c_g[code_j]).
+ *   codes, norms: as tq_gtq_quantize_keys; v: device fp16 [batch][n_kv_heads][capacity][128].
+ *   q: device [batch][n_q_heads][128] of q_dtype (TQ_F32 or TQ_F16); n_q_heads a multiple
+ *      of n_kv_heads, query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   seq_lens: device int32 [batch] (each clamped to [0, max_len]) or NULL (all max_len);
+ *      max_len <= capacity.
+ *   n_splits: key-axis sections as tq_decode_attention's: [s*C, min(T, (s+1)*C)),
+ *      C = ceil(T / n_splits).
+ *   out, lse_out: n_splits == 1: fp32 [batch][n_q_heads][128], natural-log lse (or NULL).
+ *   part_o, part_lse: n_splits > 1: original-domain section partials for tq_merge_splits
+ *      with rot == NULL.
+ * Scores and sums in fp32.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or
+ * scale; TQ_ECAPACITY for max_len > capacity. */
+tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes, const float* norms,
+                           const void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,
+                           tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                           int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

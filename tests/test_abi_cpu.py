@@ -277,6 +277,91 @@ def test_merge_without_rotation_validation(lib):
     assert m(None, 2, 1, 4, None, FAKE, FAKE, None, None) == TQ_EINVAL
 
 
+def test_gtq_allocate_matches_oracle(lib):
+    from oracle import blockgtq as bg
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        L = [64, 5, 17][trial % 3]
+        e = np.exp(rng.standard_normal(L) * 3).astype(np.float32)
+        if trial % 4 == 0:
+            e[: L // 2] = e[0]  # ties
+        b_min, b_max = [(1, 4), (0, 3), (2, 4)][trial % 3]
+        for budget in (L * b_min, (L * (b_min + b_max)) // 2, L * b_max, L * b_min + 1):
+            want = bg.allocate(e.astype(np.float64), budget, b_min, b_max)
+            got = tq.gtq_allocate(e, budget, b_min, b_max)
+            assert np.array_equal(want, got), (trial, budget)
+
+
+def test_gtq_allocate_validation(lib):
+    e = np.ones(4, dtype=np.float32)
+    b = np.zeros(4, dtype=np.int32)
+    f = lib.tq_gtq_allocate
+    assert f(None, 4, 8, 1, 4, b.ctypes.data) == TQ_EINVAL
+    assert f(e.ctypes.data, 4, 8, 1, 4, None) == TQ_EINVAL
+    assert f(e.ctypes.data, 0, 8, 1, 4, b.ctypes.data) == TQ_EINVAL
+    assert f(e.ctypes.data, 4, 3, 1, 4, b.ctypes.data) == TQ_EINVAL    # below 4 x b_min
+    assert f(e.ctypes.data, 4, 17, 1, 4, b.ctypes.data) == TQ_EINVAL   # above 4 x b_max
+    assert f(e.ctypes.data, 4, 8, 3, 2, b.ctypes.data) == TQ_EINVAL
+    bad = e.copy()
+    bad[2] = -1.0
+    assert f(bad.ctypes.data, 4, 8, 1, 4, b.ctypes.data) == TQ_EINVAL
+    bad[2] = np.nan
+    assert f(bad.ctypes.data, 4, 8, 1, 4, b.ctypes.data) == TQ_EINVAL
+
+
+def test_gtq_prepare_matches_oracle(lib):
+    from oracle import blockgtq as bg
+    rng = np.random.default_rng(8)
+    for trial in range(3):
+        bits = rng.integers(1, 5, 64).astype(np.int32)
+        if trial == 2:
+            bits[:] = 3  # one group of all 128 coordinates
+        gauss = rng.standard_normal((4, 128, 128)).astype(np.float32)
+        head = tq.GtqHead()
+        rot = np.zeros(tq.GTQ_ROTATION_FLOATS, dtype=np.float32)
+        assert lib.tq_gtq_prepare(bits.ctypes.data, gauss.ctypes.data, ctypes.byref(head), rot.ctypes.data) == TQ_OK
+        enc = bg.head_encoders(bits, gauss.astype(np.float64))
+        assert head.n_groups == len(enc)
+        for g, (w, coords, qm, c, m) in enumerate(enc):
+            n = len(coords)
+            assert head.width[g] == w and head.dim[g] == n
+            assert [head.coord[head.start[g] + j] for j in range(n)] == list(coords)
+            got = rot[head.rot_offset[g]:head.rot_offset[g] + n * n].reshape(n, n)
+            assert np.allclose(got, qm, atol=2e-5), (trial, g)
+            assert np.allclose([head.centroid[g][k] for k in range(2 ** w)], c, rtol=2e-6, atol=1e-7)
+            assert np.allclose([head.boundary[g][k] for k in range(2 ** w - 1)], m, rtol=2e-6, atol=1e-7)
+        assert all(head.start[g] == 128 for g in range(head.n_groups, 4))
+    assert lib.tq_gtq_prepare(np.full(64, 5, np.int32).ctypes.data, gauss.ctypes.data, ctypes.byref(head),
+                              rot.ctypes.data) == TQ_EINVAL
+
+
+def test_gtq_call_validation(lib):
+    qk = lib.tq_gtq_quantize_keys
+    assert qk(None, FAKE, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL
+    assert qk(FAKE, FAKE, FAKE, 2, 1, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL   # bf16 keys
+    assert qk(FAKE, FAKE, FAKE, 1, 0, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 4, 30, 32, FAKE, FAKE, None) == TQ_ECAPACITY
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, 32, FAKE, FAKE, None) == TQ_OK          # nothing launched
+    at = lib.tq_gtq_attention
+
+    def call(**kw):
+        a = dict(heads=FAKE, rot=FAKE, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, q=FAKE, qd=1, hq=8,
+                 max_len=64, scale=0.1, splits=1, out=FAKE, part=FAKE)
+        a.update(kw)
+        return at(a["heads"], a["rot"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["q"],
+                  a["qd"], a["hq"], None, a["max_len"], a["scale"], a["splits"], a["out"], None, a["part"], a["part"],
+                  None)
+    for k in ("heads", "rot", "codes", "norms", "v", "q"):
+        assert call(**{k: None}) == TQ_EINVAL, k
+    assert call(qd=2) == TQ_EINVAL
+    assert call(hq=7) == TQ_EINVAL
+    assert call(splits=0) == TQ_EINVAL
+    assert call(out=None) == TQ_EINVAL
+    assert call(splits=3, part=None) == TQ_EINVAL
+    assert call(scale=float("nan")) == TQ_EINVAL
+    assert call(max_len=65) == TQ_ECAPACITY
+
+
 def test_product_path_has_no_cpu_fallback():
     # the binding must not reach the oracle or any CPU computation
     src = open(os.path.join(ROOT, "compressed_domain_attention_amd", "__init__.py")).read()

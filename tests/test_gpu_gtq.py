@@ -1,0 +1,158 @@
+"""GPU parity of Block-GTQ keys through the C ABI against the oracle (oracle/blockgtq.py).
+
+Encoding: codes equal the oracle's except coordinates whose rotated value lies within 2e-6
+of a decision boundary (the library rotates with the fp32-rounded rotation, the oracle with
+fp64: their rotated values differ by about 1e-7), at most 1e-4 of all coordinates; norms
+within 1e-6 relative.  Attention is fed the oracle's codes and norms and compared with fp64
+attention on the oracle's dequantised keys and the fp16 values: within 1e-4 relative per
+row (fp32 sums of the same decoded keys), lse within 1e-4.  Rows are ragged, with an empty
+one; sections 1, 3 and 40; query groups of 4, 8 and 16 heads (two slices).
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_domain_attention_amd as tq
+import workloads
+from helpers import row_rel_err
+from oracle import attention, blockgtq as bg
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+LSE_ATOL = 1e-4
+BOUNDARY_EPS = 2e-6
+LENS = [300, 77, 0]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.library()
+
+
+def case(hq=32, hkv=8, lens=LENS, cap=320, seed=0):
+    w = replace(workloads.WORKLOADS["gtq32k"], batch=len(lens), n_q_heads=hq, n_kv_heads=hkv, seq_len=cap)
+    inp = workloads.generate(w, seed)
+    s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
+    bits = np.stack([bg.allocate(s[h].astype(np.float64), 3 * 64, 1, 4) for h in range(hkv)])
+    enc = [bg.head_encoders(bits[h], inp["gauss"][h].astype(np.float64)) for h in range(hkv)]
+    print("gtq case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, flush=True)
+    return w, inp, bits, enc
+
+
+def oracle_keys(w, inp, enc):
+    bsz, hkv, cap = w.batch, w.n_kv_heads, w.seq_len
+    codes = np.zeros((bsz, hkv, cap, 128), np.uint8)
+    norms = np.zeros((bsz, hkv, cap, 4), np.float32)
+    ys = np.zeros((bsz, hkv, cap, 128))
+    for b in range(bsz):
+        for h in range(hkv):
+            c, n, y = bg.quantize_keys(inp["k"][b, h].astype(np.float64), enc[h])
+            codes[b, h], ys[b, h] = c, y
+            norms[b, h, :, :n.shape[1]] = n
+    return codes, norms, ys
+
+
+def test_encoding_matches_oracle():
+    w, inp, bits, enc = case()
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    codes = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 64), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 4), dtype=torch.float32, device="cuda")
+    x = torch.from_numpy(inp["k"]).cuda()
+    # two calls: the first 100 tokens, then the rest at position 100
+    tq.gtq_quantize_keys(keys, x[:, :, :100].contiguous(), codes, norms, pos0=0)
+    tq.gtq_quantize_keys(keys, x[:, :, 100:].contiguous(), codes, norms, pos0=100)
+    torch.cuda.synchronize()
+    oc, on, oy = oracle_keys(w, inp, enc)
+    got = bg.unpack_codes(codes.cpu().numpy().reshape(-1, 64)).reshape(oc.shape)
+    bad = got != oc
+    frac = bad.mean()
+    assert frac <= 1e-4, frac
+    for b, h, t, j in zip(*np.nonzero(bad)):
+        ends = np.cumsum([len(e[1]) for e in enc[h]])
+        m = enc[h][int(np.searchsorted(ends, j, side="right"))][4]  # the position's group boundaries
+        assert np.min(np.abs(m - oy[b, h, t, j])) < BOUNDARY_EPS
+    # norms of absent groups are 0 on both sides
+    assert np.allclose(norms.cpu().numpy(), on, rtol=1e-6, atol=1e-30)
+
+
+def device_inputs(w, inp, oc, on):
+    codes = torch.from_numpy(bg.pack_codes(oc.reshape(-1, 128)).reshape(oc.shape[:3] + (64,))).cuda()
+    norms = torch.from_numpy(on).cuda()
+    v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
+    return codes, norms, v, q
+
+
+def oracle_attention(w, inp, enc, oc, on, lens):
+    kd = np.zeros((w.batch, w.n_kv_heads, w.seq_len, 128))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            kd[b, h] = bg.dequantize_keys(oc[b, h], on[b, h, :, :len(enc[h])].astype(np.float64), enc[h])
+    return attention.decode(inp["q"].astype(np.float64), kd, inp["v"].astype(np.float16).astype(np.float64), lens,
+                            w.scale), kd
+
+
+def check(out, lse, ro, rl, lens):
+    for b, t in enumerate(lens):
+        for h in range(out.shape[1]):
+            if t == 0:
+                assert lse[b, h] == -np.inf and not out[b, h].any()
+                continue
+            assert row_rel_err(out[b, h], ro[b, h]) <= RTOL, (b, h)
+            assert abs(lse[b, h] - rl[b, h]) <= LSE_ATOL, (b, h)
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 40])
+def test_attention_matches_oracle(n_splits):
+    w, inp, bits, enc = case()
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    oc, on, _ = oracle_keys(w, inp, enc)
+    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
+    res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale, n_splits=n_splits)
+    if n_splits > 1:
+        res = tq.merge_splits(None, *res)
+    torch.cuda.synchronize()
+    (ro, rl), _ = oracle_attention(w, inp, enc, oc, on, LENS)
+    check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, LENS)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (32, 2)])
+def test_head_groupings(hq, hkv):
+    lens = [300, 31]
+    w, inp, bits, enc = case(hq=hq, hkv=hkv, lens=lens)
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    oc, on, _ = oracle_keys(w, inp, enc)
+    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, lse = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(lens), scale=w.scale)
+    torch.cuda.synchronize()
+    (ro, rl), _ = oracle_attention(w, inp, enc, oc, on, lens)
+    check(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, lens)
+
+
+def test_sections_are_the_oracle_splits():
+    w, inp, bits, enc = case()
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    oc, on, _ = oracle_keys(w, inp, enc)
+    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
+    po, pl = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale, n_splits=3)
+    torch.cuda.synchronize()
+    _, kd = oracle_attention(w, inp, enc, oc, on, LENS)
+    ro, rl = attention.decode_splits(inp["q"].astype(np.float64), kd, inp["v"].astype(np.float16).astype(np.float64),
+                                     LENS, w.scale, 3)
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    for s in range(3):
+        for b, t in enumerate(LENS):
+            for h in range(w.n_q_heads):
+                if not np.isfinite(rl[s, b, h]):
+                    assert pl[s, b, h] == -np.inf and not po[s, b, h].any()
+                else:
+                    assert row_rel_err(po[s, b, h], ro[s, b, h]) <= RTOL
+                    assert abs(pl[s, b, h] - rl[s, b, h]) <= LSE_ATOL

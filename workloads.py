@@ -55,6 +55,10 @@ WORKLOADS = {
                             n_splits=8),
     # 8192-token prompt in compressed pages plus 8 generated tokens in the open page; the
     # bits, group and so4 fields do not apply to the lossless codec
+    # Block-GTQ keys at a 3-bit average budget (192 bits over 64 RoPE blocks, widths 1..4)
+    # with fp16 values; log-normal channel scales give the blocks unequal energies
+    "gtq32k": Workload("gtq32k", 4, 32, 8, 32768, 3, 16, 128, False, "float16", "lognormal", n_splits=4,
+                       codec="gtq"),
     "zipfusion8k": Workload("zipfusion8k", 32, 32, 8, 8200, 16, 16, 128, False, "bfloat16", "seeded4x8",
                             n_splits=1, codec="zip"),
 }
@@ -147,7 +151,20 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
     if w.so4:
         quat = np.random.default_rng(s_so4).standard_normal((hkv, HEAD_DIM // 4, 2, 4))
         so4 = (quat / np.linalg.norm(quat, axis=-1, keepdims=True)).astype(np.float32)
+    extra = {}
+    if w.codec == "gtq":
+        # a calibration prefix of queries and keys (same laws) for the block energies, and a
+        # Gaussian matrix per (KV head, width) from which each group's random rotation is drawn
+        s_cq, s_ck, s_rot = ss.spawn(3)
+        n_cal = 256
+        q_cal = np.random.default_rng(s_cq).standard_normal((n_cal, hq, HEAD_DIM), dtype=np.float32)
+        q_cal *= np.repeat(mul_k, g, axis=0)[None]
+        k_cal = np.random.default_rng(s_ck).standard_normal((n_cal, hkv, HEAD_DIM), dtype=np.float32)
+        k_cal *= mul_k[None]
+        extra = {"q_cal": q_cal, "k_cal": k_cal,
+                 "gauss": np.random.default_rng(s_rot).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32)}
     return {
+        **extra,
         "q": bf16_bits(q) if bf16 else q.astype(dt),
         "k": k,
         "v": v,
