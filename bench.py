@@ -531,6 +531,158 @@ def zip_measured_traffic(workload, n_splits):
     return None if ent is None else ent["hbm_bytes_per_launch"]
 
 
+def gtq_setup(w, inp, dev):
+    """Block-GTQ keys from the workload's calibration prefix (energies, allocation and
+    encoders in the library), the prompt's keys encoded on the GPU (timed), fp16 values."""
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
+    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
+    keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
+    T = w.seq_len
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device=dev)
+    norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device=dev)
+    x = torch.from_numpy(inp["k"]).to(dev)
+    tq.gtq_quantize_keys(keys, x[:, :, :1].contiguous(), codes, norms)  # loads the kernel before timing
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tq.gtq_quantize_keys(keys, x, codes, norms)
+    e1.record()
+    torch.cuda.synchronize()
+    v = torch.from_numpy(inp["v"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    return keys, bits, codes, norms, v, q, e0.elapsed_time(e1)
+
+
+GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
+
+
+def run_gtq(w, inp, steps, warmup, n_splits, check=True):
+    """The step on Block-GTQ keys with fp16 values: one attention launch (sections), merged
+    without rotation."""
+    import torch
+
+    import compressed_domain_attention_amd as tq
+
+    dev = torch.device("cuda:0")
+    keys, bits, codes, norms, v, q, enc_ms = gtq_setup(w, inp, dev)
+    cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
+    reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
+    sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
+    log("cache %.1f MB x %d replicas; groups per head %s" % (cache_bytes / 1e6, reps,
+                                                             [keys.n_groups(h) for h in range(w.n_kv_heads)]))
+    S = n_splits
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    po = torch.empty((S, w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((S, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+
+    def attend(i):
+        c, n, vv = sets[i % reps]
+        if S == 1:
+            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, out=out, lse=lse)
+        else:
+            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=S, part_o=po, part_lse=pl)
+
+    def step(i):
+        attend(i)
+        if S > 1:
+            tq.merge_splits(None, po, pl, out=out, lse=lse)
+
+    def graph(fn, n):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager_out):
+        raise SystemExit("graph replay does not reproduce the eager step")
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < 0.3:
+        graphs[i % reps].replay()
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % reps].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    n_att = max(reps, 16)
+    ga = graph(lambda i: attend(i), n_att)
+    ga.replay()
+    torch.cuda.synchronize()
+    t_d = time.perf_counter()
+    ga.replay()
+    torch.cuda.synchronize()
+    reps_att = max(3, int(0.5 / max(time.perf_counter() - t_d, 1e-6)))
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(reps_att):
+        ga.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    att_ms = d0.elapsed_time(d1) / (reps_att * n_att)
+
+    parity = None
+    if check:
+        # two (sequence, KV head) units against the oracle's own encoding of the same keys
+        from helpers import OUT_RTOL, row_rel_err
+        from oracle import attention, blockgtq as bg
+        o = out.cpu().numpy()
+        parity = 0.0
+        s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
+        for b, kv in [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
+            enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, 1, 4),
+                                   inp["gauss"][kv].astype(np.float64))
+            c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)
+            kd = bg.dequantize_keys(c, nrm, enc)
+            vd = inp["v"][b, kv].astype(np.float64)
+            for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+                ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+                parity = max(parity, float(row_rel_err(o[b, h], ref)))
+        if parity > OUT_RTOL:
+            raise SystemExit("parity check failed: %.3e > %.1e" % (parity, OUT_RTOL))
+    algo = w.batch * w.n_kv_heads * w.seq_len * GTQ_BYTES_PER_TOKEN_HEAD
+    return dict(step_ms=step_ms, attn_ms=att_ms, algo_bytes=algo, reps=reps, parity=parity, encode_ms=enc_ms,
+                widths=np.bincount(bits.ravel(), minlength=5)[1:].tolist())
+
+
+def _oracle_gtq_unit(args):
+    w, b, kv = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import attention, blockgtq as bg
+    inp = _oracle_unit.inp
+    s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
+    enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, 1, 4),
+                           inp["gauss"][kv].astype(np.float64))
+    c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)  # the stored cache (not timed)
+    t0 = time.perf_counter()
+    kd = bg.dequantize_keys(c, nrm, enc)
+    vd = inp["v"][b, kv].astype(np.float64)
+    for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+        attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+    return time.perf_counter() - t0
+
+
 def _oracle_zip_unit(args):
     w, b, kv = args
     os.environ["OMP_NUM_THREADS"] = "1"
@@ -603,7 +755,8 @@ def cpu_baseline(w, inp, budget_s=15.0):
 
     cores = min(len(os.sched_getaffinity(0)), 16)
     _oracle_unit.inp = inp
-    zip_ = w.codec == "zip"
+    zip_ = w.codec in ("zip", "gtq")
+    unit_fn = {"zip": _oracle_zip_unit, "gtq": _oracle_gtq_unit}.get(w.codec, _oracle_unit)
     units = [(w, b, kv) if zip_ else (w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
     done, busy, t0 = 0, 0.0, time.perf_counter()
     with threadpool_limits(1):
@@ -611,12 +764,13 @@ def cpu_baseline(w, inp, budget_s=15.0):
         with ctx.Pool(cores) as pool:
             while done < len(units) and time.perf_counter() - t0 < budget_s:
                 batch = units[done:done + cores]
-                busy += sum(pool.map(_oracle_zip_unit if zip_ else _oracle_unit, batch))
+                busy += sum(pool.map(unit_fn, batch))
                 done += len(batch)
     wall = time.perf_counter() - t0
     token_heads = done * w.seq_len
-    what = ("decompress the stored pages + fp64 attention (compression of the stream not timed)" if zip_
-            else "fp64 dequantise + attention")
+    what = {"zip": "decompress the stored pages + fp64 attention (compression of the stream not timed)",
+            "gtq": "fp64 decode of the stored keys + attention (encoding of the stream not timed)"}.get(
+        w.codec, "fp64 dequantise + attention")
     # the rate over the time the workers spent in the timed part, all workers together
     value = token_heads / (busy / cores) if zip_ else token_heads / wall
     return {"value": value, "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
@@ -829,6 +983,32 @@ def main():
             zip_counter_run(w, inp, n_splits)
         else:
             counter_run(w, inp, n_splits, args.schedule)
+        return
+    if w.codec == "gtq":
+        r = run_gtq(w, inp, args.steps, args.warmup, n_splits, check=not args.no_check)
+        units = w.batch * w.n_kv_heads * w.seq_len
+        achieved = r["algo_bytes"] / (r["attn_ms"] / 1e3) / 1e9
+        probe = stream_read_probe_gbs()
+        log("step %.3f ms, attention kernel %.3f ms -> %.0f GB/s (%.1f%% of 8 TB/s, %.1f%% of the %.0f GB/s probe); "
+            "widths 1-4 bits: %s blocks; key encoding %.3f ms" % (
+                r["step_ms"], r["attn_ms"], achieved, 100 * achieved / HBM_PEAK_GBS, 100 * achieved / probe, probe,
+                r["widths"], r["encode_ms"]))
+        print(json.dumps({
+            "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32 FMA (Block-GTQ 4-bit key containers, fp16 values)",
+            "data": "synthetic (seeded Gaussian activations with log-normal channel scales; workloads.py)",
+            "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                       "seq_len": w.seq_len, "keys": "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
+                       "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
+                       "step": "attention over encoded keys and fp16 values" +
+                               (", then merge" if n_splits > 1 else ""),
+                       "cache_replicas": r["reps"]},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gtq_attention_kernel"},
+            "cpu_baseline": cpu, "attention_kernel_ms": r["attn_ms"], "algorithmic_bytes_per_launch": r["algo_bytes"],
+            "block_widths": r["widths"], "key_encoding_ms": r["encode_ms"], "stream_read_probe_GBps": probe,
+            "parity_worst_row_rel_err": r["parity"]}), flush=True)
         return
     if w.codec == "zip":
         r = run_zip(w, inp, args.steps, args.warmup, n_splits, check=not args.no_check)

@@ -17,7 +17,7 @@ __all__ = [
     "NativeLibraryMissing", "TQError", "Codebook", "make_codebook", "Rotation", "PackedCache",
     "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
     "zip_store", "zip_compress", "zip_attention",
-    "gtq_allocate", "GtqKeys", "gtq_quantize_keys", "gtq_attention",
+    "gtq_block_energies", "gtq_allocate", "GtqKeys", "gtq_quantize_keys", "gtq_attention",
     "TQ_KEYS", "TQ_VALUES",
 ]
 
@@ -78,7 +78,7 @@ _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
            "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
-           "tq_zip_compress", "tq_zip_attention", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
+           "tq_zip_compress", "tq_zip_attention", "tq_gtq_block_energies", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
            "tq_gtq_attention")
 
 
@@ -115,6 +115,8 @@ def library():
     lib.tq_zip_compress.restype = I
     lib.tq_zip_attention.argtypes = [P, P, P, P, I, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_zip_attention.restype = I
+    lib.tq_gtq_block_energies.argtypes = [P, P, I, I, I, P]
+    lib.tq_gtq_block_energies.restype = I
     lib.tq_gtq_allocate.argtypes = [P, I, I, I, I, P]
     lib.tq_gtq_allocate.restype = I
     lib.tq_gtq_prepare.argtypes = [P, P, ctypes.POINTER(GtqHead), P]
@@ -407,6 +409,20 @@ def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=
 
 
 GTQ_ROTATION_FLOATS = 16384
+
+
+def gtq_block_energies(q_cal, k_cal):
+    """Block energies [n_kv_heads, 64] from calibration queries [N, n_q_heads, 128] and keys
+    [N, n_kv_heads, 128] (host arrays; computed in the library on the host)."""
+    import numpy as np
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    k = np.ascontiguousarray(k_cal, dtype=np.float32)
+    if q.ndim != 3 or k.ndim != 3 or q.shape[0] != k.shape[0] or q.shape[2] != HEAD_DIM or k.shape[2] != HEAD_DIM:
+        raise ValueError("q_cal [N, n_q_heads, 128] and k_cal [N, n_kv_heads, 128] are required")
+    out = np.zeros((k.shape[1], 64), dtype=np.float32)
+    _check(library().tq_gtq_block_energies(q.ctypes.data, k.ctypes.data, q.shape[0], q.shape[1], k.shape[1],
+                                           out.ctypes.data), "tq_gtq_block_energies")
+    return out
 
 
 def gtq_allocate(energies, budget: int, b_min: int = 1, b_max: int = 4):

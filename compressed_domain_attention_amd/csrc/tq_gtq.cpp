@@ -7,6 +7,28 @@
 
 #include "tq.h"
 
+extern "C" tq_status tq_gtq_block_energies(const float* q_cal, const float* k_cal, int32_t n_tokens,
+                                           int32_t n_q_heads, int32_t n_kv_heads, float* energies) {
+  if (q_cal == nullptr || k_cal == nullptr || energies == nullptr) return TQ_EINVAL;
+  if (n_tokens <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return TQ_EINVAL;
+  const int g = n_q_heads / n_kv_heads;
+  for (int h = 0; h < n_kv_heads; ++h) {
+    for (int i = 0; i < TQ_GTQ_BLOCKS; ++i) {
+      double sq = 0.0, sk = 0.0;
+      for (int t = 0; t < n_tokens; ++t) {
+        for (int r = 0; r < g; ++r) {
+          const float* q = q_cal + ((size_t)t * n_q_heads + h * g + r) * 128 + 2 * i;
+          sq += (double)q[0] * q[0] + (double)q[1] * q[1];
+        }
+        const float* k = k_cal + ((size_t)t * n_kv_heads + h) * 128 + 2 * i;
+        sk += (double)k[0] * k[0] + (double)k[1] * k[1];
+      }
+      energies[h * TQ_GTQ_BLOCKS + i] = (float)(0.5 * (sq / ((double)n_tokens * g) + sk / n_tokens));
+    }
+  }
+  return TQ_OK;
+}
+
 extern "C" tq_status tq_gtq_allocate(const float* energies, int32_t n_blocks, int32_t budget, int32_t b_min,
                                      int32_t b_max, int32_t* bits) {
   if (energies == nullptr || bits == nullptr || n_blocks <= 0) return TQ_EINVAL;

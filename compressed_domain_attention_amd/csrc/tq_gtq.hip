@@ -114,9 +114,8 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
 // partial scores for every head, summed over the quarter lanes; one wave per head runs the
 // online softmax over the chunk; thread (8 coordinates, token slot) adds 4 tokens of the
 // chunk for every head.  Results are in the original domain.
-template <bool QF16>
+template <int MAXH, bool QF16>
 __global__ __launch_bounds__(256) void gtq_attention_kernel(const GtqAttnArgs a) {
-  constexpr int MAXH = 8;
   __shared__ __attribute__((aligned(16))) float qb[MAXH * 128];  // rotated query, later the output
   __shared__ float pw[MAXH][64];
   __shared__ float hm[MAXH], hsum[MAXH], halpha[MAXH];
@@ -337,8 +336,14 @@ hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hip
 
 hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t stream) {
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(256);
-  if (q_f16) hipLaunchKernelGGL(gtq_attention_kernel<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(gtq_attention_kernel<false>, grid, block, 0, stream, a);
+  // slices of up to 4 heads keep the accumulators of a thread at 32 registers
+  if (a.heads_per_slice <= 4) {
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<4, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_attention_kernel<4, false>), grid, block, 0, stream, a);
+  } else {
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<8, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_attention_kernel<8, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

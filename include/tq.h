@@ -312,6 +312,16 @@ tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const 
 #define TQ_GTQ_MAX_GROUPS 4
 #define TQ_GTQ_ROTATION_FLOATS 16384 /* per head: every group's n x n rotation */
 
+/* Block energies from a calibration prefix (host): energies[h][i] = 1/2 (mean over tokens
+ * and the query heads reading KV head h of ||q^(i)||^2 + mean over tokens of ||k_h^(i)||^2),
+ * block i = coordinates (2i, 2i+1), accumulated in double.
+ *   q_cal: host float [n_tokens][n_q_heads][128]; k_cal: host float [n_tokens][n_kv_heads][128];
+ *   energies: host float [n_kv_heads][64].
+ * Errors: TQ_EINVAL for null pointers, non-positive counts or n_q_heads not a multiple of
+ * n_kv_heads. */
+tq_status tq_gtq_block_energies(const float* q_cal, const float* k_cal, int32_t n_tokens, int32_t n_q_heads,
+                                int32_t n_kv_heads, float* energies);
+
 /* Greedy integer allocation (host): bits[i] for n_blocks blocks with energies[i] >= 0.
  * Every block starts at b_min; each of the budget - n_blocks*b_min remaining bits goes to
  * the block below b_max with the largest (3/4) energies[i] 4^-bits[i] (in double; ties to

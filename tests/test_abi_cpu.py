@@ -292,6 +292,18 @@ def test_gtq_allocate_matches_oracle(lib):
             assert np.array_equal(want, got), (trial, budget)
 
 
+def test_gtq_block_energies_match_oracle(lib):
+    from oracle import blockgtq as bg
+    rng = np.random.default_rng(9)
+    q = (rng.standard_normal((40, 8, 128)) * np.exp(rng.standard_normal(128))).astype(np.float32)
+    k = (rng.standard_normal((40, 2, 128)) * np.exp(rng.standard_normal(128))).astype(np.float32)
+    assert np.allclose(tq.gtq_block_energies(q, k), bg.block_energies(q, k), rtol=1e-6)
+    e = np.zeros(128, dtype=np.float32)
+    assert lib.tq_gtq_block_energies(None, FAKE, 4, 8, 2, e.ctypes.data) == TQ_EINVAL
+    assert lib.tq_gtq_block_energies(FAKE, FAKE, 4, 7, 2, e.ctypes.data) == TQ_EINVAL
+    assert lib.tq_gtq_block_energies(FAKE, FAKE, 0, 8, 2, e.ctypes.data) == TQ_EINVAL
+
+
 def test_gtq_allocate_validation(lib):
     e = np.ones(4, dtype=np.float32)
     b = np.zeros(4, dtype=np.int32)
