@@ -65,7 +65,8 @@ class GtqHead(ctypes.Structure):
     """tq_gtq_head: one KV head's Block-GTQ key encoder (layout in include/tq.h)."""
     _fields_ = [("n_groups", ctypes.c_int32), ("width", ctypes.c_int32 * 4), ("start", ctypes.c_int32 * 4),
                 ("dim", ctypes.c_int32 * 4), ("rot_offset", ctypes.c_int32 * 4), ("coord", ctypes.c_int32 * 128),
-                ("centroid", (ctypes.c_float * 16) * 4), ("boundary", (ctypes.c_float * 15) * 4)]
+                ("centroid", (ctypes.c_float * 16) * 4), ("boundary", (ctypes.c_float * 15) * 4),
+                ("f16_scale", ctypes.c_float * 4)]
 
 
 class _Cache(ctypes.Structure):

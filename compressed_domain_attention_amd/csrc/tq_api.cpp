@@ -378,6 +378,7 @@ extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rot
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
   if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
+  if (capacity > (1 << 24)) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's values
   const int group = n_q_heads / n_kv_heads;
   const int hps = group < 8 ? group : 8;
   const int slices = (group + hps - 1) / hps;

@@ -31,6 +31,32 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// The pair {v[l], v[l ^ 16]} (or l ^ 32) in some order, with the row (half) swaps of
+// gfx950: plain vector instructions, no round trip through the LDS crossbar.  Reductions
+// (max, sum) over the pair do not depend on the order.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_rows(float v) {  // max over lanes l, l^16, l^32, l^48
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_rows(float v) {  // sum over lanes l, l^16, l^32, l^48
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
+}
+
 // Direct global -> LDS copies: every lane reads BYTES bytes and the data lands in LDS at
 // lds_base + lane * stride (lds_base is wave-uniform, passed in M0), where the stride is
 // BYTES for 4- and 16-byte copies and 16 for 12-byte copies (the fourth dword of each lane

@@ -101,6 +101,7 @@ extern "C" tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gaus
     if (st != TQ_OK) return st;
     for (int k = 0; k < 16; ++k) head->centroid[g][k] = cb.centroid[k];
     for (int k = 0; k < 15; ++k) head->boundary[g][k] = cb.boundary[k];
+    head->f16_scale[g] = cb.f16_scale;
     pos += n;
     off += n * n;
     ++g;

@@ -31,6 +31,11 @@ __device__ __forceinline__ int group_of(const tq_gtq_head& h, int j) {
   return (j >= h.start[1]) + (j >= h.start[2]) + (j >= h.start[3]);
 }
 
+template <typename T>
+__device__ __forceinline__ T lds_read(const uint8_t* p) {
+  return *(const T*)p;
+}
+
 // Copies one head's encoder into LDS (all threads of the block take part).
 __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* src) {
   constexpr int words = sizeof(tq_gtq_head) / 4;
@@ -106,222 +111,334 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
 }
 
 // ---------------------------------------------------------------------------------------
-// Decode attention over Block-GTQ keys and fp16 values, vector arithmetic in fp32.  One
-// workgroup per (sequence, KV head, section, head slice of up to 8 heads).  The prologue
-// rotates the slice's queries by every group's rotation into group order (scale and log2 e
-// folded in).  64-token chunks: thread (token, quarter) decodes the 32 group-order
-// positions of its quarter (code -> the group's centroid -> times the group norm) and forms
-// partial scores for every head, summed over the quarter lanes; one wave per head runs the
-// online softmax over the chunk; thread (8 coordinates, token slot) adds 4 tokens of the
-// chunk for every head.  Results are in the original domain.
-template <int MAXH, bool QF16>
-__global__ __launch_bounds__(256) void gtq_attention_kernel(const GtqAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float qb[MAXH * 128];  // rotated query, later the output
-  __shared__ float pw[MAXH][64];
-  __shared__ float hm[MAXH], hsum[MAXH], halpha[MAXH];
-  __shared__ __attribute__((aligned(16))) float ob[4][MAXH][128];
-  __shared__ float lse2[MAXH];
-  __shared__ float cbt[4][16];
-  __shared__ tq_gtq_head hd;
+// Decode attention over Block-GTQ keys and fp16 values on the matrix unit (fp16 operands,
+// fp32 accumulation, the page's tensor-core form).  One workgroup of NW waves per
+// (sequence, KV head, section, slice of up to 8 query heads).  The section's 16-token tiles
+// go to the waves in turn; each wave streams its tiles through its own ring of D LDS stages
+// with direct global -> LDS copies (a stage: the 16 key records, their group norms, the 16
+// fp16 value rows).
+//
+// Scores: the query is rotated per group in the prologue (q~ = Q_g^T q_g, scale and log2 e
+// folded in) and laid out in k-blocks of 32 positions that each belong to one group (a
+// group of n positions takes ceil(n/32) blocks, the tail zero-padded), divided by the
+// group codebook's fp16 scale s and split into fp16 hi + lo columns.  A key operand is 8
+// codes of one token decoded through per-group tables of the fp16 hi and lo parts of s c
+// (two products per block, so scores keep fp32-level accuracy); after a group's last block
+// its partial dot is multiplied by the token's group norm.  The output product,
+// the lazy softmax and the merge of waves are those of the codec kernel: weights as fp16
+// hi + lo rows from the lanes' score registers in k slots 8j .. 8j+3, values 4 tokens of
+// one coordinate per lane.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 x, u32x4 y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x), __builtin_bit_cast(half8_t, y), c, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, half2_t{(_Float16)x, (_Float16)y});
+}
+__device__ __forceinline__ float f16_lo(float x) { return x - (float)(_Float16)x; }
+
+constexpr float kRescaleG = 8.f;  // log2 headroom of the lazily updated softmax reference
+constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil(n/32) <= 7
+
+template <int NW, int D, bool QF16>
+__global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
+  constexpr int STAGE = 6144;  // key records 1 KB, norms 1 KB (256 B used), values 4 KB
+  constexpr int NDMA = 6;
+  constexpr int WAVE_LDS = D * STAGE;
+  static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NW * WAVE_LDS];
+  // fp16 hi (x) and lo (y) parts of s c for the two codes of a byte, per group
+  __shared__ __attribute__((aligned(8))) uint2 ptab[4][256];
+  __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
+  __shared__ tq_gtq_head hd;
+  __shared__ int kbg[kMaxKb + 1], kbm[kMaxKb + 1], nkb_s;
+  __shared__ float part_m[NW][8], part_l[NW][8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x / a.n_slices, slice = blockIdx.x - unit * a.n_slices;
   const int split = unit % a.n_splits, kv = (unit / a.n_splits) % a.n_kv_heads;
   const int b = unit / (a.n_splits * a.n_kv_heads);
   const int h0 = kv * a.group_size + slice * a.heads_per_slice;
   const int hs = min(a.heads_per_slice, a.group_size - slice * a.heads_per_slice);
-  // lengths beyond max_len (checked against the capacity on the host) are clamped
   const int T = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_len)) : a.max_len;
   const int C = (T + a.n_splits - 1) / a.n_splits;
   const int lo = min(T, split * C), hi = min(T, lo + C);
+  const int ntiles = lo < hi ? (hi - lo + 15) >> 4 : 0;
+  const int n = ntiles > wv ? (ntiles - wv + NW - 1) / NW : 0;  // this wave's tiles
 
   const size_t row0 = ((size_t)b * a.n_kv_heads + kv) * a.capacity;
-  const int st = tid >> 2, qd = tid & 3;   // scores: token, quarter
-  const int dg = tid & 15, ts = tid >> 4;  // values: 8 coordinates, token slot
   const uint8_t* kc = a.codes + row0 * 64;
-  const float* kn = a.norms + row0 * 4;
-  const uint8_t* vb = (const uint8_t*)a.v + row0 * 128 * 2;
+  const uint8_t* kn = (const uint8_t*)(a.norms + row0 * 4);
+  const uint8_t* vbp = (const uint8_t*)a.v + row0 * 256;
+  const int cap = a.capacity;
+  uint8_t* wlds = lds + wv * WAVE_LDS;
+  const uint32_t wlds_a = lds_addr(wlds);
 
-  uint4 nk, nv[4];
-  float4 nn;
-  auto fetch = [&](int c0) {
-    const int tk = c0 + st;
-    if (tk < hi) {
-      nk = *(const uint4*)(kc + (size_t)tk * 64 + 16 * qd);
-      nn = *(const float4*)(kn + (size_t)tk * 4);
-    }
+  auto tok0_of = [&](int s) { return lo + 16 * (wv + NW * s); };
+  // stage s: 16 key records (lane: token tok0 + l/4, 16 bytes), 16 norm quads (lanes 0-15),
+  // 16 value rows (4 copies; lane: token tok0 + 4k + l/16); tokens past the capacity are
+  // replaced by the tile's first token (masked when used)
+  auto issue = [&](int s) {
+    const int t0 = tok0_of(s);
+    const uint32_t dst = wlds_a + (s % D) * STAGE;
+    int t = t0 + (lane >> 2);
+    lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
+    t = t0 + lane;
+    lds_dma<16, true>(dst + 1024, kn, (lane < 16 && t < cap) ? (uint32_t)(t * 16) : (uint32_t)(t0 * 16));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tv = c0 + ts + 16 * j;
-      if (tv < hi) nv[j] = *(const uint4*)(vb + ((size_t)tv * 128 + 8 * dg) * 2);
+    for (int k = 0; k < 4; ++k) {
+      t = t0 + 4 * k + (lane >> 4);
+      lds_dma<16, true>(dst + 2048 + 1024 * k, vbp,
+                        t < cap ? (uint32_t)(t * 256 + 16 * (lane & 15)) : (uint32_t)(t0 * 256));
     }
   };
-  if (lo < hi) fetch(lo);  // the first chunk's reads overlap the set-up
 
+  // prologue: the head's encoder, the k-block plan, pair tables, the rotated query
   stage_head(&hd, (const tq_gtq_head*)a.heads + kv);
   __syncthreads();
-  if (tid < 64) cbt[tid >> 4][tid & 15] = hd.centroid[tid >> 4][tid & 15];
-  {
-    // q~_j = sum_r Q_g[r][j - start] q[coord[start + r]] for group-order position j
-    const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
-    for (int i = tid; i < hs * 128; i += 256) {
-      const int hh = i >> 7, j = i & 127;
-      const int g = group_of(hd, j), s0 = hd.start[g], n = hd.dim[g];
-      const size_t qbase = ((size_t)b * a.n_q_heads + h0 + hh) * 128;
-      const float* rr = grot + hd.rot_offset[g] + (j - s0);
-      float acc = 0.f;
-      for (int r = 0; r < n; ++r) {
-        const int c = hd.coord[s0 + r];
-        const float x = QF16 ? (float)((const _Float16*)a.q)[qbase + c] : ((const float*)a.q)[qbase + c];
-        acc = fmaf(rr[r * n], x, acc);
+  if (tid == 0) {
+    int nk = 0;
+    for (int g = 0; g < hd.n_groups; ++g)
+      for (int m = 0; m < (hd.dim[g] + 31) / 32 && nk < kMaxKb; ++m, ++nk) {
+        kbg[nk] = g;
+        kbm[nk] = m;
       }
-      qb[i] = acc * a.scale_log2;
+    kbg[nk] = -1;
+    nkb_s = nk;
+  }
+  for (int i = tid; i < 4 * 256; i += 64 * NW) {
+    const int g = i >> 8, by = i & 255;
+    const float sc = hd.f16_scale[g];
+    const float c0 = sc * hd.centroid[g][by & 15], c1 = sc * hd.centroid[g][by >> 4];
+    ptab[g][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
+  }
+  {
+    const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
+    for (int i = tid; i < 8 * 128; i += 64 * NW) {
+      const int hh = i >> 7, j = i & 127;
+      float acc = 0.f;
+      if (hh < hs) {
+        const int g = group_of(hd, j), s0 = hd.start[g], nd = hd.dim[g];
+        const size_t qbase = ((size_t)b * a.n_q_heads + h0 + hh) * 128;
+        const float* rr = grot + hd.rot_offset[g] + (j - s0);
+        for (int r = 0; r < nd; ++r) {
+          const int c = hd.coord[s0 + r];
+          const float x = QF16 ? (float)((const _Float16*)a.q)[qbase + c] : ((const float*)a.q)[qbase + c];
+          acc = fmaf(rr[r * nd], x, acc);
+        }
+        acc *= a.scale_log2 / hd.f16_scale[g];
+      }
+      qt[hh][j] = acc;
     }
-  }
-  if (tid < MAXH) {
-    hm[tid] = -INFINITY;
-    hsum[tid] = 0.f;
-  }
-  // this lane's 32 positions 32 qd + e: their groups, two bits each
-  uint32_t gbits0 = 0, gbits1 = 0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    gbits0 |= (uint32_t)group_of(hd, 32 * qd + e) << (2 * e);
-    gbits1 |= (uint32_t)group_of(hd, 32 * qd + 16 + e) << (2 * e);
   }
   __syncthreads();
-
-  float acc[MAXH][8];
+  const int col = lane & 15;
+  const int jr = lane >> 4;
+  const int nkb = nkb_s;
+  u32x4 qf[kMaxKb];
 #pragma unroll
-  for (int h = 0; h < MAXH; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-  for (int c0 = lo; c0 < hi; c0 += 64) {
-    const uint4 ck = nk;
-    const float4 cn = nn;
-    const uint4 cv0 = nv[0], cv1 = nv[1], cv2 = nv[2], cv3 = nv[3];
-    if (c0 + 64 < hi) fetch(c0 + 64);
-    // scores of the chunk's tokens, all heads
-    {
-      const int tok = c0 + st;
-      const uint32_t w[4] = {ck.x, ck.y, ck.z, ck.w};
-      float kx[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const uint32_t code = (w[e >> 3] >> (4 * (e & 7))) & 15u;
-        const uint32_t g = ((e < 16 ? gbits0 : gbits1) >> (2 * (e & 15))) & 3u;
-        const float nu = g == 0 ? cn.x : g == 1 ? cn.y : g == 2 ? cn.z : cn.w;
-        kx[e] = cbt[g][code] * nu;
-      }
-#pragma unroll
-      for (int h = 0; h < MAXH; ++h) {
-        if (h < hs) {
-          const float4* qp = (const float4*)(qb + h * 128 + 32 * qd);
-          float sc = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float4 qq = qp[i];
-            sc = fmaf(qq.x, kx[4 * i], sc);
-            sc = fmaf(qq.y, kx[4 * i + 1], sc);
-            sc = fmaf(qq.z, kx[4 * i + 2], sc);
-            sc = fmaf(qq.w, kx[4 * i + 3], sc);
-          }
-          sc += lane_xor(sc, 1, lane);
-          sc += lane_xor(sc, 2, lane);
-          if (qd == 0) pw[h][st] = tok < hi ? sc : -INFINITY;  // tokens past the section are masked
-        }
-      }
-    }
-    __syncthreads();
-    // online softmax per head over the chunk (log2 units)
-    for (int h = wv; h < hs; h += 4) {
-      const float sc = pw[h][lane];
-      float bm = sc;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) bm = fmaxf(bm, lane_xor(bm, o, lane));
-      const float mold = hm[h];
-      const float mnew = fmaxf(mold, bm);
-      const float al = mnew > mold ? __builtin_amdgcn_exp2f(mold - mnew) : 1.f;
-      const float mu = mnew == -INFINITY ? 0.f : mnew;
-      const float p = __builtin_amdgcn_exp2f(sc - mu);
-      float psum = p;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) psum += lane_xor(psum, o, lane);
-      pw[h][lane] = p;
-      if (lane == 0) {
-        hm[h] = mnew;
-        hsum[h] = hsum[h] * al + psum;
-        halpha[h] = al;
-      }
-    }
-    __syncthreads();
-    // value sums: tokens ts, ts + 16, ts + 32, ts + 48 of the chunk, coordinates 8 dg .. + 7
-    {
-#pragma unroll
-      for (int h = 0; h < MAXH; ++h) {
-        if (h < hs) {
-          const float al = halpha[h];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-        }
-      }
-      const uint4 cvs[4] = {cv0, cv1, cv2, cv3};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (c0 + ts + 16 * j < hi) {
-          const uint32_t x[4] = {cvs[j].x, cvs[j].y, cvs[j].z, cvs[j].w};
-          float vx[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-            const h2_t hh = __builtin_bit_cast(h2_t, x[e]);
-            vx[2 * e] = (float)hh[0];
-            vx[2 * e + 1] = (float)hh[1];
-          }
-#pragma unroll
-          for (int h = 0; h < MAXH; ++h) {
-            if (h < hs) {
-              const float p = pw[h][ts + 16 * j];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();  // the weights are rewritten by the next chunk
-  }
-
-  // sum the 16 token slots (lane bits 4, 5, then the four waves), normalise
-#pragma unroll
-  for (int h = 0; h < MAXH; ++h) {
-    if (h < hs) {
+  for (int kb = 0; kb < kMaxKb; ++kb) {
+    qf[kb] = u32x4{0u, 0u, 0u, 0u};
+    if (kb < nkb) {
+      const int g = kbg[kb], m = kbm[kb];
+      const int hh = col & 7;
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = acc[h][e];
-        x += lane_xor(x, 16, lane);
-        x += lane_xor(x, 32, lane);
-        if ((lane >> 4) == 0) ob[wv][h][8 * dg + e] = x;
+        const int p = 32 * m + 8 * jr + e;
+        float v = p < hd.dim[g] ? qt[hh][hd.start[g] + p] : 0.f;
+        x[e] = col >= 8 ? f16_lo(v) : v;
       }
+      qf[kb] = u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
     }
   }
+  // the k-block plan in registers: group, its first position, and per lane the byte of
+  // its first code and a mask of its live code pairs (positions past the group are zeros)
+  int kgrp[kMaxKb];
+  uint32_t kbyte[kMaxKb], klive[kMaxKb];
+  bool klast[kMaxKb], kfull[kMaxKb];
+#pragma unroll
+  for (int kb = 0; kb < kMaxKb; ++kb) {
+    const int g = kb < nkb ? __builtin_amdgcn_readfirstlane(kbg[kb]) : 0;
+    const int m = kb < nkb ? __builtin_amdgcn_readfirstlane(kbm[kb]) : 0;
+    const int dimg = hd.dim[g];
+    const int p = 32 * m + 8 * jr;
+    kgrp[kb] = g;
+    kbyte[kb] = (uint32_t)((hd.start[g] + p) >> 1);
+    uint32_t live = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) live |= (p + 2 * k < dimg ? 1u : 0u) << k;
+    klive[kb] = live;
+    klast[kb] = kb < nkb && __builtin_amdgcn_readfirstlane(kbg[kb + 1]) != g;
+    kfull[kb] = 32 * (m + 1) <= dimg;  // every lane's codes lie inside the group
+  }
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]));
+  vm_wait<0>();
+  for (int s = 0; s < D; ++s)
+    if (s < n) issue(s);
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY, thr = -INFINITY, lsum = 0.f;
+
+  for (int s = 0; s < n; ++s) {
+    const int younger = min(D - 1, n - 1 - s);
+    if (younger >= 3) vm_wait<3 * NDMA>();
+    else if (younger == 2) vm_wait<2 * NDMA>();
+    else if (younger == 1) vm_wait<NDMA>();
+    else vm_wait<0>();
+    const int t0 = tok0_of(s);
+    const int nv = min(16, hi - t0);
+    const uint8_t* sb = wlds + (s % D) * STAGE;
+
+    // ---- scores: the key operand row is token col; lane's k slots are codes 8 jr .. + 7
+    const uint8_t* rec = sb + 64 * col;
+    // two accumulators (key hi and lo parts) halve the chain of dependent products
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, cur = f32x4{0.f, 0.f, 0.f, 0.f}, cur2 = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t cb[kMaxKb];
+#pragma unroll
+    for (int kb = 0; kb < kMaxKb; ++kb) {  // every code word first
+      const uint32_t bo = kbyte[kb];
+      // the 4 code bytes from two aligned words (the byte offset is any multiple of 1)
+      const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
+      cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kMaxKb; ++kb) {
+      if (kb < nkb) {
+        const int g = kgrp[kb];
+        u32x4 oph, opl;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint2 e = ptab[g][(cb[kb] >> (8 * k)) & 255u];  // always a valid entry
+          oph[k] = e.x;
+          opl[k] = e.y;
+        }
+        if (!kfull[kb]) {  // a group's zero-padded tail block
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t m = (klive[kb] >> k) & 1u ? 0xFFFFFFFFu : 0u;
+            oph[k] &= m;
+            opl[k] &= m;
+          }
+        }
+        // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
+        cur = mfma_f16(oph, qf[kb], cur);
+        cur2 = mfma_f16(opl, qf[kb], cur2);
+        if (klast[kb]) {  // the group's last block: times each token's group norm
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[e] = fmaf(lds_read<float>(sb + 1024 + 16 * (4 * jr + e) + 4 * g), cur[e] + cur2[e], sc[e]);
+          cur = cur2 = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = sc[e] + dpp<0x128>(sc[e]);  // hi + lo query parts
+      x[e] = 4 * jr + e < nv ? v : -INFINITY;
+      bm = fmaxf(bm, x[e]);
+    }
+    bm = max_rows(bm);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bm > thr) != 0, 0)) {
+      const float mnew = fmaxf(mref, bm);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float al = __shfl(alpha, (4 * jr + e) & 7);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct][e] *= al;
+      }
+      mref = mnew;
+      thr = mnew + kRescaleG;
+    }
+    u32x4 pf;
+    {
+      float pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = __builtin_amdgcn_exp2f(x[e] - mref);
+        lsum += pw[e];
+        if (col >= 8) pw[e] = f16_lo(pw[e]);
+      }
+      pf = u32x4{pack_f16(pw[0], pw[1]), pack_f16(pw[2], pw[3]), 0u, 0u};
+    }
+    // ---- output: values of tokens 4 jr .. + 3 at coordinate 16 ct + col (zero past the row)
+    u32x2 vw[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint8_t* vp = sb + 2048 + 256 * 4 * jr + 2 * (16 * ct + col);
+      vw[ct] = u32x2{(uint32_t)lds_read<uint16_t>(vp) | ((uint32_t)lds_read<uint16_t>(vp + 256) << 16),
+                     (uint32_t)lds_read<uint16_t>(vp + 512) | ((uint32_t)lds_read<uint16_t>(vp + 768) << 16)};
+    }
+    if (nv < 16) {  // a partial tile: tokens past the row carry zeros (their weights are 0)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const int t = 4 * jr;
+        vw[ct].x &= (t < nv ? 0xFFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
+        vw[ct].y &= (t + 2 < nv ? 0xFFFFu : 0u) | (t + 3 < nv ? 0xFFFF0000u : 0u);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma_f16(pf, u32x4{vw[ct].x, vw[ct].y, 0u, 0u}, acc[ct]);
+    if (s + D < n) {
+      lds_wait();
+      issue(s + D);
+    }
+  }
+
+  // ---- merge the waves
+  vm_wait<0>();
+  lsum = sum_rows(lsum);
   __syncthreads();
-  for (int i = tid; i < hs * 128; i += 256) {
-    const int h = i >> 7, c = i & 127;
-    const float L = hsum[h];
-    qb[i] = L > 0.f ? (ob[0][h][c] + ob[1][h][c] + ob[2][h][c] + ob[3][h][c]) / L : 0.f;
-    if (c == 0) lse2[h] = L > 0.f ? hm[h] + __log2f(L) : -INFINITY;
+  float* po = (float*)wlds;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float o0, o1;
+      pair32(acc[ct][e], o0, o1);
+      if (jr < 2) po[(4 * jr + e) * 128 + 16 * ct + col] = o0 + o1;
+    }
+  if (lane < 8) {
+    part_m[wv][lane] = mref;
+    part_l[wv][lane] = lsum;
   }
   __syncthreads();
-  if (a.n_splits == 1) {
-    const size_t row = (size_t)b * a.n_q_heads + h0;
-    if (a.lse_out && tid < hs) a.lse_out[row + tid] = lse2[tid] * kLn2g;
-    for (int i = tid; i < hs * 128; i += 256) a.out[(row + (i >> 7)) * 128 + (i & 127)] = qb[i];
-  } else {
-    const size_t prow = ((size_t)split * a.batch + b) * a.n_q_heads + h0;
-    if (tid < hs) a.part_lse[prow + tid] = lse2[tid] * kLn2g;
-    for (int i = tid; i < hs * 128; i += 256) a.part_o[(prow + (i >> 7)) * 128 + (i & 127)] = qb[i];
+  for (int idx = tid; idx < hs * 128; idx += 64 * NW) {
+    const int h = idx >> 7, c = idx & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, part_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = part_m[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(part_m[w][h] - M);
+      L += f * part_l[w][h];
+      O += f * ((const float*)(lds + w * WAVE_LDS))[h * 128 + c];
+    }
+    const float o = L > 0.f ? O / L : 0.f;
+    const float lse = L > 0.f ? (M + __log2f(L)) * kLn2g : -INFINITY;
+    if (a.n_splits == 1) {
+      const size_t row = (size_t)b * a.n_q_heads + h0 + h;
+      a.out[row * 128 + c] = o;
+      if (c == 0 && a.lse_out) a.lse_out[row] = lse;
+    } else {
+      const size_t row = ((size_t)split * a.batch + b) * a.n_q_heads + h0 + h;
+      a.part_o[row * 128 + c] = o;
+      if (c == 0) a.part_lse[row] = lse;
+    }
   }
 }
 
@@ -335,15 +452,11 @@ hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hip
 }
 
 hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t stream) {
-  const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(256);
-  // slices of up to 4 heads keep the accumulators of a thread at 32 registers
-  if (a.heads_per_slice <= 4) {
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<4, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_attention_kernel<4, false>), grid, block, 0, stream, a);
-  } else {
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<8, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_attention_kernel<8, false>), grid, block, 0, stream, a);
-  }
+  constexpr int NW = 8, D = 2;
+  const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
+  if (a.heads_per_slice > 8) return hipErrorInvalidValue;
+  if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

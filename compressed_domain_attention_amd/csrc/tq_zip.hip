@@ -162,32 +162,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 // x = hi + lo with hi, lo BF16 (round to nearest even): hi + lo carries 16 significant bits
 __device__ __forceinline__ float bf16_lo(float x) { return x - (float)(__bf16)x; }
 
-// The pair {v[l], v[l ^ 16]} (or l ^ 32) in some order, with the row (half) swaps of
-// gfx950: plain vector instructions, no round trip through the LDS crossbar.  Reductions
-// (max, sum) over the pair do not depend on the order.
-__device__ __forceinline__ void pair16(float v, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void pair32(float v, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_rows(float v) {  // max over lanes l, l^16, l^32, l^48
-  float a, b;
-  pair16(v, a, b);
-  pair32(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float sum_rows(float v) {  // sum over lanes l, l^16, l^32, l^48
-  float a, b;
-  pair16(v, a, b);
-  pair32(a + b, a, b);
-  return a + b;
-}
-
 // kept ? raw : coded, word by word (a bit select, no branch)
 __device__ __forceinline__ u32x4 pick(bool kept, u32x4 raw, u32x4 coded) {
   const uint32_t m = kept ? 0xFFFFFFFFu : 0u;

@@ -341,6 +341,8 @@ typedef struct {
   int32_t coord[128];               /* original coordinate of group-order position j */
   float centroid[TQ_GTQ_MAX_GROUPS][16];
   float boundary[TQ_GTQ_MAX_GROUPS][15];
+  float f16_scale[TQ_GTQ_MAX_GROUPS];  /* the codebook's tq_codebook.f16_scale: the matrix-core
+                                          decode holds fp16(s c) and divides the query by s */
 } tq_gtq_head;
 
 /* Builds one head's encoder on the host from its 64 block widths (1 .. 4) and a Gaussian

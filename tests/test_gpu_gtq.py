@@ -5,7 +5,7 @@ of a decision boundary (the library rotates with the fp32-rounded rotation, the 
 fp64: their rotated values differ by about 1e-7), at most 1e-4 of all coordinates; norms
 within 1e-6 relative.  Attention is fed the oracle's codes and norms and compared with fp64
 attention on the oracle's dequantised keys and the fp16 values: within 1e-4 relative per
-row (fp32 sums of the same decoded keys), lse within 1e-4.  Rows are ragged, with an empty
+row (fp32 sums of fp16 hi + lo operands), lse within 1e-4 + 1e-5 |lse|.  Rows are ragged, with an empty
 one; sections 1, 3 and 40; query groups of 4, 8 and 16 heads (two slices).
 """
 
@@ -22,8 +22,11 @@ from oracle import attention, blockgtq as bg
 
 pytestmark = pytest.mark.gpu
 
+# fp16 operands with fp32 accumulation (the page's tensor-core form); keys, query and weights
+# are each carried as fp16 hi + lo parts, so the sums keep fp32-level accuracy
 RTOL = 1e-4
 LSE_ATOL = 1e-4
+LSE_RTOL = 1e-5
 BOUNDARY_EPS = 2e-6
 LENS = [300, 77, 0]
 
@@ -98,13 +101,16 @@ def oracle_attention(w, inp, enc, oc, on, lens):
 
 
 def check(out, lse, ro, rl, lens):
+    worst = worst_lse = 0.0
     for b, t in enumerate(lens):
         for h in range(out.shape[1]):
             if t == 0:
                 assert lse[b, h] == -np.inf and not out[b, h].any()
                 continue
-            assert row_rel_err(out[b, h], ro[b, h]) <= RTOL, (b, h)
-            assert abs(lse[b, h] - rl[b, h]) <= LSE_ATOL, (b, h)
+            worst = max(worst, float(row_rel_err(out[b, h], ro[b, h])))
+            worst_lse = max(worst_lse, abs(float(lse[b, h] - rl[b, h])))
+    print("worst row error %.2e, lse %.2e" % (worst, worst_lse), flush=True)
+    assert worst <= RTOL and worst_lse <= LSE_ATOL + LSE_RTOL * float(np.max(np.abs(rl[np.isfinite(rl)])))
 
 
 @pytest.mark.parametrize("n_splits", [1, 3, 40])
@@ -155,4 +161,4 @@ def test_sections_are_the_oracle_splits():
                     assert pl[s, b, h] == -np.inf and not po[s, b, h].any()
                 else:
                     assert row_rel_err(po[s, b, h], ro[s, b, h]) <= RTOL
-                    assert abs(pl[s, b, h] - rl[s, b, h]) <= LSE_ATOL
+                    assert abs(pl[s, b, h] - rl[s, b, h]) <= LSE_ATOL + LSE_RTOL * abs(rl[s, b, h])

@@ -57,7 +57,7 @@ WORKLOADS = {
     # bits, group and so4 fields do not apply to the lossless codec
     # Block-GTQ keys at a 3-bit average budget (192 bits over 64 RoPE blocks, widths 1..4)
     # with fp16 values; log-normal channel scales give the blocks unequal energies
-    "gtq32k": Workload("gtq32k", 4, 32, 8, 32768, 3, 16, 128, False, "float16", "lognormal", n_splits=16,
+    "gtq32k": Workload("gtq32k", 4, 32, 8, 32768, 3, 16, 128, False, "float16", "lognormal", n_splits=8,
                        codec="gtq"),
     "zipfusion8k": Workload("zipfusion8k", 32, 32, 8, 8200, 16, 16, 128, False, "bfloat16", "seeded4x8",
                             n_splits=1, codec="zip"),
