@@ -666,6 +666,64 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
                 widths=np.bincount(bits.ravel(), minlength=5)[1:].tolist())
 
 
+GTQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gtq_traffic.json")
+GTQ_KERNEL_SRC = os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", "tq_gtq.hip")
+
+
+def gtq_kernel_hash():
+    return hashlib.sha256(open(GTQ_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def gtq_counter_run(w, inp, n_splits, launches=24):
+    """rocprofv3 --pmc dispatches for Block-GTQ: the calibration copies, then `launches`
+    attention launches over the cache replicas, as run_gtq times them."""
+    import ctypes
+
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    from compressed_domain_attention_amd import build as _b
+
+    dev = torch.device("cuda:0")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.tq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
+    torch.cuda.synchronize()
+    del src, dst
+    keys, bits, codes, norms, v, q, _ = gtq_setup(w, inp, dev)
+    cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
+    reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
+    sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
+    S = max(n_splits, 1)
+    po = torch.empty((S, w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((S, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    for i in range(launches):
+        c, n, vv = sets[i % reps]
+        if n_splits == 1:
+            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, out=out)
+        else:
+            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=n_splits, part_o=po,
+                             part_lse=pl)
+    torch.cuda.synchronize()
+    log("counter run: 3 copies of %d bytes, %d Block-GTQ attention launches over %d replicas" % (
+        COPY_BYTES, launches, reps))
+
+
+def gtq_measured_traffic(workload, n_splits):
+    if not os.path.exists(GTQ_TRAFFIC_FILE):
+        return None
+    rec = json.load(open(GTQ_TRAFFIC_FILE))
+    if rec.get("kernel_sha256_16") != gtq_kernel_hash():
+        return None
+    ent = rec.get("workloads", {}).get("%s/S%d" % (workload, n_splits))
+    return None if ent is None else ent["hbm_bytes_per_launch"]
+
+
 def _oracle_gtq_unit(args):
     w, b, kv = args
     os.environ["OMP_NUM_THREADS"] = "1"
@@ -909,25 +967,29 @@ def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
 
 
 def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
-    """As write_traffic, for the codec's attention kernel (profiles/zip_traffic.json)."""
+    """As write_traffic, for the codec's or Block-GTQ's attention kernel
+    (profiles/zip_traffic.json, profiles/gtq_traffic.json)."""
+    kname = "gtq_attention" if w.codec == "gtq" else "zip_attention"
+    out_file = GTQ_TRAFFIC_FILE if w.codec == "gtq" else ZIP_TRAFFIC_FILE
+    khash = gtq_kernel_hash() if w.codec == "gtq" else zip_kernel_hash()
     fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", CALIBRATION_KERNEL), _per_dispatch(write_csv, "WRITE_SIZE", CALIBRATION_KERNEL)
-    fd = _per_dispatch(fetch_csv, "FETCH_SIZE", "zip_attention")
-    wd = _per_dispatch(write_csv, "WRITE_SIZE", "zip_attention")
+    fd = _per_dispatch(fetch_csv, "FETCH_SIZE", kname)
+    wd = _per_dispatch(write_csv, "WRITE_SIZE", kname)
     if not (fc and wc and fd and wd):
-        raise SystemExit("counter files hold no copy or zip attention dispatches")
+        raise SystemExit("counter files hold no copy or %s dispatches" % kname)
     f_factor = COPY_BYTES / (sum(fc) / len(fc) * 1024)
     w_factor = COPY_BYTES / (sum(wc) / len(wc) * 1024)
     fd, wd = fd[len(fd) // 2:], wd[len(wd) // 2:]
     read = sum(fd) / len(fd) * 1024 * f_factor
     written = sum(wd) / len(wd) * 1024 * w_factor
-    rec = json.load(open(ZIP_TRAFFIC_FILE)) if os.path.exists(ZIP_TRAFFIC_FILE) else {}
-    if rec.get("kernel_sha256_16") != zip_kernel_hash():
-        rec = {"kernel_sha256_16": zip_kernel_hash(), "workloads": {}}
+    rec = json.load(open(out_file)) if os.path.exists(out_file) else {}
+    if rec.get("kernel_sha256_16") != khash:
+        rec = {"kernel_sha256_16": khash, "workloads": {}}
     rec["workloads"]["%s/S%d" % (w.name, n_splits)] = {
         "hbm_bytes_per_launch": read + written, "read_bytes": read, "written_bytes": written,
         "fetch_scale": f_factor, "write_scale": w_factor, "commands": commands}
-    os.makedirs(os.path.dirname(ZIP_TRAFFIC_FILE), exist_ok=True)
-    with open(ZIP_TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_file), exist_ok=True)
+    with open(out_file, "w") as f:
         json.dump(rec, f, indent=1)
     log("traffic %s/S%d: read %.1f MB + written %.2f MB per launch (scales %.3f, %.3f)" % (
         w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
@@ -961,7 +1023,7 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     n_splits = args.splits if args.splits is not None else w.n_splits
     if args.write_traffic:
-        if w.codec == "zip":
+        if w.codec in ("zip", "gtq"):
             write_zip_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
         else:
             write_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
@@ -981,6 +1043,8 @@ def main():
     if args.counter_run:
         if w.codec == "zip":
             zip_counter_run(w, inp, n_splits)
+        elif w.codec == "gtq":
+            gtq_counter_run(w, inp, n_splits)
         else:
             counter_run(w, inp, n_splits, args.schedule)
         return
@@ -996,7 +1060,7 @@ def main():
         print(json.dumps({
             "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f32 FMA (Block-GTQ 4-bit key containers, fp16 values)",
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ 4-bit key containers, fp16 values)",
             "data": "synthetic (seeded Gaussian activations with log-normal channel scales; workloads.py)",
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                        "seq_len": w.seq_len, "keys": "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
@@ -1005,7 +1069,8 @@ def main():
                                (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gtq_attention_kernel"},
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": gtq_measured_traffic(w.name, n_splits),
+                         "kernel": "gtq_attention_kernel"},
             "cpu_baseline": cpu, "attention_kernel_ms": r["attn_ms"], "algorithmic_bytes_per_launch": r["algo_bytes"],
             "block_widths": r["widths"], "key_encoding_ms": r["encode_ms"], "stream_read_probe_GBps": probe,
             "parity_worst_row_rel_err": r["parity"]}), flush=True)
