@@ -82,8 +82,15 @@ __device__ __forceinline__ void lds_dma(uint32_t lds_base, const void* sbase, ui
     else
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx3 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
                    : "memory", "m0");
+  } else if (BYTES == 4) {
+    if (STREAM)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
   } else {
-    static_assert(BYTES == 12 || BYTES == 16, "whole-lane copies of 12 or 16 bytes");
+    static_assert(BYTES == 4 || BYTES == 12 || BYTES == 16, "whole-lane copies of 4, 12 or 16 bytes");
   }
 }
 template <int BYTES, bool STREAM>

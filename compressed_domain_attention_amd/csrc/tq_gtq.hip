@@ -120,15 +120,20 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
 //
 // Scores: the query is rotated per group in the prologue (q~ = Q_g^T q_g, scale and log2 e
 // folded in) and laid out in k-blocks of 32 positions that each belong to one group (a
-// group of n positions takes ceil(n/32) blocks, the tail zero-padded), divided by the
+// group of n positions takes ceil(n/32) blocks; query positions past the group are zero,
+// so the codes of the next group that share the block contribute nothing), divided by the
 // group codebook's fp16 scale s and split into fp16 hi + lo columns.  A key operand is 8
-// codes of one token decoded through per-group tables of the fp16 hi and lo parts of s c
-// (two products per block, so scores keep fp32-level accuracy); after a group's last block
-// its partial dot is multiplied by the token's group norm.  The output product,
-// the lazy softmax and the merge of waves are those of the codec kernel: weights as fp16
-// hi + lo rows from the lanes' score registers in k slots 8j .. 8j+3, values 4 tokens of
-// one coordinate per lane.
+// codes of one token decoded through the block's table of the fp16 hi and lo parts of s c
+// for the two codes of a byte (two products per block, so scores keep fp32-level
+// accuracy); each block's partial dot is multiplied by the token's group norm.  Tables sit
+// at fixed LDS offsets per block and the norms group-major, so the unrolled block loop has
+// no branch, mask or per-lane index beyond the code bytes.  The output product,
+// the lazy softmax and the merge of waves are those of the codec kernel; the output
+// product is a 16x16x16 one: weights as fp16 hi + lo rows straight from the lanes' score
+// registers (k slots 4j .. 4j+3 = the lane's tokens), values 4 tokens of one coordinate
+// per lane, each read into one half of a register.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,6 +142,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4 mfma_f16(u32x4 x, u32x4 y, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x), __builtin_bit_cast(half8_t, y), c, 0,
                                                 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k16(u32x2 x, u32x2 y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, x), __builtin_bit_cast(half4_t, y), c, 0, 0,
+                                               0);
 }
 __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
   return __builtin_bit_cast(uint32_t, half2_t{(_Float16)x, (_Float16)y});
@@ -148,13 +157,18 @@ constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil
 
 template <int NW, int D, bool QF16>
 __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
-  constexpr int STAGE = 6144;  // key records 1 KB, norms 1 KB (256 B used), values 4 KB
+  constexpr int STAGE = 5376;  // key records 1 KB, norms 256 B (group-major), values 4 KB
+  constexpr int NORM_AT = 1024, VAL_AT = 1280;
   constexpr int NDMA = 6;
   constexpr int WAVE_LDS = D * STAGE;
   static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NW * WAVE_LDS];
-  // fp16 hi (x) and lo (y) parts of s c for the two codes of a byte, per group
-  __shared__ __attribute__((aligned(8))) uint2 ptab[4][256];
+  constexpr int TAB_BYTES = kMaxKb * 256 * 8;
+  // the pair tables first, so that their addresses fit the LDS instructions' offset field
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
+  uint2(*const ptab)[256] = (uint2(*)[256])lds_all;
+  uint8_t* const lds = lds_all + TAB_BYTES;
+  // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
+  // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
   __shared__ tq_gtq_head hd;
   __shared__ int kbg[kMaxKb + 1], kbm[kMaxKb + 1], nkb_s;
@@ -182,20 +196,21 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   const uint32_t wlds_a = lds_addr(wlds);
 
   auto tok0_of = [&](int s) { return lo + 16 * (wv + NW * s); };
-  // stage s: 16 key records (lane: token tok0 + l/4, 16 bytes), 16 norm quads (lanes 0-15),
-  // 16 value rows (4 copies; lane: token tok0 + 4k + l/16); tokens past the capacity are
-  // replaced by the tile's first token (masked when used)
+  // stage s: 16 key records (lane: token tok0 + l/4, 16 bytes), the 64 norms group-major
+  // (lane: group l/16 of token tok0 + l%16), 16 value rows (4 copies; lane: token
+  // tok0 + 4k + l/16); tokens past the capacity are replaced by the tile's first token
+  // (their weights are 0)
   auto issue = [&](int s) {
     const int t0 = tok0_of(s);
     const uint32_t dst = wlds_a + (s % D) * STAGE;
     int t = t0 + (lane >> 2);
     lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
-    t = t0 + lane;
-    lds_dma<16, true>(dst + 1024, kn, (lane < 16 && t < cap) ? (uint32_t)(t * 16) : (uint32_t)(t0 * 16));
+    t = t0 + (lane & 15);
+    lds_dma<4, true>(dst + NORM_AT, kn, t < cap ? (uint32_t)(t * 16 + 4 * (lane >> 4)) : (uint32_t)(t0 * 16));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       t = t0 + 4 * k + (lane >> 4);
-      lds_dma<16, true>(dst + 2048 + 1024 * k, vbp,
+      lds_dma<16, true>(dst + VAL_AT + 1024 * k, vbp,
                         t < cap ? (uint32_t)(t * 256 + 16 * (lane & 15)) : (uint32_t)(t0 * 256));
     }
   };
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   __syncthreads();
   if (tid == 0) {
     int nk = 0;
-    for (int g = 0; g < hd.n_groups; ++g)
+    for (int g = 0; g < min(hd.n_groups, TQ_GTQ_MAX_GROUPS); ++g)
       for (int m = 0; m < (hd.dim[g] + 31) / 32 && nk < kMaxKb; ++m, ++nk) {
         kbg[nk] = g;
         kbm[nk] = m;
@@ -213,11 +228,16 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     kbg[nk] = -1;
     nkb_s = nk;
   }
-  for (int i = tid; i < 4 * 256; i += 64 * NW) {
-    const int g = i >> 8, by = i & 255;
+  __syncthreads();
+  const int nkb = __builtin_amdgcn_readfirstlane(nkb_s);
+  for (int i = tid; i < kMaxKb * 256; i += 64 * NW) {
+    const int kb = i >> 8, by = i & 255, g = kb < nkb ? kbg[kb] : 0;
+    // codes past the codebook decode to 0
+    const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
     const float sc = hd.f16_scale[g];
-    const float c0 = sc * hd.centroid[g][by & 15], c1 = sc * hd.centroid[g][by >> 4];
-    ptab[g][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
+    const float c0 = (by & 15) < nc ? sc * hd.centroid[g][by & 15] : 0.f;
+    const float c1 = (by >> 4) < nc ? sc * hd.centroid[g][by >> 4] : 0.f;
+    ptab[kb][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
   }
   {
     const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
@@ -241,45 +261,40 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   __syncthreads();
   const int col = lane & 15;
   const int jr = lane >> 4;
-  const int nkb = nkb_s;
-  u32x4 qf[kMaxKb];
+  // query operands: block kb's positions 8 jr .. + 3 (qa) and + 4 .. + 7 (qb), each pair
+  // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]
+  u32x4 qa[kMaxKb], qb[kMaxKb];
 #pragma unroll
   for (int kb = 0; kb < kMaxKb; ++kb) {
-    qf[kb] = u32x4{0u, 0u, 0u, 0u};
+    qa[kb] = qb[kb] = u32x4{0u, 0u, 0u, 0u};
     if (kb < nkb) {
       const int g = kbg[kb], m = kbm[kb];
       const int hh = col & 7;
-      float x[8];
+      uint32_t x[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = 32 * m + 8 * jr + e;
-        float v = p < hd.dim[g] ? qt[hh][hd.start[g] + p] : 0.f;
-        x[e] = col >= 8 ? f16_lo(v) : v;
+      for (int e = 0; e < 4; ++e) {
+        const int p = 32 * m + 8 * jr + 2 * e;
+        const float v0 = p < hd.dim[g] ? qt[hh][hd.start[g] + p] : 0.f;
+        const float v1 = p + 1 < hd.dim[g] ? qt[hh][hd.start[g] + p + 1] : 0.f;
+        x[e] = col >= 8 ? pack_f16(f16_lo(v0), f16_lo(v1)) : pack_f16(v0, v1);
       }
-      qf[kb] = u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
+      qa[kb] = u32x4{x[0], x[0], x[1], x[1]};
+      qb[kb] = u32x4{x[2], x[2], x[3], x[3]};
     }
   }
-  // the k-block plan in registers: group, its first position, and per lane the byte of
-  // its first code and a mask of its live code pairs (positions past the group are zeros)
+  // the k-block plan in registers: the block's group (uniform) and per lane the byte of its
+  // first code (reads past a record's 64 bytes stay inside the stage and meet zero query)
   int kgrp[kMaxKb];
-  uint32_t kbyte[kMaxKb], klive[kMaxKb];
-  bool klast[kMaxKb], kfull[kMaxKb];
+  uint32_t kbyte[kMaxKb];
 #pragma unroll
   for (int kb = 0; kb < kMaxKb; ++kb) {
     const int g = kb < nkb ? __builtin_amdgcn_readfirstlane(kbg[kb]) : 0;
     const int m = kb < nkb ? __builtin_amdgcn_readfirstlane(kbm[kb]) : 0;
-    const int dimg = hd.dim[g];
-    const int p = 32 * m + 8 * jr;
     kgrp[kb] = g;
-    kbyte[kb] = (uint32_t)((hd.start[g] + p) >> 1);
-    uint32_t live = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) live |= (p + 2 * k < dimg ? 1u : 0u) << k;
-    klive[kb] = live;
-    klast[kb] = kb < nkb && __builtin_amdgcn_readfirstlane(kbg[kb + 1]) != g;
-    kfull[kb] = 32 * (m + 1) <= dimg;  // every lane's codes lie inside the group
+    kbyte[kb] = (uint32_t)((hd.start[g] + 32 * m + 8 * jr) >> 1);
   }
-  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]));
+  asm volatile("" ::"v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "v"(qa[4]), "v"(qa[5]), "v"(qa[6]));
+  asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]), "v"(qb[4]), "v"(qb[5]), "v"(qb[6]));
   vm_wait<0>();
   for (int s = 0; s < D; ++s)
     if (s < n) issue(s);
@@ -301,8 +316,8 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 
     // ---- scores: the key operand row is token col; lane's k slots are codes 8 jr .. + 7
     const uint8_t* rec = sb + 64 * col;
-    // two accumulators (key hi and lo parts) halve the chain of dependent products
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, cur = f32x4{0.f, 0.f, 0.f, 0.f}, cur2 = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every block is computed (those past the head's last have zero tables and query), so
+    // the unrolled loop is one basic block the compiler can interleave
     uint32_t cb[kMaxKb];
 #pragma unroll
     for (int kb = 0; kb < kMaxKb; ++kb) {  // every code word first
@@ -311,35 +326,27 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
       cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
     }
+    // key operands straight from the table reads: [hi pair, lo pair] of two bytes each
+    u32x4 ka[kMaxKb], kb2[kMaxKb];
 #pragma unroll
     for (int kb = 0; kb < kMaxKb; ++kb) {
-      if (kb < nkb) {
-        const int g = kgrp[kb];
-        u32x4 oph, opl;
+      const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
+      const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
+      ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
+      kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+    }
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint2 e = ptab[g][(cb[kb] >> (8 * k)) & 255u];  // always a valid entry
-          oph[k] = e.x;
-          opl[k] = e.y;
-        }
-        if (!kfull[kb]) {  // a group's zero-padded tail block
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t m = (klive[kb] >> k) & 1u ? 0xFFFFFFFFu : 0u;
-            oph[k] &= m;
-            opl[k] &= m;
-          }
-        }
-        // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
-        cur = mfma_f16(oph, qf[kb], cur);
-        cur2 = mfma_f16(opl, qf[kb], cur2);
-        if (klast[kb]) {  // the group's last block: times each token's group norm
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sc[e] = fmaf(lds_read<float>(sb + 1024 + 16 * (4 * jr + e) + 4 * g), cur[e] + cur2[e], sc[e]);
-          cur = cur2 = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
+    for (int kb = 0; kb < kMaxKb; ++kb) {
+      // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
+      f32x4 cur = mfma_f16(ka[kb], qa[kb], f32x4{0.f, 0.f, 0.f, 0.f});
+      cur = mfma_f16(kb2[kb], qb[kb], cur);
+      // times the group norms of the lane's tokens 4 jr .. + 3
+      const float4 nr = lds_read<float4>(sb + NORM_AT + 64 * kgrp[kb] + 16 * jr);
+      sc[0] = fmaf(nr.x, cur[0], sc[0]);
+      sc[1] = fmaf(nr.y, cur[1], sc[1]);
+      sc[2] = fmaf(nr.z, cur[2], sc[2]);
+      sc[3] = fmaf(nr.w, cur[3], sc[3]);
     }
     float x[4];
     float bm = -INFINITY;
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       mref = mnew;
       thr = mnew + kRescaleG;
     }
-    u32x4 pf;
+    u32x2 pf;
     {
       float pw[4];
 #pragma unroll
@@ -372,15 +379,21 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
         lsum += pw[e];
         if (col >= 8) pw[e] = f16_lo(pw[e]);
       }
-      pf = u32x4{pack_f16(pw[0], pw[1]), pack_f16(pw[2], pw[3]), 0u, 0u};
+      pf = u32x2{pack_f16(pw[0], pw[1]), pack_f16(pw[2], pw[3])};
     }
-    // ---- output: values of tokens 4 jr .. + 3 at coordinate 16 ct + col (zero past the row)
+    // ---- output: values of tokens 4 jr .. + 3; tile ct holds coordinate
+    // 64 (ct / 4) + 4 col + ct % 4, so one 8-byte read per token serves four tiles
     u32x2 vw[8];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const uint8_t* vp = sb + 2048 + 256 * 4 * jr + 2 * (16 * ct + col);
-      vw[ct] = u32x2{(uint32_t)lds_read<uint16_t>(vp) | ((uint32_t)lds_read<uint16_t>(vp + 256) << 16),
-                     (uint32_t)lds_read<uint16_t>(vp + 512) | ((uint32_t)lds_read<uint16_t>(vp + 768) << 16)};
+    for (int u = 0; u < 2; ++u) {
+      uint2 r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = lds_read<uint2>(sb + VAL_AT + 256 * (4 * jr + e) + 128 * u + 8 * col);
+      // tile 4u + j: [v(t0, j), v(t1, j)], [v(t2, j), v(t3, j)]
+      vw[4 * u + 0] = u32x2{__builtin_amdgcn_perm(r[1].x, r[0].x, 0x05040100u), __builtin_amdgcn_perm(r[3].x, r[2].x, 0x05040100u)};
+      vw[4 * u + 1] = u32x2{__builtin_amdgcn_perm(r[1].x, r[0].x, 0x07060302u), __builtin_amdgcn_perm(r[3].x, r[2].x, 0x07060302u)};
+      vw[4 * u + 2] = u32x2{__builtin_amdgcn_perm(r[1].y, r[0].y, 0x05040100u), __builtin_amdgcn_perm(r[3].y, r[2].y, 0x05040100u)};
+      vw[4 * u + 3] = u32x2{__builtin_amdgcn_perm(r[1].y, r[0].y, 0x07060302u), __builtin_amdgcn_perm(r[3].y, r[2].y, 0x07060302u)};
     }
     if (nv < 16) {  // a partial tile: tokens past the row carry zeros (their weights are 0)
 #pragma unroll
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma_f16(pf, u32x4{vw[ct].x, vw[ct].y, 0u, 0u}, acc[ct]);
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma_f16_k16(pf, vw[ct], acc[ct]);
     if (s + D < n) {
       lds_wait();
       issue(s + D);
@@ -409,7 +422,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     for (int e = 0; e < 4; ++e) {
       float o0, o1;
       pair32(acc[ct][e], o0, o1);
-      if (jr < 2) po[(4 * jr + e) * 128 + 16 * ct + col] = o0 + o1;
+      if (jr < 2) po[(4 * jr + e) * 128 + 64 * (ct >> 2) + 4 * col + (ct & 3)] = o0 + o1;
     }
   if (lane < 8) {
     part_m[wv][lane] = mref;

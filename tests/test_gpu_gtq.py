@@ -162,3 +162,33 @@ def test_sections_are_the_oracle_splits():
                 else:
                     assert row_rel_err(po[s, b, h], ro[s, b, h]) <= RTOL
                     assert abs(pl[s, b, h] - rl[s, b, h]) <= LSE_ATOL + LSE_RTOL * abs(rl[s, b, h])
+
+
+# explicit allocations per KV head: one group (4 k-blocks), two groups of 64 (4 blocks),
+# four groups with odd-sized tails (7 blocks), and three groups (5 blocks)
+PATTERNS = [
+    [3] * 64,
+    [2] * 32 + [4] * 32,
+    [1] * 3 + [2] * 20 + [3] * 20 + [4] * 21,
+    [4, 1] * 8 + [3] * 48,
+]
+
+
+def test_allocation_shapes():
+    lens = [300, 45]
+    w, inp, _, _ = case(hq=16, hkv=4, lens=lens)
+    bits = np.array(PATTERNS, dtype=np.int32)
+    enc = [bg.head_encoders(bits[h], inp["gauss"][h].astype(np.float64)) for h in range(4)]
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    assert [keys.n_groups(h) for h in range(4)] == [1, 2, 4, 3]
+    oc, on, _ = oracle_keys(w, inp, enc)
+    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for n_splits in (1, 3):
+        res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(lens), scale=w.scale,
+                               n_splits=n_splits)
+        if n_splits > 1:
+            res = tq.merge_splits(None, *res)
+        torch.cuda.synchronize()
+        (ro, rl), _ = oracle_attention(w, inp, enc, oc, on, lens)
+        check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, lens)
