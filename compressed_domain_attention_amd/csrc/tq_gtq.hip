@@ -43,14 +43,15 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
 }
 
 // ---------------------------------------------------------------------------------------
-// Key encoding.  One workgroup per (64-token tile, KV head, sequence) stages the head's
-// encoder and rotations in LDS; each wave encodes one token at a time: lane l holds
+// Key encoding.  One workgroup per (512-token chunk, KV head, sequence) stages the head's
+// encoder and rotations in LDS once; each wave encodes one token at a time: lane l holds
 // group-order positions 2l and 2l + 1 (always in one group: groups start at even positions
 // and have even sizes).
+constexpr int kQuantTokens = 512;
 template <bool XF16>
 __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a) {
-  __shared__ float rot[TQ_GTQ_ROTATION_FLOATS];
-  __shared__ float ubuf[4][128];
+  __shared__ __attribute__((aligned(16))) float rot[TQ_GTQ_ROTATION_FLOATS];
+  __shared__ __attribute__((aligned(16))) float ubuf[4][128];
   __shared__ tq_gtq_head hd;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
   const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
   const int nb = (1 << hd.width[g]) - 1;
   const size_t stream = (size_t)b * a.n_kv_heads + h;
-  for (int t = wv; t < 64; t += 4) {
-    const int i = tile * 64 + t;
+  for (int t = wv; t < kQuantTokens; t += 4) {
+    const int i = tile * kQuantTokens + t;
     if (i >= a.n_new) break;
     const size_t xrow = (stream * a.n_new + i) * 128;
     float x0, x1;
@@ -90,13 +91,20 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // y = Q^T u for this lane's two positions of its group
-    float y0 = 0.f, y1 = 0.f;
+    // (two rows per step into two sums each, so that the LDS reads of a step overlap; the
+    // group's dimension is even)
+    float y0 = 0.f, y1 = 0.f, z0 = 0.f, z1 = 0.f;
     const float* q0 = rot + off + (j0 - st);
-    for (int r = 0; r < n; ++r) {
-      const float u = ubuf[wv][st + r];
-      y0 = fmaf(q0[r * n], u, y0);
-      y1 = fmaf(q0[r * n + 1], u, y1);
+    for (int r = 0; r < n; r += 2) {
+      const float2 u = *(const float2*)&ubuf[wv][st + r];
+      const float2 qa = *(const float2*)&q0[r * n], qb = *(const float2*)&q0[(r + 1) * n];
+      y0 = fmaf(qa.x, u.x, y0);
+      y1 = fmaf(qa.y, u.x, y1);
+      z0 = fmaf(qb.x, u.y, z0);
+      z1 = fmaf(qb.y, u.y, z1);
     }
+    y0 += z0;
+    y1 += z1;
     uint32_t c0 = 0, c1 = 0;
     for (int k = 0; k < nb; ++k) {  // compare-count against the group's boundaries
       c0 += y0 > hd.boundary[g][k];
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 }  // namespace
 
 hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream) {
-  const dim3 grid((a.n_new + 63) / 64, a.n_kv_heads, batch), block(256);
+  const dim3 grid((a.n_new + kQuantTokens - 1) / kQuantTokens, a.n_kv_heads, batch), block(256);
   if (x_f16) hipLaunchKernelGGL(gtq_quantize_kernel<true>, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(gtq_quantize_kernel<false>, grid, block, 0, stream, a);
   return hipGetLastError();
