@@ -533,7 +533,9 @@ def zip_measured_traffic(workload, n_splits):
 
 def gtq_setup(w, inp, dev):
     """Block-GTQ keys from the workload's calibration prefix (energies, allocation and
-    encoders in the library), the prompt's keys encoded on the GPU (timed), fp16 values."""
+    encoders in the library), the prompt's keys encoded on the GPU (timed), fp16 values.
+    The last token (slot T - 1) is the step's new one: its key and value are returned for
+    the step to append."""
     import torch
 
     import compressed_domain_attention_amd as tq
@@ -544,30 +546,33 @@ def gtq_setup(w, inp, dev):
     codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device=dev)
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device=dev)
     x = torch.from_numpy(inp["k"]).to(dev)
-    tq.gtq_quantize_keys(keys, x[:, :, :1].contiguous(), codes, norms)  # loads the kernel before timing
+    prompt = x[:, :, :T - 1].contiguous()
+    tq.gtq_quantize_keys(keys, prompt[:, :, :1].contiguous(), codes, norms)  # loads the kernel before timing
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    tq.gtq_quantize_keys(keys, x, codes, norms)
+    tq.gtq_quantize_keys(keys, prompt, codes, norms)
     e1.record()
     torch.cuda.synchronize()
     v = torch.from_numpy(inp["v"]).to(dev)
     q = torch.from_numpy(inp["q"]).to(dev)
-    return keys, bits, codes, norms, v, q, e0.elapsed_time(e1)
+    k_new, v_new = x[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous()
+    return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1)
 
 
 GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
 
 
 def run_gtq(w, inp, steps, warmup, n_splits, check=True):
-    """The step on Block-GTQ keys with fp16 values: one attention launch (sections), merged
-    without rotation."""
+    """The step on Block-GTQ keys with fp16 values: one launch that appends the new token
+    (key encoded, value written at slot T - 1) and attends over the T tokens in sections,
+    then the merge without rotation."""
     import torch
 
     import compressed_domain_attention_amd as tq
 
     dev = torch.device("cuda:0")
-    keys, bits, codes, norms, v, q, enc_ms = gtq_setup(w, inp, dev)
+    keys, bits, codes, norms, v, q, k_new, v_new, enc_ms = gtq_setup(w, inp, dev)
     cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
     reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
     sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
@@ -582,9 +587,11 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
     def attend(i):
         c, n, vv = sets[i % reps]
         if S == 1:
-            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, out=out, lse=lse)
+            tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale, out=out,
+                                    lse=lse)
         else:
-            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=S, part_o=po, part_lse=pl)
+            tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale, n_splits=S,
+                                    part_o=po, part_lse=pl)
 
     def step(i):
         attend(i)
@@ -676,7 +683,7 @@ def gtq_kernel_hash():
 
 def gtq_counter_run(w, inp, n_splits, launches=24):
     """rocprofv3 --pmc dispatches for Block-GTQ: the calibration copies, then `launches`
-    attention launches over the cache replicas, as run_gtq times them."""
+    append + attention launches over the cache replicas, as run_gtq times them."""
     import ctypes
 
     import torch
@@ -694,7 +701,7 @@ def gtq_counter_run(w, inp, n_splits, launches=24):
         assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
     torch.cuda.synchronize()
     del src, dst
-    keys, bits, codes, norms, v, q, _ = gtq_setup(w, inp, dev)
+    keys, bits, codes, norms, v, q, k_new, v_new, _ = gtq_setup(w, inp, dev)
     cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
     reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
     sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
@@ -705,10 +712,10 @@ def gtq_counter_run(w, inp, n_splits, launches=24):
     for i in range(launches):
         c, n, vv = sets[i % reps]
         if n_splits == 1:
-            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, out=out)
+            tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale, out=out)
         else:
-            tq.gtq_attention(keys, c, n, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=n_splits, part_o=po,
-                             part_lse=pl)
+            tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale,
+                                    n_splits=n_splits, part_o=po, part_lse=pl)
     torch.cuda.synchronize()
     log("counter run: 3 copies of %d bytes, %d Block-GTQ attention launches over %d replicas" % (
         COPY_BYTES, launches, reps))
@@ -1065,8 +1072,8 @@ def main():
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                        "seq_len": w.seq_len, "keys": "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
                        "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
-                       "step": "attention over encoded keys and fp16 values" +
-                               (", then merge" if n_splits > 1 else ""),
+                       "step": "append the new token (key encoded, fp16 value) and attend over encoded keys "
+                               "and fp16 values in one launch" + (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": gtq_measured_traffic(w.name, n_splits),

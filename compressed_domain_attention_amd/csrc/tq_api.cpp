@@ -365,11 +365,11 @@ extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float*
   return from_hip(tq::launch_gtq_quantize(a, x_dtype == TQ_F16, batch, (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
-                                      const float* norms, const void* v, int32_t capacity, int32_t batch,
-                                      int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
-                                      const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
-                                      float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
+                                    const float* norms, const void* v, int32_t capacity, int32_t batch,
+                                    int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
+                                    const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
+                                    float* out, float* lse_out, float* part_o, float* part_lse, tq::GtqAttnArgs& a) {
   if (heads == nullptr || rotations == nullptr || codes == nullptr || norms == nullptr || v == nullptr || q == nullptr)
     return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_F16) return TQ_EINVAL;
@@ -383,7 +383,6 @@ extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rot
   const int hps = group < 8 ? group : 8;
   const int slices = (group + hps - 1) / hps;
   if ((int64_t)batch * n_kv_heads * n_splits * slices > 0x7FFFFFFFll) return TQ_EINVAL;
-  tq::GtqAttnArgs a;
   std::memset(&a, 0, sizeof(a));
   a.heads = heads;
   a.rotations = rotations;
@@ -406,5 +405,47 @@ extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rot
   a.n_splits = n_splits;
   a.capacity = capacity;
   a.scale_log2 = scale * 1.4426950408889634f;
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
+                                      const float* norms, const void* v, int32_t capacity, int32_t batch,
+                                      int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
+                                      const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
+                                      float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+  tq::GtqAttnArgs a;
+  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+                                          n_q_heads, seq_lens, max_len, scale, n_splits, out, lse_out, part_o,
+                                          part_lse, a);
+  if (st != TQ_OK) return st;
+  return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes,
+                                             float* norms, void* v, int32_t capacity, int32_t batch,
+                                             int32_t n_kv_heads, const void* k_new, const void* v_new,
+                                             tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
+                                             const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
+                                             int32_t n_splits, float* out, float* lse_out, float* part_o,
+                                             float* part_lse, void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (pos0 < 0 || (pos != nullptr && max_pos < 0)) return TQ_EINVAL;
+  // rows end at their new token: length pos[b] + 1, or pos0 + 1 for every row
+  const int64_t max_len = (int64_t)(pos ? max_pos : pos0) + 1;
+  if (max_len > capacity) return TQ_ECAPACITY;
+  tq::GtqAttnArgs a;
+  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+                                          n_q_heads, pos, (int32_t)max_len, scale, n_splits, out, lse_out, part_o,
+                                          part_lse, a);
+  if (st != TQ_OK) return st;
+  a.append = 1;
+  a.x_f16 = x_dtype == TQ_F16;
+  a.len_bias = pos ? 1 : 0;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.w_codes = codes;
+  a.w_norms = norms;
+  a.w_v = v;
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }

@@ -42,6 +42,59 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
   for (int i = threadIdx.x; i < words; i += blockDim.x) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
 }
 
+// Encodes one key x[128] (fp16 or fp32) into its record: group norms, the normalised group
+// vector through the wave's 128 floats of LDS (ubuf), y = Q^T u for lane l's group-order
+// positions 2l and 2l + 1 (always in one group: groups start at even positions and have
+// even sizes), compare-count, one code byte per lane and one norm per group.  rot: the
+// head's rotations, in LDS or global memory.  Every lane of the wave takes part.
+template <bool XF16>
+__device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* rot, const void* x, float* ubuf,
+                                           uint8_t* code_rec, float* norm_rec, int lane) {
+  const int j0 = 2 * lane;
+  const int g = group_of(hd, j0);
+  const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
+  const int nb = (1 << hd.width[g]) - 1;
+  float x0, x1;
+  if (XF16) {
+    x0 = (float)((const _Float16*)x)[hd.coord[j0]];
+    x1 = (float)((const _Float16*)x)[hd.coord[j0 + 1]];
+  } else {
+    x0 = ((const float*)x)[hd.coord[j0]];
+    x1 = ((const float*)x)[hd.coord[j0 + 1]];
+  }
+  const float sq = x0 * x0 + x1 * x1;
+  float ss[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ss[k] = wave_sum(g == k ? sq : 0.f);
+  const float nu = sqrtf(g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3]);
+  ubuf[j0] = nu > 0.f ? x0 / nu : 0.f;
+  ubuf[j0 + 1] = nu > 0.f ? x1 / nu : 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // y = Q^T u for this lane's two positions of its group (two rows per step into two sums
+  // each, so that the reads of a step overlap; the group's dimension is even)
+  float y0 = 0.f, y1 = 0.f, z0 = 0.f, z1 = 0.f;
+  const float* q0 = rot + off + (j0 - st);
+  for (int r = 0; r < n; r += 2) {
+    const float2 u = *(const float2*)&ubuf[st + r];
+    const float2 qa = *(const float2*)&q0[r * n], qb = *(const float2*)&q0[(r + 1) * n];
+    y0 = fmaf(qa.x, u.x, y0);
+    y1 = fmaf(qa.y, u.x, y1);
+    z0 = fmaf(qb.x, u.y, z0);
+    z1 = fmaf(qb.y, u.y, z1);
+  }
+  y0 += z0;
+  y1 += z1;
+  uint32_t c0 = 0, c1 = 0;
+  for (int k = 0; k < nb; ++k) {  // compare-count against the group's boundaries
+    c0 += y0 > hd.boundary[g][k];
+    c1 += y1 > hd.boundary[g][k];
+  }
+  code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
+  if (lane < 4) norm_rec[lane] = lane < hd.n_groups ? sqrtf(ss[lane & 3]) : 0.f;
+}
+
 // ---------------------------------------------------------------------------------------
 // Key encoding.  One workgroup per (512-token chunk, KV head, sequence) stages the head's
 // encoder and rotations in LDS once; each wave encodes one token at a time: lane l holds
@@ -63,56 +116,13 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
   for (int i = tid; i < used; i += 256) rot[i] = grot[i];
   __syncthreads();
 
-  const int j0 = 2 * lane;
-  const int g = group_of(hd, j0);
-  const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
-  const int nb = (1 << hd.width[g]) - 1;
   const size_t stream = (size_t)b * a.n_kv_heads + h;
   for (int t = wv; t < kQuantTokens; t += 4) {
     const int i = tile * kQuantTokens + t;
     if (i >= a.n_new) break;
-    const size_t xrow = (stream * a.n_new + i) * 128;
-    float x0, x1;
-    if (XF16) {
-      x0 = (float)((const _Float16*)a.x)[xrow + hd.coord[j0]];
-      x1 = (float)((const _Float16*)a.x)[xrow + hd.coord[j0 + 1]];
-    } else {
-      x0 = ((const float*)a.x)[xrow + hd.coord[j0]];
-      x1 = ((const float*)a.x)[xrow + hd.coord[j0 + 1]];
-    }
-    const float sq = x0 * x0 + x1 * x1;
-    float ss[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ss[k] = wave_sum(g == k ? sq : 0.f);
-    const float nu = sqrtf(g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3]);
-    ubuf[wv][j0] = nu > 0.f ? x0 / nu : 0.f;
-    ubuf[wv][j0 + 1] = nu > 0.f ? x1 / nu : 0.f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // y = Q^T u for this lane's two positions of its group
-    // (two rows per step into two sums each, so that the LDS reads of a step overlap; the
-    // group's dimension is even)
-    float y0 = 0.f, y1 = 0.f, z0 = 0.f, z1 = 0.f;
-    const float* q0 = rot + off + (j0 - st);
-    for (int r = 0; r < n; r += 2) {
-      const float2 u = *(const float2*)&ubuf[wv][st + r];
-      const float2 qa = *(const float2*)&q0[r * n], qb = *(const float2*)&q0[(r + 1) * n];
-      y0 = fmaf(qa.x, u.x, y0);
-      y1 = fmaf(qa.y, u.x, y1);
-      z0 = fmaf(qb.x, u.y, z0);
-      z1 = fmaf(qb.y, u.y, z1);
-    }
-    y0 += z0;
-    y1 += z1;
-    uint32_t c0 = 0, c1 = 0;
-    for (int k = 0; k < nb; ++k) {  // compare-count against the group's boundaries
-      c0 += y0 > hd.boundary[g][k];
-      c1 += y1 > hd.boundary[g][k];
-    }
     const size_t rec = stream * a.capacity + a.pos0 + i;
-    a.codes[rec * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
-    if (lane < 4) a.norms[rec * 4 + lane] = lane < hd.n_groups ? sqrtf(ss[lane & 3]) : 0.f;
+    encode_key<XF16>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4), ubuf[wv],
+                     a.codes + rec * 64, a.norms + rec * 4, lane);
     // the next token's writes to ubuf follow this token's reads in program order
     __builtin_amdgcn_wave_barrier();
   }
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   const int b = unit / (a.n_splits * a.n_kv_heads);
   const int h0 = kv * a.group_size + slice * a.heads_per_slice;
   const int hs = min(a.heads_per_slice, a.group_size - slice * a.heads_per_slice);
-  const int T = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_len)) : a.max_len;
+  const int T = a.seq_lens ? max(0, min(a.seq_lens[b] + a.len_bias, a.max_len)) : a.max_len;
   const int C = (T + a.n_splits - 1) / a.n_splits;
   const int lo = min(T, split * C), hi = min(T, lo + C);
   const int ntiles = lo < hi ? (hi - lo + 15) >> 4 : 0;
@@ -226,6 +236,28 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   // prologue: the head's encoder, the k-block plan, pair tables, the rotated query
   stage_head(&hd, (const tq_gtq_head*)a.heads + kv);
   __syncthreads();
+  // Fused append: if this workgroup's section holds the row's new slot, wave 0 writes that
+  // token's key record and value row (reading the rotations from global memory, with its
+  // own ring space as scratch) while the other waves build the tables; the barriers below
+  // order its stores before any copy of the cache.  Other sections do not read the slot.
+  if (a.append && wv == 0) {
+    const int p = a.seq_lens ? a.seq_lens[b] : a.max_len - 1;  // the new slot: rows end at it
+    if (p >= 0 && p < a.max_len && p >= lo && p < hi) {
+      const size_t st = (size_t)b * a.n_kv_heads + kv, rec = st * a.capacity + p;
+      const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
+      _Float16* vd = (_Float16*)a.w_v + rec * 128;
+      if (a.x_f16) {
+        encode_key<true>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
+                         a.w_norms + rec * 4, lane);
+        ((uint32_t*)vd)[lane] = ((const uint32_t*)a.v_new)[st * 64 + lane];
+      } else {
+        encode_key<false>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
+                          a.w_norms + rec * 4, lane);
+        const float2 x = ((const float2*)a.v_new)[st * 64 + lane];
+        ((uint32_t*)vd)[lane] = pack_f16(x.x, x.y);
+      }
+    }
+  }
   if (tid == 0) {
     int nk = 0;
     for (int g = 0; g < min(hd.n_groups, TQ_GTQ_MAX_GROUPS); ++g)

@@ -162,6 +162,17 @@ struct GtqAttnArgs {
   int32_t n_splits;
   int32_t capacity;
   float scale_log2;
+  // Fused append (append != 0): each row's new key is encoded and its value row written at
+  // slot seq_lens[b] (or max_len - 1 when seq_lens is NULL) before the section holding that
+  // slot reads the cache; rows then end there (len_bias = 1: length seq_lens[b] + 1).
+  int32_t append;
+  int32_t x_f16;            // k_new and v_new are fp16 (else fp32; values stored as fp16)
+  int32_t len_bias;
+  const void* k_new;        // [batch][n_kv_heads][128]
+  const void* v_new;        // [batch][n_kv_heads][128]
+  uint8_t* w_codes;         // the cache again, writable (append only)
+  float* w_norms;
+  void* w_v;
 };
 
 struct MergeArgs {

@@ -378,12 +378,36 @@ tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations,
  *   out, lse_out: n_splits == 1: fp32 [batch][n_q_heads][128], natural-log lse (or NULL).
  *   part_o, part_lse: n_splits > 1: original-domain section partials for tq_merge_splits
  *      with rot == NULL.
- * Scores and sums in fp32.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or
- * scale; TQ_ECAPACITY for max_len > capacity. */
+ * Scores and weighted sums are fp16 matrix products of hi + lo parts (key levels, query,
+ * weights) with fp32 accumulation.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts
+ * or scale; TQ_ECAPACITY for max_len > capacity or capacity > 2^24. */
 tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes, const float* norms,
                            const void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,
                            tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
                            int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
+
+/* One decode step with its new token over Block-GTQ keys and fp16 values: the same cache
+ * contents and outputs, bit for bit, as tq_gtq_quantize_keys of the new key at its slot and
+ * a write of the new value row (converted to fp16 when x_dtype is TQ_F32), followed by
+ * tq_gtq_attention over rows of length pos[b] + 1 (pos0 + 1 when pos is NULL) with max_len
+ * = max_pos + 1 (pos0 + 1) ("RoPE-Aware Bit Allocation ...", packed-cache paragraph: keys
+ * are encoded on write and the decode kernel reads the packed cache).  One launch: the
+ * workgroups whose key-axis section holds a row's new slot write that token before reading
+ * the cache.
+ *   codes, norms, v: the cache, as tq_gtq_attention's, written at the new slots.
+ *   k_new, v_new: device [batch][n_kv_heads][128] of x_dtype (TQ_F32 or TQ_F16).
+ *   pos: device int32 [batch], each row's new slot, or NULL to use pos0 for every row;
+ *      max_pos: host upper bound on pos[] (ignored when pos is NULL).  A device slot outside
+ *      [0, max_pos] writes nothing and its row length is clamped as seq_lens' are.
+ * Other arguments as tq_gtq_attention.  Errors: those of tq_gtq_attention; TQ_EINVAL for
+ * null k_new or v_new, a bad x_dtype or a negative pos0 or max_pos; TQ_ECAPACITY when
+ * max_pos + 1 (pos0 + 1) > capacity.  Nothing is written when a check fails. */
+tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes, float* norms,
+                                  void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* k_new,
+                                  const void* v_new, tq_dtype x_dtype, const int32_t* pos, int32_t pos0,
+                                  int32_t max_pos, const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
+                                  int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

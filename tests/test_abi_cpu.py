@@ -374,6 +374,28 @@ def test_gtq_call_validation(lib):
     assert call(max_len=65) == TQ_ECAPACITY
 
 
+def test_gtq_append_call_validation(lib):
+    ap = lib.tq_gtq_append_attention
+
+    def call(**kw):
+        a = dict(heads=FAKE, rot=FAKE, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, kn=FAKE, vn=FAKE, xd=1,
+                 pos=None, pos0=10, max_pos=0, q=FAKE, qd=1, hq=8, scale=0.1, splits=1, out=FAKE, part=FAKE)
+        a.update(kw)
+        return ap(a["heads"], a["rot"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["kn"],
+                  a["vn"], a["xd"], a["pos"], a["pos0"], a["max_pos"], a["q"], a["qd"], a["hq"], a["scale"],
+                  a["splits"], a["out"], None, a["part"], a["part"], None)
+    for k in ("heads", "rot", "codes", "norms", "v", "q", "kn", "vn"):
+        assert call(**{k: None}) == TQ_EINVAL, k
+    assert call(xd=2) == TQ_EINVAL             # bf16 new tokens
+    assert call(qd=2) == TQ_EINVAL
+    assert call(pos0=-1) == TQ_EINVAL
+    assert call(pos=FAKE, max_pos=-1) == TQ_EINVAL
+    assert call(hq=7) == TQ_EINVAL
+    assert call(splits=3, part=None) == TQ_EINVAL
+    assert call(pos0=64) == TQ_ECAPACITY       # the new slot past the capacity
+    assert call(pos=FAKE, max_pos=64) == TQ_ECAPACITY
+
+
 def test_product_path_has_no_cpu_fallback():
     # the binding must not reach the oracle or any CPU computation
     src = open(os.path.join(ROOT, "compressed_domain_attention_amd", "__init__.py")).read()

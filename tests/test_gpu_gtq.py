@@ -192,3 +192,75 @@ def test_allocation_shapes():
         torch.cuda.synchronize()
         (ro, rl), _ = oracle_attention(w, inp, enc, oc, on, lens)
         check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, lens)
+
+
+def device_cache(w, inp, keys):
+    codes = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 64), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 4), dtype=torch.float32, device="cuda")
+    tq.gtq_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, pos0=0)
+    v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
+    return codes, norms, v
+
+
+def same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_append_step_equals_encode_then_attend(n_splits):
+    # one launch (encode the new key and write its value at slot P, then attend over P + 1
+    # tokens) against the two calls it stands for: bit for bit, cache and outputs
+    lens = [320, 320, 320]
+    w, inp, bits, enc = case(lens=lens)
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    P = 250
+    rng = np.random.default_rng(7)
+    k_new = torch.from_numpy((rng.standard_normal((3, w.n_kv_heads, 128)) * 3).astype(np.float16)).cuda()
+    v_new = torch.from_numpy(rng.standard_normal((3, w.n_kv_heads, 128)).astype(np.float16)).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
+    a = device_cache(w, inp, keys)
+    b = tuple(t.clone() for t in a)
+    res_a = tq.gtq_append_attention(keys, *a, k_new, v_new, q, pos0=P, scale=w.scale, n_splits=n_splits)
+    tq.gtq_quantize_keys(keys, k_new[:, :, None, :].contiguous(), b[0], b[1], pos0=P)
+    b[2][:, :, P] = v_new
+    res_b = tq.gtq_attention(keys, *b, q, max_len=P + 1, scale=w.scale, n_splits=n_splits)
+    torch.cuda.synchronize()
+    assert same(a, b)
+    assert same(res_a, res_b)
+
+
+def test_append_step_per_row_slots():
+    # device positions per row (a row of one token, a slot on a section boundary), fp32 new
+    # tokens, and the new records against the oracle's encoding
+    lens = [320, 320, 320, 320]
+    w, inp, bits, enc = case(lens=lens)
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    pos = [299, 0, 100, 33]
+    rng = np.random.default_rng(8)
+    kn = (rng.standard_normal((4, w.n_kv_heads, 128)) * 2).astype(np.float32)
+    vn = rng.standard_normal((4, w.n_kv_heads, 128)).astype(np.float32)
+    k_new, v_new = torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float32)).cuda()
+    pos_d = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    a = device_cache(w, inp, keys)
+    b = tuple(t.clone() for t in a)
+    res_a = tq.gtq_append_attention(keys, *a, k_new, v_new, q, pos=pos_d, scale=w.scale, n_splits=3)
+    for r, p in enumerate(pos):
+        tq.gtq_quantize_keys(keys, k_new[r:r + 1, :, None, :].contiguous(), b[0][r:r + 1], b[1][r:r + 1], pos0=p)
+        b[2][r, :, p] = v_new[r].half()
+    res_b = tq.gtq_attention(keys, *b, q, seq_lens=pos_d + 1, max_len=max(pos) + 1, scale=w.scale, n_splits=3)
+    torch.cuda.synchronize()
+    assert same(a, b)
+    assert same(res_a, res_b)
+    codes = bg.unpack_codes(a[0].cpu().numpy().reshape(-1, 64)).reshape(4, w.n_kv_heads, w.seq_len, 128)
+    norms = a[1].cpu().numpy()
+    for r, p in enumerate(pos):
+        for h in range(w.n_kv_heads):
+            oc, on, oy = bg.quantize_keys(kn[r, h][None].astype(np.float64), enc[h])
+            bad = np.nonzero(codes[r, h, p] != oc[0])[0]
+            assert len(bad) <= 2
+            ends = np.cumsum([len(e[1]) for e in enc[h]])
+            for j in bad:
+                m = enc[h][int(np.searchsorted(ends, j, side="right"))][4]
+                assert np.min(np.abs(m - oy[0, j])) < BOUNDARY_EPS
+            assert np.allclose(norms[r, h, p, :len(enc[h])], on[0], rtol=1e-6)
