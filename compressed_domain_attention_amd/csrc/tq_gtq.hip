@@ -140,16 +140,19 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
 // folded in) and laid out in k-blocks of 32 positions that each belong to one group (a
 // group of n positions takes ceil(n/32) blocks; query positions past the group are zero,
 // so the codes of the next group that share the block contribute nothing), divided by the
-// group codebook's fp16 scale s and split into fp16 hi + lo columns.  A key operand is 8
-// codes of one token decoded through the block's table of the fp16 hi and lo parts of s c
-// for the two codes of a byte (two products per block, so scores keep fp32-level
-// accuracy); each block's partial dot is multiplied by the token's group norm.  Tables sit
-// at fixed LDS offsets per block and the norms group-major, so the unrolled block loop has
-// no branch, mask or per-lane index beyond the code bytes.  The output product,
-// the lazy softmax and the merge of waves are those of the codec kernel; the output
-// product is a 16x16x16 one: weights as fp16 hi + lo rows straight from the lanes' score
-// registers (k slots 4j .. 4j+3 = the lane's tokens), values 4 tokens of one coordinate
-// per lane, each read into one half of a register.
+// group codebook's fp16 scale s and split into fp16 hi + lo columns.  The block's table
+// holds, per code byte, the fp16 hi parts of s c for its two codes and then their lo
+// parts, so a key operand is [hi pair, lo pair] of two bytes (four codes of one token)
+// straight from two table reads, against a query operand that holds each position pair
+// twice; two products cover a lane's 8 codes of the block with both key parts (scores
+// keep fp32-level accuracy).  Each block's partial dot is multiplied by the token's group
+// norm.  Tables sit at fixed LDS offsets per block and the norms group-major, so the
+// unrolled block loop has no branch, mask or per-lane index beyond the code bytes.  The
+// lazy softmax and the merge of waves are those of the codec kernel; the output product
+// is a 16x16x16 one: weights as fp16 hi + lo rows straight from the lanes' score registers
+// (k slots 4j .. 4j+3 = the lane's tokens), values of 4 tokens per lane read 8 bytes (4
+// coordinates) at a time and paired by byte permutes, so tile ct holds coordinate
+// 64 (ct / 4) + 4 col + ct % 4.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
   __shared__ tq_gtq_head hd;
-  __shared__ int kbg[kMaxKb + 1], kbm[kMaxKb + 1], nkb_s;
+  __shared__ int kbg[kMaxKb], kbm[kMaxKb], nkb_s;  // k-block -> group, block within it
   __shared__ float part_m[NW][8], part_l[NW][8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -265,7 +268,6 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
         kbg[nk] = g;
         kbm[nk] = m;
       }
-    kbg[nk] = -1;
     nkb_s = nk;
   }
   __syncthreads();

@@ -1,0 +1,139 @@
+"""Parity at the benchmark sizes, in the launch configuration bench.py times, on sampled outputs.
+
+Each test builds one benchmark workload at its full size (isoquant32k: B=8, T=32768, TQ3 with
+SO(4); zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys),
+runs the step bench.py times (append of slot T-1 fused into the attention launch where the
+format has one, the same sections, then the merge) and compares every query head of three
+(sequence, KV head) units with the oracle, which encodes and attends over those units alone.
+Bars: 2e-3 per row for the packed cache (fp16 weights, the tolerance of the other packed-cache
+parity tests), 1e-4 for the lossless codec and for Block-GTQ (hi + lo fp16 operands).
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_domain_attention_amd as tq
+import workloads
+from helpers import OUT_RTOL, row_rel_err
+from oracle import attention, blockgtq as bg, codebook, quant, zipcodec as zc
+
+pytestmark = pytest.mark.gpu
+
+EXACT_RTOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.library()
+
+
+def units(w):
+    return [(0, 0), (w.batch // 2, w.n_kv_heads // 2 + 1), (w.batch - 1, w.n_kv_heads - 1)]
+
+
+def announce(name, w):
+    print("full-size case %s: B=%d Hq=%d Hkv=%d T=%d S=%d" % (name, w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len,
+                                                              w.n_splits), flush=True)
+
+
+def test_isoquant32k_step():
+    w = workloads.WORKLOADS["isoquant32k"]
+    announce(w.name, w)
+    inp = workloads.generate(w, 0)
+    T, S = w.seq_len, w.n_splits
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, torch.from_numpy(inp["so4"]).cuda())
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    kc = tq.PackedCache(w.batch, w.n_kv_heads, T, w.bits_k, w.group, tq.TQ_KEYS)
+    vc = tq.PackedCache(w.batch, w.n_kv_heads, T, w.bits_v, w.group, tq.TQ_VALUES)
+    tq.quantize_append(rot, kc, kx[:, :, :T - 1].contiguous())
+    tq.quantize_append(rot, vc, vx[:, :, :T - 1].contiguous())
+    q = torch.from_numpy(inp["q"]).cuda()
+    po, pl = tq.append_decode_attention(rot, kc, vc, kx[:, :, T - 1:].contiguous(), vx[:, :, T - 1:].contiguous(), q,
+                                        pos0=T - 1, scale=w.scale, n_splits=S)
+    out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    del kx, vx, kc, vc
+    ck, mk = codebook.lloyd_max(w.bits_k, w.group)
+    cv, mv = codebook.lloyd_max(w.bits_v, w.group)
+    worst, t0 = 0.0, time.perf_counter()
+    for b, kv in units(w):
+        so, sg = inp["so4"][kv], inp["signs"][kv]
+        ki, kn, _ = quant.quantize(inp["k"][b, kv].astype(np.float64), sg, w.group, ck, mk, so)
+        vi, vn, _ = quant.quantize(inp["v"][b, kv].astype(np.float64), sg, w.group, cv, mv, so)
+        kd = quant.dequantize(ki, kn, sg, w.group, ck, so)
+        vd = quant.dequantize(vi, vn, sg, w.group, cv, so)
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            worst = max(worst, float(row_rel_err(out[b, h], ref)))
+    print("worst row error %.2e (oracle %.1fs)" % (worst, time.perf_counter() - t0), flush=True)
+    assert worst <= OUT_RTOL
+
+
+def test_zipfusion8k_step():
+    w = workloads.WORKLOADS["zipfusion8k"]
+    announce(w.name, w)
+    inp = workloads.generate(w, 0)
+    T, pages = w.seq_len, w.seq_len // 16
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    stores, tails = [], []
+    for role, rc in (("k", tq.TQ_KEYS), ("v", tq.TQ_VALUES)):
+        s, m = tq.zip_store(w.batch, w.n_kv_heads, pages)
+        tq.zip_compress(bf16(inp[role][:, :, :16 * pages]), s, m, rc, n_pages=pages)
+        t = torch.zeros((w.batch, w.n_kv_heads, 16, 128), dtype=torch.bfloat16, device="cuda")
+        t[:, :, :T - 16 * pages] = bf16(inp[role][:, :, 16 * pages:T])
+        stores += [s, m]
+        tails.append(t)
+    res = tq.zip_attention(*stores, *tails, bf16(inp["q"]), max_len=T, scale=w.scale, n_splits=w.n_splits)
+    if w.n_splits > 1:
+        res = tq.merge_splits(None, *res)
+    torch.cuda.synchronize()
+    out = res[0].cpu().numpy()
+    worst = 0.0
+    for b, kv in units(w):
+        kf, vf = zc.bf16_to_float(inp["k"][b, kv, :T]), zc.bf16_to_float(inp["v"][b, kv, :T])
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref, _ = attention.softmax_attend(zc.bf16_to_float(inp["q"][b, h]), kf, vf, w.scale)
+            worst = max(worst, float(row_rel_err(out[b, h], ref)))
+    print("worst row error %.2e" % worst, flush=True)
+    assert worst <= EXACT_RTOL
+
+
+def test_gtq32k_step():
+    w = workloads.WORKLOADS["gtq32k"]
+    announce(w.name, w)
+    inp = workloads.generate(w, 0)
+    T, S = w.seq_len, w.n_splits
+    energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
+    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device="cuda")
+    kx = torch.from_numpy(inp["k"]).cuda()
+    v = torch.from_numpy(inp["v"]).cuda()
+    tq.gtq_quantize_keys(keys, kx[:, :, :T - 1].contiguous(), codes, norms)
+    q = torch.from_numpy(inp["q"]).cuda()
+    po, pl = tq.gtq_append_attention(keys, codes, norms, v, kx[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous(),
+                                     q, pos0=T - 1, scale=w.scale, n_splits=S)
+    out, lse = tq.merge_splits(None, po, pl)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    worst = 0.0
+    for b, kv in units(w):
+        # the library's allocation is the oracle's (exact, checked on the CPU)
+        enc = bg.head_encoders(bits[kv], inp["gauss"][kv].astype(np.float64))
+        c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)
+        kd = bg.dequantize_keys(c, nrm, enc)
+        vd = inp["v"][b, kv].astype(np.float64)
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            worst = max(worst, float(row_rel_err(out[b, h], ref)))
+    print("worst row error %.2e" % worst, flush=True)
+    assert worst <= EXACT_RTOL
