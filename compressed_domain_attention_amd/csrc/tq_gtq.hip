@@ -183,6 +183,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   constexpr int NDMA = 6;
   constexpr int WAVE_LDS = D * STAGE;
   static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
+  static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
   constexpr int TAB_BYTES = kMaxKb * 256 * 8;
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
@@ -191,8 +192,8 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
   // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
+  __shared__ float qraw[8][128];  // the slice's query rows, original coordinates
   __shared__ tq_gtq_head hd;
-  __shared__ int kbg[kMaxKb], kbm[kMaxKb], nkb_s;  // k-block -> group, block within it
   __shared__ float part_m[NW][8], part_l[NW][8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -236,13 +237,19 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     }
   };
 
-  // prologue: the head's encoder, the k-block plan, pair tables, the rotated query
+  // prologue: the head's encoder and the slice's query rows (one round trip), then the
+  // k-block plan, the pair tables and the rotated query
   stage_head(&hd, (const tq_gtq_head*)a.heads + kv);
+  for (int i = tid; i < 8 * 128; i += 64 * NW) {
+    const int hh = i >> 7, c = i & 127;
+    const size_t qi = ((size_t)b * a.n_q_heads + h0 + hh) * 128 + c;
+    qraw[hh][c] = hh >= hs ? 0.f : QF16 ? (float)((const _Float16*)a.q)[qi] : ((const float*)a.q)[qi];
+  }
   __syncthreads();
   // Fused append: if this workgroup's section holds the row's new slot, wave 0 writes that
   // token's key record and value row (reading the rotations from global memory, with its
-  // own ring space as scratch) while the other waves build the tables; the barriers below
-  // order its stores before any copy of the cache.  Other sections do not read the slot.
+  // own ring space as scratch) while the other waves build the tables; the barrier below
+  // orders its stores before any copy of the cache.  Other sections do not read the slot.
   if (a.append && wv == 0) {
     const int p = a.seq_lens ? a.seq_lens[b] : a.max_len - 1;  // the new slot: rows end at it
     if (p >= 0 && p < a.max_len && p >= lo && p < hi) {
@@ -261,19 +268,20 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       }
     }
   }
-  if (tid == 0) {
-    int nk = 0;
-    for (int g = 0; g < min(hd.n_groups, TQ_GTQ_MAX_GROUPS); ++g)
-      for (int m = 0; m < (hd.dim[g] + 31) / 32 && nk < kMaxKb; ++m, ++nk) {
-        kbg[nk] = g;
-        kbm[nk] = m;
-      }
-    nkb_s = nk;
+  // The k-block plan, uniform and in registers: group g takes blocks cum[g] .. cum[g+1]-1
+  // (ceil(dim_g / 32) of them), so block kb belongs to the group whose range holds it.
+  int cum[TQ_GTQ_MAX_GROUPS + 1];
+  {
+    const int ng = min(__builtin_amdgcn_readfirstlane(hd.n_groups), TQ_GTQ_MAX_GROUPS);
+    cum[0] = 0;
+#pragma unroll
+    for (int g = 0; g < TQ_GTQ_MAX_GROUPS; ++g)
+      cum[g + 1] = cum[g] + (g < ng ? (__builtin_amdgcn_readfirstlane(hd.dim[g]) + 31) / 32 : 0);
   }
-  __syncthreads();
-  const int nkb = __builtin_amdgcn_readfirstlane(nkb_s);
+  const int nkb = min(cum[TQ_GTQ_MAX_GROUPS], kMaxKb);
+  auto group_of_block = [&](int kb) { return (kb >= cum[1]) + (kb >= cum[2]) + (kb >= cum[3]); };
   for (int i = tid; i < kMaxKb * 256; i += 64 * NW) {
-    const int kb = i >> 8, by = i & 255, g = kb < nkb ? kbg[kb] : 0;
+    const int kb = i >> 8, by = i & 255, g = kb < nkb ? group_of_block(kb) : 0;
     // codes past the codebook decode to 0
     const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
     const float sc = hd.f16_scale[g];
@@ -282,58 +290,57 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     ptab[kb][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
   }
   {
+    // q~_g = Q_g^T q_g: thread (j, k) takes group-order position j of heads k, k + NW/2, ..,
+    // which share the rotation column Q_g[:, j]
     const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
-    for (int i = tid; i < 8 * 128; i += 64 * NW) {
-      const int hh = i >> 7, j = i & 127;
-      float acc = 0.f;
-      if (hh < hs) {
-        const int g = group_of(hd, j), s0 = hd.start[g], nd = hd.dim[g];
-        const size_t qbase = ((size_t)b * a.n_q_heads + h0 + hh) * 128;
-        const float* rr = grot + hd.rot_offset[g] + (j - s0);
-        for (int r = 0; r < nd; ++r) {
-          const int c = hd.coord[s0 + r];
-          const float x = QF16 ? (float)((const _Float16*)a.q)[qbase + c] : ((const float*)a.q)[qbase + c];
-          acc = fmaf(rr[r * nd], x, acc);
-        }
-        acc *= a.scale_log2 / hd.f16_scale[g];
-      }
-      qt[hh][j] = acc;
+    constexpr int HK = 16 / NW;  // heads per thread
+    const int j = tid & 127, k0 = tid >> 7;
+    const int g = group_of(hd, j), s0 = hd.start[g], nd = hd.dim[g];
+    const float* rr = grot + hd.rot_offset[g] + (j - s0);
+    float acc[HK];
+#pragma unroll
+    for (int e = 0; e < HK; ++e) acc[e] = 0.f;
+#pragma unroll 16
+    for (int r = 0; r < nd; ++r) {
+      const float w = rr[r * nd];
+      const int c = hd.coord[s0 + r];
+#pragma unroll
+      for (int e = 0; e < HK; ++e) acc[e] = fmaf(w, qraw[k0 + (NW / 2) * e][c], acc[e]);
     }
+    const float f = a.scale_log2 / hd.f16_scale[g];
+#pragma unroll
+    for (int e = 0; e < HK; ++e) qt[k0 + (NW / 2) * e][j] = acc[e] * f;
   }
   __syncthreads();
   const int col = lane & 15;
   const int jr = lane >> 4;
   // query operands: block kb's positions 8 jr .. + 3 (qa) and + 4 .. + 7 (qb), each pair
-  // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]
+  // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]; and per block its
+  // group (uniform) and the byte of the lane's first code (reads past a record's 64 bytes
+  // stay inside the stage and meet zero query)
   u32x4 qa[kMaxKb], qb[kMaxKb];
+  int kgrp[kMaxKb];
+  uint32_t kbyte[kMaxKb];
 #pragma unroll
   for (int kb = 0; kb < kMaxKb; ++kb) {
+    const int g = kb < nkb ? group_of_block(kb) : 0, m = kb < nkb ? kb - cum[g] : 0;
+    const int dg = hd.dim[g], sg = hd.start[g];
+    kgrp[kb] = g;
+    kbyte[kb] = (uint32_t)((sg + 32 * m + 8 * jr) >> 1);
     qa[kb] = qb[kb] = u32x4{0u, 0u, 0u, 0u};
     if (kb < nkb) {
-      const int g = kbg[kb], m = kbm[kb];
       const int hh = col & 7;
       uint32_t x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int p = 32 * m + 8 * jr + 2 * e;
-        const float v0 = p < hd.dim[g] ? qt[hh][hd.start[g] + p] : 0.f;
-        const float v1 = p + 1 < hd.dim[g] ? qt[hh][hd.start[g] + p + 1] : 0.f;
+        const float v0 = p < dg ? qt[hh][sg + p] : 0.f;
+        const float v1 = p + 1 < dg ? qt[hh][sg + p + 1] : 0.f;
         x[e] = col >= 8 ? pack_f16(f16_lo(v0), f16_lo(v1)) : pack_f16(v0, v1);
       }
       qa[kb] = u32x4{x[0], x[0], x[1], x[1]};
       qb[kb] = u32x4{x[2], x[2], x[3], x[3]};
     }
-  }
-  // the k-block plan in registers: the block's group (uniform) and per lane the byte of its
-  // first code (reads past a record's 64 bytes stay inside the stage and meet zero query)
-  int kgrp[kMaxKb];
-  uint32_t kbyte[kMaxKb];
-#pragma unroll
-  for (int kb = 0; kb < kMaxKb; ++kb) {
-    const int g = kb < nkb ? __builtin_amdgcn_readfirstlane(kbg[kb]) : 0;
-    const int m = kb < nkb ? __builtin_amdgcn_readfirstlane(kbm[kb]) : 0;
-    kgrp[kb] = g;
-    kbyte[kb] = (uint32_t)((hd.start[g] + 32 * m + 8 * jr) >> 1);
   }
   asm volatile("" ::"v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "v"(qa[4]), "v"(qa[5]), "v"(qa[6]));
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]), "v"(qb[4]), "v"(qb[5]), "v"(qb[6]));
