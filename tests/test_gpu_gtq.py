@@ -264,3 +264,32 @@ def test_append_step_per_row_slots():
                 m = enc[h][int(np.searchsorted(ends, j, side="right"))][4]
                 assert np.min(np.abs(m - oy[0, j])) < BOUNDARY_EPS
             assert np.allclose(norms[r, h, p, :len(enc[h])], on[0], rtol=1e-6)
+
+
+def test_capacity_off_the_tile_grid():
+    # a capacity that is not a multiple of 16: the last tile's copies past the capacity are
+    # redirected inside the row, and the fused step appends at the last slot
+    lens = [301, 17]
+    w, inp, bits, enc = case(lens=lens, cap=301)
+    keys = tq.GtqKeys(bits, inp["gauss"])
+    oc, on, _ = oracle_keys(w, inp, enc)
+    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for n_splits in (1, 4):
+        res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=301, scale=w.scale, n_splits=n_splits)
+        if n_splits > 1:
+            res = tq.merge_splits(None, *res)
+        torch.cuda.synchronize()
+        (ro, rl), _ = oracle_attention(w, inp, enc, oc, on, lens)
+        check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, lens)
+    # the fused step at slot 300 (the capacity's last) against the two calls
+    k_new = torch.from_numpy(inp["k"][:, :, 300].astype(np.float16)).cuda()
+    v_new = torch.from_numpy(inp["v"][:, :, 300].astype(np.float16)).cuda()
+    a = (codes.clone(), norms.clone(), v.clone())
+    b = (codes.clone(), norms.clone(), v.clone())
+    res_a = tq.gtq_append_attention(keys, *a, k_new, v_new, q, pos0=300, scale=w.scale, n_splits=4)
+    tq.gtq_quantize_keys(keys, k_new[:, :, None, :].contiguous(), b[0], b[1], pos0=300)
+    b[2][:, :, 300] = v_new
+    res_b = tq.gtq_attention(keys, *b, q, max_len=301, scale=w.scale, n_splits=4)
+    torch.cuda.synchronize()
+    assert same(a, b) and same(res_a, res_b)
