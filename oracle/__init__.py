@@ -28,6 +28,9 @@ What it computes, and where the pages define it (page title, then section):
   one TQ-MSE encoder per width (rotation, codebook, compare-count), nibble records
   ("RoPE-Aware Bit Allocation ...", overview, energy score, greedy allocation, grouping and
   packed-cache paragraphs).
+* ``qjl``       -- two-stage keys: (b-1)-bit TQ-MSE plus the sign bits of a Gaussian projection
+  of the residual, and the unbiased inner-product estimate they give ("TurboQuant ... MNN on
+  phones", 2.4 and 3.2).
 * ``zipcodec``  -- the lossless BF16 exponent codec of the KV cache: chunk rule, 4-bit
   codes, page metadata and the decode by integer adds ("ZipFusion ...", compression format
   and register decode sections).
@@ -37,4 +40,4 @@ Parity pins for each function live in ``tests/test_oracle_*.py``; nothing here i
 "parity unpinned".
 """
 
-from . import codebook, rotation, quant, layout, attention, zipcodec, blockgtq  # noqa: F401
+from . import codebook, rotation, quant, layout, attention, zipcodec, blockgtq, qjl  # noqa: F401

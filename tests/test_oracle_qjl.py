@@ -1,0 +1,103 @@
+"""Pins of the two-stage (MSE + QJL) key oracle ("TurboQuant ... MNN on phones", 2.4 and 3.2):
+the Gaussian sign identity the estimator rests on, its unbiasedness and variance over random
+projections, the MSE stage's inner-product shrink that the second stage removes, and the
+sign packing.  Monte Carlo bounds are 5 standard errors."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import blockgtq as bg
+from oracle import codebook, qjl
+
+
+def test_gaussian_sign_identity():
+    # E[<s, q> sgn <s, r>] = sqrt(2/pi) <q, r> / |r| for s ~ N(0, I)
+    rng = np.random.default_rng(0)
+    d, n = 16, 400000
+    q, r = rng.standard_normal(d), rng.standard_normal(d)
+    s = rng.standard_normal((n, d))
+    t = (s @ q) * np.sign(s @ r)
+    want = math.sqrt(2 / math.pi) * (q @ r) / np.linalg.norm(r)
+    se = math.sqrt((q @ q - (2 / math.pi) * (q @ r / np.linalg.norm(r)) ** 2) / n)
+    assert abs(t.mean() - want) < 5 * se
+
+
+def test_estimator_is_unbiased_with_the_closed_form_variance():
+    rng = np.random.default_rng(1)
+    d = m = 128
+    q, r = rng.standard_normal(d), 0.3 * rng.standard_normal(d)
+    n = 3000
+    est = np.empty(n)
+    for i in range(n):
+        S = rng.standard_normal((m, d))
+        signs, rn = qjl.encode_residual(r[None], S)
+        est[i] = qjl.estimate(q, signs, rn, S)[0]
+    var = qjl.estimate_variance(q, r, m)
+    assert abs(est.mean() - q @ r) < 5 * math.sqrt(var / n)
+    assert abs(est.var(ddof=1) / var - 1) < 5 * math.sqrt(2 / (n - 1))
+
+
+def test_mse_stage_shrinks_and_two_stages_do_not():
+    # 2.4: the MSE quantiser shrinks inner products; over uniformly random rotations
+    # E<q, x_hat> = (1 - d D(b, d)) <q, x> exactly (centroid cells: E[c(Y) Y] = E[Y^2] - D).
+    # At 1 bit that is about 2/pi.  Adding the QJL estimate of the residual removes it.
+    rng = np.random.default_rng(2)
+    d, n = 128, 1500
+    x, q = rng.standard_normal(d), rng.standard_normal(d)
+    x_dot_q = x @ q
+    mse, two = np.empty(n), np.empty(n)
+    for i in range(n):
+        enc = qjl.mse_encoders(1, rng.standard_normal((4, d, d)))
+        S = rng.standard_normal((d, d))
+        codes, nu, signs, rn, xh = qjl.encode_keys(x[None], enc, S)
+        mse[i] = xh[0] @ q
+        two[i] = qjl.scores(q, xh, signs, rn, S)[0]
+    shrink = 1 - d * codebook.distortion(1, d)
+    assert abs(shrink - 2 / math.pi) < 0.01
+    assert abs(mse.mean() - shrink * x_dot_q) < 5 * mse.std(ddof=1) / math.sqrt(n)
+    assert abs(two.mean() - x_dot_q) < 5 * two.std(ddof=1) / math.sqrt(n)
+    # and the shrink is a real bias at this sample size, not noise
+    assert abs(mse.mean() - x_dot_q) > 10 * mse.std(ddof=1) / math.sqrt(n)
+
+
+def test_encode_keys_stage_one_is_the_single_group_tq_mse():
+    rng = np.random.default_rng(3)
+    gauss = rng.standard_normal((4, 128, 128))
+    for bits in (1, 2):
+        enc = qjl.mse_encoders(bits, gauss)
+        assert enc[0][0] == bits
+        x = rng.standard_normal((5, 128))
+        S = rng.standard_normal((128, 128))
+        codes, nu, signs, rn, xh = qjl.encode_keys(x, enc, S)
+        c2, n2, _ = bg.quantize_keys(x, enc)
+        assert np.array_equal(codes, c2) and np.allclose(nu, n2[:, 0], rtol=0, atol=0)
+        assert np.allclose(rn, np.linalg.norm(x - xh, axis=1), rtol=1e-12)
+        assert np.array_equal(qjl.unpack_signs(signs), (x - xh) @ S.T >= 0)
+
+
+def test_sign_packing_and_zero_residual():
+    rng = np.random.default_rng(4)
+    b = rng.random((7, 128)) < 0.5
+    p = qjl.pack_signs(b)
+    assert p.shape == (7, 16) and np.array_equal(qjl.unpack_signs(p), b)
+    one = np.zeros(128, bool)
+    one[9] = True  # bit 9 -> byte 1, bit 1
+    assert list(qjl.pack_signs(one)[:3]) == [0, 2, 0]
+    S = rng.standard_normal((128, 128))
+    signs, rn = qjl.encode_residual(np.zeros((1, 128)), S)
+    assert rn[0] == 0.0 and np.all(qjl.unpack_signs(signs))  # zero projections count as +
+    assert qjl.estimate(rng.standard_normal(128), signs, rn, S)[0] == 0.0
+
+
+@pytest.mark.parametrize("seed", [5, 6])
+def test_attend_is_softmax_over_the_two_stage_scores(seed):
+    rng = np.random.default_rng(seed)
+    enc = qjl.mse_encoders(1, rng.standard_normal((4, 128, 128)))
+    S = rng.standard_normal((128, 128))
+    x, v, q = rng.standard_normal((40, 128)), rng.standard_normal((40, 128)), rng.standard_normal(128)
+    _, _, signs, rn, xh = qjl.encode_keys(x, enc, S)
+    s = 0.1 * qjl.scores(q, xh, signs, rn, S)
+    w = np.exp(s - s.max())
+    assert np.allclose(qjl.attend(q, xh, signs, rn, S, v, 0.1), (w / w.sum()) @ v, rtol=1e-12)
