@@ -18,6 +18,7 @@ __all__ = [
     "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
     "zip_store", "zip_compress", "zip_attention",
     "gtq_block_energies", "gtq_allocate", "GtqKeys", "gtq_quantize_keys", "gtq_attention", "gtq_append_attention",
+    "QjlKeys", "qjl_quantize_keys", "qjl_attention",
     "TQ_KEYS", "TQ_VALUES",
 ]
 
@@ -80,7 +81,8 @@ _lib = None
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
            "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
            "tq_zip_compress", "tq_zip_attention", "tq_gtq_block_energies", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
-           "tq_gtq_attention", "tq_gtq_append_attention")
+           "tq_gtq_attention", "tq_gtq_append_attention", "tq_gtq_qjl_projection", "tq_gtq_qjl_quantize_keys",
+           "tq_gtq_qjl_attention")
 
 
 def library():
@@ -128,6 +130,12 @@ def library():
     lib.tq_gtq_attention.restype = I
     lib.tq_gtq_append_attention.argtypes = [P, P, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P, P, P, P, P]
     lib.tq_gtq_append_attention.restype = I
+    lib.tq_gtq_qjl_projection.argtypes = [P, P, P, P]
+    lib.tq_gtq_qjl_projection.restype = I
+    lib.tq_gtq_qjl_quantize_keys.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P]
+    lib.tq_gtq_qjl_quantize_keys.restype = I
+    lib.tq_gtq_qjl_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
+    lib.tq_gtq_qjl_attention.restype = I
     _lib = lib
     return lib
 
@@ -466,6 +474,27 @@ class GtqKeys:
         return self.heads_host[h].n_groups
 
 
+class QjlKeys(GtqKeys):
+    """Two-stage key encoders: a one-group Block-GTQ head at `bits` bits (the MSE stage,
+    rotation from gauss[h, bits-1]) and the QJL projection S [n_kv_heads, 128, 128] of the
+    residual, held as (S Q)^T per head."""
+
+    def __init__(self, bits, gauss, S, device="cuda"):
+        import numpy as np
+        g = np.ascontiguousarray(gauss, dtype=np.float32)
+        hkv = g.shape[0]
+        sp = np.ascontiguousarray(S, dtype=np.float32)
+        if sp.shape != (hkv, 128, 128):
+            raise ValueError("S must be float32 [n_kv_heads, 128, 128]")
+        super().__init__(np.full((hkv, 64), bits, dtype=np.int32), g, device)
+        rot = self.rotations.cpu().numpy()
+        proj = np.zeros((hkv, 128 * 128), dtype=np.float32)
+        for h in range(hkv):
+            _check(library().tq_gtq_qjl_projection(ctypes.byref(self.heads_host[h]), rot[h].ctypes.data,
+                                                   sp[h].ctypes.data, proj[h].ctypes.data), "tq_gtq_qjl_projection")
+        self.proj = torch.from_numpy(proj).to(device)
+
+
 def gtq_quantize_keys(enc: GtqKeys, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, pos0: int = 0):
     """Encode x [batch, n_kv_heads, n_new, 128] (fp16/fp32) into codes uint8 [batch,
     n_kv_heads, capacity, 64] and norms fp32 [batch, n_kv_heads, capacity, 4] at pos0 .."""
@@ -557,4 +586,57 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
         _ptr(enc.heads), _ptr(enc.rotations), _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(k_new),
         _ptr(v_new), _DTYPES[k_new.dtype], _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits,
         _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_gtq_append_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+def qjl_quantize_keys(enc: QjlKeys, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, signs: torch.Tensor,
+                      pos0: int = 0):
+    """Two-stage encoding of x [batch, n_kv_heads, n_new, 128] (fp16/fp32): codes and norms as
+    gtq_quantize_keys (norm slot 1: the residual's coefficient), signs uint8 [batch,
+    n_kv_heads, capacity, 16]."""
+    if x.dtype not in _DTYPES or not x.is_contiguous() or x.dim() != 4 or x.shape[3] != HEAD_DIM:
+        raise ValueError("x must be contiguous [batch, n_kv_heads, n_new, 128] float16/float32")
+    bsz, hkv, n_new = x.shape[:3]
+    cap = codes.shape[2]
+    if hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or codes.dtype != torch.uint8 or \
+            tuple(norms.shape) != (bsz, hkv, cap, 4) or norms.dtype != torch.float32 or \
+            tuple(signs.shape) != (bsz, hkv, cap, 16) or signs.dtype != torch.uint8 or \
+            not (codes.is_contiguous() and norms.is_contiguous() and signs.is_contiguous()):
+        raise ValueError("codes uint8 [b, kv, cap, 64], norms float32 [b, kv, cap, 4], signs uint8 [b, kv, cap, 16]")
+    _check(library().tq_gtq_qjl_quantize_keys(_ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(x),
+                                              _DTYPES[x.dtype], bsz, hkv, n_new, pos0, cap, _ptr(codes),
+                                              _ptr(norms), _ptr(signs), _stream()), "tq_gtq_qjl_quantize_keys")
+
+
+def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_len=None, scale=None, n_splits=1,
+                  out=None, lse=None, part_o=None, part_lse=None):
+    """Decode attention over two-stage keys and fp16 values; returns as gtq_attention."""
+    if v.dtype != torch.float16 or not v.is_contiguous() or v.dim() != 4 or v.shape[3] != HEAD_DIM:
+        raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    hkv, cap = v.shape[1], v.shape[2]
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+            tuple(norms.shape) != (bsz, hkv, cap, 4) or tuple(signs.shape) != (bsz, hkv, cap, 16):
+        raise ValueError("codes, norms, signs and v must describe the same [batch, n_kv_heads, capacity] cache")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
+        raise ValueError("seq_lens must be int32 [batch]")
+    if max_len is None:
+        max_len = int(seq_lens.max().item()) if seq_lens is not None else cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_gtq_qjl_attention(
+        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(codes), _ptr(norms), _ptr(signs), _ptr(v), cap,
+        bsz, hkv, _ptr(q), _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse),
+        _ptr(part_o), _ptr(part_lse), _stream()), "tq_gtq_qjl_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)

@@ -342,9 +342,9 @@ extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_m
   return from_hip(tq::launch_zip_attention(a, (int)q_dtype, (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x,
-                                          tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new,
-                                          int32_t pos0, int32_t capacity, uint8_t* codes, float* norms, void* stream) {
+static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, const float* proj, const void* x,
+                              tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0,
+                              int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, void* stream) {
   if (heads == nullptr || rotations == nullptr || x == nullptr || codes == nullptr || norms == nullptr)
     return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
@@ -353,6 +353,7 @@ extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float*
   if ((int64_t)pos0 + n_new > capacity) return TQ_ECAPACITY;
   if (n_new == 0) return TQ_OK;
   tq::GtqQuantArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.heads = heads;
   a.rotations = rotations;
   a.x = x;
@@ -362,7 +363,25 @@ extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float*
   a.n_new = n_new;
   a.pos0 = pos0;
   a.capacity = capacity;
+  a.proj = proj;
+  a.signs = signs;
   return from_hip(tq::launch_gtq_quantize(a, x_dtype == TQ_F16, batch, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x,
+                                          tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new,
+                                          int32_t pos0, int32_t capacity, uint8_t* codes, float* norms, void* stream) {
+  return gtq_quantize(heads, rotations, nullptr, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, codes, norms,
+                      nullptr, stream);
+}
+
+extern "C" tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                              const void* x, tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads,
+                                              int32_t n_new, int32_t pos0, int32_t capacity, uint8_t* codes,
+                                              float* norms, uint8_t* signs, void* stream) {
+  if (proj == nullptr || signs == nullptr) return TQ_EINVAL;
+  return gtq_quantize(heads, rotations, proj, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, codes, norms,
+                      signs, stream);
 }
 
 static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
@@ -418,6 +437,23 @@ extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rot
                                           n_q_heads, seq_lens, max_len, scale, n_splits, out, lse_out, part_o,
                                           part_lse, a);
   if (st != TQ_OK) return st;
+  return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                          const uint8_t* codes, const float* norms, const uint8_t* signs, const void* v,
+                                          int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,
+                                          tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens,
+                                          int32_t max_len, float scale, int32_t n_splits, float* out, float* lse_out,
+                                          float* part_o, float* part_lse, void* stream) {
+  if (proj == nullptr || signs == nullptr) return TQ_EINVAL;
+  tq::GtqAttnArgs a;
+  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+                                          n_q_heads, seq_lens, max_len, scale, n_splits, out, lse_out, part_o,
+                                          part_lse, a);
+  if (st != TQ_OK) return st;
+  a.proj = proj;
+  a.signs = signs;
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 

@@ -110,3 +110,20 @@ extern "C" tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gaus
   for (int k = g; k < TQ_GTQ_MAX_GROUPS; ++k) head->start[k] = 128;
   return TQ_OK;
 }
+
+extern "C" tq_status tq_gtq_qjl_projection(const tq_gtq_head* head, const float* rotation, const float* S,
+                                           float* proj) {
+  if (head == nullptr || rotation == nullptr || S == nullptr || proj == nullptr) return TQ_EINVAL;
+  // the two-stage keys' first stage is one group of all 128 coordinates in order
+  if (head->n_groups != 1 || head->dim[0] != 128 || head->rot_offset[0] != 0) return TQ_EINVAL;
+  for (int j = 0; j < 128; ++j)
+    if (head->coord[j] != j) return TQ_EINVAL;
+  // M = S Q in double; stored transposed: proj[j][i] = M[i][j]
+  for (int i = 0; i < 128; ++i)
+    for (int j = 0; j < 128; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < 128; ++c) acc += (double)S[i * 128 + c] * (double)rotation[c * 128 + j];
+      proj[j * 128 + i] = (float)acc;
+    }
+  return TQ_OK;
+}

@@ -47,9 +47,13 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
 // positions 2l and 2l + 1 (always in one group: groups start at even positions and have
 // even sizes), compare-count, one code byte per lane and one norm per group.  rot: the
 // head's rotations, in LDS or global memory.  Every lane of the wave takes part.
-template <bool XF16>
+// QJL (two-stage keys, one group): also the m = 128 sign bits of S r into sign_rec and
+// sqrt(pi/2)/m |r| into norm slot 1, from the rotated-domain residual e = y - c_hat
+// (S r = |x| M e with M = S Q; proj[j][i] = M[i][j], in LDS or global memory).
+template <bool XF16, bool QJL = false>
 __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* rot, const void* x, float* ubuf,
-                                           uint8_t* code_rec, float* norm_rec, int lane) {
+                                           uint8_t* code_rec, float* norm_rec, int lane, const float* proj = nullptr,
+                                           uint8_t* sign_rec = nullptr) {
   const int j0 = 2 * lane;
   const int g = group_of(hd, j0);
   const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
@@ -92,7 +96,28 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
     c1 += y1 > hd.boundary[g][k];
   }
   code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
-  if (lane < 4) norm_rec[lane] = lane < hd.n_groups ? sqrtf(ss[lane & 3]) : 0.f;
+  float coef = 0.f;
+  if (QJL) {
+    const float e0 = y0 - hd.centroid[0][c0], e1 = y1 - hd.centroid[0][c1];
+    // every lane's reads of u are complete (in-order LDS): e takes u's place
+    ubuf[j0] = e0;
+    ubuf[j0 + 1] = e1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float s0 = 0.f, s1 = 0.f;  // (M e)_i for i = lane and lane + 64
+#pragma unroll 8
+    for (int j = 0; j < 128; ++j) {
+      const float e = ubuf[j];
+      s0 = fmaf(proj[j * 128 + lane], e, s0);
+      s1 = fmaf(proj[j * 128 + 64 + lane], e, s1);
+    }
+    const float ee = wave_sum(e0 * e0 + e1 * e1);
+    const uint64_t b0 = __builtin_amdgcn_ballot_w64(s0 >= 0.f), b1 = __builtin_amdgcn_ballot_w64(s1 >= 0.f);
+    if (lane < 4) ((uint32_t*)sign_rec)[lane] = (uint32_t)((lane < 2 ? b0 : b1) >> (32 * (lane & 1)));
+    coef = 1.2533141373155003f / 128.f * sqrtf(ss[0]) * sqrtf(ee);  // sqrt(pi/2)/m |x| |e|
+  }
+  if (lane < 4) norm_rec[lane] = QJL && lane == 1 ? coef : lane < hd.n_groups ? sqrtf(ss[lane & 3]) : 0.f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -101,9 +126,10 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
 // group-order positions 2l and 2l + 1 (always in one group: groups start at even positions
 // and have even sizes).
 constexpr int kQuantTokens = 512;
-template <bool XF16>
+template <bool XF16, bool QJL>
 __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a) {
   __shared__ __attribute__((aligned(16))) float rot[TQ_GTQ_ROTATION_FLOATS];
+  __shared__ __attribute__((aligned(16))) float projl[QJL ? 128 * 128 : 1];
   __shared__ __attribute__((aligned(16))) float ubuf[4][128];
   __shared__ tq_gtq_head hd;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -114,6 +140,8 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
   for (int g = 0; g < hd.n_groups; ++g) used = hd.rot_offset[g] + hd.dim[g] * hd.dim[g];
   const float* grot = a.rotations + (size_t)h * TQ_GTQ_ROTATION_FLOATS;
   for (int i = tid; i < used; i += 256) rot[i] = grot[i];
+  if (QJL)
+    for (int i = tid; i < 128 * 128; i += 256) projl[i] = a.proj[(size_t)h * 128 * 128 + i];
   __syncthreads();
 
   const size_t stream = (size_t)b * a.n_kv_heads + h;
@@ -121,8 +149,8 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
     const int i = tile * kQuantTokens + t;
     if (i >= a.n_new) break;
     const size_t rec = stream * a.capacity + a.pos0 + i;
-    encode_key<XF16>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4), ubuf[wv],
-                     a.codes + rec * 64, a.norms + rec * 4, lane);
+    encode_key<XF16, QJL>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4), ubuf[wv],
+                          a.codes + rec * 64, a.norms + rec * 4, lane, projl, QJL ? a.signs + rec * 16 : nullptr);
     // the next token's writes to ubuf follow this token's reads in program order
     __builtin_amdgcn_wave_barrier();
   }
@@ -176,19 +204,24 @@ __device__ __forceinline__ float f16_lo(float x) { return x - (float)(_Float16)x
 constexpr float kRescaleG = 8.f;  // log2 headroom of the lazily updated softmax reference
 constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil(n/32) <= 7
 
-template <int NW, int D, bool QF16>
+// QJL: two-stage keys (one MSE group plus sign bits of the projected residual): four more
+// k-blocks whose key operands are +-1 (exact in fp16, from a table indexed by a sign byte)
+// against the projected query S q = M Q^T q, times the coefficient in norm slot 1.
+template <int NW, int D, bool QF16, bool QJL>
 __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
-  constexpr int STAGE = 5376;  // key records 1 KB, norms 256 B (group-major), values 4 KB
-  constexpr int NORM_AT = 1024, VAL_AT = 1280;
-  constexpr int NDMA = 6;
+  // a stage: key records 1 KB, norms 256 B (group-major), values 4 KB, sign bytes 256 B
+  constexpr int STAGE = QJL ? 5632 : 5376;
+  constexpr int NORM_AT = 1024, VAL_AT = 1280, SIGN_AT = 5376;
+  constexpr int NDMA = QJL ? 7 : 6;
   constexpr int WAVE_LDS = D * STAGE;
   static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
   static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
-  constexpr int TAB_BYTES = kMaxKb * 256 * 8;
+  constexpr int TAB_BYTES = kMaxKb * 256 * 8 + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
   uint2(*const ptab)[256] = (uint2(*)[256])lds_all;
   uint8_t* const lds = lds_all + TAB_BYTES;
+  uint8_t* const pmtab = lds_all + kMaxKb * 256 * 8;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
   // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
@@ -213,6 +246,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   const uint8_t* kc = a.codes + row0 * 64;
   const uint8_t* kn = (const uint8_t*)(a.norms + row0 * 4);
   const uint8_t* vbp = (const uint8_t*)a.v + row0 * 256;
+  const uint8_t* sgb = QJL ? a.signs + row0 * 16 : nullptr;
   const int cap = a.capacity;
   uint8_t* wlds = lds + wv * WAVE_LDS;
   const uint32_t wlds_a = lds_addr(wlds);
@@ -234,6 +268,10 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       t = t0 + 4 * k + (lane >> 4);
       lds_dma<16, true>(dst + VAL_AT + 1024 * k, vbp,
                         t < cap ? (uint32_t)(t * 256 + 16 * (lane & 15)) : (uint32_t)(t0 * 256));
+    }
+    if (QJL) {  // 16 tokens' sign bytes (lane: token tok0 + l/4, 4 bytes)
+      t = t0 + (lane >> 2);
+      lds_dma<4, true>(dst + SIGN_AT, sgb, t < cap ? (uint32_t)(t * 16 + 4 * (lane & 3)) : (uint32_t)(t0 * 16));
     }
   };
 
@@ -311,9 +349,47 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 #pragma unroll
     for (int e = 0; e < HK; ++e) qt[k0 + (NW / 2) * e][j] = acc[e] * f;
   }
+  if (QJL) {  // the +-1 table: entry by, fp16 pair k = (bit 2k, bit 2k + 1) of by, 1 -> +1
+    for (int i = tid; i < 256 * 4; i += 64 * NW) {
+      const int by = i >> 2, k = i & 3;
+      ((uint32_t*)pmtab)[i] = pack_f16((by >> (2 * k)) & 1 ? 1.f : -1.f, (by >> (2 * k + 1)) & 1 ? 1.f : -1.f);
+    }
+  }
   __syncthreads();
   const int col = lane & 15;
   const int jr = lane >> 4;
+  // QJL: the projected query w = M q~ (q~ = Q^T q, already scaled in qt by scale_log2 / s,
+  // so w is scaled back by s) into qraw, then its operands: block m's positions
+  // 32 m + 8 jr .. + 7, fp16 hi (columns 0-7) and lo (8-15) parts
+  u32x4 qq[QJL ? 4 : 1];
+  if (QJL) {
+    const int i = tid & 127, k0 = tid >> 7;
+    constexpr int HK = 16 / NW;
+    const float* pj = a.proj + (size_t)kv * 128 * 128;
+    float acc[HK];
+#pragma unroll
+    for (int e = 0; e < HK; ++e) acc[e] = 0.f;
+#pragma unroll 16
+    for (int jj = 0; jj < 128; ++jj) {
+      const float w = pj[jj * 128 + i];
+#pragma unroll
+      for (int e = 0; e < HK; ++e) acc[e] = fmaf(w, qt[k0 + (NW / 2) * e][jj], acc[e]);
+    }
+    const float s0 = hd.f16_scale[0];
+#pragma unroll
+    for (int e = 0; e < HK; ++e) qraw[k0 + (NW / 2) * e][i] = acc[e] * s0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = qraw[col & 7][32 * m + 8 * jr + 2 * e], v1 = qraw[col & 7][32 * m + 8 * jr + 2 * e + 1];
+        x[e] = col >= 8 ? pack_f16(f16_lo(v0), f16_lo(v1)) : pack_f16(v0, v1);
+      }
+      qq[m] = u32x4{x[0], x[1], x[2], x[3]};
+    }
+  }
   // query operands: block kb's positions 8 jr .. + 3 (qa) and + 4 .. + 7 (qb), each pair
   // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]; and per block its
   // group (uniform) and the byte of the lane's first code (reads past a record's 64 bytes
@@ -396,6 +472,19 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       sc[1] = fmaf(nr.y, cur[1], sc[1]);
       sc[2] = fmaf(nr.z, cur[2], sc[2]);
       sc[3] = fmaf(nr.w, cur[3], sc[3]);
+    }
+    if (QJL) {  // the residual's estimate: sign operands against S q, times slot 1
+      f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t by = lds_read<uint8_t>(sb + SIGN_AT + 16 * col + 4 * m + jr);
+        cq = mfma_f16(lds_read<u32x4>(pmtab + 16 * by), qq[m], cq);
+      }
+      const float4 nr = lds_read<float4>(sb + NORM_AT + 64 + 16 * jr);
+      sc[0] = fmaf(nr.x, cq[0], sc[0]);
+      sc[1] = fmaf(nr.y, cq[1], sc[1]);
+      sc[2] = fmaf(nr.z, cq[2], sc[2]);
+      sc[3] = fmaf(nr.w, cq[3], sc[3]);
     }
     float x[4];
     float bm = -INFINITY;
@@ -508,8 +597,13 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 
 hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream) {
   const dim3 grid((a.n_new + kQuantTokens - 1) / kQuantTokens, a.n_kv_heads, batch), block(256);
-  if (x_f16) hipLaunchKernelGGL(gtq_quantize_kernel<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(gtq_quantize_kernel<false>, grid, block, 0, stream, a);
+  if (a.signs) {
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true>), grid, block, 0, stream, a);
+  } else {
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -517,8 +611,13 @@ hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t st
   constexpr int NW = 8, D = 2;
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
   if (a.heads_per_slice > 8) return hipErrorInvalidValue;
-  if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false>), grid, block, 0, stream, a);
+  if (a.signs) {
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

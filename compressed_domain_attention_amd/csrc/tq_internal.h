@@ -138,6 +138,8 @@ struct GtqQuantArgs {
   int32_t n_new;
   int32_t pos0;
   int32_t capacity;
+  const float* proj;        // two-stage keys: [n_kv_heads][128][128], (S Q)^T; else NULL
+  uint8_t* signs;           // two-stage keys: [batch][n_kv_heads][capacity][16]; else NULL
 };
 
 struct GtqAttnArgs {
@@ -173,6 +175,10 @@ struct GtqAttnArgs {
   uint8_t* w_codes;         // the cache again, writable (append only)
   float* w_norms;
   void* w_v;
+  // two-stage keys (signs != NULL): proj [n_kv_heads][128][128] = (S Q)^T, signs
+  // [batch][n_kv_heads][capacity][16]
+  const float* proj;
+  const uint8_t* signs;
 };
 
 struct MergeArgs {

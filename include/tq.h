@@ -354,6 +354,21 @@ typedef struct {
  * tq_make_codebook(width, n).  Errors: TQ_EINVAL for null pointers or widths outside 1..4. */
 tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gauss, tq_gtq_head* head, float* rotation);
 
+/* Two-stage keys ("TurboQuant ... MNN on phones", 2.4 and 3.2: (b-1)-bit MSE plus a
+ * 1-bit QJL residual whose sign bits give an unbiased inner-product estimate).  The first
+ * stage is a Block-GTQ head whose 64 blocks all have width b - 1 (one group of the 128
+ * coordinates in order, rotation Q); the second stores, per key, the m = 128 sign bits of
+ * S r, r = x - x_hat the residual and S the m x 128 projection (independent N(0, 1)
+ * entries, the caller's), and sqrt(pi/2)/m |r| in the record's norm slot 1.  The query's
+ * score is <q, x_hat> + sqrt(pi/2)/m |r| sum_i (S q)_i sgn((S r)_i).
+ * Since x = |x| Q y, r = |x| Q (y - c_hat) and S r = |x| (S Q)(y - c_hat); one matrix
+ * M = S Q serves both the key encoding and the query (S q = M Q^T q).
+ *
+ * tq_gtq_qjl_projection (host): proj[j][i] = M[i][j] (M = S Q in double, stored fp32) for
+ *   a head prepared by tq_gtq_prepare with every block at one width; S: [128][128]
+ *   row-major; rotation: that head's rotation array.  TQ_EINVAL for another head layout. */
+tq_status tq_gtq_qjl_projection(const tq_gtq_head* head, const float* rotation, const float* S, float* proj);
+
 /* Encodes n_new keys per (sequence, KV head) into token positions pos0 .. pos0+n_new-1.
  *   heads:     device tq_gtq_head [n_kv_heads]; rotations: device float [n_kv_heads][16384].
  *   x:         device [batch][n_kv_heads][n_new][128] of x_dtype (TQ_F32 or TQ_F16).
@@ -385,6 +400,28 @@ tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, con
                            const void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,
                            tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
                            int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
+
+/* Two-stage keys (see tq_gtq_qjl_projection): the first stage exactly as
+ * tq_gtq_quantize_keys with the one-group head, plus, per key, the 16 bytes of sign bits of
+ * S r (bit i of the 128 in byte i/8 at bit i mod 8; a zero projection counts as +) into
+ * signs [batch][n_kv_heads][capacity][16] and sqrt(pi/2)/128 |r| into norm slot 1.
+ *   proj: device [n_kv_heads][128 * 128] from tq_gtq_qjl_projection.
+ * Errors: those of tq_gtq_quantize_keys; TQ_EINVAL for a null proj or signs. */
+tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj, const void* x,
+                                   tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0,
+                                   int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, void* stream);
+
+/* Decode attention over two-stage keys and fp16 values: as tq_gtq_attention, with each
+ * score <q, x_hat> + sqrt(pi/2)/128 |r| sum_i (S q)_i sgn((S r)_i) (the projected query
+ * S q = M Q^T q is formed once per workgroup; the signs are exact in fp16).  Arguments and
+ * errors as tq_gtq_attention, plus proj and signs as tq_gtq_qjl_quantize_keys (TQ_EINVAL
+ * when null). */
+tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                               const uint8_t* codes, const float* norms, const uint8_t* signs, const void* v,
+                               int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q, tq_dtype q_dtype,
+                               int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
+                               int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
+                               void* stream);
 
 /* One decode step with its new token over Block-GTQ keys and fp16 values: the same cache
  * contents and outputs, bit for bit, as tq_gtq_quantize_keys of the new key at its slot and

@@ -12,6 +12,7 @@ import pytest
 
 import compressed_domain_attention_amd as tq
 from oracle import codebook as ocb
+from oracle import qjl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tq.h")
@@ -394,6 +395,45 @@ def test_gtq_append_call_validation(lib):
     assert call(splits=3, part=None) == TQ_EINVAL
     assert call(pos0=64) == TQ_ECAPACITY       # the new slot past the capacity
     assert call(pos=FAKE, max_pos=64) == TQ_ECAPACITY
+
+
+def test_qjl_projection_matches_oracle(lib):
+    # proj[j][i] = (S Q)[i][j] for the one-group head the oracle's MSE stage uses
+    rng = np.random.default_rng(11)
+    gauss = rng.standard_normal((4, 128, 128)).astype(np.float32)
+    S = rng.standard_normal((128, 128)).astype(np.float32)
+    head = tq.GtqHead()
+    rot = np.zeros(tq.GTQ_ROTATION_FLOATS, dtype=np.float32)
+    assert lib.tq_gtq_prepare(np.full(64, 1, np.int32).ctypes.data, gauss.ctypes.data, ctypes.byref(head),
+                              rot.ctypes.data) == TQ_OK
+    proj = np.zeros(128 * 128, dtype=np.float32)
+    assert lib.tq_gtq_qjl_projection(ctypes.byref(head), rot.ctypes.data, S.ctypes.data, proj.ctypes.data) == TQ_OK
+    qm = qjl.mse_encoders(1, gauss.astype(np.float64))[0][2]
+    assert np.allclose(proj.reshape(128, 128).T, S.astype(np.float64) @ qm, atol=1e-4)
+    # the projection needs the one-group layout
+    bits = np.full(64, 1, np.int32)
+    bits[5] = 2
+    assert lib.tq_gtq_prepare(bits.ctypes.data, gauss.ctypes.data, ctypes.byref(head), rot.ctypes.data) == TQ_OK
+    assert lib.tq_gtq_qjl_projection(ctypes.byref(head), rot.ctypes.data, S.ctypes.data,
+                                     proj.ctypes.data) == TQ_EINVAL
+    assert lib.tq_gtq_qjl_projection(None, rot.ctypes.data, S.ctypes.data, proj.ctypes.data) == TQ_EINVAL
+
+
+def test_qjl_call_validation(lib):
+    qk = lib.tq_gtq_qjl_quantize_keys
+    assert qk(FAKE, FAKE, None, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, FAKE, None) == TQ_EINVAL   # no projection
+    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, None, None) == TQ_EINVAL   # no signs
+    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 4, 30, 32, FAKE, FAKE, FAKE, None) == TQ_ECAPACITY
+    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, 32, FAKE, FAKE, FAKE, None) == TQ_OK     # nothing launched
+    at = lib.tq_gtq_qjl_attention
+
+    def call(**kw):
+        a = dict(proj=FAKE, signs=FAKE, codes=FAKE, max_len=64, splits=1, out=FAKE)
+        a.update(kw)
+        return at(FAKE, FAKE, a["proj"], a["codes"], FAKE, a["signs"], FAKE, 64, 1, 2, FAKE, 1, 8, None,
+                  a["max_len"], 0.1, a["splits"], a["out"], None, FAKE, FAKE, None)
+    assert call(proj=None) == TQ_EINVAL and call(signs=None) == TQ_EINVAL and call(codes=None) == TQ_EINVAL
+    assert call(out=None) == TQ_EINVAL and call(max_len=65) == TQ_ECAPACITY
 
 
 def test_product_path_has_no_cpu_fallback():

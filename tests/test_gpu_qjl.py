@@ -1,0 +1,140 @@
+"""GPU parity of two-stage keys (1-bit TQ-MSE + 1-bit QJL residual, oracle/qjl.py) through the
+C ABI.
+
+Encoding: MSE codes equal the oracle's except coordinates within 2e-6 of a boundary (at most
+1e-4 of them), the MSE norm within 1e-6 relative, the residual coefficient
+sqrt(pi/2)/128 |r| within 1e-4 relative (keys with a boundary code excluded: their residual
+differs), and the sign bits equal the oracle's except projections within 1e-4 |r| |S_i| of
+zero (the library projects the rotated-domain residual with the fp32 product S Q).
+Attention is fed the oracle's records and compared with the oracle's two-stage attention
+(fp64 scores <q, x_hat> + the estimate, fp16 values): within 1e-4 per row, lse within
+1e-4 + 1e-5 |lse|.  Rows are ragged with an empty one; sections 1 and 3.
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_domain_attention_amd as tq
+import workloads
+from helpers import row_rel_err
+from oracle import blockgtq as bg, qjl
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+LSE_ATOL = 1e-4
+LSE_RTOL = 1e-5
+LENS = [300, 77, 0]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.library()
+
+
+def case(lens=LENS, cap=320, hq=32, hkv=8, seed=0):
+    w = replace(workloads.WORKLOADS["qjl32k"], batch=len(lens), n_q_heads=hq, n_kv_heads=hkv, seq_len=cap)
+    inp = workloads.generate(w, seed)
+    bits = w.bits_k - 1  # the MSE stage
+    enc = [qjl.mse_encoders(bits, inp["gauss"][h].astype(np.float64)) for h in range(hkv)]
+    print("qjl case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, flush=True)
+    return w, inp, bits, enc
+
+
+def oracle_records(w, inp, enc):
+    shp = (w.batch, w.n_kv_heads, w.seq_len)
+    codes, norms = np.zeros(shp + (128,), np.uint8), np.zeros(shp + (4,), np.float32)
+    signs, rn, xh = np.zeros(shp + (16,), np.uint8), np.zeros(shp), np.zeros(shp + (128,))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            S = inp["proj"][h].astype(np.float64)
+            c, nu, sg, r, x_hat = qjl.encode_keys(inp["k"][b, h].astype(np.float64), enc[h], S)
+            codes[b, h], signs[b, h], rn[b, h], xh[b, h] = c, sg, r, x_hat
+            norms[b, h, :, 0] = nu
+            norms[b, h, :, 1] = np.sqrt(np.pi / 2) / 128 * r
+    return codes, norms, signs, rn, xh
+
+
+def test_encoding_matches_oracle():
+    w, inp, bits, enc = case()
+    keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
+    shp = (w.batch, w.n_kv_heads, w.seq_len)
+    codes = torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")
+    signs = torch.zeros(shp + (16,), dtype=torch.uint8, device="cuda")
+    x = torch.from_numpy(inp["k"]).cuda()
+    tq.qjl_quantize_keys(keys, x[:, :, :100].contiguous(), codes, norms, signs, pos0=0)
+    tq.qjl_quantize_keys(keys, x[:, :, 100:].contiguous(), codes, norms, signs, pos0=100)
+    torch.cuda.synchronize()
+    oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
+    got = bg.unpack_codes(codes.cpu().numpy().reshape(-1, 64)).reshape(oc.shape)
+    bad = got != oc
+    assert bad.mean() <= 1e-4, bad.mean()
+    n = norms.cpu().numpy()
+    assert np.allclose(n[..., 0], on[..., 0], rtol=1e-6, atol=0)
+    clean = ~bad.any(axis=-1)
+    assert np.allclose(n[..., 1][clean], on[..., 1][clean], rtol=1e-4, atol=0)
+    assert np.all(n[..., 2:] == 0)
+    # sign bits: exact except projections of the residual that are nearly zero
+    gs = qjl.unpack_signs(signs.cpu().numpy())
+    os_ = qjl.unpack_signs(osg)
+    diff = (gs != os_) & clean[..., None]
+    worst = 0
+    for b, h, t in zip(*np.nonzero(diff.any(axis=-1))):
+        S = inp["proj"][h].astype(np.float64)
+        r = inp["k"][b, h, t].astype(np.float64) - oxh[b, h, t]
+        proj = S @ r
+        for i in np.nonzero(diff[b, h, t])[0]:
+            assert abs(proj[i]) < 1e-4 * np.linalg.norm(r) * np.linalg.norm(S[i]), (b, h, t, i)
+        worst += 1
+    assert diff.mean() <= 1e-4, diff.mean()
+
+
+def check(out, lse, ro, rl, lens):
+    worst = worst_lse = 0.0
+    for b, t in enumerate(lens):
+        for h in range(out.shape[1]):
+            if t == 0:
+                assert lse[b, h] == -np.inf and not out[b, h].any()
+                continue
+            worst = max(worst, float(row_rel_err(out[b, h], ro[b, h])))
+            worst_lse = max(worst_lse, abs(float(lse[b, h] - rl[b, h])))
+    print("worst row error %.2e, lse %.2e" % (worst, worst_lse), flush=True)
+    assert worst <= RTOL and worst_lse <= LSE_ATOL + LSE_RTOL * float(np.max(np.abs(rl[np.isfinite(rl)])))
+
+
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_attention_matches_oracle(n_splits):
+    w, inp, bits, enc = case()
+    keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
+    oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
+    codes = torch.from_numpy(bg.pack_codes(oc.reshape(-1, 128)).reshape(oc.shape[:3] + (64,))).cuda()
+    norms, signs = torch.from_numpy(on).cuda(), torch.from_numpy(osg).cuda()
+    v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
+    seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
+    res = tq.qjl_attention(keys, codes, norms, signs, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale,
+                           n_splits=n_splits)
+    if n_splits > 1:
+        res = tq.merge_splits(None, *res)
+    torch.cuda.synchronize()
+    ro = np.zeros((w.batch, w.n_q_heads, 128))
+    rl = np.full((w.batch, w.n_q_heads), -np.inf)
+    vf = inp["v"].astype(np.float16).astype(np.float64)
+    for b, t in enumerate(LENS):
+        if t == 0:
+            continue
+        for h in range(w.n_q_heads):
+            kv = h // w.group_size
+            S = inp["proj"][kv].astype(np.float64)
+            qv = inp["q"][b, h].astype(np.float64)
+            s = w.scale * qjl.scores(qv, oxh[b, kv, :t], osg[b, kv, :t], orn[b, kv, :t], S)
+            m = s.max()
+            p = np.exp(s - m)
+            ro[b, h] = (p / p.sum()) @ vf[b, kv, :t]
+            rl[b, h] = m + np.log(p.sum())
+    check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, LENS)

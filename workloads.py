@@ -59,6 +59,9 @@ WORKLOADS = {
     # with fp16 values; log-normal channel scales give the blocks unequal energies
     "gtq32k": Workload("gtq32k", 4, 32, 8, 32768, 3, 16, 128, False, "float16", "lognormal", n_splits=8,
                        codec="gtq"),
+    # two-stage keys at 2 bits (1-bit MSE + 1-bit QJL residual), fp16 values
+    "qjl32k": Workload("qjl32k", 4, 32, 8, 32768, 2, 16, 128, False, "float16", "lognormal", n_splits=8,
+                       codec="qjl"),
     "zipfusion8k": Workload("zipfusion8k", 32, 32, 8, 8200, 16, 16, 128, False, "bfloat16", "seeded4x8",
                             n_splits=1, codec="zip"),
 }
@@ -163,6 +166,12 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
         k_cal *= mul_k[None]
         extra = {"q_cal": q_cal, "k_cal": k_cal,
                  "gauss": np.random.default_rng(s_rot).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32)}
+    if w.codec == "qjl":
+        # per KV head: Gaussian matrices for the MSE stage's rotation (as Block-GTQ's) and
+        # the residual's projection S (m = 128 rows)
+        s_rot, s_proj = ss.spawn(2)
+        extra = {"gauss": np.random.default_rng(s_rot).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32),
+                 "proj": np.random.default_rng(s_proj).standard_normal((hkv, HEAD_DIM, HEAD_DIM), dtype=np.float32)}
     return {
         **extra,
         "q": bf16_bits(q) if bf16 else q.astype(dt),
