@@ -539,13 +539,27 @@ def gtq_setup(w, inp, dev):
     import torch
 
     import compressed_domain_attention_amd as tq
-    energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
-    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
-    keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
     T = w.seq_len
     codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device=dev)
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device=dev)
     x = torch.from_numpy(inp["k"]).to(dev)
+    if w.codec == "qjl":  # two-stage keys: the whole prompt encoded, no append in the step
+        bits = np.full((w.n_kv_heads, 64), w.bits_k - 1, dtype=np.int32)
+        keys = tq.QjlKeys(w.bits_k - 1, inp["gauss"], inp["proj"], device=dev)
+        signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device=dev)
+        tq.qjl_quantize_keys(keys, x[:, :, :1].contiguous(), codes, norms, signs)  # loads the kernel
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.qjl_quantize_keys(keys, x, codes, norms, signs)
+        e1.record()
+        torch.cuda.synchronize()
+        v = torch.from_numpy(inp["v"]).to(dev)
+        q = torch.from_numpy(inp["q"]).to(dev)
+        return keys, bits, codes, norms, v, q, None, None, e0.elapsed_time(e1), signs
+    energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
+    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
+    keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
     prompt = x[:, :, :T - 1].contiguous()
     tq.gtq_quantize_keys(keys, prompt[:, :, :1].contiguous(), codes, norms)  # loads the kernel before timing
     torch.cuda.synchronize()
@@ -557,10 +571,11 @@ def gtq_setup(w, inp, dev):
     v = torch.from_numpy(inp["v"]).to(dev)
     q = torch.from_numpy(inp["q"]).to(dev)
     k_new, v_new = x[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous()
-    return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1)
+    return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1), None
 
 
 GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
+QJL_BYTES_PER_TOKEN_HEAD = 64 + 16 + 16 + 256  # and the residual's 128 sign bits
 
 
 def run_gtq(w, inp, steps, warmup, n_splits, check=True):
@@ -572,10 +587,12 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
     import compressed_domain_attention_amd as tq
 
     dev = torch.device("cuda:0")
-    keys, bits, codes, norms, v, q, k_new, v_new, enc_ms = gtq_setup(w, inp, dev)
-    cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
+    keys, bits, codes, norms, v, q, k_new, v_new, enc_ms, signs = gtq_setup(w, inp, dev)
+    qjl = signs is not None
+    cache = (codes, norms, v, signs) if qjl else (codes, norms, v)
+    cache_bytes = sum(t.numel() * t.element_size() for t in cache)
     reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
-    sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
+    sets = [cache] + [tuple(t.clone() for t in cache) for _ in range(reps - 1)]
     log("cache %.1f MB x %d replicas; groups per head %s" % (cache_bytes / 1e6, reps,
                                                              [keys.n_groups(h) for h in range(w.n_kv_heads)]))
     S = n_splits
@@ -585,6 +602,14 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
     pl = torch.empty((S, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
 
     def attend(i):
+        if qjl:
+            c, n, vv, sg = sets[i % reps]
+            if S == 1:
+                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, out=out, lse=lse)
+            else:
+                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=S, part_o=po,
+                                 part_lse=pl)
+            return
         c, n, vv = sets[i % reps]
         if S == 1:
             tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale, out=out,
@@ -653,11 +678,19 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
     if check:
         # two (sequence, KV head) units against the oracle's own encoding of the same keys
         from helpers import OUT_RTOL, row_rel_err
-        from oracle import attention, blockgtq as bg
+        from oracle import attention, blockgtq as bg, qjl as oq
         o = out.cpu().numpy()
         parity = 0.0
-        s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
-        for b, kv in [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
+        for b, kv in [(0, 0), (w.batch - 1, w.n_kv_heads - 1)] if qjl else []:
+            enc = oq.mse_encoders(w.bits_k - 1, inp["gauss"][kv].astype(np.float64))
+            S_ = inp["proj"][kv].astype(np.float64)
+            _, _, sg, rn, xh = oq.encode_keys(inp["k"][b, kv].astype(np.float64), enc, S_)
+            vd = inp["v"][b, kv].astype(np.float64)
+            for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+                ref = oq.attend(inp["q"][b, h].astype(np.float64), xh, sg, rn, S_, vd, w.scale)
+                parity = max(parity, float(row_rel_err(o[b, h], ref)))
+        s = None if qjl else bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
+        for b, kv in [] if qjl else [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
             enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, 1, 4),
                                    inp["gauss"][kv].astype(np.float64))
             c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)
@@ -668,7 +701,7 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
                 parity = max(parity, float(row_rel_err(o[b, h], ref)))
         if parity > OUT_RTOL:
             raise SystemExit("parity check failed: %.3e > %.1e" % (parity, OUT_RTOL))
-    algo = w.batch * w.n_kv_heads * w.seq_len * GTQ_BYTES_PER_TOKEN_HEAD
+    algo = w.batch * w.n_kv_heads * w.seq_len * (QJL_BYTES_PER_TOKEN_HEAD if qjl else GTQ_BYTES_PER_TOKEN_HEAD)
     return dict(step_ms=step_ms, attn_ms=att_ms, algo_bytes=algo, reps=reps, parity=parity, encode_ms=enc_ms,
                 widths=np.bincount(bits.ravel(), minlength=5)[1:].tolist())
 
@@ -701,15 +734,24 @@ def gtq_counter_run(w, inp, n_splits, launches=24):
         assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
     torch.cuda.synchronize()
     del src, dst
-    keys, bits, codes, norms, v, q, k_new, v_new, _ = gtq_setup(w, inp, dev)
-    cache_bytes = sum(t.numel() * t.element_size() for t in (codes, norms, v))
+    keys, bits, codes, norms, v, q, k_new, v_new, _, signs = gtq_setup(w, inp, dev)
+    cache = (codes, norms, v) if signs is None else (codes, norms, v, signs)
+    cache_bytes = sum(t.numel() * t.element_size() for t in cache)
     reps = min(256, max(2, math.ceil((1 << 30) / cache_bytes)))
-    sets = [(codes, norms, v)] + [tuple(t.clone() for t in (codes, norms, v)) for _ in range(reps - 1)]
+    sets = [cache] + [tuple(t.clone() for t in cache) for _ in range(reps - 1)]
     S = max(n_splits, 1)
     po = torch.empty((S, w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
     pl = torch.empty((S, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
     for i in range(launches):
+        if signs is not None:
+            c, n, vv, sg = sets[i % reps]
+            if n_splits == 1:
+                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, out=out)
+            else:
+                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=n_splits,
+                                 part_o=po, part_lse=pl)
+            continue
         c, n, vv = sets[i % reps]
         if n_splits == 1:
             tq.gtq_append_attention(keys, c, n, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale, out=out)
@@ -745,6 +787,21 @@ def _oracle_gtq_unit(args):
     vd = inp["v"][b, kv].astype(np.float64)
     for h in range(kv * w.group_size, (kv + 1) * w.group_size):
         attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+    return time.perf_counter() - t0
+
+
+def _oracle_qjl_unit(args):
+    w, b, kv = args
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import qjl
+    inp = _oracle_unit.inp
+    enc = qjl.mse_encoders(w.bits_k - 1, inp["gauss"][kv].astype(np.float64))
+    S = inp["proj"][kv].astype(np.float64)
+    _, _, sg, rn, xh = qjl.encode_keys(inp["k"][b, kv].astype(np.float64), enc, S)  # the stored cache (not timed)
+    t0 = time.perf_counter()
+    vd = inp["v"][b, kv].astype(np.float64)
+    for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+        qjl.attend(inp["q"][b, h].astype(np.float64), xh, sg, rn, S, vd, w.scale)
     return time.perf_counter() - t0
 
 
@@ -820,8 +877,8 @@ def cpu_baseline(w, inp, budget_s=15.0):
 
     cores = min(len(os.sched_getaffinity(0)), 16)
     _oracle_unit.inp = inp
-    zip_ = w.codec in ("zip", "gtq")
-    unit_fn = {"zip": _oracle_zip_unit, "gtq": _oracle_gtq_unit}.get(w.codec, _oracle_unit)
+    zip_ = w.codec in ("zip", "gtq", "qjl")  # units that time their own decode part
+    unit_fn = {"zip": _oracle_zip_unit, "gtq": _oracle_gtq_unit, "qjl": _oracle_qjl_unit}.get(w.codec, _oracle_unit)
     units = [(w, b, kv) if zip_ else (w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
     done, busy, t0 = 0, 0.0, time.perf_counter()
     with threadpool_limits(1):
@@ -834,7 +891,8 @@ def cpu_baseline(w, inp, budget_s=15.0):
     wall = time.perf_counter() - t0
     token_heads = done * w.seq_len
     what = {"zip": "decompress the stored pages + fp64 attention (compression of the stream not timed)",
-            "gtq": "fp64 decode of the stored keys + attention (encoding of the stream not timed)"}.get(
+            "gtq": "fp64 decode of the stored keys + attention (encoding of the stream not timed)",
+            "qjl": "fp64 two-stage scores (decoded keys + residual estimate) + attention (encoding not timed)"}.get(
         w.codec, "fp64 dequantise + attention")
     # the rate over the time the workers spent in the timed part, all workers together
     value = token_heads / (busy / cores) if zip_ else token_heads / wall
@@ -976,9 +1034,10 @@ def write_traffic(w, n_splits, fetch_csv, write_csv, commands):
 def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
     """As write_traffic, for the codec's or Block-GTQ's attention kernel
     (profiles/zip_traffic.json, profiles/gtq_traffic.json)."""
-    kname = "gtq_attention" if w.codec == "gtq" else "zip_attention"
-    out_file = GTQ_TRAFFIC_FILE if w.codec == "gtq" else ZIP_TRAFFIC_FILE
-    khash = gtq_kernel_hash() if w.codec == "gtq" else zip_kernel_hash()
+    gtq = w.codec in ("gtq", "qjl")  # one kernel source, one traffic file
+    kname = "gtq_attention" if gtq else "zip_attention"
+    out_file = GTQ_TRAFFIC_FILE if gtq else ZIP_TRAFFIC_FILE
+    khash = gtq_kernel_hash() if gtq else zip_kernel_hash()
     fc, wc = _per_dispatch(fetch_csv, "FETCH_SIZE", CALIBRATION_KERNEL), _per_dispatch(write_csv, "WRITE_SIZE", CALIBRATION_KERNEL)
     fd = _per_dispatch(fetch_csv, "FETCH_SIZE", kname)
     wd = _per_dispatch(write_csv, "WRITE_SIZE", kname)
@@ -1030,7 +1089,7 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     n_splits = args.splits if args.splits is not None else w.n_splits
     if args.write_traffic:
-        if w.codec in ("zip", "gtq"):
+        if w.codec in ("zip", "gtq", "qjl"):
             write_zip_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
         else:
             write_traffic(w, n_splits, args.write_traffic[0], args.write_traffic[1], args.commands)
@@ -1050,12 +1109,13 @@ def main():
     if args.counter_run:
         if w.codec == "zip":
             zip_counter_run(w, inp, n_splits)
-        elif w.codec == "gtq":
+        elif w.codec in ("gtq", "qjl"):
             gtq_counter_run(w, inp, n_splits)
         else:
             counter_run(w, inp, n_splits, args.schedule)
         return
-    if w.codec == "gtq":
+    if w.codec in ("gtq", "qjl"):
+        qjl = w.codec == "qjl"
         r = run_gtq(w, inp, args.steps, args.warmup, n_splits, check=not args.no_check)
         units = w.batch * w.n_kv_heads * w.seq_len
         achieved = r["algo_bytes"] / (r["attn_ms"] / 1e3) / 1e9
@@ -1067,13 +1127,19 @@ def main():
         print(json.dumps({
             "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ 4-bit key containers, fp16 values)",
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16 MFMA operands (hi + lo parts; signs exact), f32 accumulate (two-stage keys: 1-bit MSE in 4-bit "
+                     "containers + 1-bit QJL signs; fp16 values)" if qjl else
+                     "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ 4-bit key containers, fp16 values)",
             "data": "synthetic (seeded Gaussian activations with log-normal channel scales; workloads.py)",
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-                       "seq_len": w.seq_len, "keys": "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
+                       "seq_len": w.seq_len,
+                       "keys": ("two-stage, %d bits: %d-bit TQ-MSE + 1-bit QJL residual" % (w.bits_k, w.bits_k - 1))
+                       if qjl else "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
                        "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
-                       "step": "append the new token (key encoded, fp16 value) and attend over encoded keys "
-                               "and fp16 values in one launch" + (", then merge" if n_splits > 1 else ""),
+                       "step": ("attention over two-stage keys and fp16 values" if qjl else
+                                "append the new token (key encoded, fp16 value) and attend over encoded keys "
+                                "and fp16 values in one launch") + (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": gtq_measured_traffic(w.name, n_splits),
