@@ -1,12 +1,13 @@
 """Parity at the benchmark sizes, in the launch configuration bench.py times, on sampled outputs.
 
 Each test builds one benchmark workload at its full size (isoquant32k: B=8, T=32768, TQ3 with
-SO(4); zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys),
+SO(4); zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys;
+qjl32k: B=4, T=32768, two-stage keys),
 runs the step bench.py times (append of slot T-1 fused into the attention launch where the
 format has one, the same sections, then the merge) and compares every query head of three
 (sequence, KV head) units with the oracle, which encodes and attends over those units alone.
 Bars: 2e-3 per row for the packed cache (fp16 weights, the tolerance of the other packed-cache
-parity tests), 1e-4 for the lossless codec and for Block-GTQ (hi + lo fp16 operands).
+parity tests), 1e-4 for the lossless codec, Block-GTQ and two-stage keys (hi + lo fp16 operands).
 """
 
 import time
@@ -18,7 +19,7 @@ import torch
 import compressed_domain_attention_amd as tq
 import workloads
 from helpers import OUT_RTOL, row_rel_err
-from oracle import attention, blockgtq as bg, codebook, quant, zipcodec as zc
+from oracle import attention, blockgtq as bg, codebook, qjl, quant, zipcodec as zc
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +135,35 @@ def test_gtq32k_step():
         vd = inp["v"][b, kv].astype(np.float64)
         for h in range(kv * w.group_size, (kv + 1) * w.group_size):
             ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            worst = max(worst, float(row_rel_err(out[b, h], ref)))
+    print("worst row error %.2e" % worst, flush=True)
+    assert worst <= EXACT_RTOL
+
+
+def test_qjl32k_step():
+    w = workloads.WORKLOADS["qjl32k"]
+    announce(w.name, w)
+    inp = workloads.generate(w, 0)
+    T, S = w.seq_len, w.n_splits
+    keys = tq.QjlKeys(w.bits_k - 1, inp["gauss"], inp["proj"])
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device="cuda")
+    signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device="cuda")
+    tq.qjl_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, signs)
+    v = torch.from_numpy(inp["v"]).cuda()
+    q = torch.from_numpy(inp["q"]).cuda()
+    po, pl = tq.qjl_attention(keys, codes, norms, signs, v, q, max_len=T, scale=w.scale, n_splits=S)
+    out, lse = tq.merge_splits(None, po, pl)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    worst = 0.0
+    for b, kv in units(w):
+        enc = qjl.mse_encoders(w.bits_k - 1, inp["gauss"][kv].astype(np.float64))
+        Sm = inp["proj"][kv].astype(np.float64)
+        _, _, sg, rn, xh = qjl.encode_keys(inp["k"][b, kv].astype(np.float64), enc, Sm)
+        vd = inp["v"][b, kv].astype(np.float64)
+        for h in range(kv * w.group_size, (kv + 1) * w.group_size):
+            ref = qjl.attend(inp["q"][b, h].astype(np.float64), xh, sg, rn, Sm, vd, w.scale)
             worst = max(worst, float(row_rel_err(out[b, h], ref)))
     print("worst row error %.2e" % worst, flush=True)
     assert worst <= EXACT_RTOL
