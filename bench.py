@@ -543,20 +543,22 @@ def gtq_setup(w, inp, dev):
     codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device=dev)
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device=dev)
     x = torch.from_numpy(inp["k"]).to(dev)
-    if w.codec == "qjl":  # two-stage keys: the whole prompt encoded, no append in the step
+    if w.codec == "qjl":  # two-stage keys
         bits = np.full((w.n_kv_heads, 64), w.bits_k - 1, dtype=np.int32)
         keys = tq.QjlKeys(w.bits_k - 1, inp["gauss"], inp["proj"], device=dev)
         signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device=dev)
-        tq.qjl_quantize_keys(keys, x[:, :, :1].contiguous(), codes, norms, signs)  # loads the kernel
+        prompt = x[:, :, :T - 1].contiguous()
+        tq.qjl_quantize_keys(keys, prompt[:, :, :1].contiguous(), codes, norms, signs)  # loads the kernel
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        tq.qjl_quantize_keys(keys, x, codes, norms, signs)
+        tq.qjl_quantize_keys(keys, prompt, codes, norms, signs)
         e1.record()
         torch.cuda.synchronize()
         v = torch.from_numpy(inp["v"]).to(dev)
         q = torch.from_numpy(inp["q"]).to(dev)
-        return keys, bits, codes, norms, v, q, None, None, e0.elapsed_time(e1), signs
+        k_new, v_new = x[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous()
+        return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1), signs
     energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
     bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
     keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
@@ -605,10 +607,11 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
         if qjl:
             c, n, vv, sg = sets[i % reps]
             if S == 1:
-                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, out=out, lse=lse)
+                tq.qjl_append_attention(keys, c, n, sg, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale,
+                                        out=out, lse=lse)
             else:
-                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=S, part_o=po,
-                                 part_lse=pl)
+                tq.qjl_append_attention(keys, c, n, sg, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale,
+                                        n_splits=S, part_o=po, part_lse=pl)
             return
         c, n, vv = sets[i % reps]
         if S == 1:
@@ -747,10 +750,11 @@ def gtq_counter_run(w, inp, n_splits, launches=24):
         if signs is not None:
             c, n, vv, sg = sets[i % reps]
             if n_splits == 1:
-                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, out=out)
+                tq.qjl_append_attention(keys, c, n, sg, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale,
+                                        out=out)
             else:
-                tq.qjl_attention(keys, c, n, sg, vv, q, max_len=w.seq_len, scale=w.scale, n_splits=n_splits,
-                                 part_o=po, part_lse=pl)
+                tq.qjl_append_attention(keys, c, n, sg, vv, k_new, v_new, q, pos0=w.seq_len - 1, scale=w.scale,
+                                        n_splits=n_splits, part_o=po, part_lse=pl)
             continue
         c, n, vv = sets[i % reps]
         if n_splits == 1:
@@ -1137,9 +1141,8 @@ def main():
                        "keys": ("two-stage, %d bits: %d-bit TQ-MSE + 1-bit QJL residual" % (w.bits_k, w.bits_k - 1))
                        if qjl else "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
                        "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
-                       "step": ("attention over two-stage keys and fp16 values" if qjl else
-                                "append the new token (key encoded, fp16 value) and attend over encoded keys "
-                                "and fp16 values in one launch") + (", then merge" if n_splits > 1 else ""),
+                       "step": "append the new token (key encoded, fp16 value) and attend over encoded keys "
+                               "and fp16 values in one launch" + (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": gtq_measured_traffic(w.name, n_splits),

@@ -18,7 +18,7 @@ __all__ = [
     "quantize_append", "decode_attention", "merge_splits", "library", "LIB_PATH",
     "zip_store", "zip_compress", "zip_attention",
     "gtq_block_energies", "gtq_allocate", "GtqKeys", "gtq_quantize_keys", "gtq_attention", "gtq_append_attention",
-    "QjlKeys", "qjl_quantize_keys", "qjl_attention",
+    "QjlKeys", "qjl_quantize_keys", "qjl_attention", "qjl_append_attention",
     "TQ_KEYS", "TQ_VALUES",
 ]
 
@@ -82,7 +82,7 @@ EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_qua
            "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
            "tq_zip_compress", "tq_zip_attention", "tq_gtq_block_energies", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
            "tq_gtq_attention", "tq_gtq_append_attention", "tq_gtq_qjl_projection", "tq_gtq_qjl_quantize_keys",
-           "tq_gtq_qjl_attention")
+           "tq_gtq_qjl_attention", "tq_gtq_qjl_append_attention")
 
 
 def library():
@@ -136,6 +136,9 @@ def library():
     lib.tq_gtq_qjl_quantize_keys.restype = I
     lib.tq_gtq_qjl_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_gtq_qjl_attention.restype = I
+    lib.tq_gtq_qjl_append_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P, P,
+                                                P, P, P]
+    lib.tq_gtq_qjl_append_attention.restype = I
     _lib = lib
     return lib
 
@@ -639,4 +642,45 @@ def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_le
         _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(codes), _ptr(norms), _ptr(signs), _ptr(v), cap,
         bsz, hkv, _ptr(q), _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse),
         _ptr(part_o), _ptr(part_lse), _stream()), "tq_gtq_qjl_attention")
+    return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+def qjl_append_attention(enc: QjlKeys, codes, norms, signs, v, k_new, v_new, q, pos=None, pos0: int = 0,
+                         max_pos: int = None, scale=None, n_splits=1, out=None, lse=None, part_o=None,
+                         part_lse=None):
+    """gtq_append_attention for two-stage keys: the new key's codes, norm, sign bits and
+    coefficient and its value written at pos (or pos0), then attention, in one launch."""
+    if v.dtype != torch.float16 or not v.is_contiguous() or v.dim() != 4 or v.shape[3] != HEAD_DIM:
+        raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    hkv, cap = v.shape[1], v.shape[2]
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+            tuple(norms.shape) != (bsz, hkv, cap, 4) or tuple(signs.shape) != (bsz, hkv, cap, 16):
+        raise ValueError("codes, norms, signs and v must describe the same [batch, n_kv_heads, capacity] cache")
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x.dtype != k_new.dtype or x.dtype not in _DTYPES or not x.is_contiguous() or \
+                tuple(x.shape) != (bsz, hkv, HEAD_DIM):
+            raise ValueError("%s must be contiguous [batch, n_kv_heads, 128] of k_new's dtype" % name)
+    if pos is not None and (pos.dtype != torch.int32 or pos.numel() != bsz):
+        raise ValueError("pos must be int32 [batch]")
+    if max_pos is None:
+        max_pos = int(pos.max().item()) if pos is not None else pos0
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = q.device
+    if n_splits == 1:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    _check(library().tq_gtq_qjl_append_attention(
+        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(codes), _ptr(norms), _ptr(signs), _ptr(v), cap,
+        bsz, hkv, _ptr(k_new), _ptr(v_new), _DTYPES[k_new.dtype], _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype],
+        hq, scale, n_splits, _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()),
+        "tq_gtq_qjl_append_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)

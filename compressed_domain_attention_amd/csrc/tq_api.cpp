@@ -457,13 +457,12 @@ extern "C" tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float*
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes,
-                                             float* norms, void* v, int32_t capacity, int32_t batch,
-                                             int32_t n_kv_heads, const void* k_new, const void* v_new,
-                                             tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
-                                             const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
-                                             int32_t n_splits, float* out, float* lse_out, float* part_o,
-                                             float* part_lse, void* stream) {
+static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                 uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
+                                 int32_t batch, int32_t n_kv_heads, const void* k_new, const void* v_new,
+                                 tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos, const void* q,
+                                 tq_dtype q_dtype, int32_t n_q_heads, float scale, int32_t n_splits, float* out,
+                                 float* lse_out, float* part_o, float* part_lse, void* stream) {
   if (k_new == nullptr || v_new == nullptr) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
   if (pos0 < 0 || (pos != nullptr && max_pos < 0)) return TQ_EINVAL;
@@ -483,5 +482,34 @@ extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const flo
   a.w_codes = codes;
   a.w_norms = norms;
   a.w_v = v;
+  a.proj = proj;
+  a.signs = signs;
+  a.w_signs = signs;
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes,
+                                             float* norms, void* v, int32_t capacity, int32_t batch,
+                                             int32_t n_kv_heads, const void* k_new, const void* v_new,
+                                             tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
+                                             const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
+                                             int32_t n_splits, float* out, float* lse_out, float* part_o,
+                                             float* part_lse, void* stream) {
+  return gtq_append_step(heads, rotations, nullptr, codes, norms, nullptr, v, capacity, batch, n_kv_heads, k_new,
+                         v_new, x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads, scale, n_splits, out, lse_out,
+                         part_o, part_lse, stream);
+}
+
+extern "C" tq_status tq_gtq_qjl_append_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                                 uint8_t* codes, float* norms, uint8_t* signs, void* v,
+                                                 int32_t capacity, int32_t batch, int32_t n_kv_heads,
+                                                 const void* k_new, const void* v_new, tq_dtype x_dtype,
+                                                 const int32_t* pos, int32_t pos0, int32_t max_pos, const void* q,
+                                                 tq_dtype q_dtype, int32_t n_q_heads, float scale, int32_t n_splits,
+                                                 float* out, float* lse_out, float* part_o, float* part_lse,
+                                                 void* stream) {
+  if (proj == nullptr || signs == nullptr) return TQ_EINVAL;
+  return gtq_append_step(heads, rotations, proj, codes, norms, signs, v, capacity, batch, n_kv_heads, k_new, v_new,
+                         x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads, scale, n_splits, out, lse_out, part_o,
+                         part_lse, stream);
 }

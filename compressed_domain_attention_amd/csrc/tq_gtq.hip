@@ -294,13 +294,16 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const size_t st = (size_t)b * a.n_kv_heads + kv, rec = st * a.capacity + p;
       const float* grot = a.rotations + (size_t)kv * TQ_GTQ_ROTATION_FLOATS;
       _Float16* vd = (_Float16*)a.w_v + rec * 128;
+      // two-stage keys: also the sign bits (M^T read from global memory)
+      const float* pj = QJL ? a.proj + (size_t)kv * 128 * 128 : nullptr;
+      uint8_t* srec = QJL ? a.w_signs + rec * 16 : nullptr;
       if (a.x_f16) {
-        encode_key<true>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
-                         a.w_norms + rec * 4, lane);
+        encode_key<true, QJL>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
+                              a.w_norms + rec * 4, lane, pj, srec);
         ((uint32_t*)vd)[lane] = ((const uint32_t*)a.v_new)[st * 64 + lane];
       } else {
-        encode_key<false>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
-                          a.w_norms + rec * 4, lane);
+        encode_key<false, QJL>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
+                               a.w_norms + rec * 4, lane, pj, srec);
         const float2 x = ((const float2*)a.v_new)[st * 64 + lane];
         ((uint32_t*)vd)[lane] = pack_f16(x.x, x.y);
       }

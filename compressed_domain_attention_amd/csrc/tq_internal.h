@@ -179,6 +179,7 @@ struct GtqAttnArgs {
   // [batch][n_kv_heads][capacity][16]
   const float* proj;
   const uint8_t* signs;
+  uint8_t* w_signs;         // writable, for the fused append of two-stage keys
 };
 
 struct MergeArgs {

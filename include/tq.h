@@ -446,6 +446,18 @@ tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotatio
                                   int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
                                   void* stream);
 
+/* The decode step with its new token over two-stage keys: as tq_gtq_append_attention, with
+ * the new key's sign bits and residual coefficient written too (tq_gtq_qjl_quantize_keys'
+ * encoding, bit for bit) and attention as tq_gtq_qjl_attention.  Errors: those of
+ * tq_gtq_append_attention; TQ_EINVAL for a null proj or signs. */
+tq_status tq_gtq_qjl_append_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                      uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
+                                      int32_t batch, int32_t n_kv_heads, const void* k_new, const void* v_new,
+                                      tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
+                                      const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
+                                      int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

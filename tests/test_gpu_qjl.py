@@ -138,3 +138,50 @@ def test_attention_matches_oracle(n_splits):
             ro[b, h] = (p / p.sum()) @ vf[b, kv, :t]
             rl[b, h] = m + np.log(p.sum())
     check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, LENS)
+
+
+def device_cache(w, inp, keys):
+    shp = (w.batch, w.n_kv_heads, w.seq_len)
+    codes = torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")
+    signs = torch.zeros(shp + (16,), dtype=torch.uint8, device="cuda")
+    tq.qjl_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, signs)
+    return codes, norms, signs, torch.from_numpy(inp["v"].astype(np.float16)).cuda()
+
+
+def same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+def test_append_step_equals_encode_then_attend(per_row):
+    # one launch against encoding the new key (and writing its value) then attending: bit
+    # for bit, cache and outputs; fp16 new tokens for one slot, fp32 for per-row slots
+    lens = [320, 320, 320]
+    w, inp, bits, enc = case(lens=lens)
+    keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
+    rng = np.random.default_rng(9)
+    dt = np.float32 if per_row else np.float16
+    k_new = torch.from_numpy((rng.standard_normal((3, w.n_kv_heads, 128)) * 2).astype(dt)).cuda()
+    v_new = torch.from_numpy(rng.standard_normal((3, w.n_kv_heads, 128)).astype(dt)).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
+    a = device_cache(w, inp, keys)
+    b = tuple(t.clone() for t in a)
+    if per_row:
+        pos = [299, 0, 150]
+        pos_d = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        res_a = tq.qjl_append_attention(keys, *a, k_new, v_new, q, pos=pos_d, scale=w.scale, n_splits=3)
+        for r, p in enumerate(pos):
+            tq.qjl_quantize_keys(keys, k_new[r:r + 1, :, None, :].contiguous(), b[0][r:r + 1], b[1][r:r + 1],
+                                 b[2][r:r + 1], pos0=p)
+            b[3][r, :, p] = v_new[r].half()
+        res_b = tq.qjl_attention(keys, *b, q, seq_lens=pos_d + 1, max_len=max(pos) + 1, scale=w.scale, n_splits=3)
+    else:
+        P = 250
+        res_a = tq.qjl_append_attention(keys, *a, k_new, v_new, q, pos0=P, scale=w.scale, n_splits=3)
+        tq.qjl_quantize_keys(keys, k_new[:, :, None, :].contiguous(), b[0], b[1], b[2], pos0=P)
+        b[3][:, :, P] = v_new
+        res_b = tq.qjl_attention(keys, *b, q, max_len=P + 1, scale=w.scale, n_splits=3)
+    torch.cuda.synchronize()
+    assert same(a, b)
+    assert same(res_a, res_b)
