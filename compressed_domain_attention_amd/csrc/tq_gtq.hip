@@ -216,12 +216,14 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   constexpr int WAVE_LDS = D * STAGE;
   static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
   static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
-  constexpr int TAB_BYTES = kMaxKb * 256 * 8 + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
+  // k-blocks: up to 7 for a Block-GTQ head; two-stage keys have one group of 128 (4 blocks)
+  constexpr int KB = QJL ? 4 : kMaxKb;
+  constexpr int TAB_BYTES = KB * 256 * 8 + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
   uint2(*const ptab)[256] = (uint2(*)[256])lds_all;
   uint8_t* const lds = lds_all + TAB_BYTES;
-  uint8_t* const pmtab = lds_all + kMaxKb * 256 * 8;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
+  uint8_t* const pmtab = lds_all + KB * 256 * 8;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
   // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
@@ -319,9 +321,9 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     for (int g = 0; g < TQ_GTQ_MAX_GROUPS; ++g)
       cum[g + 1] = cum[g] + (g < ng ? (__builtin_amdgcn_readfirstlane(hd.dim[g]) + 31) / 32 : 0);
   }
-  const int nkb = min(cum[TQ_GTQ_MAX_GROUPS], kMaxKb);
+  const int nkb = min(cum[TQ_GTQ_MAX_GROUPS], KB);
   auto group_of_block = [&](int kb) { return (kb >= cum[1]) + (kb >= cum[2]) + (kb >= cum[3]); };
-  for (int i = tid; i < kMaxKb * 256; i += 64 * NW) {
+  for (int i = tid; i < KB * 256; i += 64 * NW) {
     const int kb = i >> 8, by = i & 255, g = kb < nkb ? group_of_block(kb) : 0;
     // codes past the codebook decode to 0
     const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
@@ -397,11 +399,11 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]; and per block its
   // group (uniform) and the byte of the lane's first code (reads past a record's 64 bytes
   // stay inside the stage and meet zero query)
-  u32x4 qa[kMaxKb], qb[kMaxKb];
-  int kgrp[kMaxKb];
-  uint32_t kbyte[kMaxKb];
+  u32x4 qa[KB], qb[KB];
+  int kgrp[KB];
+  uint32_t kbyte[KB];
 #pragma unroll
-  for (int kb = 0; kb < kMaxKb; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int g = kb < nkb ? group_of_block(kb) : 0, m = kb < nkb ? kb - cum[g] : 0;
     const int dg = hd.dim[g], sg = hd.start[g];
     kgrp[kb] = g;
@@ -446,18 +448,18 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     const uint8_t* rec = sb + 64 * col;
     // every block is computed (those past the head's last have zero tables and query), so
     // the unrolled loop is one basic block the compiler can interleave
-    uint32_t cb[kMaxKb];
+    uint32_t cb[KB];
 #pragma unroll
-    for (int kb = 0; kb < kMaxKb; ++kb) {  // every code word first
+    for (int kb = 0; kb < KB; ++kb) {  // every code word first
       const uint32_t bo = kbyte[kb];
       // the 4 code bytes from two aligned words (the byte offset is any multiple of 1)
       const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
       cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
     }
     // key operands straight from the table reads: [hi pair, lo pair] of two bytes each
-    u32x4 ka[kMaxKb], kb2[kMaxKb];
+    u32x4 ka[KB], kb2[KB];
 #pragma unroll
-    for (int kb = 0; kb < kMaxKb; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
       const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
       ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     }
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < kMaxKb; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
       f32x4 cur = mfma_f16(ka[kb], qa[kb], f32x4{0.f, 0.f, 0.f, 0.f});
       cur = mfma_f16(kb2[kb], qb[kb], cur);
