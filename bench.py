@@ -546,6 +546,7 @@ def gtq_setup(w, inp, dev):
     if w.codec == "qjl":  # two-stage keys
         bits = np.full((w.n_kv_heads, 64), w.bits_k - 1, dtype=np.int32)
         keys = tq.QjlKeys(w.bits_k - 1, inp["gauss"], inp["proj"], device=dev)
+        codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device=dev)
         signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device=dev)
         prompt = x[:, :, :T - 1].contiguous()
         tq.qjl_quantize_keys(keys, prompt[:, :, :1].contiguous(), codes, norms, signs)  # loads the kernel
@@ -577,7 +578,10 @@ def gtq_setup(w, inp, dev):
 
 
 GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
-QJL_BYTES_PER_TOKEN_HEAD = 64 + 16 + 16 + 256  # and the residual's 128 sign bits
+# two-stage keys: first-stage codes (16 bytes of bits at one bit, else 64 of nibbles), the
+# norm slots, the residual's 128 sign bits, fp16 values
+def qjl_bytes_per_token_head(w):
+    return (16 if w.bits_k - 1 == 1 else 64) + 16 + 16 + 256
 
 
 def run_gtq(w, inp, steps, warmup, n_splits, check=True):
@@ -704,7 +708,7 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
                 parity = max(parity, float(row_rel_err(o[b, h], ref)))
         if parity > OUT_RTOL:
             raise SystemExit("parity check failed: %.3e > %.1e" % (parity, OUT_RTOL))
-    algo = w.batch * w.n_kv_heads * w.seq_len * (QJL_BYTES_PER_TOKEN_HEAD if qjl else GTQ_BYTES_PER_TOKEN_HEAD)
+    algo = w.batch * w.n_kv_heads * w.seq_len * (qjl_bytes_per_token_head(w) if qjl else GTQ_BYTES_PER_TOKEN_HEAD)
     return dict(step_ms=step_ms, attn_ms=att_ms, algo_bytes=algo, reps=reps, parity=parity, encode_ms=enc_ms,
                 widths=np.bincount(bits.ravel(), minlength=5)[1:].tolist())
 
@@ -1132,8 +1136,8 @@ def main():
             "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
-            "dtype": "f16 MFMA operands (hi + lo parts; signs exact), f32 accumulate (two-stage keys: 1-bit MSE in 4-bit "
-                     "containers + 1-bit QJL signs; fp16 values)" if qjl else
+            "dtype": "f16 MFMA operands (hi + lo query parts against exact +-1 codes and signs), f32 accumulate "
+                     "(two-stage keys: 1-bit MSE codes + 1-bit QJL signs, 16 bytes each; fp16 values)" if qjl else
                      "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ 4-bit key containers, fp16 values)",
             "data": "synthetic (seeded Gaussian activations with log-normal channel scales; workloads.py)",
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,

@@ -132,12 +132,12 @@ def library():
     lib.tq_gtq_append_attention.restype = I
     lib.tq_gtq_qjl_projection.argtypes = [P, P, P, P]
     lib.tq_gtq_qjl_projection.restype = I
-    lib.tq_gtq_qjl_quantize_keys.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P]
+    lib.tq_gtq_qjl_quantize_keys.argtypes = [P, P, P, I, P, I, I, I, I, I, I, P, P, P, P]
     lib.tq_gtq_qjl_quantize_keys.restype = I
-    lib.tq_gtq_qjl_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
+    lib.tq_gtq_qjl_attention.argtypes = [P, P, P, I, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_gtq_qjl_attention.restype = I
-    lib.tq_gtq_qjl_append_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P, P,
-                                                P, P, P]
+    lib.tq_gtq_qjl_append_attention.argtypes = [P, P, P, I, P, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P,
+                                                P, P, P, P]
     lib.tq_gtq_qjl_append_attention.restype = I
     _lib = lib
     return lib
@@ -480,7 +480,8 @@ class GtqKeys:
 class QjlKeys(GtqKeys):
     """Two-stage key encoders: a one-group Block-GTQ head at `bits` bits (the MSE stage,
     rotation from gauss[h, bits-1]) and the QJL projection S [n_kv_heads, 128, 128] of the
-    residual, held as (S Q)^T per head."""
+    residual, held as (S Q)^T per head.  At bits == 1 the codes are stored as bits, 16 bytes
+    per key (code_bytes); otherwise as gtq_quantize_keys' 64 bytes."""
 
     def __init__(self, bits, gauss, S, device="cuda"):
         import numpy as np
@@ -489,7 +490,11 @@ class QjlKeys(GtqKeys):
         sp = np.ascontiguousarray(S, dtype=np.float32)
         if sp.shape != (hkv, 128, 128):
             raise ValueError("S must be float32 [n_kv_heads, 128, 128]")
+        if bits not in (1, 2, 3):
+            raise ValueError("the first stage takes 1, 2 or 3 bits")
         super().__init__(np.full((hkv, 64), bits, dtype=np.int32), g, device)
+        self.mse_bits = bits
+        self.code_bytes = 16 if bits == 1 else 64
         rot = self.rotations.cpu().numpy()
         proj = np.zeros((hkv, 128 * 128), dtype=np.float32)
         for h in range(hkv):
@@ -594,19 +599,22 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
 
 def qjl_quantize_keys(enc: QjlKeys, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, signs: torch.Tensor,
                       pos0: int = 0):
-    """Two-stage encoding of x [batch, n_kv_heads, n_new, 128] (fp16/fp32): codes and norms as
-    gtq_quantize_keys (norm slot 1: the residual's coefficient), signs uint8 [batch,
-    n_kv_heads, capacity, 16]."""
+    """Two-stage encoding of x [batch, n_kv_heads, n_new, 128] (fp16/fp32): codes uint8
+    [batch, n_kv_heads, capacity, enc.code_bytes], norms as gtq_quantize_keys (norm slot 1:
+    the residual's coefficient), signs uint8 [batch, n_kv_heads, capacity, 16]."""
     if x.dtype not in _DTYPES or not x.is_contiguous() or x.dim() != 4 or x.shape[3] != HEAD_DIM:
         raise ValueError("x must be contiguous [batch, n_kv_heads, n_new, 128] float16/float32")
     bsz, hkv, n_new = x.shape[:3]
     cap = codes.shape[2]
-    if hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or codes.dtype != torch.uint8 or \
+    cb = enc.code_bytes
+    if hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, cb) or codes.dtype != torch.uint8 or \
             tuple(norms.shape) != (bsz, hkv, cap, 4) or norms.dtype != torch.float32 or \
             tuple(signs.shape) != (bsz, hkv, cap, 16) or signs.dtype != torch.uint8 or \
             not (codes.is_contiguous() and norms.is_contiguous() and signs.is_contiguous()):
-        raise ValueError("codes uint8 [b, kv, cap, 64], norms float32 [b, kv, cap, 4], signs uint8 [b, kv, cap, 16]")
-    _check(library().tq_gtq_qjl_quantize_keys(_ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(x),
+        raise ValueError("codes uint8 [b, kv, cap, %d], norms float32 [b, kv, cap, 4], signs uint8 [b, kv, cap, 16]"
+                         % cb)
+    _check(library().tq_gtq_qjl_quantize_keys(_ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), enc.mse_bits,
+                                              _ptr(x),
                                               _DTYPES[x.dtype], bsz, hkv, n_new, pos0, cap, _ptr(codes),
                                               _ptr(norms), _ptr(signs), _stream()), "tq_gtq_qjl_quantize_keys")
 
@@ -620,7 +628,7 @@ def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_le
         raise ValueError("q must be a contiguous float16/float32 tensor")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
-    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
             tuple(norms.shape) != (bsz, hkv, cap, 4) or tuple(signs.shape) != (bsz, hkv, cap, 16):
         raise ValueError("codes, norms, signs and v must describe the same [batch, n_kv_heads, capacity] cache")
     if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
@@ -639,7 +647,8 @@ def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_le
         if part_lse is None:
             part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
     _check(library().tq_gtq_qjl_attention(
-        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(codes), _ptr(norms), _ptr(signs), _ptr(v), cap,
+        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), enc.mse_bits, _ptr(codes), _ptr(norms), _ptr(signs),
+        _ptr(v), cap,
         bsz, hkv, _ptr(q), _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse),
         _ptr(part_o), _ptr(part_lse), _stream()), "tq_gtq_qjl_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)
@@ -656,7 +665,7 @@ def qjl_append_attention(enc: QjlKeys, codes, norms, signs, v, k_new, v_new, q, 
         raise ValueError("q must be a contiguous float16/float32 tensor")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
-    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
             tuple(norms.shape) != (bsz, hkv, cap, 4) or tuple(signs.shape) != (bsz, hkv, cap, 16):
         raise ValueError("codes, norms, signs and v must describe the same [batch, n_kv_heads, capacity] cache")
     for name, x in (("k_new", k_new), ("v_new", v_new)):
@@ -679,7 +688,8 @@ def qjl_append_attention(enc: QjlKeys, codes, norms, signs, v, k_new, v_new, q, 
         if part_lse is None:
             part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
     _check(library().tq_gtq_qjl_append_attention(
-        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), _ptr(codes), _ptr(norms), _ptr(signs), _ptr(v), cap,
+        _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), enc.mse_bits, _ptr(codes), _ptr(norms), _ptr(signs),
+        _ptr(v), cap,
         bsz, hkv, _ptr(k_new), _ptr(v_new), _DTYPES[k_new.dtype], _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype],
         hq, scale, n_splits, _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()),
         "tq_gtq_qjl_append_attention")

@@ -37,6 +37,14 @@ __device__ __forceinline__ T lds_read(const uint8_t* p) {
 }
 
 // Copies one head's encoder into LDS (all threads of the block take part).
+// bit k of x (k < 16) moves to bit 2k
+__device__ __forceinline__ uint32_t spread_bits(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return (x | (x << 1)) & 0x55555555u;
+}
+
 __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* src) {
   constexpr int words = sizeof(tq_gtq_head) / 4;
   for (int i = threadIdx.x; i < words; i += blockDim.x) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
@@ -50,14 +58,17 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
 // QJL (two-stage keys, one group): also the m = 128 sign bits of S r into sign_rec and
 // sqrt(pi/2)/m |r| into norm slot 1, from the rotated-domain residual e = y - c_hat
 // (S r = |x| M e with M = S Q; proj[j][i] = M[i][j], in LDS or global memory).
-template <bool XF16, bool QJL = false>
+// B1 (one-bit first stage): the 128 codes are written as 16 bytes of bits instead (code of
+// position i in byte i/8 at bit i mod 8, as the sign bits) and compared against the first
+// boundary only, so every code is 0 or 1 whatever the head's width.
+template <bool XF16, bool QJL = false, bool B1 = false>
 __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* rot, const void* x, float* ubuf,
                                            uint8_t* code_rec, float* norm_rec, int lane, const float* proj = nullptr,
                                            uint8_t* sign_rec = nullptr) {
   const int j0 = 2 * lane;
   const int g = group_of(hd, j0);
   const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
-  const int nb = (1 << hd.width[g]) - 1;
+  const int nb = B1 ? 1 : (1 << hd.width[g]) - 1;
   float x0, x1;
   if (XF16) {
     x0 = (float)((const _Float16*)x)[hd.coord[j0]];
@@ -95,7 +106,16 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
     c0 += y0 > hd.boundary[g][k];
     c1 += y1 > hd.boundary[g][k];
   }
-  code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
+  if (B1) {
+    // bit l of m0 (m1) is the code of position 2l (2l + 1): word w interleaves bits
+    // 16 w .. 16 w + 15 of both
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(c0 != 0), m1 = __builtin_amdgcn_ballot_w64(c1 != 0);
+    if (lane < 4)
+      ((uint32_t*)code_rec)[lane] = spread_bits((uint32_t)(m0 >> (16 * lane)) & 0xFFFFu) |
+                                    (spread_bits((uint32_t)(m1 >> (16 * lane)) & 0xFFFFu) << 1);
+  } else {
+    code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
+  }
   float coef = 0.f;
   if (QJL) {
     const float e0 = y0 - hd.centroid[0][c0], e1 = y1 - hd.centroid[0][c1];
@@ -126,8 +146,9 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
 // group-order positions 2l and 2l + 1 (always in one group: groups start at even positions
 // and have even sizes).
 constexpr int kQuantTokens = 512;
-template <bool XF16, bool QJL>
+template <bool XF16, bool QJL, bool B1>
 __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a) {
+  constexpr int CREC = B1 ? 16 : 64;  // code bytes per key
   __shared__ __attribute__((aligned(16))) float rot[TQ_GTQ_ROTATION_FLOATS];
   __shared__ __attribute__((aligned(16))) float projl[QJL ? 128 * 128 : 1];
   __shared__ __attribute__((aligned(16))) float ubuf[4][128];
@@ -149,8 +170,9 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
     const int i = tile * kQuantTokens + t;
     if (i >= a.n_new) break;
     const size_t rec = stream * a.capacity + a.pos0 + i;
-    encode_key<XF16, QJL>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4), ubuf[wv],
-                          a.codes + rec * 64, a.norms + rec * 4, lane, projl, QJL ? a.signs + rec * 16 : nullptr);
+    encode_key<XF16, QJL, B1>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4),
+                              ubuf[wv], a.codes + rec * CREC, a.norms + rec * 4, lane, projl,
+                              QJL ? a.signs + rec * 16 : nullptr);
     // the next token's writes to ubuf follow this token's reads in program order
     __builtin_amdgcn_wave_barrier();
   }
@@ -207,8 +229,14 @@ constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil
 // QJL: two-stage keys (one MSE group plus sign bits of the projected residual): four more
 // k-blocks whose key operands are +-1 (exact in fp16, from a table indexed by a sign byte)
 // against the projected query S q = M Q^T q, times the coefficient in norm slot 1.
-template <int NW, int D, bool QF16, bool QJL>
+// B1 (one-bit first stage, 16 code bytes per key): the two levels c0 < c1 are written as
+// mid + half (2 bit - 1), so <q~, c[code]> = mid sum_j q~_j + half sum_j q~_j (+-1)_j: four
+// more +-1 products against half q~, plus mid sum_j q~_j added per head, replace the pair
+// tables.
+template <int NW, int D, bool QF16, bool QJL, bool B1 = false>
 __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
+  static_assert(!B1 || QJL, "one-bit codes are the first stage of two-stage keys");
+  constexpr int CREC = B1 ? 16 : 64;  // code bytes per key
   // a stage: key records 1 KB, norms 256 B (group-major), values 4 KB, sign bytes 256 B
   constexpr int STAGE = QJL ? 5632 : 5376;
   constexpr int NORM_AT = 1024, VAL_AT = 1280, SIGN_AT = 5376;
@@ -218,12 +246,13 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
   // k-blocks: up to 7 for a Block-GTQ head; two-stage keys have one group of 128 (4 blocks)
   constexpr int KB = QJL ? 4 : kMaxKb;
-  constexpr int TAB_BYTES = KB * 256 * 8 + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
+  constexpr int PTAB_BYTES = B1 ? 0 : KB * 256 * 8;
+  constexpr int TAB_BYTES = PTAB_BYTES + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
   uint2(*const ptab)[256] = (uint2(*)[256])lds_all;
   uint8_t* const lds = lds_all + TAB_BYTES;
-  uint8_t* const pmtab = lds_all + KB * 256 * 8;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
+  uint8_t* const pmtab = lds_all + PTAB_BYTES;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
   // their lo parts; zero for the blocks past the head's last, which then add nothing)
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   const int n = ntiles > wv ? (ntiles - wv + NW - 1) / NW : 0;  // this wave's tiles
 
   const size_t row0 = ((size_t)b * a.n_kv_heads + kv) * a.capacity;
-  const uint8_t* kc = a.codes + row0 * 64;
+  const uint8_t* kc = a.codes + row0 * CREC;
   const uint8_t* kn = (const uint8_t*)(a.norms + row0 * 4);
   const uint8_t* vbp = (const uint8_t*)a.v + row0 * 256;
   const uint8_t* sgb = QJL ? a.signs + row0 * 16 : nullptr;
@@ -262,7 +291,10 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     const int t0 = tok0_of(s);
     const uint32_t dst = wlds_a + (s % D) * STAGE;
     int t = t0 + (lane >> 2);
-    lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
+    if (B1)  // 16 tokens' code bytes (lane: token tok0 + l/4, 4 bytes)
+      lds_dma<4, true>(dst, kc, t < cap ? (uint32_t)(t * 16 + 4 * (lane & 3)) : (uint32_t)(t0 * 16));
+    else
+      lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
     t = t0 + (lane & 15);
     lds_dma<4, true>(dst + NORM_AT, kn, t < cap ? (uint32_t)(t * 16 + 4 * (lane >> 4)) : (uint32_t)(t0 * 16));
 #pragma unroll
@@ -300,12 +332,12 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const float* pj = QJL ? a.proj + (size_t)kv * 128 * 128 : nullptr;
       uint8_t* srec = QJL ? a.w_signs + rec * 16 : nullptr;
       if (a.x_f16) {
-        encode_key<true, QJL>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
-                              a.w_norms + rec * 4, lane, pj, srec);
+        encode_key<true, QJL, B1>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds,
+                                  a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
         ((uint32_t*)vd)[lane] = ((const uint32_t*)a.v_new)[st * 64 + lane];
       } else {
-        encode_key<false, QJL>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds, a.w_codes + rec * 64,
-                               a.w_norms + rec * 4, lane, pj, srec);
+        encode_key<false, QJL, B1>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds,
+                                   a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
         const float2 x = ((const float2*)a.v_new)[st * 64 + lane];
         ((uint32_t*)vd)[lane] = pack_f16(x.x, x.y);
       }
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   }
   const int nkb = min(cum[TQ_GTQ_MAX_GROUPS], KB);
   auto group_of_block = [&](int kb) { return (kb >= cum[1]) + (kb >= cum[2]) + (kb >= cum[3]); };
-  for (int i = tid; i < KB * 256; i += 64 * NW) {
+  for (int i = tid; i < (B1 ? 0 : KB * 256); i += 64 * NW) {
     const int kb = i >> 8, by = i & 255, g = kb < nkb ? group_of_block(kb) : 0;
     // codes past the codebook decode to 0
     const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
@@ -395,6 +427,28 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       qq[m] = u32x4{x[0], x[1], x[2], x[3]};
     }
   }
+  // B1: half s q~ as +-1 operands (block m's positions 32 m + 8 jr .. + 7, fp16 hi in columns
+  // 0-7, lo in 8-15) and mid s sum_j q~_j for the hi columns (qt holds q~ / s)
+  u32x4 qm[B1 ? 4 : 1];
+  float moff = 0.f;
+  if (B1) {
+    const float s0 = hd.f16_scale[0], c0 = hd.centroid[0][0], c1 = hd.centroid[0][1];
+    const float hf = 0.5f * (c1 - c0) * s0, md = 0.5f * (c0 + c1) * s0;
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = qt[col & 7][32 * m + 8 * jr + 2 * e], v1 = qt[col & 7][32 * m + 8 * jr + 2 * e + 1];
+        part += v0 + v1;
+        x[e] = col >= 8 ? pack_f16(f16_lo(hf * v0), f16_lo(hf * v1)) : pack_f16(hf * v0, hf * v1);
+      }
+      qm[m] = u32x4{x[0], x[1], x[2], x[3]};
+    }
+    part = sum_rows(part);
+    moff = col < 8 ? md * part : 0.f;
+  }
   // query operands: block kb's positions 8 jr .. + 3 (qa) and + 4 .. + 7 (qb), each pair
   // twice, matching key operands [hi pair, lo pair, hi pair, lo pair]; and per block its
   // group (uniform) and the byte of the lane's first code (reads past a record's 64 bytes
@@ -409,7 +463,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     kgrp[kb] = g;
     kbyte[kb] = (uint32_t)((sg + 32 * m + 8 * jr) >> 1);
     qa[kb] = qb[kb] = u32x4{0u, 0u, 0u, 0u};
-    if (kb < nkb) {
+    if (!B1 && kb < nkb) {
       const int hh = col & 7;
       uint32_t x[4];
 #pragma unroll
@@ -423,8 +477,10 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       qb[kb] = u32x4{x[2], x[2], x[3], x[3]};
     }
   }
-  asm volatile("" ::"v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "v"(qa[4]), "v"(qa[5]), "v"(qa[6]));
-  asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]), "v"(qb[4]), "v"(qb[5]), "v"(qb[6]));
+  if (!B1) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) asm volatile("" ::"v"(qa[kb]), "v"(qb[kb]));
+  }
   vm_wait<0>();
   for (int s = 0; s < D; ++s)
     if (s < n) issue(s);
@@ -445,38 +501,52 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     const uint8_t* sb = wlds + (s % D) * STAGE;
 
     // ---- scores: the key operand row is token col; lane's k slots are codes 8 jr .. + 7
-    const uint8_t* rec = sb + 64 * col;
-    // every block is computed (those past the head's last have zero tables and query), so
-    // the unrolled loop is one basic block the compiler can interleave
-    uint32_t cb[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {  // every code word first
-      const uint32_t bo = kbyte[kb];
-      // the 4 code bytes from two aligned words (the byte offset is any multiple of 1)
-      const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
-      cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
-    }
-    // key operands straight from the table reads: [hi pair, lo pair] of two bytes each
-    u32x4 ka[KB], kb2[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
-      const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
-      ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
-      kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
-    }
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (B1) {  // code bytes as +-1 operands against half q~, then + mid sum q~, times the norm
+      f32x4 cm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
-      f32x4 cur = mfma_f16(ka[kb], qa[kb], f32x4{0.f, 0.f, 0.f, 0.f});
-      cur = mfma_f16(kb2[kb], qb[kb], cur);
-      // times the group norms of the lane's tokens 4 jr .. + 3
-      const float4 nr = lds_read<float4>(sb + NORM_AT + 64 * kgrp[kb] + 16 * jr);
-      sc[0] = fmaf(nr.x, cur[0], sc[0]);
-      sc[1] = fmaf(nr.y, cur[1], sc[1]);
-      sc[2] = fmaf(nr.z, cur[2], sc[2]);
-      sc[3] = fmaf(nr.w, cur[3], sc[3]);
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t by = lds_read<uint8_t>(sb + 16 * col + 4 * m + jr);
+        cm = mfma_f16(lds_read<u32x4>(pmtab + 16 * by), qm[m], cm);
+      }
+      const float4 nr = lds_read<float4>(sb + NORM_AT + 16 * jr);
+      sc[0] = nr.x * (cm[0] + moff);
+      sc[1] = nr.y * (cm[1] + moff);
+      sc[2] = nr.z * (cm[2] + moff);
+      sc[3] = nr.w * (cm[3] + moff);
+    } else {
+      const uint8_t* rec = sb + 64 * col;
+      // every block is computed (those past the head's last have zero tables and query), so
+      // the unrolled loop is one basic block the compiler can interleave
+      uint32_t cb[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {  // every code word first
+        const uint32_t bo = kbyte[kb];
+        // the 4 code bytes from two aligned words (the byte offset is any multiple of 1)
+        const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
+        cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
+      }
+      // key operands straight from the table reads: [hi pair, lo pair] of two bytes each
+      u32x4 ka[KB], kb2[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
+        const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
+        ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
+        kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        // (c_hi + c_lo) (q_hi + q_lo): both key parts against both query columns
+        f32x4 cur = mfma_f16(ka[kb], qa[kb], f32x4{0.f, 0.f, 0.f, 0.f});
+        cur = mfma_f16(kb2[kb], qb[kb], cur);
+        // times the group norms of the lane's tokens 4 jr .. + 3
+        const float4 nr = lds_read<float4>(sb + NORM_AT + 64 * kgrp[kb] + 16 * jr);
+        sc[0] = fmaf(nr.x, cur[0], sc[0]);
+        sc[1] = fmaf(nr.y, cur[1], sc[1]);
+        sc[2] = fmaf(nr.z, cur[2], sc[2]);
+        sc[3] = fmaf(nr.w, cur[3], sc[3]);
+      }
     }
     if (QJL) {  // the residual's estimate: sign operands against S q, times slot 1
       f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -602,12 +672,16 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 
 hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream) {
   const dim3 grid((a.n_new + kQuantTokens - 1) / kQuantTokens, a.n_kv_heads, batch), block(256);
-  if (a.signs) {
-    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true>), grid, block, 0, stream, a);
+  if (a.bit1 && !a.signs) return hipErrorInvalidValue;
+  if (a.bit1) {
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true, true>), grid, block, 0, stream, a);
+  } else if (a.signs) {
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true, false>), grid, block, 0, stream, a);
   } else {
-    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_quantize_kernel<false, false>), grid, block, 0, stream, a);
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -616,7 +690,11 @@ hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t st
   constexpr int NW = 8, D = 2;
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
   if (a.heads_per_slice > 8) return hipErrorInvalidValue;
-  if (a.signs) {
+  if (a.bit1 && !a.signs) return hipErrorInvalidValue;
+  if (a.bit1) {
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, true, true>), grid, block, 0, stream, a);
+  } else if (a.signs) {
     if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, true>), grid, block, 0, stream, a);
   } else {

@@ -140,6 +140,7 @@ struct GtqQuantArgs {
   int32_t capacity;
   const float* proj;        // two-stage keys: [n_kv_heads][128][128], (S Q)^T; else NULL
   uint8_t* signs;           // two-stage keys: [batch][n_kv_heads][capacity][16]; else NULL
+  int32_t bit1;             // two-stage keys with a one-bit first stage: codes [..][16] of bits
 };
 
 struct GtqAttnArgs {
@@ -180,6 +181,7 @@ struct GtqAttnArgs {
   const float* proj;
   const uint8_t* signs;
   uint8_t* w_signs;         // writable, for the fused append of two-stage keys
+  int32_t bit1;             // two-stage keys with a one-bit first stage: codes [..][16] of bits
 };
 
 struct MergeArgs {

@@ -406,18 +406,28 @@ tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, con
  * S r (bit i of the 128 in byte i/8 at bit i mod 8; a zero projection counts as +) into
  * signs [batch][n_kv_heads][capacity][16] and sqrt(pi/2)/128 |r| into norm slot 1.
  *   proj: device [n_kv_heads][128 * 128] from tq_gtq_qjl_projection.
- * Errors: those of tq_gtq_quantize_keys; TQ_EINVAL for a null proj or signs. */
-tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj, const void* x,
+ *   mse_bits: the first stage's width, which the heads were prepared with (1, 2 or 3; b - 1
+ *      for b-bit keys, "TurboQuant ... MNN on phones", 3.2).  At 1 the codes are stored as
+ *      bits, codes [batch][n_kv_heads][capacity][16], code of position i in byte i/8 at bit
+ *      i mod 8 (a 2-bit key then takes 32 bytes of codes and signs); at 2 and 3 they are
+ *      tq_gtq_quantize_keys' [capacity][64] bytes.  A value other than the heads' width
+ *      gives wrong codes but no access outside the buffers.
+ * Errors: those of tq_gtq_quantize_keys; TQ_EINVAL for a null proj or signs or mse_bits
+ * outside 1..3. */
+tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj,
+                                   int32_t mse_bits, const void* x,
                                    tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0,
                                    int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, void* stream);
 
 /* Decode attention over two-stage keys and fp16 values: as tq_gtq_attention, with each
  * score <q, x_hat> + sqrt(pi/2)/128 |r| sum_i (S q)_i sgn((S r)_i) (the projected query
  * S q = M Q^T q is formed once per workgroup; the signs are exact in fp16).  Arguments and
- * errors as tq_gtq_attention, plus proj and signs as tq_gtq_qjl_quantize_keys (TQ_EINVAL
- * when null). */
+ * errors as tq_gtq_attention, plus proj, mse_bits (the codes' layout) and signs as
+ * tq_gtq_qjl_quantize_keys (TQ_EINVAL when null or out of range).  With one-bit codes the
+ * first stage's score is mid sum_j q~_j + half sum_j q~_j (+-1)_j for its two levels
+ * mid -+ half, again with exact +-1 operands. */
 tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
-                               const uint8_t* codes, const float* norms, const uint8_t* signs, const void* v,
+                               int32_t mse_bits, const uint8_t* codes, const float* norms, const uint8_t* signs, const void* v,
                                int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q, tq_dtype q_dtype,
                                int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
                                int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse,
@@ -449,9 +459,9 @@ tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotatio
 /* The decode step with its new token over two-stage keys: as tq_gtq_append_attention, with
  * the new key's sign bits and residual coefficient written too (tq_gtq_qjl_quantize_keys'
  * encoding, bit for bit) and attention as tq_gtq_qjl_attention.  Errors: those of
- * tq_gtq_append_attention; TQ_EINVAL for a null proj or signs. */
+ * tq_gtq_append_attention; TQ_EINVAL for a null proj or signs or mse_bits outside 1..3. */
 tq_status tq_gtq_qjl_append_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
-                                      uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
+                                      int32_t mse_bits, uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
                                       int32_t batch, int32_t n_kv_heads, const void* k_new, const void* v_new,
                                       tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
                                       const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,

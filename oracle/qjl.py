@@ -49,6 +49,23 @@ def unpack_signs(packed, m=HEAD_DIM):
     return np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=-1, bitorder="little", count=m).astype(bool)
 
 
+def pack_codes(codes, bits):
+    """The first stage's codes [T, 128] as stored: at 1 bit the 128 bits in 16 bytes (code of
+    position i in byte i // 8 at bit i % 8, the sign bits' order); at 2-3 bits Block-GTQ's
+    64 bytes of nibbles."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if bits == 1:
+        assert c.max(initial=0) <= 1
+        return pack_signs(c == 1)
+    return blockgtq.pack_codes(c)
+
+
+def unpack_codes(packed, bits):
+    if bits == 1:
+        return unpack_signs(packed).astype(np.uint8)
+    return blockgtq.unpack_codes(packed)
+
+
 def encode_residual(r, S):
     """QJL of residuals r [T, d] with projection S [m, d] -> (sign bytes [T, m/8], |r| [T])."""
     r = np.asarray(r, dtype=np.float64)

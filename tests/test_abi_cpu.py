@@ -421,19 +421,22 @@ def test_qjl_projection_matches_oracle(lib):
 
 def test_qjl_call_validation(lib):
     qk = lib.tq_gtq_qjl_quantize_keys
-    assert qk(FAKE, FAKE, None, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, FAKE, None) == TQ_EINVAL   # no projection
-    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, None, None) == TQ_EINVAL   # no signs
-    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 4, 30, 32, FAKE, FAKE, FAKE, None) == TQ_ECAPACITY
-    assert qk(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, 32, FAKE, FAKE, FAKE, None) == TQ_OK     # nothing launched
+    assert qk(FAKE, FAKE, None, 1, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, FAKE, None) == TQ_EINVAL   # no projection
+    assert qk(FAKE, FAKE, FAKE, 1, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, None, None) == TQ_EINVAL   # no signs
+    for bad in (0, 4):  # the first stage's width
+        assert qk(FAKE, FAKE, FAKE, bad, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, FAKE, None) == TQ_EINVAL
+    assert qk(FAKE, FAKE, FAKE, 1, FAKE, 1, 1, 1, 4, 30, 32, FAKE, FAKE, FAKE, None) == TQ_ECAPACITY
+    assert qk(FAKE, FAKE, FAKE, 2, FAKE, 1, 1, 1, 0, 0, 32, FAKE, FAKE, FAKE, None) == TQ_OK     # nothing launched
     at = lib.tq_gtq_qjl_attention
 
     def call(**kw):
-        a = dict(proj=FAKE, signs=FAKE, codes=FAKE, max_len=64, splits=1, out=FAKE)
+        a = dict(proj=FAKE, bits=1, signs=FAKE, codes=FAKE, max_len=64, splits=1, out=FAKE)
         a.update(kw)
-        return at(FAKE, FAKE, a["proj"], a["codes"], FAKE, a["signs"], FAKE, 64, 1, 2, FAKE, 1, 8, None,
+        return at(FAKE, FAKE, a["proj"], a["bits"], a["codes"], FAKE, a["signs"], FAKE, 64, 1, 2, FAKE, 1, 8, None,
                   a["max_len"], 0.1, a["splits"], a["out"], None, FAKE, FAKE, None)
     assert call(proj=None) == TQ_EINVAL and call(signs=None) == TQ_EINVAL and call(codes=None) == TQ_EINVAL
     assert call(out=None) == TQ_EINVAL and call(max_len=65) == TQ_ECAPACITY
+    assert call(bits=0) == TQ_EINVAL and call(bits=4) == TQ_EINVAL
 
 
 def test_product_path_has_no_cpu_fallback():

@@ -2,7 +2,7 @@
 
 Each test builds one benchmark workload at its full size (isoquant32k: B=8, T=32768, TQ3 with
 SO(4); zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys;
-qjl32k: B=4, T=32768, two-stage keys),
+qjl32k: B=4, T=32768, two-stage keys with one-bit first-stage codes),
 runs the step bench.py times (append of slot T-1 fused into the attention launch where the
 format has one, the same sections, then the merge) and compares every query head of three
 (sequence, KV head) units with the oracle, which encodes and attends over those units alone.
@@ -146,7 +146,7 @@ def test_qjl32k_step():
     inp = workloads.generate(w, 0)
     T, S = w.seq_len, w.n_splits
     keys = tq.QjlKeys(w.bits_k - 1, inp["gauss"], inp["proj"])
-    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device="cuda")
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device="cuda")
     signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device="cuda")
     tq.qjl_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, signs)

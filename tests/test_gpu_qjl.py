@@ -1,6 +1,8 @@
 """GPU parity of two-stage keys (1-bit TQ-MSE + 1-bit QJL residual, oracle/qjl.py) through the
 C ABI.
 
+Both stored layouts of the first stage: one-bit codes as 16 bytes of bits (2-bit keys) and
+2-bit codes in 64 bytes of nibbles (3-bit keys).
 Encoding: MSE codes equal the oracle's except coordinates within 2e-6 of a boundary (at most
 1e-4 of them), the MSE norm within 1e-6 relative, the residual coefficient
 sqrt(pi/2)/128 |r| within 1e-4 relative (keys with a boundary code excluded: their residual
@@ -20,7 +22,7 @@ import torch
 import compressed_domain_attention_amd as tq
 import workloads
 from helpers import row_rel_err
-from oracle import blockgtq as bg, qjl
+from oracle import qjl
 
 pytestmark = pytest.mark.gpu
 
@@ -36,12 +38,13 @@ def gpu():
     tq.library()
 
 
-def case(lens=LENS, cap=320, hq=32, hkv=8, seed=0):
-    w = replace(workloads.WORKLOADS["qjl32k"], batch=len(lens), n_q_heads=hq, n_kv_heads=hkv, seq_len=cap)
+def case(lens=LENS, cap=320, hq=32, hkv=8, seed=0, bits_k=2):
+    w = replace(workloads.WORKLOADS["qjl32k"], batch=len(lens), n_q_heads=hq, n_kv_heads=hkv, seq_len=cap,
+                bits_k=bits_k)
     inp = workloads.generate(w, seed)
     bits = w.bits_k - 1  # the MSE stage
     enc = [qjl.mse_encoders(bits, inp["gauss"][h].astype(np.float64)) for h in range(hkv)]
-    print("qjl case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, flush=True)
+    print("qjl case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, "bits", bits_k, flush=True)
     return w, inp, bits, enc
 
 
@@ -59,11 +62,13 @@ def oracle_records(w, inp, enc):
     return codes, norms, signs, rn, xh
 
 
-def test_encoding_matches_oracle():
-    w, inp, bits, enc = case()
+@pytest.mark.parametrize("bits_k", [2, 3])
+def test_encoding_matches_oracle(bits_k):
+    w, inp, bits, enc = case(bits_k=bits_k)
     keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
     shp = (w.batch, w.n_kv_heads, w.seq_len)
-    codes = torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")
+    cb = keys.code_bytes
+    codes = torch.zeros(shp + (cb,), dtype=torch.uint8, device="cuda")
     norms = torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")
     signs = torch.zeros(shp + (16,), dtype=torch.uint8, device="cuda")
     x = torch.from_numpy(inp["k"]).cuda()
@@ -71,7 +76,7 @@ def test_encoding_matches_oracle():
     tq.qjl_quantize_keys(keys, x[:, :, 100:].contiguous(), codes, norms, signs, pos0=100)
     torch.cuda.synchronize()
     oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
-    got = bg.unpack_codes(codes.cpu().numpy().reshape(-1, 64)).reshape(oc.shape)
+    got = qjl.unpack_codes(codes.cpu().numpy().reshape(-1, cb), bits).reshape(oc.shape)
     bad = got != oc
     assert bad.mean() <= 1e-4, bad.mean()
     n = norms.cpu().numpy()
@@ -107,12 +112,13 @@ def check(out, lse, ro, rl, lens):
     assert worst <= RTOL and worst_lse <= LSE_ATOL + LSE_RTOL * float(np.max(np.abs(rl[np.isfinite(rl)])))
 
 
-@pytest.mark.parametrize("n_splits", [1, 3])
-def test_attention_matches_oracle(n_splits):
-    w, inp, bits, enc = case()
+@pytest.mark.parametrize("n_splits,bits_k", [(1, 2), (3, 2), (3, 3)])
+def test_attention_matches_oracle(n_splits, bits_k):
+    w, inp, bits, enc = case(bits_k=bits_k)
     keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
     oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
-    codes = torch.from_numpy(bg.pack_codes(oc.reshape(-1, 128)).reshape(oc.shape[:3] + (64,))).cuda()
+    packed = qjl.pack_codes(oc.reshape(-1, 128), bits)
+    codes = torch.from_numpy(packed.reshape(oc.shape[:3] + (keys.code_bytes,))).cuda()
     norms, signs = torch.from_numpy(on).cuda(), torch.from_numpy(osg).cuda()
     v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
     q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
@@ -142,7 +148,7 @@ def test_attention_matches_oracle(n_splits):
 
 def device_cache(w, inp, keys):
     shp = (w.batch, w.n_kv_heads, w.seq_len)
-    codes = torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros(shp + (keys.code_bytes,), dtype=torch.uint8, device="cuda")
     norms = torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")
     signs = torch.zeros(shp + (16,), dtype=torch.uint8, device="cuda")
     tq.qjl_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, signs)
@@ -153,12 +159,12 @@ def same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("per_row", [False, True])
-def test_append_step_equals_encode_then_attend(per_row):
+@pytest.mark.parametrize("per_row,bits_k", [(False, 2), (True, 2), (True, 3)])
+def test_append_step_equals_encode_then_attend(per_row, bits_k):
     # one launch against encoding the new key (and writing its value) then attending: bit
     # for bit, cache and outputs; fp16 new tokens for one slot, fp32 for per-row slots
     lens = [320, 320, 320]
-    w, inp, bits, enc = case(lens=lens)
+    w, inp, bits, enc = case(lens=lens, bits_k=bits_k)
     keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
     rng = np.random.default_rng(9)
     dt = np.float32 if per_row else np.float16

@@ -91,6 +91,36 @@ def test_sign_packing_and_zero_residual():
     assert qjl.estimate(rng.standard_normal(128), signs, rn, S)[0] == 0.0
 
 
+def test_stored_codes_layout():
+    # one-bit codes: position i in byte i // 8 at bit i % 8; wider ones: Block-GTQ nibbles
+    rng = np.random.default_rng(7)
+    c1 = (rng.random((5, 128)) < 0.5).astype(np.uint8)
+    p1 = qjl.pack_codes(c1, 1)
+    assert p1.shape == (5, 16) and np.array_equal(qjl.unpack_codes(p1, 1), c1)
+    one = np.zeros((1, 128), np.uint8)
+    one[0, 13] = 1  # byte 1, bit 5
+    assert list(qjl.pack_codes(one, 1)[0, :3]) == [0, 32, 0]
+    c2 = rng.integers(0, 4, (5, 128)).astype(np.uint8)
+    p2 = qjl.pack_codes(c2, 2)
+    assert p2.shape == (5, 64) and np.array_equal(qjl.unpack_codes(p2, 2), c2)
+    with pytest.raises(AssertionError):
+        qjl.pack_codes(c2, 1)
+
+
+def test_one_bit_levels_split_into_midpoint_and_signs():
+    # the decomposition the one-bit attention uses: <q, c[code]> = mid sum q + half <q, +-1>
+    rng = np.random.default_rng(8)
+    enc = qjl.mse_encoders(1, rng.standard_normal((4, 128, 128)))
+    cent = np.asarray(enc[0][3], dtype=np.float64)
+    assert cent.shape == (2,) and cent[0] < 0 < cent[1]
+    x, q = rng.standard_normal((9, 128)), rng.standard_normal(128)
+    codes, nu, _, _, xh = qjl.encode_keys(x, enc, rng.standard_normal((128, 128)))
+    qt = enc[0][2].T @ q  # the rotated query, group order
+    mid, half = cent.mean(), (cent[1] - cent[0]) / 2
+    got = nu * (mid * qt.sum() + half * ((2.0 * codes - 1.0) @ qt))
+    assert np.allclose(got, xh @ q, rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("seed", [5, 6])
 def test_attend_is_softmax_over_the_two_stage_scores(seed):
     rng = np.random.default_rng(seed)
