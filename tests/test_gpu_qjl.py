@@ -112,8 +112,10 @@ def check(out, lse, ro, rl, lens):
     assert worst <= RTOL and worst_lse <= LSE_ATOL + LSE_RTOL * float(np.max(np.abs(rl[np.isfinite(rl)])))
 
 
-@pytest.mark.parametrize("n_splits,bits_k", [(1, 2), (3, 2), (3, 3)])
-def test_attention_matches_oracle(n_splits, bits_k):
+@pytest.mark.parametrize("n_splits,bits_k,q_dtype", [(1, 2, np.float16), (3, 2, np.float16), (3, 3, np.float16),
+                                                     (3, 2, np.float32)])
+def test_attention_matches_oracle(n_splits, bits_k, q_dtype):
+    # fp32 queries carry the same (fp16-representable) values: the oracle is unchanged
     w, inp, bits, enc = case(bits_k=bits_k)
     keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
     oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
@@ -121,7 +123,7 @@ def test_attention_matches_oracle(n_splits, bits_k):
     codes = torch.from_numpy(packed.reshape(oc.shape[:3] + (keys.code_bytes,))).cuda()
     norms, signs = torch.from_numpy(on).cuda(), torch.from_numpy(osg).cuda()
     v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
-    q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
+    q = torch.from_numpy(inp["q"].astype(np.float16).astype(q_dtype)).cuda()
     seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
     res = tq.qjl_attention(keys, codes, norms, signs, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale,
                            n_splits=n_splits)
@@ -137,7 +139,7 @@ def test_attention_matches_oracle(n_splits, bits_k):
         for h in range(w.n_q_heads):
             kv = h // w.group_size
             S = inp["proj"][kv].astype(np.float64)
-            qv = inp["q"][b, h].astype(np.float64)
+            qv = inp["q"][b, h].astype(np.float16).astype(np.float64)
             s = w.scale * qjl.scores(qv, oxh[b, kv, :t], osg[b, kv, :t], orn[b, kv, :t], S)
             m = s.max()
             p = np.exp(s - m)
