@@ -82,23 +82,26 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
     newk = kx[:, :, T - 1:T].contiguous()
     newv = vx[:, :, T - 1:T].contiguous()
 
-    # prefill: the whole prompt quantised in one call per tensor (after one small call that
-    # loads the kernels, so the timing excludes code-object loading)
+    # prefill: the whole prompt (T - 1 tokens: slot T - 1 is the step's) quantised into both
+    # caches in one launch, timed alone with events on the launch stream (the contiguous
+    # prompt tensors exist before the timed region; one small call first loads the kernels)
     k0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev)
     v0 = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev)
-    tq.quantize_append(rot, k0, newk, pos0=0)
-    tq.quantize_append(rot, v0, newv, pos0=0)
+    tq.quantize_append_kv(rot, k0, v0, newk, newv, pos0=0)
+    pk = kx[:, :, :T - 1].contiguous() if T > 1 else kx
+    pv = vx[:, :, :T - 1].contiguous() if T > 1 else vx
+    del kx, vx
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    tq.quantize_append(rot, k0, kx[:, :, :T - 1].contiguous() if T > 1 else kx)
-    tq.quantize_append(rot, v0, vx[:, :, :T - 1].contiguous() if T > 1 else vx)
+    tq.quantize_append_kv(rot, k0, v0, pk, pv)
     e1.record()
     torch.cuda.synchronize()
     prefill_ms = e0.elapsed_time(e1)
-    in_bytes = 2 * (T - 1) * w.batch * w.n_kv_heads * 128 * kx.element_size()
-    out_bytes = 2 * (T - 1) * w.batch * w.n_kv_heads * bytes_per_token_head(w) // 2
-    del kx, vx
+    n_pre = pk.shape[2]
+    in_bytes = 2 * n_pre * w.batch * w.n_kv_heads * 128 * pk.element_size()
+    out_bytes = n_pre * w.batch * w.n_kv_heads * bytes_per_token_head(w)
+    del pk, pv
 
     cache_bytes = sum(t.numel() * t.element_size() for t in (k0.codes, k0.norms, v0.codes, v0.norms))
     # replicas totalling >= 1 GiB defeat the 256 MB last-level cache (capped for tiny caches,
@@ -876,16 +879,34 @@ def _oracle_unit(args):
     return time.perf_counter() - t0
 
 
+# Worker processes of the CPU baseline: the host cores this process may run on, capped at
+# the CPU share of one GPU on the benchmark hosts (16 cores per GPU).
+CPU_SHARE = 16
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, budget_s=15.0):
-    """The oracle decode (dequantise every K/V vector of a stream, plain fp64 softmax
-    attention for its query heads) on whole (sequence, KV head) streams of the same
-    workload, one stream per worker process, until about budget_s of work is done."""
+    """The oracle decode on whole (sequence, KV head) streams of the same workload, one stream
+    per worker process, until about budget_s of work is done.  Every codec times the same part
+    in its worker: decoding the stored stream (dequantise, or decompress, or decode the keys)
+    plus fp64 attention for the stream's query heads; encoding the stream is not timed.  The
+    rate is the streams' token*heads over the workers' busy time divided by the workers."""
     import multiprocessing as mp
     from threadpoolctl import threadpool_limits
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, CPU_SHARE)
     _oracle_unit.inp = inp
-    zip_ = w.codec in ("zip", "gtq", "qjl")  # units that time their own decode part
+    zip_ = w.codec in ("zip", "gtq", "qjl")
     unit_fn = {"zip": _oracle_zip_unit, "gtq": _oracle_gtq_unit, "qjl": _oracle_qjl_unit}.get(w.codec, _oracle_unit)
     units = [(w, b, kv) if zip_ else (w, b, kv, 0) for b in range(w.batch) for kv in range(w.n_kv_heads)]
     done, busy, t0 = 0, 0.0, time.perf_counter()
@@ -898,16 +919,16 @@ def cpu_baseline(w, inp, budget_s=15.0):
                 done += len(batch)
     wall = time.perf_counter() - t0
     token_heads = done * w.seq_len
-    what = {"zip": "decompress the stored pages + fp64 attention (compression of the stream not timed)",
-            "gtq": "fp64 decode of the stored keys + attention (encoding of the stream not timed)",
-            "qjl": "fp64 two-stage scores (decoded keys + residual estimate) + attention (encoding not timed)"}.get(
+    what = {"zip": "decompress the stored pages + fp64 attention",
+            "gtq": "fp64 decode of the stored keys + attention",
+            "qjl": "fp64 two-stage scores (decoded keys + residual estimate) + attention"}.get(
         w.codec, "fp64 dequantise + attention")
-    # the rate over the time the workers spent in the timed part, all workers together
-    value = token_heads / (busy / cores) if zip_ else token_heads / wall
-    return {"value": value, "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d (sequence, KV head) streams of %s (T=%d), %s, "
-                      "%d worker processes x 1 thread, %.1fs wall" % (done, len(units), w.name, w.seq_len, what,
-                                                                       cores, wall)}
+    return {"value": token_heads / (busy / cores), "unit": "KV token·heads/s", "cores": cores, "kind": "oracle",
+            "affinity_cores": affinity, "cpu_model": cpu_model(),
+            "sample": "%d of %d (sequence, KV head) streams of %s (T=%d): %s (encoding of the stream not timed), "
+                      "%d worker processes x 1 thread (the host's %d available cores capped at the %d-core CPU share "
+                      "of one GPU), rate over the workers' busy time %.1fs, %.1fs wall" % (
+                          done, len(units), w.name, w.seq_len, what, cores, affinity, CPU_SHARE, busy, wall)}
 
 
 def stream_read_probe_gbs():
@@ -1069,6 +1090,33 @@ def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
         w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
 
 
+# the packed-cache configurations timed after the headline, in the same run and JSON line
+OTHER_CONFIGS = ("long128k", "batched", "gqa8k", "tiny")
+
+
+def config_summary(w, r, n_splits, probe):
+    """One configuration's numbers: the decode launch against the HBM roofline (algorithmic
+    bytes = codes + norms of every (token, KV head)), the whole step's rate, the sampled
+    oracle check and the one-launch prefill of the prompt."""
+    units = w.batch * w.n_kv_heads * w.seq_len
+    algo = units * bytes_per_token_head(w)
+    achieved = algo / (r["decode_ms"] / 1e3) / 1e9
+    out = {
+        "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "seq_len": w.seq_len,
+        "bits_k": w.bits_k, "bits_v": w.bits_v, "group": w.group, "so4": w.so4, "n_splits": n_splits,
+        "value": units / (r["ms_per_step"] / 1e3), "unit": "KV token·heads/s", "ms_per_step": r["ms_per_step"],
+        "decode_kernel_ms": r["decode_ms"], "algorithmic_bytes_per_launch": algo,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "probe_frac": achieved / probe,
+                     "traffic": measured_traffic(w.name, n_splits)},
+        "prefill_ms": r["prefill_ms"], "prefill_GBps": r["prefill_bytes"] / 1e6 / r["prefill_ms"],
+        "parity_worst_row_rel_err": r["parity"], "cache_replicas": r["reps"],
+    }
+    if r["cache_bytes"] * r["reps"] < (1 << 30):
+        out["note"] = "cache-resident (%d bytes x %d replicas): a launch-latency figure" % (r["cache_bytes"], r["reps"])
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1088,6 +1136,8 @@ def main():
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--counter-run into profiles/decode_traffic.json")
     ap.add_argument("--commands", default="", help="the profiling commands, recorded with --write-traffic")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline configuration (the others are timed after it by default)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -1214,6 +1264,22 @@ def main():
     algo_bytes = units * bytes_per_token_head(w)
     achieved = algo_bytes / (r["decode_ms"] / 1e3) / 1e9
     probe = stream_read_probe_gbs()
+    # every other packed-cache configuration, each with its own section count: the decode
+    # launch's roofline fraction, the step rate and a sampled oracle check, in the same line
+    others = {}
+    if w.name == HEADLINE and not args.headline_only:
+        del inp
+        for name in OTHER_CONFIGS:
+            torch.cuda.empty_cache()
+            w2 = workloads.WORKLOADS[name]
+            log("config %s: %s, splits %d" % (name, w2, w2.n_splits))
+            inp2 = workloads.generate(w2, 0)
+            r2 = run_gpu(w2, inp2, args.steps, args.warmup, w2.n_splits, args.schedule, check=not args.no_check)
+            del inp2
+            others[name] = config_summary(w2, r2, w2.n_splits, probe)
+            log("  step %.4f ms, decode kernel %.4f ms -> %.0f GB/s (%.1f%% of 8 TB/s); parity %s" % (
+                r2["ms_per_step"], r2["decode_ms"], others[name]["roofline"]["achieved"],
+                100 * others[name]["roofline"]["frac"], r2["parity"]))
     log("step %.3f ms, decode kernel %.3f ms -> %.0f GB/s (%.1f%% of 8 TB/s, %.1f%% of the %.0f GB/s stream-read "
         "probe); prefill %.3f ms for %.2f GB (%.0f GB/s)" % (
             r["ms_per_step"], r["decode_ms"], achieved, 100 * achieved / HBM_PEAK_GBS, 100 * achieved / probe, probe,
@@ -1245,6 +1311,8 @@ def main():
         "stream_read_probe_GBps": probe,
         "parity_worst_row_rel_err": r["parity"],
     }
+    if others:
+        line["configs"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -690,9 +692,19 @@ struct Block {
 };
 
 // Lazy softmax rescale: the running maximum is only moved when a block raises it by more
-// than 2^3, so p = 2^(s - m) stays below 8 and p * norm inside the fp16 range for value
-// group norms below 8188.
+// than 2^3, so p = 2^(s - m) stays below 8.
 constexpr float kRescaleLog2 = 3.0f;
+// The value weight p * norm is rounded to fp16 for the matrix product.  Its range is kept by
+// a power of two 2^-E folded into the softmax offset (the weights and their sum carry the
+// same factor, so it cancels in the output and is added back to the lse).  E moves lazily,
+// per 32-token block: when some weight of the block exceeds 2^15 or none reaches 2^-10, E is
+// reset so that the block's largest weight lies in [2^3, 2^4).  Every block's largest
+// weights are then normal fp16 numbers (full precision), and a weight that falls to fp16's
+// subnormal range is below 2^-4 of its block's largest, with an absolute error of at most
+// 2^-25.  E is clamped to [-90, 90], so that the weights and their fp32 sum stay finite at
+// any cache length (value group norms up to about 2^100).
+constexpr float kWeightHi = 32768.0f, kWeightLo = 0.0009765625f;  // 2^15, 2^-10
+constexpr int kWeightTop = 3;                                       // largest weight to [2^3, 2^4)
 
 // Maximum / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), with the gfx950
 // row swaps: each returns the pair {x[l], x[l ^ 16]} (or ^ 32) as two values, and max and
@@ -991,8 +1003,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   };
 
   // running maximum (prescaled units), sum, the rescale bound m_run + 2^3 (prescaled) and
-  // the exponent offset -m_run (log2 units) plus the dead-column mask
+  // the exponent offset -m_run - ve (log2 units) plus the dead-column mask; ve is the
+  // wave-uniform exponent E of the value weights' scale 2^-E
   float m_run = -INFINITY, l_run = 0.f, thr = -INFINITY, nmq = cdead;
+  float ve = 0.f;
   f32x4 O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1055,11 +1069,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     }
     const int t0 = blk * kTile;
     const bool edge = t0 < lo || t0 + kTile > hi;  // wave-uniform
+    // the value group norms of this lane's scores (a token's norm of its coordinate group)
+    float vn[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) vn[k] = FOLD || k < 4 ? cb.vn0[k & 3] : cb.vn1[k - 4];
     if (edge) {
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
         const int t = FOLD ? t0 + 16 * half + 4 * qg + k : t0 + 16 * (k >> 2) + 4 * qg + (k & 3);
-        if (t < lo || t >= hi) x[k] = -INFINITY;
+        if (t < lo || t >= hi) {
+          x[k] = -INFINITY;
+          vn[k] = 0.f;  // masked slots may hold undefined norms
+        }
       }
     }
     // Lazy maximum: while no score of the block exceeds the column's running maximum by
@@ -1078,21 +1099,43 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
       l_run *= al;
       m_run = mnew;
       thr = m_run + kRescaleLog2 * qs;
-      nmq = (m_run == -INFINITY ? 0.f : -m_run * qinv) + cdead;
+      nmq = (m_run == -INFINITY ? 0.f : -m_run * qinv) - ve + cdead;
     }
-    float p[NP];
+    float p[NP], lp[NP];
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
-      p[k] = __builtin_amdgcn_exp2f(fmaf(x[k], qinv, nmq));
+      lp[k] = fmaf(x[k], qinv, nmq);  // log2 of the weight, 2^-E included
+      p[k] = __builtin_amdgcn_exp2f(lp[k]);
       l_run += p[k];
     }
     float pv[NP];
+    float pm = 0.f;
 #pragma unroll
-    for (int k = 0; k < NP; ++k) pv[k] = p[k] * (FOLD || k < 4 ? cb.vn0[k & 3] : cb.vn1[k - 4]);
-    if (edge) {
+    for (int k = 0; k < NP; ++k) {
+      pv[k] = p[k] * vn[k];
+      pm = fmaxf(pm, pv[k]);
+    }
+    // The value weights' scale: rescaled only when a weight of the block would leave fp16's
+    // range (above 2^15) or when every weight of the block is below 2^-10.  The block's
+    // largest weight is found from log2 p + log2 norm, which cannot overflow.
+    if (__builtin_amdgcn_ballot_w64(pm > kWeightHi) != 0 || __builtin_amdgcn_ballot_w64(pm >= kWeightLo) == 0) {
+      float wl = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < NP; ++k)
-        if (p[k] == 0.f) pv[k] = 0.f;  // masked slots may hold undefined norms
+      for (int k = 0; k < NP; ++k) wl = fmaxf(wl, vn[k] > 0.f ? lp[k] + __log2f(vn[k]) : -INFINITY);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) wl = fmaxf(wl, lane_xor(wl, o, lane));
+      wl = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wl)));
+      if (wl > -INFINITY) {  // some weight is nonzero
+        const int en = min(max((int)ve + (int)floorf(wl) - kWeightTop, -90), 90);
+        const float al = ldexpf(1.f, (int)ve - en);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) O[i] *= al;
+        l_run *= al;  // this block's weights included
+#pragma unroll
+        for (int k = 0; k < NP; ++k) pv[k] *= al;
+        nmq += ve - (float)en;
+        ve = (float)en;
+      }
     }
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     u32x4 bp;
@@ -1134,7 +1177,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   // ---- combine the partials of the workgroup: one per wave, or per wave and tile when
   // folded (scores in prescaled units -> log2 units)
   const float lt = rows_sum(l_run);
-  const float m2 = m_run == -INFINITY ? -INFINITY : m_run * qinv;
+  // the weights and their sum carry 2^-E: the partial's log2 maximum takes E back
+  const float m2 = m_run == -INFINITY ? -INFINITY : m_run * qinv + ve;
   __syncthreads();                          // every wave is done with the tables
   const int part = FOLD ? 2 * wv + half : wv;
   float* so = scr;                          // [NPART][HPS][128]
@@ -1701,17 +1745,18 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
   return hipErrorInvalidValue;
 }
 
-// Compute units of the current device, read once per device.
+// Compute units of the current device, read once per device.  The cache is atomic: calls
+// from several host threads may both read the attribute and store the same value.
 static int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,

@@ -149,7 +149,15 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
                                 const void* xk, const void* xv, tq_dtype x_dtype, int32_t n_new,
                                 const int32_t* pos, int32_t pos0, int32_t max_pos, void* stream);
 
-/* One decode step of attention for every query head against the packed cache.
+/* One decode step of attention for every query head against the packed cache, computed
+ * in the rotated domain straight from the codes: the query is rotated once per head, each
+ * score is the sum over groups of the key group norm times the dot of the rotated query with
+ * the codebook values of the key's codes, the value sum accumulates the weight times the
+ * value group norm times the value's codebook values, and one inverse rotation is applied to
+ * the output ("TurboQuant: ... MNN on phones", 3.3, the key and value paths;
+ * "RotaryQuant ...", key design 3: score, softmax, value accumulation and inverse rotation
+ * fused over the packed cache; "RoPE-Aware Bit Allocation ...", packed-cache implementation
+ * details: the key axis split into sections merged by log-sum-exp).
  *   q:        device [batch][n_q_heads][128] of q_dtype; query head h reads KV head
  *             h / (n_q_heads / n_kv_heads) (contiguous groups).
  *   seq_lens: device int32 [batch] (each <= max_len) or NULL = every row has max_len
@@ -163,10 +171,22 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
  *             normalised per section) and part_lse [n_splits][batch][n_q_heads]; an empty
  *             section has lse = -inf and a zero partial.  Finish with tq_merge_splits.
  * A row with no tokens gives out = 0 and lse = -inf.
- * The MFMA schedule converts the scaled query (after an exact power-of-two prescale) and
- * p * value-norm to fp16.  Its running maximum may lag the true one by up to 2^3, so p <= 8
- * and value group norms must stay below 8188 for p * norm to fit fp16; larger values need
- * the VEC schedule. */
+ * The MFMA schedule converts the scaled query (after an exact power-of-two prescale, split
+ * into fp16 high and low parts) and the value weights p * value-norm to fp16, and holds the
+ * codebook levels as fp16 at their fp16-exact scale (worst level 2.6e-5 for 3-bit, 9e-5 for
+ * 4-bit codebooks).  The value weights carry a power of two that is reset per 32-token block
+ * whenever a weight would pass 2^15 or all of the block's weights fall below 2^-10 (the sum
+ * of the weights carries it too, so it cancels): any value norm up to about 2^100 keeps the
+ * weights in fp16's range, and each block's largest weights at full fp16 precision.  Scores
+ * carry the codebook's level error: up to about 1e-3 nats for keys and queries with 8x
+ * outlier channels (lse errors up to 6e-4 were measured on such rows).  When an output row is
+ * carried by a token far below the softmax maximum (weight 1e-6 but a value norm 1e4 times
+ * the others), that absolute score error becomes the row's relative error.  The VEC schedule
+ * is fp32 throughout.
+ * Errors: TQ_EINVAL for null pointers, bad dtypes, counts, scale or schedule, caches that
+ * do not match the rotation or each other, or a missing output for the split count;
+ * TQ_ECAPACITY for max_len > capacity; TQ_EUNSUPPORTED for bits or groups outside 3/4 and
+ * 32/128. */
 tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
                               const void* q, tq_dtype q_dtype, int32_t n_q_heads,
                               const int32_t* seq_lens, int32_t max_len, float scale,

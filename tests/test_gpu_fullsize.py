@@ -1,7 +1,8 @@
 """Parity at the benchmark sizes, in the launch configuration bench.py times, on sampled outputs.
 
-Each test builds one benchmark workload at its full size (isoquant32k: B=8, T=32768, TQ3 with
-SO(4); zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys;
+Each test builds one benchmark workload at its full size (the packed-cache configurations:
+isoquant32k B=8 T=32768 TQ3 with SO(4), long128k B=1 T=131072 with 64 sections, batched B=32
+T=4096 TQ4/TQ3, gqa8k B=1 T=8192 with 32 sections, tiny T=256 fp32; zipfusion8k: B=32, T=8200, lossless BF16 pages; gtq32k: B=4, T=32768, Block-GTQ keys;
 qjl32k: B=4, T=32768, two-stage keys with one-bit first-stage codes),
 runs the step bench.py times (append of slot T-1 fused into the attention launch where the
 format has one, the same sections, then the merge) and compares every query head of three
@@ -33,7 +34,7 @@ def gpu():
 
 
 def units(w):
-    return [(0, 0), (w.batch // 2, w.n_kv_heads // 2 + 1), (w.batch - 1, w.n_kv_heads - 1)]
+    return [(0, 0), (w.batch // 2, min(w.n_kv_heads - 1, w.n_kv_heads // 2 + 1)), (w.batch - 1, w.n_kv_heads - 1)]
 
 
 def announce(name, w):
@@ -41,38 +42,50 @@ def announce(name, w):
                                                               w.n_splits), flush=True)
 
 
-def test_isoquant32k_step():
-    w = workloads.WORKLOADS["isoquant32k"]
+@pytest.mark.parametrize("name", ["isoquant32k", "long128k", "batched", "gqa8k", "tiny"])
+def test_packed_cache_step(name):
+    # every packed-cache configuration at full size, with its own section count: isoquant32k
+    # (whole-head rotation with SO(4)), long128k (64 key chunks and their merge), batched (TQ4
+    # keys / TQ3 values, more workgroups than compute units), gqa8k (32 sections), tiny (fp32,
+    # one section)
+    w = workloads.WORKLOADS[name]
     announce(w.name, w)
     inp = workloads.generate(w, 0)
     T, S = w.seq_len, w.n_splits
-    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, torch.from_numpy(inp["so4"]).cuda())
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).cuda()
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, so4)
     kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
     kc = tq.PackedCache(w.batch, w.n_kv_heads, T, w.bits_k, w.group, tq.TQ_KEYS)
     vc = tq.PackedCache(w.batch, w.n_kv_heads, T, w.bits_v, w.group, tq.TQ_VALUES)
-    tq.quantize_append(rot, kc, kx[:, :, :T - 1].contiguous())
-    tq.quantize_append(rot, vc, vx[:, :, :T - 1].contiguous())
+    tq.quantize_append_kv(rot, kc, vc, kx[:, :, :T - 1].contiguous(), vx[:, :, :T - 1].contiguous())
     q = torch.from_numpy(inp["q"]).cuda()
-    po, pl = tq.append_decode_attention(rot, kc, vc, kx[:, :, T - 1:].contiguous(), vx[:, :, T - 1:].contiguous(), q,
-                                        pos0=T - 1, scale=w.scale, n_splits=S)
-    out, lse = tq.merge_splits(rot, po, pl)
+    if S == 1:
+        out, lse = tq.append_decode_attention(rot, kc, vc, kx[:, :, T - 1:].contiguous(), vx[:, :, T - 1:].contiguous(),
+                                              q, pos0=T - 1, scale=w.scale, n_splits=1)
+    else:
+        po, pl = tq.append_decode_attention(rot, kc, vc, kx[:, :, T - 1:].contiguous(), vx[:, :, T - 1:].contiguous(),
+                                            q, pos0=T - 1, scale=w.scale, n_splits=S)
+        out, lse = tq.merge_splits(rot, po, pl)
     torch.cuda.synchronize()
-    out = out.cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
     del kx, vx, kc, vc
     ck, mk = codebook.lloyd_max(w.bits_k, w.group)
     cv, mv = codebook.lloyd_max(w.bits_v, w.group)
-    worst, t0 = 0.0, time.perf_counter()
-    for b, kv in units(w):
-        so, sg = inp["so4"][kv], inp["signs"][kv]
+    worst, worst_lse, t0 = 0.0, 0.0, time.perf_counter()
+    for b, kv in sorted(set(units(w))):
+        so = None if inp["so4"] is None else inp["so4"][kv]
+        sg = inp["signs"][kv]
         ki, kn, _ = quant.quantize(inp["k"][b, kv].astype(np.float64), sg, w.group, ck, mk, so)
         vi, vn, _ = quant.quantize(inp["v"][b, kv].astype(np.float64), sg, w.group, cv, mv, so)
         kd = quant.dequantize(ki, kn, sg, w.group, ck, so)
         vd = quant.dequantize(vi, vn, sg, w.group, cv, so)
         for h in range(kv * w.group_size, (kv + 1) * w.group_size):
-            ref, _ = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
+            ref, ref_lse = attention.softmax_attend(inp["q"][b, h].astype(np.float64), kd, vd, w.scale)
             worst = max(worst, float(row_rel_err(out[b, h], ref)))
-    print("worst row error %.2e (oracle %.1fs)" % (worst, time.perf_counter() - t0), flush=True)
+            worst_lse = max(worst_lse, abs(float(lse[b, h]) - ref_lse) / max(1.0, abs(ref_lse)))
+    print("worst row error %.2e, lse %.2e (oracle %.1fs)" % (worst, worst_lse, time.perf_counter() - t0), flush=True)
     assert worst <= OUT_RTOL
+    assert worst_lse <= 1e-4
 
 
 def test_zipfusion8k_step():
@@ -149,10 +162,14 @@ def test_qjl32k_step():
     codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device="cuda")
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device="cuda")
     signs = torch.zeros((w.batch, w.n_kv_heads, T, 16), dtype=torch.uint8, device="cuda")
-    tq.qjl_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, signs)
+    kx = torch.from_numpy(inp["k"]).cuda()
+    tq.qjl_quantize_keys(keys, kx[:, :, :T - 1].contiguous(), codes, norms, signs)
     v = torch.from_numpy(inp["v"]).cuda()
     q = torch.from_numpy(inp["q"]).cuda()
-    po, pl = tq.qjl_attention(keys, codes, norms, signs, v, q, max_len=T, scale=w.scale, n_splits=S)
+    # the step bench.py times: the new token's key and value written at slot T-1 inside the
+    # attention launch
+    po, pl = tq.qjl_append_attention(keys, codes, norms, signs, v, kx[:, :, T - 1].contiguous(),
+                                     v[:, :, T - 1].contiguous(), q, pos0=T - 1, scale=w.scale, n_splits=S)
     out, lse = tq.merge_splits(None, po, pl)
     torch.cuda.synchronize()
     out = out.cpu().numpy()

@@ -391,3 +391,110 @@ def test_end_to_end_append_then_decode(name):
     oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
     ref, _ = oracle_decode(w, inp, dequantized(w, inp, oqk), dequantized(w, inp, oqv), np.full(w.batch, t))
     assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
+
+
+def scaled_values(inp, vscale, seed):
+    """The workload's values (fp32) times a scale: a constant, or per token 10^u with u uniform
+    in [-4, 4] ("mixed": value group norms spanning eight decades inside one row)."""
+    v = inp["v"].astype(np.float32)
+    if vscale == "mixed":
+        rng = np.random.default_rng(seed)
+        return (v * 10.0 ** rng.uniform(-4, 4, size=v.shape[:3] + (1,))).astype(np.float32)
+    return (v * np.float32(vscale)).astype(np.float32)
+
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("vscale", [1e-4, 1e4, "mixed"])
+@pytest.mark.parametrize("name", ["gqa8k", "batched", "long128k", "isoquant32k"])
+def test_decode_value_scales(name, vscale, schedule):
+    # The norm is stored apart from the unit vector ("TurboQuant ...", 2.1), so a value group
+    # norm can be any fp32 number; the matrix-core schedule rounds the value weights p * norm
+    # to fp16 and must keep them in range at any scale.  Ragged rows and key-axis sections
+    # with empty ones exercise the masked slots.
+    w, inp = setup(name, seed=13, seq_len=150, batch=2)
+    inp = dict(inp, v=scaled_values(inp, vscale, 13))
+    if vscale == "mixed":
+        # With value norms spread over eight decades a row's output can be carried by a token
+        # whose softmax weight is 1e-6; the row error is then that token's absolute score
+        # error, which for the workloads' outlier keys reaches 1e-3 on the matrix-core path
+        # (fp16 codebook levels at their fp16-exact scale).  Keys at a quarter of their size
+        # keep scores within a few units, so this case measures the value weights' range.
+        inp["k"] = (inp["k"].astype(np.float32) * np.float32(0.25)).astype(np.float32)
+    t = w.seq_len
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, round_up(t, 32))
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens = np.array([t, 37], dtype=np.int32)
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    ref_out, ref_lse = oracle_decode(w, inp, kd, vd, lens)
+    seq = torch.from_numpy(lens).cuda()
+    for n_splits in (1, 3, 8):
+        if n_splits == 1:
+            out, lse = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, schedule=schedule)
+        else:
+            po, pl = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
+            out, lse = tq.merge_splits(rot, po, pl)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.isfinite(o).all()
+        err = row_rel_err(o, ref_out)
+        print("value scale %s, splits %d: max row rel err %.3e" % (vscale, n_splits, err.max()), flush=True)
+        assert err.max() <= OUT_RTOL
+        np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+def zero_code(bits):
+    # a zero group normalises to y = 0; its code counts the boundaries strictly below 0
+    # (the middle boundary is 0 itself), i.e. 2^(bits-1) - 1
+    return (1 << (bits - 1)) - 1
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_zero_groups_append_and_decode(name):
+    # Zero groups store norm 0 and the code of y = 0, and decode to zero: whole zero tokens,
+    # a zero 32-coordinate group inside otherwise nonzero tokens, and a zero last token, in
+    # keys and values, appended in one call and one token at a time; then both schedules
+    # against the oracle on those caches.
+    w, inp = setup(name, seed=14, seq_len=100, batch=2)
+    kx, vx = inp["k"].astype(np.float32), inp["v"].astype(np.float32)
+    kx[0, :, 5] = 0.0
+    vx[0, :, 5] = 0.0
+    kx[1, :, 40:45, 32:64] = 0.0
+    vx[1, :, 60:63, 96:128] = 0.0
+    vx[0, :, 10:12] = 0.0
+    kx[:, :, 99] = 0.0
+    vx[:, :, 99] = 0.0
+    inp = dict(inp, k=kx, v=vx)
+    t = w.seq_len
+    cap = round_up(t, 32)
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, cap)
+    kt, vt = torch.from_numpy(kx).cuda(), torch.from_numpy(vx).cuda()
+    tq.quantize_append_kv(rot, k, v, kt[:, :, :t - 1].contiguous(), vt[:, :, :t - 1].contiguous())
+    tq.quantize_append_kv(rot, k, v, kt[:, :, t - 1:].contiguous(), vt[:, :, t - 1:].contiguous(), pos0=t - 1)
+    torch.cuda.synchronize()
+    for role, cache, x in (("k", k, kx), ("v", v, vx)):
+        oq = oracle_quantize(w, inp, role)
+        idx, n = download(cache, role)
+        zero = (np.abs(x.reshape(x.shape[:3] + (128 // w.group, w.group))).max(-1) == 0)
+        assert zero.any()
+        assert np.all(n[:, :, :t][zero] == 0.0) and np.all(oq["norms"][zero] == 0.0)
+        zc = np.repeat(zero, w.group, axis=-1)
+        assert np.all(idx[:, :, :t][zc] == zero_code(cache.bits)) and np.all(oq["idx"][zc] == zero_code(cache.bits))
+        check_codes(idx, n, oq, t)
+    q = torch.from_numpy(inp["q"]).cuda()
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    ref, ref_lse = oracle_decode(w, inp, dequantized(w, inp, oqk), dequantized(w, inp, oqv), np.full(w.batch, t))
+    for schedule in ("mfma", "vec"):
+        for n_splits in (1, 4):
+            if n_splits == 1:
+                out, lse = tq.decode_attention(rot, k, v, q, max_len=t, schedule=schedule)
+            else:
+                po, pl = tq.decode_attention(rot, k, v, q, max_len=t, n_splits=n_splits, schedule=schedule)
+                out, lse = tq.merge_splits(rot, po, pl)
+            torch.cuda.synchronize()
+            err = row_rel_err(out.cpu().numpy(), ref)
+            print("zero groups: schedule %s splits %d: max row rel err %.3e" % (schedule, n_splits, err.max()),
+                  flush=True)
+            assert err.max() <= OUT_RTOL
+            np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)

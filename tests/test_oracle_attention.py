@@ -182,3 +182,32 @@ def test_quantised_attention_error_is_small_relative_to_exact():
     approx, _ = attention.decode(q, kd, vd, [200], 128 ** -0.5)
     rel = np.linalg.norm(approx - exact) / np.linalg.norm(exact)
     assert rel < 0.35
+
+
+@pytest.mark.parametrize("group,use_so4,hkv,g", [(32, False, 2, 4), (32, False, 1, 1), (128, True, 2, 4),
+                                                 (128, False, 3, 2), (32, True, 2, 8)])
+def test_rotate_heads_equals_dense_per_kv_head_rotation(group, use_so4, hkv, g):
+    # Split partials are compared in the rotated domain of the query head's KV head
+    # ("RotaryQuant ...", key design 3: one rotation per KV head, shared by its keys, values and
+    # the queries that read it).  Each head's R is built here as a dense matrix from scipy's
+    # Hadamard and the 4x4 matrix forms of the quaternion products, with the KV head of query
+    # head h written out as h // g; a wrong head map, a dropped SO(4) stage or a transposed
+    # R changes the result because every KV head has its own signs and quaternions.
+    import scipy.linalg
+
+    from test_oracle_rotation import left_matrix, right_matrix
+
+    rng = np.random.default_rng(26)
+    signs = np.where(rng.random((hkv, 128)) < 0.5, -1.0, 1.0)
+    so4 = unit_quats(rng, (hkv, 32, 2)) if use_so4 else None
+    hq = hkv * g
+    x = rng.standard_normal((3, hq, 128))
+    got = attention.rotate_heads(x, signs, group, so4, g)
+    hblk = scipy.linalg.block_diag(*[scipy.linalg.hadamard(group) / np.sqrt(group)] * (128 // group))
+    for h in range(hq):
+        kv = h // g
+        r = hblk @ np.diag(signs[kv])
+        if use_so4:
+            r = scipy.linalg.block_diag(*[left_matrix(ql) @ right_matrix(qr * np.array([1, -1, -1, -1]))
+                                          for ql, qr in so4[kv]]) @ r
+        np.testing.assert_allclose(got[:, h], x[:, h] @ r.T, atol=1e-13)
