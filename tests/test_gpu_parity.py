@@ -498,3 +498,38 @@ def test_zero_groups_append_and_decode(name):
                   flush=True)
             assert err.max() <= OUT_RTOL
             np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("name,n_q_heads", [("long128k", 16), ("batched", 64), ("gqa8k", 48), ("gqa8k", 128)])
+def test_decode_more_than_four_heads_per_kv_head(name, n_q_heads, schedule):
+    # more query heads per KV head than one workgroup serves: 32-coordinate groups take 4 heads
+    # per workgroup, so G = 6, 8 and 16 run in 2, 2 and 4 head slices (the last one partial for
+    # G = 6), for the shared 3-bit table and for 4-bit keys with 3-bit values; ragged rows and
+    # sections
+    from dataclasses import replace
+    w = replace(workloads.WORKLOADS[name], n_q_heads=n_q_heads).with_len(130, batch=2)
+    inp = workloads.generate(w, 15)
+    print("case", name, "G", w.group_size, flush=True)
+    t = w.seq_len
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, round_up(t, 32))
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens = np.array([t, 45], dtype=np.int32)
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    ref_out, ref_lse = oracle_decode(w, inp, kd, vd, lens)
+    seq = torch.from_numpy(lens).cuda()
+    for n_splits in (1, 3):
+        if n_splits == 1:
+            out, lse = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, schedule=schedule)
+        else:
+            po, pl = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
+            ref_po, ref_pl = oracle_decode(w, inp, kd, vd, lens, n_splits)
+            assert row_rel_err(po.cpu().numpy(), ref_po).max() <= OUT_RTOL
+            np.testing.assert_allclose(pl.cpu().numpy(), ref_pl, rtol=1e-4, atol=1e-4)
+            out, lse = tq.merge_splits(rot, po, pl)
+        torch.cuda.synchronize()
+        err = row_rel_err(out.cpu().numpy(), ref_out)
+        print("splits %d: max row rel err %.3e" % (n_splits, err.max()), flush=True)
+        assert err.max() <= OUT_RTOL
+        np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
