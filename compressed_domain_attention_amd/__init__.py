@@ -79,7 +79,8 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("tq_status_string", "tq_make_codebook", "tq_quantize_append", "tq_quantize_append_kv",
-           "tq_decode_attention", "tq_append_decode_attention", "tq_dense_attention", "tq_merge_splits",
+           "tq_decode_attention", "tq_append_decode_attention", "tq_append_decode_attention_static",
+           "tq_dense_attention", "tq_merge_splits",
            "tq_zip_compress", "tq_zip_attention", "tq_gtq_block_energies", "tq_gtq_allocate", "tq_gtq_prepare", "tq_gtq_quantize_keys",
            "tq_gtq_attention", "tq_gtq_append_attention", "tq_gtq_qjl_projection", "tq_gtq_qjl_quantize_keys",
            "tq_gtq_qjl_attention", "tq_gtq_qjl_append_attention")
@@ -110,6 +111,10 @@ def library():
                                                ctypes.POINTER(_Cache), P, P, I, P, I, I, P, I, I, F, I, I, P, P, P,
                                                P, P]
     lib.tq_append_decode_attention.restype = I
+    lib.tq_append_decode_attention_static.argtypes = [ctypes.POINTER(_Rotation), ctypes.POINTER(_Cache),
+                                                      ctypes.POINTER(_Cache), P, P, I, P, I, I, P, I, I, F, I, I,
+                                                      P, P, P]
+    lib.tq_append_decode_attention_static.restype = I
     lib.tq_dense_attention.argtypes = [ctypes.POINTER(_Rotation), P, P, I, I, I, P, I, I, P, I, F, I, P, P, P]
     lib.tq_dense_attention.restype = I
     lib.tq_merge_splits.argtypes = [ctypes.POINTER(_Rotation), I, I, I, P, P, P, P, P]
@@ -294,6 +299,39 @@ def append_decode_attention(rot: Rotation, keys: PackedCache, values: PackedCach
         _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits, _SCHEDULES[schedule], _ptr(out),
         _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_append_decode_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)
+
+
+STATIC_PARTIAL_FLOATS = 1 << 20  # the library's static partial buffer, floats per device
+
+
+def append_decode_attention_static(rot: Rotation, keys: PackedCache, values: PackedCache, xk: torch.Tensor,
+                                   xv: torch.Tensor, q: torch.Tensor, out: torch.Tensor, lse: torch.Tensor = None,
+                                   pos: torch.Tensor = None, pos0: int = 0, max_pos: int = None, scale=None,
+                                   n_splits=1, schedule="auto"):
+    """append_decode_attention with n_splits sections and the merge, the section partials in
+    the library's static device buffer (no allocation by the call): writes out [batch, n_q_heads,
+    128] fp32 and, if given, lse [batch, n_q_heads]; returns (out, lse)."""
+    for x in (xk, xv):
+        if x.dtype not in _DTYPES or not x.is_contiguous():
+            raise ValueError("xk and xv must be contiguous float16/float32 tensors")
+    if xk.dtype != xv.dtype or xk.shape != xv.shape or xk.shape[2] != 1:
+        raise ValueError("xk and xv must have the same dtype and shape, one token per stream")
+    if q.dtype not in _DTYPES or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16/float32 tensor")
+    bsz, hq = q.shape[0], q.shape[1]
+    if tuple(out.shape) != (bsz, hq, HEAD_DIM) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [batch, n_q_heads, 128]")
+    if lse is not None and (tuple(lse.shape) != (bsz, hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [batch, n_q_heads]")
+    if max_pos is None:
+        max_pos = int(pos.max().item()) if pos is not None else pos0
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    _check(library().tq_append_decode_attention_static(
+        ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(xk), _ptr(xv), _DTYPES[xk.dtype],
+        _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits, _SCHEDULES[schedule], _ptr(out),
+        _ptr(lse), _stream()), "tq_append_decode_attention_static")
+    return out, lse
 
 
 def dense_attention(rot: Rotation, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, seq_lens=None, max_len=None,

@@ -208,6 +208,29 @@ extern "C" tq_status tq_append_decode_attention(const tq_rotation* rot, const tq
   return from_hip(tq::launch_decode(a, sched, keys->bits, values->bits, q_dtype == TQ_F16, same, s));
 }
 
+extern "C" tq_status tq_append_decode_attention_static(const tq_rotation* rot, const tq_cache* keys,
+                                                       const tq_cache* values, const void* xk, const void* xv,
+                                                       tq_dtype x_dtype, const int32_t* pos, int32_t pos0,
+                                                       int32_t max_pos, const void* q, tq_dtype q_dtype,
+                                                       int32_t n_q_heads, float scale, int32_t n_splits,
+                                                       tq_schedule schedule, float* out, float* lse_out,
+                                                       void* stream) {
+  if (out == nullptr || n_q_heads <= 0 || n_splits < 1 || keys == nullptr || keys->batch <= 0) return TQ_EINVAL;
+  if (n_splits == 1)  // no partials: the step writes out itself
+    return tq_append_decode_attention(rot, keys, values, xk, xv, x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads,
+                                      scale, 1, schedule, out, lse_out, nullptr, nullptr, stream);
+  const int64_t rows = (int64_t)n_splits * keys->batch * n_q_heads;
+  if (rows * (TQ_HEAD_DIM + 1) > tq::kStaticPartialFloats) return TQ_ECAPACITY;
+  float* part = nullptr;
+  if (tq::static_partials(&part) != hipSuccess) return TQ_EHIP;
+  float* part_lse = part + rows * TQ_HEAD_DIM;
+  const tq_status st = tq_append_decode_attention(rot, keys, values, xk, xv, x_dtype, pos, pos0, max_pos, q, q_dtype,
+                                                  n_q_heads, scale, n_splits, schedule, nullptr, nullptr, part,
+                                                  part_lse, stream);
+  if (st != TQ_OK) return st;
+  return tq_merge_splits(rot, n_splits, keys->batch, n_q_heads, part, part_lse, out, lse_out, stream);
+}
+
 extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* v, tq_dtype kv_dtype,
                                         int32_t batch, int32_t capacity, const void* q, tq_dtype q_dtype,
                                         int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,

@@ -216,6 +216,13 @@ hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hip
 hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
+// Library-owned device buffer for the section partials of the allocation-free decode step:
+// kStaticPartialFloats floats per device (4 MiB), shared by every call on that device.  Sets
+// *p to the calling thread's current device's copy (its address is looked up once per
+// device); returns the hipError_t of the lookup.
+constexpr int64_t kStaticPartialFloats = 1 << 20;
+hipError_t static_partials(float** p);
+
 // Heads one workgroup of the matrix-core schedule can serve: the 16 MFMA columns hold
 // (norm group, head) pairs for 32-groups and (query part, head) pairs for whole-head groups.
 inline int mfma_heads_per_slice(int rot_group) { return rot_group == 32 ? 4 : 8; }

@@ -1745,6 +1745,29 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
   return hipErrorInvalidValue;
 }
 
+// The section partials of the allocation-free decode step live here, one copy per device,
+// for callers that cannot allocate (HIP graph capture, serving loops).  In host code the
+// array's name is not a device address: every host use goes through the address
+// hipGetSymbolAddress returns for the current device, looked up once per device and kept.
+static __device__ __align__(256) float scratch[kStaticPartialFloats];
+
+hipError_t static_partials(float** p) {
+  static std::atomic<float*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  float* a = addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    void* q = nullptr;
+    if ((e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    a = (float*)q;
+    addr[dev].store(a, std::memory_order_release);
+  }
+  *p = a;
+  return hipSuccess;
+}
+
 // Compute units of the current device, read once per device.  The cache is atomic: calls
 // from several host threads may both read the attribute and store the same value.
 static int device_cus() {

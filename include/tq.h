@@ -209,6 +209,30 @@ tq_status tq_append_decode_attention(const tq_rotation* rot, const tq_cache* key
                                      int32_t n_q_heads, float scale, int32_t n_splits, tq_schedule schedule,
                                      float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the decode step of tq_append_decode_attention with
+ * n_splits key-axis sections followed by tq_merge_splits, with the section partials held in a
+ * library-owned static device buffer instead of caller buffers.  The result, cache bytes and
+ * out/lse_out, equals that of tq_append_decode_attention(..., n_splits, part_o = P,
+ * part_lse = L) followed by tq_merge_splits(rot, n_splits, keys->batch, n_q_heads, P, L, out,
+ * lse_out) bit for bit; n_splits == 1 is tq_append_decode_attention itself.
+ *   out: device [batch][n_q_heads][128] fp32; lse_out: device [batch][n_q_heads] or NULL.
+ * The buffer holds TQ_STATIC_PARTIAL_FLOATS (1048576) floats per device, 4 MiB, allocated with
+ * the library and kept until the process ends; its address is looked up once per device on
+ * the first call there.  Nothing in it needs clearing: every section writes its partial.
+ * Every call on a device shares that device's buffer, which keeps the last call's partials:
+ * calls that overlap on one device (different streams, or host threads) race.  No memory is
+ * allocated or freed by this call.
+ * Errors: those of the two calls it stands for; TQ_ECAPACITY when n_splits * batch *
+ * n_q_heads * 129 > TQ_STATIC_PARTIAL_FLOATS; TQ_EHIP when the buffer's address cannot be
+ * obtained.  Nothing is written when a check fails. */
+#define TQ_STATIC_PARTIAL_FLOATS (1 << 20)
+tq_status tq_append_decode_attention_static(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
+                                            const void* xk, const void* xv, tq_dtype x_dtype, const int32_t* pos,
+                                            int32_t pos0, int32_t max_pos, const void* q, tq_dtype q_dtype,
+                                            int32_t n_q_heads, float scale, int32_t n_splits, tq_schedule schedule,
+                                            float* out, float* lse_out, void* stream);
+
 /* Attention over an unquantised K/V region, as key-axis section partials that merge with the
  * packed cache's: the prefill kept in fp16 while only decode-phase tokens are quantised
  * ("RotaryQuant ...", method overview, deferred prefill), or a window of recent tokens kept
