@@ -1090,6 +1090,61 @@ def write_zip_traffic(w, n_splits, fetch_csv, write_csv, commands):
         w.name, n_splits, read / 1e6, written / 1e6, f_factor, w_factor))
 
 
+def schedule_sweep():
+    """Decode launch time of the matrix-core and the vector schedule over the cache length T and
+    the query heads per KV head (one sequence, 8 KV heads, one section, HIP-graph timing), for
+    32-groups (TQ3, gqa8k's inputs) and whole-head groups with SO(4) (isoquant32k's inputs).
+    Prints one table row per point."""
+    from dataclasses import replace
+
+    import torch
+
+    import compressed_domain_attention_amd as tq
+
+    def launch_us(fn, n=200):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (2 * n) * 1e3
+
+    print("| group | query heads per KV head | T | matrix cores (us) | vector (us) | vector / matrix | max diff |")
+    print("|---|---|---|---|---|---|---|")
+    for base in ("gqa8k", "isoquant32k"):
+        for g in (1, 4, 8):
+            for T in (32, 64, 128, 256, 511, 512, 1024, 2048, 8192):
+                w = replace(workloads.WORKLOADS[base], n_q_heads=8 * g, n_kv_heads=8).with_len(T, batch=1)
+                inp = workloads.generate(w, 0)
+                so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).cuda()
+                rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, so4)
+                cap = (T + 31) // 32 * 32
+                k = tq.PackedCache(1, 8, cap, w.bits_k, w.group, tq.TQ_KEYS)
+                v = tq.PackedCache(1, 8, cap, w.bits_v, w.group, tq.TQ_VALUES)
+                tq.quantize_append_kv(rot, k, v, torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda())
+                q = torch.from_numpy(inp["q"]).cuda()
+                out = torch.empty((1, w.n_q_heads, 128), device="cuda")
+                lse = torch.empty((1, w.n_q_heads), device="cuda")
+                t = {s: launch_us(lambda: tq.decode_attention(rot, k, v, q, max_len=T, schedule=s, out=out, lse=lse))
+                     for s in ("mfma", "vec")}
+                a, _ = tq.decode_attention(rot, k, v, q, max_len=T, schedule="mfma")
+                b, _ = tq.decode_attention(rot, k, v, q, max_len=T, schedule="vec")
+                torch.cuda.synchronize()
+                diff = float((a - b).abs().max() / b.abs().max())
+                print("| %d | %d | %d | %.2f | %.2f | %.1f | %.1e |" % (w.group, g, T, t["mfma"], t["vec"],
+                                                                     t["vec"] / t["mfma"], diff), flush=True)
+
+
 # the packed-cache configurations timed after the headline, in the same run and JSON line
 OTHER_CONFIGS = ("long128k", "batched", "gqa8k", "tiny")
 
@@ -1136,6 +1191,8 @@ def main():
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--counter-run into profiles/decode_traffic.json")
     ap.add_argument("--commands", default="", help="the profiling commands, recorded with --write-traffic")
+    ap.add_argument("--schedule-sweep", action="store_true",
+                    help="print the decode launch time of both schedules over T and heads per KV head, then exit")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline configuration (the others are timed after it by default)")
     args = ap.parse_args()
@@ -1144,6 +1201,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.schedule_sweep:
+        schedule_sweep()
+        return
     w = workloads.WORKLOADS[args.workload]
     n_splits = args.splits if args.splits is not None else w.n_splits
     if args.write_traffic:

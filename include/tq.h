@@ -70,7 +70,9 @@ typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
 /* Decode schedules.  MFMA: scores and value sum as matrix-core products of fp16
  * operands with fp32 accumulation (the key codebook scaled to be nearly fp16-exact, see
  * tq_codebook.f16_scale, and the query split into two fp16 parts).  VEC: plain fp32 vector arithmetic, token-parallel
- * scores and dimension-parallel value sum.  AUTO picks MFMA whenever it applies. */
+ * scores and dimension-parallel value sum.  AUTO picks MFMA: measured on MI355X it is faster at
+ * every cache length from 32 to 8192 tokens, for 1, 4 and 8 query heads per KV head and both
+ * rotation groups (2x at 32 tokens, growing to 28-48x at 8192), so no length threshold applies. */
 typedef enum { TQ_SCHEDULE_AUTO = 0, TQ_SCHEDULE_VEC = 1, TQ_SCHEDULE_MFMA = 2 } tq_schedule;
 
 /* Static description of an error code (never NULL). */

@@ -533,3 +533,19 @@ def test_decode_more_than_four_heads_per_kv_head(name, n_q_heads, schedule):
         print("splits %d: max row rel err %.3e" % (n_splits, err.max()), flush=True)
         assert err.max() <= OUT_RTOL
         np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("t", [32, 511, 512, 513])
+def test_decode_both_schedules_around_the_pages_threshold(t, schedule):
+    # the pages switch the value accumulation from word- to dimension-parallel at T = 512; here
+    # the matrix-core schedule is faster at every T measured, and both schedules must hold the
+    # bar on either side of that length
+    w, inp = setup("gqa8k", seed=16, seq_len=t, batch=1)
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, round_up(t, 32))
+    ref, ref_lse = oracle_decode(w, inp, dequantized(w, inp, oqk), dequantized(w, inp, oqv), np.full(1, t))
+    out, lse = tq.decode_attention(rot, k, v, torch.from_numpy(inp["q"]).cuda(), max_len=t, schedule=schedule)
+    torch.cuda.synchronize()
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
