@@ -728,10 +728,13 @@ __device__ __forceinline__ T load_at(const uint8_t* base, uint32_t off) {
 }
 
 // NW waves per workgroup: 4 with two workgroups per CU, or 8 with one (grids of at most
-// one workgroup per CU, where four waves would leave one wave per SIMD).
-template <int BK, int BV, int NG, bool QF16, bool QUAD, int NW>
+// one workgroup per CU, where four waves would leave one wave per SIMD).  D blocks per wave
+// in the register ring: 2, or 1 where a wave holds only a few blocks (each ring slot costs
+// a round of loads that the texture path processes even past the last block).
+template <int BK, int BV, int NG, bool QF16, bool QUAD, int NW, int D>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(D == 1 || D == 2, "one or two blocks in flight per wave");
   constexpr int NT = 64 * NW;
   constexpr int LDS_BUDGET = NW == 4 ? 80 * 1024 : 160 * 1024;  // per workgroup
   // whole-head groups: the query's hi and lo parts take separate columns (8 + 8), so one
@@ -761,22 +764,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   static_assert(!QUAD || (BK == 3 && BV == 3), "the four-code table holds 3-bit codes");
   constexpr int KT_BYTES = QUAD ? 32768 : NEK * RK * 4, VT_BYTES = QUAD ? 0 : NEV * RV * 4;
   constexpr int VT_AT = KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
-  // Prefetch ring: per wave, D slots of one 32-token block each, filled by direct
-  // global -> LDS copies in the lane order the block is read back in: key codes (two
-  // 16-token halves), value words (two halves), then the key and value norm blocks.
-  constexpr int KSZ = 4 * BK, VSZ = 4 * BV, NSZ = NG == 1 ? 4 : 16;  // bytes per lane per copy
-  constexpr int LST = 16;  // LDS bytes per lane of a code copy (12-byte copies land 16 apart)
-  constexpr int S_K1 = 64 * LST, S_V0 = 128 * LST, S_V1 = S_V0 + 64 * LST, S_N = S_V1 + 64 * LST;
-  constexpr int SLOT = S_N + 64 * NSZ;
-  constexpr int RING_AT = VT_AT + VT_BYTES;
+  // Block ring: each wave keeps its next D blocks of 32 tokens in registers.  They
+  // are read with buffer loads: the (sequence, KV head) slab in a buffer resource, the
+  // block's offset in a scalar register and the lane's offset fixed, so a load costs no
+  // address arithmetic, and the stream does not pass through the LDS, whose bandwidth the
+  // table reads need.
+  constexpr int NLD = FOLD ? 6 : 8;  // loads per block: key codes x2, value words x2, norms
+  constexpr int TAB_BYTES = VT_AT + VT_BYTES;
   // the pool and the other shared arrays (query rows, staged inputs, codebook, reductions)
   // stay within the workgroup's share of the CU's 160 KB
   constexpr int STATIC_LDS = HPS * kHeadDim * 4 + (kHeadDim + 256) * 4 + 256;
-  constexpr int D = RING_AT + 3 * NW * SLOT + STATIC_LDS <= LDS_BUDGET ? 3 : 2;
-  constexpr int NDMA = 5;  // copies per block
-  // the epilogue reuses the space for the per-wave partial results
+  // the epilogue reuses the tables' space for the per-wave partial results
   constexpr int SCR_BYTES = NPART * HPS * (kHeadDim + 2) * 4;
-  constexpr int POOL = RING_AT + D * NW * SLOT > SCR_BYTES ? RING_AT + D * NW * SLOT : SCR_BYTES;
+  constexpr int POOL = TAB_BYTES > SCR_BYTES ? TAB_BYTES : SCR_BYTES;
   static_assert(POOL + STATIC_LDS <= LDS_BUDGET, "the workgroups of a CU share its 160 KB of LDS");
   __shared__ __attribute__((aligned(16))) uint8_t pool[POOL];
   __shared__ __attribute__((aligned(16))) float qbuf[HPS * kHeadDim];
@@ -849,53 +849,60 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   }
   // ---- then the first D blocks of this wave into its ring
   const int nblk = blk0 + wv < blk1 ? (blk1 - (blk0 + wv) + NW - 1) / NW : 0;  // this wave's blocks
-  const uint32_t ring = lds_addr(pool) + RING_AT + wv * (D * SLOT);
-  const uint8_t* nlane = (lane < 32 ? knbase : vnbase) + (lane & 31) * NSZ;
-  // copies block j of this wave (clamped to its last block, so the count per block is
-  // fixed and the waits are static) into slot j % D
-  auto fetch = [&](int j) {
-    const int blk = blk0 + wv + NW * min(j, nblk - 1);
-    const uint32_t sl = __builtin_amdgcn_readfirstlane(ring + (j % D) * SLOT);
-    const uint8_t* kb = kbase + (size_t)blk * kTile * KREC;
-    const uint8_t* vb = vbase + (size_t)blk * VTILE;
-    lds_dma<KSZ, true>(sl, kb, koff);
-    lds_dma<KSZ, true>(sl + S_K1, kb, koff + 16 * KREC);
-    lds_dma<VSZ, true>(sl + S_V0, vb, voff);
-    lds_dma<VSZ, true>(sl + S_V1, vb, voff + VSZ);
-    lds_dma_addr<NSZ, true>(sl + S_N, nlane + (size_t)blk * (NG * kTile * 4));
-  };
-  auto read_block = [&](int j) {
-    const uint8_t* sl = pool + RING_AT + wv * (D * SLOT) + (j % D) * SLOT;
+  constexpr int kRsrc = 0x00020000;  // raw buffer, 32-bit data format
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, a.capacity * KREC, kRsrc);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, ntile * VTILE, kRsrc);
+  const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc((void*)knbase, 0, ntile * NG * kTile * 4, kRsrc);
+  const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc((void*)vnbase, 0, ntile * NG * kTile * 4, kRsrc);
+  // The same slabs with no records: every access is out of range, returns zeros and moves
+  // no data.  Loads past the wave's last block use them, so that every ring refill is
+  // issued and the compiler's count of the loads in flight stays exact.
+  const __amdgpu_buffer_rsrc_t zk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, 0, kRsrc);
+  const __amdgpu_buffer_rsrc_t zv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, 0, kRsrc);
+  const __amdgpu_buffer_rsrc_t zkn = __builtin_amdgcn_make_buffer_rsrc((void*)knbase, 0, 0, kRsrc);
+  const __amdgpu_buffer_rsrc_t zvn = __builtin_amdgcn_make_buffer_rsrc((void*)vnbase, 0, 0, kRsrc);
+  constexpr int kStream = 2;  // non-temporal: the cache stream is read once
+  // loads block j of this wave; past the last block (clamped to it, so the offset stays
+  // inside the slab) it reads nothing
+  auto load_block = [&](int j) {
+    const bool live = j < nblk;  // wave-uniform
+    const int blk = __builtin_amdgcn_readfirstlane(blk0 + wv + NW * min(j, max(nblk - 1, 0)));
+    const int ko = blk * (kTile * KREC), vo = blk * VTILE, no = blk * (NG * kTile * 4);
+    const __amdgpu_buffer_rsrc_t bk = live ? rk : zk, bv = live ? rv : zv;
+    const __amdgpu_buffer_rsrc_t bkn = live ? rkn : zkn, bvn = live ? rvn : zvn;
     Block<BK, BV> d;
     if (BK == 3) {
-      const uint3 x0 = load_at<uint3>(sl, lane * LST), x1 = load_at<uint3>(sl + S_K1, lane * LST);
-      d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z;
-      d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z;
+      const auto x0 = __builtin_amdgcn_raw_buffer_load_b96(bk, koff, ko, kStream);
+      const auto x1 = __builtin_amdgcn_raw_buffer_load_b96(bk, koff + 16 * KREC, ko, kStream);
+      d.k0[0] = x0[0]; d.k0[1] = x0[1]; d.k0[2] = x0[2];
+      d.k1[0] = x1[0]; d.k1[1] = x1[1]; d.k1[2] = x1[2];
     } else {
-      const uint4 x0 = load_at<uint4>(sl, lane * LST), x1 = load_at<uint4>(sl + S_K1, lane * LST);
-      d.k0[0] = x0.x; d.k0[1] = x0.y; d.k0[2] = x0.z; d.k0[BK - 1] = x0.w;
-      d.k1[0] = x1.x; d.k1[1] = x1.y; d.k1[2] = x1.z; d.k1[BK - 1] = x1.w;
+      const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(bk, koff, ko, kStream);
+      const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(bk, koff + 16 * KREC, ko, kStream);
+      d.k0[0] = x0[0]; d.k0[1] = x0[1]; d.k0[2] = x0[2]; d.k0[BK - 1] = x0[3];
+      d.k1[0] = x1[0]; d.k1[1] = x1[1]; d.k1[2] = x1[2]; d.k1[BK - 1] = x1[3];
     }
     if (BV == 3) {
-      const uint3 y0 = load_at<uint3>(sl + S_V0, lane * LST), y1 = load_at<uint3>(sl + S_V1, lane * LST);
-      d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y1.x; d.v[4] = y1.y; d.v[5] = y1.z;
+      const auto y0 = __builtin_amdgcn_raw_buffer_load_b96(bv, voff, vo, kStream);
+      const auto y1 = __builtin_amdgcn_raw_buffer_load_b96(bv, voff + 12, vo, kStream);
+      d.v[0] = y0[0]; d.v[1] = y0[1]; d.v[2] = y0[2]; d.v[3] = y1[0]; d.v[4] = y1[1]; d.v[5] = y1[2];
     } else {
-      const uint4 y0 = load_at<uint4>(sl + S_V0, lane * LST), y1 = load_at<uint4>(sl + S_V1, lane * LST);
-      d.v[0] = y0.x; d.v[1] = y0.y; d.v[2] = y0.z; d.v[3] = y0.w;
-      d.v[4] = y1.x; d.v[5] = y1.y; d.v[2 * BV - 2] = y1.z; d.v[2 * BV - 1] = y1.w;
+      const auto y0 = __builtin_amdgcn_raw_buffer_load_b128(bv, voff, vo, kStream);
+      const auto y1 = __builtin_amdgcn_raw_buffer_load_b128(bv, voff + 16, vo, kStream);
+      d.v[0] = y0[0]; d.v[1] = y0[1]; d.v[2] = y0[2]; d.v[3] = y0[3];
+      d.v[4] = y1[0]; d.v[5] = y1[1]; d.v[2 * BV - 2] = y1[2]; d.v[2 * BV - 1] = y1[3];
     }
-    d.kn0 = load_at<f32x4>(sl + S_N, noff);
-    d.vn0 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff);
+    d.kn0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(bkn, noff, no, kStream));
+    d.vn0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(bvn, noff, no, kStream));
     if (!FOLD) {
-      d.kn1 = load_at<f32x4>(sl + S_N, noff + 16);
-      d.vn1 = load_at<f32x4>(sl + S_N + 32 * NSZ, noff + 16);
+      d.kn1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(bkn, noff + 16, no, kStream));
+      d.vn1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(bvn, noff + 16, no, kStream));
     }
     return d;
   };
+  Block<BK, BV> ring[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    if (j < nblk) fetch(j);
-  }
+  for (int j = 0; j < D; ++j) ring[j] = load_block(j);
 
   // ---- decode tables, built while the staged inputs are in flight.  The codebook's fp16
   // values (kernel arguments at constant offsets: scalar loads) go to lanes 0-15 of one
@@ -930,11 +937,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     const int e = i / RV;
     ((uint32_t*)(pool + VT_AT))[i] = (uint32_t)__shfl(vcb, e & ((1 << BV) - 1)) | ((uint32_t)__shfl(vcb, e >> BV) << 16);
   }
-  // the staged inputs (copied before the ring's min(D, nblk) blocks) have landed
-  if (nblk >= D) vm_wait<NDMA * D>();
-  else if (D == 3 && nblk == 2) vm_wait<2 * NDMA>();
-  else if (nblk >= 1) vm_wait<NDMA>();
-  else vm_wait<0>();
+  // the staged inputs (copied before the ring's D blocks) have landed
+  vm_wait<D * NLD>();
   __syncthreads();
 
   // ---- rotated, scaled query (log2 units) with a power-of-two prescale into fp16 range
@@ -1158,21 +1162,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     for (int w = 0; w < 8; ++w) O[w] = mfma16(va[w], bp, O[w]);
   };
 
-  // Block j waits until its copies are complete (the younger blocks, at most D - 1, may
-  // still be in flight; copies complete in issue order), is read into registers, and once
-  // those reads are complete its slot is refilled with block j + D, so D blocks load
-  // during the arithmetic.  No copy is issued past the wave's last block.
-  for (int j = 0; j < nblk; ++j) {
-    const int younger = min(D - 1, nblk - 1 - j);  // wave-uniform
-    if (younger == D - 1) vm_wait<NDMA * (D - 1)>();
-    else if (younger == 1) vm_wait<NDMA>();
-    else vm_wait<0>();
-    const Block<BK, BV> cb = read_block(j);
-    lds_wait();
-    if (j + D < nblk) fetch(j + D);
-    process(cb, blk0 + wv + NW * j);
+  // Block j is processed from ring slot j % D, which then takes block j + D: with D = 2 the
+  // next block loads during the arithmetic.
+  for (int j0 = 0; j0 < nblk; j0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int j = j0 + s;
+      if (j < nblk) process(ring[s], blk0 + wv + NW * j);
+      ring[s] = load_block(j + D);
+    }
   }
-  vm_wait<0>();  // no copy may land in the pool once it is reused below
 
   // ---- combine the partials of the workgroup: one per wave, or per wave and tile when
   // folded (scores in prescaled units -> log2 units)
@@ -1790,13 +1789,22 @@ hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits
   if (schedule == 2) {
     // a grid that leaves CUs without a second workgroup runs eight waves per workgroup
     const int nw = units <= device_cus() ? 8 : 4;
-#define TQ_MF(BK, BV, NG, QF, QD)                                                                  \
-  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF && shared_table == QD) {              \
-    if (nw == 8)                                                                                   \
-      hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, 8>), grid, dim3(512), 0, stream, a); \
-    else                                                                                           \
-      hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, 4>), grid, dim3(256), 0, stream, a); \
-    return hipGetLastError();                                                                      \
+    // blocks per wave (an upper bound): a one-block ring where a wave holds fewer than four
+    const int per_wave = ((a.max_len + a.n_splits - 1) / a.n_splits + 2 * kTile - 1) / kTile / nw;
+    const bool deep = ng == 1 || per_wave >= 4;
+#define TQ_MF_D(BK, BV, NG, QF, QD, NW)                                                                  \
+  if (deep)                                                                                             \
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, NW, 2>), grid, dim3(64 * NW), 0, stream, a); \
+  else                                                                                                  \
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, BV, NG, QF, QD, NW, NG == 1 ? 2 : 1>), grid, dim3(64 * NW), 0, stream, a);
+#define TQ_MF(BK, BV, NG, QF, QD)                                                        \
+  if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF && shared_table == QD) {    \
+    if (nw == 8) {                                                                       \
+      TQ_MF_D(BK, BV, NG, QF, QD, 8)                                                     \
+    } else {                                                                             \
+      TQ_MF_D(BK, BV, NG, QF, QD, 4)                                                     \
+    }                                                                                    \
+    return hipGetLastError();                                                            \
   }
 #define TQ_MF_Q(BK, BV, NG, QD) TQ_MF(BK, BV, NG, true, QD) TQ_MF(BK, BV, NG, false, QD)
 #define TQ_MF_NG(BK, BV, QD) TQ_MF_Q(BK, BV, 4, QD) TQ_MF_Q(BK, BV, 1, QD)
@@ -1804,6 +1812,7 @@ hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits
 #undef TQ_MF_NG
 #undef TQ_MF_Q
 #undef TQ_MF
+#undef TQ_MF_D
   } else {
 #define TQ_VEC(BK, BV, NG, QF)                                                               \
   if (bits_k == BK && bits_v == BV && ng == NG && q_f16 == QF) {                             \
