@@ -22,6 +22,11 @@ struct AppendArgs {
   int32_t n_kv_heads;
   int32_t capacity;
   float boundary[15];
+  // edge mode of the tile kernel: when n_edges > 0, block x handles tile edge[x] (tiles
+  // counted from pos / 32) and nothing else; the whole tiles between went to the
+  // matrix-core append
+  int32_t n_edges;
+  int32_t edge[2];
 };
 
 struct DecodeArgs {

@@ -12,6 +12,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "tq_internal.h"
@@ -397,7 +398,7 @@ __device__ __forceinline__ void append_tile(const AppendArgs& a, int b, int h, i
 
 template <int BITS, int GROUP, bool VALUES, bool XF16>
 __global__ __launch_bounds__(128) void append_kernel(const AppendArgs a) {
-  append_tile<BITS, GROUP, VALUES, XF16>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+  append_tile<BITS, GROUP, VALUES, XF16>(a, blockIdx.z, blockIdx.y, a.n_edges ? a.edge[blockIdx.x] : blockIdx.x);
 }
 
 // One new token per (sequence, KV head), keys and values together: one wave per stream,
@@ -541,10 +542,11 @@ __global__ __launch_bounds__(256) void append_step_kernel(const AppendArgs ak, c
 // values' (same tiles, same rotation).
 template <int BK, int BV, int GROUP, bool XF16>
 __global__ __launch_bounds__(128) void append_kv_kernel(const AppendArgs ak, const AppendArgs av, int batch) {
+  const int tile = ak.n_edges ? ak.edge[blockIdx.x] : blockIdx.x;
   if ((int)blockIdx.z < batch) {
-    append_tile<BK, GROUP, false, XF16>(ak, blockIdx.z, blockIdx.y, blockIdx.x);
+    append_tile<BK, GROUP, false, XF16>(ak, blockIdx.z, blockIdx.y, tile);
   } else {
-    append_tile<BV, GROUP, true, XF16>(av, blockIdx.z - batch, blockIdx.y, blockIdx.x);
+    append_tile<BV, GROUP, true, XF16>(av, blockIdx.z - batch, blockIdx.y, tile);
   }
 }
 
@@ -714,6 +716,12 @@ __device__ __forceinline__ float rows_max(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ uint32_t rows_or(uint32_t x) {  // or over lanes l, l^16, l^32, l^48
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] | a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] | b[1];
 }
 __device__ __forceinline__ float rows_sum(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -1228,6 +1236,298 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Append of whole tiles by matrix cores (fp16 vectors, one start position for all rows).
+//
+// The rotation of one KV head is a fixed 128 x 128 matrix R applied to the raw vector (the
+// norm divides afterwards): R[o][k] = s[k] / sqrt(g) * sum_j M[o][j] H[j][k], with s the
+// sign flips, H the Sylvester Hadamard on each g-block and M the SO(4) block matrix
+// (identity without SO(4)).  A tile of 32 tokens is one product of R with the tile's
+// vectors.  The fp16 vectors are exact operands; R is split into fp16 high and low parts,
+// so two products give the rotated values to about fp32 accuracy.  The workgroup builds R
+// once, in LDS, already in matrix-core operand order (16 x 32 blocks of 64 lanes x 16
+// bytes: conflict-free reads; 32-groups keep only the diagonal blocks).  Each wave then
+// takes whole tiles on its own, loading the next tile's vectors during this one's
+// arithmetic.  A token's norm comes from the same operands (fp16 pair dot products, fp32
+// sums).  Codes are counted against the boundaries with the quantiser's odd symmetry (the
+// boundaries are exactly symmetric, the middle one exactly zero): the sign, then a binary
+// search of the upper half's boundaries on |y|.  Keys take the products as (output, token), so a lane holds four
+// consecutive coordinates of one token and the four lane rows together a 96-bit chunk of
+// its record; values take them as (token, output), so a lane holds, across both token
+// blocks, the eight tokens of one stored value word.
+// Number of the quantiser's upper-half boundaries (sorted, NU = 3 or 7) strictly below
+// a >= 0, by binary search: two or three comparisons.
+template <int NU>
+__device__ __forceinline__ uint32_t upper_count(float a, const float* ub) {
+  if (NU == 3) {
+    const bool c1 = a > ub[1];
+    const bool c2 = a > (c1 ? ub[2] : ub[0]);
+    return (c1 ? 2u : 0u) + (c2 ? 1u : 0u);
+  } else {
+    const bool c1 = a > ub[3];
+    const bool c2 = a > (c1 ? ub[5] : ub[1]);
+    const bool c3 = a > (c1 ? (c2 ? ub[6] : ub[4]) : (c2 ? ub[2] : ub[0]));
+    return (c1 ? 4u : 0u) + (c2 ? 2u : 0u) + (c3 ? 1u : 0u);
+  }
+}
+
+template <int BITS, int GROUP, bool VALUES, int NWV>
+__device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, int h, int j_begin, int j_end,
+                                                  uint8_t* rlds) {
+  constexpr int NG = kHeadDim / GROUP;
+  constexpr int NKS = GROUP == 128 ? 4 : 1;  // K steps of 32 per output block
+  constexpr int HALF = 1 << (BITS - 1);     // codes of the quantiser's upper half
+  constexpr int NU = HALF - 1;               // boundaries above zero
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, qg = lane >> 4;
+  const size_t stream = (size_t)b * a.n_kv_heads + h;
+  const int ntile = a.capacity / kTile;
+  const float gscale = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  float ub[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) ub[k] = a.boundary[HALF + k];
+
+  // ---- R in LDS: operand (part, ob, s) at ((part * 8 + ob) * NKS + s) * 1 KB, lane l's 16 bytes
+  // holding R[16 ob + (l & 15)][32 ks + 8 (l >> 4) + 0..7] (ks = s, or ob >> 1 for 32-groups)
+  for (int op = wv; op < 8 * NKS; op += NWV) {
+    const int ob = op / NKS, ks = GROUP == 128 ? op % NKS : ob >> 1;
+    const int o = 16 * ob + col;
+    float mrow[4];  // row o & 3 of the SO(4) matrix of o's 4-block
+    if (a.so4 != nullptr) {
+      const float* qp = a.so4 + ((size_t)h * 32 + (o >> 2)) * 8;
+      const Quat ql = qload(qp), qrc = qconj(qload(qp + 4));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const Quat e{c == 0 ? 1.f : 0.f, c == 1 ? 1.f : 0.f, c == 2 ? 1.f : 0.f, c == 3 ? 1.f : 0.f};
+        const Quat r = qmul(qmul(ql, e), qrc);
+        const int i = o & 3;
+        mrow[c] = i == 0 ? r.w : i == 1 ? r.x : i == 2 ? r.y : r.z;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mrow[c] = c == (o & 3) ? 1.f : 0.f;
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t hw = 0, lw = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = 32 * ks + 8 * qg + 2 * p + e;
+        float r = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int jj = (o & ~3) + c;
+          r += (__builtin_popcount(jj & k & (GROUP - 1)) & 1) ? -mrow[c] : mrow[c];
+        }
+        r *= a.signs[h * kHeadDim + k] * gscale;
+        const _Float16 rh = (_Float16)r;
+        hw |= f16_bits(rh) << (16 * e);
+        lw |= f16_bits((_Float16)(r - (float)rh)) << (16 * e);
+      }
+      hi[p] = hw;
+      lo[p] = lw;
+    }
+    *(u32x4*)(rlds + (0 * 8 * NKS + op) * 1024 + 16 * lane) = hi;
+    *(u32x4*)(rlds + (1 * 8 * NKS + op) * 1024 + 16 * lane) = lo;
+  }
+  __syncthreads();
+  auto r_op = [&](int part, int ob, int s) {
+    return *(const u32x4*)(rlds + ((part * 8 + ob) * NKS + s) * 1024 + 16 * lane);
+  };
+
+  // ---- this stream's vectors: fp16 rows of 256 bytes; lane (col, qg) reads token
+  // 16 tb + col, bytes 64 ks + 16 qg .. + 15 of its row
+  constexpr int kRsrc = 0x00020000;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.x + stream * a.n_new * 256), 0, a.n_new * 256, kRsrc);
+  const uint32_t xoff = col * 256 + 16 * qg;
+  auto load_tile = [&](int j, u32x4 (&B)[2][4]) {
+    const int so = __builtin_amdgcn_readfirstlane((min(j, j_end - 1) * kTile - a.pos0) * 256);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        B[tb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 4096 * tb + 64 * ks, so, 2));
+  };
+
+  auto tile_step = [&](int j, const u32x4 (&B)[2][4]) {
+    // norms of tokens 16 tb + col (one per 32-group)
+    float inv[2][NG];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (GROUP == 128 || ks == g) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t w = B[tb][ks][p];  // (a bit cast of the vector element itself reads element 0)
+              const h2_t v = __builtin_bit_cast(h2_t, w);
+              if (p & 1) s1 = __builtin_amdgcn_fdot2(v, v, s1, false);
+              else s0 = __builtin_amdgcn_fdot2(v, v, s0, false);
+            }
+          }
+        }
+        const float nrm = sqrtf(rows_sum(s0 + s1));
+        inv[tb][g] = nrm > 0.f ? 1.0f / nrm : 0.f;
+        if (qg == g % 4)  // one row of lanes per group writes
+          a.norms[(stream * ntile + j) * (NG * kTile) + g * kTile + norm_pos(16 * tb + col)] = nrm;
+      }
+    }
+    // values: the norm of token 16 tb + 4 qg + i lives in lane 4 qg + i
+    float vinv[2][NG][4];
+    if (VALUES) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vinv[tb][g][i] = __shfl(inv[tb][g], 4 * qg + i);
+    }
+    const int t0 = j * kTile;
+    uint32_t vword[8];
+    uint32_t kf[2][2];  // keys: fields of output blocks 2c, 2c + 1 for both token blocks
+#pragma unroll
+    for (int ob = 0; ob < 8; ++ob) {
+      const int g = GROUP == 32 ? ob >> 1 : 0;
+      // R's operands are read per output block: hoisted out of the loops they would hold
+      // every block's operands in registers at once
+      asm volatile("" ::: "memory");
+      u32x4 ahi[NKS], alo[NKS];
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2) {
+        ahi[s2] = r_op(0, ob, s2);
+        alo[s2] = r_op(1, ob, s2);
+      }
+      vword[ob] = 0u;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+          const int ks = GROUP == 128 ? s2 : ob >> 1;
+          if (VALUES) {
+            acc = mfma16(B[tb][ks], ahi[s2], acc);
+            acc = mfma16(B[tb][ks], alo[s2], acc);
+          } else {
+            acc = mfma16(ahi[s2], B[tb][ks], acc);
+            acc = mfma16(alo[s2], B[tb][ks], acc);
+          }
+        }
+        uint32_t f = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = acc[i] * (VALUES ? vinv[tb][g][i] : inv[tb][g]);
+          uint32_t m;
+          if (VALUES && NU == 7) {  // (the search's selects cost 4-bit value words too many registers)
+            m = 0;
+#pragma unroll
+            for (int k = 0; k < NU; ++k) m += fabsf(y) > ub[k] ? 1u : 0u;
+          } else {
+            m = upper_count<NU>(fabsf(y), ub);
+          }
+          const uint32_t code = (y > 0.f ? (uint32_t)HALF : (uint32_t)(HALF - 1)) ^ m;
+          f |= code << (BITS * i);
+        }
+        if (VALUES) vword[ob] |= f << (4 * BITS * tb);
+        else kf[ob & 1][tb] = f;
+      }
+      if (!VALUES && (ob & 1)) {
+        // chunk c = ob / 2 (coordinates 32 c .. + 31) of token 16 tb + col: lane row qg holds
+        // coordinates 4 qg .. + 3 of both output blocks; place them and merge the four rows
+        const int c = ob >> 1;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          // chunk bit of coordinate 32 c + m: BITS * m.  3-bit: the second block starts at bit
+          // 48, taken relative to bit 32; 4-bit: at bit 64, relative to bit 64
+          const uint64_t p0 = (uint64_t)kf[0][tb] << (BITS * 4 * qg);
+          const uint64_t p1 = (uint64_t)kf[1][tb] << (BITS == 3 ? 12 * qg + 16 : 16 * qg);
+          uint32_t w0 = (uint32_t)p0, w1, w2, w3 = 0u;
+          if (BITS == 3) {
+            w1 = (uint32_t)(p0 >> 32) | (uint32_t)p1;
+            w2 = (uint32_t)(p1 >> 32);
+          } else {
+            w1 = (uint32_t)(p0 >> 32);
+            w2 = (uint32_t)p1;
+            w3 = (uint32_t)(p1 >> 32);
+          }
+          w0 = rows_or(w0); w1 = rows_or(w1); w2 = rows_or(w2);
+          if (BITS == 4) w3 = rows_or(w3);
+          if (qg == 0) {
+            uint32_t* o = (uint32_t*)(a.codes + (stream * a.capacity + t0 + 16 * tb + col) * (16 * BITS) + c * (4 * BITS));
+            if (BITS == 3) {
+              o[0] = w0; o[1] = w1; o[2] = w2;
+            } else {
+              *(uint4*)o = make_uint4(w0, w1, w2, w3);
+            }
+          }
+        }
+      }
+    }
+    if (VALUES) {  // words u = 0..7 of (q, m) = (qg, col): consecutive in the tile
+      uint32_t* vt = (uint32_t*)(a.codes + (stream * ntile + j) * (kTile * 16 * BITS) + (qg * 16 + col) * 8 * BITS);
+      if (BITS == 3) {
+#pragma unroll
+        for (int e = 0; e < 6; ++e) {  // dword e = bits 32 e .. + 31 of the 8 x 24-bit words
+          const int bit = 32 * e, wi = bit / 24, sh = bit % 24;  // sh in {0, 8, 16}
+          vt[e] = (vword[wi] >> sh) | (vword[wi + 1] << (24 - sh));
+        }
+      } else {
+        *(uint4*)vt = make_uint4(vword[0], vword[1], vword[2], vword[3]);
+        *(uint4*)(vt + 4) = make_uint4(vword[4], vword[5], vword[6], vword[7]);
+      }
+    }
+  };
+
+  // this wave's tiles j_begin + wv, + NWV, ...: two in registers, the next one loading
+  // during the arithmetic (past the last the load repeats it: every load is issued, so the
+  // compiler's count of loads in flight stays exact)
+  u32x4 B0[2][4], B1[2][4];
+  const int jw = j_begin + wv;
+  load_tile(jw, B0);
+  for (int j = jw; j < j_end; j += 2 * NWV) {
+    load_tile(j + NWV, B1);
+    tile_step(j, B0);
+    load_tile(j + 2 * NWV, B0);
+    if (j + NWV < j_end) tile_step(j + NWV, B1);
+  }
+}
+
+// Waves per workgroup and workgroups per CU: whole-head groups keep 64 KB of R in LDS (two
+// workgroups of six waves), 32-groups 16 KB (three of four); three waves per SIMD either way.
+template <int GROUP>
+struct MfmaAppendShape {
+  static constexpr int kWaves = GROUP == 128 ? 6 : 4;
+  static constexpr int kPerCu = GROUP == 128 ? 2 : 3;
+  static constexpr int kLds = 2 * 8 * (GROUP == 128 ? 4 : 1) * 1024;
+};
+
+// Whole tiles [j0, j0 + n_full) of every (sequence, KV head), per_wg tiles per workgroup.
+template <int BITS, int GROUP, bool VALUES>
+__global__ __launch_bounds__(64 * MfmaAppendShape<GROUP>::kWaves, MfmaAppendShape<GROUP>::kPerCu) void append_mfma_kernel(
+    const AppendArgs a, int j0, int n_full, int per_wg) {
+  using S = MfmaAppendShape<GROUP>;
+  __shared__ __attribute__((aligned(16))) uint8_t rlds[S::kLds];
+  const int jb = j0 + blockIdx.x * per_wg;
+  append_mfma_tiles<BITS, GROUP, VALUES, S::kWaves>(a, blockIdx.z, blockIdx.y, jb, min(jb + per_wg, j0 + n_full), rlds);
+}
+// Keys (grid z < batch) and values in one launch.
+template <int BK, int BV, int GROUP>
+__global__ __launch_bounds__(64 * MfmaAppendShape<GROUP>::kWaves, MfmaAppendShape<GROUP>::kPerCu) void append_mfma_kv_kernel(
+    const AppendArgs ak, const AppendArgs av, int batch, int j0, int n_full, int per_wg) {
+  using S = MfmaAppendShape<GROUP>;
+  __shared__ __attribute__((aligned(16))) uint8_t rlds[S::kLds];
+  const int jb = j0 + blockIdx.x * per_wg, je = min(jb + per_wg, j0 + n_full);
+  if ((int)blockIdx.z < batch) append_mfma_tiles<BK, GROUP, false, S::kWaves>(ak, blockIdx.z, blockIdx.y, jb, je, rlds);
+  else append_mfma_tiles<BV, GROUP, true, S::kWaves>(av, blockIdx.z - batch, blockIdx.y, jb, je, rlds);
+}
+
 // ---------------------------------------------------------------------------------------
 // Vector (fp32) decode: token-parallel scores, dimension-parallel value sum, 64-token
 // steps.  Plain arithmetic; the cross-check for the matrix-core schedule and the fallback
@@ -1695,8 +1995,52 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
 // ---------------------------------------------------------------------------------------
 // Launchers.
 
+static int device_cus();
+
+// Whole tiles go to the matrix-core append when the vectors are fp16, every row starts at
+// the same position and at least one tile is whole: tiles [j0, j0 + n_full), counted from
+// slot 0.  The partial tiles at either end (at most two per row) stay with the tile kernel,
+// in its edge mode (tiles counted from pos0 / 32).
+static bool mfma_append_split(const AppendArgs& a, bool x_f16, int& j0, int& n_full, AppendArgs& edges) {
+  if (!x_f16 || a.pos != nullptr || a.n_new < 2 * kTile || a.n_edges != 0) return false;
+  const int first = (a.pos0 + kTile - 1) / kTile, end = (a.pos0 + a.n_new) / kTile;
+  if (end <= first) return false;
+  j0 = first;
+  n_full = end - first;
+  edges = a;
+  edges.n_edges = 0;
+  if (a.pos0 % kTile) edges.edge[edges.n_edges++] = 0;
+  if ((a.pos0 + a.n_new) % kTile) edges.edge[edges.n_edges++] = end - a.pos0 / kTile;
+  return true;
+}
+
+// Whole tiles per workgroup: one round of workgroups (per_cu per CU) over all rows (and
+// roles), each wave with at least two tiles where there are enough.
+static int mfma_append_chunks(int n_full, int rows, int per_cu, int& per_wg) {
+  int chunks = std::max(1, std::min(n_full, (per_cu * device_cus() + rows - 1) / rows));
+  per_wg = (n_full + chunks - 1) / chunks;
+  return (n_full + per_wg - 1) / per_wg;
+}
+
 hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, bool x_f16, int batch,
                          int n_tiles, hipStream_t stream) {
+  int j0 = 0, n_full = 0;
+  AppendArgs edges;
+  if (mfma_append_split(a, x_f16, j0, n_full, edges)) {
+    int per_wg = 0;
+    const dim3 mgrid(mfma_append_chunks(n_full, batch * a.n_kv_heads, group == 128 ? 2 : 3, per_wg), a.n_kv_heads,
+                     batch);
+#define TQ_APPEND_M(B, G, V)                                                                          \
+  if (bits == B && group == G && values == V)                                                         \
+    hipLaunchKernelGGL((append_mfma_kernel<B, G, V>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, a, j0, \
+                       n_full, per_wg);
+    TQ_APPEND_M(3, 32, false) TQ_APPEND_M(3, 32, true) TQ_APPEND_M(3, 128, false) TQ_APPEND_M(3, 128, true)
+    TQ_APPEND_M(4, 32, false) TQ_APPEND_M(4, 32, true) TQ_APPEND_M(4, 128, false) TQ_APPEND_M(4, 128, true)
+#undef TQ_APPEND_M
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || edges.n_edges == 0) return e;
+    return launch_append(edges, bits, group, values, x_f16, batch, edges.n_edges, stream);  // edge mode
+  }
   const dim3 grid(n_tiles, a.n_kv_heads, batch), block(128);
 #define TQ_APPEND(B, G, V, X)                                                        \
   if (bits == B && group == G && values == V && x_f16 == X) {                        \
@@ -1728,6 +2072,23 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
 #undef TQ_STEP_X
 #undef TQ_STEP
     return hipErrorInvalidValue;
+  }
+  int j0 = 0, n_full = 0;
+  AppendArgs ek, ev;
+  if (mfma_append_split(ak, x_f16, j0, n_full, ek) && mfma_append_split(av, x_f16, j0, n_full, ev)) {
+    int per_wg = 0;
+    const dim3 mgrid(mfma_append_chunks(n_full, 2 * batch * ak.n_kv_heads, group == 128 ? 2 : 3, per_wg), ak.n_kv_heads,
+                     2 * batch);
+#define TQ_APPEND_KV_M(BK, BV, G)                                                                              \
+  if (bits_k == BK && bits_v == BV && group == G)                                                             \
+    hipLaunchKernelGGL((append_mfma_kv_kernel<BK, BV, G>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, ak, \
+                       av, batch, j0, n_full, per_wg);
+    TQ_APPEND_KV_M(3, 3, 32) TQ_APPEND_KV_M(3, 3, 128) TQ_APPEND_KV_M(4, 3, 32) TQ_APPEND_KV_M(4, 3, 128)
+    TQ_APPEND_KV_M(3, 4, 32) TQ_APPEND_KV_M(3, 4, 128) TQ_APPEND_KV_M(4, 4, 32) TQ_APPEND_KV_M(4, 4, 128)
+#undef TQ_APPEND_KV_M
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ek.n_edges == 0) return e;
+    return launch_append_kv(ek, ev, bits_k, bits_v, group, x_f16, batch, ek.n_edges, stream);  // edge mode
   }
   const dim3 grid(n_tiles, ak.n_kv_heads, 2 * batch), block(128);
 #define TQ_APPEND_KV(BK, BV, G, X)                                                              \

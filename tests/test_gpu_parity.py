@@ -112,6 +112,31 @@ def test_append_incremental_and_device_positions():
         assert not idx[:, :, t:].any()
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name", ["gqa8k", "batched", "isoquant32k"])
+def test_append_whole_tiles_between_partial_edges(name, fused):
+    # a chunk that starts and ends inside a 32-token tile: the whole tiles between take the
+    # matrix-core append (fp16 vectors, one start position for every row), the partial
+    # tiles at both ends the tile kernel, which must keep the earlier tokens of the first
+    w, inp = setup(name, seq_len=190, batch=2)
+    t, p0 = w.seq_len, 7
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, 224)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    for lo, hi in ((0, p0), (p0, t)):
+        xs, ys = kx[:, :, lo:hi].contiguous(), vx[:, :, lo:hi].contiguous()
+        if fused:
+            tq.quantize_append_kv(rot, k, v, xs, ys, pos0=lo)
+        else:
+            tq.quantize_append(rot, k, xs, pos0=lo)
+            tq.quantize_append(rot, v, ys, pos0=lo)
+    torch.cuda.synchronize()
+    for role, cache in (("k", k), ("v", v)):
+        idx, n = download(cache, role)
+        check_codes(idx, n, oracle_quantize(w, inp, role), t)
+        assert not idx[:, :, t:].any() and not n[:, :, t:].any()
+
+
 @pytest.mark.parametrize("name", ["batched", "isoquant32k", "tiny"])
 def test_fused_append_equals_separate_calls(name):
     # multi-token appends in one launch give the two separate calls' bytes exactly: a
