@@ -1017,6 +1017,42 @@ def counter_run(w, inp, n_splits, schedule, launches=24):
     log("counter run: 3 copies of %d bytes, %d decode launches over %d replicas" % (COPY_BYTES, launches, reps))
 
 
+def prefill_run(w, inp, launches=6):
+    """Dispatches for rocprofv3 passes over the prefill: three copies of COPY_BYTES through the
+    probe library (known traffic), then `launches` quantisations of the whole prompt (T - 1
+    tokens of keys and values, one call each) into the same caches, as bench timing issues
+    the prefill.  Prints nothing on stdout."""
+    import ctypes
+
+    import torch
+
+    import compressed_domain_attention_amd as tq
+    from compressed_domain_attention_amd import build as _b
+
+    dev = torch.device("cuda:0")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.tq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.tq_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, 4096, stream) == 0
+    torch.cuda.synchronize()
+    del src, dst
+    T = w.seq_len
+    cap = (T + 31) // 32 * 32
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).to(dev)
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).to(dev), w.group, so4)
+    k = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS, device=dev)
+    v = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, device=dev)
+    pk = torch.from_numpy(inp["k"][:, :, :T - 1].copy()).to(dev)
+    pv = torch.from_numpy(inp["v"][:, :, :T - 1].copy()).to(dev)
+    for _ in range(launches):
+        tq.quantize_append_kv(rot, k, v, pk, pv)
+    torch.cuda.synchronize()
+    log("prefill run: 3 copies of %d bytes, %d prefills of %d tokens" % (COPY_BYTES, launches, T - 1))
+
+
 CALIBRATION_KERNEL = "(anonymous namespace)::copy_kernel("  # the probe library's copy, not torch's
 
 
@@ -1185,6 +1221,8 @@ def main():
     ap.add_argument("--tail", type=int, default=0,
                     help="an unquantised tail of this many tokens per row (dense sections merged with the packed ones)")
     ap.add_argument("--tail-splits", type=int, default=None)
+    ap.add_argument("--prefill-run", action="store_true",
+                    help="only the prefill quantisation (after three calibration copies), for rocprofv3 passes")
     ap.add_argument("--counter-run", action="store_true",
                     help="only issue the calibration copies and decode launches (run under rocprofv3 --pmc)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -1217,6 +1255,11 @@ def main():
     inp = workloads.generate(w, 0)
     log("generated inputs in %.1fs" % (time.perf_counter() - t_gen))
     cpu = None
+    if args.prefill_run:
+        if w.codec != "turboquant":
+            raise SystemExit("--prefill-run covers the packed-cache workloads")
+        prefill_run(w, inp)
+        return
     if not args.no_cpu_baseline and not args.counter_run:
         # runs before anything initialises the GPU in this process (the pool forks)
         cpu = cpu_baseline(w, inp)
