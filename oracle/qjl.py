@@ -49,21 +49,31 @@ def unpack_signs(packed, m=HEAD_DIM):
     return np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=-1, bitorder="little", count=m).astype(bool)
 
 
+def code_bytes(bits):
+    """Stored bytes of one key's first-stage codes: b - 1 bits per coordinate, 128 of them."""
+    return HEAD_DIM * bits // 8
+
+
 def pack_codes(codes, bits):
-    """The first stage's codes [T, 128] as stored: at 1 bit the 128 bits in 16 bytes (code of
-    position i in byte i // 8 at bit i % 8, the sign bits' order); at 2-3 bits Block-GTQ's
-    64 bytes of nibbles."""
+    """The first stage's codes [T, 128] as stored, bit-packed at their own width ("TurboQuant
+    ... MNN on phones", 3.2: the two stages take b bits per coordinate in total): code of
+    position i at bit offset bits * i of the key's little-endian bit string, 16 * bits bytes.
+    At 1 bit that is byte i // 8, bit i % 8 (the sign bits' order); at 2 bits four codes per
+    byte; at 3 bits eight codes in three bytes, sum_j code_j << 3j, the packed cache's unit
+    ("TurboQuant ...", 3.3)."""
     c = np.asarray(codes, dtype=np.uint8)
-    if bits == 1:
-        assert c.max(initial=0) <= 1
-        return pack_signs(c == 1)
-    return blockgtq.pack_codes(c)
+    assert bits in (1, 2, 3) and c.shape[-1] == HEAD_DIM and c.max(initial=0) < (1 << bits)
+    planes = (c[..., :, None] >> np.arange(bits, dtype=np.uint8)) & 1  # [..., 128, bits], LSB first
+    stream = planes.reshape(c.shape[:-1] + (HEAD_DIM * bits,)).astype(bool)
+    return np.packbits(stream, axis=-1, bitorder="little")
 
 
 def unpack_codes(packed, bits):
-    if bits == 1:
-        return unpack_signs(packed).astype(np.uint8)
-    return blockgtq.unpack_codes(packed)
+    p = np.asarray(packed, dtype=np.uint8)
+    assert p.shape[-1] == code_bytes(bits)
+    stream = np.unpackbits(p, axis=-1, bitorder="little", count=HEAD_DIM * bits)
+    planes = stream.reshape(p.shape[:-1] + (HEAD_DIM, bits)).astype(np.uint8)
+    return np.sum(planes << np.arange(bits, dtype=np.uint8), axis=-1).astype(np.uint8)
 
 
 def encode_residual(r, S):

@@ -4,12 +4,15 @@ projections, the MSE stage's inner-product shrink that the second stage removes,
 sign packing.  Monte Carlo bounds are 5 standard errors."""
 
 import math
+import os
 
 import numpy as np
 import pytest
 
 from oracle import blockgtq as bg
 from oracle import codebook, qjl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def test_gaussian_sign_identity():
@@ -91,20 +94,64 @@ def test_sign_packing_and_zero_residual():
     assert qjl.estimate(rng.standard_normal(128), signs, rn, S)[0] == 0.0
 
 
-def test_stored_codes_layout():
-    # one-bit codes: position i in byte i // 8 at bit i % 8; wider ones: Block-GTQ nibbles
-    rng = np.random.default_rng(7)
-    c1 = (rng.random((5, 128)) < 0.5).astype(np.uint8)
-    p1 = qjl.pack_codes(c1, 1)
-    assert p1.shape == (5, 16) and np.array_equal(qjl.unpack_codes(p1, 1), c1)
-    one = np.zeros((1, 128), np.uint8)
-    one[0, 13] = 1  # byte 1, bit 5
-    assert list(qjl.pack_codes(one, 1)[0, :3]) == [0, 32, 0]
-    c2 = rng.integers(0, 4, (5, 128)).astype(np.uint8)
-    p2 = qjl.pack_codes(c2, 2)
-    assert p2.shape == (5, 64) and np.array_equal(qjl.unpack_codes(p2, 2), c2)
+def _bit_string_pack(codes, bits):
+    """An independent writer of the stored layout: the key's codes as one Python integer,
+    code i at bit bits * i, written out little-endian."""
+    out = []
+    for row in np.asarray(codes):
+        word = 0
+        for i, c in enumerate(row):
+            word |= int(c) << (bits * i)
+        out.append(list(word.to_bytes(16 * bits, "little")))
+    return np.array(out, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_stored_codes_layout(bits):
+    # b - 1 bits per coordinate, bit-packed: 16, 32 or 48 bytes per key
+    rng = np.random.default_rng(7 + bits)
+    c = rng.integers(0, 1 << bits, (5, 128)).astype(np.uint8)
+    p = qjl.pack_codes(c, bits)
+    assert p.shape == (5, 16 * bits) == (5, qjl.code_bytes(bits))
+    assert np.array_equal(p, _bit_string_pack(c, bits))
+    assert np.array_equal(qjl.unpack_codes(p, bits), c)
+    for i in (0, 13, 127):  # the top code at one position sets exactly its bits
+        one = np.zeros((1, 128), np.uint8)
+        one[0, i] = (1 << bits) - 1
+        got = np.unpackbits(qjl.pack_codes(one, bits)[0], bitorder="little")
+        assert list(np.flatnonzero(got)) == list(range(bits * i, bits * i + bits))
     with pytest.raises(AssertionError):
-        qjl.pack_codes(c2, 1)
+        qjl.pack_codes(np.full((1, 128), 1 << bits, np.uint8), bits)
+
+
+def test_stored_codes_worked_examples():
+    # at 1 bit: position 13 is byte 1, bit 5
+    one = np.zeros((1, 128), np.uint8)
+    one[0, 13] = 1
+    assert list(qjl.pack_codes(one, 1)[0, :3]) == [0, 32, 0]
+    # at 3 bits: the packed cache's hand-written three-byte words (tests/golden)
+    n3 = 0
+    for line in open(os.path.join(GOLDEN, "pack_layout_examples.txt")):
+        f = line.split()
+        if len(f) != 13 or f[0] != "word" or f[1] != "3":
+            continue
+        codes = np.zeros((1, 128), np.uint8)
+        codes[0, :8] = [int(x, 16) for x in f[2:10]]
+        assert list(qjl.pack_codes(codes, 3)[0, :3]) == [int(x, 16) for x in f[10:13]]
+        n3 += 1
+    assert n3 >= 5
+    # at 2 bits: hand-written from the rule (code j of a byte at bits 2j .. 2j + 1)
+    n2 = 0
+    for line in open(os.path.join(GOLDEN, "qjl_code_layout.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.split()
+        bits, codes_hex, bytes_hex = int(f[0]), f[1:9], f[9:]
+        codes = np.zeros((1, 128), np.uint8)
+        codes[0, :8] = [int(x, 16) for x in codes_hex]
+        assert list(qjl.pack_codes(codes, bits)[0, :len(bytes_hex)]) == [int(x, 16) for x in bytes_hex]
+        n2 += 1
+    assert n2 >= 4
 
 
 def test_one_bit_levels_split_into_midpoint_and_signs():
