@@ -581,10 +581,10 @@ def gtq_setup(w, inp, dev):
 
 
 GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
-# two-stage keys: first-stage codes (16 bytes of bits at one bit, else 64 of nibbles), the
-# norm slots, the residual's 128 sign bits, fp16 values
+# two-stage keys: first-stage codes (b - 1 bits per coordinate, bit-packed), the norm
+# slots, the residual's 128 sign bits, fp16 values
 def qjl_bytes_per_token_head(w):
-    return (16 if w.bits_k - 1 == 1 else 64) + 16 + 16 + 256
+    return 16 * (w.bits_k - 1) + 16 + 16 + 256
 
 
 def run_gtq(w, inp, steps, warmup, n_splits, check=True):

@@ -518,8 +518,8 @@ class GtqKeys:
 class QjlKeys(GtqKeys):
     """Two-stage key encoders: a one-group Block-GTQ head at `bits` bits (the MSE stage,
     rotation from gauss[h, bits-1]) and the QJL projection S [n_kv_heads, 128, 128] of the
-    residual, held as (S Q)^T per head.  At bits == 1 the codes are stored as bits, 16 bytes
-    per key (code_bytes); otherwise as gtq_quantize_keys' 64 bytes."""
+    residual, held as (S Q)^T per head.  The codes are stored bit-packed at `bits` bits per
+    coordinate: 16 * bits bytes per key (code_bytes)."""
 
     def __init__(self, bits, gauss, S, device="cuda"):
         import numpy as np
@@ -532,7 +532,7 @@ class QjlKeys(GtqKeys):
             raise ValueError("the first stage takes 1, 2 or 3 bits")
         super().__init__(np.full((hkv, 64), bits, dtype=np.int32), g, device)
         self.mse_bits = bits
-        self.code_bytes = 16 if bits == 1 else 64
+        self.code_bytes = 16 * bits
         rot = self.rotations.cpu().numpy()
         proj = np.zeros((hkv, 128 * 128), dtype=np.float32)
         for h in range(hkv):

@@ -369,7 +369,7 @@ extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_m
 
 static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, const float* proj, const void* x,
                               tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0,
-                              int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, int32_t bit1,
+                              int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, int32_t code_bits,
                               void* stream) {
   if (heads == nullptr || rotations == nullptr || x == nullptr || codes == nullptr || norms == nullptr)
     return TQ_EINVAL;
@@ -391,7 +391,7 @@ static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, 
   a.capacity = capacity;
   a.proj = proj;
   a.signs = signs;
-  a.bit1 = bit1;
+  a.code_bits = code_bits;
   return from_hip(tq::launch_gtq_quantize(a, x_dtype == TQ_F16, batch, (hipStream_t)stream));
 }
 
@@ -408,7 +408,7 @@ extern "C" tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const fl
                                               float* norms, uint8_t* signs, void* stream) {
   if (proj == nullptr || signs == nullptr || mse_bits < 1 || mse_bits > 3) return TQ_EINVAL;
   return gtq_quantize(heads, rotations, proj, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, codes, norms,
-                      signs, mse_bits == 1, stream);
+                      signs, mse_bits, stream);
 }
 
 static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
@@ -481,12 +481,12 @@ extern "C" tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float*
   if (st != TQ_OK) return st;
   a.proj = proj;
   a.signs = signs;
-  a.bit1 = mse_bits == 1;
+  a.code_bits = mse_bits;
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 
 static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotations, const float* proj,
-                                 int32_t bit1, uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
+                                 int32_t code_bits, uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
                                  int32_t batch, int32_t n_kv_heads, const void* k_new, const void* v_new,
                                  tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos, const void* q,
                                  tq_dtype q_dtype, int32_t n_q_heads, float scale, int32_t n_splits, float* out,
@@ -513,7 +513,7 @@ static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotation
   a.proj = proj;
   a.signs = signs;
   a.w_signs = signs;
-  a.bit1 = bit1;
+  a.code_bits = code_bits;
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 
@@ -538,7 +538,7 @@ extern "C" tq_status tq_gtq_qjl_append_attention(const tq_gtq_head* heads, const
                                                  float* out, float* lse_out, float* part_o, float* part_lse,
                                                  void* stream) {
   if (proj == nullptr || signs == nullptr || mse_bits < 1 || mse_bits > 3) return TQ_EINVAL;
-  return gtq_append_step(heads, rotations, proj, mse_bits == 1, codes, norms, signs, v, capacity, batch, n_kv_heads, k_new, v_new,
+  return gtq_append_step(heads, rotations, proj, mse_bits, codes, norms, signs, v, capacity, batch, n_kv_heads, k_new, v_new,
                          x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads, scale, n_splits, out, lse_out, part_o,
                          part_lse, stream);
 }

@@ -58,17 +58,18 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
 // QJL (two-stage keys, one group): also the m = 128 sign bits of S r into sign_rec and
 // sqrt(pi/2)/m |r| into norm slot 1, from the rotated-domain residual e = y - c_hat
 // (S r = |x| M e with M = S Q; proj[j][i] = M[i][j], in LDS or global memory).
-// B1 (one-bit first stage): the 128 codes are written as 16 bytes of bits instead (code of
-// position i in byte i/8 at bit i mod 8, as the sign bits) and compared against the first
-// boundary only, so every code is 0 or 1 whatever the head's width.
-template <bool XF16, bool QJL = false, bool B1 = false>
+// PK (two-stage keys: the first stage's width, 1 to 3): the 128 codes are written
+// bit-packed, code of position i at bit PK i of the record's little-endian bit string (16 PK
+// bytes), and compared against the first 2^PK - 1 boundaries only, so every code fits its
+// field whatever the head's width.  PK = 0: Block-GTQ's one nibble per position.
+template <bool XF16, bool QJL = false, int PK = 0>
 __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* rot, const void* x, float* ubuf,
                                            uint8_t* code_rec, float* norm_rec, int lane, const float* proj = nullptr,
                                            uint8_t* sign_rec = nullptr) {
   const int j0 = 2 * lane;
   const int g = group_of(hd, j0);
   const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
-  const int nb = B1 ? 1 : (1 << hd.width[g]) - 1;
+  const int nb = PK ? min((1 << hd.width[g]) - 1, (1 << PK) - 1) : (1 << hd.width[g]) - 1;
   float x0, x1;
   if (XF16) {
     x0 = (float)((const _Float16*)x)[hd.coord[j0]];
@@ -106,13 +107,23 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
     c0 += y0 > hd.boundary[g][k];
     c1 += y1 > hd.boundary[g][k];
   }
-  if (B1) {
+  if (PK == 1) {
     // bit l of m0 (m1) is the code of position 2l (2l + 1): word w interleaves bits
     // 16 w .. 16 w + 15 of both
     const uint64_t m0 = __builtin_amdgcn_ballot_w64(c0 != 0), m1 = __builtin_amdgcn_ballot_w64(c1 != 0);
     if (lane < 4)
       ((uint32_t*)code_rec)[lane] = spread_bits((uint32_t)(m0 >> (16 * lane)) & 0xFFFFu) |
                                     (spread_bits((uint32_t)(m1 >> (16 * lane)) & 0xFFFFu) << 1);
+  } else if (PK == 2) {
+    // byte k holds positions 4k .. 4k + 3: the 4-bit fields of lanes 2k and 2k + 1
+    const uint32_t f = c0 | (c1 << 2), other = (uint32_t)__shfl_xor((int)f, 1);
+    if (!(lane & 1)) code_rec[lane >> 1] = (uint8_t)(f | (other << 4));
+  } else if (PK == 3) {
+    // bytes 3k .. 3k + 2 hold positions 8k .. 8k + 7: the 6-bit fields of lanes 4k .. 4k + 3
+    const int f = (int)(c0 | (c1 << 3)), q = lane & ~3;
+    const uint32_t w = (uint32_t)__shfl(f, q) | ((uint32_t)__shfl(f, q + 1) << 6) | ((uint32_t)__shfl(f, q + 2) << 12) |
+                       ((uint32_t)__shfl(f, q + 3) << 18);
+    if ((lane & 3) < 3) code_rec[3 * (lane >> 2) + (lane & 3)] = (uint8_t)(w >> (8 * (lane & 3)));
   } else {
     code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
   }
@@ -146,9 +157,9 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
 // group-order positions 2l and 2l + 1 (always in one group: groups start at even positions
 // and have even sizes).
 constexpr int kQuantTokens = 512;
-template <bool XF16, bool QJL, bool B1>
+template <bool XF16, bool QJL, int PK>
 __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a) {
-  constexpr int CREC = B1 ? 16 : 64;  // code bytes per key
+  constexpr int CREC = PK ? 16 * PK : 64;  // code bytes per key
   __shared__ __attribute__((aligned(16))) float rot[TQ_GTQ_ROTATION_FLOATS];
   __shared__ __attribute__((aligned(16))) float projl[QJL ? 128 * 128 : 1];
   __shared__ __attribute__((aligned(16))) float ubuf[4][128];
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
     const int i = tile * kQuantTokens + t;
     if (i >= a.n_new) break;
     const size_t rec = stream * a.capacity + a.pos0 + i;
-    encode_key<XF16, QJL, B1>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4),
+    encode_key<XF16, QJL, PK>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4),
                               ubuf[wv], a.codes + rec * CREC, a.norms + rec * 4, lane, projl,
                               QJL ? a.signs + rec * 16 : nullptr);
     // the next token's writes to ubuf follow this token's reads in program order
@@ -229,14 +240,18 @@ constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil
 // QJL: two-stage keys (one MSE group plus sign bits of the projected residual): four more
 // k-blocks whose key operands are +-1 (exact in fp16, from a table indexed by a sign byte)
 // against the projected query S q = M Q^T q, times the coefficient in norm slot 1.
-// B1 (one-bit first stage, 16 code bytes per key): the two levels c0 < c1 are written as
-// mid + half (2 bit - 1), so <q~, c[code]> = mid sum_j q~_j + half sum_j q~_j (+-1)_j: four
-// more +-1 products against half q~, plus mid sum_j q~_j added per head, replace the pair
-// tables.
-template <int NW, int D, bool QF16, bool QJL, bool B1 = false>
+// PK: the first stage's width (1 to 3), its codes bit-packed in 16 PK bytes per key.
+// PK = 1: the two levels c0 < c1 are written as mid + half (2 bit - 1), so
+// <q~, c[code]> = mid sum_j q~_j + half sum_j q~_j (+-1)_j: four more +-1 products against
+// half q~, plus mid sum_j q~_j added per head, replace the pair tables.  PK = 2: one table of
+// 256 entries, a code byte's four codes as [hi pair, lo pair, hi pair, lo pair] (one 16-byte
+// read per four codes).  PK = 3: one table of 64 entries over two codes, [hi pair, lo pair],
+// read four times per lane's 24-bit word.
+template <int NW, int D, bool QF16, bool QJL, int PK = 0>
 __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
-  static_assert(!B1 || QJL, "one-bit codes are the first stage of two-stage keys");
-  constexpr int CREC = B1 ? 16 : 64;  // code bytes per key
+  static_assert((PK != 0) == QJL && PK >= 0 && PK <= 3, "packed codes are the first stage of two-stage keys");
+  constexpr bool B1 = PK == 1;
+  constexpr int CREC = PK ? 16 * PK : 64;  // code bytes per key
   // a stage: key records 1 KB, norms 256 B (group-major), values 4 KB, sign bytes 256 B
   constexpr int STAGE = QJL ? 5632 : 5376;
   constexpr int NORM_AT = 1024, VAL_AT = 1280, SIGN_AT = 5376;
@@ -246,7 +261,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
   // k-blocks: up to 7 for a Block-GTQ head; two-stage keys have one group of 128 (4 blocks)
   constexpr int KB = QJL ? 4 : kMaxKb;
-  constexpr int PTAB_BYTES = B1 ? 0 : KB * 256 * 8;
+  constexpr int PTAB_BYTES = PK == 0 ? KB * 256 * 8 : PK == 2 ? 256 * 16 : PK == 3 ? 64 * 8 : 0;
   constexpr int TAB_BYTES = PTAB_BYTES + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
@@ -254,7 +269,10 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   uint8_t* const lds = lds_all + TAB_BYTES;
   uint8_t* const pmtab = lds_all + PTAB_BYTES;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
-  // their lo parts; zero for the blocks past the head's last, which then add nothing)
+  // their lo parts; zero for the blocks past the head's last, which then add nothing.
+  // PK = 2, 3: the one group's table, ptab4 or ptab6, at the same place)
+  u32x4* const ptab4 = (u32x4*)lds_all;
+  uint2* const ptab6 = (uint2*)lds_all;
   __shared__ __attribute__((aligned(16))) float qt[8][128];  // rotated, scaled query, group order
   __shared__ float qraw[8][128];  // the slice's query rows, original coordinates
   __shared__ tq_gtq_head hd;
@@ -291,10 +309,18 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     const int t0 = tok0_of(s);
     const uint32_t dst = wlds_a + (s % D) * STAGE;
     int t = t0 + (lane >> 2);
-    if (B1)  // 16 tokens' code bytes (lane: token tok0 + l/4, 4 bytes)
+    if (B1) {  // 16 tokens' code bytes (lane: token tok0 + l/4, 4 bytes)
       lds_dma<4, true>(dst, kc, t < cap ? (uint32_t)(t * 16 + 4 * (lane & 3)) : (uint32_t)(t0 * 16));
-    else
+    } else if (PK) {
+      // the 16 tokens' 16 PK-byte records are one span: lane l copies its bytes 16 l .. + 15
+      // (token tok0 + l / PK); lanes past the span repeat the first lanes into the stage's
+      // unused key bytes
+      const int l = lane % (16 * PK);
+      t = t0 + l / PK;
+      lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * CREC + 16 * (l % PK)) : (uint32_t)(t0 * CREC));
+    } else {
       lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
+    }
     t = t0 + (lane & 15);
     lds_dma<4, true>(dst + NORM_AT, kn, t < cap ? (uint32_t)(t * 16 + 4 * (lane >> 4)) : (uint32_t)(t0 * 16));
 #pragma unroll
@@ -332,11 +358,11 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const float* pj = QJL ? a.proj + (size_t)kv * 128 * 128 : nullptr;
       uint8_t* srec = QJL ? a.w_signs + rec * 16 : nullptr;
       if (a.x_f16) {
-        encode_key<true, QJL, B1>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds,
+        encode_key<true, QJL, PK>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds,
                                   a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
         ((uint32_t*)vd)[lane] = ((const uint32_t*)a.v_new)[st * 64 + lane];
       } else {
-        encode_key<false, QJL, B1>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds,
+        encode_key<false, QJL, PK>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds,
                                    a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
         const float2 x = ((const float2*)a.v_new)[st * 64 + lane];
         ((uint32_t*)vd)[lane] = pack_f16(x.x, x.y);
@@ -355,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   }
   const int nkb = min(cum[TQ_GTQ_MAX_GROUPS], KB);
   auto group_of_block = [&](int kb) { return (kb >= cum[1]) + (kb >= cum[2]) + (kb >= cum[3]); };
-  for (int i = tid; i < (B1 ? 0 : KB * 256); i += 64 * NW) {
+  for (int i = tid; i < (PK ? 0 : KB * 256); i += 64 * NW) {
     const int kb = i >> 8, by = i & 255, g = kb < nkb ? group_of_block(kb) : 0;
     // codes past the codebook decode to 0
     const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
@@ -363,6 +389,21 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     const float c0 = (by & 15) < nc ? sc * hd.centroid[g][by & 15] : 0.f;
     const float c1 = (by >> 4) < nc ? sc * hd.centroid[g][by >> 4] : 0.f;
     ptab[kb][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
+  }
+  if (PK == 2 || PK == 3) {  // the one group's levels (codes past its codebook decode to 0)
+    const int nc = 1 << min(max(hd.width[0], 1), PK);
+    const float sc = hd.f16_scale[0];
+    auto lev = [&](int c) { return c < nc ? sc * hd.centroid[0][c] : 0.f; };
+    for (int i = tid; i < (PK == 2 ? 256 : 64); i += 64 * NW) {
+      if (PK == 2) {
+        const float c0 = lev(i & 3), c1 = lev((i >> 2) & 3), c2 = lev((i >> 4) & 3), c3 = lev(i >> 6);
+        ptab4[i] = u32x4{pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)), pack_f16(c2, c3),
+                         pack_f16(f16_lo(c2), f16_lo(c3))};
+      } else {
+        const float c0 = lev(i & 7), c1 = lev(i >> 3);
+        ptab6[i] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
+      }
+    }
   }
   {
     // q~_g = Q_g^T q_g: thread (j, k) takes group-order position j of heads k, k + NW/2, ..,
@@ -515,25 +556,40 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       sc[2] = nr.z * (cm[2] + moff);
       sc[3] = nr.w * (cm[3] + moff);
     } else {
-      const uint8_t* rec = sb + 64 * col;
+      const uint8_t* rec = sb + CREC * col;
       // every block is computed (those past the head's last have zero tables and query), so
       // the unrolled loop is one basic block the compiler can interleave
       uint32_t cb[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {  // every code word first
-        const uint32_t bo = kbyte[kb];
-        // the 4 code bytes from two aligned words (the byte offset is any multiple of 1)
-        const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
-        cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
+        if (PK == 2) {  // positions 32 kb + 8 jr .. + 7: two bytes
+          cb[kb] = lds_read<uint16_t>(rec + 8 * kb + 2 * jr);
+        } else {
+          // the lane's code bytes (4 nibble bytes, or the 3 bytes of a 24-bit word at
+          // 12 kb + 3 jr) from two aligned words (the byte offset is any multiple of 1)
+          const uint32_t bo = PK == 3 ? (uint32_t)(12 * kb + 3 * jr) : kbyte[kb];
+          const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4);
+          cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
+        }
       }
-      // key operands straight from the table reads: [hi pair, lo pair] of two bytes each
+      // key operands straight from the table reads: [hi pair, lo pair] of two codes each
       u32x4 ka[KB], kb2[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
-        const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
-        ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
-        kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+        if (PK == 2) {
+          ka[kb] = ptab4[cb[kb] & 255u];
+          kb2[kb] = ptab4[(cb[kb] >> 8) & 255u];
+        } else if (PK == 3) {
+          const uint2 e0 = ptab6[cb[kb] & 63u], e1 = ptab6[(cb[kb] >> 6) & 63u];
+          const uint2 e2 = ptab6[(cb[kb] >> 12) & 63u], e3 = ptab6[(cb[kb] >> 18) & 63u];
+          ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
+          kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+        } else {
+          const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
+          const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
+          ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
+          kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -672,17 +728,14 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 
 hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream) {
   const dim3 grid((a.n_new + kQuantTokens - 1) / kQuantTokens, a.n_kv_heads, batch), block(256);
-  if (a.bit1 && !a.signs) return hipErrorInvalidValue;
-  if (a.bit1) {
-    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true, true>), grid, block, 0, stream, a);
-  } else if (a.signs) {
-    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_quantize_kernel<false, true, false>), grid, block, 0, stream, a);
-  } else {
-    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, false, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_quantize_kernel<false, false, false>), grid, block, 0, stream, a);
+  if ((a.code_bits != 0) != (a.signs != nullptr) || a.code_bits < 0 || a.code_bits > 3) return hipErrorInvalidValue;
+#define TQ_GQ(PK)                                                                                            \
+  if (a.code_bits == PK) {                                                                                   \
+    if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, PK != 0, PK>), grid, block, 0, stream, a);      \
+    else hipLaunchKernelGGL((gtq_quantize_kernel<false, PK != 0, PK>), grid, block, 0, stream, a);           \
   }
+  TQ_GQ(0) TQ_GQ(1) TQ_GQ(2) TQ_GQ(3)
+#undef TQ_GQ
   return hipGetLastError();
 }
 
@@ -690,17 +743,14 @@ hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t st
   constexpr int NW = 8, D = 2;
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
   if (a.heads_per_slice > 8) return hipErrorInvalidValue;
-  if (a.bit1 && !a.signs) return hipErrorInvalidValue;
-  if (a.bit1) {
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, true, true>), grid, block, 0, stream, a);
-  } else if (a.signs) {
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, true>), grid, block, 0, stream, a);
-  } else {
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, false>), grid, block, 0, stream, a);
+  if ((a.code_bits != 0) != (a.signs != nullptr) || a.code_bits < 0 || a.code_bits > 3) return hipErrorInvalidValue;
+#define TQ_GA(PK)                                                                                                 \
+  if (a.code_bits == PK) {                                                                                        \
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, PK != 0, PK>), grid, block, 0, stream, a);   \
+    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, PK != 0, PK>), grid, block, 0, stream, a);        \
   }
+  TQ_GA(0) TQ_GA(1) TQ_GA(2) TQ_GA(3)
+#undef TQ_GA
   return hipGetLastError();
 }
 

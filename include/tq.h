@@ -447,17 +447,20 @@ tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, con
                            tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
                            int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
 
-/* Two-stage keys (see tq_gtq_qjl_projection): the first stage exactly as
- * tq_gtq_quantize_keys with the one-group head, plus, per key, the 16 bytes of sign bits of
- * S r (bit i of the 128 in byte i/8 at bit i mod 8; a zero projection counts as +) into
- * signs [batch][n_kv_heads][capacity][16] and sqrt(pi/2)/128 |r| into norm slot 1.
+/* Two-stage keys (see tq_gtq_qjl_projection): the first stage's codes and norm as
+ * tq_gtq_quantize_keys computes them with the one-group head, plus, per key, the 16 bytes of
+ * sign bits of S r (bit i of the 128 in byte i/8 at bit i mod 8; a zero projection counts
+ * as +) into signs [batch][n_kv_heads][capacity][16] and sqrt(pi/2)/128 |r| into norm slot 1.
  *   proj: device [n_kv_heads][128 * 128] from tq_gtq_qjl_projection.
  *   mse_bits: the first stage's width, which the heads were prepared with (1, 2 or 3; b - 1
- *      for b-bit keys, "TurboQuant ... MNN on phones", 3.2).  At 1 the codes are stored as
- *      bits, codes [batch][n_kv_heads][capacity][16], code of position i in byte i/8 at bit
- *      i mod 8 (a 2-bit key then takes 32 bytes of codes and signs); at 2 and 3 they are
- *      tq_gtq_quantize_keys' [capacity][64] bytes.  A value other than the heads' width
- *      gives wrong codes but no access outside the buffers.
+ *      for b-bit keys, "TurboQuant ... MNN on phones", 3.2: the two stages take b bits per
+ *      coordinate).  The codes are stored bit-packed at that width: codes
+ *      [batch][n_kv_heads][capacity][16 * mse_bits], code of position i at bit offset
+ *      mse_bits * i of the key's little-endian bit string (1 bit: byte i/8, bit i mod 8;
+ *      2 bits: four codes per byte; 3 bits: eight codes in three bytes, sum_j c_j << 3j, the
+ *      packed cache's unit).  A b-bit key thus takes 16 (b - 1) + 16 bytes of codes and
+ *      signs plus two floats.  A value other than the heads' width gives wrong codes but no
+ *      access outside the buffers (codes are capped at 2^mse_bits - 1).
  * Errors: those of tq_gtq_quantize_keys; TQ_EINVAL for a null proj or signs or mse_bits
  * outside 1..3. */
 tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj,
@@ -471,7 +474,8 @@ tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotati
  * errors as tq_gtq_attention, plus proj, mse_bits (the codes' layout) and signs as
  * tq_gtq_qjl_quantize_keys (TQ_EINVAL when null or out of range).  With one-bit codes the
  * first stage's score is mid sum_j q~_j + half sum_j q~_j (+-1)_j for its two levels
- * mid -+ half, again with exact +-1 operands. */
+ * mid -+ half, again with exact +-1 operands; 2- and 3-bit codes are decoded through one
+ * table of the group's levels (four codes per entry at 2 bits, two at 3 bits). */
 tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float* rotations, const float* proj,
                                int32_t mse_bits, const uint8_t* codes, const float* norms, const uint8_t* signs, const void* v,
                                int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q, tq_dtype q_dtype,

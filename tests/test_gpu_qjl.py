@@ -1,8 +1,8 @@
 """GPU parity of two-stage keys (1-bit TQ-MSE + 1-bit QJL residual, oracle/qjl.py) through the
 C ABI.
 
-Both stored layouts of the first stage: one-bit codes as 16 bytes of bits (2-bit keys) and
-2-bit codes in 64 bytes of nibbles (3-bit keys).
+Every stored width of the first stage, bit-packed: one-bit codes in 16 bytes (2-bit keys),
+2-bit codes in 32 bytes (3-bit keys) and 3-bit codes in 48 bytes (4-bit keys).
 Encoding: MSE codes equal the oracle's except coordinates within 2e-6 of a boundary (at most
 1e-4 of them), the MSE norm within 1e-6 relative, the residual coefficient
 sqrt(pi/2)/128 |r| within 1e-4 relative (keys with a boundary code excluded: their residual
@@ -62,7 +62,7 @@ def oracle_records(w, inp, enc):
     return codes, norms, signs, rn, xh
 
 
-@pytest.mark.parametrize("bits_k", [2, 3])
+@pytest.mark.parametrize("bits_k", [2, 3, 4])
 def test_encoding_matches_oracle(bits_k):
     w, inp, bits, enc = case(bits_k=bits_k)
     keys = tq.QjlKeys(bits, inp["gauss"], inp["proj"])
@@ -113,7 +113,7 @@ def check(out, lse, ro, rl, lens):
 
 
 @pytest.mark.parametrize("n_splits,bits_k,q_dtype", [(1, 2, np.float16), (3, 2, np.float16), (3, 3, np.float16),
-                                                     (3, 2, np.float32)])
+                                                     (3, 2, np.float32), (1, 4, np.float16), (3, 4, np.float32)])
 def test_attention_matches_oracle(n_splits, bits_k, q_dtype):
     # fp32 queries carry the same (fp16-representable) values: the oracle is unchanged
     w, inp, bits, enc = case(bits_k=bits_k)
@@ -161,7 +161,7 @@ def same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("per_row,bits_k", [(False, 2), (True, 2), (True, 3)])
+@pytest.mark.parametrize("per_row,bits_k", [(False, 2), (True, 2), (True, 3), (False, 4)])
 def test_append_step_equals_encode_then_attend(per_row, bits_k):
     # one launch against encoding the new key (and writing its value) then attending: bit
     # for bit, cache and outputs; fp16 new tokens for one slot, fp32 for per-row slots
