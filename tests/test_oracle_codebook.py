@@ -141,3 +141,58 @@ def test_inner_product_shrink_matches_page(bits, dim):
     shrink = dim * codebook.distortion(bits, dim)
     target = FACTS["inner_product_shrink_3bit" if bits == 3 else "inner_product_shrink_4bit"]["value"]
     assert abs(shrink - target) < 0.5 * target
+
+
+# ---- 5 to 8 bits (byte containers of "RoPE-Aware Bit Allocation ..."): Newton's method on
+# the same fixed-point conditions
+
+WIDE = [(5, 2), (5, 8), (6, 32), (7, 4), (8, 2), (8, 16), (8, 128)]
+
+
+def cell_mass(lo, hi, dim):
+    """Incomplete-beta mass of [lo, hi], from the nearer tail (F(-t) = 1 - F(t))."""
+    return beta_cdf(-lo, dim) - beta_cdf(-hi, dim) if lo >= 0 else beta_cdf(hi, dim) - beta_cdf(lo, dim)
+
+
+@pytest.mark.parametrize("bits,dim", WIDE)
+def test_wide_lloyd_max_fixed_point_closed_form(bits, dim):
+    c, m = codebook.lloyd_max(bits, dim)
+    assert c.shape == (2 ** bits,) and np.all(np.diff(c) > 0) and -1 < c[0] and c[-1] < 1
+    np.testing.assert_allclose(m, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=1e-16)
+    np.testing.assert_allclose(c, -c[::-1], atol=1e-15)
+    edges = np.concatenate([[-1.0], m, [1.0]])
+    for k in range(2 ** bits):
+        cond_mean = first_moment(edges[k], edges[k + 1], dim) / cell_mass(edges[k], edges[k + 1], dim)
+        assert abs(cond_mean - c[k]) < 1e-11 * max(1.0, abs(c[k]) * np.sqrt(dim)), k
+
+
+@pytest.mark.parametrize("bits,dim", [(3, 32), (4, 128), (3, 2), (4, 8)])
+def test_newton_equals_the_plain_iteration(bits, dim):
+    # two methods, one fixed point: the 5-8-bit solver run at 3-4 bits
+    c_newton, _ = codebook._lloyd_max_newton(bits, dim)
+    c_plain, _ = codebook.lloyd_max(bits, dim)
+    np.testing.assert_allclose(c_newton, c_plain, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dim", [8, 32, 128])
+def test_wide_mse_bounds_and_high_rate_limit(dim):
+    # 2.3: dim * D1 <= 2.7 / 4^b at every width, and at high rate dim * D1 * 4^b rises
+    # towards the Panter-Dite constant dim / 12 * (int f^(1/3))^3 (written out by quadrature)
+    pd = dim / 12.0 * integrate.quad(lambda t: codebook.density(np.array([t]), dim)[0] ** (1 / 3), -1, 1,
+                                     epsabs=1e-13, limit=400)[0] ** 3
+    scaled = [dim * codebook.distortion(b, dim) * 4 ** b for b in (5, 6, 7, 8)]
+    assert all(s < FACTS["mse_upper_constant"]["value"] for s in scaled)
+    assert all(x < y for x, y in zip(scaled, scaled[1:])) and scaled[-1] < pd
+    assert pd - scaled[-1] < 0.015 * pd
+
+
+def test_wide_centroids_are_cell_means_of_sphere_coordinates():
+    rng = np.random.default_rng(98)
+    dim, bits = 8, 5
+    x = rng.standard_normal((200000, dim))
+    t = (x / np.linalg.norm(x, axis=1, keepdims=True)).ravel()
+    c, m = codebook.lloyd_max(bits, dim)
+    cell = np.searchsorted(m, t)
+    for k in range(2 ** bits):
+        s = t[cell == k]
+        assert abs(s.mean() - c[k]) < 5 * s.std() / np.sqrt(len(s)), k
