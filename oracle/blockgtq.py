@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 Source: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (aitrends.kr): the overview
 (RoPE splits the head dimension into 2-D frequency blocks; the query-key logit is exactly a
 sum of per-block dot products), the block energy score, the greedy integer allocation, the
-grouping into one TQ-MSE encoder per bit width, and the packed-cache paragraph (nibble
-containers; the main benchmark evaluates keys only, values kept in fp16).
+grouping into one TQ-MSE encoder per bit width, and the packed-cache paragraphs (low-bit
+groups in nibble containers, high-bit groups in bytes; the main benchmark evaluates keys
+only, values kept in fp16).
 
 * Energy of block i of KV head h: s_i = 1/2 (E_{t, g in G(h)} ||q_g,t^(i)||^2 +
   E_t ||k_h,t^(i)||^2), over a short calibration prefix; G(h) = the query heads reading h.
@@ -18,14 +19,17 @@ containers; the main benchmark evaluates keys only, values kept in fp16).
   normalise -> rotate -> per-coordinate Lloyd-Max search at that width).
 
 Readings (the pages leave these open): block i is coordinates (2i, 2i+1) (RoPE's 2-D
-pairs); greedy ties go to the lowest block index; widths run from 1 to 4 bits (nibble
-containers); a group's coordinates are its blocks' pairs in block order; its rotation is
-the orthogonal factor Q (with positive diagonal of R) of the leading n x n part of a
-Gaussian matrix drawn per (KV head, width), n = the group's dimension -- a uniformly random
-rotation, as the TurboQuant-MSE encoder assumes; the codebook is the Lloyd-Max quantiser
-for a rotated unit vector's coordinate in n dimensions; a token's key record holds one
-4-bit code per coordinate in group order (widths ascending, then the group's rotated
-coordinate order), even coordinates in the low nibble, and one fp32 norm per group.
+pairs); greedy ties go to the lowest block index; widths run from 1 to 8 bits, those up to
+4 in nibble containers and 5 to 8 in byte containers; a group's coordinates are its blocks'
+pairs in block order; its rotation is the orthogonal factor Q (with positive diagonal of R)
+of the leading n x n part of a Gaussian matrix drawn per (KV head, width), n = the group's
+dimension -- a uniformly random rotation, as the TurboQuant-MSE encoder assumes; the
+codebook is the Lloyd-Max quantiser for a rotated unit vector's coordinate in n dimensions.
+A token's key record holds the codes in group order (widths ascending, then the group's
+rotated coordinate order): the P positions of nibble groups first, position j in byte j/2
+(low nibble for even j), then the positions of byte groups, one byte each from byte P/2;
+zero bytes pad it to the record size (64 bytes when no group is wider than 4 bits, else
+the used bytes rounded up to 16, one size for a whole cache); and one fp32 norm per group.
 """
 
 import heapq
@@ -37,6 +41,8 @@ from . import codebook
 
 HEAD_DIM = 128
 BLOCKS = HEAD_DIM // 2
+MAX_WIDTH = 8
+NIBBLE_MAX = 4  # widths above this take byte containers
 
 
 def block_energies(q_cal, k_cal):
@@ -76,7 +82,7 @@ def allocate(s, budget, b_min, b_max):
     return b
 
 
-def groups(b, b_min=1, b_max=4):
+def groups(b, b_min=1, b_max=MAX_WIDTH):
     """The groups of a head's allocation: [(width, coordinates)] for every width present,
     widths ascending, coordinates = the blocks' pairs in block order."""
     out = []
@@ -143,23 +149,49 @@ def dequantize_keys(codes, norms, enc):
     return out
 
 
-def pack_codes(codes):
-    """[T, 128] codes (< 16) -> [T, 64] bytes: code j in byte j // 2, low nibble for even j."""
+def nibble_positions(enc):
+    """P: the group-order positions held in nibbles (the groups of width <= 4 come first)."""
+    return sum(len(coords) for w, coords, *_ in enc if w <= NIBBLE_MAX)
+
+
+def code_bytes(enc):
+    """Code bytes one record of this head needs: 64 when every group fits a nibble, else the
+    P / 2 nibble bytes plus one byte per wider position, rounded up to 16."""
+    p = nibble_positions(enc)
+    if p == HEAD_DIM:
+        return HEAD_DIM // 2
+    return -(-(p // 2 + HEAD_DIM - p) // 16) * 16
+
+
+def pack_codes(codes, enc=None, record_bytes=None):
+    """[T, 128] codes in group order -> [T, record_bytes] bytes.  Without enc every position
+    is a nibble (64 bytes: code j in byte j // 2, low nibble for even j); with enc the
+    positions past the nibble groups take one byte each from byte P / 2, and zero bytes pad
+    the record to record_bytes (default: code_bytes(enc))."""
     codes = np.asarray(codes, dtype=np.uint8)
-    return (codes[:, 0::2] & 0xF) | ((codes[:, 1::2] & 0xF) << 4)
-
-
-def unpack_codes(packed):
-    p = np.asarray(packed, dtype=np.uint8)
-    out = np.zeros((p.shape[0], HEAD_DIM), dtype=np.uint8)
-    out[:, 0::2] = p & 0xF
-    out[:, 1::2] = p >> 4
+    p = HEAD_DIM if enc is None else nibble_positions(enc)
+    r = (HEAD_DIM // 2 if enc is None else code_bytes(enc)) if record_bytes is None else record_bytes
+    assert p % 2 == 0 and r >= p // 2 + HEAD_DIM - p
+    assert np.all(codes[:, :p] < 16)
+    out = np.zeros((codes.shape[0], r), dtype=np.uint8)
+    out[:, :p // 2] = (codes[:, 0:p:2] & 0xF) | ((codes[:, 1:p:2] & 0xF) << 4)
+    out[:, p // 2:p // 2 + HEAD_DIM - p] = codes[:, p:]
     return out
 
 
-def key_record_bytes(n_groups):
-    """Stored bytes of one (token, KV head) key: 64 code bytes + one fp32 norm per group."""
-    return HEAD_DIM // 2 + 4 * n_groups
+def unpack_codes(packed, enc=None):
+    p_ = np.asarray(packed, dtype=np.uint8)
+    p = HEAD_DIM if enc is None else nibble_positions(enc)
+    out = np.zeros((p_.shape[0], HEAD_DIM), dtype=np.uint8)
+    out[:, 0:p:2] = p_[:, :p // 2] & 0xF
+    out[:, 1:p:2] = p_[:, :p // 2] >> 4
+    out[:, p:] = p_[:, p // 2:p // 2 + HEAD_DIM - p]
+    return out
+
+
+def key_record_bytes(n_groups, record_bytes=HEAD_DIM // 2):
+    """Stored bytes of one (token, KV head) key: the code bytes + one fp32 norm per group."""
+    return record_bytes + 4 * n_groups
 
 
 def rate_law_gain(s, b, i):

@@ -149,3 +149,80 @@ def test_codes_follow_the_compare_count_rule_and_zero_groups():
             for j in range(n):
                 assert codes[t, pos + j] == np.searchsorted(m, ys[t, pos + j], side="left")
         pos += n
+
+
+# ---- widths 5 to 8: byte containers ("RoPE-Aware Bit Allocation ...", packed-cache
+# implementation details: low-bit groups in nibbles, high-bit groups in bytes)
+
+def wide_allocation():
+    # 4 high-energy blocks at 6 bits, two at 5, the rest at 3: budget 3.25 bits
+    s = np.ones(64)
+    s[[5, 9, 40, 63]] = 4.0 ** 3
+    s[[7, 20]] = 4.0 ** 2
+    b = bg.allocate(s, 208, 1, 8)
+    assert sorted(set(b)) == [3, 5, 6]
+    return b
+
+
+def test_groups_and_allocation_up_to_eight_bits():
+    b = wide_allocation()
+    assert list(b[[5, 9, 40, 63]]) == [6] * 4 and list(b[[7, 20]]) == [5, 5]
+    gs = bg.groups(b)
+    assert [w for w, _ in gs] == [3, 5, 6]
+    assert list(gs[1][1]) == [14, 15, 40, 41] and list(gs[2][1]) == [10, 11, 18, 19, 80, 81, 126, 127]
+    # greedy = brute force with the wide range on a tiny head
+    s = np.array([50.0, 1.0, 900.0])
+    best, arg = bg.brute_force_min(s, 15, 1, 8)
+    assert list(bg.allocate(s, 15, 1, 8)) == list(arg)
+
+
+def _independent_record(codes, widths_by_position, record_bytes):
+    """Writes one record position by position: nibbles while the width is at most 4 (two
+    per byte, even position low), then one byte per position."""
+    out = bytearray(record_bytes)
+    byte, half = 0, 0
+    for j, (c, w) in enumerate(zip(codes, widths_by_position)):
+        if w <= 4:
+            out[byte] |= int(c) << (4 * half)
+            byte, half = (byte + half, 1 - half)
+        else:
+            out[byte] = int(c)
+            byte += 1
+    return list(out)
+
+
+def test_byte_container_record_layout():
+    rng = np.random.default_rng(11)
+    b = wide_allocation()
+    enc = bg.head_encoders(b, rng.standard_normal((8, 128, 128)))
+    p = bg.nibble_positions(enc)
+    assert p == 128 - 12 and bg.code_bytes(enc) == 80  # 58 nibble bytes + 12 bytes -> 80
+    x = rng.standard_normal((6, 128))
+    codes, norms, _ = bg.quantize_keys(x, enc)
+    assert codes[:, p:].max() >= 16  # byte groups use their range
+    packed = bg.pack_codes(codes, enc)
+    widths = np.concatenate([np.full(len(coords), w) for w, coords, *_ in enc])
+    for t in range(6):
+        assert list(packed[t]) == _independent_record(codes[t], widths, 80)
+    assert np.array_equal(bg.unpack_codes(packed, enc), codes)
+    # a wider record for the whole cache keeps the layout and pads with zeros
+    wide = bg.pack_codes(codes, enc, record_bytes=96)
+    assert np.array_equal(wide[:, :80], packed) and not wide[:, 80:].any()
+    # heads without wide groups keep the 64-byte nibble record
+    enc4 = bg.head_encoders(np.array([1, 2, 3, 4] * 16), rng.standard_normal((8, 128, 128)))
+    assert bg.code_bytes(enc4) == 64
+    c4, _, _ = bg.quantize_keys(x, enc4)
+    assert np.array_equal(bg.pack_codes(c4, enc4), bg.pack_codes(c4))
+
+
+def test_wide_groups_encode_within_the_rate_law():
+    rng = np.random.default_rng(12)
+    enc = bg.head_encoders(wide_allocation(), rng.standard_normal((8, 128, 128)))
+    x = rng.standard_normal((2000, 128))
+    codes, norms, _ = bg.quantize_keys(x, enc)
+    xr = bg.dequantize_keys(codes, norms, enc)
+    for w, coords, qm, c, m in enc:
+        n = len(coords)
+        err = np.sum((x[:, coords] - xr[:, coords]) ** 2, axis=1) / np.sum(x[:, coords] ** 2, axis=1)
+        d = n * codebook.distortion(w, n)
+        assert abs(err.mean() - d) < 0.1 * d, (w, n, err.mean(), d)

@@ -164,8 +164,13 @@ def generate(w: Workload, seed: int = 0, with_kv: bool = True):
         q_cal *= np.repeat(mul_k, g, axis=0)[None]
         k_cal = np.random.default_rng(s_ck).standard_normal((n_cal, hkv, HEAD_DIM), dtype=np.float32)
         k_cal *= mul_k[None]
-        extra = {"q_cal": q_cal, "k_cal": k_cal,
-                 "gauss": np.random.default_rng(s_rot).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32)}
+        # widths 5-8 (byte containers) draw from a stream of their own, so that widths 1-4
+        # keep their matrices
+        (s_rot_wide,) = ss.spawn(1)
+        gauss = np.concatenate(
+            [np.random.default_rng(s_rot).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32),
+             np.random.default_rng(s_rot_wide).standard_normal((hkv, 4, HEAD_DIM, HEAD_DIM), dtype=np.float32)], axis=1)
+        extra = {"q_cal": q_cal, "k_cal": k_cal, "gauss": gauss}
     if w.codec == "qjl":
         # per KV head: Gaussian matrices for the MSE stage's rotation (as Block-GTQ's) and
         # the residual's projection S (m = 128 rows)
