@@ -543,7 +543,6 @@ def gtq_setup(w, inp, dev):
 
     import compressed_domain_attention_amd as tq
     T = w.seq_len
-    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device=dev)
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device=dev)
     x = torch.from_numpy(inp["k"]).to(dev)
     if w.codec == "qjl":  # two-stage keys
@@ -566,6 +565,7 @@ def gtq_setup(w, inp, dev):
     energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
     bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
     keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device=dev)
     prompt = x[:, :, :T - 1].contiguous()
     tq.gtq_quantize_keys(keys, prompt[:, :, :1].contiguous(), codes, norms)  # loads the kernel before timing
     torch.cuda.synchronize()

@@ -66,7 +66,8 @@ class GtqHead(ctypes.Structure):
     """tq_gtq_head: one KV head's Block-GTQ key encoder (layout in include/tq.h)."""
     _fields_ = [("n_groups", ctypes.c_int32), ("width", ctypes.c_int32 * 4), ("start", ctypes.c_int32 * 4),
                 ("dim", ctypes.c_int32 * 4), ("rot_offset", ctypes.c_int32 * 4), ("coord", ctypes.c_int32 * 128),
-                ("centroid", (ctypes.c_float * 16) * 4), ("boundary", (ctypes.c_float * 15) * 4),
+                ("byte_at", ctypes.c_int32 * 4), ("code_used", ctypes.c_int32), ("code_bytes", ctypes.c_int32),
+                ("centroid", (ctypes.c_float * 256) * 4), ("boundary", (ctypes.c_float * 255) * 4),
                 ("f16_scale", ctypes.c_float * 4)]
 
 
@@ -129,11 +130,12 @@ def library():
     lib.tq_gtq_allocate.restype = I
     lib.tq_gtq_prepare.argtypes = [P, P, ctypes.POINTER(GtqHead), P]
     lib.tq_gtq_prepare.restype = I
-    lib.tq_gtq_quantize_keys.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
+    lib.tq_gtq_quantize_keys.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P]
     lib.tq_gtq_quantize_keys.restype = I
-    lib.tq_gtq_attention.argtypes = [P, P, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
+    lib.tq_gtq_attention.argtypes = [P, P, I, P, P, P, I, I, I, P, I, I, P, I, F, I, P, P, P, P, P]
     lib.tq_gtq_attention.restype = I
-    lib.tq_gtq_append_attention.argtypes = [P, P, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P, P, P, P, P]
+    lib.tq_gtq_append_attention.argtypes = [P, P, I, P, P, P, I, I, I, P, P, I, P, I, I, P, I, I, F, I, P, P, P, P,
+                                            P]
     lib.tq_gtq_append_attention.restype = I
     lib.tq_gtq_qjl_projection.argtypes = [P, P, P, P]
     lib.tq_gtq_qjl_projection.restype = I
@@ -490,16 +492,19 @@ def gtq_allocate(energies, budget: int, b_min: int = 1, b_max: int = 4):
 class GtqKeys:
     """Block-GTQ key encoders of every KV head (built on the host, held on the device).
 
-    block_bits: int [n_kv_heads, 64] widths in 1..4; gauss: float32 [n_kv_heads, 4, 128, 128]
-    (width w of head h uses gauss[h, w-1])."""
+    block_bits: int [n_kv_heads, 64] widths in 1..8 (at most four distinct per head); gauss:
+    float32 [n_kv_heads, W, 128, 128] with W >= the largest width (width w of head h uses
+    gauss[h, w-1]).  code_bytes: the record's code bytes for the whole cache, the largest of
+    the heads' (64 when no group is wider than 4 bits)."""
 
     def __init__(self, block_bits, gauss, device="cuda"):
         import numpy as np
         bits = np.ascontiguousarray(block_bits, dtype=np.int32)
         g = np.ascontiguousarray(gauss, dtype=np.float32)
         hkv = bits.shape[0]
-        if bits.shape != (hkv, 64) or g.shape != (hkv, 4, 128, 128):
-            raise ValueError("block_bits [n_kv_heads, 64] and gauss [n_kv_heads, 4, 128, 128] are required")
+        if bits.shape != (hkv, 64) or g.ndim != 4 or g.shape[0] != hkv or g.shape[2:] != (128, 128) or \
+                g.shape[1] < int(bits.max()):
+            raise ValueError("block_bits [n_kv_heads, 64] and gauss [n_kv_heads, W >= max width, 128, 128] are required")
         self.heads_host = (GtqHead * hkv)()
         rot = np.zeros((hkv, GTQ_ROTATION_FLOATS), dtype=np.float32)
         for h in range(hkv):
@@ -510,6 +515,7 @@ class GtqKeys:
         self.rotations = torch.from_numpy(rot).to(device)
         self.n_kv_heads = hkv
         self.block_bits = bits
+        self.code_bytes = max(self.heads_host[h].code_bytes for h in range(hkv))
 
     def n_groups(self, h):
         return self.heads_host[h].n_groups
@@ -543,18 +549,20 @@ class QjlKeys(GtqKeys):
 
 def gtq_quantize_keys(enc: GtqKeys, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor, pos0: int = 0):
     """Encode x [batch, n_kv_heads, n_new, 128] (fp16/fp32) into codes uint8 [batch,
-    n_kv_heads, capacity, 64] and norms fp32 [batch, n_kv_heads, capacity, 4] at pos0 .."""
+    n_kv_heads, capacity, enc.code_bytes] and norms fp32 [batch, n_kv_heads, capacity, 4] at
+    pos0 .."""
     if x.dtype not in _DTYPES or not x.is_contiguous() or x.dim() != 4 or x.shape[3] != HEAD_DIM:
         raise ValueError("x must be contiguous [batch, n_kv_heads, n_new, 128] float16/float32")
     bsz, hkv, n_new = x.shape[:3]
     if hkv != enc.n_kv_heads:
         raise ValueError("x has %d KV heads, the encoders %d" % (hkv, enc.n_kv_heads))
     cap = codes.shape[2]
-    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (bsz, hkv, cap, 64) or not codes.is_contiguous()
+    cb = enc.code_bytes
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (bsz, hkv, cap, cb) or not codes.is_contiguous()
             or norms.dtype != torch.float32 or tuple(norms.shape) != (bsz, hkv, cap, 4) or not norms.is_contiguous()):
-        raise ValueError("codes uint8 [batch, n_kv_heads, capacity, 64] and norms float32 [.., capacity, 4]")
+        raise ValueError("codes uint8 [batch, n_kv_heads, capacity, %d] and norms float32 [.., capacity, 4]" % cb)
     _check(library().tq_gtq_quantize_keys(_ptr(enc.heads), _ptr(enc.rotations), _ptr(x), _DTYPES[x.dtype], bsz, hkv,
-                                          n_new, pos0, cap, _ptr(codes), _ptr(norms), _stream()),
+                                          n_new, pos0, cap, cb, _ptr(codes), _ptr(norms), _stream()),
            "tq_gtq_quantize_keys")
     return codes, norms
 
@@ -569,7 +577,7 @@ def gtq_attention(enc: GtqKeys, codes, norms, v, q, seq_lens=None, max_len=None,
         raise ValueError("q must be a contiguous float16/float32 tensor")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
-    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
             tuple(norms.shape) != (bsz, hkv, cap, 4):
         raise ValueError("codes, norms and v must describe the same [batch, n_kv_heads, capacity] cache")
     if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != bsz):
@@ -588,7 +596,7 @@ def gtq_attention(enc: GtqKeys, codes, norms, v, q, seq_lens=None, max_len=None,
         if part_lse is None:
             part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
     _check(library().tq_gtq_attention(
-        _ptr(enc.heads), _ptr(enc.rotations), _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(q),
+        _ptr(enc.heads), _ptr(enc.rotations), enc.code_bytes, _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(q),
         _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse), _ptr(part_o),
         _ptr(part_lse), _stream()), "tq_gtq_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)
@@ -606,7 +614,7 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
         raise ValueError("q must be a contiguous float16/float32 tensor")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
-    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, 64) or \
+    if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
             tuple(norms.shape) != (bsz, hkv, cap, 4):
         raise ValueError("codes, norms and v must describe the same [batch, n_kv_heads, capacity] cache")
     for name, x in (("k_new", k_new), ("v_new", v_new)):
@@ -629,7 +637,7 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
         if part_lse is None:
             part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
     _check(library().tq_gtq_append_attention(
-        _ptr(enc.heads), _ptr(enc.rotations), _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(k_new),
+        _ptr(enc.heads), _ptr(enc.rotations), enc.code_bytes, _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(k_new),
         _ptr(v_new), _DTYPES[k_new.dtype], _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits,
         _ptr(out), _ptr(lse), _ptr(part_o), _ptr(part_lse), _stream()), "tq_gtq_append_attention")
     return (out, lse) if n_splits == 1 else (part_o, part_lse)

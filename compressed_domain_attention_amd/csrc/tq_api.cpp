@@ -367,15 +367,19 @@ extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_m
   return from_hip(tq::launch_zip_attention(a, (int)q_dtype, (hipStream_t)stream));
 }
 
+// A Block-GTQ record's code bytes: 64 (nibbles only) up to 128, a multiple of 16.
+static bool valid_gtq_code_bytes(int32_t b) { return b >= 64 && b <= 128 && b % 16 == 0; }
+
 static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, const float* proj, const void* x,
                               tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0,
-                              int32_t capacity, uint8_t* codes, float* norms, uint8_t* signs, int32_t code_bits,
-                              void* stream) {
+                              int32_t capacity, int32_t code_bytes, uint8_t* codes, float* norms, uint8_t* signs,
+                              int32_t code_bits, void* stream) {
   if (heads == nullptr || rotations == nullptr || x == nullptr || codes == nullptr || norms == nullptr)
     return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_F16) return TQ_EINVAL;
   if (batch <= 0 || batch > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_new < 0 || pos0 < 0 || capacity <= 0)
     return TQ_EINVAL;
+  if (code_bits == 0 && !valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
   if ((int64_t)pos0 + n_new > capacity) return TQ_ECAPACITY;
   if (n_new == 0) return TQ_OK;
   tq::GtqQuantArgs a;
@@ -392,14 +396,16 @@ static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, 
   a.proj = proj;
   a.signs = signs;
   a.code_bits = code_bits;
+  a.code_bytes = code_bits ? 16 * code_bits : code_bytes;
   return from_hip(tq::launch_gtq_quantize(a, x_dtype == TQ_F16, batch, (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x,
                                           tq_dtype x_dtype, int32_t batch, int32_t n_kv_heads, int32_t n_new,
-                                          int32_t pos0, int32_t capacity, uint8_t* codes, float* norms, void* stream) {
-  return gtq_quantize(heads, rotations, nullptr, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, codes, norms,
-                      nullptr, 0, stream);
+                                          int32_t pos0, int32_t capacity, int32_t code_bytes, uint8_t* codes,
+                                          float* norms, void* stream) {
+  return gtq_quantize(heads, rotations, nullptr, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, code_bytes,
+                      codes, norms, nullptr, 0, stream);
 }
 
 extern "C" tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const float* rotations, const float* proj,
@@ -407,11 +413,12 @@ extern "C" tq_status tq_gtq_qjl_quantize_keys(const tq_gtq_head* heads, const fl
                                               int32_t n_new, int32_t pos0, int32_t capacity, uint8_t* codes,
                                               float* norms, uint8_t* signs, void* stream) {
   if (proj == nullptr || signs == nullptr || mse_bits < 1 || mse_bits > 3) return TQ_EINVAL;
-  return gtq_quantize(heads, rotations, proj, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, codes, norms,
+  return gtq_quantize(heads, rotations, proj, x, x_dtype, batch, n_kv_heads, n_new, pos0, capacity, 0, codes, norms,
                       signs, mse_bits, stream);
 }
 
-static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
+static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes,
+                                    const uint8_t* codes,
                                     const float* norms, const void* v, int32_t capacity, int32_t batch,
                                     int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
                                     const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
@@ -423,6 +430,7 @@ static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotat
     return TQ_EINVAL;
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
   if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
+  if (code_bytes != 0 && !valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
   if (capacity > (1 << 24)) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's values
   const int group = n_q_heads / n_kv_heads;
@@ -450,17 +458,20 @@ static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotat
   a.n_slices = slices;
   a.n_splits = n_splits;
   a.capacity = capacity;
+  a.code_bytes = code_bytes;
   a.scale_log2 = scale * 1.4426950408889634f;
   return TQ_OK;
 }
 
-extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes,
+extern "C" tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes,
+                                      const uint8_t* codes,
                                       const float* norms, const void* v, int32_t capacity, int32_t batch,
                                       int32_t n_kv_heads, const void* q, tq_dtype q_dtype, int32_t n_q_heads,
                                       const int32_t* seq_lens, int32_t max_len, float scale, int32_t n_splits,
                                       float* out, float* lse_out, float* part_o, float* part_lse, void* stream) {
+  if (!valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
   tq::GtqAttnArgs a;
-  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+  const tq_status st = gtq_attention_args(heads, rotations, code_bytes, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
                                           n_q_heads, seq_lens, max_len, scale, n_splits, out, lse_out, part_o,
                                           part_lse, a);
   if (st != TQ_OK) return st;
@@ -475,7 +486,7 @@ extern "C" tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float*
                                           float* part_o, float* part_lse, void* stream) {
   if (proj == nullptr || signs == nullptr || mse_bits < 1 || mse_bits > 3) return TQ_EINVAL;
   tq::GtqAttnArgs a;
-  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+  const tq_status st = gtq_attention_args(heads, rotations, 0, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
                                           n_q_heads, seq_lens, max_len, scale, n_splits, out, lse_out, part_o,
                                           part_lse, a);
   if (st != TQ_OK) return st;
@@ -486,7 +497,7 @@ extern "C" tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float*
 }
 
 static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotations, const float* proj,
-                                 int32_t code_bits, uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
+                                 int32_t code_bits, int32_t code_bytes, uint8_t* codes, float* norms, uint8_t* signs, void* v, int32_t capacity,
                                  int32_t batch, int32_t n_kv_heads, const void* k_new, const void* v_new,
                                  tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos, const void* q,
                                  tq_dtype q_dtype, int32_t n_q_heads, float scale, int32_t n_splits, float* out,
@@ -498,7 +509,7 @@ static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotation
   const int64_t max_len = (int64_t)(pos ? max_pos : pos0) + 1;
   if (max_len > capacity) return TQ_ECAPACITY;
   tq::GtqAttnArgs a;
-  const tq_status st = gtq_attention_args(heads, rotations, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
+  const tq_status st = gtq_attention_args(heads, rotations, code_bytes, codes, norms, v, capacity, batch, n_kv_heads, q, q_dtype,
                                           n_q_heads, pos, (int32_t)max_len, scale, n_splits, out, lse_out, part_o,
                                           part_lse, a);
   if (st != TQ_OK) return st;
@@ -517,14 +528,16 @@ static tq_status gtq_append_step(const tq_gtq_head* heads, const float* rotation
   return from_hip(tq::launch_gtq_attention(a, q_dtype == TQ_F16, (hipStream_t)stream));
 }
 
-extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes,
+extern "C" tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes,
+                                             uint8_t* codes,
                                              float* norms, void* v, int32_t capacity, int32_t batch,
                                              int32_t n_kv_heads, const void* k_new, const void* v_new,
                                              tq_dtype x_dtype, const int32_t* pos, int32_t pos0, int32_t max_pos,
                                              const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,
                                              int32_t n_splits, float* out, float* lse_out, float* part_o,
                                              float* part_lse, void* stream) {
-  return gtq_append_step(heads, rotations, nullptr, 0, codes, norms, nullptr, v, capacity, batch, n_kv_heads, k_new,
+  if (!valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
+  return gtq_append_step(heads, rotations, nullptr, 0, code_bytes, codes, norms, nullptr, v, capacity, batch, n_kv_heads, k_new,
                          v_new, x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads, scale, n_splits, out, lse_out,
                          part_o, part_lse, stream);
 }
@@ -538,7 +551,7 @@ extern "C" tq_status tq_gtq_qjl_append_attention(const tq_gtq_head* heads, const
                                                  float* out, float* lse_out, float* part_o, float* part_lse,
                                                  void* stream) {
   if (proj == nullptr || signs == nullptr || mse_bits < 1 || mse_bits > 3) return TQ_EINVAL;
-  return gtq_append_step(heads, rotations, proj, mse_bits, codes, norms, signs, v, capacity, batch, n_kv_heads, k_new, v_new,
+  return gtq_append_step(heads, rotations, proj, mse_bits, 0, codes, norms, signs, v, capacity, batch, n_kv_heads, k_new, v_new,
                          x_dtype, pos, pos0, max_pos, q, q_dtype, n_q_heads, scale, n_splits, out, lse_out, part_o,
                          part_lse, stream);
 }

@@ -117,6 +117,114 @@ extern "C" tq_status tq_make_codebook(int32_t bits, int32_t dim, tq_codebook* ou
   return TQ_OK;
 }
 
+namespace tq {
+
+// Lloyd-Max levels for 5 .. 8 bits (the byte containers of Block-GTQ keys): the conditions
+// of 2.3 (each level the mean of its cell, boundaries at midpoints) solved by Newton's
+// method, since the plain iteration above converges too slowly at 32 .. 256 levels.  The
+// residual r_k = c_k - E[t | cell k] depends on c_{k-1}, c_k, c_{k+1} through the cell's two
+// boundaries, so the Jacobian is tridiagonal (Thomas algorithm).  Cell integrals are taken
+// in theta (t = sin theta): the mass of (1 - t^2)^mu dt is cos^(dim-2) theta d theta, smooth
+// for every dim >= 2, by Gauss-Legendre panels; the first moment is closed form.  The start
+// places levels at quantiles of the density^(1/3) law (the asymptotic point density of
+// optimal quantisers, Panter and Dite).  Writes 2^bits centroids and 2^bits - 1 boundaries
+// (fp32) and the fp16 scale; returns false if the iteration does not settle.
+bool wide_codebook(int bits, int dim, float* centroid, float* boundary, float* scale) {
+  if (bits < 5 || bits > 8 || dim < 2) return false;
+  const int n = 1 << bits;
+  const double mu = 0.5 * (dim - 3), pw = dim - 2.0;
+  auto cos_mass = [&](double lo, double hi) {  // int_lo^hi (1 - t^2)^mu dt
+    const double a = std::asin(std::fmax(-1.0, std::fmin(1.0, lo))), b = std::asin(std::fmax(-1.0, std::fmin(1.0, hi)));
+    if (b <= a) return 0.0;
+    const int panels = 8;
+    const double h = (b - a) / panels;
+    double total = 0.0;
+    for (int p = 0; p < panels; ++p) {
+      const double mid = a + (p + 0.5) * h, half = 0.5 * h;
+      double sum = 0.0;
+      for (int k = 0; k < 8; ++k)
+        sum += kWeights[k] * (std::pow(std::cos(mid - half * kNodes[k]), pw) + std::pow(std::cos(mid + half * kNodes[k]), pw));
+      total += sum * half;
+    }
+    return total;
+  };
+  auto dens = [&](double t) { return integrand(t, mu); };
+  // start: quantiles of f^(1/3), integrated in theta (f^(1/3) dt = cos^(dim/3) theta d theta)
+  const int G = 20000;
+  static thread_local double cum[G + 1];
+  cum[0] = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double t0 = -M_PI / 2 + M_PI * i / G, t1 = -M_PI / 2 + M_PI * (i + 1) / G;
+    cum[i + 1] = cum[i] + 0.5 * (std::pow(std::cos(t0), dim / 3.0) + std::pow(std::cos(t1), dim / 3.0)) * (t1 - t0);
+  }
+  double c[256], m0[256], mean[256], b[256], res[256];
+  for (int k = 0, i = 0; k < n; ++k) {
+    const double target = (k + 0.5) / n * cum[G];
+    while (i < G - 1 && cum[i + 1] < target) ++i;
+    const double f = (target - cum[i]) / (cum[i + 1] - cum[i]);
+    c[k] = std::sin(-M_PI / 2 + M_PI * (i + f) / G);
+  }
+  for (int it = 0; it < 100; ++it) {
+    for (int k = 0; k + 1 < n; ++k) b[k] = 0.5 * (c[k] + c[k + 1]);
+    double worst = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const double lo = k ? b[k - 1] : -1.0, hi = k + 1 < n ? b[k] : 1.0;
+      m0[k] = cos_mass(lo, hi);
+      mean[k] = first_moment(lo, hi, mu) / m0[k];
+      res[k] = c[k] - mean[k];
+      worst = std::fmax(worst, std::fabs(res[k]));
+    }
+    if (worst < 1e-13) break;
+    // tridiagonal Jacobian: d mean_k / d b = (b - mean_k) f(b) / m0_k at the upper boundary,
+    // minus that at the lower one; a boundary moves by half of either neighbouring level
+    double lo_d[256], di[256], up_d[256];
+    for (int k = 0; k < n; ++k) {
+      di[k] = 1.0;
+      lo_d[k] = up_d[k] = 0.0;
+      if (k + 1 < n) {
+        const double u = (b[k] - mean[k]) * dens(b[k]) / (2.0 * m0[k]);
+        di[k] -= u;
+        up_d[k] = -u;
+      }
+      if (k > 0) {
+        const double l = (b[k - 1] - mean[k]) * dens(b[k - 1]) / (2.0 * m0[k]);
+        di[k] += l;
+        lo_d[k] = l;
+      }
+    }
+    // Thomas algorithm
+    double cp[256], dp[256], step[256];
+    cp[0] = up_d[0] / di[0];
+    dp[0] = res[0] / di[0];
+    for (int k = 1; k < n; ++k) {
+      const double den = di[k] - lo_d[k] * cp[k - 1];
+      cp[k] = up_d[k] / den;
+      dp[k] = (res[k] - lo_d[k] * dp[k - 1]) / den;
+    }
+    step[n - 1] = dp[n - 1];
+    for (int k = n - 2; k >= 0; --k) step[k] = dp[k] - cp[k] * step[k + 1];
+    double lam = 1.0, nc[256];
+    for (int tries = 0; tries < 60; ++tries, lam *= 0.5) {
+      bool ok = true;
+      for (int k = 0; k < n; ++k) nc[k] = c[k] - lam * step[k];
+      for (int k = 0; k < n && ok; ++k) ok = nc[k] > -1.0 && nc[k] < 1.0 && (k == 0 || nc[k] > nc[k - 1]);
+      if (ok) break;
+    }
+    for (int k = 0; k < n; ++k) c[k] = nc[k];
+  }
+  double worst = 0.0;
+  for (int k = 0; k < n; ++k) worst = std::fmax(worst, std::fabs(res[k]));
+  if (!(worst < 1e-10)) return false;
+  double sym[256];
+  for (int k = 0; k < n; ++k) sym[k] = 0.5 * (c[k] - c[n - 1 - k]);
+  for (int k = 0; k < n; ++k) centroid[k] = (float)sym[k];
+  for (int k = 0; k + 1 < n; ++k) boundary[k] = (float)(0.5 * (sym[k] + sym[k + 1]));
+  *scale = f16_scale(centroid, n);
+  return true;
+}
+
+}  // namespace tq
+
 extern "C" const char* tq_status_string(tq_status s) {
   switch (s) {
     case TQ_OK: return "ok";

@@ -7,6 +7,11 @@
 
 #include "tq.h"
 
+namespace tq {
+// 5 .. 8-bit Lloyd-Max codebook (tq_codebook.cpp)
+bool wide_codebook(int bits, int dim, float* centroid, float* boundary, float* scale);
+}
+
 extern "C" tq_status tq_gtq_block_energies(const float* q_cal, const float* k_cal, int32_t n_tokens,
                                            int32_t n_q_heads, int32_t n_kv_heads, float* energies) {
   if (q_cal == nullptr || k_cal == nullptr || energies == nullptr) return TQ_EINVAL;
@@ -58,12 +63,16 @@ extern "C" tq_status tq_gtq_allocate(const float* energies, int32_t n_blocks, in
 extern "C" tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gauss, tq_gtq_head* head,
                                     float* rotation) {
   if (block_bits == nullptr || gauss == nullptr || head == nullptr || rotation == nullptr) return TQ_EINVAL;
-  for (int i = 0; i < TQ_GTQ_BLOCKS; ++i)
-    if (block_bits[i] < 1 || block_bits[i] > 4) return TQ_EINVAL;
+  int present = 0;
+  for (int i = 0; i < TQ_GTQ_BLOCKS; ++i) {
+    if (block_bits[i] < 1 || block_bits[i] > TQ_GTQ_MAX_WIDTH) return TQ_EINVAL;
+    present |= 1 << block_bits[i];
+  }
+  if (__builtin_popcount(present) > TQ_GTQ_MAX_GROUPS) return TQ_EUNSUPPORTED;
   std::memset(head, 0, sizeof(*head));
   std::memset(rotation, 0, sizeof(float) * TQ_GTQ_ROTATION_FLOATS);
   int pos = 0, off = 0, g = 0;
-  for (int w = 1; w <= 4; ++w) {
+  for (int w = 1; w <= TQ_GTQ_MAX_WIDTH; ++w) {
     std::vector<int> coords;
     for (int i = 0; i < TQ_GTQ_BLOCKS; ++i)
       if (block_bits[i] == w) {
@@ -96,18 +105,31 @@ extern "C" tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gaus
       for (int r = 0; r < n; ++r) q[(size_t)r * n + c] = v[r] / nrm;
     }
     for (int i = 0; i < n * n; ++i) rotation[off + i] = (float)q[i];
-    tq_codebook cb;
-    const tq_status st = tq_make_codebook(w, n, &cb);
-    if (st != TQ_OK) return st;
-    for (int k = 0; k < 16; ++k) head->centroid[g][k] = cb.centroid[k];
-    for (int k = 0; k < 15; ++k) head->boundary[g][k] = cb.boundary[k];
-    head->f16_scale[g] = cb.f16_scale;
+    if (w <= 4) {
+      tq_codebook cb;
+      const tq_status st = tq_make_codebook(w, n, &cb);
+      if (st != TQ_OK) return st;
+      for (int k = 0; k < 16; ++k) head->centroid[g][k] = cb.centroid[k];
+      for (int k = 0; k < 15; ++k) head->boundary[g][k] = cb.boundary[k];
+      head->f16_scale[g] = cb.f16_scale;
+    } else if (!tq::wide_codebook(w, n, head->centroid[g], head->boundary[g], &head->f16_scale[g])) {
+      return TQ_EUNSUPPORTED;
+    }
     pos += n;
     off += n * n;
     ++g;
   }
   head->n_groups = g;
   for (int k = g; k < TQ_GTQ_MAX_GROUPS; ++k) head->start[k] = 128;
+  // record layout: the nibble groups' P positions (two per byte), then a byte per position
+  // of the wider groups
+  int nib = 0;
+  for (int k = 0; k < g; ++k)
+    if (head->width[k] <= 4) nib += head->dim[k];
+  for (int k = 0; k < g; ++k) head->byte_at[k] = head->width[k] <= 4 ? head->start[k] / 2 : nib / 2 + head->start[k] - nib;
+  for (int k = g; k < TQ_GTQ_MAX_GROUPS; ++k) head->byte_at[k] = nib / 2 + 128 - nib;
+  head->code_used = nib / 2 + 128 - nib;
+  head->code_bytes = nib == 128 ? 64 : (head->code_used + 15) / 16 * 16;
   return TQ_OK;
 }
 

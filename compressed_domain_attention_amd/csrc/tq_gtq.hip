@@ -45,6 +45,18 @@ __device__ __forceinline__ uint32_t spread_bits(uint32_t x) {
   return (x | (x << 1)) & 0x55555555u;
 }
 
+// Number of the sorted boundaries bnd[0 .. nb) strictly below y (the compare-count code), by
+// binary search: at most 8 steps for the 255 boundaries of an 8-bit codebook.
+__device__ __forceinline__ uint32_t count_below(float y, const float* bnd, int nb) {
+  int lo = 0, hi = nb;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (bnd[mid] < y) lo = mid + 1;
+    else hi = mid;
+  }
+  return (uint32_t)lo;
+}
+
 __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* src) {
   constexpr int words = sizeof(tq_gtq_head) / 4;
   for (int i = threadIdx.x; i < words; i += blockDim.x) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
@@ -61,11 +73,13 @@ __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* 
 // PK (two-stage keys: the first stage's width, 1 to 3): the 128 codes are written
 // bit-packed, code of position i at bit PK i of the record's little-endian bit string (16 PK
 // bytes), and compared against the first 2^PK - 1 boundaries only, so every code fits its
-// field whatever the head's width.  PK = 0: Block-GTQ's one nibble per position.
+// field whatever the head's width.  PK = 0: a Block-GTQ record of rec_bytes code bytes, a
+// nibble per position of groups up to 4 bits and a byte per position of wider ones (at the
+// head's byte_at), zeros from code_used on; nothing is written past rec_bytes.
 template <bool XF16, bool QJL = false, int PK = 0>
 __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* rot, const void* x, float* ubuf,
                                            uint8_t* code_rec, float* norm_rec, int lane, const float* proj = nullptr,
-                                           uint8_t* sign_rec = nullptr) {
+                                           uint8_t* sign_rec = nullptr, int rec_bytes = 64) {
   const int j0 = 2 * lane;
   const int g = group_of(hd, j0);
   const int st = hd.start[g], n = hd.dim[g], off = hd.rot_offset[g];
@@ -102,11 +116,8 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
   }
   y0 += z0;
   y1 += z1;
-  uint32_t c0 = 0, c1 = 0;
-  for (int k = 0; k < nb; ++k) {  // compare-count against the group's boundaries
-    c0 += y0 > hd.boundary[g][k];
-    c1 += y1 > hd.boundary[g][k];
-  }
+  // compare-count against the group's boundaries
+  const uint32_t c0 = count_below(y0, hd.boundary[g], nb), c1 = count_below(y1, hd.boundary[g], nb);
   if (PK == 1) {
     // bit l of m0 (m1) is the code of position 2l (2l + 1): word w interleaves bits
     // 16 w .. 16 w + 15 of both
@@ -125,7 +136,15 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
                        ((uint32_t)__shfl(f, q + 3) << 18);
     if ((lane & 3) < 3) code_rec[3 * (lane >> 2) + (lane & 3)] = (uint8_t)(w >> (8 * (lane & 3)));
   } else {
-    code_rec[lane] = (uint8_t)(c0 | (c1 << 4));
+    if (hd.width[g] <= 4) {
+      const int o = hd.byte_at[g] + ((j0 - st) >> 1);
+      if (o < rec_bytes) code_rec[o] = (uint8_t)(c0 | (c1 << 4));
+    } else {
+      const int o = hd.byte_at[g] + (j0 - st);
+      if (o < rec_bytes) code_rec[o] = (uint8_t)c0;
+      if (o + 1 < rec_bytes) code_rec[o + 1] = (uint8_t)c1;
+    }
+    for (int i = hd.code_used + lane; i < rec_bytes; i += 64) code_rec[i] = 0;
   }
   float coef = 0.f;
   if (QJL) {
@@ -159,7 +178,7 @@ __device__ __forceinline__ void encode_key(const tq_gtq_head& hd, const float* r
 constexpr int kQuantTokens = 512;
 template <bool XF16, bool QJL, int PK>
 __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a) {
-  constexpr int CREC = PK ? 16 * PK : 64;  // code bytes per key
+  const int CREC = PK ? 16 * PK : a.code_bytes;  // code bytes per key
   __shared__ __attribute__((aligned(16))) float rot[TQ_GTQ_ROTATION_FLOATS];
   __shared__ __attribute__((aligned(16))) float projl[QJL ? 128 * 128 : 1];
   __shared__ __attribute__((aligned(16))) float ubuf[4][128];
@@ -183,7 +202,7 @@ __global__ __launch_bounds__(256) void gtq_quantize_kernel(const GtqQuantArgs a)
     const size_t rec = stream * a.capacity + a.pos0 + i;
     encode_key<XF16, QJL, PK>(hd, rot, (const uint8_t*)a.x + (stream * a.n_new + i) * 128 * (XF16 ? 2 : 4),
                               ubuf[wv], a.codes + rec * CREC, a.norms + rec * 4, lane, projl,
-                              QJL ? a.signs + rec * 16 : nullptr);
+                              QJL ? a.signs + rec * 16 : nullptr, CREC);
     // the next token's writes to ubuf follow this token's reads in program order
     __builtin_amdgcn_wave_barrier();
   }
@@ -247,27 +266,37 @@ constexpr int kMaxKb = 7;         // k-blocks of a head: sum over groups of ceil
 // 256 entries, a code byte's four codes as [hi pair, lo pair, hi pair, lo pair] (one 16-byte
 // read per four codes).  PK = 3: one table of 64 entries over two codes, [hi pair, lo pair],
 // read four times per lane's 24-bit word.
-template <int NW, int D, bool QF16, bool QJL, int PK = 0>
+// WIDE (Block-GTQ records of more than 64 code bytes, with byte-container groups): the
+// stage holds 2 KB of key records (two copies per stage); k-blocks of byte groups read the
+// lane's 8 code bytes and decode each through its group's 256-entry table of [hi, lo] fp16
+// parts, paired into operands by byte permutes.
+template <int NW, int D, bool QF16, bool QJL, int PK = 0, bool WIDE = false>
 __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArgs a) {
   static_assert((PK != 0) == QJL && PK >= 0 && PK <= 3, "packed codes are the first stage of two-stage keys");
+  static_assert(!WIDE || PK == 0, "byte containers are Block-GTQ records");
   constexpr bool B1 = PK == 1;
-  constexpr int CREC = PK ? 16 * PK : 64;  // code bytes per key
-  // a stage: key records 1 KB, norms 256 B (group-major), values 4 KB, sign bytes 256 B
-  constexpr int STAGE = QJL ? 5632 : 5376;
-  constexpr int NORM_AT = 1024, VAL_AT = 1280, SIGN_AT = 5376;
-  constexpr int NDMA = QJL ? 7 : 6;
+  const int CREC = PK ? 16 * PK : WIDE ? a.code_bytes : 64;  // code bytes per key
+  // a stage: key records 1 KB (2 KB when WIDE), norms 256 B (group-major), values 4 KB,
+  // sign bytes 256 B
+  constexpr int KAREA = WIDE ? 2048 : 1024;
+  constexpr int NORM_AT = KAREA, VAL_AT = KAREA + 256, SIGN_AT = KAREA + 4352;
+  constexpr int STAGE = QJL ? SIGN_AT + 256 : SIGN_AT;
+  constexpr int NDMA = (QJL ? 7 : 6) + (WIDE ? 1 : 0);
   constexpr int WAVE_LDS = D * STAGE;
   static_assert(D >= 2 && D * NDMA <= 63, "ring depth within the memory counter");
   static_assert(NW == 4 || NW == 8, "the query rotation maps 64 NW threads onto 128 positions x 8 heads");
   // k-blocks: up to 7 for a Block-GTQ head; two-stage keys have one group of 128 (4 blocks)
   constexpr int KB = QJL ? 4 : kMaxKb;
   constexpr int PTAB_BYTES = PK == 0 ? KB * 256 * 8 : PK == 2 ? 256 * 16 : PK == 3 ? 64 * 8 : 0;
-  constexpr int TAB_BYTES = PTAB_BYTES + (QJL ? 256 * 16 : 0);  // pair tables, +-1 table
+  constexpr int WTAB_BYTES = WIDE ? TQ_GTQ_MAX_GROUPS * 256 * 4 : 0;
+  constexpr int TAB_BYTES = PTAB_BYTES + WTAB_BYTES + (QJL ? 256 * 16 : 0);  // pair tables, byte tables, +-1 table
   // the pair tables first, so that their addresses fit the LDS instructions' offset field
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[TAB_BYTES + NW * WAVE_LDS];
   uint2(*const ptab)[256] = (uint2(*)[256])lds_all;
   uint8_t* const lds = lds_all + TAB_BYTES;
-  uint8_t* const pmtab = lds_all + PTAB_BYTES;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
+  uint8_t* const pmtab = lds_all + PTAB_BYTES + WTAB_BYTES;  // QJL: byte -> 8 fp16 +-1 (bit e: position e)
+  // WIDE: per group, a byte code's level as fp16 hi | fp16 lo << 16 (zero past the codebook)
+  uint32_t(*const wtab)[256] = (uint32_t(*)[256])(lds_all + PTAB_BYTES);
   // (ptab: per k-block and byte, the fp16 hi parts of s c for the byte's two codes, then
   // their lo parts; zero for the blocks past the head's last, which then add nothing.
   // PK = 2, 3: the one group's table, ptab4 or ptab6, at the same place)
@@ -318,6 +347,16 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const int l = lane % (16 * PK);
       t = t0 + l / PK;
       lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * CREC + 16 * (l % PK)) : (uint32_t)(t0 * CREC));
+    } else if (WIDE) {
+      // the 16 records (CREC bytes each, a multiple of 16) are one span: copy d moves its
+      // bytes 1024 d + 16 l .. + 15; lanes past the span read the tile's first record
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int o = 1024 * d + 16 * lane, tk = o / CREC;
+        t = t0 + tk;
+        lds_dma<16, true>(dst + 1024 * d, kc,
+                          tk < 16 && t < cap ? (uint32_t)(t * CREC + (o - tk * CREC)) : (uint32_t)(t0 * CREC));
+      }
     } else {
       lds_dma<16, true>(dst, kc, t < cap ? (uint32_t)(t * 64 + 16 * (lane & 3)) : (uint32_t)(t0 * 64));
     }
@@ -359,11 +398,11 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       uint8_t* srec = QJL ? a.w_signs + rec * 16 : nullptr;
       if (a.x_f16) {
         encode_key<true, QJL, PK>(hd, grot, (const _Float16*)a.k_new + st * 128, (float*)wlds,
-                                  a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
+                                  a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec, CREC);
         ((uint32_t*)vd)[lane] = ((const uint32_t*)a.v_new)[st * 64 + lane];
       } else {
         encode_key<false, QJL, PK>(hd, grot, (const float*)a.k_new + st * 128, (float*)wlds,
-                                   a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec);
+                                   a.w_codes + rec * CREC, a.w_norms + rec * 4, lane, pj, srec, CREC);
         const float2 x = ((const float2*)a.v_new)[st * 64 + lane];
         ((uint32_t*)vd)[lane] = pack_f16(x.x, x.y);
       }
@@ -383,12 +422,20 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   auto group_of_block = [&](int kb) { return (kb >= cum[1]) + (kb >= cum[2]) + (kb >= cum[3]); };
   for (int i = tid; i < (PK ? 0 : KB * 256); i += 64 * NW) {
     const int kb = i >> 8, by = i & 255, g = kb < nkb ? group_of_block(kb) : 0;
-    // codes past the codebook decode to 0
-    const int nc = kb < nkb ? 1 << min(max(hd.width[g], 1), 4) : 0;
+    // codes past the codebook decode to 0 (and byte groups do not use these tables)
+    const int nc = kb < nkb && hd.width[g] <= 4 ? 1 << max(hd.width[g], 1) : 0;
     const float sc = hd.f16_scale[g];
     const float c0 = (by & 15) < nc ? sc * hd.centroid[g][by & 15] : 0.f;
     const float c1 = (by >> 4) < nc ? sc * hd.centroid[g][by >> 4] : 0.f;
     ptab[kb][by] = make_uint2(pack_f16(c0, c1), pack_f16(f16_lo(c0), f16_lo(c1)));
+  }
+  if (WIDE) {
+    for (int i = tid; i < TQ_GTQ_MAX_GROUPS * 256; i += 64 * NW) {
+      const int g = i >> 8, c = i & 255;
+      const int nc = g < hd.n_groups && hd.width[g] > 4 ? 1 << min(hd.width[g], 8) : 0;
+      const float v = c < nc ? hd.f16_scale[g] * hd.centroid[g][c] : 0.f;
+      wtab[g][c] = pack_f16(v, f16_lo(v));
+    }
   }
   if (PK == 2 || PK == 3) {  // the one group's levels (codes past its codebook decode to 0)
     const int nc = 1 << min(max(hd.width[0], 1), PK);
@@ -497,12 +544,15 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
   u32x4 qa[KB], qb[KB];
   int kgrp[KB];
   uint32_t kbyte[KB];
+  bool kwide[KB];  // WIDE: the block's group has byte containers (uniform)
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int g = kb < nkb ? group_of_block(kb) : 0, m = kb < nkb ? kb - cum[g] : 0;
     const int dg = hd.dim[g], sg = hd.start[g];
     kgrp[kb] = g;
-    kbyte[kb] = (uint32_t)((sg + 32 * m + 8 * jr) >> 1);
+    kwide[kb] = WIDE && kb < nkb && __builtin_amdgcn_readfirstlane(hd.width[g]) > 4;
+    // nibble groups: byte (position) / 2; byte groups: one byte per position from byte_at
+    kbyte[kb] = kwide[kb] ? (uint32_t)(hd.byte_at[g] + 32 * m + 8 * jr) : (uint32_t)((sg + 32 * m + 8 * jr) >> 1);
     qa[kb] = qb[kb] = u32x4{0u, 0u, 0u, 0u};
     if (!B1 && kb < nkb) {
       const int hh = col & 7;
@@ -559,10 +609,17 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
       const uint8_t* rec = sb + CREC * col;
       // every block is computed (those past the head's last have zero tables and query), so
       // the unrolled loop is one basic block the compiler can interleave
-      uint32_t cb[KB];
+      uint32_t cb[KB], cb2[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {  // every code word first
-        if (PK == 2) {  // positions 32 kb + 8 jr .. + 7: two bytes
+        cb2[kb] = 0u;
+        if (WIDE && kwide[kb]) {  // the lane's 8 code bytes from three aligned words
+          const uint32_t bo = kbyte[kb];
+          const uint32_t w0 = lds_read<uint32_t>(rec + (bo & ~3u)), w1 = lds_read<uint32_t>(rec + (bo & ~3u) + 4),
+                         w2 = lds_read<uint32_t>(rec + (bo & ~3u) + 8);
+          cb[kb] = __builtin_amdgcn_alignbyte(w1, w0, bo & 3u);
+          cb2[kb] = __builtin_amdgcn_alignbyte(w2, w1, bo & 3u);
+        } else if (PK == 2) {  // positions 32 kb + 8 jr .. + 7: two bytes
           cb[kb] = lds_read<uint16_t>(rec + 8 * kb + 2 * jr);
         } else {
           // the lane's code bytes (4 nibble bytes, or the 3 bytes of a 24-bit word at
@@ -584,6 +641,19 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
           const uint2 e2 = ptab6[(cb[kb] >> 12) & 63u], e3 = ptab6[(cb[kb] >> 18) & 63u];
           ka[kb] = u32x4{e0.x, e0.y, e1.x, e1.y};
           kb2[kb] = u32x4{e2.x, e2.y, e3.x, e3.y};
+        } else if (WIDE && kwide[kb]) {
+          // one code per byte: [hi, lo] words paired by permutes into [hi pair, lo pair]
+          const uint32_t* wt = wtab[kgrp[kb]];
+          uint32_t e[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = wt[(cb[kb] >> (8 * i)) & 255u];
+            e[4 + i] = wt[(cb2[kb] >> (8 * i)) & 255u];
+          }
+          ka[kb] = u32x4{__builtin_amdgcn_perm(e[1], e[0], 0x05040100u), __builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                         __builtin_amdgcn_perm(e[3], e[2], 0x05040100u), __builtin_amdgcn_perm(e[3], e[2], 0x07060302u)};
+          kb2[kb] = u32x4{__builtin_amdgcn_perm(e[5], e[4], 0x05040100u), __builtin_amdgcn_perm(e[5], e[4], 0x07060302u),
+                          __builtin_amdgcn_perm(e[7], e[6], 0x05040100u), __builtin_amdgcn_perm(e[7], e[6], 0x07060302u)};
         } else {
           const uint2 e0 = ptab[kb][cb[kb] & 255u], e1 = ptab[kb][(cb[kb] >> 8) & 255u];
           const uint2 e2 = ptab[kb][(cb[kb] >> 16) & 255u], e3 = ptab[kb][cb[kb] >> 24];
@@ -729,6 +799,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 hipError_t launch_gtq_quantize(const GtqQuantArgs& a, bool x_f16, int batch, hipStream_t stream) {
   const dim3 grid((a.n_new + kQuantTokens - 1) / kQuantTokens, a.n_kv_heads, batch), block(256);
   if ((a.code_bits != 0) != (a.signs != nullptr) || a.code_bits < 0 || a.code_bits > 3) return hipErrorInvalidValue;
+  if (a.code_bits == 0 && (a.code_bytes < 64 || a.code_bytes > 128 || a.code_bytes % 16)) return hipErrorInvalidValue;
 #define TQ_GQ(PK)                                                                                            \
   if (a.code_bits == PK) {                                                                                   \
     if (x_f16) hipLaunchKernelGGL((gtq_quantize_kernel<true, PK != 0, PK>), grid, block, 0, stream, a);      \
@@ -744,12 +815,14 @@ hipError_t launch_gtq_attention(const GtqAttnArgs& a, bool q_f16, hipStream_t st
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(64 * NW);
   if (a.heads_per_slice > 8) return hipErrorInvalidValue;
   if ((a.code_bits != 0) != (a.signs != nullptr) || a.code_bits < 0 || a.code_bits > 3) return hipErrorInvalidValue;
-#define TQ_GA(PK)                                                                                                 \
-  if (a.code_bits == PK) {                                                                                        \
-    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, PK != 0, PK>), grid, block, 0, stream, a);   \
-    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, PK != 0, PK>), grid, block, 0, stream, a);        \
+  const bool wide = a.code_bits == 0 && a.code_bytes > 64;
+  if (a.code_bits == 0 && (a.code_bytes < 64 || a.code_bytes > 128 || a.code_bytes % 16)) return hipErrorInvalidValue;
+#define TQ_GA(PK, W)                                                                                                 \
+  if (a.code_bits == PK && wide == W) {                                                                              \
+    if (q_f16) hipLaunchKernelGGL((gtq_attention_kernel<NW, D, true, PK != 0, PK, W>), grid, block, 0, stream, a);   \
+    else hipLaunchKernelGGL((gtq_attention_kernel<NW, D, false, PK != 0, PK, W>), grid, block, 0, stream, a);        \
   }
-  TQ_GA(0) TQ_GA(1) TQ_GA(2) TQ_GA(3)
+  TQ_GA(0, false) TQ_GA(0, true) TQ_GA(1, false) TQ_GA(2, false) TQ_GA(3, false)
 #undef TQ_GA
   return hipGetLastError();
 }

@@ -137,7 +137,7 @@ struct GtqQuantArgs {
   const void* heads;        // tq_gtq_head [n_kv_heads]
   const float* rotations;   // [n_kv_heads][16384]
   const void* x;            // [batch][n_kv_heads][n_new][128]
-  uint8_t* codes;           // [batch][n_kv_heads][capacity][64, or 16 code_bits]
+  uint8_t* codes;           // [batch][n_kv_heads][capacity][code_bytes, or 16 code_bits]
   float* norms;             // [batch][n_kv_heads][capacity][4]
   int32_t n_kv_heads;
   int32_t n_new;
@@ -145,8 +145,9 @@ struct GtqQuantArgs {
   int32_t capacity;
   const float* proj;        // two-stage keys: [n_kv_heads][128][128], (S Q)^T; else NULL
   uint8_t* signs;           // two-stage keys: [batch][n_kv_heads][capacity][16]; else NULL
-  int32_t code_bits;        // 0: Block-GTQ nibbles, codes [..][64]; 1-3: two-stage keys' first
-                            // stage bit-packed at that width, codes [..][16 code_bits]
+  int32_t code_bits;        // 0: Block-GTQ records, codes [..][code_bytes]; 1-3: two-stage keys'
+                            // first stage bit-packed at that width, codes [..][16 code_bits]
+  int32_t code_bytes;       // Block-GTQ record code bytes: 64 .. 128, a multiple of 16
 };
 
 struct GtqAttnArgs {
@@ -187,8 +188,9 @@ struct GtqAttnArgs {
   const float* proj;
   const uint8_t* signs;
   uint8_t* w_signs;         // writable, for the fused append of two-stage keys
-  int32_t code_bits;        // 0: Block-GTQ nibbles, codes [..][64]; 1-3: two-stage keys' first
-                            // stage bit-packed at that width, codes [..][16 code_bits]
+  int32_t code_bits;        // 0: Block-GTQ records, codes [..][code_bytes]; 1-3: two-stage keys'
+                            // first stage bit-packed at that width, codes [..][16 code_bits]
+  int32_t code_bytes;       // Block-GTQ record code bytes: 64 .. 128, a multiple of 16
 };
 
 struct MergeArgs {

@@ -342,7 +342,8 @@ tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const 
  * block energy score, greedy allocation, grouping and packed-cache paragraphs).
  *
  * A head's 128 key coordinates form 64 RoPE blocks, block i = coordinates (2i, 2i+1).  Each
- * block gets an integer width b_i in [b_min, b_max] (1 <= b_min <= b_max <= 4) with
+ * block gets an integer width b_i in [b_min, b_max] (1 <= b_min <= b_max <= 8, at most four
+ * distinct widths per head: b_max - b_min <= 3 guarantees it) with
  * sum b_i = budget, greedily by the marginal gain (3/4) s_i 4^-b_i of the objective
  * sum s_i 4^-b_i, s_i the block's energy.  Blocks of equal width form one group, encoded by
  * one TQ-MSE encoder: the group's coordinates (its blocks' pairs in block order, n = 2 x
@@ -350,12 +351,17 @@ tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_meta, const 
  * by compare-count against the width's Lloyd-Max boundaries for n dimensions.  Values are
  * kept in fp16, the configuration of the page's main benchmark (keys only).
  *
- * Key record of one (token, KV head): codes[64] bytes, one 4-bit code per position of the
- * group order (groups by width ascending, each in its rotated coordinate order), position j
- * in byte j/2, the low nibble for even j; norms[4] fp32, one per group (0 for absent
- * groups). */
+ * Key record of one (token, KV head): code_bytes bytes of codes in group order (groups by
+ * width ascending, each in its rotated coordinate order).  Groups of width <= 4 take nibble
+ * containers, groups of width 5 .. 8 byte containers ("RoPE-Aware Bit Allocation ...",
+ * packed-cache implementation details): the P positions of nibble groups first, position j
+ * in byte j/2 (low nibble for even j), then one byte per position of the byte groups from
+ * byte P/2, then zero padding.  code_bytes is one value for a whole cache: 64 when no head
+ * has a group wider than 4 bits, else at least every head's tq_gtq_head.code_bytes (a
+ * multiple of 16, at most 128).  Then norms[4] fp32, one per group (0 for absent groups). */
 #define TQ_GTQ_BLOCKS 64
 #define TQ_GTQ_MAX_GROUPS 4
+#define TQ_GTQ_MAX_WIDTH 8
 #define TQ_GTQ_ROTATION_FLOATS 16384 /* per head: every group's n x n rotation */
 
 /* Block energies from a calibration prefix (host): energies[h][i] = 1/2 (mean over tokens
@@ -385,19 +391,26 @@ typedef struct {
   int32_t dim[TQ_GTQ_MAX_GROUPS];   /* coordinates of group g (0 if absent) */
   int32_t rot_offset[TQ_GTQ_MAX_GROUPS]; /* group g's rotation in the head's rotation array */
   int32_t coord[128];               /* original coordinate of group-order position j */
-  float centroid[TQ_GTQ_MAX_GROUPS][16];
-  float boundary[TQ_GTQ_MAX_GROUPS][15];
+  int32_t byte_at[TQ_GTQ_MAX_GROUPS];  /* record byte of group g's first code */
+  int32_t code_used;                /* code bytes the layout fills: P/2 + (128 - P) */
+  int32_t code_bytes;               /* code_used rounded up to 16; 64 without byte groups */
+  float centroid[TQ_GTQ_MAX_GROUPS][256];  /* 2^width levels each */
+  float boundary[TQ_GTQ_MAX_GROUPS][255];
   float f16_scale[TQ_GTQ_MAX_GROUPS];  /* the codebook's tq_codebook.f16_scale: the matrix-core
                                           decode holds fp16(s c) and divides the query by s */
 } tq_gtq_head;
 
-/* Builds one head's encoder on the host from its 64 block widths (1 .. 4) and a Gaussian
- * matrix per width (gauss: float [4][128][128], width w uses gauss[w-1]).  Group g's
- * rotation Q is the orthogonal factor, with positive diagonal of R, of the leading n x n
- * part of its width's matrix (QR by Gram-Schmidt in double): a uniformly random rotation.
- * rotation: float [16384] (host), group g's Q row-major at rot_offset[g] (Q[i][j] =
- * rotation[rot_offset + i*n + j]; y_j = sum_i Q[i][j] u_i).  Codebooks are
- * tq_make_codebook(width, n).  Errors: TQ_EINVAL for null pointers or widths outside 1..4. */
+/* Builds one head's encoder on the host from its 64 block widths (1 .. 8) and a Gaussian
+ * matrix per width (gauss: float [max width][128][128], width w uses gauss[w-1]; only the
+ * widths present are read).  Group g's rotation Q is the orthogonal factor, with positive
+ * diagonal of R, of the leading n x n part of its width's matrix (QR by Gram-Schmidt in
+ * double): a uniformly random rotation.  rotation: float [16384] (host), group g's Q
+ * row-major at rot_offset[g] (Q[i][j] = rotation[rot_offset + i*n + j]; y_j = sum_i Q[i][j]
+ * u_i).  Codebooks are tq_make_codebook(width, n) up to 4 bits; at 5 .. 8 bits the same
+ * Lloyd-Max conditions ("TurboQuant ... MNN on phones", 2.3) solved by Newton's method.
+ * Sets the record layout (byte_at, code_used, code_bytes; see the key record above).
+ * Errors: TQ_EINVAL for null pointers or widths outside 1..8; TQ_EUNSUPPORTED for more than
+ * four distinct widths. */
 tq_status tq_gtq_prepare(const int32_t* block_bits, const float* gauss, tq_gtq_head* head, float* rotation);
 
 /* Two-stage keys ("TurboQuant ... MNN on phones", 2.4 and 3.2: (b-1)-bit MSE plus a
@@ -418,18 +431,22 @@ tq_status tq_gtq_qjl_projection(const tq_gtq_head* head, const float* rotation, 
 /* Encodes n_new keys per (sequence, KV head) into token positions pos0 .. pos0+n_new-1.
  *   heads:     device tq_gtq_head [n_kv_heads]; rotations: device float [n_kv_heads][16384].
  *   x:         device [batch][n_kv_heads][n_new][128] of x_dtype (TQ_F32 or TQ_F16).
- *   codes:     device uint8 [batch][n_kv_heads][capacity][64]; norms: device float
- *              [batch][n_kv_heads][capacity][4].
- * Errors: TQ_EINVAL for null pointers, bad dtype or counts; TQ_ECAPACITY when
+ *   code_bytes: the record's code bytes (64, 80, 96, 112 or 128), the same for every head
+ *              and at least each head's tq_gtq_head.code_bytes; a smaller value gives
+ *              wrong codes for a head with byte groups but no access outside the record.
+ *   codes:     device uint8 [batch][n_kv_heads][capacity][code_bytes] (padding written as
+ *              zeros); norms: device float [batch][n_kv_heads][capacity][4].
+ * Errors: TQ_EINVAL for null pointers, bad dtype, counts or code_bytes; TQ_ECAPACITY when
  * pos0 + n_new > capacity.  n_new == 0 is a no-op. */
 tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x, tq_dtype x_dtype,
                                int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0, int32_t capacity,
-                               uint8_t* codes, float* norms, void* stream);
+                               int32_t code_bytes, uint8_t* codes, float* norms, void* stream);
 
 /* Decode attention over Block-GTQ keys and fp16 values: out = softmax(scale q K^T) V with
  * every key decoded from its codes, group norms and the rotated query (q~_g = Q_g^T q_g,
  * so q . k = sum_g norm_g sum_j q~_j c_g[code_j]).
- *   codes, norms: as tq_gtq_quantize_keys; v: device fp16 [batch][n_kv_heads][capacity][128].
+ *   code_bytes, codes, norms: as tq_gtq_quantize_keys; v: device fp16
+ *      [batch][n_kv_heads][capacity][128].
  *   q: device [batch][n_q_heads][128] of q_dtype (TQ_F32 or TQ_F16); n_q_heads a multiple
  *      of n_kv_heads, query head h reads KV head h / (n_q_heads / n_kv_heads).
  *   seq_lens: device int32 [batch] (each clamped to [0, max_len]) or NULL (all max_len);
@@ -440,9 +457,12 @@ tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations,
  *   part_o, part_lse: n_splits > 1: original-domain section partials for tq_merge_splits
  *      with rot == NULL.
  * Scores and weighted sums are fp16 matrix products of hi + lo parts (key levels, query,
- * weights) with fp32 accumulation.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts
- * or scale; TQ_ECAPACITY for max_len > capacity or capacity > 2^24. */
-tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, const uint8_t* codes, const float* norms,
+ * weights) with fp32 accumulation; nibble codes are decoded two at a time through pair
+ * tables, byte codes one at a time through a 256-entry table per group.  Errors: TQ_EINVAL
+ * for null pointers, bad dtypes, counts, scale or code_bytes; TQ_ECAPACITY for max_len >
+ * capacity or capacity > 2^24. */
+tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes, const uint8_t* codes,
+                           const float* norms,
                            const void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,
                            tq_dtype q_dtype, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
                            int32_t n_splits, float* out, float* lse_out, float* part_o, float* part_lse, void* stream);
@@ -499,7 +519,8 @@ tq_status tq_gtq_qjl_attention(const tq_gtq_head* heads, const float* rotations,
  * Other arguments as tq_gtq_attention.  Errors: those of tq_gtq_attention; TQ_EINVAL for
  * null k_new or v_new, a bad x_dtype or a negative pos0 or max_pos; TQ_ECAPACITY when
  * max_pos + 1 (pos0 + 1) > capacity.  Nothing is written when a check fails. */
-tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, uint8_t* codes, float* norms,
+tq_status tq_gtq_append_attention(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes, uint8_t* codes,
+                                  float* norms,
                                   void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* k_new,
                                   const void* v_new, tq_dtype x_dtype, const int32_t* pos, int32_t pos0,
                                   int32_t max_pos, const void* q, tq_dtype q_dtype, int32_t n_q_heads, float scale,

@@ -344,24 +344,58 @@ def test_gtq_prepare_matches_oracle(lib):
             assert np.allclose([head.centroid[g][k] for k in range(2 ** w)], c, rtol=2e-6, atol=1e-7)
             assert np.allclose([head.boundary[g][k] for k in range(2 ** w - 1)], m, rtol=2e-6, atol=1e-7)
         assert all(head.start[g] == 128 for g in range(head.n_groups, 4))
-    assert lib.tq_gtq_prepare(np.full(64, 5, np.int32).ctypes.data, gauss.ctypes.data, ctypes.byref(head),
+    assert head.code_bytes == 64 and head.code_used == 64
+    assert lib.tq_gtq_prepare(np.full(64, 9, np.int32).ctypes.data, gauss.ctypes.data, ctypes.byref(head),
                               rot.ctypes.data) == TQ_EINVAL
+    five = np.array([1, 2, 3, 4, 5] * 12 + [1] * 4, np.int32)  # five distinct widths
+    assert lib.tq_gtq_prepare(five.ctypes.data, np.zeros((5, 128, 128), np.float32).ctypes.data,
+                              ctypes.byref(head), rot.ctypes.data) == TQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("widths", [(3, 5, 6), (2, 4, 7, 8), (5,), (8,)])
+def test_gtq_prepare_byte_containers_match_oracle(lib, widths):
+    # widths 5-8: host codebooks (Newton's method in C++) against the oracle's; the record
+    # layout against the oracle's nibble/byte split
+    from oracle import blockgtq as bg
+    rng = np.random.default_rng(sum(widths))
+    bits = np.array([widths[i % len(widths)] for i in range(64)], np.int32)
+    rng.shuffle(bits)
+    gauss = rng.standard_normal((8, 128, 128)).astype(np.float32)
+    head = tq.GtqHead()
+    rot = np.zeros(tq.GTQ_ROTATION_FLOATS, dtype=np.float32)
+    assert lib.tq_gtq_prepare(bits.ctypes.data, gauss.ctypes.data, ctypes.byref(head), rot.ctypes.data) == TQ_OK
+    enc = bg.head_encoders(bits, gauss.astype(np.float64))
+    assert head.n_groups == len(enc)
+    p = bg.nibble_positions(enc)
+    assert head.code_bytes == bg.code_bytes(enc) and head.code_used == p // 2 + 128 - p
+    for g, (w, coords, qm, c, m) in enumerate(enc):
+        n = len(coords)
+        assert head.width[g] == w and head.dim[g] == n
+        assert head.byte_at[g] == (head.start[g] // 2 if w <= 4 else p // 2 + head.start[g] - p)
+        cg = np.array([head.centroid[g][k] for k in range(2 ** w)])
+        mg = np.array([head.boundary[g][k] for k in range(2 ** w - 1)])
+        # within a few fp32 ulps of the fp64 oracle
+        assert np.allclose(cg, c, rtol=4e-7, atol=2e-8), (w, n, np.max(np.abs(cg - c)))
+        assert np.allclose(mg, m, rtol=4e-7, atol=2e-8), (w, n)
+        assert np.all(np.diff(cg) > 0) and np.array_equal(cg, -cg[::-1])
 
 
 def test_gtq_call_validation(lib):
     qk = lib.tq_gtq_quantize_keys
-    assert qk(None, FAKE, FAKE, 1, 1, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL
-    assert qk(FAKE, FAKE, FAKE, 2, 1, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL   # bf16 keys
-    assert qk(FAKE, FAKE, FAKE, 1, 0, 1, 4, 0, 32, FAKE, FAKE, None) == TQ_EINVAL
-    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 4, 30, 32, FAKE, FAKE, None) == TQ_ECAPACITY
-    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, 32, FAKE, FAKE, None) == TQ_OK          # nothing launched
+    assert qk(None, FAKE, FAKE, 1, 1, 1, 4, 0, 32, 64, FAKE, FAKE, None) == TQ_EINVAL
+    assert qk(FAKE, FAKE, FAKE, 2, 1, 1, 4, 0, 32, 64, FAKE, FAKE, None) == TQ_EINVAL   # bf16 keys
+    assert qk(FAKE, FAKE, FAKE, 1, 0, 1, 4, 0, 32, 64, FAKE, FAKE, None) == TQ_EINVAL
+    for bad in (0, 48, 72, 144):  # record code bytes: 64 .. 128 in steps of 16
+        assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 4, 0, 32, bad, FAKE, FAKE, None) == TQ_EINVAL, bad
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 4, 30, 32, 64, FAKE, FAKE, None) == TQ_ECAPACITY
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, 32, 80, FAKE, FAKE, None) == TQ_OK          # nothing launched
     at = lib.tq_gtq_attention
 
     def call(**kw):
-        a = dict(heads=FAKE, rot=FAKE, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, q=FAKE, qd=1, hq=8,
-                 max_len=64, scale=0.1, splits=1, out=FAKE, part=FAKE)
+        a = dict(heads=FAKE, rot=FAKE, cb=64, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, q=FAKE, qd=1,
+                 hq=8, max_len=64, scale=0.1, splits=1, out=FAKE, part=FAKE)
         a.update(kw)
-        return at(a["heads"], a["rot"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["q"],
+        return at(a["heads"], a["rot"], a["cb"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["q"],
                   a["qd"], a["hq"], None, a["max_len"], a["scale"], a["splits"], a["out"], None, a["part"], a["part"],
                   None)
     for k in ("heads", "rot", "codes", "norms", "v", "q"):
@@ -372,6 +406,7 @@ def test_gtq_call_validation(lib):
     assert call(out=None) == TQ_EINVAL
     assert call(splits=3, part=None) == TQ_EINVAL
     assert call(scale=float("nan")) == TQ_EINVAL
+    assert call(cb=0) == TQ_EINVAL and call(cb=136) == TQ_EINVAL and call(cb=100) == TQ_EINVAL
     assert call(max_len=65) == TQ_ECAPACITY
 
 
@@ -379,10 +414,11 @@ def test_gtq_append_call_validation(lib):
     ap = lib.tq_gtq_append_attention
 
     def call(**kw):
-        a = dict(heads=FAKE, rot=FAKE, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, kn=FAKE, vn=FAKE, xd=1,
-                 pos=None, pos0=10, max_pos=0, q=FAKE, qd=1, hq=8, scale=0.1, splits=1, out=FAKE, part=FAKE)
+        a = dict(heads=FAKE, rot=FAKE, cb=64, codes=FAKE, norms=FAKE, v=FAKE, cap=64, batch=1, hkv=2, kn=FAKE,
+                 vn=FAKE, xd=1, pos=None, pos0=10, max_pos=0, q=FAKE, qd=1, hq=8, scale=0.1, splits=1, out=FAKE,
+                 part=FAKE)
         a.update(kw)
-        return ap(a["heads"], a["rot"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["kn"],
+        return ap(a["heads"], a["rot"], a["cb"], a["codes"], a["norms"], a["v"], a["cap"], a["batch"], a["hkv"], a["kn"],
                   a["vn"], a["xd"], a["pos"], a["pos0"], a["max_pos"], a["q"], a["qd"], a["hq"], a["scale"],
                   a["splits"], a["out"], None, a["part"], a["part"], None)
     for k in ("heads", "rot", "codes", "norms", "v", "q", "kn", "vn"):
@@ -393,6 +429,7 @@ def test_gtq_append_call_validation(lib):
     assert call(pos=FAKE, max_pos=-1) == TQ_EINVAL
     assert call(hq=7) == TQ_EINVAL
     assert call(splits=3, part=None) == TQ_EINVAL
+    assert call(cb=32) == TQ_EINVAL
     assert call(pos0=64) == TQ_ECAPACITY       # the new slot past the capacity
     assert call(pos=FAKE, max_pos=64) == TQ_ECAPACITY
 

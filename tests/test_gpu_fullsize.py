@@ -128,7 +128,7 @@ def test_gtq32k_step():
     energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
     bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
     keys = tq.GtqKeys(bits, inp["gauss"])
-    codes = torch.zeros((w.batch, w.n_kv_heads, T, 64), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device="cuda")
     norms = torch.zeros((w.batch, w.n_kv_heads, T, 4), dtype=torch.float32, device="cuda")
     kx = torch.from_numpy(inp["k"]).cuda()
     v = torch.from_numpy(inp["v"]).cuda()

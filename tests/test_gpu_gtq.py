@@ -6,7 +6,9 @@ fp64: their rotated values differ by about 1e-7), at most 1e-4 of all coordinate
 within 1e-6 relative.  Attention is fed the oracle's codes and norms and compared with fp64
 attention on the oracle's dequantised keys and the fp16 values: within 1e-4 relative per
 row (fp32 sums of fp16 hi + lo operands), lse within 1e-4 + 1e-5 |lse|.  Rows are ragged, with an empty
-one; sections 1, 3 and 40; query groups of 4, 8 and 16 heads (two slices).
+one; sections 1, 3 and 40; query groups of 4, 8 and 16 heads (two slices).  Widths 1-4 (nibble
+records of 64 bytes), 2-5 (80-byte records with a byte group) and 5-8 (128-byte records, byte
+groups only).
 """
 
 from dataclasses import replace
@@ -37,14 +39,35 @@ def gpu():
     tq.library()
 
 
-def case(hq=32, hkv=8, lens=LENS, cap=320, seed=0):
+# (b_min, b_max, budget): nibble records; one byte group (80-byte records); byte groups only
+RANGES = [(1, 4, 192), (2, 5, 192), (5, 8, 384)]
+
+
+def case(hq=32, hkv=8, lens=LENS, cap=320, seed=0, widths=RANGES[0]):
     w = replace(workloads.WORKLOADS["gtq32k"], batch=len(lens), n_q_heads=hq, n_kv_heads=hkv, seq_len=cap)
     inp = workloads.generate(w, seed)
     s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
-    bits = np.stack([bg.allocate(s[h].astype(np.float64), 3 * 64, 1, 4) for h in range(hkv)])
+    lo, hi, budget = widths
+    bits = np.stack([bg.allocate(s[h].astype(np.float64), budget, lo, hi) for h in range(hkv)])
     enc = [bg.head_encoders(bits[h], inp["gauss"][h].astype(np.float64)) for h in range(hkv)]
-    print("gtq case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, flush=True)
+    print("gtq case", (len(lens), hq, hkv, cap), "lens", lens, "seed", seed, "widths", widths, flush=True)
     return w, inp, bits, enc
+
+
+def pack_records(oc, enc, cb):
+    """The oracle's codes [b, kv, T, 128] as records of cb bytes, each head in its layout."""
+    out = np.zeros(oc.shape[:3] + (cb,), np.uint8)
+    for h in range(oc.shape[1]):
+        out[:, h] = bg.pack_codes(oc[:, h].reshape(-1, 128), enc[h], record_bytes=cb).reshape(oc.shape[0], -1, cb)
+    return out
+
+
+def unpack_records(codes, enc):
+    c = codes.cpu().numpy() if hasattr(codes, "cpu") else codes
+    out = np.zeros(c.shape[:3] + (128,), np.uint8)
+    for h in range(c.shape[1]):
+        out[:, h] = bg.unpack_codes(c[:, h].reshape(-1, c.shape[3]), enc[h]).reshape(c.shape[0], -1, 128)
+    return out
 
 
 def oracle_keys(w, inp, enc):
@@ -60,10 +83,13 @@ def oracle_keys(w, inp, enc):
     return codes, norms, ys
 
 
-def test_encoding_matches_oracle():
-    w, inp, bits, enc = case()
+@pytest.mark.parametrize("widths", RANGES)
+def test_encoding_matches_oracle(widths):
+    w, inp, bits, enc = case(widths=widths)
     keys = tq.GtqKeys(bits, inp["gauss"])
-    codes = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 64), dtype=torch.uint8, device="cuda")
+    cb = keys.code_bytes
+    assert cb == max(bg.code_bytes(e) for e in enc) and (cb > 64) == (widths[1] > 4)
+    codes = torch.full((w.batch, w.n_kv_heads, w.seq_len, cb), 0xA5, dtype=torch.uint8, device="cuda")
     norms = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 4), dtype=torch.float32, device="cuda")
     x = torch.from_numpy(inp["k"]).cuda()
     # two calls: the first 100 tokens, then the rest at position 100
@@ -71,7 +97,10 @@ def test_encoding_matches_oracle():
     tq.gtq_quantize_keys(keys, x[:, :, 100:].contiguous(), codes, norms, pos0=100)
     torch.cuda.synchronize()
     oc, on, oy = oracle_keys(w, inp, enc)
-    got = bg.unpack_codes(codes.cpu().numpy().reshape(-1, 64)).reshape(oc.shape)
+    raw = codes.cpu().numpy()
+    for h in range(w.n_kv_heads):  # padding past the head's layout is written as zeros
+        assert not raw[:, h, :, enc_used(enc[h]):].any()
+    got = unpack_records(raw, enc)
     bad = got != oc
     frac = bad.mean()
     assert frac <= 1e-4, frac
@@ -83,8 +112,13 @@ def test_encoding_matches_oracle():
     assert np.allclose(norms.cpu().numpy(), on, rtol=1e-6, atol=1e-30)
 
 
-def device_inputs(w, inp, oc, on):
-    codes = torch.from_numpy(bg.pack_codes(oc.reshape(-1, 128)).reshape(oc.shape[:3] + (64,))).cuda()
+def enc_used(e):
+    p = bg.nibble_positions(e)
+    return p // 2 + 128 - p
+
+
+def device_inputs(w, inp, oc, on, enc, cb=64):
+    codes = torch.from_numpy(pack_records(oc, enc, cb)).cuda()
     norms = torch.from_numpy(on).cuda()
     v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
     q = torch.from_numpy(inp["q"].astype(np.float16)).cuda()
@@ -113,12 +147,13 @@ def check(out, lse, ro, rl, lens):
     assert worst <= RTOL and worst_lse <= LSE_ATOL + LSE_RTOL * float(np.max(np.abs(rl[np.isfinite(rl)])))
 
 
-@pytest.mark.parametrize("n_splits", [1, 3, 40])
-def test_attention_matches_oracle(n_splits):
-    w, inp, bits, enc = case()
+@pytest.mark.parametrize("n_splits,widths", [(1, RANGES[0]), (3, RANGES[0]), (40, RANGES[0]), (1, RANGES[1]),
+                                             (3, RANGES[2])])
+def test_attention_matches_oracle(n_splits, widths):
+    w, inp, bits, enc = case(widths=widths)
     keys = tq.GtqKeys(bits, inp["gauss"])
     oc, on, _ = oracle_keys(w, inp, enc)
-    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    codes, norms, v, q = device_inputs(w, inp, oc, on, enc, keys.code_bytes)
     seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
     res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale, n_splits=n_splits)
     if n_splits > 1:
@@ -134,7 +169,7 @@ def test_head_groupings(hq, hkv):
     w, inp, bits, enc = case(hq=hq, hkv=hkv, lens=lens)
     keys = tq.GtqKeys(bits, inp["gauss"])
     oc, on, _ = oracle_keys(w, inp, enc)
-    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    codes, norms, v, q = device_inputs(w, inp, oc, on, enc, keys.code_bytes)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out, lse = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(lens), scale=w.scale)
     torch.cuda.synchronize()
@@ -146,7 +181,7 @@ def test_sections_are_the_oracle_splits():
     w, inp, bits, enc = case()
     keys = tq.GtqKeys(bits, inp["gauss"])
     oc, on, _ = oracle_keys(w, inp, enc)
-    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    codes, norms, v, q = device_inputs(w, inp, oc, on, enc, keys.code_bytes)
     seq = torch.tensor(LENS, dtype=torch.int32, device="cuda")
     po, pl = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(LENS), scale=w.scale, n_splits=3)
     torch.cuda.synchronize()
@@ -182,7 +217,7 @@ def test_allocation_shapes():
     keys = tq.GtqKeys(bits, inp["gauss"])
     assert [keys.n_groups(h) for h in range(4)] == [1, 2, 4, 3]
     oc, on, _ = oracle_keys(w, inp, enc)
-    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    codes, norms, v, q = device_inputs(w, inp, oc, on, enc, keys.code_bytes)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     for n_splits in (1, 3):
         res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=max(lens), scale=w.scale,
@@ -195,7 +230,7 @@ def test_allocation_shapes():
 
 
 def device_cache(w, inp, keys):
-    codes = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 64), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, keys.code_bytes), dtype=torch.uint8, device="cuda")
     norms = torch.zeros((w.batch, w.n_kv_heads, w.seq_len, 4), dtype=torch.float32, device="cuda")
     tq.gtq_quantize_keys(keys, torch.from_numpy(inp["k"]).cuda(), codes, norms, pos0=0)
     v = torch.from_numpy(inp["v"].astype(np.float16)).cuda()
@@ -206,12 +241,12 @@ def same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("n_splits", [1, 3])
-def test_append_step_equals_encode_then_attend(n_splits):
+@pytest.mark.parametrize("n_splits,widths", [(1, RANGES[0]), (3, RANGES[0]), (3, RANGES[1]), (1, RANGES[2])])
+def test_append_step_equals_encode_then_attend(n_splits, widths):
     # one launch (encode the new key and write its value at slot P, then attend over P + 1
     # tokens) against the two calls it stands for: bit for bit, cache and outputs
     lens = [320, 320, 320]
-    w, inp, bits, enc = case(lens=lens)
+    w, inp, bits, enc = case(lens=lens, widths=widths)
     keys = tq.GtqKeys(bits, inp["gauss"])
     P = 250
     rng = np.random.default_rng(7)
@@ -252,7 +287,7 @@ def test_append_step_per_row_slots():
     torch.cuda.synchronize()
     assert same(a, b)
     assert same(res_a, res_b)
-    codes = bg.unpack_codes(a[0].cpu().numpy().reshape(-1, 64)).reshape(4, w.n_kv_heads, w.seq_len, 128)
+    codes = unpack_records(a[0], enc)
     norms = a[1].cpu().numpy()
     for r, p in enumerate(pos):
         for h in range(w.n_kv_heads):
@@ -273,7 +308,7 @@ def test_capacity_off_the_tile_grid():
     w, inp, bits, enc = case(lens=lens, cap=301)
     keys = tq.GtqKeys(bits, inp["gauss"])
     oc, on, _ = oracle_keys(w, inp, enc)
-    codes, norms, v, q = device_inputs(w, inp, oc, on)
+    codes, norms, v, q = device_inputs(w, inp, oc, on, enc, keys.code_bytes)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     for n_splits in (1, 4):
         res = tq.gtq_attention(keys, codes, norms, v, q, seq_lens=seq, max_len=301, scale=w.scale, n_splits=n_splits)
