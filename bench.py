@@ -563,7 +563,7 @@ def gtq_setup(w, inp, dev):
         k_new, v_new = x[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous()
         return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1), signs
     energies = tq.gtq_block_energies(inp["q_cal"], inp["k_cal"])
-    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, 1, 4) for h in range(w.n_kv_heads)])
+    bits = np.stack([tq.gtq_allocate(energies[h], w.bits_k * 64, *GTQ_RANGE) for h in range(w.n_kv_heads)])
     keys = tq.GtqKeys(bits, inp["gauss"], device=dev)
     codes = torch.zeros((w.batch, w.n_kv_heads, T, keys.code_bytes), dtype=torch.uint8, device=dev)
     prompt = x[:, :, :T - 1].contiguous()
@@ -580,7 +580,13 @@ def gtq_setup(w, inp, dev):
     return keys, bits, codes, norms, v, q, k_new, v_new, e0.elapsed_time(e1), None
 
 
-GTQ_BYTES_PER_TOKEN_HEAD = 64 + 16 + 256  # key codes, the four group norms, fp16 values
+# Block-GTQ widths [b_min, b_max] of the allocation (--gtq-widths); above 4 bits the
+# high-bit groups take byte containers and the records grow past 64 bytes
+GTQ_RANGE = (1, 4)
+
+
+def gtq_bytes_per_token_head(code_bytes):
+    return code_bytes + 16 + 256  # key codes, the four group norms, fp16 values
 # two-stage keys: first-stage codes (b - 1 bits per coordinate, bit-packed), the norm
 # slots, the residual's 128 sign bits, fp16 values
 def qjl_bytes_per_token_head(w):
@@ -701,7 +707,7 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
                 parity = max(parity, float(row_rel_err(o[b, h], ref)))
         s = None if qjl else bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
         for b, kv in [] if qjl else [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]:
-            enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, 1, 4),
+            enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, *GTQ_RANGE),
                                    inp["gauss"][kv].astype(np.float64))
             c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)
             kd = bg.dequantize_keys(c, nrm, enc)
@@ -711,9 +717,10 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
                 parity = max(parity, float(row_rel_err(o[b, h], ref)))
         if parity > OUT_RTOL:
             raise SystemExit("parity check failed: %.3e > %.1e" % (parity, OUT_RTOL))
-    algo = w.batch * w.n_kv_heads * w.seq_len * (qjl_bytes_per_token_head(w) if qjl else GTQ_BYTES_PER_TOKEN_HEAD)
+    algo = w.batch * w.n_kv_heads * w.seq_len * (qjl_bytes_per_token_head(w) if qjl else
+                                                 gtq_bytes_per_token_head(keys.code_bytes))
     return dict(step_ms=step_ms, attn_ms=att_ms, algo_bytes=algo, reps=reps, parity=parity, encode_ms=enc_ms,
-                widths=np.bincount(bits.ravel(), minlength=5)[1:].tolist())
+                widths=np.bincount(bits.ravel(), minlength=9)[1:].tolist(), code_bytes=keys.code_bytes)
 
 
 GTQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gtq_traffic.json")
@@ -790,7 +797,7 @@ def _oracle_gtq_unit(args):
     from oracle import attention, blockgtq as bg
     inp = _oracle_unit.inp
     s = bg.block_energies(inp["q_cal"], inp["k_cal"]).astype(np.float32)
-    enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, 1, 4),
+    enc = bg.head_encoders(bg.allocate(s[kv].astype(np.float64), w.bits_k * 64, *GTQ_RANGE),
                            inp["gauss"][kv].astype(np.float64))
     c, nrm, _ = bg.quantize_keys(inp["k"][b, kv].astype(np.float64), enc)  # the stored cache (not timed)
     t0 = time.perf_counter()
@@ -1231,6 +1238,8 @@ def main():
     ap.add_argument("--commands", default="", help="the profiling commands, recorded with --write-traffic")
     ap.add_argument("--schedule-sweep", action="store_true",
                     help="print the decode launch time of both schedules over T and heads per KV head, then exit")
+    ap.add_argument("--gtq-widths", default="1,4", metavar="LO,HI",
+                    help="Block-GTQ allocation range [b_min, b_max]; above 4 bits groups take byte containers")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline configuration (the others are timed after it by default)")
     args = ap.parse_args()
@@ -1239,6 +1248,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    global GTQ_RANGE
+    GTQ_RANGE = tuple(int(x) for x in args.gtq_widths.split(","))
+    if len(GTQ_RANGE) != 2 or not 1 <= GTQ_RANGE[0] <= GTQ_RANGE[1] <= 8 or GTQ_RANGE[1] - GTQ_RANGE[0] > 3:
+        raise SystemExit("--gtq-widths LO,HI with 1 <= LO <= HI <= 8 and at most four widths")
     if args.schedule_sweep:
         schedule_sweep()
         return
@@ -1282,27 +1295,30 @@ def main():
         achieved = r["algo_bytes"] / (r["attn_ms"] / 1e3) / 1e9
         probe = stream_read_probe_gbs()
         log("step %.3f ms, attention kernel %.3f ms -> %.0f GB/s (%.1f%% of 8 TB/s, %.1f%% of the %.0f GB/s probe); "
-            "widths 1-4 bits: %s blocks; key encoding %.3f ms" % (
+            "blocks at widths 1-8 bits: %s; %d code bytes per key; key encoding %.3f ms" % (
                 r["step_ms"], r["attn_ms"], achieved, 100 * achieved / HBM_PEAK_GBS, 100 * achieved / probe, probe,
-                r["widths"], r["encode_ms"]))
+                r["widths"], r["code_bytes"], r["encode_ms"]))
         print(json.dumps({
             "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
             "dtype": "f16 MFMA operands (hi + lo query parts against exact +-1 codes and signs), f32 accumulate "
                      "(two-stage keys: 1-bit MSE codes + 1-bit QJL signs, 16 bytes each; fp16 values)" if qjl else
-                     "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ 4-bit key containers, fp16 values)",
+                     "f16 MFMA operands (hi + lo parts), f32 accumulate (Block-GTQ nibble%s key containers, fp16 values)"
+                     % (" and byte" if r["code_bytes"] > 64 else ""),
             "data": "synthetic (seeded Gaussian activations with log-normal channel scales; workloads.py)",
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                        "seq_len": w.seq_len,
                        "keys": ("two-stage, %d bits: %d-bit TQ-MSE + 1-bit QJL residual" % (w.bits_k, w.bits_k - 1))
-                       if qjl else "Block-GTQ, %d-bit average budget, widths 1-4" % w.bits_k,
+                       if qjl else "Block-GTQ, %d-bit average budget, widths %d-%d, %d code bytes per key" % (
+                           w.bits_k, GTQ_RANGE[0], GTQ_RANGE[1], r["code_bytes"]),
                        "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
                        "step": "append the new token (key encoded, fp16 value) and attend over encoded keys "
                                "and fp16 values in one launch" + (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": gtq_measured_traffic(w.name, n_splits),
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": gtq_measured_traffic(w.name, n_splits) if qjl or GTQ_RANGE == (1, 4) else None,
                          "kernel": "gtq_attention_kernel"},
             "cpu_baseline": cpu, "attention_kernel_ms": r["attn_ms"], "algorithmic_bytes_per_launch": r["algo_bytes"],
             "block_widths": r["widths"], "key_encoding_ms": r["encode_ms"], "stream_read_probe_GBps": probe,
