@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_codebook.cpp", "tq_api.cpp", "tq_gtq.cpp", "tq_kernels.hip", "tq_zip.hip", "tq_gtq.hip"]
+SOURCES = ["tq_codebook.cpp", "tq_api.cpp", "tq_gtq.cpp", "tq_kernels.hip", "tq_zip.hip", "tq_gtq.hip", "tq_dense.hip"]
 PROBE_LIB = os.path.join(HERE, "libtqprobe.so")   # bandwidth probe used by the benchmark
 PROBE_SOURCES = ["tq_probe.hip"]
 

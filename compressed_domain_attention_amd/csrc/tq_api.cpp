@@ -244,6 +244,7 @@ extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, c
   if (batch <= 0 || capacity <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
+  if (capacity > (1 << 24)) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's fp16 rows
   tq::DenseArgs a;
   std::memset(&a, 0, sizeof(a));
   a.k = k;

@@ -121,5 +121,69 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// ---------------------------------------------------------------------------------------
+// Quaternions (real, i, j, k): the IsoQuant block rotation v -> q_L v conj(q_R).
+struct Quat {
+  float w, x, y, z;
+};
+__device__ __forceinline__ Quat qmul(Quat a, Quat b) {
+  return {a.w * b.w - a.x * b.x - a.y * b.y - a.z * b.z, a.w * b.x + a.x * b.w + a.y * b.z - a.z * b.y,
+          a.w * b.y - a.x * b.z + a.y * b.w + a.z * b.x, a.w * b.z + a.x * b.y - a.y * b.x + a.z * b.w};
+}
+__device__ __forceinline__ Quat qconj(Quat a) { return {a.w, -a.x, -a.y, -a.z}; }
+__device__ __forceinline__ Quat qload(const float* p) {
+  const float4 v = *(const float4*)p;
+  return {v.x, v.y, v.z, v.w};
+}
+
+// Rotation of nh head vectors held in LDS (buf[nh][128]) by the whole workgroup.
+// Forward: signs, normalised Hadamard on every `group` block, then SO(4) if present.
+// Inverse: the reverse.  Called uniformly by every thread of the block.
+template <bool FWD>
+__device__ void lds_rotate(float* buf, int nh, const float* signs, const float* so4, int group) {
+  const int nt = blockDim.x, tid = threadIdx.x, n = nh * 128;
+  if (FWD) {
+    for (int i = tid; i < n; i += nt) buf[i] *= signs[i & 127];
+    __syncthreads();
+  } else if (so4 != nullptr) {
+    for (int p = tid; p < nh * 32; p += nt) {
+      float* v = buf + (p >> 5) * 128 + 4 * (p & 31);
+      const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
+      const Quat o = qmul(qmul(qconj(l), Quat{v[0], v[1], v[2], v[3]}), r);
+      v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
+    }
+    __syncthreads();
+  }
+  for (int s = 1; s < group; s <<= 1) {
+    for (int p = tid; p < nh * 64; p += nt) {
+      const int j = p & 63;
+      const int i0 = (p >> 6) * 128 + (j / s) * 2 * s + (j % s);
+      const float x0 = buf[i0], x1 = buf[i0 + s];
+      buf[i0] = x0 + x1;
+      buf[i0 + s] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const float hs = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  if (FWD) {
+    for (int i = tid; i < n; i += nt) buf[i] *= hs;
+    __syncthreads();
+    if (so4 != nullptr) {
+      for (int p = tid; p < nh * 32; p += nt) {
+        float* v = buf + (p >> 5) * 128 + 4 * (p & 31);
+        const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
+        const Quat o = qmul(qmul(l, Quat{v[0], v[1], v[2], v[3]}), qconj(r));
+        v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int i = tid; i < n; i += nt) buf[i] *= hs * signs[i & 127];
+    __syncthreads();
+  }
+}
+
+
+
 }  // namespace
 }  // namespace tq

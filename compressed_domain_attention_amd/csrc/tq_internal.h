@@ -218,6 +218,7 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
 hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits_v, bool q_f16, bool shared_table,
                          hipStream_t stream);
 hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t stream);
+hipError_t launch_dense_mfma(const DenseArgs& a, bool q_f16, hipStream_t stream);  // fp16 K/V (tq_dense.hip)
 hipError_t launch_zip_compress(const ZipCompressArgs& a, int batch, int n_pages, hipStream_t stream);
 // q_type: 0 fp32, 1 fp16, 2 bf16
 hipError_t launch_zip_attention(const ZipAttnArgs& a, int q_type, hipStream_t stream);

@@ -33,69 +33,6 @@ __device__ __forceinline__ int norm_pos(int t) { return 8 * ((t >> 2) & 3) + 4 *
 
 __device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
-// ---------------------------------------------------------------------------------------
-// Quaternions (real, i, j, k): the IsoQuant block rotation v -> q_L v conj(q_R).
-struct Quat {
-  float w, x, y, z;
-};
-__device__ __forceinline__ Quat qmul(Quat a, Quat b) {
-  return {a.w * b.w - a.x * b.x - a.y * b.y - a.z * b.z, a.w * b.x + a.x * b.w + a.y * b.z - a.z * b.y,
-          a.w * b.y - a.x * b.z + a.y * b.w + a.z * b.x, a.w * b.z + a.x * b.y - a.y * b.x + a.z * b.w};
-}
-__device__ __forceinline__ Quat qconj(Quat a) { return {a.w, -a.x, -a.y, -a.z}; }
-__device__ __forceinline__ Quat qload(const float* p) {
-  const float4 v = *(const float4*)p;
-  return {v.x, v.y, v.z, v.w};
-}
-
-// Rotation of nh head vectors held in LDS (buf[nh][128]) by the whole workgroup.
-// Forward: signs, normalised Hadamard on every `group` block, then SO(4) if present.
-// Inverse: the reverse.  Called uniformly by every thread of the block.
-template <bool FWD>
-__device__ void lds_rotate(float* buf, int nh, const float* signs, const float* so4, int group) {
-  const int nt = blockDim.x, tid = threadIdx.x, n = nh * kHeadDim;
-  if (FWD) {
-    for (int i = tid; i < n; i += nt) buf[i] *= signs[i & (kHeadDim - 1)];
-    __syncthreads();
-  } else if (so4 != nullptr) {
-    for (int p = tid; p < nh * 32; p += nt) {
-      float* v = buf + (p >> 5) * kHeadDim + 4 * (p & 31);
-      const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
-      const Quat o = qmul(qmul(qconj(l), Quat{v[0], v[1], v[2], v[3]}), r);
-      v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
-    }
-    __syncthreads();
-  }
-  for (int s = 1; s < group; s <<= 1) {
-    for (int p = tid; p < nh * 64; p += nt) {
-      const int j = p & 63;
-      const int i0 = (p >> 6) * kHeadDim + (j / s) * 2 * s + (j % s);
-      const float x0 = buf[i0], x1 = buf[i0 + s];
-      buf[i0] = x0 + x1;
-      buf[i0 + s] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  const float hs = group == 32 ? 0.17677669529663688f : 0.088388347648318440f;
-  if (FWD) {
-    for (int i = tid; i < n; i += nt) buf[i] *= hs;
-    __syncthreads();
-    if (so4 != nullptr) {
-      for (int p = tid; p < nh * 32; p += nt) {
-        float* v = buf + (p >> 5) * kHeadDim + 4 * (p & 31);
-        const Quat l = qload(so4 + 8 * (p & 31)), r = qload(so4 + 8 * (p & 31) + 4);
-        const Quat o = qmul(qmul(l, Quat{v[0], v[1], v[2], v[3]}), qconj(r));
-        v[0] = o.w; v[1] = o.x; v[2] = o.y; v[3] = o.z;
-      }
-      __syncthreads();
-    }
-  } else {
-    for (int i = tid; i < n; i += nt) buf[i] *= hs * signs[i & (kHeadDim - 1)];
-    __syncthreads();
-  }
-}
-
-
 // Forward rotation of up to eight query heads in registers: wave w, lane l holds head
 // 2w + (l >> 5), coordinates 4(l & 31) .. +3 (one SO(4) block).  The first two Hadamard
 // stages are in-lane, the rest exchange with lane l ^ m inside the 32-lane half.  The
@@ -1671,52 +1608,41 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Attention over an unquantised K/V region (fp16 or fp32): the prefill kept in fp16, or a
-// window of recent tokens ("RotaryQuant ...", method overview: deferred prefill; "RoPE-Aware
-// Bit Allocation ...", results: the recent-token buffer).  Same section split as the packed
-// decode; each section's partial is rotated forward by R, so that it is in the rotated domain
-// of the packed partials and the merge's one inverse rotation applies to both.
+// Attention over an unquantised fp32 K/V region: a window of recent tokens or a prefill kept
+// unquantised ("RotaryQuant ...", method overview: deferred prefill; "RoPE-Aware Bit
+// Allocation ...", results: the recent-token buffer).  fp16 regions take the matrix-core
+// kernel (tq_dense.hip); fp32 values are not exact fp16 operands, so this one sums with fp32
+// fused multiply-adds.  Same section split as the packed decode; each section's partial is
+// rotated forward by R, so that it is in the rotated domain of the packed partials and the
+// merge's one inverse rotation applies to both.
 //
 // One workgroup per (sequence, KV head, section, head slice of up to 8 heads), 64-token
 // chunks: thread (token, quarter) forms 32-coordinate partial scores for every head, summed
 // over the four quarter lanes by DPP; one wave per head runs the online softmax over the
 // chunk; thread (8 coordinates, token slot) accumulates 4 tokens of each chunk per head.
 // Raw 16-byte words of one thread's share of a 64-token chunk: 32 key values of its score
-// token, 8 value coordinates of each of its 4 value tokens; converted to fp32 when used.
-template <bool KV16>
+// token, 8 value coordinates of each of its 4 value tokens.
 struct DenseRaw {
-  static constexpr int KW = KV16 ? 4 : 8;  // 16-byte words per 32 values
-  static constexpr int VW = KV16 ? 1 : 2;  // per 8 values
+  static constexpr int KW = 8;  // 16-byte words per 32 values
+  static constexpr int VW = 2;  // per 8 values
   uint4 k[KW];
   uint4 v[4][VW];
 };
 
-template <bool KV16>
 __device__ __forceinline__ void unpack8(const uint4* w, float* out) {
-  if (KV16) {
-    const uint32_t x[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-      const h2_t h = __builtin_bit_cast(h2_t, x[j]);
-      out[2 * j] = (float)h[0];
-      out[2 * j + 1] = (float)h[1];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      out[4 * j] = __uint_as_float(w[j].x);
-      out[4 * j + 1] = __uint_as_float(w[j].y);
-      out[4 * j + 2] = __uint_as_float(w[j].z);
-      out[4 * j + 3] = __uint_as_float(w[j].w);
-    }
+  for (int j = 0; j < 2; ++j) {
+    out[4 * j] = __uint_as_float(w[j].x);
+    out[4 * j + 1] = __uint_as_float(w[j].y);
+    out[4 * j + 2] = __uint_as_float(w[j].z);
+    out[4 * j + 3] = __uint_as_float(w[j].w);
   }
 }
 
-template <bool KV16, bool QF16>
+template <bool QF16>
 __global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
   constexpr int MAXH = 8;
-  constexpr int ES = KV16 ? 2 : 4;  // bytes per value
+  constexpr int ES = 4;  // bytes per value
   __shared__ __attribute__((aligned(16))) float qb[MAXH * kHeadDim];  // scaled query, later the output
   __shared__ float pw[MAXH][64];                                      // chunk scores, then weights
   __shared__ float hm[MAXH], hsum[MAXH], halpha[MAXH];
@@ -1740,12 +1666,12 @@ __global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
   const uint8_t* kb = (const uint8_t*)a.k + row0 * kHeadDim * ES;
   const uint8_t* vb = (const uint8_t*)a.v + row0 * kHeadDim * ES;
   // this thread's raw words of the chunk at c0 (tokens past the section are not read)
-  auto fetch = [&](int c0, DenseRaw<KV16>& r) {
+  auto fetch = [&](int c0, DenseRaw& r) {
     const int tk = c0 + st;
     if (tk < hi) {
       const uint4* p = (const uint4*)(kb + ((size_t)tk * kHeadDim + 32 * qd) * ES);
 #pragma unroll
-      for (int i = 0; i < DenseRaw<KV16>::KW; ++i) r.k[i] = p[i];
+      for (int i = 0; i < DenseRaw::KW; ++i) r.k[i] = p[i];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1753,11 +1679,11 @@ __global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
       if (tv < hi) {
         const uint4* p = (const uint4*)(vb + ((size_t)tv * kHeadDim + 8 * dg) * ES);
 #pragma unroll
-        for (int i = 0; i < DenseRaw<KV16>::VW; ++i) r.v[j][i] = p[i];
+        for (int i = 0; i < DenseRaw::VW; ++i) r.v[j][i] = p[i];
       }
     }
   };
-  DenseRaw<KV16> nxt;
+  DenseRaw nxt;
   if (lo < hi) fetch(lo, nxt);  // the first chunk's reads overlap the query set-up
 
   for (int i = tid; i < hs * kHeadDim; i += 256) {
@@ -1777,14 +1703,14 @@ __global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   for (int c0 = lo; c0 < hi; c0 += 64) {
-    const DenseRaw<KV16> cur = nxt;
+    const DenseRaw cur = nxt;
     if (c0 + 64 < hi) fetch(c0 + 64, nxt);  // the next chunk loads during this one
     // scores of the chunk's tokens, all heads (scale and log2 e folded into the query)
     {
       const int tok = c0 + st;
       float kx[32];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) unpack8<KV16>(cur.k + i * (KV16 ? 1 : 2), kx + 8 * i);
+      for (int i = 0; i < 4; ++i) unpack8(cur.k + 2 * i, kx + 8 * i);
 #pragma unroll
       for (int h = 0; h < MAXH; ++h) {
         if (h < hs) {
@@ -1841,7 +1767,7 @@ __global__ __launch_bounds__(256) void dense_kernel(const DenseArgs a) {
       for (int j = 0; j < 4; ++j) {
         if (c0 + ts + 16 * j < hi) {
           float vx[8];
-          unpack8<KV16>(cur.v[j], vx);
+          unpack8(cur.v[j], vx);
 #pragma unroll
           for (int h = 0; h < MAXH; ++h) {
             if (h < hs) {
@@ -2196,10 +2122,9 @@ hipError_t launch_decode(const DecodeArgs& a, int schedule, int bits_k, int bits
 
 hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t stream) {
   const dim3 grid(a.batch * a.n_kv_heads * a.n_splits * a.n_slices), block(256);
-  if (kv_f16 && q_f16) hipLaunchKernelGGL((dense_kernel<true, true>), grid, block, 0, stream, a);
-  else if (kv_f16) hipLaunchKernelGGL((dense_kernel<true, false>), grid, block, 0, stream, a);
-  else if (q_f16) hipLaunchKernelGGL((dense_kernel<false, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((dense_kernel<false, false>), grid, block, 0, stream, a);
+  if (kv_f16) return launch_dense_mfma(a, q_f16, stream);  // fp16 rows are exact matrix-core operands
+  if (q_f16) hipLaunchKernelGGL((dense_kernel<true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((dense_kernel<false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

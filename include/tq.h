@@ -253,9 +253,12 @@ tq_status tq_append_decode_attention_static(const tq_rotation* rot, const tq_cac
  *             [n_splits][batch][n_q_heads] natural-log lse; an empty section has lse = -inf
  *             and a zero partial).  Pointing them at section S of a larger partial buffer
  *             puts these sections after S packed ones for one tq_merge_splits call.
- * Scores and sums are fp32.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or
- * scale, n_q_heads not a multiple of the rotation's KV heads; TQ_ECAPACITY for
- * max_len > capacity. */
+ * fp16 K/V run on the matrix cores: fp16 rows are exact operands against the query's fp16
+ * high and low parts, weights enter the value product as fp16 high + low parts, with fp32
+ * accumulation (scores and sums at fp32-level accuracy).  fp32 K/V are summed with fp32
+ * fused multiply-adds.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or scale,
+ * n_q_heads not a multiple of the rotation's KV heads; TQ_ECAPACITY for max_len > capacity
+ * or capacity > 2^24. */
 tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* v, tq_dtype kv_dtype,
                              int32_t batch, int32_t capacity, const void* q, tq_dtype q_dtype,
                              int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
