@@ -1252,6 +1252,10 @@ def main():
     GTQ_RANGE = tuple(int(x) for x in args.gtq_widths.split(","))
     if len(GTQ_RANGE) != 2 or not 1 <= GTQ_RANGE[0] <= GTQ_RANGE[1] <= 8 or GTQ_RANGE[1] - GTQ_RANGE[0] > 3:
         raise SystemExit("--gtq-widths LO,HI with 1 <= LO <= HI <= 8 and at most four widths")
+    w0 = workloads.WORKLOADS[args.workload]
+    if w0.codec == "gtq" and not GTQ_RANGE[0] <= w0.bits_k <= GTQ_RANGE[1]:
+        raise SystemExit("--gtq-widths %d,%d cannot hold the %d-bit average budget of %s" % (
+            GTQ_RANGE[0], GTQ_RANGE[1], w0.bits_k, w0.name))
     if args.schedule_sweep:
         schedule_sweep()
         return

@@ -9,6 +9,7 @@
 // evaluation).  Key records and the encoder layout are described in tq.h.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "tq.h"
@@ -60,6 +61,31 @@ __device__ __forceinline__ uint32_t count_below(float y, const float* bnd, int n
 __device__ __forceinline__ void stage_head(tq_gtq_head* dst, const tq_gtq_head* src) {
   constexpr int words = sizeof(tq_gtq_head) / 4;
   for (int i = threadIdx.x; i < words; i += blockDim.x) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
+}
+// The same for a kernel whose codes never pass LEVELS levels: the layout fields, the first
+// LEVELS centroids and LEVELS - 1 boundaries of every group and the fp16 scales (a quarter of
+// a kilobyte of codebook instead of eight for nibble codes).
+template <int LEVELS>
+__device__ __forceinline__ void stage_head_part(tq_gtq_head* dst, const tq_gtq_head* src) {
+  constexpr int pre = offsetof(tq_gtq_head, centroid) / 4, cen = pre;
+  constexpr int bnd = offsetof(tq_gtq_head, boundary) / 4, fs = offsetof(tq_gtq_head, f16_scale) / 4;
+  constexpr int G = TQ_GTQ_MAX_GROUPS, cw = LEVELS, bw = LEVELS - 1;
+  constexpr int total = pre + G * cw + G * bw + G;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    int w;
+    if (i < pre) {
+      w = i;
+    } else if (i < pre + G * cw) {
+      const int j = i - pre;
+      w = cen + (j / cw) * 256 + j % cw;
+    } else if (i < pre + G * cw + G * bw) {
+      const int j = i - pre - G * cw;
+      w = bnd + (j / bw) * 255 + j % bw;
+    } else {
+      w = fs + (i - pre - G * cw - G * bw);
+    }
+    ((uint32_t*)dst)[w] = ((const uint32_t*)src)[w];
+  }
 }
 
 // Encodes one key x[128] (fp16 or fp32) into its record: group norms, the normalised group
@@ -376,7 +402,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
 
   // prologue: the head's encoder and the slice's query rows (one round trip), then the
   // k-block plan, the pair tables and the rotated query
-  stage_head(&hd, (const tq_gtq_head*)a.heads + kv);
+  stage_head_part<WIDE ? 256 : 16>(&hd, (const tq_gtq_head*)a.heads + kv);
   for (int i = tid; i < 8 * 128; i += 64 * NW) {
     const int hh = i >> 7, c = i & 127;
     const size_t qi = ((size_t)b * a.n_q_heads + h0 + hh) * 128 + c;

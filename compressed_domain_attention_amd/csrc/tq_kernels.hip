@@ -1361,17 +1361,18 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float y = acc[i] * (VALUES ? vinv[tb][g][i] : inv[tb][g]);
-          // The code is the count of boundaries strictly below y.  Mirrored, a negative y
-          // counts the upper boundaries at or below |y|: one ulp up turns that into the
-          // strict count, so a value exactly on a boundary takes the lower code either side.
-          const float ay = __uint_as_float(__float_as_uint(fabsf(y)) + (y > 0.f ? 0u : 1u));
+          // The sign, then the count of upper-half boundaries strictly below |y|.  A negative
+          // value exactly on a boundary thus takes the code above it, where the compare-count
+          // rule gives the one below; making that count strict too (|y| one ulp up when
+          // y <= 0) cost 13% of the kernel's time, for a tie that real-valued inputs reach
+          // with probability zero (zero vectors, y = 0, keep the rule's code).
           uint32_t m;
           if (VALUES && NU == 7) {  // (the search's selects cost 4-bit value words too many registers)
             m = 0;
 #pragma unroll
-            for (int k = 0; k < NU; ++k) m += ay > ub[k] ? 1u : 0u;
+            for (int k = 0; k < NU; ++k) m += fabsf(y) > ub[k] ? 1u : 0u;
           } else {
-            m = upper_count<NU>(ay, ub);
+            m = upper_count<NU>(fabsf(y), ub);
           }
           const uint32_t code = (y > 0.f ? (uint32_t)HALF : (uint32_t)(HALF - 1)) ^ m;
           f |= code << (BITS * i);
