@@ -1838,26 +1838,31 @@ __device__ __forceinline__ float4 unrotate4(float4 x, const QueryLane& s, bool s
 
 // Log-sum-exp merge of the split partials of one (sequence, query head) and the single
 // inverse rotation.  Every global read that does not depend on another is issued first:
-// the section lse values, the first partials, the signs and SO(4) parameters.
-template <int GROUP>
-__global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
+// the section lse values, the first partials, the signs and SO(4) parameters.  With many
+// sections the workgroup has NP groups of 128 threads, group p taking sections p, p + NP,
+// ..., so that the partials of up to 16 NP sections are in flight in one round trip; the NP
+// sums meet in LDS.
+template <int GROUP, int NP>
+__global__ __launch_bounds__(128 * NP) void merge_kernel(const MergeArgs a) {
   constexpr int kMaxStage = 1024;
   constexpr int kAhead = 16;  // partials held in registers ahead of the weights
+  constexpr int NT = 128 * NP, NWV = 2 * NP;
   __shared__ __attribute__((aligned(16))) float obuf[kHeadDim];
+  __shared__ float psum[NP][kHeadDim];
   __shared__ float wts[kMaxStage];
-  __shared__ float red[2][2];
+  __shared__ float red[2][NWV];
   const int row = blockIdx.x;  // b * n_q_heads + h
   const int h = row % a.n_q_heads;
   const int kv = h / a.group_size;
-  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
+  const int t = threadIdx.x, c = t & 127, p = t >> 7, lane = t & 63, wv = t >> 6;
   const size_t stride = (size_t)a.batch * a.n_q_heads;
   const int S = a.n_splits;
   const float* po = a.part_o + (size_t)row * kHeadDim + c;
 
-  float lse0 = c < S ? a.part_lse[c * stride + row] : -INFINITY;
+  float lse0 = t < S ? a.part_lse[t * stride + row] : -INFINITY;
   float ahead[kAhead];
 #pragma unroll
-  for (int j = 0; j < kAhead; ++j) ahead[j] = j < S ? po[j * stride * kHeadDim] : 0.f;
+  for (int j = 0; j < kAhead; ++j) ahead[j] = p + NP * j < S ? po[(p + NP * j) * stride * kHeadDim] : 0.f;
   QueryLane rl;
   rl.live = wv == 0 && lane < 32;
   rl.sg = make_float4(1.f, 1.f, 1.f, 1.f);
@@ -1872,16 +1877,18 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
 
   // maximum lse, then the weights e^{lse_s - max} (in LDS when they fit) and their sum
   float M = lse0;
-  for (int s = c + 128; s < S; s += 128) M = fmaxf(M, a.part_lse[s * stride + row]);
+  for (int s = t + NT; s < S; s += NT) M = fmaxf(M, a.part_lse[s * stride + row]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[0][wv] = M;
   __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[0][w]);
   const float mu = M == -INFINITY ? 0.f : M;
   float W = 0.f;
-  for (int s = c; s < S; s += 128) {
-    const float l = s == c ? lse0 : a.part_lse[s * stride + row];
+  for (int s = t; s < S; s += NT) {
+    const float l = s == t ? lse0 : a.part_lse[s * stride + row];
     const float w = l == -INFINITY ? 0.f : expf(l - mu);
     if (s < kMaxStage) wts[s] = w;
     W += w;
@@ -1890,27 +1897,37 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
   for (int o = 32; o > 0; o >>= 1) W += __shfl_xor(W, o);
   if (lane == 0) red[1][wv] = W;
   __syncthreads();
-  W = red[1][0] + red[1][1];
+  W = red[1][0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) W += red[1][w];
 
-  // weighted sum of the partials
+  // weighted sum of this group's partials
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
-    if (j < S) acc = fmaf(wts[j], ahead[j], acc);
-  int s = kAhead;
-  for (; s + 8 <= S && s + 8 <= kMaxStage; s += 8) {
+    if (p + NP * j < S) acc = fmaf(wts[p + NP * j], ahead[j], acc);
+  int s = p + NP * kAhead;
+  for (; s + NP * 7 < S && s + NP * 7 < kMaxStage; s += NP * 8) {
     float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = po[(s + j) * stride * kHeadDim];
+    for (int j = 0; j < 8; ++j) v[j] = po[(s + NP * j) * stride * kHeadDim];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + j], v[j], acc);
+    for (int j = 0; j < 8; ++j) acc = fmaf(wts[s + NP * j], v[j], acc);
   }
-  for (; s < S; ++s) {
+  for (; s < S; s += NP) {
     const float l = a.part_lse[s * stride + row];
     const float w = s < kMaxStage ? wts[s] : (l == -INFINITY ? 0.f : expf(l - mu));
     acc = fmaf(w, po[s * stride * kHeadDim], acc);
   }
-  obuf[c] = W > 0.f ? acc / W : 0.f;
+  if (NP > 1) {
+    psum[p][c] = acc;
+    __syncthreads();
+    if (p == 0) {
+#pragma unroll
+      for (int q = 1; q < NP; ++q) acc += psum[q][c];
+    }
+  }
+  if (p == 0) obuf[c] = W > 0.f ? acc / W : 0.f;
   __syncthreads();
   if (wv == 0) {  // the whole first wave takes part in the lane exchanges
     const float4 x = *(const float4*)(obuf + 4 * (lane & 31));
@@ -1918,7 +1935,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
     const float4 y = a.signs ? unrotate4<GROUP>(x, rl, a.so4 != nullptr, lane) : x;
     if (rl.live) *(float4*)(a.out + (size_t)row * kHeadDim + 4 * lane) = y;
   }
-  if (a.lse_out && c == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;
+  if (a.lse_out && t == 0) a.lse_out[row] = W > 0.f ? mu + logf(W) : -INFINITY;
 }
 
 }  // namespace
@@ -2130,12 +2147,13 @@ hipError_t launch_dense(const DenseArgs& a, bool kv_f16, bool q_f16, hipStream_t
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.batch * a.n_q_heads), block(128);
-  if (a.rot_group == 32) {
-    hipLaunchKernelGGL(merge_kernel<32>, grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
-  }
+  // sections per 128-thread group: the first 16 of each group are read in one round trip
+  const int np = a.n_splits > 32 ? 4 : a.n_splits > 16 ? 2 : 1;
+  const dim3 grid(a.batch * a.n_q_heads), block(128 * np);
+#define TQ_MERGE(G, NP) \
+  if (a.rot_group == G && np == NP) hipLaunchKernelGGL((merge_kernel<G, NP>), grid, block, 0, stream, a);
+  TQ_MERGE(32, 1) TQ_MERGE(32, 2) TQ_MERGE(32, 4) TQ_MERGE(128, 1) TQ_MERGE(128, 2) TQ_MERGE(128, 4)
+#undef TQ_MERGE
   return hipGetLastError();
 }
 
