@@ -44,6 +44,59 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+STEPS_PER_GRAPH = 8
+
+
+def capture_graph(torch, fn, indices):
+    """One HIP graph holding fn(i) for every i in indices (run once on a side stream first)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(indices[0])
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in indices:
+            fn(i)
+    return g
+
+
+def time_steps(torch, step, reps, steps, warmup, check=None):
+    """ms per step of `steps` steps that cycle through the reps cache replicas in order.  They
+    run as replays of HIP graphs that each hold G consecutive steps (G the largest divisor of
+    reps up to STEPS_PER_GRAPH, so the replicas keep their order), the remainder as one-step
+    graphs: every step does its own GPU work, and the host's launch overhead is shared by G
+    steps as it is by a model's layers.  Warm-up: at least `warmup` steps and 0.3 s, so the
+    device is at its settled clock.  check() runs after the first replay and after the timed
+    steps."""
+    G = max(d for d in range(1, min(STEPS_PER_GRAPH, reps) + 1) if reps % d == 0)
+    single = [capture_graph(torch, step, [r]) for r in range(reps)]
+    multi = [capture_graph(torch, step, list(range(j * G, (j + 1) * G))) for j in range(reps // G)]
+    single[0].replay()
+    torch.cuda.synchronize()
+    if check:
+        check()
+    t_w, i = time.perf_counter(), 0
+    while i * G < warmup or time.perf_counter() - t_w < 0.3:
+        multi[i % len(multi)].replay()
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    q, rem = divmod(steps, G)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(q):
+        multi[i % len(multi)].replay()
+    for i in range(rem):
+        single[(q * G + i) % reps].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    if check:
+        check()
+    return t0.elapsed_time(t1) / steps
+
+
 def bytes_per_token_head(w):
     """Packed bytes of one (token, KV head): key + value codes and fp32 group norms."""
     ng = 128 // w.group
@@ -144,48 +197,17 @@ def run_gpu(w, inp, steps, warmup, n_splits, schedule, check=True):
     torch.cuda.synchronize()
     eager_out = out.clone()
 
-    # HIP graphs: one per cache replica holding exactly one step (no host work per kernel
-    # in the timed loop), and one holding a run of decode launches for the kernel timing
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(0)
-    torch.cuda.current_stream().wait_stream(side)
-    graphs = []
-    for r in range(reps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        graphs.append(g)
-    n_dec = max(reps, 16)
-    gdec = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gdec):
-        for i in range(n_dec):
-            decode(i)
-    torch.cuda.synchronize()
+    # the steps as HIP graph replays (no host work per kernel in the timed loop); every replay
+    # must reproduce the eager step
+    def same_as_eager():
+        if not torch.equal(out, eager_out):
+            raise SystemExit("graph replays do not reproduce the eager step")
 
-    graphs[0].replay()
+    total_ms = steps * time_steps(torch, step, reps, steps, warmup, same_as_eager)
+    # one graph holding a run of decode launches for the kernel timing
+    n_dec = max(reps, 16)
+    gdec = capture_graph(torch, decode, list(range(n_dec)))
     torch.cuda.synchronize()
-    if not torch.equal(out, eager_out):
-        raise SystemExit("graph replay does not reproduce the eager step")
-    # warm-up: the W steps asked for, and at least ~0.3 s of them, so that the timed region
-    # sees the device at its settled clock and power state rather than ramping up from idle
-    t_w, i = time.perf_counter(), 0
-    while i < warmup or time.perf_counter() - t_w < 0.3:
-        graphs[i % reps].replay()
-        i += 1
-        if i % 256 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % reps].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    if not torch.equal(out, eager_out):
-        raise SystemExit("graph replays drifted from the eager step")
 
     # decode kernel alone: back-to-back launches in one graph, events on the launch stream
     gdec.replay()
@@ -257,35 +279,11 @@ def run_tail(w, inp, n_tail, tail_splits, steps, warmup, n_splits, schedule):
         dense(i)
         tq.merge_splits(rot, po, pl, out=out, lse=lse)
 
-    def graph(fn, n):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
-
     for i in range(max(warmup, 1)):
         step(i)
     torch.cuda.synchronize()
-    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
-    t_w, i = time.perf_counter(), 0
-    while i < warmup or time.perf_counter() - t_w < 0.3:
-        graphs[i % reps].replay()
-        i += 1
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % reps].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    gd = graph(dense, 16)
+    step_ms = time_steps(torch, step, reps, steps, warmup)
+    gd = capture_graph(torch, dense, list(range(16)))
     gd.replay()
     torch.cuda.synchronize()
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -411,42 +409,18 @@ def run_zip(w, inp, steps, warmup, n_splits, check=True):
             tq.merge_splits(None, po, pl, out=out, lse=lse)
 
     def graph(fn, n):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
+        return capture_graph(torch, fn, list(range(n)))
 
     for i in range(max(warmup, 1)):
         step(i)
     torch.cuda.synchronize()
     eager_out = out.clone()
-    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    if not torch.equal(out, eager_out):
-        raise SystemExit("graph replay does not reproduce the eager step")
-    t_w, i = time.perf_counter(), 0
-    while i < warmup or time.perf_counter() - t_w < 0.3:
-        graphs[i % reps].replay()
-        i += 1
-        if i % 256 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % reps].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    if not torch.equal(out, eager_out):
-        raise SystemExit("graph replays drifted from the eager step")
+
+    def same_as_eager():
+        if not torch.equal(out, eager_out):
+            raise SystemExit("graph replays do not reproduce the eager step")
+
+    step_ms = time_steps(torch, step, reps, steps, warmup, same_as_eager)
     n_att = max(reps, 16)
     ga = graph(lambda i: attend(i), n_att)
     ga.replay()
@@ -640,40 +614,18 @@ def run_gtq(w, inp, steps, warmup, n_splits, check=True):
             tq.merge_splits(None, po, pl, out=out, lse=lse)
 
     def graph(fn, n):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
+        return capture_graph(torch, fn, list(range(n)))
 
     for i in range(max(warmup, 1)):
         step(i)
     torch.cuda.synchronize()
     eager_out = out.clone()
-    graphs = [graph(lambda i, r=r: step(r), 1) for r in range(reps)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    if not torch.equal(out, eager_out):
-        raise SystemExit("graph replay does not reproduce the eager step")
-    t_w, i = time.perf_counter(), 0
-    while i < warmup or time.perf_counter() - t_w < 0.3:
-        graphs[i % reps].replay()
-        i += 1
-        if i % 256 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % reps].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
+
+    def same_as_eager():
+        if not torch.equal(out, eager_out):
+            raise SystemExit("graph replays do not reproduce the eager step")
+
+    step_ms = time_steps(torch, step, reps, steps, warmup, same_as_eager)
     n_att = max(reps, 16)
     ga = graph(lambda i: attend(i), n_att)
     ga.replay()
@@ -1316,7 +1268,7 @@ def main():
                        "keys": ("two-stage, %d bits: %d-bit TQ-MSE + 1-bit QJL residual" % (w.bits_k, w.bits_k - 1))
                        if qjl else "Block-GTQ, %d-bit average budget, widths %d-%d, %d code bytes per key" % (
                            w.bits_k, GTQ_RANGE[0], GTQ_RANGE[1], r["code_bytes"]),
-                       "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
+                       "values": "fp16", "n_splits": n_splits, "timing": "HIP graph replays of up to %d consecutive steps each, over the cache replicas in turn" % STEPS_PER_GRAPH,
                        "step": "append the new token (key encoded, fp16 value) and attend over encoded keys "
                                "and fp16 values in one launch" + (", then merge" if n_splits > 1 else ""),
                        "cache_replicas": r["reps"]},
@@ -1345,7 +1297,7 @@ def main():
             "data": "synthetic (seeded Gaussian activations with outlier channels, rounded to BF16; workloads.py)",
             "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                        "seq_len": w.seq_len, "codec": "lossless BF16 exponent codec (16-token pages)",
-                       "n_splits": n_splits, "timing": "HIP graph replay, one graph per step",
+                       "n_splits": n_splits, "timing": "HIP graph replays of up to %d consecutive steps each, over the cache replicas in turn" % STEPS_PER_GRAPH,
                        "step": "attention from the compressed pages + open page" +
                                (", then merge" if n_splits > 1 else " (one section per row: no merge)"),
                        "store_replicas": r["reps"]},
@@ -1420,7 +1372,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16 MFMA operands, f32 accumulate (3/4-bit codes)",
         "data": "synthetic (seeded Gaussian activations with outlier channels; workloads.py)",
-        "config": {"workload": w.name, "timing": "HIP graph replay, one graph per step", "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+        "config": {"workload": w.name, "timing": "HIP graph replays of up to %d consecutive steps each, over the cache replicas in turn" % STEPS_PER_GRAPH, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "seq_len": w.seq_len, "bits_k": w.bits_k, "bits_v": w.bits_v, "group": w.group,
                    "so4": w.so4, "n_splits": n_splits, "schedule": args.schedule,
                    "step": "append 1 token K+V and decode in one launch, then merge", "cache_replicas": r["reps"]},
