@@ -230,6 +230,34 @@ def test_dense_sections_match_oracle(name, n_splits):
         np.testing.assert_allclose(pl.cpu().numpy(), ref_pl, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("kv_dtype,q_dtype,n_q_heads", [(np.float16, np.float32, 32), (np.float16, np.float16, 64),
+                                                     (np.float32, np.float16, 64)])
+def test_dense_query_dtypes_and_head_slices(kv_dtype, q_dtype, n_q_heads):
+    # both query dtypes against fp16 and fp32 rows, and 16 query heads per KV head (two
+    # workgroup slices of 8), with ragged rows and an empty one
+    from dataclasses import replace
+    w, inp = setup("long128k", seed=13, seq_len=150, batch=3)
+    w = replace(w, n_q_heads=n_q_heads)
+    rng = np.random.default_rng(13)
+    q32 = (rng.standard_normal((w.batch, n_q_heads, 128)) * 0.5).astype(np.float16).astype(np.float32)
+    inp = dict(inp, q=q32.astype(q_dtype))
+    rot = device_rotation(w, inp)
+    kx = inp["k"].astype(kv_dtype)
+    vx = inp["v"].astype(kv_dtype)
+    lens = np.array([150, 0, 67], dtype=np.int32)
+    po, pl = tq.dense_attention(rot, torch.from_numpy(kx).cuda(), torch.from_numpy(vx).cuda(),
+                                torch.from_numpy(inp["q"]).cuda(), seq_lens=torch.from_numpy(lens).cuda(),
+                                max_len=150, n_splits=3)
+    out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(w, inp, kx.astype(np.float64), vx.astype(np.float64), lens)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print("dense %s K/V, %s q, %d heads: max row rel err %.3e" % (np.dtype(kv_dtype).name, np.dtype(q_dtype).name,
+                                                                  n_q_heads, err.max()), flush=True)
+    assert err.max() <= DENSE_RTOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_packed_prefix_with_unquantised_tail(name):
     # a row is a packed prefix plus an unquantised tail (recent tokens, or an fp16 prefill):
