@@ -13,6 +13,7 @@
 // form: asin(hi) - asin(lo).
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "tq.h"
 
@@ -151,7 +152,7 @@ bool wide_codebook(int bits, int dim, float* centroid, float* boundary, float* s
   auto dens = [&](double t) { return integrand(t, mu); };
   // start: quantiles of f^(1/3), integrated in theta (f^(1/3) dt = cos^(dim/3) theta d theta)
   const int G = 20000;
-  static thread_local double cum[G + 1];
+  std::vector<double> cum(G + 1);
   cum[0] = 0.0;
   for (int i = 0; i < G; ++i) {
     const double t0 = -M_PI / 2 + M_PI * i / G, t1 = -M_PI / 2 + M_PI * (i + 1) / G;
