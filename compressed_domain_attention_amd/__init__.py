@@ -25,6 +25,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 HEAD_DIM = 128
 TILE = 32
+MAX_CAPACITY = 1 << 24  # tokens per (sequence, head) of any cache
 TQ_KEYS = 0
 TQ_VALUES = 1
 _SCHEDULES = {"auto": 0, "vec": 1, "mfma": 2}

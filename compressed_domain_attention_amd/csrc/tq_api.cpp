@@ -27,6 +27,7 @@ tq_status check_cache(const tq_cache* c, const tq_rotation* rot, tq_role role) {
   if (c->group != rot->group) return TQ_EINVAL;
   if (c->bits != 3 && c->bits != 4) return TQ_EUNSUPPORTED;
   if (!valid_codebook(c->codebook, c->bits, c->group)) return TQ_EINVAL;
+  if (c->capacity > TQ_MAX_CAPACITY) return TQ_ECAPACITY;
   return TQ_OK;
 }
 
@@ -244,7 +245,7 @@ extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, c
   if (batch <= 0 || capacity <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
-  if (capacity > (1 << 24)) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's fp16 rows
+  if (capacity > TQ_MAX_CAPACITY) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's fp16 rows
   tq::DenseArgs a;
   std::memset(&a, 0, sizeof(a));
   a.k = k;
@@ -381,7 +382,7 @@ static tq_status gtq_quantize(const tq_gtq_head* heads, const float* rotations, 
   if (batch <= 0 || batch > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_new < 0 || pos0 < 0 || capacity <= 0)
     return TQ_EINVAL;
   if (code_bits == 0 && !valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
-  if ((int64_t)pos0 + n_new > capacity) return TQ_ECAPACITY;
+  if ((int64_t)pos0 + n_new > capacity || capacity > TQ_MAX_CAPACITY) return TQ_ECAPACITY;
   if (n_new == 0) return TQ_OK;
   tq::GtqQuantArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -433,7 +434,7 @@ static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotat
   if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
   if (code_bytes != 0 && !valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
-  if (capacity > (1 << 24)) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's values
+  if (capacity > TQ_MAX_CAPACITY) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's values
   const int group = n_q_heads / n_kv_heads;
   const int hps = group < 8 ? group : 8;
   const int slices = (group + hps - 1) / hps;

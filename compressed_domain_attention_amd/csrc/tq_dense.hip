@@ -94,13 +94,13 @@ __global__ __launch_bounds__(64 * NW) void dense_mfma_kernel(const DenseArgs a) 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * k + (lane >> 4), j = lane & 15, t = t0 + r;
-      lds_dma<16, true>(dst + 1024 * k, kbase, t < cap ? (uint32_t)(t * 256 + 16 * (j ^ r)) : (uint32_t)(t0 * 256));
+      lds_dma<16, true>(dst + 1024 * k, kbase, t < cap ? (uint32_t)t * 256u + 16u * (j ^ r) : (uint32_t)t0 * 256u);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t = t0 + 4 * k + (lane >> 4);
       lds_dma<16, true>(dst + VAL_AT + 1024 * k, vbase,
-                        t < cap ? (uint32_t)(t * 256 + 16 * (lane & 15)) : (uint32_t)(t0 * 256));
+                        t < cap ? (uint32_t)t * 256u + 16u * (lane & 15) : (uint32_t)t0 * 256u);
     }
   };
 

@@ -392,7 +392,7 @@ __global__ __launch_bounds__(64 * NW) void gtq_attention_kernel(const GtqAttnArg
     for (int k = 0; k < 4; ++k) {
       t = t0 + 4 * k + (lane >> 4);
       lds_dma<16, true>(dst + VAL_AT + 1024 * k, vbp,
-                        t < cap ? (uint32_t)(t * 256 + 16 * (lane & 15)) : (uint32_t)(t0 * 256));
+                        t < cap ? (uint32_t)t * 256u + 16u * (lane & 15) : (uint32_t)t0 * 256u);
     }
     if (QJL) {  // 16 tokens' sign bytes (lane: token tok0 + l/4, 4 bytes)
       t = t0 + (lane >> 2);

@@ -1948,9 +1948,11 @@ static int device_cus();
 // Whole tiles go to the matrix-core append when the vectors are fp16, every row starts at
 // the same position and at least one tile is whole: tiles [j0, j0 + n_full), counted from
 // slot 0.  The partial tiles at either end (at most two per row) stay with the tile kernel,
-// in its edge mode (tiles counted from pos0 / 32).
+// in its edge mode (tiles counted from pos0 / 32).  Calls of more than 2^22 vectors per row
+// (a row's input past 1 GiB, beyond the kernel's 32-bit buffer offsets with room to spare)
+// take the tile kernel whole.
 static bool mfma_append_split(const AppendArgs& a, bool x_f16, int& j0, int& n_full, AppendArgs& edges) {
-  if (!x_f16 || a.pos != nullptr || a.n_new < 2 * kTile || a.n_edges != 0) return false;
+  if (!x_f16 || a.pos != nullptr || a.n_new < 2 * kTile || a.n_new > (1 << 22) || a.n_edges != 0) return false;
   const int first = (a.pos0 + kTile - 1) / kTile, end = (a.pos0 + a.n_new) / kTile;
   if (end <= first) return false;
   j0 = first;

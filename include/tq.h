@@ -27,7 +27,9 @@
  *     log-sum-exp ("RoPE-Aware Bit Allocation for KV-Cache Quantization", packed-cache
  *     implementation details).
  *
- * Fixed sizes: head dimension 128; cache capacity a multiple of the 32-token tile.
+ * Fixed sizes: head dimension 128; cache capacity a multiple of the 32-token tile and at
+ * most TQ_MAX_CAPACITY tokens per (sequence, head) (packed, unquantised, Block-GTQ and
+ * two-stage caches; the lossless page store states its own limits).
  *
  * Packed layout (the pages fix only the unit: 8 three-bit codes in 3 bytes, or two
  * four-bit codes per byte, "TurboQuant ...", 3.3).  A word of 8 codes of b bits is the
@@ -54,12 +56,14 @@ extern "C" {
 
 #define TQ_HEAD_DIM 128
 #define TQ_TILE 32
+/* Tokens per (sequence, head) of any cache: byte offsets within one stream stay 32-bit. */
+#define TQ_MAX_CAPACITY (1 << 24)
 
 typedef enum {
   TQ_OK = 0,
   TQ_EINVAL = 1,        /* null pointer, bad size or inconsistent arguments */
   TQ_EUNSUPPORTED = 2,  /* valid but not implemented (bits, group, head grouping) */
-  TQ_ECAPACITY = 3,     /* a write or read would pass the cache capacity */
+  TQ_ECAPACITY = 3,     /* a write or read would pass the cache capacity, or a capacity above TQ_MAX_CAPACITY */
   TQ_EHIP = 4           /* a HIP launch or runtime call failed */
 } tq_status;
 
@@ -119,7 +123,7 @@ typedef struct {
   float* norms;         /* device, layout above */
   int32_t batch;
   int32_t n_kv_heads;
-  int32_t capacity;     /* tokens per (sequence, head); multiple of 32 */
+  int32_t capacity;     /* tokens per (sequence, head); multiple of 32, <= TQ_MAX_CAPACITY */
   int32_t bits;         /* 3 or 4 */
   int32_t group;        /* must equal the rotation's group */
   tq_role role;
@@ -136,7 +140,8 @@ typedef struct {
  *          capacity check (ignored when pos == NULL).
  * Slots [pos, pos + n_new) of every (sequence, head) are written; neighbouring value
  * slots that share a packed word are preserved.  A zero group stores norm 0 and the
- * code of 0.  Errors: TQ_ECAPACITY if max(pos) + n_new > capacity. */
+ * code of 0.  Errors: TQ_ECAPACITY if max(pos) + n_new > capacity or capacity >
+ * TQ_MAX_CAPACITY. */
 tq_status tq_quantize_append(const tq_rotation* rot, const tq_cache* cache, const void* x,
                              tq_dtype x_dtype, int32_t n_new, const int32_t* pos, int32_t pos0,
                              int32_t max_pos, void* stream);
@@ -187,8 +192,8 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
  * is fp32 throughout.
  * Errors: TQ_EINVAL for null pointers, bad dtypes, counts, scale or schedule, caches that
  * do not match the rotation or each other, or a missing output for the split count;
- * TQ_ECAPACITY for max_len > capacity; TQ_EUNSUPPORTED for bits or groups outside 3/4 and
- * 32/128. */
+ * TQ_ECAPACITY for max_len > capacity or capacity > TQ_MAX_CAPACITY; TQ_EUNSUPPORTED for
+ * bits or groups outside 3/4 and 32/128. */
 tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,
                               const void* q, tq_dtype q_dtype, int32_t n_q_heads,
                               const int32_t* seq_lens, int32_t max_len, float scale,
@@ -258,7 +263,7 @@ tq_status tq_append_decode_attention_static(const tq_rotation* rot, const tq_cac
  * accumulation (scores and sums at fp32-level accuracy).  fp32 K/V are summed with fp32
  * fused multiply-adds.  Errors: TQ_EINVAL for null pointers, bad dtypes, counts or scale,
  * n_q_heads not a multiple of the rotation's KV heads; TQ_ECAPACITY for max_len > capacity
- * or capacity > 2^24. */
+ * or capacity > TQ_MAX_CAPACITY. */
 tq_status tq_dense_attention(const tq_rotation* rot, const void* k, const void* v, tq_dtype kv_dtype,
                              int32_t batch, int32_t capacity, const void* q, tq_dtype q_dtype,
                              int32_t n_q_heads, const int32_t* seq_lens, int32_t max_len, float scale,
@@ -440,7 +445,7 @@ tq_status tq_gtq_qjl_projection(const tq_gtq_head* head, const float* rotation, 
  *   codes:     device uint8 [batch][n_kv_heads][capacity][code_bytes] (padding written as
  *              zeros); norms: device float [batch][n_kv_heads][capacity][4].
  * Errors: TQ_EINVAL for null pointers, bad dtype, counts or code_bytes; TQ_ECAPACITY when
- * pos0 + n_new > capacity.  n_new == 0 is a no-op. */
+ * pos0 + n_new > capacity or capacity > TQ_MAX_CAPACITY.  n_new == 0 is a no-op. */
 tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations, const void* x, tq_dtype x_dtype,
                                int32_t batch, int32_t n_kv_heads, int32_t n_new, int32_t pos0, int32_t capacity,
                                int32_t code_bytes, uint8_t* codes, float* norms, void* stream);
@@ -463,7 +468,7 @@ tq_status tq_gtq_quantize_keys(const tq_gtq_head* heads, const float* rotations,
  * weights) with fp32 accumulation; nibble codes are decoded two at a time through pair
  * tables, byte codes one at a time through a 256-entry table per group.  Errors: TQ_EINVAL
  * for null pointers, bad dtypes, counts, scale or code_bytes; TQ_ECAPACITY for max_len >
- * capacity or capacity > 2^24. */
+ * capacity or capacity > TQ_MAX_CAPACITY. */
 tq_status tq_gtq_attention(const tq_gtq_head* heads, const float* rotations, int32_t code_bytes, const uint8_t* codes,
                            const float* norms,
                            const void* v, int32_t capacity, int32_t batch, int32_t n_kv_heads, const void* q,

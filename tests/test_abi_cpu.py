@@ -278,6 +278,29 @@ def test_merge_without_rotation_validation(lib):
     assert m(None, 2, 1, 4, None, FAKE, FAKE, None, None) == TQ_EINVAL
 
 
+
+def test_capacity_limit(lib):
+    # every cache of at most TQ_MAX_CAPACITY tokens per (sequence, head) is accepted, one
+    # tile more is rejected before anything is launched (32-bit offsets within a stream)
+    m = re.search(r"#define TQ_MAX_CAPACITY \(1 << (\d+)\)", open(HEADER).read())
+    cap = 1 << int(m.group(1))
+    assert tq.MAX_CAPACITY == cap
+    over = cap + tq.TILE
+    rot = make_rot()
+    for role in (tq.TQ_KEYS, tq.TQ_VALUES):
+        assert append(rot, make_cache(role, capacity=cap), n_new=0) == TQ_OK
+        assert append(rot, make_cache(role, capacity=over), n_new=0) == TQ_ECAPACITY
+    k, v = make_cache(tq.TQ_KEYS, capacity=over), make_cache(tq.TQ_VALUES, capacity=over)
+    assert append_kv(rot, k, v, n_new=0) == TQ_ECAPACITY
+    assert decode(rot, k, v) == TQ_ECAPACITY
+    assert append_decode(rot, k, v) == TQ_ECAPACITY
+    assert dense(rot, capacity=over) == TQ_ECAPACITY
+    qk = lib.tq_gtq_quantize_keys
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, cap, 64, FAKE, FAKE, None) == TQ_OK
+    assert qk(FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, over, 64, FAKE, FAKE, None) == TQ_ECAPACITY
+    assert lib.tq_gtq_attention(FAKE, FAKE, 64, FAKE, FAKE, FAKE, over, 1, 2, FAKE, 1, 8, None, 10, 0.1, 1, FAKE, None,
+                                FAKE, FAKE, None) == TQ_ECAPACITY
+
 def test_gtq_allocate_matches_oracle(lib):
     from oracle import blockgtq as bg
     rng = np.random.default_rng(7)

@@ -9,6 +9,8 @@ format has one, the same sections, then the merge) and compares every query head
 (sequence, KV head) units with the oracle, which encodes and attends over those units alone.
 Bars: 2e-3 per row for the packed cache (fp16 weights, the tolerance of the other packed-cache
 parity tests), 1e-4 for the lossless codec, Block-GTQ and two-stage keys (hi + lo fp16 operands).
+One more case fills a stream of the largest capacity the library accepts (2^24 tokens) and
+reads all of it.
 """
 
 import time
@@ -19,7 +21,7 @@ import torch
 
 import compressed_domain_attention_amd as tq
 import workloads
-from helpers import OUT_RTOL, row_rel_err
+from helpers import OUT_RTOL, check_codes, dequantized, oracle_quantize, row_rel_err, unpack
 from oracle import attention, blockgtq as bg, codebook, qjl, quant, zipcodec as zc
 
 pytestmark = pytest.mark.gpu
@@ -184,3 +186,59 @@ def test_qjl32k_step():
             worst = max(worst, float(row_rel_err(out[b, h], ref)))
     print("worst row error %.2e" % worst, flush=True)
     assert worst <= EXACT_RTOL
+
+
+def test_maximum_capacity_step():
+    # One (sequence, KV head) stream of TQ_MAX_CAPACITY tokens (IsoQuant TQ3 with SO(4), 4 query
+    # heads): tile 0 takes 32 tokens and is copied to every tile but the last three; the last
+    # 96 slots are written by one prefill call at cap - 96 (its two whole tiles on the matrix
+    # cores, the partial last tile on the tile kernel) and by the step's fused append at
+    # cap - 1, and the decode reads all 2^24 slots in 64 sections.  The oracle attends over
+    # the 128 distinct tokens, the copied ones through the lse of their set plus the log of
+    # their number of copies.
+    from dataclasses import replace
+    cap = tq.MAX_CAPACITY
+    w = replace(workloads.WORKLOADS["isoquant32k"], batch=1, n_q_heads=4, n_kv_heads=1, seq_len=128, n_splits=64)
+    announce("maximum capacity %d" % cap, w)
+    inp = workloads.generate(w, 0)
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, torch.from_numpy(inp["so4"]).cuda())
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    kc = tq.PackedCache(1, 1, cap, w.bits_k, w.group, tq.TQ_KEYS)
+    vc = tq.PackedCache(1, 1, cap, w.bits_v, w.group, tq.TQ_VALUES)
+    ntile = cap // tq.TILE
+    tq.quantize_append_kv(rot, kc, vc, kx[:, :, :32].contiguous(), vx[:, :, :32].contiguous(), pos0=0)
+    kt = kc.codes.view(1, 1, ntile, -1)
+    for a in (kt, vc.codes, kc.norms, vc.norms):
+        a[:, :, 1:ntile - 3] = a[:, :, :1]
+    tq.quantize_append_kv(rot, kc, vc, kx[:, :, 32:127].contiguous(), vx[:, :, 32:127].contiguous(), pos0=cap - 96)
+    q = torch.from_numpy(inp["q"]).cuda()
+    po, pl = tq.append_decode_attention(rot, kc, vc, kx[:, :, 127:].contiguous(), vx[:, :, 127:].contiguous(), q,
+                                        pos0=cap - 1, scale=w.scale, n_splits=w.n_splits)
+    out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    # the cache's last three tiles and one copied tile in the middle, against the oracle
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    part = lambda oq, lo, hi: dict(oq, idx=oq["idx"][:, :, lo:hi], norms=oq["norms"][:, :, lo:hi],
+                                   dist=oq["dist"][:, :, lo:hi])
+    for tile, lo, n in ((ntile - 3, 32, 96), (ntile // 2, 0, 32)):
+        nt = n // tq.TILE
+        kcodes = kc.codes[:, :, tq.TILE * tile:tq.TILE * tile + n].cpu().numpy()
+        vcodes = vc.codes[:, :, tile:tile + nt].cpu().numpy()
+        for oq, codes, c, role in ((oqk, kcodes, kc, "k"), (oqv, vcodes, vc, "v")):
+            idx, nrm = unpack(codes, c.norms[:, :, tile:tile + nt].cpu().numpy(), oq["bits"], role)
+            check_codes(idx, nrm, part(oq, lo, lo + n), n)
+    del kc, vc, kt
+    kd, vd = dequantized(w, inp, oqk)[0, 0], dequantized(w, inp, oqv)[0, 0]
+    copies = (cap - 96) // 32
+    worst = worst_lse = 0.0
+    for h in range(w.n_q_heads):
+        qh = inp["q"][0, h].astype(np.float64)
+        oa, la = attention.softmax_attend(qh, kd[:32], vd[:32], w.scale)
+        ob, lb = attention.softmax_attend(qh, kd[32:], vd[32:], w.scale)
+        ref, ref_lse = attention.merge(np.stack([oa, ob]), np.array([la + np.log(copies), lb]))
+        worst = max(worst, float(row_rel_err(out[0, h], ref)))
+        worst_lse = max(worst_lse, abs(float(lse[0, h]) - float(ref_lse)) / max(1.0, abs(float(ref_lse))))
+    print("worst row error %.2e, lse %.2e" % (worst, worst_lse), flush=True)
+    assert worst <= OUT_RTOL
+    assert worst_lse <= 1e-4

@@ -1,9 +1,9 @@
 """GPU parity of Block-GTQ keys through the C ABI against the oracle (oracle/blockgtq.py).
 
-Encoding: codes equal the oracle's except coordinates whose rotated value lies within 2e-6
+Encoding: codes equal the oracle's except coordinates whose rotated value lies within 1e-6
 of a decision boundary (the library rotates with the fp32-rounded rotation, the oracle with
-fp64: their rotated values differ by about 1e-7), at most 1e-4 of all coordinates; norms
-within 1e-6 relative.  Attention is fed the oracle's codes and norms and compared with fp64
+fp64: their rotated values differ by about 1e-7), at most 1e-5 of all coordinates (the
+packed cache's code bar); norms within 1e-6 relative.  Attention is fed the oracle's codes and norms and compared with fp64
 attention on the oracle's dequantised keys and the fp16 values: within 1e-4 relative per
 row (fp32 sums of fp16 hi + lo operands), lse within 1e-4 + 1e-5 |lse|.  Rows are ragged, with an empty
 one; sections 1, 3 and 40; query groups of 4, 8 and 16 heads (two slices).  Widths 1-4 (nibble
@@ -29,7 +29,8 @@ pytestmark = pytest.mark.gpu
 RTOL = 1e-4
 LSE_ATOL = 1e-4
 LSE_RTOL = 1e-5
-BOUNDARY_EPS = 2e-6
+BOUNDARY_EPS = 1e-6
+FLIP_FRACTION = 1e-5
 LENS = [300, 77, 0]
 
 
@@ -102,8 +103,8 @@ def test_encoding_matches_oracle(widths):
         assert not raw[:, h, :, enc_used(enc[h]):].any()
     got = unpack_records(raw, enc)
     bad = got != oc
-    frac = bad.mean()
-    assert frac <= 1e-4, frac
+    print("code flips: %d of %d" % (bad.sum(), bad.size), flush=True)
+    assert bad.mean() <= FLIP_FRACTION, bad.mean()
     for b, h, t, j in zip(*np.nonzero(bad)):
         ends = np.cumsum([len(e[1]) for e in enc[h]])
         m = enc[h][int(np.searchsorted(ends, j, side="right"))][4]  # the position's group boundaries

@@ -3,8 +3,8 @@ C ABI.
 
 Every stored width of the first stage, bit-packed: one-bit codes in 16 bytes (2-bit keys),
 2-bit codes in 32 bytes (3-bit keys) and 3-bit codes in 48 bytes (4-bit keys).
-Encoding: MSE codes equal the oracle's except coordinates within 2e-6 of a boundary (at most
-1e-4 of them), the MSE norm within 1e-6 relative, the residual coefficient
+Encoding: MSE codes equal the oracle's except coordinates within 1e-6 of a boundary (at most
+1e-5 of them, the packed cache's code bar), the MSE norm within 1e-6 relative, the residual coefficient
 sqrt(pi/2)/128 |r| within 1e-4 relative (keys with a boundary code excluded: their residual
 differs), and the sign bits equal the oracle's except projections within 1e-4 |r| |S_i| of
 zero (the library projects the rotated-domain residual with the fp32 product S Q).
@@ -22,7 +22,7 @@ import torch
 import compressed_domain_attention_amd as tq
 import workloads
 from helpers import row_rel_err
-from oracle import qjl
+from oracle import blockgtq as bg, qjl
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,8 @@ RTOL = 1e-4
 LSE_ATOL = 1e-4
 LSE_RTOL = 1e-5
 LENS = [300, 77, 0]
+BOUNDARY_EPS = 1e-6
+FLIP_FRACTION = 1e-5
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -78,7 +80,12 @@ def test_encoding_matches_oracle(bits_k):
     oc, on, osg, orn, oxh = oracle_records(w, inp, enc)
     got = qjl.unpack_codes(codes.cpu().numpy().reshape(-1, cb), bits).reshape(oc.shape)
     bad = got != oc
-    assert bad.mean() <= 1e-4, bad.mean()
+    print("first-stage code flips: %d of %d" % (bad.sum(), bad.size), flush=True)
+    assert bad.mean() <= FLIP_FRACTION, bad.mean()
+    for b, h, t in sorted(set(zip(*np.nonzero(bad)[:3]))):
+        _, _, y = bg.quantize_keys(inp["k"][b, h, t][None].astype(np.float64), enc[h])
+        for j in np.nonzero(bad[b, h, t])[0]:
+            assert np.min(np.abs(enc[h][0][4] - y[0, j])) < BOUNDARY_EPS, (b, h, t, j)
     n = norms.cpu().numpy()
     assert np.allclose(n[..., 0], on[..., 0], rtol=1e-6, atol=0)
     clean = ~bad.any(axis=-1)
