@@ -1,6 +1,7 @@
 // C ABI of the packed-KV decode attention library: argument checks on the host, then one
 // launch per call on the caller's stream.  No allocation, no global state.
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 
 #include "tq.h"
@@ -23,6 +24,8 @@ tq_status check_cache(const tq_cache* c, const tq_rotation* rot, tq_role role) {
   if (c == nullptr || c->codes == nullptr || c->norms == nullptr) return TQ_EINVAL;
   if (c->role != role) return TQ_EINVAL;
   if (c->batch <= 0 || c->capacity <= 0 || (c->capacity % TQ_TILE) != 0) return TQ_EINVAL;
+  // launch grid dimensions: the appends take (sequence, role) and KV heads as grid axes
+  if (c->batch > 32767 || c->n_kv_heads > 65535) return TQ_EINVAL;
   if (c->n_kv_heads != rot->n_kv_heads) return TQ_EINVAL;
   if (c->group != rot->group) return TQ_EINVAL;
   if (c->bits != 3 && c->bits != 4) return TQ_EUNSUPPORTED;
@@ -32,6 +35,12 @@ tq_status check_cache(const tq_cache* c, const tq_rotation* rot, tq_role role) {
 }
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// Attention launches one workgroup per (row, KV head, section, head slice), at most one per
+// (row, query head, section): that count must fit a one-dimensional grid.
+bool grid_fits(int32_t batch, int32_t n_q_heads, int32_t n_splits) {
+  return (int64_t)batch * n_q_heads * n_splits <= INT32_MAX;
+}
 
 // Host checks shared by the append calls; fills the launch arguments of one cache.
 tq_status append_args(const tq_rotation* rot, const tq_cache* cache, const void* x, tq_dtype x_dtype, int32_t n_new,
@@ -119,6 +128,7 @@ tq_status decode_args(const tq_rotation* rot, const tq_cache* keys, const tq_cac
   if (values->capacity != keys->capacity) return TQ_EINVAL;
 
   const int group_size = n_q_heads / rot->n_kv_heads;
+  if (!grid_fits(keys->batch, n_q_heads, n_splits)) return TQ_EINVAL;
   // every supported (bits, group) pair has a matrix-core kernel, and it is the faster schedule
   // at every cache length measured (32 to 8192 tokens, 1 to 8 query heads per KV head), so
   // AUTO takes it without a length threshold
@@ -244,6 +254,7 @@ extern "C" tq_status tq_dense_attention(const tq_rotation* rot, const void* k, c
   if ((kv_dtype != TQ_F32 && kv_dtype != TQ_F16) || (q_dtype != TQ_F32 && q_dtype != TQ_F16)) return TQ_EINVAL;
   if (batch <= 0 || capacity <= 0 || n_q_heads <= 0 || n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (!grid_fits(batch, n_q_heads, n_splits)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;
   if (capacity > TQ_MAX_CAPACITY) return TQ_ECAPACITY;  // 32-bit byte offsets within a stream's fp16 rows
   tq::DenseArgs a;
@@ -278,6 +289,7 @@ extern "C" tq_status tq_merge_splits(const tq_rotation* rot, int32_t n_splits, i
     if (st != TQ_OK) return st;
   }
   if (n_splits < 1 || batch <= 0 || n_q_heads <= 0) return TQ_EINVAL;
+  if ((int64_t)batch * n_q_heads > INT32_MAX) return TQ_EINVAL;  // one thread group per output row
   if (rot != nullptr && n_q_heads % rot->n_kv_heads != 0) return TQ_EINVAL;
   if (part_o == nullptr || part_lse == nullptr || out == nullptr) return TQ_EINVAL;
   tq::MergeArgs a;
@@ -431,6 +443,7 @@ static tq_status gtq_attention_args(const tq_gtq_head* heads, const float* rotat
   if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads != 0 || capacity <= 0)
     return TQ_EINVAL;
   if (n_splits < 1 || max_len < 0 || !std::isfinite(scale)) return TQ_EINVAL;
+  if (!grid_fits(batch, n_q_heads, n_splits)) return TQ_EINVAL;
   if (n_splits == 1 ? out == nullptr : (part_o == nullptr || part_lse == nullptr)) return TQ_EINVAL;
   if (code_bytes != 0 && !valid_gtq_code_bytes(code_bytes)) return TQ_EINVAL;
   if (max_len > capacity) return TQ_ECAPACITY;

@@ -121,8 +121,8 @@ typedef struct {
 typedef struct {
   void* codes;          /* device, layout above for `role` */
   float* norms;         /* device, layout above */
-  int32_t batch;
-  int32_t n_kv_heads;
+  int32_t batch;        /* 1 .. 32767 */
+  int32_t n_kv_heads;   /* 1 .. 65535, the rotation's */
   int32_t capacity;     /* tokens per (sequence, head); multiple of 32, <= TQ_MAX_CAPACITY */
   int32_t bits;         /* 3 or 4 */
   int32_t group;        /* must equal the rotation's group */
@@ -190,8 +190,9 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
  * carried by a token far below the softmax maximum (weight 1e-6 but a value norm 1e4 times
  * the others), that absolute score error becomes the row's relative error.  The VEC schedule
  * is fp32 throughout.
- * Errors: TQ_EINVAL for null pointers, bad dtypes, counts, scale or schedule, caches that
- * do not match the rotation or each other, or a missing output for the split count;
+ * Errors: TQ_EINVAL for null pointers, bad dtypes, counts (batch * n_q_heads * n_splits at
+ * most 2^31 - 1), scale or schedule, caches that do not match the rotation or each other, or
+ * a missing output for the split count;
  * TQ_ECAPACITY for max_len > capacity or capacity > TQ_MAX_CAPACITY; TQ_EUNSUPPORTED for
  * bits or groups outside 3/4 and 32/128. */
 tq_status tq_decode_attention(const tq_rotation* rot, const tq_cache* keys, const tq_cache* values,

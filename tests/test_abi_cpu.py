@@ -301,6 +301,18 @@ def test_capacity_limit(lib):
     assert lib.tq_gtq_attention(FAKE, FAKE, 64, FAKE, FAKE, FAKE, over, 1, 2, FAKE, 1, 8, None, 10, 0.1, 1, FAKE, None,
                                 FAKE, FAKE, None) == TQ_ECAPACITY
 
+def test_grid_limits(lib):
+    # counts that would not fit the launch grids are rejected on the host
+    rot = make_rot()
+    k, v = make_cache(tq.TQ_KEYS), make_cache(tq.TQ_VALUES)
+    assert append(rot, make_cache(tq.TQ_KEYS, batch=32768), n_new=0) == TQ_EINVAL
+    assert append(rot, make_cache(tq.TQ_KEYS, batch=32767), n_new=0) == TQ_OK
+    assert decode(rot, k, v, n_splits=1 << 30) == TQ_EINVAL        # 4 heads x 2^30 sections
+    assert append_decode(rot, k, v, n_splits=1 << 30) == TQ_EINVAL
+    assert dense(rot, n_splits=1 << 30) == TQ_EINVAL
+    assert lib.tq_merge_splits(None, 2, 1 << 16, 1 << 16, FAKE, FAKE, FAKE, None, None) == TQ_EINVAL
+
+
 def test_gtq_allocate_matches_oracle(lib):
     from oracle import blockgtq as bg
     rng = np.random.default_rng(7)
