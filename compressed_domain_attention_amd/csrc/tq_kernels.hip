@@ -1209,7 +1209,7 @@ __device__ __forceinline__ uint32_t upper_count(float a, const float* ub) {
   }
 }
 
-template <int BITS, int GROUP, bool VALUES, int NWV>
+template <int BITS, int GROUP, bool VALUES, int NWV, bool EXACT>
 __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, int h, int j_begin, int j_end,
                                                   uint8_t* rlds) {
   constexpr int NG = kHeadDim / GROUP;
@@ -1223,6 +1223,10 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
   const size_t stream = (size_t)b * a.n_kv_heads + h;
   const int ntile = a.capacity / kTile;
   const float gscale = GROUP == 32 ? 0.17677669529663688f : 0.088388347648318440f;
+  // EXACT (no SO(4) blocks): the rotation's entries are +-1/sqrt(g); stored as +-1 they are
+  // exact fp16 operands (the low parts vanish and their products are skipped), and 1/sqrt(g)
+  // joins the 1/norm scale of the results.
+  const float rscale = EXACT ? 1.f : gscale, yscale = EXACT ? gscale : 1.f;
   float ub[NU];
 #pragma unroll
   for (int k = 0; k < NU; ++k) ub[k] = a.boundary[HALF + k];
@@ -1260,7 +1264,7 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
           const int jj = (o & ~3) + c;
           r += (__builtin_popcount(jj & k & (GROUP - 1)) & 1) ? -mrow[c] : mrow[c];
         }
-        r *= a.signs[h * kHeadDim + k] * gscale;
+        r *= a.signs[h * kHeadDim + k] * rscale;
         const _Float16 rh = (_Float16)r;
         hw |= f16_bits(rh) << (16 * e);
         lw |= f16_bits((_Float16)(r - (float)rh)) << (16 * e);
@@ -1312,7 +1316,7 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
           }
         }
         const float nrm = sqrtf(rows_sum(s0 + s1));
-        inv[tb][g] = nrm > 0.f ? 1.0f / nrm : 0.f;
+        inv[tb][g] = nrm > 0.f ? yscale / nrm : 0.f;
         if (qg == g % 4)  // one row of lanes per group writes
           a.norms[(stream * ntile + j) * (NG * kTile) + g * kTile + norm_pos(16 * tb + col)] = nrm;
       }
@@ -1340,7 +1344,7 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
 #pragma unroll
       for (int s2 = 0; s2 < NKS; ++s2) {
         ahi[s2] = r_op(0, ob, s2);
-        alo[s2] = r_op(1, ob, s2);
+        if (!EXACT) alo[s2] = r_op(1, ob, s2);
       }
       vword[ob] = 0u;
 #pragma unroll
@@ -1351,10 +1355,10 @@ __device__ __forceinline__ void append_mfma_tiles(const AppendArgs& a, int b, in
           const int ks = GROUP == 128 ? s2 : ob >> 1;
           if (VALUES) {
             acc = mfma16(B[tb][ks], ahi[s2], acc);
-            acc = mfma16(B[tb][ks], alo[s2], acc);
+            if (!EXACT) acc = mfma16(B[tb][ks], alo[s2], acc);
           } else {
             acc = mfma16(ahi[s2], B[tb][ks], acc);
-            acc = mfma16(alo[s2], B[tb][ks], acc);
+            if (!EXACT) acc = mfma16(alo[s2], B[tb][ks], acc);
           }
         }
         uint32_t f = 0;
@@ -1451,23 +1455,24 @@ struct MfmaAppendShape {
 };
 
 // Whole tiles [j0, j0 + n_full) of every (sequence, KV head), per_wg tiles per workgroup.
-template <int BITS, int GROUP, bool VALUES>
+template <int BITS, int GROUP, bool VALUES, bool EXACT>
 __global__ __launch_bounds__(64 * MfmaAppendShape<GROUP>::kWaves, MfmaAppendShape<GROUP>::kPerCu) void append_mfma_kernel(
     const AppendArgs a, int j0, int n_full, int per_wg) {
   using S = MfmaAppendShape<GROUP>;
   __shared__ __attribute__((aligned(16))) uint8_t rlds[S::kLds];
   const int jb = j0 + blockIdx.x * per_wg;
-  append_mfma_tiles<BITS, GROUP, VALUES, S::kWaves>(a, blockIdx.z, blockIdx.y, jb, min(jb + per_wg, j0 + n_full), rlds);
+  append_mfma_tiles<BITS, GROUP, VALUES, S::kWaves, EXACT>(a, blockIdx.z, blockIdx.y, jb, min(jb + per_wg, j0 + n_full),
+                                                           rlds);
 }
 // Keys (grid z < batch) and values in one launch.
-template <int BK, int BV, int GROUP>
+template <int BK, int BV, int GROUP, bool EXACT>
 __global__ __launch_bounds__(64 * MfmaAppendShape<GROUP>::kWaves, MfmaAppendShape<GROUP>::kPerCu) void append_mfma_kv_kernel(
     const AppendArgs ak, const AppendArgs av, int batch, int j0, int n_full, int per_wg) {
   using S = MfmaAppendShape<GROUP>;
   __shared__ __attribute__((aligned(16))) uint8_t rlds[S::kLds];
   const int jb = j0 + blockIdx.x * per_wg, je = min(jb + per_wg, j0 + n_full);
-  if ((int)blockIdx.z < batch) append_mfma_tiles<BK, GROUP, false, S::kWaves>(ak, blockIdx.z, blockIdx.y, jb, je, rlds);
-  else append_mfma_tiles<BV, GROUP, true, S::kWaves>(av, blockIdx.z - batch, blockIdx.y, jb, je, rlds);
+  if ((int)blockIdx.z < batch) append_mfma_tiles<BK, GROUP, false, S::kWaves, EXACT>(ak, blockIdx.z, blockIdx.y, jb, je, rlds);
+  else append_mfma_tiles<BV, GROUP, true, S::kWaves, EXACT>(av, blockIdx.z - batch, blockIdx.y, jb, je, rlds);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1980,12 +1985,15 @@ hipError_t launch_append(const AppendArgs& a, int bits, int group, bool values, 
     int per_wg = 0;
     const dim3 mgrid(mfma_append_chunks(n_full, batch * a.n_kv_heads, group == 128 ? 2 : 3, per_wg), a.n_kv_heads,
                      batch);
-#define TQ_APPEND_M(B, G, V)                                                                          \
-  if (bits == B && group == G && values == V)                                                         \
-    hipLaunchKernelGGL((append_mfma_kernel<B, G, V>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, a, j0, \
+    const bool ex = a.so4 == nullptr;  // a rotation without SO(4) blocks: exact +-1 operands
+#define TQ_APPEND_M(B, G, V, E)                                                                          \
+  if (bits == B && group == G && values == V && ex == E)                                                 \
+    hipLaunchKernelGGL((append_mfma_kernel<B, G, V, E>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, a, j0, \
                        n_full, per_wg);
-    TQ_APPEND_M(3, 32, false) TQ_APPEND_M(3, 32, true) TQ_APPEND_M(3, 128, false) TQ_APPEND_M(3, 128, true)
-    TQ_APPEND_M(4, 32, false) TQ_APPEND_M(4, 32, true) TQ_APPEND_M(4, 128, false) TQ_APPEND_M(4, 128, true)
+#define TQ_APPEND_M2(B, G, V) TQ_APPEND_M(B, G, V, false) TQ_APPEND_M(B, G, V, true)
+    TQ_APPEND_M2(3, 32, false) TQ_APPEND_M2(3, 32, true) TQ_APPEND_M2(3, 128, false) TQ_APPEND_M2(3, 128, true)
+    TQ_APPEND_M2(4, 32, false) TQ_APPEND_M2(4, 32, true) TQ_APPEND_M2(4, 128, false) TQ_APPEND_M2(4, 128, true)
+#undef TQ_APPEND_M2
 #undef TQ_APPEND_M
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || edges.n_edges == 0) return e;
@@ -2029,12 +2037,15 @@ hipError_t launch_append_kv(const AppendArgs& ak, const AppendArgs& av, int bits
     int per_wg = 0;
     const dim3 mgrid(mfma_append_chunks(n_full, 2 * batch * ak.n_kv_heads, group == 128 ? 2 : 3, per_wg), ak.n_kv_heads,
                      2 * batch);
-#define TQ_APPEND_KV_M(BK, BV, G)                                                                              \
-  if (bits_k == BK && bits_v == BV && group == G)                                                             \
-    hipLaunchKernelGGL((append_mfma_kv_kernel<BK, BV, G>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, ak, \
+    const bool ex = ak.so4 == nullptr;  // a rotation without SO(4) blocks: exact +-1 operands
+#define TQ_APPEND_KV_M(BK, BV, G, E)                                                                              \
+  if (bits_k == BK && bits_v == BV && group == G && ex == E)                                                     \
+    hipLaunchKernelGGL((append_mfma_kv_kernel<BK, BV, G, E>), mgrid, dim3(64 * MfmaAppendShape<G>::kWaves), 0, stream, ak, \
                        av, batch, j0, n_full, per_wg);
-    TQ_APPEND_KV_M(3, 3, 32) TQ_APPEND_KV_M(3, 3, 128) TQ_APPEND_KV_M(4, 3, 32) TQ_APPEND_KV_M(4, 3, 128)
-    TQ_APPEND_KV_M(3, 4, 32) TQ_APPEND_KV_M(3, 4, 128) TQ_APPEND_KV_M(4, 4, 32) TQ_APPEND_KV_M(4, 4, 128)
+#define TQ_APPEND_KV_M2(BK, BV, G) TQ_APPEND_KV_M(BK, BV, G, false) TQ_APPEND_KV_M(BK, BV, G, true)
+    TQ_APPEND_KV_M2(3, 3, 32) TQ_APPEND_KV_M2(3, 3, 128) TQ_APPEND_KV_M2(4, 3, 32) TQ_APPEND_KV_M2(4, 3, 128)
+    TQ_APPEND_KV_M2(3, 4, 32) TQ_APPEND_KV_M2(3, 4, 128) TQ_APPEND_KV_M2(4, 4, 32) TQ_APPEND_KV_M2(4, 4, 128)
+#undef TQ_APPEND_KV_M2
 #undef TQ_APPEND_KV_M
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || ek.n_edges == 0) return e;
