@@ -567,22 +567,24 @@ __device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, 
 // ---------------------------------------------------------------------------------------
 // Matrix-core decode.
 //
-// Scores: for a 16-token tile, D[token][col] = sum_k A[token][k] B[k][col].  A holds key
-// codebook values decoded through LDS tables, B the rotated query, col = (norm group,
-// head) so that D holds per-group partial dots, which are scaled by the group norms and
-// summed across the group lanes.  The key codebook and the query are each split into an
-// fp16 high and low part; one A operand carries 4 codes as [hi x4 | lo x4] and is
-// multiplied by [q_hi x4 | q_hi x4] and by [q_lo x4 | 0 x4], which together give
-// (c_hi + c_lo) q_hi + c_hi q_lo: the score keeps fp32-level accuracy.
+// Scores: for a 16-token tile, D[token][col] = sum_k A[token][k] B[k][col].  A holds the
+// keys' codebook levels decoded through LDS tables, as fp16 numbers at the codebook's fp16
+// scale s (the levels c * s are fp16 values within 3e-5 relative for 3-bit codebooks, 1e-4
+// for 4-bit; the query carries 1/s).  B is the rotated query, prescaled by a power of two and
+// split into fp16 high and low parts: whole-head groups put the parts in columns c and c + 8
+// (one product per key operand); 32-coordinate groups use columns (group, head) and take one
+// product with each part, so D holds per-group partial dots, scaled by the group norms and
+// summed across the group lanes.
 // Values: O[coord][col] += sum_k A[coord][k] P'[k][col] over the 32 tokens of a tile, with
-// A = value codebook values (a value word holds 8 tokens of one coordinate) and P' = p *
-// value norm in fp16, taken straight from the score registers.  Online softmax per column.
+// A = value codebook levels (a value word holds 8 tokens of one coordinate) and P' = p *
+// value norm in fp16 (with a power-of-two range factor), taken straight from the score
+// registers.  Online softmax per column.
 //
-// Decode tables: an index of two codes (6 bits for 3-bit codes, 8 for 4-bit) selects an
-// entry holding the two fp16 values (keys: 8 bytes, the high parts then the low parts;
-// values: 4 bytes).  Every table is stored 32 times, copy c serving lanes c and c + 32, with
-// the copies of one entry side by side: the bank a lane reads is fixed by its lane number,
-// so data-dependent lookups never conflict (LDS serves 32 lanes per pass).
+// Decode tables: 3-bit keys and values sharing one codebook use a table indexed by four
+// codes (4096 entries of four fp16 levels); otherwise an index of two codes (6 bits for
+// 3-bit codes, 8 for 4-bit) selects an entry of two fp16 levels, stored in 32 copies (3-bit)
+// or 8 and 16 (4-bit keys and values), copy c serving lanes c, c + 32 ... with the copies of
+// one entry side by side, so that the bank a lane reads is fixed by its lane number.
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
                                                 0, 0);

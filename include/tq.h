@@ -185,11 +185,12 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
  * whenever a weight would pass 2^15 or all of the block's weights fall below 2^-10 (the sum
  * of the weights carries it too, so it cancels): any value norm up to about 2^100 keeps the
  * weights in fp16's range, and each block's largest weights at full fp16 precision.  Scores
- * carry the codebook's level error: up to about 1e-3 nats for keys and queries with 8x
- * outlier channels (lse errors up to 6e-4 were measured on such rows).  When an output row is
- * carried by a token far below the softmax maximum (weight 1e-6 but a value norm 1e4 times
- * the others), that absolute score error becomes the row's relative error.  The VEC schedule
- * is fp32 throughout.
+ * carry the codebook's level error, at most that relative error times scale * |q| * |k|:
+ * on keys and queries with 8x outlier channels (scores up to about 30) lse errors up to
+ * 9e-4 were measured with 3-bit keys and 1.7e-3 with 4-bit keys, and output rows up to
+ * 1.3e-3 off.  When an output row is carried by a token far below the softmax maximum
+ * (weight 1e-6 but a value norm 1e4 times the others), that absolute score error becomes the
+ * row's relative error.  The VEC schedule is fp32 throughout.
  * Errors: TQ_EINVAL for null pointers, bad dtypes, counts (batch * n_q_heads * n_splits at
  * most 2^31 - 1), scale or schedule, caches that do not match the rotation or each other, or
  * a missing output for the split count;

@@ -593,6 +593,58 @@ def test_decode_more_than_four_heads_per_kv_head(name, n_q_heads, schedule):
 
 
 @pytest.mark.parametrize("schedule", ["mfma", "vec"])
+@pytest.mark.parametrize("bits_k,bits_v,group_size,so4", [(4, 4, 1, True), (4, 3, 3, True), (3, 4, 8, False),
+                                                          (3, 3, 12, True), (4, 4, 16, False)])
+def test_whole_head_groups_bits_and_head_counts(bits_k, bits_v, group_size, so4, schedule):
+    # 128-coordinate groups with every pair of code widths (two-code tables for 4-bit codes,
+    # the shared four-code table for 3/3), with and without SO(4) blocks, and query groups of
+    # 1, 3, 8, 12 and 16 heads per KV head (one head slice of up to 8: partial, full, a full
+    # and a partial one, two); 10 sections of 4 rows x 8 KV heads give more workgroups than
+    # compute units (the four-wave instance), 1 and 3 sections the eight-wave one
+    from dataclasses import replace
+    w = replace(workloads.WORKLOADS["isoquant32k"], bits_k=bits_k, bits_v=bits_v, so4=so4,
+                n_q_heads=8 * group_size).with_len(150, batch=4)
+    inp = workloads.generate(w, 21)
+    print("case bits %d/%d G %d so4 %s" % (bits_k, bits_v, group_size, so4), flush=True)
+    t = w.seq_len
+    rot = device_rotation(w, inp)
+    k, v, oqk, oqv = oracle_caches(w, inp, round_up(t, 32))
+    q = torch.from_numpy(inp["q"]).cuda()
+    lens = np.array([t, 45, 0, 97], dtype=np.int32)
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    ref_out, ref_lse = oracle_decode(w, inp, kd, vd, lens)
+    seq = torch.from_numpy(lens).cuda()
+    # The matrix-core schedule holds the codebook levels as fp16 numbers (relative error at
+    # most 3e-5 for 3-bit and 1e-4 for 4-bit levels, checked on the CPU), so a score moves by
+    # at most that times scale * |q| * |k_hat| (Cauchy-Schwarz), and an lse by at most the
+    # largest such bound of its row: these inputs reach scores near 30, where that passes 1e-4.
+    eps = 3e-5 if bits_k == 3 else 1e-4
+    qn = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)                      # [B, Hq]
+    kmax = np.linalg.norm(kd, axis=-1).max(axis=-1).repeat(group_size, axis=1)      # [B, Hq]
+    lse_atol = 1e-4 + (eps * w.scale * qn * kmax if schedule == "mfma" else 0.0 * qn)
+    for n_splits in (1, 3, 10):
+        if n_splits == 1:
+            out, lse = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, schedule=schedule)
+        else:
+            po, pl = tq.decode_attention(rot, k, v, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
+            ref_po, ref_pl = oracle_decode(w, inp, kd, vd, lens, n_splits)
+            assert row_rel_err(po.cpu().numpy(), ref_po).max() <= OUT_RTOL
+            gp, live_s = pl.cpu().numpy(), np.isfinite(ref_pl)
+            assert np.array_equal(np.isfinite(gp), live_s)  # empty sections: -inf
+            assert np.all(np.abs(gp - ref_pl)[live_s] <= np.broadcast_to(lse_atol, ref_pl.shape)[live_s])
+            out, lse = tq.merge_splits(rot, po, pl)
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        assert not o[2].any() and np.all(l[2] == -np.inf)  # the empty row
+        live = [0, 1, 3]
+        err = row_rel_err(o[live], ref_out[live])
+        dl = np.abs(l[live] - ref_lse[live])
+        print("splits %d: max row rel err %.3e, lse err %.2e (bound %.2e)" % (n_splits, err.max(), dl.max(),
+                                                                          lse_atol[live].min()), flush=True)
+        assert err.max() <= OUT_RTOL
+        assert np.all(dl <= lse_atol[live])
+
+@pytest.mark.parametrize("schedule", ["mfma", "vec"])
 @pytest.mark.parametrize("t", [32, 511, 512, 513])
 def test_decode_both_schedules_around_the_pages_threshold(t, schedule):
     # the pages switch the value accumulation from word- to dimension-parallel at T = 512; here
