@@ -778,9 +778,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   }
 
   // ---- The small inputs (this wave's two query rows, the signs, the SO(4) parameters) are
-  // staged in LDS by direct copies issued ahead of the ring's, so that one counted wait
-  // covers them while the ring copies stay in flight (a register load would make the
-  // compiler wait for every outstanding copy).  The raw rows sit at the start of the
+  // staged in LDS by direct copies issued ahead of the ring's loads, so that one counted
+  // wait covers them while the ring's loads stay in flight (a register load would make the
+  // compiler wait for every outstanding load).  The raw rows sit at the start of the
   // wave's own two rows of qbuf, which it later overwrites with the rotated query.
   const uint32_t qraw = lds_addr(qbuf) + wv * (2 * kHeadDim * 4);
   {
@@ -1184,7 +1184,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
 // sign flips, H the Sylvester Hadamard on each g-block and M the SO(4) block matrix
 // (identity without SO(4)).  A tile of 32 tokens is one product of R with the tile's
 // vectors.  The fp16 vectors are exact operands; R is split into fp16 high and low parts,
-// so two products give the rotated values to about fp32 accuracy.  The workgroup builds R
+// so two products give the rotated values to about fp32 accuracy (without SO(4) blocks R's
+// entries are +-1/sqrt(g): stored as +-1 they are exact and one product suffices).  The
+// workgroup builds R
 // once, in LDS, already in matrix-core operand order (16 x 32 blocks of 64 lanes x 16
 // bytes: conflict-free reads; 32-groups keep only the diagonal blocks).  Each wave then
 // takes whole tiles on its own, loading the next tile's vectors during this one's
