@@ -1323,13 +1323,15 @@ def main():
         print(json.dumps({
             "metric": METRIC, "value": units / (r["step_ms"] / 1e3), "unit": "KV token·heads/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands (packed); f32 FMA (tail)",
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands, f32 accumulate (packed codes and fp16 tail rows; "
+                     "fp32 tail rows: f32 FMA)",
             "data": "synthetic (seeded Gaussian activations with outlier channels; workloads.py)",
             "config": {"workload": "%s+tail%d" % (w.name, args.tail), "n_splits": n_splits, "tail_tokens": args.tail,
                        "tail_splits": tail_splits, "tail_dtype": w.dtype,
                        "step": "append+decode launch, dense tail launch, merge", "cache_replicas": r["reps"]},
             "roofline": {"bound": "hbm", "achieved": dense_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dense_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "dense_kernel"},
+                         "frac": dense_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "dense_mfma_kernel" if w.dtype == "float16" else "dense_kernel"},
             "cpu_baseline": cpu, "dense_kernel_ms": r["dense_ms"], "tail_bytes_per_launch": r["tail_bytes"],
             "parity_worst_row_rel_err": r["parity"]}), flush=True)
         return
