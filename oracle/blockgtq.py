@@ -189,11 +189,6 @@ def unpack_codes(packed, enc=None):
     return out
 
 
-def key_record_bytes(n_groups, record_bytes=HEAD_DIM // 2):
-    """Stored bytes of one (token, KV head) key: the code bytes + one fp32 norm per group."""
-    return record_bytes + 4 * n_groups
-
-
 def rate_law_gain(s, b, i):
     """J(b) - J(b + e_i), the closed form (3/4) s_i 4^-b_i."""
     return 0.75 * float(s[i]) * 4.0 ** (-float(b[i]))
