@@ -242,3 +242,39 @@ def test_maximum_capacity_step():
     print("worst row error %.2e, lse %.2e" % (worst, worst_lse), flush=True)
     assert worst <= OUT_RTOL
     assert worst_lse <= 1e-4
+
+
+def test_prefill_call_past_the_matrix_core_limit():
+    # One call of 2^22 + 33 fp16 vectors per row (one sequence, one KV head, IsoQuant TQ3 with
+    # SO(4)) at slot 7: calls longer than 2^22 vectors per row are taken whole by the
+    # per-token kernel.  A seeded 4096-token block is repeated to that length; sampled slots
+    # at the start, the middle and the end match the oracle's codes and norms.
+    from dataclasses import replace
+    n = (1 << 22) + 33
+    pos0 = 7
+    cap = (pos0 + n + tq.TILE - 1) // tq.TILE * tq.TILE
+    w = replace(workloads.WORKLOADS["isoquant32k"], batch=1, n_q_heads=4, n_kv_heads=1, seq_len=4096)
+    announce("prefill of %d tokens" % n, w)
+    inp = workloads.generate(w, 3)
+    reps = (n + 4095) // 4096
+    kx = torch.from_numpy(inp["k"]).cuda().repeat(1, 1, reps, 1)[:, :, :n].contiguous()
+    vx = torch.from_numpy(inp["v"]).cuda().repeat(1, 1, reps, 1)[:, :, :n].contiguous()
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, torch.from_numpy(inp["so4"]).cuda())
+    kc = tq.PackedCache(1, 1, cap, w.bits_k, w.group, tq.TQ_KEYS)
+    vc = tq.PackedCache(1, 1, cap, w.bits_v, w.group, tq.TQ_VALUES)
+    tq.quantize_append_kv(rot, kc, vc, kx, vx, pos0=pos0)
+    torch.cuda.synchronize()
+    del kx, vx
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    part = lambda oq, idx: dict(oq, idx=oq["idx"][:, :, idx], norms=oq["norms"][:, :, idx], dist=oq["dist"][:, :, idx])
+    ntile = cap // tq.TILE
+    for tile in (0, 1, ntile // 2, ntile - 2, ntile - 1):
+        slots = np.arange(tile * tq.TILE, (tile + 1) * tq.TILE)
+        live = (slots >= pos0) & (slots < pos0 + n)
+        src = (slots - pos0) % 4096  # the input token each slot holds
+        kcodes = kc.codes[:, :, tile * tq.TILE:(tile + 1) * tq.TILE].cpu().numpy()
+        vcodes = vc.codes[:, :, tile:tile + 1].cpu().numpy()
+        for oq, codes, c, role in ((oqk, kcodes, kc, "k"), (oqv, vcodes, vc, "v")):
+            idx, nrm = unpack(codes, c.norms[:, :, tile:tile + 1].cpu().numpy(), oq["bits"], role)
+            check_codes(idx[:, :, live], nrm[:, :, live], part(oq, src[live]), int(live.sum()))
+            assert not idx[:, :, ~live].any() and not nrm[:, :, ~live].any()  # slots outside the call
