@@ -163,8 +163,17 @@ def _check(status, what):
         raise TQError(status, what)
 
 
+def _device_ptr(t, what="tensor"):
+    """The raw address of a tensor the kernels read or write: it must live on the current GPU
+    (a host address passed to a kernel would fault the device)."""
+    if not t.is_cuda or t.device.index != torch.cuda.current_device():
+        raise ValueError("%s must be on the current GPU (cuda:%d), not %s" % (
+            what, torch.cuda.current_device() if torch.cuda.is_available() else 0, t.device))
+    return t.data_ptr()
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else ctypes.c_void_p(_device_ptr(t))
 
 
 def _stream():
@@ -186,8 +195,12 @@ class Rotation:
         self.so4 = None if so4 is None else so4.contiguous().to(torch.float32)
         self.group = group
         self.n_kv_heads = self.signs.shape[0]
-        self.c = _Rotation(group, self.n_kv_heads, self.signs.data_ptr(),
-                           None if self.so4 is None else self.so4.data_ptr())
+        if self.signs.dim() != 2 or self.signs.shape[1] != HEAD_DIM:
+            raise ValueError("signs must be [n_kv_heads, %d]" % HEAD_DIM)
+        if self.so4 is not None and tuple(self.so4.shape) != (self.n_kv_heads, HEAD_DIM // 4, 2, 4):
+            raise ValueError("so4 must be [n_kv_heads, %d, 2, 4]" % (HEAD_DIM // 4))
+        self.c = _Rotation(group, self.n_kv_heads, _device_ptr(self.signs, "signs"),
+                           None if self.so4 is None else _device_ptr(self.so4, "so4"))
 
 
 class PackedCache:
@@ -201,15 +214,21 @@ class PackedCache:
         self.bits, self.group, self.role = bits, group, role
         self.codebook = codebook if codebook is not None else make_codebook(bits, group)
         ng = HEAD_DIM // group
+        shape = ((batch, n_kv_heads, capacity, 16 * bits) if role == TQ_KEYS
+                 else (batch, n_kv_heads, capacity // TILE, TILE * 16 * bits))
+        nshape = (batch, n_kv_heads, capacity // TILE, ng, TILE)
         if codes is None:
-            shape = ((batch, n_kv_heads, capacity, 16 * bits) if role == TQ_KEYS
-                     else (batch, n_kv_heads, capacity // TILE, TILE * 16 * bits))
             codes = torch.zeros(shape, dtype=torch.uint8, device=device)
         if norms is None:
-            norms = torch.zeros((batch, n_kv_heads, capacity // TILE, ng, TILE), dtype=torch.float32, device=device)
+            norms = torch.zeros(nshape, dtype=torch.float32, device=device)
+        # caller-supplied buffers: the kernels address them by the layout, so it must match
+        if codes.dtype != torch.uint8 or codes.numel() != math.prod(shape) or not codes.is_contiguous():
+            raise ValueError("codes must be a contiguous uint8 tensor of %s elements" % (shape,))
+        if norms.dtype != torch.float32 or norms.numel() != math.prod(nshape) or not norms.is_contiguous():
+            raise ValueError("norms must be a contiguous float32 tensor of %s elements" % (nshape,))
         self.codes, self.norms = codes, norms
-        self.c = _Cache(codes.data_ptr(), norms.data_ptr(), batch, n_kv_heads, capacity, bits, group, role,
-                        self.codebook)
+        self.c = _Cache(_device_ptr(codes, "codes"), _device_ptr(norms, "norms"), batch, n_kv_heads, capacity, bits,
+                        group, role, self.codebook)
 
 
 def quantize_append(rot: Rotation, cache: PackedCache, x: torch.Tensor, pos: torch.Tensor = None, pos0: int = 0,

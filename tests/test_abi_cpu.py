@@ -515,3 +515,23 @@ def test_product_path_has_no_cpu_fallback():
     # the binding must not reach the oracle or any CPU computation
     src = open(os.path.join(ROOT, "compressed_domain_attention_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("NativeLibraryMissing", "")
+
+
+def test_binding_rejects_host_tensors_and_wrong_buffers(lib):
+    # the binding hands raw addresses to the kernels: host tensors and caller buffers that do
+    # not match the cache layout are refused before any call
+    import torch
+    with pytest.raises(ValueError, match="current GPU"):
+        tq.PackedCache(1, 2, 64, 3, 32, tq.TQ_KEYS, device="cpu")
+    with pytest.raises(ValueError, match="current GPU"):
+        tq.Rotation(torch.ones(2, 128), 32)
+    with pytest.raises(ValueError, match="signs must be"):
+        tq.Rotation(torch.ones(2, 64), 32)
+    with pytest.raises(ValueError, match="so4 must be"):
+        tq.Rotation(torch.ones(2, 128), 128, torch.zeros(2, 16, 2, 4))
+    with pytest.raises(ValueError, match="codes must be"):
+        tq.PackedCache(1, 2, 64, 3, 32, tq.TQ_KEYS, codes=torch.zeros(1, 2, 32, 48, dtype=torch.uint8),
+                       norms=torch.zeros(1, 2, 2, 4, 32))
+    with pytest.raises(ValueError, match="norms must be"):
+        tq.PackedCache(1, 2, 64, 3, 32, tq.TQ_KEYS, codes=torch.zeros(1, 2, 64, 48, dtype=torch.uint8),
+                       norms=torch.zeros(1, 2, 2, 4, 32, dtype=torch.float64))
