@@ -176,6 +176,34 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(_device_ptr(t))
 
 
+def _need(t, shape, dtypes, name):
+    """Refuse a tensor that the call would address in another size, type or layout."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s, not %s %s" % (
+            name, "/".join(str(d).replace("torch.", "") for d in dtypes), tuple(shape),
+            str(t.dtype).replace("torch.", ""), tuple(t.shape)))
+
+
+def _outputs(n_splits, bsz, hq, dev, out, lse, part_o, part_lse):
+    """The attention calls' outputs: caller buffers checked, missing ones allocated."""
+    f32 = (torch.float32,)
+    if n_splits == 1:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
+        _need(out, (bsz, hq, HEAD_DIM), f32, "out")
+        _need(lse, (bsz, hq), f32, "lse")
+    else:
+        if part_o is None:
+            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+        _need(part_o, (n_splits, bsz, hq, HEAD_DIM), f32, "part_o")
+        _need(part_lse, (n_splits, bsz, hq), f32, "part_lse")
+    return out, lse, part_o, part_lse
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -236,7 +264,9 @@ def quantize_append(rot: Rotation, cache: PackedCache, x: torch.Tensor, pos: tor
     """Quantise x [batch, n_kv_heads, n_new, 128] (fp16/fp32) into slots pos.. of the cache."""
     if x.dtype not in _DTYPES or not x.is_contiguous():
         raise ValueError("x must be a contiguous float16/float32 tensor")
-    n_new = x.shape[2]
+    n_new = x.shape[2] if x.dim() == 4 else -1
+    _need(x, (cache.batch, cache.n_kv_heads, n_new, HEAD_DIM), tuple(_DTYPES), "x")
+    _need(pos, (cache.batch,), (torch.int32,), "pos")
     if max_pos is None:
         max_pos = int(pos.max().item()) if pos is not None else pos0
     _check(library().tq_quantize_append(ctypes.byref(rot.c), ctypes.byref(cache.c), _ptr(x), _DTYPES[x.dtype],
@@ -251,6 +281,9 @@ def quantize_append_kv(rot: Rotation, keys: PackedCache, values: PackedCache, xk
             raise ValueError("xk and xv must be contiguous float16/float32 tensors")
     if xk.dtype != xv.dtype or xk.shape != xv.shape:
         raise ValueError("xk and xv must have the same dtype and shape")
+    n_new = xk.shape[2] if xk.dim() == 4 else -1
+    _need(xk, (keys.batch, keys.n_kv_heads, n_new, HEAD_DIM), tuple(_DTYPES), "xk")
+    _need(pos, (keys.batch,), (torch.int32,), "pos")
     if max_pos is None:
         max_pos = int(pos.max().item()) if pos is not None else pos0
     _check(library().tq_quantize_append_kv(ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c),
@@ -264,22 +297,14 @@ def decode_attention(rot: Rotation, keys: PackedCache, values: PackedCache, q: t
     """One decode step.  n_splits == 1 -> (out, lse); n_splits > 1 -> (part_o, part_lse)."""
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
-    bsz, hq = q.shape[0], q.shape[1]
+    bsz, hq = keys.batch, q.shape[1] if q.dim() == 3 else -1
+    _need(q, (bsz, hq, HEAD_DIM), tuple(_DTYPES), "q")
+    _need(seq_lens, (bsz,), (torch.int32,), "seq_lens")
     if max_len is None:
         max_len = int(seq_lens.max().item()) if seq_lens is not None else keys.capacity
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        if out is None:
-            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if lse is None:
-            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_decode_attention(
         ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(q), _DTYPES[q.dtype], hq,
         _ptr(seq_lens), max_len, scale, n_splits, _SCHEDULES[schedule], _ptr(out), _ptr(lse), _ptr(part_o),
@@ -300,22 +325,17 @@ def append_decode_attention(rot: Rotation, keys: PackedCache, values: PackedCach
         raise ValueError("xk and xv must have the same dtype and shape, one token per stream")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    _need(xk, (keys.batch, keys.n_kv_heads, 1, HEAD_DIM), tuple(_DTYPES), "xk")
+    _need(q, (keys.batch, q.shape[1] if q.dim() == 3 else -1, HEAD_DIM), tuple(_DTYPES), "q")
+    _need(pos, (keys.batch,), (torch.int32,), "pos")
     if max_pos is None:
         max_pos = int(pos.max().item()) if pos is not None else pos0
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        if out is None:
-            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if lse is None:
-            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_append_decode_attention(
         ctypes.byref(rot.c), ctypes.byref(keys.c), ctypes.byref(values.c), _ptr(xk), _ptr(xv), _DTYPES[xk.dtype],
         _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits, _SCHEDULES[schedule], _ptr(out),
@@ -340,6 +360,11 @@ def append_decode_attention_static(rot: Rotation, keys: PackedCache, values: Pac
         raise ValueError("xk and xv must have the same dtype and shape, one token per stream")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    _need(xk, (keys.batch, keys.n_kv_heads, 1, HEAD_DIM), tuple(_DTYPES), "xk")
+    _need(q, (keys.batch, q.shape[1] if q.dim() == 3 else -1, HEAD_DIM), tuple(_DTYPES), "q")
+    _need(pos, (keys.batch,), (torch.int32,), "pos")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     if tuple(out.shape) != (bsz, hq, HEAD_DIM) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be contiguous float32 [batch, n_q_heads, 128]")
@@ -368,6 +393,8 @@ def dense_attention(rot: Rotation, k: torch.Tensor, v: torch.Tensor, q: torch.Te
         raise ValueError("k and v must have the same dtype and shape")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     if k.shape[0] != bsz or k.shape[1] != rot.n_kv_heads:
         raise ValueError("k and v must be [batch, n_kv_heads, capacity, 128] for this query and rotation")
@@ -394,11 +421,17 @@ def dense_attention(rot: Rotation, k: torch.Tensor, v: torch.Tensor, q: torch.Te
 def merge_splits(rot, part_o: torch.Tensor, part_lse: torch.Tensor, out=None, lse=None):
     """Log-sum-exp merge of split partials and the inverse rotation -> (out, lse).  rot=None
     merges partials of the original domain (zip_attention's) with no rotation."""
+    if part_lse.dim() != 3:
+        raise ValueError("part_lse must be [n_splits, batch, n_q_heads]")
     n_splits, bsz, hq = part_lse.shape
+    _need(part_o, (n_splits, bsz, hq, HEAD_DIM), (torch.float32,), "part_o")
+    _need(part_lse, (n_splits, bsz, hq), (torch.float32,), "part_lse")
     if out is None:
         out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=part_o.device)
     if lse is None:
         lse = torch.empty((bsz, hq), dtype=torch.float32, device=part_o.device)
+    _need(out, (bsz, hq, HEAD_DIM), (torch.float32,), "out")
+    _need(lse, (bsz, hq), (torch.float32,), "lse")
     _check(library().tq_merge_splits(None if rot is None else ctypes.byref(rot.c), n_splits, bsz, hq,
                                      _ptr(part_o), _ptr(part_lse),
                                      _ptr(out), _ptr(lse), _stream()), "tq_merge_splits")
@@ -446,6 +479,8 @@ def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=
     otherwise (part_o, part_lse) in the original domain, for merge_splits(None, ...)."""
     if q.dtype not in _ZIP_Q_DTYPES or not q.is_contiguous() or q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be contiguous [batch, n_q_heads, 128] float32/float16/bfloat16")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     for t in (k_tail, v_tail):
         if t.dtype != torch.bfloat16 or t.dim() != 4 or t.shape[3] != HEAD_DIM or not t.is_contiguous():
@@ -464,17 +499,7 @@ def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=
         max_len = int(seq_lens.max().item()) if seq_lens is not None else ZIP_PAGE * pages
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        if out is None:
-            out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if lse is None:
-            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_zip_attention(
         _ptr(k_store), _ptr(k_meta), _ptr(v_store), _ptr(v_meta), pages, _ptr(k_tail), _ptr(v_tail),
         k_tail.shape[2], bsz, hkv, _ptr(q), _ZIP_Q_DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits,
@@ -595,6 +620,8 @@ def gtq_attention(enc: GtqKeys, codes, norms, v, q, seq_lens=None, max_len=None,
         raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
     if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
@@ -606,15 +633,7 @@ def gtq_attention(enc: GtqKeys, codes, norms, v, q, seq_lens=None, max_len=None,
         max_len = int(seq_lens.max().item()) if seq_lens is not None else cap
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
-        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_gtq_attention(
         _ptr(enc.heads), _ptr(enc.rotations), enc.code_bytes, _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(q),
         _DTYPES[q.dtype], hq, _ptr(seq_lens), max_len, scale, n_splits, _ptr(out), _ptr(lse), _ptr(part_o),
@@ -632,6 +651,8 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
         raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
     if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
@@ -647,15 +668,7 @@ def gtq_append_attention(enc: GtqKeys, codes, norms, v, k_new, v_new, q, pos=Non
         max_pos = int(pos.max().item()) if pos is not None else pos0
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
-        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_gtq_append_attention(
         _ptr(enc.heads), _ptr(enc.rotations), enc.code_bytes, _ptr(codes), _ptr(norms), _ptr(v), cap, bsz, hkv, _ptr(k_new),
         _ptr(v_new), _DTYPES[k_new.dtype], _ptr(pos), pos0, max_pos, _ptr(q), _DTYPES[q.dtype], hq, scale, n_splits,
@@ -692,6 +705,8 @@ def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_le
         raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
     if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
@@ -703,15 +718,7 @@ def qjl_attention(enc: QjlKeys, codes, norms, signs, v, q, seq_lens=None, max_le
         max_len = int(seq_lens.max().item()) if seq_lens is not None else cap
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
-        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_gtq_qjl_attention(
         _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), enc.mse_bits, _ptr(codes), _ptr(norms), _ptr(signs),
         _ptr(v), cap,
@@ -729,6 +736,8 @@ def qjl_append_attention(enc: QjlKeys, codes, norms, signs, v, k_new, v_new, q, 
         raise ValueError("v must be contiguous float16 [batch, n_kv_heads, capacity, 128]")
     if q.dtype not in _DTYPES or not q.is_contiguous():
         raise ValueError("q must be a contiguous float16/float32 tensor")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     hkv, cap = v.shape[1], v.shape[2]
     if v.shape[0] != bsz or hkv != enc.n_kv_heads or tuple(codes.shape) != (bsz, hkv, cap, enc.code_bytes) or \
@@ -744,15 +753,7 @@ def qjl_append_attention(enc: QjlKeys, codes, norms, signs, v, k_new, v_new, q, 
         max_pos = int(pos.max().item()) if pos is not None else pos0
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = q.device
-    if n_splits == 1:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev) if out is None else out
-        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    else:
-        if part_o is None:
-            part_o = torch.empty((n_splits, bsz, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        if part_lse is None:
-            part_lse = torch.empty((n_splits, bsz, hq), dtype=torch.float32, device=dev)
+    out, lse, part_o, part_lse = _outputs(n_splits, bsz, hq, q.device, out, lse, part_o, part_lse)
     _check(library().tq_gtq_qjl_append_attention(
         _ptr(enc.heads), _ptr(enc.rotations), _ptr(enc.proj), enc.mse_bits, _ptr(codes), _ptr(norms), _ptr(signs),
         _ptr(v), cap,

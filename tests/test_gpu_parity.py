@@ -658,3 +658,38 @@ def test_decode_both_schedules_around_the_pages_threshold(t, schedule):
     torch.cuda.synchronize()
     assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+def test_binding_refuses_mismatched_buffers():
+    # buffers the kernels would address past their end, or in another type, are refused by the
+    # binding before any launch (host-side checks only; nothing runs on the device)
+    w, inp = setup("gqa8k", seq_len=64, batch=2)
+    rot = device_rotation(w, inp)
+    k, v = empty_caches(w, 64)
+    q = torch.from_numpy(inp["q"]).cuda()
+    x = torch.from_numpy(inp["k"]).cuda()
+    bad = [
+        lambda: tq.decode_attention(rot, k, v, q[:1]),                                    # fewer rows than the cache
+        lambda: tq.decode_attention(rot, k, v, q[..., :64].contiguous()),                 # not 128 wide
+        lambda: tq.decode_attention(rot, k, v, q, seq_lens=torch.zeros(1, dtype=torch.int32, device="cuda")),
+        lambda: tq.decode_attention(rot, k, v, q, seq_lens=torch.zeros(2, dtype=torch.int64, device="cuda")),
+        lambda: tq.decode_attention(rot, k, v, q, out=torch.empty(2, w.n_q_heads, 64, device="cuda")),
+        lambda: tq.decode_attention(rot, k, v, q, n_splits=3, part_o=torch.empty(2, 2, w.n_q_heads, 128, device="cuda")),
+        lambda: tq.quantize_append(rot, k, x[:1].contiguous()),                           # fewer rows
+        lambda: tq.quantize_append(rot, k, x, pos=torch.zeros(3, dtype=torch.int32, device="cuda")),
+        lambda: tq.quantize_append_kv(rot, k, v, x[:, :1].contiguous(), x[:, :1].contiguous()),  # fewer KV heads
+        lambda: tq.append_decode_attention(rot, k, v, x[:, :, :1].contiguous(), x[:, :, :1].contiguous(), q[:1],
+                                           pos0=10),
+        lambda: tq.merge_splits(rot, torch.empty(3, 2, w.n_q_heads, 128, device="cuda"),
+                                torch.empty(3, 2, w.n_q_heads + 1, device="cuda")),
+        lambda: tq.decode_attention(rot, k, v, q.cpu()),                                  # host memory
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+        torch.cuda.synchronize()
+    # the well-formed call still runs
+    tq.quantize_append_kv(rot, k, v, x, torch.from_numpy(inp["v"]).cuda())
+    out, lse = tq.decode_attention(rot, k, v, q, max_len=64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
