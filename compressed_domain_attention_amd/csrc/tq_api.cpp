@@ -1,5 +1,6 @@
 // C ABI of the packed-KV decode attention library: argument checks on the host, then one
-// launch per call on the caller's stream.  No allocation, no global state.
+// launch per call on the caller's stream.  No allocation; the only state is per-device (the
+// compute-unit count, and the static partial buffer's address).
 #include <cmath>
 #include <cstdint>
 #include <cstring>

@@ -3,8 +3,10 @@
  * bit-packed KV cache (3- or 4-bit codes), for AMD Instinct MI355X (gfx950).
  *
  * C ABI.  Every pointer marked "device" is device memory owned by the caller; the library
- * never allocates or frees memory, keeps no global state and launches everything on the
- * HIP stream it is given (passed as void* = hipStream_t, NULL = default stream).  Calls
+ * never allocates or frees memory and launches everything on the HIP stream it is given
+ * (passed as void* = hipStream_t, NULL = default stream).  Its only state: each device's
+ * compute-unit count, read once (a thread-safe cache), and the static partial buffer of
+ * tq_append_decode_attention_static with its per-device address.  Calls
  * return without synchronising.  Argument errors are detected on the host before any
  * launch: the call then returns TQ_EINVAL / TQ_EUNSUPPORTED / TQ_ECAPACITY and writes
  * nothing.  A failed launch returns TQ_EHIP.  No C++ exception crosses this boundary.
