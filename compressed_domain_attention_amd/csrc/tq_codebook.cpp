@@ -233,6 +233,7 @@ extern "C" const char* tq_status_string(tq_status s) {
     case TQ_EUNSUPPORTED: return "unsupported configuration";
     case TQ_ECAPACITY: return "cache capacity exceeded";
     case TQ_EHIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }

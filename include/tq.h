@@ -61,17 +61,21 @@ extern "C" {
 /* Tokens per (sequence, head) of any cache: byte offsets within one stream stay 32-bit. */
 #define TQ_MAX_CAPACITY (1 << 24)
 
+/* Every enum below ends with a *_MAX_ENUM member: it gives the type the range of a 32-bit
+ * int, so that any value a caller passes (an invalid one included, which the calls reject
+ * with TQ_EINVAL) is a defined value of the type. */
 typedef enum {
   TQ_OK = 0,
   TQ_EINVAL = 1,        /* null pointer, bad size or inconsistent arguments */
   TQ_EUNSUPPORTED = 2,  /* valid but not implemented (bits, group, head grouping) */
   TQ_ECAPACITY = 3,     /* a write or read would pass the cache capacity, or a capacity above TQ_MAX_CAPACITY */
-  TQ_EHIP = 4           /* a HIP launch or runtime call failed */
+  TQ_EHIP = 4,          /* a HIP launch or runtime call failed */
+  TQ_STATUS_MAX_ENUM = 0x7FFFFFFF
 } tq_status;
 
 /* TQ_BF16 is accepted only where a declaration says so (the compressed BF16 cache). */
-typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
-typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2, TQ_DTYPE_MAX_ENUM = 0x7FFFFFFF } tq_dtype;
+typedef enum { TQ_KEYS = 0, TQ_VALUES = 1, TQ_ROLE_MAX_ENUM = 0x7FFFFFFF } tq_role;
 
 /* Decode schedules.  MFMA: scores and value sum as matrix-core products of fp16
  * operands with fp32 accumulation (the key codebook scaled to be nearly fp16-exact, see
@@ -79,7 +83,12 @@ typedef enum { TQ_KEYS = 0, TQ_VALUES = 1 } tq_role;
  * scores and dimension-parallel value sum.  AUTO picks MFMA: measured on MI355X it is faster at
  * every cache length from 32 to 8192 tokens, for 1, 4 and 8 query heads per KV head and both
  * rotation groups (2x at 32 tokens, growing to 28-48x at 8192), so no length threshold applies. */
-typedef enum { TQ_SCHEDULE_AUTO = 0, TQ_SCHEDULE_VEC = 1, TQ_SCHEDULE_MFMA = 2 } tq_schedule;
+typedef enum {
+  TQ_SCHEDULE_AUTO = 0,
+  TQ_SCHEDULE_VEC = 1,
+  TQ_SCHEDULE_MFMA = 2,
+  TQ_SCHEDULE_MAX_ENUM = 0x7FFFFFFF
+} tq_schedule;
 
 /* Static description of an error code (never NULL). */
 const char* tq_status_string(tq_status s);
