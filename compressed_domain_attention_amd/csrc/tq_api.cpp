@@ -40,7 +40,8 @@ tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 // Attention launches one workgroup per (row, KV head, section, head slice), at most one per
 // (row, query head, section): that count must fit a one-dimensional grid.
 bool grid_fits(int32_t batch, int32_t n_q_heads, int32_t n_splits) {
-  return (int64_t)batch * n_q_heads * n_splits <= INT32_MAX;
+  // the counts are positive (checked before); the product of two fits 64 bits, the third divides
+  return (int64_t)batch * n_q_heads <= INT32_MAX / n_splits;
 }
 
 // Host checks shared by the append calls; fills the launch arguments of one cache.
@@ -352,8 +353,8 @@ extern "C" tq_status tq_zip_attention(const uint8_t* k_store, const uint8_t* k_m
   if ((int64_t)store_pages * tq::kZipSlot > 0xFFFFFFFFll) return TQ_ECAPACITY;
   if ((int64_t)max_len > (int64_t)tq::kZipPage * store_pages + tq::kZipPage - 1) return TQ_ECAPACITY;
   if (store_pages == 0 && max_len > tail_rows) return TQ_ECAPACITY;
+  if (!grid_fits(batch, n_q_heads, n_splits)) return TQ_EINVAL;
   const int hps = group <= 4 ? group : 8;
-  if ((int64_t)batch * n_kv_heads * n_splits * ((group + hps - 1) / hps) > 0x7FFFFFFFll) return TQ_EINVAL;
   tq::ZipAttnArgs a;
   std::memset(&a, 0, sizeof(a));
   a.k_store = k_store;
