@@ -199,7 +199,8 @@ tq_status tq_quantize_append_kv(const tq_rotation* rot, const tq_cache* keys, co
  * carry the codebook's level error, at most that relative error times scale * |q| * |k|:
  * on keys and queries with 8x outlier channels (scores up to about 30) lse errors up to
  * 9e-4 were measured with 3-bit keys and 1.7e-3 with 4-bit keys, and output rows up to
- * 1.3e-3 off.  When an output row is carried by a token far below the softmax maximum
+ * 1.3e-3 off; with two 10x channels shared by queries and keys (scores near 90) output rows
+ * reach 2-3e-3.  For such inputs the VEC schedule (fp32 levels) keeps rows near 1e-5.  When an output row is carried by a token far below the softmax maximum
  * (weight 1e-6 but a value norm 1e4 times the others), that absolute score error becomes the
  * row's relative error.  The VEC schedule is fp32 throughout.
  * Errors: TQ_EINVAL for null pointers, bad dtypes, counts (batch * n_q_heads * n_splits at
