@@ -62,14 +62,16 @@ def dequantized(w, inp, oq):
     return out
 
 
-def check_codes(got_idx, got_norms, oq, t):
-    """Assert the code and norm bar; returns the number of excused near-boundary flips."""
+def check_codes(got_idx, got_norms, oq, t, rate_bar=True):
+    """Assert the code and norm bar; returns the number of excused near-boundary flips.
+    rate_bar=False leaves the flip rate to the caller (which pools it over several cases)."""
     ref, dist = oq["idx"], oq["dist"]
     g = got_idx[:, :, :t]
     diff = g != ref
     flips = int(diff.sum())
     assert np.all(dist[diff] < CODE_BOUNDARY_EPS), "code mismatch away from a boundary"
-    assert flips <= CODE_FLIP_FRACTION * ref.size + 0, "too many near-boundary flips: %d" % flips
+    if rate_bar:
+        assert flips <= CODE_FLIP_FRACTION * ref.size + 0, "too many near-boundary flips: %d" % flips
     n_ref = oq["norms"].astype(np.float64)
     n_got = got_norms[:, :, :t].astype(np.float64)
     zero = n_ref == 0

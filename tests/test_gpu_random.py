@@ -1,0 +1,109 @@
+"""Seeded random configurations of the packed cache through the C ABI against the oracle.
+
+Each case draws a rotation group (32 or 128) with or without SO(4) blocks, key and value
+code widths (3 or 4 bits), 1-3 KV heads with 1-12 query heads each, 1-3 rows of ragged
+lengths (an empty one now and then) in a cache of up to 300 tokens, fp16 or fp32 inputs
+and queries, 1-16 key-axis sections and the schedule.  The cache is filled by two append
+calls (a cut at a random position, so that partial tiles and the matrix-core whole-tile
+path meet), its codes and norms are checked against the oracle's, and the decode (with the
+merge when sectioned) against fp64 attention over the oracle's dequantised cache."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_domain_attention_amd as tq
+import workloads
+from helpers import CODE_FLIP_FRACTION, OUT_RTOL, check_codes, dequantized, oracle_decode, oracle_quantize, round_up, row_rel_err, unpack
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 32
+FLIPS = {"flips": 0, "coords": 0, "cases": 0}  # pooled over the cases of one session
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.library()
+
+
+def draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    group = int(rng.choice([32, 128]))
+    hkv, g = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 4, 5, 8, 12]))
+    t = int(rng.integers(1, 301))
+    w = replace(workloads.WORKLOADS["isoquant32k"], batch=int(rng.integers(1, 4)), n_kv_heads=hkv, n_q_heads=g * hkv,
+                seq_len=t, bits_k=int(rng.choice([3, 4])), bits_v=int(rng.choice([3, 4])), group=group,
+                so4=bool(rng.integers(0, 2)), dtype=str(rng.choice(["float16", "float32"])))
+    lens = rng.integers(0, t + 1, size=w.batch).astype(np.int32)
+    lens[int(rng.integers(0, w.batch))] = t
+    cut = int(rng.integers(0, t + 1))
+    n_splits = int(rng.choice([1, 2, 3, 7, 16]))
+    schedule = str(rng.choice(["auto", "auto", "vec"]))
+    q_dtype = str(rng.choice(["float16", "float32"]))
+    return w, lens, cut, n_splits, schedule, q_dtype
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_configuration(seed):
+    w, lens, cut, n_splits, schedule, q_dtype = draw(seed)
+    print("random case %d: B=%d Hq=%d Hkv=%d T=%d bits %d/%d g=%d so4=%s %s q %s lens %s cut %d S=%d %s" % (
+        seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.bits_k, w.bits_v, w.group, w.so4, w.dtype, q_dtype,
+        list(lens), cut, n_splits, schedule), flush=True)
+    inp = workloads.generate(w, seed)
+    t, cap = w.seq_len, round_up(w.seq_len, 32) + 32 * (seed % 2)
+    so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).cuda()
+    rot = tq.Rotation(torch.from_numpy(inp["signs"]).cuda(), w.group, so4)
+    kc = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_k, w.group, tq.TQ_KEYS)
+    vc = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES)
+    kx, vx = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    if cut > 0:
+        tq.quantize_append_kv(rot, kc, vc, kx[:, :, :cut].contiguous(), vx[:, :, :cut].contiguous(), pos0=0)
+    if cut < t:
+        tq.quantize_append_kv(rot, kc, vc, kx[:, :, cut:].contiguous(), vx[:, :, cut:].contiguous(), pos0=cut)
+    q = torch.from_numpy(inp["q"].astype(np.float32)).cuda().to(getattr(torch, q_dtype))
+    seq = torch.from_numpy(lens).cuda()
+    if n_splits == 1:
+        out, lse = tq.decode_attention(rot, kc, vc, q, seq_lens=seq, max_len=t, schedule=schedule)
+    else:
+        po, pl = tq.decode_attention(rot, kc, vc, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
+        out, lse = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    # the cache against the oracle's codes and norms
+    oqk, oqv = oracle_quantize(w, inp, "k"), oracle_quantize(w, inp, "v")
+    for oq, c, role in ((oqk, kc, "k"), (oqv, vc, "v")):
+        idx, nrm = unpack(c.codes.cpu().numpy(), c.norms.cpu().numpy(), c.bits, role)
+        # every differing code lies within 1e-6 of a boundary; the rate is pooled over the cases
+        FLIPS["flips"] += check_codes(idx, nrm, oq, t, rate_bar=False)
+        FLIPS["coords"] += oq["idx"].size
+    # attention against fp64 attention over the oracle's cache
+    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    qq = dict(inp, q=q.float().cpu().numpy())
+    ref, ref_lse = oracle_decode(w, qq, kd, vd, lens)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    empty = lens == 0
+    assert not o[empty].any() and np.all(l[empty] == -np.inf)
+    live = ~empty
+    err = row_rel_err(o[live], ref[live])
+    # lse: the matrix-core schedule's fp16 key levels move a score by at most their relative
+    # error (3e-5 for 3-bit, 1e-4 for 4-bit levels) times scale * |q| * max |k_hat| of the row
+    eps = 0.0 if schedule == "vec" else (3e-5 if w.bits_k == 3 else 1e-4)
+    kmax = np.linalg.norm(kd, axis=-1).max(axis=-1).repeat(w.group_size, axis=1)
+    bound = 1e-4 + 1e-5 * np.abs(ref_lse) + eps * w.scale * np.linalg.norm(qq["q"].astype(np.float64), axis=-1) * kmax
+    dl = np.abs(l[live] - ref_lse[live])
+    print("   max row rel err %.2e, lse err %.2e" % (err.max(initial=0), dl.max(initial=0)), flush=True)
+    assert err.max(initial=0) <= OUT_RTOL
+    assert np.all(dl <= bound[live])
+    FLIPS["cases"] += 1
+
+
+def test_random_configurations_flip_rate():
+    # the code bar's rate (near-boundary flips at most 1e-5 of all coordinates) over every case
+    # of the session: a single case of 60 thousand coordinates cannot hold a rate of 1e-5
+    if FLIPS["cases"] < N_CASES:
+        pytest.skip("the rate is pooled over all %d random cases of one run" % N_CASES)
+    print("near-boundary flips: %d of %d coordinates" % (FLIPS["flips"], FLIPS["coords"]), flush=True)
+    assert FLIPS["flips"] <= CODE_FLIP_FRACTION * FLIPS["coords"]
