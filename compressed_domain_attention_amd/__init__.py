@@ -479,8 +479,6 @@ def zip_attention(k_store, k_meta, v_store, v_meta, k_tail, v_tail, q, seq_lens=
     otherwise (part_o, part_lse) in the original domain, for merge_splits(None, ...)."""
     if q.dtype not in _ZIP_Q_DTYPES or not q.is_contiguous() or q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be contiguous [batch, n_q_heads, 128] float32/float16/bfloat16")
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
-        raise ValueError("q must be [batch, n_q_heads, 128]")
     bsz, hq = q.shape[0], q.shape[1]
     for t in (k_tail, v_tail):
         if t.dtype != torch.bfloat16 or t.dim() != 4 or t.shape[3] != HEAD_DIM or not t.is_contiguous():

@@ -1,8 +1,10 @@
-"""Seeded random configurations of the unquantised region, Block-GTQ keys and two-stage keys
-through the C ABI against the oracle: head counts and groupings, ragged rows (an empty one
-now and then), section counts, dtypes and, for Block-GTQ, the width range and bit budget of
-the allocation.  Block-GTQ and two-stage keys are encoded by the library in two calls cut at a
-random slot and compared with the oracle's records; attention runs on the oracle's records."""
+"""Seeded random configurations of the unquantised region, Block-GTQ keys, two-stage keys and
+lossless BF16 pages through the C ABI against the oracle: head counts and groupings, ragged
+rows (an empty one now and then), section counts, dtypes and, for Block-GTQ, the width range
+and bit budget of the allocation.  Block-GTQ and two-stage keys are encoded by the library in
+two calls cut at a random slot and compared with the oracle's records; attention runs on the
+oracle's records.  BF16 pages are compressed in two calls cut at a random page, must equal the
+oracle's store and metadata byte for byte, and attention reads the library's pages."""
 
 from dataclasses import replace
 
@@ -13,13 +15,13 @@ import torch
 import compressed_domain_attention_amd as tq
 import workloads
 from helpers import oracle_decode, row_rel_err
-from oracle import blockgtq as bg, qjl
+from oracle import blockgtq as bg, qjl, zipcodec as zc
 
 pytestmark = pytest.mark.gpu
 
 DENSE_RTOL = 1e-4  # fp32 scores and sums over unquantised inputs
 FLIPS = {"flips": 0, "coords": 0, "cases": 0}  # code flips near a boundary, pooled over cases
-N_GTQ, N_QJL = 12, 8
+N_GTQ, N_QJL, N_ZIP = 12, 8, 12
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -207,6 +209,78 @@ def test_random_qjl(seed):
             rl[b, h] = m + np.log(p.sum())
     check(res[0].cpu().numpy(), res[1].cpu().numpy(), ro, rl, lens)
     FLIPS["cases"] += 1
+
+
+def exponent_windows(rng, x, pages, role):
+    """Set the exponents of a few random chunks of x (BF16 bits [B, H, T, 128]) to a window
+    of width 14 to 17 from an even or odd base, touching both ends: chunks at and just past
+    the largest coded span."""
+    for _ in range(int(rng.integers(0, 9))):
+        b, h, p = (int(rng.integers(0, n)) for n in x.shape[:2] + (pages,))
+        vals = zc.page_values(x[b, h, zc.PAGE * p:zc.PAGE * (p + 1)], role).reshape(zc.CHUNKS, zc.CHUNK)
+        c, lo, span = int(rng.integers(0, zc.CHUNKS)), int(rng.integers(100, 113)), int(rng.integers(14, 18))
+        e = lo + rng.integers(0, span + 1, size=zc.CHUNK)
+        e[rng.permutation(zc.CHUNK)[:2]] = (lo, lo + span)
+        vals[c] = (vals[c] & 0x807F) | (e.astype(np.uint16) << 7)
+        x[b, h, zc.PAGE * p:zc.PAGE * (p + 1)] = zc.page_from_values(vals.reshape(-1), role)
+
+
+@pytest.mark.parametrize("seed", range(N_ZIP))
+def test_random_zip(seed):
+    from test_gpu_zip import ROLE, check_rows, dev_bf16, oracle_stores
+    rng = np.random.default_rng(9700 + seed)
+    hkv, g = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 5, 8, 16, 24]))
+    batch, pages = int(rng.integers(1, 4)), int(rng.integers(1, 21))
+    open_tail = bool(rng.integers(0, 2))
+    # an open page past the store's last page when the tail is a 16-row buffer
+    t = int(rng.integers(1, zc.PAGE * pages + (zc.PAGE if open_tail else 1)))
+    lens = ragged(rng, batch, t)
+    n_splits = int(rng.choice([1, 2, 3, 7, 16]))
+    q_dtype = [torch.bfloat16, torch.float32, torch.float16][int(rng.integers(0, 3))]
+    scale = float(rng.uniform(0.04, 0.12))
+    w = replace(workloads.WORKLOADS["zipfusion8k"], batch=batch, n_q_heads=g * hkv, n_kv_heads=hkv,
+                seq_len=zc.PAGE * (pages + 1))
+    print("zip case %d: B=%d Hq=%d Hkv=%d pages %d lens %s S=%d q %s scale %.3f %s tail" % (
+        seed, batch, g * hkv, hkv, pages, lens.tolist(), n_splits, q_dtype, scale,
+        "open-page" if open_tail else "whole-cache"), flush=True)
+    inp = workloads.generate(w, seed)
+    for role in ("k", "v"):
+        exponent_windows(rng, inp[role], pages, role)
+    # the library's stores from two calls cut at a random page, against the oracle's
+    cut = int(rng.integers(0, pages + 1))
+    dev = {}
+    for role in ("k", "v"):
+        s, m = tq.zip_store(batch, hkv, pages)
+        x = dev_bf16(inp[role])
+        if cut > 0:
+            tq.zip_compress(x, s, m, ROLE[role], n_pages=cut)
+        if cut < pages:
+            tq.zip_compress(x, s, m, ROLE[role], n_pages=pages - cut, src_page0=cut, dst_page0=cut)
+        os_, om = oracle_stores(inp[role], pages, role)
+        assert np.array_equal(m.cpu().numpy(), om), role
+        assert np.array_equal(s.cpu().numpy(), os_), role
+        dev[role] = (s, m)
+    # tails: the whole BF16 cache, or 16-row buffers holding each row's open page
+    if open_tail:
+        tails = {r: np.zeros((batch, hkv, zc.PAGE, 128), np.uint16) for r in ("k", "v")}
+        for b, n in enumerate(lens):
+            for i in range(zc.PAGE * (int(n) // zc.PAGE), int(n)):
+                for r in ("k", "v"):
+                    tails[r][b, :, i % zc.PAGE] = inp[r][b, :, i]
+    else:
+        tails = {r: inp[r][:, :, :zc.PAGE * pages] for r in ("k", "v")}
+    qb = dev_bf16(inp["q"])
+    q = qb if q_dtype == torch.bfloat16 else qb.float().to(q_dtype)
+    res = tq.zip_attention(dev["k"][0], dev["k"][1], dev["v"][0], dev["v"][1], dev_bf16(tails["k"]),
+                           dev_bf16(tails["v"]), q, seq_lens=torch.from_numpy(lens).cuda(), max_len=t, scale=scale,
+                           n_splits=n_splits)
+    if n_splits > 1:
+        res = tq.merge_splits(None, *res)
+    torch.cuda.synchronize()
+    ks, km = oracle_stores(inp["k"], pages, "k")
+    vs, vm = oracle_stores(inp["v"], pages, "v")
+    ref_o, ref_l = zc.decode_from_pages(inp["q"], ks, km, vs, vm, tails["k"], tails["v"], lens, scale)
+    check_rows(res[0].cpu().numpy(), res[1].cpu().numpy(), ref_o, ref_l, lens, g)
 
 
 def test_random_codecs_flip_rate():
