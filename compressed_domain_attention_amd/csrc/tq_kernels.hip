@@ -580,11 +580,11 @@ __device__ __forceinline__ void token_range(const DecodeArgs& a, const Unit& u, 
 // value norm in fp16 (with a power-of-two range factor), taken straight from the score
 // registers.  Online softmax per column.
 //
-// Decode tables: 3-bit keys and values sharing one codebook use a table indexed by four
-// codes (4096 entries of four fp16 levels); otherwise an index of two codes (6 bits for
-// 3-bit codes, 8 for 4-bit) selects an entry of two fp16 levels, stored in 32 copies (3-bit)
-// or 8 and 16 (4-bit keys and values), copy c serving lanes c, c + 32 ... with the copies of
-// one entry side by side, so that the bank a lane reads is fixed by its lane number.
+// Decode tables: 3-bit codes are read through a table indexed by four codes (4096 entries
+// of four fp16 levels), one for keys and values that share a codebook; 4-bit codes through
+// an index of two codes (8 bits) that selects an entry of two fp16 levels, stored in 16
+// copies, copy c serving lanes c, c + 16 ... with the copies of one entry side by side, so
+// that the bank a lane reads is fixed by its lane number.
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
                                                 0, 0);
@@ -696,21 +696,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   constexpr bool FOLD = SPLITQ;
   constexpr int NPART = FOLD ? 2 * NW : NW;  // partial results per head in the epilogue
   constexpr int NP = FOLD ? 4 : 8;           // scores per lane and block
-  constexpr int NEK = BK == 3 ? 64 : 256;   // table entries: all pairs of codes
-  constexpr int NEV = BV == 3 ? 64 : 256;
+  constexpr int NEK = 256, NEV = 256;  // two-code table entries: all pairs of 4-bit codes
   constexpr int KREC = 16 * BK;
   constexpr int VTILE = kTile * 16 * BV;
-  // Decode tables.  3-bit keys and values with one codebook (QUAD) share one table indexed
-  // by four codes (12 bits, 4096 entries of four fp16 values, 32 KB): one read per four
-  // codes.  Otherwise two-code tables [entry][copies]: keys at 0, values at VT_AT (a power of two
-  // no smaller than either table, so a value address is VT_AT | offset).  3-bit tables have
-  // 32 copies (conflict-free); 4-bit tables have 8 (key) or 16 (value) copies to fit the
-  // LDS budget of two workgroups per CU, at the price of occasional bank conflicts.
-  constexpr int RK = BK == 3 ? 32 : 16, RV = BV == 3 ? 32 : 16;
-  constexpr int SHK = BK == 3 ? 7 : 6, SHV = BV == 3 ? 7 : 6;  // log2 of an entry's row bytes
-  static_assert(!QUAD || (BK == 3 && BV == 3), "the four-code table holds 3-bit codes");
-  constexpr int KT_BYTES = QUAD ? 32768 : NEK * RK * 4, VT_BYTES = QUAD ? 0 : NEV * RV * 4;
-  constexpr int VT_AT = KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
+  // Decode tables.  3-bit codes are read through tables indexed by four codes (12 bits, 4096
+  // entries of four fp16 values, 32 KB): one read per four codes.  3-bit keys and values
+  // with one codebook (QUAD) share the keys' table.  4-bit codes use two-code tables
+  // [entry][copies] with 16 copies, to fit the LDS budget of two workgroups per CU at the
+  // price of occasional bank conflicts.  Keys sit at 0, values at VT_AT: right after a
+  // four-code value table's keys, else a power of two no smaller than either table, so that
+  // a two-code value address is VT_AT | offset.
+  static_assert(!QUAD || (BK == 3 && BV == 3), "the shared four-code table holds 3-bit codes");
+  constexpr bool KQ = BK == 3, VQ = BV == 3 && !QUAD;  // four-code key and value tables
+  constexpr int RK = 16, RV = 16;
+  constexpr int SHK = 6, SHV = 6;  // log2 of a two-code entry's row bytes
+  constexpr int KT_BYTES = KQ ? 32768 : NEK * RK * 4, VT_BYTES = QUAD ? 0 : VQ ? 32768 : NEV * RV * 4;
+  constexpr int VT_AT = VQ ? KT_BYTES : KT_BYTES > VT_BYTES ? KT_BYTES : VT_BYTES;
   // Block ring: each wave keeps its next D blocks of 32 tokens in registers.  They
   // are read with buffer loads: the (sequence, KV head) slab in a buffer resource, the
   // block's offset in a scalar register and the lane's offset fixed, so a load costs no
@@ -863,24 +864,28 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
       vcb = (int)f16_bits((_Float16)(QUAD ? a.vcent[c] * a.kscale : a.vcent[c]));
     }
   }
-  if (QUAD) {
-    // Thread tid owns the entries whose two low codes are (tid >> 3) & 7, tid & 7; wave wv
-    // takes 64 / NW of the 64 pairs of high codes.  The low half of a thread's entries is
-    // fixed, and each step writes 64 consecutive entries.
-    const uint32_t lo = (uint32_t)__shfl(kcb, tid & 7) | ((uint32_t)__shfl(kcb, (tid >> 3) & 7) << 16);
+  // A four-code table: thread tid owns the entries whose two low codes are (tid >> 3) & 7,
+  // tid & 7; wave wv takes 64 / NW of the 64 pairs of high codes.  The low half of a
+  // thread's entries is fixed, and each step writes 64 consecutive entries.
+  auto quad_table = [&](uint8_t* base, int cb) {
+    const uint32_t lo = (uint32_t)__shfl(cb, tid & 7) | ((uint32_t)__shfl(cb, (tid >> 3) & 7) << 16);
 #pragma unroll
     for (int j = 0; j < 64 / NW; ++j) {
       const int hc = wv * (64 / NW) + j, c2 = hc & 7, c3 = hc >> 3;
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(kcb, c2) | ((uint32_t)__builtin_amdgcn_readlane(kcb, c3) << 16);
-      ((uint2*)pool)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, hi);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(cb, c2) | ((uint32_t)__builtin_amdgcn_readlane(cb, c3) << 16);
+      ((uint2*)base)[(tid & 63) | (c2 << 6) | (c3 << 9)] = make_uint2(lo, hi);
     }
+  };
+  if (KQ) {
+    quad_table(pool, kcb);
   } else {
     for (int i = tid; i < NEK * RK; i += NT) {
       const int e = i / RK;
       ((uint32_t*)pool)[i] = (uint32_t)__shfl(kcb, e & ((1 << BK) - 1)) | ((uint32_t)__shfl(kcb, e >> BK) << 16);
     }
   }
-  for (int i = tid; i < (QUAD ? 0 : NEV * RV); i += NT) {
+  if (VQ) quad_table(pool + VT_AT, vcb);
+  for (int i = tid; i < (BV == 3 ? 0 : NEV * RV); i += NT) {
     const int e = i / RV;
     ((uint32_t*)(pool + VT_AT))[i] = (uint32_t)__shfl(vcb, e & ((1 << BV) - 1)) | ((uint32_t)__shfl(vcb, e >> BV) << 16);
   }
@@ -944,7 +949,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
   const uint32_t klane = (lane & (RK - 1)) << 2, vlane = VT_AT | ((lane & (RV - 1)) << 2);
   auto key_operand = [&](const uint32_t* kk, int f) {
     u32x4 r;
-    if (QUAD) {
+    if (KQ) {
       const uint2 x0 = lds_at<uint2>(pool, quad_lds_addr(kk, 24 * f)), x1 = lds_at<uint2>(pool, quad_lds_addr(kk, 24 * f + 12));
       return u32x4{x0.x, x0.y, x1.x, x1.y};
     }
@@ -984,8 +989,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_mfma_kernel(c
     }
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      if (QUAD) {
-        const uint2 x0 = lds_at<uint2>(pool, quad_lds_addr(cb.v, 24 * f)), x1 = lds_at<uint2>(pool, quad_lds_addr(cb.v, 24 * f + 12));
+      if (BV == 3) {
+        const uint8_t* vt = pool + (QUAD ? 0 : VT_AT);
+        const uint2 x0 = lds_at<uint2>(vt, quad_lds_addr(cb.v, 24 * f)), x1 = lds_at<uint2>(vt, quad_lds_addr(cb.v, 24 * f + 12));
         va[f] = u32x4{x0.x, x0.y, x1.x, x1.y};
       } else {
 #pragma unroll
