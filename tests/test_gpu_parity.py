@@ -394,6 +394,11 @@ def test_decode_with_distinct_value_codebook(name):
         out, _ = tq.decode_attention(rot, k, v2, q, max_len=t, schedule=schedule)
         torch.cuda.synchronize()
         assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
+    # 20 sections: 320 workgroups, more than the compute units, so the four-wave kernel runs
+    po, pl = tq.decode_attention(rot, k, v2, q, max_len=t, n_splits=20, schedule="mfma")
+    out, _ = tq.merge_splits(rot, po, pl)
+    torch.cuda.synchronize()
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= OUT_RTOL
 
 
 def test_schedules_agree_and_are_deterministic():
