@@ -44,15 +44,18 @@ def draw(seed):
     n_splits = int(rng.choice([1, 2, 3, 7, 16]))
     schedule = str(rng.choice(["auto", "auto", "vec"]))
     q_dtype = str(rng.choice(["float16", "float32"]))
-    return w, lens, cut, n_splits, schedule, q_dtype
+    # now and then the decode reads the values through a codebook of their own (levels 1% up),
+    # which 3-bit keys and values cannot share a table with
+    distinct = bool(rng.random() < (0.5 if (w.bits_k, w.bits_v) == (3, 3) else 0.25))
+    return w, lens, cut, n_splits, schedule, q_dtype, distinct
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration(seed):
-    w, lens, cut, n_splits, schedule, q_dtype = draw(seed)
-    print("random case %d: B=%d Hq=%d Hkv=%d T=%d bits %d/%d g=%d so4=%s %s q %s lens %s cut %d S=%d %s" % (
+    w, lens, cut, n_splits, schedule, q_dtype, distinct = draw(seed)
+    print("random case %d: B=%d Hq=%d Hkv=%d T=%d bits %d/%d g=%d so4=%s %s q %s lens %s cut %d S=%d %s%s" % (
         seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.bits_k, w.bits_v, w.group, w.so4, w.dtype, q_dtype,
-        list(lens), cut, n_splits, schedule), flush=True)
+        lens.tolist(), cut, n_splits, schedule, " distinct value codebook" if distinct else ""), flush=True)
     inp = workloads.generate(w, seed)
     t, cap = w.seq_len, round_up(w.seq_len, 32) + 32 * (seed % 2)
     so4 = None if inp["so4"] is None else torch.from_numpy(inp["so4"]).cuda()
@@ -66,10 +69,17 @@ def test_random_configuration(seed):
         tq.quantize_append_kv(rot, kc, vc, kx[:, :, cut:].contiguous(), vx[:, :, cut:].contiguous(), pos0=cut)
     q = torch.from_numpy(inp["q"].astype(np.float32)).cuda().to(getattr(torch, q_dtype))
     seq = torch.from_numpy(lens).cuda()
+    vd_c = vc
+    if distinct:
+        cb = tq.make_codebook(w.bits_v, w.group)
+        for i in range(1 << w.bits_v):
+            cb.centroid[i] *= 1.01
+        vd_c = tq.PackedCache(w.batch, w.n_kv_heads, cap, w.bits_v, w.group, tq.TQ_VALUES, codes=vc.codes,
+                              norms=vc.norms, codebook=cb)
     if n_splits == 1:
-        out, lse = tq.decode_attention(rot, kc, vc, q, seq_lens=seq, max_len=t, schedule=schedule)
+        out, lse = tq.decode_attention(rot, kc, vd_c, q, seq_lens=seq, max_len=t, schedule=schedule)
     else:
-        po, pl = tq.decode_attention(rot, kc, vc, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
+        po, pl = tq.decode_attention(rot, kc, vd_c, q, seq_lens=seq, max_len=t, n_splits=n_splits, schedule=schedule)
         out, lse = tq.merge_splits(rot, po, pl)
     torch.cuda.synchronize()
     # the cache against the oracle's codes and norms
@@ -80,7 +90,8 @@ def test_random_configuration(seed):
         FLIPS["flips"] += check_codes(idx, nrm, oq, t, rate_bar=False)
         FLIPS["coords"] += oq["idx"].size
     # attention against fp64 attention over the oracle's cache
-    kd, vd = dequantized(w, inp, oqk), dequantized(w, inp, oqv)
+    kd = dequantized(w, inp, oqk)
+    vd = dequantized(w, inp, dict(oqv, centroids=np.asarray(oqv["centroids"]) * 1.01) if distinct else oqv)
     qq = dict(inp, q=q.float().cpu().numpy())
     ref, ref_lse = oracle_decode(w, qq, kd, vd, lens)
     o, l = out.cpu().numpy(), lse.cpu().numpy()
